@@ -1,0 +1,346 @@
+"""CPU oracle for one round of conditional draft-tree construction.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it, to check and to time against.
+It shares no code with the HIP library.
+
+What it computes, step by step, and where the pages define it
+-------------------------------------------------------------
+Pages cited (each by its title and section):
+  * "Resumen Técnico: Domino" -- Methodology 1 (parallel backbone: hidden
+    states H for the whole block, base logits through the frozen target LM
+    head) and Methodology 2 (Domino head: a GRU summarises the embeddings of
+    the preceding draft tokens into a causal state S; a low-rank head maps
+    the concatenation [H_i ; S_{i-1}] to rank r and back to vocabulary
+    space, giving Delta L_i; final logits L_i = L_base_i + Delta L_i).
+  * "Resumen Técnico: DominoTree" -- Main components 1 (best-first max-heap
+    keyed by cumulative path log-probability, children scored by the
+    path-specific correction; H is shared by all paths) and 2 (the
+    correction is restricted to the Top-M marginal candidates of each depth,
+    a 256 x M slice, before the Top-k children are chosen).
+  * "DARTree: Speculative Diffusion Decoding with Autoregressive Draft
+    Trees" -- Methodology 1 (depth-wise expansion: per-depth candidates from
+    the base logits, batched correction of every active branch with its own
+    prefix state, scoring by corrected cumulative probability, keep the top
+    W branches and carry their states) and Methodology 2 (after the
+    fixed-width superarbol is built, one global Top-B over all materialised
+    prefixes; Lemma 1: with a non-positive depth bonus beta this equals the
+    set a sequential best-first max-heap would pick).
+
+Readings where the pages leave a step open (each also listed in the design
+notes): log-softmax over the M candidates only; candidates per depth shared
+by all branches; every scored child enters the superarbol, only the top W
+are expanded; B excludes the root; key = score + beta * depth; GRU cell =
+the PyTorch GRUCell equations with gate blocks (r, z, n); state starts at 0
+and first consumes the root (last verified) token; no nonlinearity in the
+low-rank head; H[delta] scores the children at depth delta + 1;
+tie-breaks are value descending then structural (token ascending for Top-M
+and Top-K, lexicographic token path for Top-W, depth then lexicographic
+path for Top-B); output in canonical order (depth, lexicographic path);
+scores returned without the depth bonus; the mask holds ancestors and self.
+
+Arithmetic: float64 everywhere, with values rounded to float32 at the
+storage points marked ``_st`` (``store="f32"``, the default); with
+``store="f64"`` nothing is rounded, which is what the brute-force pins use.
+In bf16 mode the only bf16 values are the stored weights and Hq = bf16(H).
+"""
+import heapq
+
+import numpy as np
+
+__all__ = [
+    "bf16_round", "decode", "OracleWeights", "base_logits", "top_m",
+    "gru_cell", "log_softmax", "build_superarbol", "select_global_top_b",
+    "select_literal_heap", "emit_tree", "build_round",
+]
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+def bf16_round(x):
+    """Round float32 values to the nearest bf16 (ties to even); float32 out.
+
+    bf16 keeps the top 16 bits of an IEEE float32.  Adding 0x7FFF plus the
+    lowest kept bit and truncating is round-to-nearest-even.  Inputs are
+    finite (the round's inputs must be finite).
+    """
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)) << np.uint64(16)
+    return r.astype(np.uint32).view(np.float32)
+
+
+def decode(arr, wtype):
+    """Stored weights -> float64.  bf16 arrays arrive as uint16 bit patterns."""
+    if wtype == "bf16":
+        a = np.asarray(arr, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return a.view(np.float32).astype(np.float64)
+    return np.asarray(arr, dtype=np.float32).astype(np.float64)
+
+
+def _storer(store):
+    if store == "f32":
+        return lambda x: np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if store == "f64":
+        return lambda x: np.asarray(x, dtype=np.float64)
+    raise ValueError(store)
+
+
+class OracleWeights:
+    """The shared weights decoded to float64 (the large tables lazily)."""
+
+    def __init__(self, weights, wtype, d, s):
+        self.raw = weights
+        self.wtype = wtype
+        self.d, self.s = d, s
+        self.W_ih = decode(weights["W_ih"], wtype)
+        self.W_hh = decode(weights["W_hh"], wtype)
+        self.b_ih = np.asarray(weights["b_ih"], np.float32).astype(np.float64)
+        self.b_hh = np.asarray(weights["b_hh"], np.float32).astype(np.float64)
+        W1 = decode(weights["W1"], wtype)
+        self.W1_H = W1[:, :d]          # acts on H_i
+        self.W1_S = W1[:, d:d + s]     # acts on S_{i-1}
+        b = weights.get("bias")
+        self.bias = None if b is None else np.asarray(b, np.float32).astype(np.float64)
+
+    def emb_rows(self, toks):
+        return decode(self.raw["Emb"][np.asarray(toks, dtype=np.int64)], self.wtype)
+
+    def w2_rows(self, toks):
+        return decode(self.raw["W2"][np.asarray(toks, dtype=np.int64)], self.wtype)
+
+
+# ---------------------------------------------------------------------------
+# steps of one round
+# ---------------------------------------------------------------------------
+def base_logits(Hq, weights, wtype, store="f32", chunk=8192):
+    """L_base = Hq . W_lm^T + bias for every row of Hq (rows = depths).
+
+    Domino page, Methodology 1: the base logits come from the backbone's
+    hidden states through the frozen target LM head; the Zipf-like unigram
+    bias of the synthetic workload is added to them.  Computed one vocabulary
+    slab at a time so the float64 copy of W_lm never exists whole.
+    """
+    st = _storer(store)
+    W_lm = weights["W_lm"]
+    V = W_lm.shape[0]
+    Hq64 = np.asarray(Hq, dtype=np.float64)
+    out = np.empty((Hq64.shape[0], V), dtype=np.float64)
+    bias = weights.get("bias")
+    for lo in range(0, V, chunk):
+        hi = min(V, lo + chunk)
+        slab = Hq64 @ decode(W_lm[lo:hi], wtype).T
+        if bias is not None:
+            slab = slab + np.asarray(bias[lo:hi], np.float32).astype(np.float64)
+        out[:, lo:hi] = st(slab)
+    return out
+
+
+def top_m(row, M):
+    """Top-M tokens of one row of base logits: value descending, token
+    ascending on exact ties.  Returns (tokens, values) in that order.
+
+    DominoTree page, Main components 2; DARTree page, Methodology 1
+    (candidate selection from the base logits at each depth).
+    """
+    toks = np.arange(row.shape[0])
+    order = np.lexsort((toks, -row))[:M]
+    return order.astype(np.int64), row[order]
+
+
+def gru_cell(x, h, W, store="f32"):
+    """One GRU step, PyTorch GRUCell form, gate blocks (r, z, n).
+
+    Domino page, Methodology 2: a light GRU folds the embedding of each
+    preceding draft token into the causal state.  x: [n, e], h: [n, s].
+    """
+    st = _storer(store)
+    s = W.s
+    a = x @ W.W_ih.T + W.b_ih          # input part, [n, 3s]
+    c = h @ W.W_hh.T + W.b_hh          # state part, [n, 3s]
+    r = 1.0 / (1.0 + np.exp(-(a[:, :s] + c[:, :s])))
+    z = 1.0 / (1.0 + np.exp(-(a[:, s:2 * s] + c[:, s:2 * s])))
+    n = np.tanh(a[:, 2 * s:] + r * c[:, 2 * s:])
+    return st((1.0 - z) * n + z * h)
+
+
+def log_softmax(ell, store="f32"):
+    """Row-wise log-softmax over the M candidate columns, max-shifted."""
+    st = _storer(store)
+    m = ell.max(axis=1, keepdims=True)
+    lse = m + np.log(np.exp(ell - m).sum(axis=1, keepdims=True))
+    return st(ell - lse)
+
+
+def _key(score, depth, beta, store):
+    """Selection key score + beta * depth (DARTree page, Methodology 2)."""
+    if store == "f32":
+        return float(np.float32(score) + np.float32(np.float32(beta) * np.float32(depth)))
+    return float(score) + float(beta) * float(depth)
+
+
+def build_superarbol(Hq_req, root_tok, Lb_req, W, D, M, K, Wd, store="f32"):
+    """Depth-wise construction of one request's superarbol.
+
+    DARTree page, Methodology 1, with the Domino head as the corrected
+    drafter (Domino page, Methodology 2) and the Top-M restriction
+    (DominoTree page, Main components 2).
+
+    Hq_req: [D, d] rounded hidden states; Lb_req: [D, V] base logits.
+    Wd is the branch width W (the name W is taken by the weights).
+    Returns a dict with the node table and the per-depth intermediates.
+    """
+    st = _storer(store)
+    C = np.empty((D, M), dtype=np.int64)
+    Cl = np.empty((D, M), dtype=np.float64)
+    for dd in range(D):
+        C[dd], Cl[dd] = top_m(Lb_req[dd], M)
+    # path-independent part of the low-rank projection, shared by all paths
+    uH = st(np.asarray(Hq_req, np.float64) @ W.W1_H.T)          # [D, r]
+
+    tok, par, dep, score, path = [int(root_tok)], [-1], [0], [0.0], [()]
+    kids = [[]]
+    # the block starts with the last verified token: the GRU consumes it first
+    S = gru_cell(W.emb_rows([root_tok]), np.zeros((1, W.s)), W, store)
+    frontier = [0]
+    per_depth = []
+    for dd in range(D):
+        A = len(frontier)
+        u = st(uH[dd][None, :] + S @ W.W1_S.T)                   # [A, r]
+        ell = st(Cl[dd][None, :] + u @ W.w2_rows(C[dd]).T)      # [A, M]
+        lp = log_softmax(ell, store)                             # [A, M]
+        children = []
+        for a, p in enumerate(frontier):
+            # Top-K children of branch p: lp descending, token ascending
+            order = np.lexsort((C[dd], -lp[a]))[:K]
+            for j in order:
+                nid = len(tok)
+                tok.append(int(C[dd][j]))
+                par.append(p)
+                dep.append(dd + 1)
+                score.append(float(st(score[p] + lp[a, j])))
+                path.append(path[p] + (int(C[dd][j]),))
+                kids.append([])
+                kids[p].append(nid)
+                children.append(nid)
+        # Top-W survivors of the depth: score descending, lexicographic path
+        surv = sorted(children, key=lambda n: (-score[n], path[n]))[:Wd]
+        per_depth.append(dict(frontier=list(frontier), u=u, ell=ell, lp=lp,
+                              children=children, survivors=surv))
+        if dd + 1 < D:
+            slot = {p: a for a, p in enumerate(frontier)}
+            S = gru_cell(W.emb_rows([tok[c] for c in surv]),
+                         S[[slot[par[c]] for c in surv]], W, store)
+        frontier = surv
+    return dict(tok=tok, parent=par, depth=dep, score=score, path=path,
+                kids=kids, C=C, Cl=Cl, uH=uH, per_depth=per_depth)
+
+
+def _order_key(sa, n, beta, store):
+    """Total order used by the selection: key desc, depth asc, path asc."""
+    return (-_key(sa["score"][n], sa["depth"][n], beta, store),
+            sa["depth"][n], sa["path"][n])
+
+
+def select_global_top_b(sa, B, beta, store="f32"):
+    """One global Top-B over every materialised prefix (root excluded).
+
+    DARTree page, Methodology 2 (deferred pruning)."""
+    nodes = range(1, len(sa["tok"]))
+    ranked = sorted(nodes, key=lambda n: _order_key(sa, n, beta, store))
+    return ranked[:min(B, len(ranked))]
+
+
+def select_literal_heap(sa, B, beta, store="f32"):
+    """The sequential best-first max-heap over the same superarbol: start
+    from the root's children, pop the best node, push its children, repeat.
+
+    DominoTree page, Main components 1; DARTree page, Problem statement
+    (the heap loop) -- the definition Lemma 1 compares the global Top-B to.
+    """
+    heap = [(_order_key(sa, c, beta, store), c) for c in sa["kids"][0]]
+    heapq.heapify(heap)
+    pops = []
+    for _ in range(min(B, len(sa["tok"]) - 1)):
+        if not heap:
+            break
+        _, n = heapq.heappop(heap)
+        pops.append(n)
+        for c in sa["kids"][n]:
+            heapq.heappush(heap, (_order_key(sa, c, beta, store), c))
+    return pops
+
+
+def emit_tree(sa, sel, B):
+    """Compact tree for verification: the root, then the selected nodes in
+    canonical order (depth, lexicographic path); parents re-indexed; the
+    ancestor-or-self mask (DominoTree page, Main components 5: tree attention
+    with an ancestor-only mask).  Scores are the raw cumulative log-probs.
+    Raises if the selection is not closed under parents.
+    """
+    chosen = set(sel)
+    for n in sel:
+        p = sa["parent"][n]
+        if p != 0 and p not in chosen:
+            raise AssertionError(f"selection not ancestor-closed at node {n}")
+    order = [0] + sorted(sel, key=lambda n: (sa["depth"][n], sa["path"][n]))
+    N = B + 1
+    n_nodes = len(order)
+    idx = {n: i for i, n in enumerate(order)}
+    tok = np.full(N, -1, np.int32)
+    parent = np.full(N, -1, np.int32)
+    depth = np.full(N, -1, np.int32)
+    score = np.full(N, -np.inf, np.float32)
+    mask = np.zeros((N, N), np.uint8)
+    for i, n in enumerate(order):
+        tok[i] = sa["tok"][n]
+        depth[i] = sa["depth"][n]
+        score[i] = np.float32(sa["score"][n])
+        parent[i] = -1 if n == 0 else idx[sa["parent"][n]]
+        if i > 0:
+            mask[i] = mask[parent[i]]
+        mask[i, i] = 1
+    return dict(tok=tok, parent=parent, depth=depth, score=score, mask=mask,
+                n_nodes=n_nodes, order=order)
+
+
+def build_round(inputs, D, M, K, W, B, beta, store="f32", check_heap=True):
+    """Whole round for every request of ``inputs`` (as drawn by ``synth``).
+
+    Returns per-request outputs (tok, parent, depth, score, mask, n_nodes)
+    and the superarbol trace used by the checkers.
+    """
+    wts, wtype = inputs["weights"], inputs["wtype"]
+    H = np.asarray(inputs["H"], dtype=np.float32)
+    b, Dh, d = H.shape
+    assert Dh >= D
+    s = wts["W_hh"].shape[1]
+    Wo = OracleWeights(wts, wtype, d, s)
+    Hq = bf16_round(H[:, :D]) if wtype == "bf16" else H[:, :D]
+    Lb = base_logits(Hq.reshape(b * D, d), wts, wtype, store).reshape(b, D, -1)
+    reqs = []
+    for q in range(b):
+        sa = build_superarbol(Hq[q], int(inputs["root"][q]), Lb[q], Wo,
+                              D, M, K, W, store)
+        sel = select_global_top_b(sa, B, beta, store)
+        if check_heap:
+            pops = select_literal_heap(sa, B, beta, store)
+            if set(pops) != set(sel):
+                raise AssertionError("Lemma 1 violated: heap and global Top-B differ")
+        out = emit_tree(sa, sel, B)
+        out["sa"] = sa
+        out["sel"] = sel
+        out["lb_sorted"] = _top_slice(Lb[q], M + 64)
+        reqs.append(out)
+    return reqs
+
+
+def _top_slice(Lb_req, n):
+    """The n best base logits per depth (for the checker's near-tie test)."""
+    res = []
+    for row in Lb_req:
+        t, v = top_m(row, min(n, row.shape[0]))
+        res.append((t, v))
+    return res
