@@ -1,0 +1,100 @@
+// Device helpers shared by the draft-tree kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dtree {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// Round a finite fp32 to bf16, nearest-even.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Weight element loads: bf16 weights arrive as raw uint16 patterns.
+__device__ __forceinline__ float wload(const uint16_t *p, size_t i) {
+  return bf16_bits_to_f32(p[i]);
+}
+__device__ __forceinline__ float wload(const float *p, size_t i) { return p[i]; }
+
+// ---------------------------------------------------------------- keys
+// Monotone map of fp32 to uint32 (larger float -> larger integer); -0 is
+// folded onto +0 so the two compare equal, as they do as floats.
+__device__ __forceinline__ uint32_t f32_ord(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord_f32(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+// 64-bit selection key, larger is better: value descending, then the tie
+// field ascending.  Valid keys are never 0, which marks an empty slot.
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t tie) {
+  return ((uint64_t)f32_ord(v) << 32) | (uint64_t)(0xFFFFFFFFu - tie);
+}
+__device__ __forceinline__ uint32_t key_tie(uint64_t k) {
+  return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull);
+}
+__device__ __forceinline__ float key_val(uint64_t k) { return ord_f32((uint32_t)(k >> 32)); }
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor((unsigned long long)v, o, WIDTH);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Block-wide bitonic sort of n (power of two) keys with an int payload,
+// descending.  All threads of the block must call it.
+__device__ inline void block_bitonic_desc(uint64_t *keys, int32_t *vals, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        int ixj = i ^ j;
+        if (ixj > i) {
+          uint64_t a = keys[i], b = keys[ixj];
+          bool desc = (i & k) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            keys[i] = b;
+            keys[ixj] = a;
+            int32_t t = vals[i];
+            vals[i] = vals[ixj];
+            vals[ixj] = t;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int next_pow2(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+}  // namespace dtree

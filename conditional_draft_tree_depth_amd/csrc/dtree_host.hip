@@ -1,0 +1,411 @@
+// Host runtime of libdtree.so: argument checks, workspace, launch sequence.
+//
+// One round (dtree_build_round) enqueues, on the caller's stream and with no
+// host synchronisation:
+//   K1  base logits + fused per-slice Top-M      (k_lmhead.hip)
+//   K1b merge of the slices -> C, Cl             (k_lmhead.hip)
+//   K2  uH = W1[:, :d] Hq, root GRU state        (k_gemm.hip)
+//   for each depth: u = uH + W1[:, d:] S, corrected logits of the M
+//       candidates, selection, GRU step of the survivors  (k_gemm/k_depth)
+//   K4  global Top-B, canonical order, mask      (k_topb.hip)
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "dtree.h"
+#include "kernels.hpp"
+
+using namespace dtree;
+
+namespace {
+thread_local std::string g_create_err;
+
+struct Ws {
+  uint64_t *part = nullptr;
+  int32_t *C = nullptr;
+  float *Cl = nullptr, *uH = nullptr, *S[2] = {nullptr, nullptr}, *u = nullptr;
+  float *ell = nullptr, *gi = nullptr, *gh = nullptr;
+  int32_t *n_tok = nullptr, *n_par = nullptr, *n_dep = nullptr;
+  float *n_score = nullptr;
+  uint32_t *n_lex = nullptr;
+  int32_t *surv[2] = {nullptr, nullptr}, *rank[2] = {nullptr, nullptr};
+  int32_t *surv_hist = nullptr, *gidx_tok = nullptr, *gidx_par = nullptr, *sel = nullptr;
+  uint32_t *status = nullptr;
+};
+
+int superarbol_nodes(int D, int K, int W) {
+  long long A = 1, NT = 1;
+  for (int dd = 0; dd < D; ++dd) {
+    NT += A * K;
+    A = A * K < W ? A * K : W;
+    if (NT > (1 << 30)) return -1;
+  }
+  return (int)NT;
+}
+}  // namespace
+
+struct dtree_ctx {
+  int device = 0;
+  dtree_weights w{};
+  dtree_caps caps{};
+  int P = 0, NTcap = 0;
+  size_t k1_smem = 0, lds_max = 0;
+  Ws ws;
+  std::string err;
+  bool has_round = false;
+  dtree_params last{};
+  int last_batch = 0, last_NT = 0;
+  // stage timing: kProfRounds rounds x (DTREE_NSTAGES + 1) events
+  bool prof = false;
+  int prof_n = 0;
+  hipEvent_t *prof_ev = nullptr;
+};
+
+static constexpr int kProfRounds = 4096;
+
+static dtree_status fail(dtree_ctx *c, dtree_status s, const std::string &m) {
+  if (c) c->err = m; else g_create_err = m;
+  return s;
+}
+
+#define HIPCHK(ctx, expr)                                                                \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(ctx, DTREE_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+namespace {
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+template <typename T>
+hipError_t alloc(T **p, size_t n) {
+  return hipMalloc(reinterpret_cast<void **>(p), (n ? n : 1) * sizeof(T));
+}
+
+void free_ws(Ws &ws) {
+  void *ptrs[] = {ws.part, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.u, ws.ell, ws.gi, ws.gh,
+                  ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
+                  ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
+                  ws.status};
+  for (void *p : ptrs)
+    if (p) (void)hipFree(p);
+  ws = Ws();
+}
+}  // namespace
+
+static void prof_mark(dtree_ctx *ctx, int stage, hipStream_t st) {
+  if (ctx->prof && ctx->prof_n < kProfRounds)
+    (void)hipEventRecord(ctx->prof_ev[ctx->prof_n * (DTREE_NSTAGES + 1) + stage], st);
+}
+
+extern "C" int32_t dtree_superarbol_nodes(const dtree_params *p) {
+  if (!p || p->D < 1 || p->K < 1 || p->W < 1) return -1;
+  return superarbol_nodes(p->D, p->K, p->W);
+}
+
+extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *caps, int device,
+                                     dtree_ctx **out) {
+  g_create_err.clear();
+  if (!w || !caps || !out) return fail(nullptr, DTREE_E_ARG, "null argument");
+  *out = nullptr;
+  if (w->wtype != DTREE_F32 && w->wtype != DTREE_BF16)
+    return fail(nullptr, DTREE_E_DTYPE, "wtype must be DTREE_F32 or DTREE_BF16");
+  if (w->d < 1 || w->V < 1 || w->e < 1 || w->s < 1 || w->r < 1)
+    return fail(nullptr, DTREE_E_ARG, "d, V, e, s, r must be >= 1");
+  if (w->V > (1 << 18)) return fail(nullptr, DTREE_E_SHAPE, "V must be <= 262144");
+  if (!w->W_lm || !w->Emb || !w->W_ih || !w->W_hh || !w->W1 || !w->W2)
+    return fail(nullptr, DTREE_E_ARG, "null weight pointer");
+  if (w->wtype == DTREE_BF16) {
+    if (w->d % 128) return fail(nullptr, DTREE_E_SHAPE, "bf16 weights need d % 128 == 0");
+    if (reinterpret_cast<uintptr_t>(w->W_lm) % 16)
+      return fail(nullptr, DTREE_E_ARG, "W_lm must be 16-byte aligned");
+  }
+  const dtree_caps &c = *caps;
+  if (c.max_batch < 1 || c.max_D < 1 || c.max_M < 1 || c.max_K < 1 || c.max_W < 1 || c.max_B < 1)
+    return fail(nullptr, DTREE_E_ARG, "caps must be >= 1");
+  if (c.max_D > 31) return fail(nullptr, DTREE_E_SHAPE, "max_D must be <= 31");
+  if (c.max_M > 128) return fail(nullptr, DTREE_E_SHAPE, "max_M must be <= 128");
+  if (c.max_W > 512) return fail(nullptr, DTREE_E_SHAPE, "max_W must be <= 512");
+  if ((long long)c.max_W * c.max_K > 1024)
+    return fail(nullptr, DTREE_E_SHAPE, "max_W * max_K must be <= 1024");
+  const int NTcap = superarbol_nodes(c.max_D, c.max_K, c.max_W);
+  if (NTcap < 0 || NTcap > 8192)
+    return fail(nullptr, DTREE_E_SHAPE, "superarbol of the caps exceeds 8192 nodes");
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
+    return fail(nullptr, DTREE_E_DEVICE, "no such HIP device");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess)
+    return fail(nullptr, DTREE_E_DEVICE, "device query failed");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(nullptr, DTREE_E_DEVICE, std::string("needs gfx950, found ") + prop.gcnArchName);
+
+  dtree_ctx *ctx = new (std::nothrow) dtree_ctx();
+  if (!ctx) return fail(nullptr, DTREE_E_NOMEM, "host allocation failed");
+  ctx->device = device;
+  ctx->w = *w;
+  ctx->caps = c;
+  ctx->NTcap = NTcap;
+  ctx->lds_max = prop.sharedMemPerBlock;
+  ctx->P = lmhead_partitions(w->V, w->wtype);
+  ctx->k1_smem = lmhead_smem(w->d, w->wtype);
+  const size_t cl_smem = corr_logits_smem(c.max_W, c.max_M, w->r, w->wtype);
+  const size_t tb_smem = topb_smem(NTcap, c.max_B);
+  auto reject = [&](dtree_status s, const std::string &m) {
+    delete ctx;
+    return fail(nullptr, s, m);
+  };
+  if (ctx->k1_smem > ctx->lds_max) return reject(DTREE_E_SHAPE, "d too large for the LM-head LDS tile");
+  if (cl_smem > ctx->lds_max) return reject(DTREE_E_SHAPE, "max_M * r + max_W * r too large for LDS");
+  if (tb_smem > ctx->lds_max) return reject(DTREE_E_SHAPE, "superarbol too large for the Top-B LDS sort");
+
+  DeviceGuard dg(device);
+  Ws &ws = ctx->ws;
+  const size_t rows = (size_t)c.max_batch * c.max_D;
+  const size_t bw = (size_t)c.max_batch * c.max_W;
+  const int s = w->s, r = w->r;
+  hipError_t e = hipSuccess;
+  auto A = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+  A(alloc(&ws.part, rows * ctx->P * c.max_M));
+  A(alloc(&ws.C, rows * c.max_M));
+  A(alloc(&ws.Cl, rows * c.max_M));
+  A(alloc(&ws.uH, rows * r));
+  A(alloc(&ws.S[0], bw * s));
+  A(alloc(&ws.S[1], bw * s));
+  A(alloc(&ws.u, bw * r));
+  A(alloc(&ws.ell, bw * c.max_M));
+  A(alloc(&ws.gi, bw * 3 * s));
+  A(alloc(&ws.gh, bw * 3 * s));
+  const size_t nt = (size_t)c.max_batch * NTcap;
+  A(alloc(&ws.n_tok, nt));
+  A(alloc(&ws.n_par, nt));
+  A(alloc(&ws.n_dep, nt));
+  A(alloc(&ws.n_score, nt));
+  A(alloc(&ws.n_lex, nt));
+  for (int i = 0; i < 2; ++i) { A(alloc(&ws.surv[i], bw)); A(alloc(&ws.rank[i], bw)); }
+  A(alloc(&ws.surv_hist, (size_t)c.max_batch * (c.max_D + 1) * c.max_W));
+  A(alloc(&ws.gidx_tok, bw));
+  A(alloc(&ws.gidx_par, bw));
+  A(alloc(&ws.sel, (size_t)c.max_batch * c.max_B));
+  A(alloc(&ws.status, 1));
+  if (e != hipSuccess) {
+    free_ws(ws);
+    return reject(DTREE_E_NOMEM, std::string("workspace: ") + hipGetErrorString(e));
+  }
+  hipError_t pe = lmhead_prepare(w->wtype, ctx->k1_smem);
+  if (pe == hipSuccess) pe = corr_logits_prepare(w->wtype, cl_smem);
+  if (pe == hipSuccess) pe = topb_prepare(tb_smem);
+  if (pe != hipSuccess) {
+    free_ws(ws);
+    return reject(DTREE_E_HIP, std::string("kernel attributes: ") + hipGetErrorString(pe));
+  }
+  *out = ctx;
+  return DTREE_OK;
+}
+
+extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p, int32_t batch,
+                                          const float *H, const int32_t *root, int32_t *tok,
+                                          int32_t *parent, int32_t *depth, float *score,
+                                          uint8_t *mask, int32_t *n_nodes, void *stream) {
+  if (!ctx) return DTREE_E_ARG;
+  ctx->err.clear();
+  if (!p) return fail(ctx, DTREE_E_ARG, "null params");
+  if (!H || !root || !tok || !parent || !depth || !score || !mask || !n_nodes)
+    return fail(ctx, DTREE_E_ARG, "null input or output pointer");
+  const dtree_caps &c = ctx->caps;
+  const int D = p->D, M = p->M, K = p->K, W = p->W, B = p->B;
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DTREE_E_ARG, "batch outside [1, max_batch]");
+  if (D < 1 || D > c.max_D) return fail(ctx, DTREE_E_ARG, "D outside [1, max_D]");
+  if (M < 1 || M > c.max_M || M > ctx->w.V) return fail(ctx, DTREE_E_ARG, "M outside [1, min(max_M, V)]");
+  if (K < 1 || K > M || K > c.max_K) return fail(ctx, DTREE_E_ARG, "K outside [1, min(M, max_K)]");
+  if (W < 1 || W > c.max_W) return fail(ctx, DTREE_E_ARG, "W outside [1, max_W]");
+  if (B < 1 || B > c.max_B) return fail(ctx, DTREE_E_ARG, "B outside [1, max_B]");
+  if (!(p->beta <= 0.0f)) return fail(ctx, DTREE_E_ARG, "beta must be <= 0 (and not NaN)");
+  if (std::isinf(p->beta)) return fail(ctx, DTREE_E_ARG, "beta must be finite");
+
+  DeviceGuard dg(ctx->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dtree_weights &w = ctx->w;
+  Ws &ws = ctx->ws;
+  const int rows = batch * D;
+  const int d = w.d, s = w.s, r = w.r;
+  const int wt = w.wtype == DTREE_BF16 ? WT_BF16 : WT_F32;
+  const size_t esz = wt == WT_BF16 ? 2 : 4;
+  ctx->has_round = false;
+
+  // K1 + K1b: candidate tables
+  prof_mark(ctx, 0, st);
+  LMHeadArgs la{H, rows, d, w.W_lm, wt, w.V, w.lm_bias, M, ctx->P, ws.part};
+  HIPCHK(ctx, launch_lmhead(la, st));
+  prof_mark(ctx, 1, st);
+  HIPCHK(ctx, launch_topm_merge(ws.part, ctx->P, M, rows, ws.C, ws.Cl, st));
+  prof_mark(ctx, 2, st);
+  // K2: uH = W1[:, :d] . Hq for every (request, depth)
+  GemmArgs g{};
+  g = GemmArgs{rows, r, d, H, WT_F32, d, nullptr, wt == WT_BF16 ? 1 : 0, w.W1, wt, d + s,
+               nullptr, nullptr, 0, 1, 0, 0, ws.uH, r};
+  HIPCHK(ctx, launch_gemm(g, st));
+
+  TreeBufs tb{};
+  tb.NT = ctx->NTcap;
+  tb.Wmax = c.max_W;
+  tb.n_tok = ws.n_tok; tb.n_par = ws.n_par; tb.n_dep = ws.n_dep;
+  tb.n_score = ws.n_score; tb.n_lex = ws.n_lex;
+  tb.surv_hist = ws.surv_hist; tb.gidx_tok = ws.gidx_tok; tb.gidx_par = ws.gidx_par;
+  tb.sel = ws.sel; tb.status = ws.status;
+  int cur = 0;
+  tb.surv_node = ws.surv[0]; tb.surv_rank = ws.rank[0];
+  tb.nsurv_node = ws.surv[1]; tb.nsurv_rank = ws.rank[1];
+  HIPCHK(ctx, launch_init_round(batch, root, tb, D + 1, st));
+  // root state: the GRU consumes the last verified token from a zero state
+  g = GemmArgs{batch, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
+               w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
+  HIPCHK(ctx, launch_gemm(g, st));
+  HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, w.b_hh, nullptr, nullptr, ws.S[0], st));
+  prof_mark(ctx, 3, st);
+
+  int A = 1, off = 1, sc = 0;
+  for (int dd = 0; dd < D; ++dd) {
+    // u = uH[req, dd] + W1[:, d:] . S  for every expanded branch
+    g = GemmArgs{batch * A, r, s, ws.S[sc], WT_F32, s, nullptr, 0,
+                 static_cast<const uint8_t *>(w.W1) + (size_t)d * esz, wt, d + s, nullptr,
+                 ws.uH, r, A, D, dd, ws.u, r};
+    HIPCHK(ctx, launch_gemm(g, st));
+    HIPCHK(ctx, launch_corr_logits(batch, A, M, r, D, dd, w.W2, wt, ws.C, ws.Cl, ws.u, ws.ell, st));
+    HIPCHK(ctx, launch_select(batch, A, M, K, W, D, dd, off, ws.C, ws.ell, tb, st));
+    const int An = A * K < W ? A * K : W;
+    if (dd + 1 < D) {
+      g = GemmArgs{batch * An, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
+                   w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
+      HIPCHK(ctx, launch_gemm(g, st));
+      g = GemmArgs{batch * An, 3 * s, s, ws.S[sc], WT_F32, s, ws.gidx_par, 0, w.W_hh, wt, s,
+                   w.b_hh, nullptr, 0, 1, 0, 0, ws.gh, 3 * s};
+      HIPCHK(ctx, launch_gemm(g, st));
+      HIPCHK(ctx, launch_gru_combine(batch * An, s, ws.gi, ws.gh, nullptr, ws.S[sc], ws.gidx_par,
+                                     ws.S[1 - sc], st));
+      sc = 1 - sc;
+    }
+    cur = 1 - cur;
+    tb.surv_node = ws.surv[cur]; tb.surv_rank = ws.rank[cur];
+    tb.nsurv_node = ws.surv[1 - cur]; tb.nsurv_rank = ws.rank[1 - cur];
+    off += A * K;
+    A = An;
+  }
+  const int NT = off;
+  prof_mark(ctx, 4, st);
+  HIPCHK(ctx, launch_topb_emit(batch, NT, B, p->beta, c.max_B, tb, tok, parent, depth, score,
+                               mask, n_nodes, st));
+  prof_mark(ctx, 5, st);
+  if (ctx->prof && ctx->prof_n < kProfRounds) ++ctx->prof_n;
+  ctx->has_round = true;
+  ctx->last = *p;
+  ctx->last_batch = batch;
+  ctx->last_NT = NT;
+  return DTREE_OK;
+}
+
+extern "C" dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace *o) {
+  if (!ctx) return DTREE_E_ARG;
+  ctx->err.clear();
+  if (!o) return fail(ctx, DTREE_E_ARG, "null trace");
+  if (!ctx->has_round) return fail(ctx, DTREE_E_STATE, "no round has been built");
+  if (req < 0 || req >= ctx->last_batch) return fail(ctx, DTREE_E_ARG, "req out of range");
+  DeviceGuard dg(ctx->device);
+  HIPCHK(ctx, hipDeviceSynchronize());
+  const dtree_params &p = ctx->last;
+  const Ws &ws = ctx->ws;
+  const size_t cm = (size_t)p.D * p.M;
+  const size_t nb = (size_t)req * ctx->NTcap;
+  const int NT = ctx->last_NT, Wm = ctx->caps.max_W;
+  if (o->C) HIPCHK(ctx, hipMemcpy(o->C, ws.C + req * cm, cm * 4, hipMemcpyDeviceToHost));
+  if (o->Cl) HIPCHK(ctx, hipMemcpy(o->Cl, ws.Cl + req * cm, cm * 4, hipMemcpyDeviceToHost));
+  if (o->node_tok) HIPCHK(ctx, hipMemcpy(o->node_tok, ws.n_tok + nb, NT * 4, hipMemcpyDeviceToHost));
+  if (o->node_parent) HIPCHK(ctx, hipMemcpy(o->node_parent, ws.n_par + nb, NT * 4, hipMemcpyDeviceToHost));
+  if (o->node_score) HIPCHK(ctx, hipMemcpy(o->node_score, ws.n_score + nb, NT * 4, hipMemcpyDeviceToHost));
+  if (o->surv)
+    HIPCHK(ctx, hipMemcpy2D(o->surv, (size_t)p.W * 4, ws.surv_hist + (size_t)req * (p.D + 1) * Wm,
+                            (size_t)Wm * 4, (size_t)p.W * 4, p.D + 1, hipMemcpyDeviceToHost));
+  if (o->sel)
+    HIPCHK(ctx, hipMemcpy(o->sel, ws.sel + (size_t)req * ctx->caps.max_B, (size_t)p.B * 4,
+                          hipMemcpyDeviceToHost));
+  uint32_t st = 0;
+  HIPCHK(ctx, hipMemcpy(&st, ws.status, 4, hipMemcpyDeviceToHost));
+  o->n_sa = NT;
+  o->status = (int32_t)st;
+  return DTREE_OK;
+}
+
+extern "C" dtree_status dtree_profile_enable(dtree_ctx *ctx, int enable) {
+  if (!ctx) return DTREE_E_ARG;
+  ctx->err.clear();
+  DeviceGuard dg(ctx->device);
+  if (enable && !ctx->prof_ev) {
+    const int n = kProfRounds * (DTREE_NSTAGES + 1);
+    ctx->prof_ev = new (std::nothrow) hipEvent_t[n];
+    if (!ctx->prof_ev) return fail(ctx, DTREE_E_NOMEM, "event table");
+    for (int i = 0; i < n; ++i) {
+      if (hipEventCreate(&ctx->prof_ev[i]) != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(ctx->prof_ev[j]);
+        delete[] ctx->prof_ev;
+        ctx->prof_ev = nullptr;
+        return fail(ctx, DTREE_E_HIP, "hipEventCreate failed");
+      }
+    }
+  }
+  ctx->prof = enable != 0;
+  ctx->prof_n = 0;
+  return DTREE_OK;
+}
+
+extern "C" dtree_status dtree_profile_read(dtree_ctx *ctx, float *ms, int32_t *rounds) {
+  if (!ctx) return DTREE_E_ARG;
+  ctx->err.clear();
+  if (!ms || !rounds) return fail(ctx, DTREE_E_ARG, "null output");
+  for (int k = 0; k < DTREE_NSTAGES; ++k) ms[k] = 0.f;
+  *rounds = 0;
+  if (!ctx->prof_ev) return DTREE_OK;
+  DeviceGuard dg(ctx->device);
+  for (int rr = 0; rr < ctx->prof_n; ++rr) {
+    hipEvent_t *e = ctx->prof_ev + rr * (DTREE_NSTAGES + 1);
+    HIPCHK(ctx, hipEventSynchronize(e[DTREE_NSTAGES]));
+    for (int k = 0; k < DTREE_NSTAGES; ++k) {
+      float t = 0.f;
+      HIPCHK(ctx, hipEventElapsedTime(&t, e[k], e[k + 1]));
+      ms[k] += t;
+    }
+  }
+  *rounds = ctx->prof_n;
+  ctx->prof_n = 0;
+  return DTREE_OK;
+}
+
+extern "C" const char *dtree_last_error(const dtree_ctx *ctx) {
+  return ctx ? ctx->err.c_str() : g_create_err.c_str();
+}
+
+extern "C" dtree_status dtree_destroy(dtree_ctx *ctx) {
+  if (!ctx) return DTREE_OK;
+  {
+    DeviceGuard dg(ctx->device);
+    free_ws(ctx->ws);
+    if (ctx->prof_ev) {
+      for (int i = 0; i < kProfRounds * (DTREE_NSTAGES + 1); ++i) (void)hipEventDestroy(ctx->prof_ev[i]);
+      delete[] ctx->prof_ev;
+    }
+  }
+  delete ctx;
+  return DTREE_OK;
+}

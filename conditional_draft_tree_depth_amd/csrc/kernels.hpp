@@ -1,0 +1,80 @@
+// Host-side launchers of the draft-tree kernels (one translation unit each).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dtree {
+
+enum { WT_F32 = 0, WT_BF16 = 1 };
+
+// ---- K1: base logits Hq . W_lm^T + bias with a fused per-workgroup Top-M.
+// Writes part[row][p][0..M) = the M best keys of vocabulary slice p for that
+// row, best first (0 = empty).  P slices per row.
+struct LMHeadArgs {
+  const float *H;      // [rows, d] fp32
+  int rows, d;
+  const void *W;       // [V, d]
+  int wtype, V;
+  const float *bias;   // [V] or null
+  int M, P;
+  uint64_t *part;      // [rows, P, M]
+};
+int lmhead_partitions(int V, int wtype);
+size_t lmhead_smem(int d, int wtype);
+hipError_t lmhead_prepare(int wtype, size_t smem);
+hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st);
+// ---- K1b: merge the P partial lists of each row into C (tokens), Cl (logits)
+hipError_t launch_topm_merge(const uint64_t *part, int P, int M, int rows,
+                             int32_t *C, float *Cl, hipStream_t st);
+
+// ---- generic fp32-activation x weight^T product with gathers and epilogue
+// Y[i][n] = sum_k X[xrow(i)][k] * W[n][k] + bias[n] + addend[arow(i)][n]
+// xrow(i) = xidx ? xidx[i] : i ; arow(i) = (i / adiv) * amul + aoff
+struct GemmArgs {
+  int R, N, Kd;
+  const void *X; int xtype; int ldx; const int32_t *xidx; int xround;
+  const void *W; int wtype; int ldw;
+  const float *bias;
+  const float *addend; int lda, adiv, amul, aoff;
+  float *Y; int ldy;
+};
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
+// GRU gates: gi, gh = input/state projections incl. biases ([R, 3s]); if gh
+// is null the previous state is zero and the state part equals b_hh.
+hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh,
+                              const float *b_hh, const float *Sprev,
+                              const int32_t *pidx, float *Snew, hipStream_t st);
+
+// ---- per-depth kernels
+struct TreeBufs {
+  int NT;              // superarbol nodes per request (root included)
+  int Wmax;            // survivor slots per request
+  int32_t *n_tok, *n_par, *n_dep;   // [b, NT]
+  float *n_score;                   // [b, NT]
+  uint32_t *n_lex;                  // [b, NT] (parent lexrank << 18) | token
+  int32_t *surv_node, *surv_rank;   // [b, Wmax] current expanded nodes
+  int32_t *nsurv_node, *nsurv_rank; // [b, Wmax] next depth
+  int32_t *surv_hist;               // [b, D+1, Wmax]
+  int32_t *gidx_tok, *gidx_par;     // [b * Wmax] gathers for the GRU step
+  int32_t *sel;                     // [b, Bmax]
+  uint32_t *status;                 // device status bits
+};
+hipError_t launch_init_round(int b, const int32_t *root, const TreeBufs &t,
+                             int Dp1, hipStream_t st);
+hipError_t launch_corr_logits(int b, int A, int M, int r, int D, int delta,
+                              const void *W2, int wtype, const int32_t *C,
+                              const float *Cl, const float *u, float *ell,
+                              hipStream_t st);
+size_t corr_logits_smem(int A, int M, int r, int wtype);
+hipError_t launch_select(int b, int A, int M, int K, int W, int D, int delta,
+                         int off, const int32_t *C, const float *ell,
+                         const TreeBufs &t, hipStream_t st);
+hipError_t launch_topb_emit(int b, int NT, int B, float beta, int Bmax,
+                            const TreeBufs &t, int32_t *tok, int32_t *parent,
+                            int32_t *depth, float *score, uint8_t *mask,
+                            int32_t *n_nodes, hipStream_t st);
+size_t topb_smem(int NT, int B);
+hipError_t topb_prepare(size_t smem);
+hipError_t corr_logits_prepare(int wtype, size_t smem);
+
+}  // namespace dtree

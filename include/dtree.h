@@ -1,0 +1,188 @@
+/*
+ * dtree.h -- C ABI of libdtree.so: one round of conditional draft-tree
+ * construction on an AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by title and section):
+ *   * "Resumen Técnico: Domino", Methodology 1 and 2: base logits
+ *     L_base = H . W_lm (+ bias) from the shared hidden states H of the draft
+ *     block; a GRU folds the embeddings of the preceding draft tokens into a
+ *     causal state S; a low-rank head maps [H_i ; S_{i-1}] to rank r (W1) and
+ *     back to vocabulary space (W2) giving Delta L_i; L = L_base + Delta L.
+ *   * "Resumen Técnico: DominoTree", Main components 1, 2 and 5: children are
+ *     scored by the path's own correction; the correction is restricted to
+ *     the Top-M marginal candidates of each depth (an r x M slice of W2)
+ *     before the Top-k children are kept; verification uses tree attention
+ *     with an ancestor-only mask.
+ *   * "DARTree: Speculative Diffusion Decoding with Autoregressive Draft
+ *     Trees", Methodology 1 and 2: the tree grows depth by depth; every
+ *     active branch of a depth is corrected in one batch with its own prefix
+ *     state; extensions are scored by corrected cumulative log-probability;
+ *     the W best branches are kept and their states carried forward; the
+ *     fixed-width superarbol so built is pruned by ONE global Top-B with a
+ *     non-positive depth bonus beta, which Lemma 1 shows selects the same
+ *     set as the sequential best-first max-heap.
+ *
+ * Conventions fixed by this library where the pages leave them open:
+ *   * log-probabilities are normalised over the M candidates of the depth;
+ *   * H row delta (0-based) scores the children at depth delta+1; the GRU
+ *     starts from a zero state and first consumes the root token (the last
+ *     verified token), so the depth-1 children use S = GRU(Emb[root], 0);
+ *   * GRU = the PyTorch GRUCell equations, gate blocks (r, z, n);
+ *   * the low-rank head is linear: u = W1 [Hq_delta ; S], Delta L = W2 u;
+ *   * every scored child enters the superarbol; only the top W per depth
+ *     are expanded; B counts selected nodes excluding the root;
+ *   * selection key = score + beta * depth (fp32), order: key descending,
+ *     then depth ascending, then token path lexicographically ascending;
+ *     Top-M and Top-K ties go to the smaller token id, Top-W ties to the
+ *     lexicographically smaller token path;
+ *   * bf16 weights: the only bf16 values are the stored weights and
+ *     Hq = bf16_rne(H); the GRU state, gate pre-activations, u, the
+ *     corrected logits, log-probs and scores are fp32.
+ *
+ * Memory: every pointer named "device" is device memory of the device the
+ * context was created on.  Weights are BORROWED (the caller keeps them alive
+ * and unchanged for the context's life); the context owns its workspace;
+ * outputs are caller-allocated.  All calls return a dtree_status; nothing
+ * throws across the ABI.  On error dtree_last_error() describes it.
+ */
+#ifndef DTREE_H
+#define DTREE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dtree_ctx dtree_ctx;
+
+typedef enum {
+  DTREE_OK = 0,
+  DTREE_E_ARG = 1,     /* bad argument value (K > M, beta > 0, NULL, ...)   */
+  DTREE_E_SHAPE = 2,   /* a size the kernels do not support                  */
+  DTREE_E_DTYPE = 3,   /* unknown weight type                                */
+  DTREE_E_DEVICE = 4,  /* not a gfx950 device, or device query failed        */
+  DTREE_E_NOMEM = 5,   /* workspace allocation failed                        */
+  DTREE_E_HIP = 6,     /* a HIP runtime call or kernel launch failed         */
+  DTREE_E_STATE = 7    /* call out of order (e.g. trace before any round)    */
+} dtree_status;
+
+typedef enum { DTREE_F32 = 0, DTREE_BF16 = 1 } dtree_dtype;
+
+/* Shared drafter weights, PyTorch module layouts, row-major, device memory.
+ * Matrices are stored as `wtype` (bf16 = raw 16-bit patterns).  Biases are
+ * fp32 and may be NULL (read as zeros).                                      */
+typedef struct {
+  int32_t d;   /* hidden size of H                                          */
+  int32_t V;   /* vocabulary size, <= 262144                                 */
+  int32_t e;   /* embedding size fed to the GRU                              */
+  int32_t s;   /* GRU state size                                             */
+  int32_t r;   /* rank of the correction bottleneck                          */
+  int32_t wtype;                /* dtree_dtype                              */
+  const void *W_lm;             /* [V, d]   LM head (nn.Linear(d, V).weight) */
+  const float *lm_bias;         /* [V]      added to the base logits or NULL */
+  const void *Emb;              /* [V, e]   token embedding table            */
+  const void *W_ih;             /* [3s, e]  GRUCell.weight_ih, blocks r,z,n  */
+  const void *W_hh;             /* [3s, s]  GRUCell.weight_hh                */
+  const float *b_ih, *b_hh;     /* [3s]     GRUCell biases or NULL           */
+  const void *W1;               /* [r, d+s] columns [0,d) act on H, [d,d+s) on S */
+  const void *W2;               /* [V, r]   row v maps u to token v's logit   */
+} dtree_weights;
+
+/* Upper bounds the workspace is sized for (dtree_create).                   */
+typedef struct {
+  int32_t max_batch;  /* requests per round                                  */
+  int32_t max_D;      /* depth, <= 31                                        */
+  int32_t max_M;      /* candidates per depth, <= 128                        */
+  int32_t max_K;      /* children per branch                                 */
+  int32_t max_W;      /* branches per depth, <= 512                          */
+  int32_t max_B;      /* node budget                                         */
+} dtree_caps;
+
+/* Per-round tree parameters.  Need 1 <= K <= M <= V, W >= 1, B >= 1,
+ * 1 <= D, each within the caps, and beta <= 0 (Lemma 1's precondition:
+ * beta > 0 returns DTREE_E_ARG).  The superarbol (root included) must hold
+ * at most 8192 nodes and A*K <= 1024 children per depth.                    */
+typedef struct {
+  int32_t D, M, K, W, B;
+  float beta;
+} dtree_params;
+
+/* Create a context on HIP device `device`: validates the weights and caps,
+ * checks the device is gfx950 and allocates the workspace (hipMalloc).
+ * bf16 weights need d % 128 == 0.  On success *out owns the workspace.      */
+dtree_status dtree_create(const dtree_weights *w, const dtree_caps *caps,
+                          int device, dtree_ctx **out);
+
+/* Enqueue one round on `stream` (a hipStream_t; NULL = default stream).
+ * Asynchronous: returns after enqueueing; nothing is synchronised inside.
+ * Argument errors are found before anything is enqueued.
+ *   H       device, [batch, D, d] fp32 hidden states (row delta scores
+ *           depth delta+1)
+ *   root    device, [batch] int32, last verified token of each request
+ * Outputs, device, caller-owned, N = B + 1 slots per request:
+ *   tok     [batch, N] int32  token of each node (row 0 = root)
+ *   parent  [batch, N] int32  index of the parent node, -1 for the root
+ *   depth   [batch, N] int32  depth, root 0
+ *   score   [batch, N] fp32   cumulative log-prob (beta not included)
+ *   mask    [batch, N, N] u8  mask[i][j] = 1 iff node j is node i or an
+ *                             ancestor of it (query row, key column)
+ *   n_nodes [batch] int32     min(B, superarbol size) + 1
+ * Nodes are in canonical order: root, then depth ascending, then token path
+ * lexicographically ascending, so parent[i] < i.  Slots past n_nodes hold
+ * tok/parent/depth = -1, score = -inf and zero mask rows and columns.
+ * H and root must stay valid until the stream work completes.  A context is
+ * not reentrant: calls on one context must not overlap.                     */
+dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
+                               int32_t batch, const float *H,
+                               const int32_t *root, int32_t *tok,
+                               int32_t *parent, int32_t *depth, float *score,
+                               uint8_t *mask, int32_t *n_nodes, void *stream);
+
+/* Number of superarbol nodes (root included) a round with `p` builds per
+ * request, or -1 if p is invalid.  Pure host arithmetic.                     */
+int32_t dtree_superarbol_nodes(const dtree_params *p);
+
+/* Debug copy of request `req`'s intermediates of the LAST round, host memory,
+ * caller-allocated with the sizes noted (for that round's params).  Any
+ * pointer may be NULL to skip that part.  Synchronises the device.          */
+typedef struct {
+  int32_t *C;          /* [D*M]  candidate tokens per depth, value desc     */
+  float *Cl;           /* [D*M]  their base logits                           */
+  int32_t *node_tok;   /* [n_sa] superarbol, node 0 = root                   */
+  int32_t *node_parent;/* [n_sa] parent node id, -1 for the root            */
+  float *node_score;   /* [n_sa]                                             */
+  int32_t *surv;       /* [(D+1)*W] expanded node ids per depth, -1 padded   */
+  int32_t *sel;        /* [B]    selected node ids in selection order, -1 pad */
+  int32_t n_sa;        /* out: superarbol nodes incl. root                   */
+  int32_t status;      /* out: device status bits (0 = fine; bit 0: the
+                          selection was not closed under parents)           */
+} dtree_trace;
+dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace *out);
+
+/* Stage timing with HIP events recorded on the round's own stream.  When
+ * enabled, every round records events between its stages:
+ *   0 base-logit GEMM with fused Top-M   1 Top-M merge
+ *   2 path-independent prologue (uH, root GRU state)
+ *   3 depth loop (correction, selection, GRU, all depths)
+ *   4 global Top-B, canonical order and mask
+ * dtree_profile_read synchronises, writes the summed milliseconds of each
+ * stage over the rounds recorded since dtree_profile_enable(ctx, 1) to
+ * ms[0..DTREE_NSTAGES) and the round count to *rounds, and clears them.
+ * At most 4096 rounds are recorded; later rounds are not timed.            */
+#define DTREE_NSTAGES 5
+dtree_status dtree_profile_enable(dtree_ctx *ctx, int enable);
+dtree_status dtree_profile_read(dtree_ctx *ctx, float *ms, int32_t *rounds);
+
+/* Text of the last error on this context ("" if none); ctx may be NULL for
+ * errors of dtree_create.  Valid until the next call on the context.        */
+const char *dtree_last_error(const dtree_ctx *ctx);
+
+/* Free the workspace.  NULL-safe.  The caller must ensure no enqueued round
+ * still runs (synchronise the stream first).                                */
+dtree_status dtree_destroy(dtree_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DTREE_H */

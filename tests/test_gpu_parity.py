@@ -1,0 +1,77 @@
+"""GPU path vs the CPU oracle, through the C ABI (needs a gfx950 GPU).
+
+Structure must be identical and scores within 1e-4; near-ties are
+tolerated only as described in checker.py.
+"""
+import numpy as np
+import pytest
+
+import synth
+import fixtures_io
+from checker import check_invariants
+from gpu_util import check_config, gpu_round, caps_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", fixtures_io.fixture_names())
+def test_golden_fixture_on_gpu(gpu_lib, name):
+    g, x, exp = fixtures_io.load(name)
+    p = g["params"]
+    cfg = synth.custom_config(d=4, V=4, e=1, s=1, r=1, batch=1, wtype="f32", **p)
+    out, tr = gpu_round(x, cfg)
+    out = out[0]
+    n = exp["n_nodes"]
+    assert out["n_nodes"] == n
+    assert out["tok"][:n].tolist() == exp["tok"]
+    assert out["parent"][:n].tolist() == exp["parent"]
+    assert out["depth"][:n].tolist() == exp["depth"]
+    assert np.max(np.abs(out["score"][:n] - np.array(exp["score"]))) < g["score_tol"]
+    assert out["mask"][:n, :n].tolist() == exp["mask"]
+    check_invariants(out, p["B"])
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_tiny_seeds_exact(gpu_lib, seed):
+    cfg = synth.CONFIGS["tiny"]
+    check_config(synth.make_inputs(cfg, seed), cfg, f"tiny seed {seed}", max_tie_frac=0.0)
+
+
+def _small_cfg(seed):
+    rng = np.random.default_rng(100 + seed)
+    wtype = "bf16" if seed % 2 else "f32"
+    M = int(rng.choice([4, 16, 33, 64, 128]))
+    K = int(rng.integers(1, min(M, 8) + 1))
+    W = int(rng.choice([1, 3, 8, 17, 64]))
+    while W * K > 1024:
+        W //= 2
+    d = 128 * int(rng.integers(1, 3)) if wtype == "bf16" else int(rng.integers(8, 100))
+    V = int(rng.integers(max(M, 40), 3000))
+    return synth.custom_config(cfg_id=5000 + seed, d=d, V=V, e=int(rng.integers(4, 80)),
+                               s=int(rng.integers(4, 70)), r=int(rng.integers(2, 64)),
+                               D=int(rng.integers(1, 9)), M=M, K=K, W=W,
+                               B=int(rng.integers(1, 300)),
+                               beta=float(rng.choice([0.0, -0.01, -0.3])),
+                               batch=int(rng.integers(1, 5)), wtype=wtype)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_small_shapes(gpu_lib, seed):
+    cfg = _small_cfg(seed)
+    check_config(synth.make_inputs(cfg, seed), cfg, f"small {seed}", max_tie_frac=0.25)
+
+
+def test_caps_larger_than_round(gpu_lib):
+    cfg = synth.CONFIGS["tiny"].with_(batch=2)
+    check_config(synth.make_inputs(cfg, 7), cfg, "tiny caps>params",
+                 caps=caps_for(cfg, max_batch=5, max_D=9, max_M=32, max_K=4, max_W=16, max_B=40))
+
+
+def test_determinism(gpu_lib):
+    cfg = synth.custom_config(cfg_id=6000, d=256, V=5000, e=64, s=64, r=32, D=6, M=32, K=4,
+                              W=8, B=40, beta=-0.05, batch=3, wtype="bf16")
+    outs, _ = gpu_round(synth.make_inputs(cfg, 1), cfg, runs=3)
+    for o in outs[1:]:
+        for q in range(cfg.batch):
+            for k in ("tok", "parent", "depth", "score", "mask"):
+                assert np.array_equal(o[q][k], outs[0][q][k])
