@@ -62,6 +62,9 @@ def load(path=LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    # torch brings its own HIP runtime; loading it first makes the library bind
+    # to that same runtime instance, so torch's device pointers are valid here
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     lib.dtree_create.argtypes = [P(dtree_weights), P(dtree_caps), ctypes.c_int,

@@ -32,6 +32,9 @@ struct Ws {
   int32_t *surv[2] = {nullptr, nullptr}, *rank[2] = {nullptr, nullptr};
   int32_t *surv_hist = nullptr, *gidx_tok = nullptr, *gidx_par = nullptr, *sel = nullptr;
   uint32_t *status = nullptr;
+  // persistent depth loop: correction tables, partial sums, arrival flags
+  float *G = nullptr, *g = nullptr, *pk_part = nullptr, *gitab = nullptr;
+  uint32_t *flags = nullptr;
 };
 
 int superarbol_nodes(int D, int K, int W) {
@@ -56,6 +59,11 @@ struct dtree_ctx {
   bool has_round = false;
   dtree_params last{};
   int last_batch = 0, last_NT = 0;
+  // persistent depth loop: available for this context, and the arrival
+  // epoch of the next round (flags only ever grow, so they need no reset)
+  bool pk = false;
+  int pk_rows = 0;
+  uint32_t epoch = 0;
   // stage timing: kProfRounds rounds x (DTREE_NSTAGES + 1) events
   bool prof = false;
   int prof_n = 0;
@@ -98,7 +106,7 @@ void free_ws(Ws &ws) {
   void *ptrs[] = {ws.part, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.u, ws.ell, ws.gi, ws.gh,
                   ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
-                  ws.status};
+                  ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.flags};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   ws = Ws();
@@ -160,7 +168,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   ctx->caps = c;
   ctx->NTcap = NTcap;
   ctx->lds_max = prop.sharedMemPerBlock;
-  ctx->P = lmhead_partitions(w->V, w->wtype);
+  ctx->P = lmhead_partitions(w->V, w->wtype, (w->r + 15) / 16);
   ctx->k1_smem = lmhead_smem(w->d, w->wtype);
   const size_t cl_smem = corr_logits_smem(c.max_W, c.max_M, w->r, w->wtype);
   const size_t tb_smem = topb_smem(NTcap, c.max_B);
@@ -201,6 +209,20 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   A(alloc(&ws.gidx_par, bw));
   A(alloc(&ws.sel, (size_t)c.max_batch * c.max_B));
   A(alloc(&ws.status, 1));
+  // the persistent depth loop needs bf16 weights and MFMA-friendly GRU sizes
+  ctx->pk = w->wtype == DTREE_BF16 && s % 128 == 0 && w->e % 128 == 0 &&
+            persist_eligible(1, c.max_D, 1, 1, 1, s, w->e, r, WT_BF16, ctx->lds_max);
+  if (ctx->pk) {
+    const int cand = c.max_batch * c.max_M < 64 ? c.max_batch * c.max_M : 64;
+    ctx->pk_rows = cand * c.max_D;
+    A(alloc(&ws.G, (size_t)ctx->pk_rows * s));
+    A(alloc(&ws.g, (size_t)ctx->pk_rows));
+    A(alloc(&ws.pk_part, persist_part_floats(s)));
+    A(alloc(&ws.gitab, persist_gitab_floats(s, c.max_D)));
+    A(alloc(&ws.flags, persist_flag_words(s)));
+    if (e == hipSuccess) A(hipMemset(ws.flags, 0, persist_flag_words(s) * 4));
+    if (e == hipSuccess) A(hipDeviceSynchronize());
+  }
   if (e != hipSuccess) {
     free_ws(ws);
     return reject(DTREE_E_NOMEM, std::string("workspace: ") + hipGetErrorString(e));
@@ -208,6 +230,9 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   hipError_t pe = lmhead_prepare(w->wtype, ctx->k1_smem);
   if (pe == hipSuccess) pe = corr_logits_prepare(w->wtype, cl_smem);
   if (pe == hipSuccess) pe = topb_prepare(tb_smem);
+  if (pe == hipSuccess) pe = skinny_prepare(ctx->lds_max);
+  if (pe == hipSuccess && ctx->pk) pe = persist_prepare(s);
+  gemm_set_lds_max(ctx->lds_max);
   if (pe != hipSuccess) {
     free_ws(ws);
     return reject(DTREE_E_HIP, std::string("kernel attributes: ") + hipGetErrorString(pe));
@@ -248,19 +273,26 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
 
   // K1 + K1b: candidate tables
   prof_mark(ctx, 0, st);
-  LMHeadArgs la{H, rows, d, w.W_lm, wt, w.V, w.lm_bias, M, ctx->P, ws.part};
+  // bf16: the LM-head kernel also produces uH = W1[:, :d] . Hq (same operand)
+  const bool fuse_uH = wt == WT_BF16 && (d + s) % 8 == 0 &&
+                       reinterpret_cast<uintptr_t>(w.W1) % 16 == 0;
+  LMHeadArgs la{H, rows, d, w.W_lm, wt, w.V, w.lm_bias, M, ctx->P, ws.part,
+                fuse_uH ? w.W1 : nullptr, d + s, r, ws.uH};
   HIPCHK(ctx, launch_lmhead(la, st));
   prof_mark(ctx, 1, st);
   HIPCHK(ctx, launch_topm_merge(ws.part, ctx->P, M, rows, ws.C, ws.Cl, st));
   prof_mark(ctx, 2, st);
-  // K2: uH = W1[:, :d] . Hq for every (request, depth)
+  // K2: uH = W1[:, :d] . Hq for every (request, depth), when not fused above
   GemmArgs g{};
-  g = GemmArgs{rows, r, d, H, WT_F32, d, nullptr, wt == WT_BF16 ? 1 : 0, w.W1, wt, d + s,
-               nullptr, nullptr, 0, 1, 0, 0, ws.uH, r};
-  HIPCHK(ctx, launch_gemm(g, st));
+  if (!fuse_uH) {
+    g = GemmArgs{rows, r, d, H, WT_F32, d, nullptr, wt == WT_BF16 ? 1 : 0, w.W1, wt, d + s,
+                 nullptr, nullptr, 0, 1, 0, 0, ws.uH, r};
+    HIPCHK(ctx, launch_gemm(g, st));
+  }
 
   TreeBufs tb{};
   tb.NT = ctx->NTcap;
+  tb.V = w.V;
   tb.Wmax = c.max_W;
   tb.n_tok = ws.n_tok; tb.n_par = ws.n_par; tb.n_dep = ws.n_dep;
   tb.n_score = ws.n_score; tb.n_lex = ws.n_lex;
@@ -270,39 +302,58 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   tb.surv_node = ws.surv[0]; tb.surv_rank = ws.rank[0];
   tb.nsurv_node = ws.surv[1]; tb.nsurv_rank = ws.rank[1];
   HIPCHK(ctx, launch_init_round(batch, root, tb, D + 1, st));
-  // root state: the GRU consumes the last verified token from a zero state
-  g = GemmArgs{batch, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
-               w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
-  HIPCHK(ctx, launch_gemm(g, st));
-  HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, w.b_hh, nullptr, nullptr, ws.S[0], st));
-  prof_mark(ctx, 3, st);
 
+  const bool pk = ctx->pk && batch * M <= 64 && batch * D * M <= ctx->pk_rows &&
+                  persist_eligible(batch, D, M, K, W, s, w.e, r, wt, ctx->lds_max);
   int A = 1, off = 1, sc = 0;
-  for (int dd = 0; dd < D; ++dd) {
-    // u = uH[req, dd] + W1[:, d:] . S  for every expanded branch
-    g = GemmArgs{batch * A, r, s, ws.S[sc], WT_F32, s, nullptr, 0,
-                 static_cast<const uint8_t *>(w.W1) + (size_t)d * esz, wt, d + s, nullptr,
-                 ws.uH, r, A, D, dd, ws.u, r};
-    HIPCHK(ctx, launch_gemm(g, st));
-    HIPCHK(ctx, launch_corr_logits(batch, A, M, r, D, dd, w.W2, wt, ws.C, ws.Cl, ws.u, ws.ell, st));
-    HIPCHK(ctx, launch_select(batch, A, M, K, W, D, dd, off, ws.C, ws.ell, tb, st));
-    const int An = A * K < W ? A * K : W;
-    if (dd + 1 < D) {
-      g = GemmArgs{batch * An, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
-                   w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
-      HIPCHK(ctx, launch_gemm(g, st));
-      g = GemmArgs{batch * An, 3 * s, s, ws.S[sc], WT_F32, s, ws.gidx_par, 0, w.W_hh, wt, s,
-                   w.b_hh, nullptr, 0, 1, 0, 0, ws.gh, 3 * s};
-      HIPCHK(ctx, launch_gemm(g, st));
-      HIPCHK(ctx, launch_gru_combine(batch * An, s, ws.gi, ws.gh, nullptr, ws.S[sc], ws.gidx_par,
-                                     ws.S[1 - sc], st));
-      sc = 1 - sc;
+  if (pk) {
+    // correction tables G = W2[C] W1[:, d:], g = Cl + W2[C] uH, then the
+    // whole depth loop as one cooperative launch
+    HIPCHK(ctx, launch_corr_tables(batch * D * M, M, D, r, s, d, d + s, w.W2, w.W1, ws.C, ws.Cl,
+                                   ws.uH, ws.G, ws.g, st));
+    prof_mark(ctx, 3, st);
+    PersistArgs pa{batch, D, M, K, W, s, w.e, w.V, w.W_ih, w.W_hh, w.Emb, w.b_ih, w.b_hh,
+                   ws.C, root, ws.G, ws.g, ws.S[0], ws.S[1], ws.pk_part, ws.gitab, ws.flags,
+                   ctx->epoch, tb};
+    HIPCHK(ctx, launch_depth_persistent(pa, st));
+    ctx->epoch += (uint32_t)D + 1u;
+    for (int dd = 0; dd < D; ++dd) {
+      off += A * K;
+      A = A * K < W ? A * K : W;
     }
-    cur = 1 - cur;
-    tb.surv_node = ws.surv[cur]; tb.surv_rank = ws.rank[cur];
-    tb.nsurv_node = ws.surv[1 - cur]; tb.nsurv_rank = ws.rank[1 - cur];
-    off += A * K;
-    A = An;
+  } else {
+    // root state: the GRU consumes the last verified token from a zero state
+    g = GemmArgs{batch, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
+                 w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
+    HIPCHK(ctx, launch_gemm(g, st));
+    HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, w.b_hh, nullptr, nullptr, ws.S[0], st));
+    prof_mark(ctx, 3, st);
+    for (int dd = 0; dd < D; ++dd) {
+      // u = uH[req, dd] + W1[:, d:] . S  for every expanded branch
+      g = GemmArgs{batch * A, r, s, ws.S[sc], WT_F32, s, nullptr, 0,
+                   static_cast<const uint8_t *>(w.W1) + (size_t)d * esz, wt, d + s, nullptr,
+                   ws.uH, r, A, D, dd, ws.u, r};
+      HIPCHK(ctx, launch_gemm(g, st));
+      HIPCHK(ctx, launch_corr_logits(batch, A, M, r, D, dd, w.W2, wt, ws.C, ws.Cl, ws.u, ws.ell, st));
+      HIPCHK(ctx, launch_select(batch, A, M, K, W, D, dd, off, ws.C, ws.ell, tb, st));
+      const int An = A * K < W ? A * K : W;
+      if (dd + 1 < D) {
+        g = GemmArgs{batch * An, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
+                     w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
+        HIPCHK(ctx, launch_gemm(g, st));
+        g = GemmArgs{batch * An, 3 * s, s, ws.S[sc], WT_F32, s, ws.gidx_par, 0, w.W_hh, wt, s,
+                     w.b_hh, nullptr, 0, 1, 0, 0, ws.gh, 3 * s};
+        HIPCHK(ctx, launch_gemm(g, st));
+        HIPCHK(ctx, launch_gru_combine(batch * An, s, ws.gi, ws.gh, nullptr, ws.S[sc], ws.gidx_par,
+                                       ws.S[1 - sc], st));
+        sc = 1 - sc;
+      }
+      cur = 1 - cur;
+      tb.surv_node = ws.surv[cur]; tb.surv_rank = ws.rank[cur];
+      tb.nsurv_node = ws.surv[1 - cur]; tb.nsurv_rank = ws.rank[1 - cur];
+      off += A * K;
+      A = An;
+    }
   }
   const int NT = off;
   prof_mark(ctx, 4, st);

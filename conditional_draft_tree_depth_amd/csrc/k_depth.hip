@@ -23,7 +23,8 @@ __global__ void k_init_round(int b, const int32_t *__restrict__ root, TreeBufs t
   __syncthreads();
   if (threadIdx.x == 0) {
     const size_t n0 = (size_t)q * t.NT;
-    t.n_tok[n0] = root[q];
+    const int32_t rt = root[q] < 0 ? 0 : (root[q] >= t.V ? t.V - 1 : root[q]);
+    t.n_tok[n0] = rt;
     t.n_par[n0] = -1;
     t.n_dep[n0] = 0;
     t.n_score[n0] = 0.f;
@@ -31,7 +32,7 @@ __global__ void k_init_round(int b, const int32_t *__restrict__ root, TreeBufs t
     t.surv_node[(size_t)q * t.Wmax] = 0;
     t.surv_rank[(size_t)q * t.Wmax] = 0;
     t.surv_hist[(size_t)q * Dp1 * t.Wmax] = 0;
-    t.gidx_tok[q] = root[q];
+    t.gidx_tok[q] = rt;
     if (q == 0) *t.status = 0u;
   }
 }

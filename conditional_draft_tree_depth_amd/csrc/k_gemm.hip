@@ -85,8 +85,136 @@ __global__ __launch_bounds__(256) void k_gemm_xwT(GemmArgs a) {
   }
 }
 
+// Skinny product on MFMA: at most 16 activation rows per workgroup (rows of
+// the B operand, staged in LDS as bf16), bf16 weight rows streamed from
+// memory as the A operand, 16 weight rows per wave, fp32 accumulation.
+// fp32 activations that must not be rounded (the GRU state) are split
+// exactly into three bf16 terms x = hi + mid + lo (each term is the bf16
+// rounding of what the previous ones left, so the remainder is below
+// 2^-24 |x|); every term is multiplied by the same weight fragment.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+constexpr int SK_WAVES = 4;
+
+__device__ __forceinline__ bf16x8 sk_bf(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int TERMS, typename XT>
+__global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int KS = a.Kd + 8;
+  uint16_t *Xs = reinterpret_cast<uint16_t *>(smem);   // [TERMS][16][KS]
+  const XT *X = static_cast<const XT *>(a.X);
+  const int r0 = blockIdx.x * 16;
+  const int nr = min(16, a.R - r0);
+  for (int i = threadIdx.x; i < 16 * a.Kd; i += blockDim.x) {
+    const int rr = i / a.Kd, k = i - rr * a.Kd;
+    uint16_t t0 = 0, t1 = 0, t2 = 0;
+    if (rr < nr) {
+      const size_t xi = (size_t)(a.xidx ? a.xidx[r0 + rr] : r0 + rr) * a.ldx + k;
+      if constexpr (sizeof(XT) == 2) {
+        t0 = X[xi];
+      } else {
+        const float x = X[xi];
+        t0 = f32_to_bf16_rne(x);
+        if constexpr (TERMS == 3) {
+          const float r1 = x - bf16_bits_to_f32(t0);
+          t1 = f32_to_bf16_rne(r1);
+          t2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(t1));
+        }
+      }
+    }
+    Xs[rr * KS + k] = t0;
+    if constexpr (TERMS == 3) {
+      Xs[(16 + rr) * KS + k] = t1;
+      Xs[(32 + rr) * KS + k] = t2;
+    }
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, g = lane >> 4;
+  const int tile = blockIdx.y * SK_WAVES + wave;
+  if (tile * 16 >= a.N) return;
+  const int n = min(tile * 16 + lr, a.N - 1);
+  const uint16_t *Wt = static_cast<const uint16_t *>(a.W);
+  const uint4 *pw = reinterpret_cast<const uint4 *>(Wt + (size_t)n * a.ldw + g * 32);
+  const uint16_t *hp = Xs + lr * KS + g * 32;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  uint4 cw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cw[j] = pw[j];
+  for (int kc = 0; kc < a.Kd; kc += 128) {
+    uint4 nw[4];
+    if (kc + 128 < a.Kd) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nw[j] = pw[(kc + 128) / 8 + j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int t = 0; t < TERMS; ++t) {
+        const uint4 xv = *reinterpret_cast<const uint4 *>(hp + t * 16 * KS + kc + 8 * j);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sk_bf(cw[j]), sk_bf(xv), acc, 0, 0, 0);
+      }
+    }
+    if (kc + 128 < a.Kd) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cw[j] = nw[j];
+    }
+  }
+  if (lr >= nr) return;
+  const int row = r0 + lr;
+  const float *add = a.addend ? a.addend + (size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda : nullptr;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int nn = tile * 16 + 4 * g + t;
+    if (nn >= a.N) continue;
+    float v = acc[t];
+    if (a.bias) v += a.bias[nn];
+    if (add) v += add[nn];
+    a.Y[(size_t)row * a.ldy + nn] = v;
+  }
+}
+
+static int skinny_terms(const GemmArgs &a) {
+  return (a.xtype == WT_F32 && !a.xround) ? 3 : 1;
+}
+
+size_t skinny_smem(int Kd, int terms) { return (size_t)terms * 16 * (Kd + 8) * 2; }
+
+bool skinny_ok(const GemmArgs &a, size_t lds_max) {
+  return a.wtype == WT_BF16 && a.Kd % 128 == 0 && a.ldw % 8 == 0 &&
+         reinterpret_cast<uintptr_t>(a.W) % 16 == 0 && a.R <= 64 &&
+         skinny_smem(a.Kd, skinny_terms(a)) <= lds_max;
+}
+
+hipError_t skinny_prepare(size_t lds_max) {
+  const void *fns[] = {reinterpret_cast<const void *>(&k_skinny_bf16<1, uint16_t>),
+                       reinterpret_cast<const void *>(&k_skinny_bf16<1, float>),
+                       reinterpret_cast<const void *>(&k_skinny_bf16<3, float>)};
+  for (const void *f : fns) {
+    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+static size_t g_lds_max = 65536;
+void gemm_set_lds_max(size_t b) { g_lds_max = b; }
+
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.R <= 0 || a.N <= 0) return hipSuccess;
+  if (skinny_ok(a, g_lds_max)) {
+    const int terms = skinny_terms(a);
+    dim3 grid((a.R + 15) / 16, ((a.N + 15) / 16 + SK_WAVES - 1) / SK_WAVES);
+    const size_t sm = skinny_smem(a.Kd, terms);
+    if (a.xtype == WT_BF16)
+      hipLaunchKernelGGL((k_skinny_bf16<1, uint16_t>), grid, dim3(SK_WAVES * 64), sm, st, a);
+    else if (terms == 1)
+      hipLaunchKernelGGL((k_skinny_bf16<1, float>), grid, dim3(SK_WAVES * 64), sm, st, a);
+    else
+      hipLaunchKernelGGL((k_skinny_bf16<3, float>), grid, dim3(SK_WAVES * 64), sm, st, a);
+    return hipGetLastError();
+  }
   dim3 grid((a.N + GT - 1) / GT, (a.R + GT - 1) / GT);
   if (a.xtype == WT_F32 && a.wtype == WT_F32)
     hipLaunchKernelGGL((k_gemm_xwT<float, float>), grid, dim3(256), 0, st, a);

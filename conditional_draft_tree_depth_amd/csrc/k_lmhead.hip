@@ -28,6 +28,12 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int K1_WAVES = 8;                 // waves per workgroup (bf16 path)
 constexpr int K1_TPW = 8;                   // max 16-token tiles per wave
 constexpr int K1_MAXCOLS = K1_WAVES * K1_TPW * 16;  // 1024 tokens per WG
+#ifndef K1_TPI
+#define K1_TPI 1      // tiles in flight per wave
+#endif
+#ifndef K1_PF
+#define K1_PF 4       // k chunks prefetched per tile
+#endif
 constexpr int K1F_THREADS = 256;            // fp32 path
 constexpr int K1F_MAXCOLS = 256;
 
@@ -72,9 +78,16 @@ __device__ void wg_topm_epilogue(const float *Ls, int lstride, int ncols, int co
   }
 }
 
+// Tiles [0, ntV) are 16-token slabs of W_lm; when W1 is given, tiles
+// [ntV, ntV + ntU) are 16-row slabs of W1[:, :d] and produce the
+// path-independent projection uH = W1[:, :d] Hq for the same rows (the same
+// B operand), written straight to uH.  A wave keeps TPI tiles in flight and
+// PF 128-wide k chunks of each prefetched in registers.
+template <int TPI, int PF>
 __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
     const float *__restrict__ H, int rows, int d, const uint16_t *__restrict__ W, int V,
-    const float *__restrict__ bias, int M, uint64_t *__restrict__ part) {
+    const float *__restrict__ bias, int M, uint64_t *__restrict__ part,
+    const uint16_t *__restrict__ W1, int ldw1, int r, float *__restrict__ uH) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int P = gridDim.y, y = blockIdx.y;
   const int row0 = blockIdx.x * 16;
@@ -83,56 +96,84 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
   uint16_t *Hs = reinterpret_cast<uint16_t *>(smem);
 
   // Hq = bf16_rne(H) for the 16 rows of this block (zeros past `rows`)
-  for (int i = threadIdx.x; i < 16 * d; i += blockDim.x) {
-    const int rr = i / d, k = i - rr * d;
-    const float v = rr < nrow ? H[(size_t)(row0 + rr) * d + k] : 0.f;
-    Hs[rr * HS + k] = f32_to_bf16_rne(v);
+  {
+    const int q4 = d >> 2;   // float4 per row
+#pragma unroll 4
+    for (int i = threadIdx.x; i < 16 * q4; i += blockDim.x) {
+      const int rr = i / q4, k = (i - rr * q4) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (rr < nrow) v = *reinterpret_cast<const float4 *>(H + (size_t)(row0 + rr) * d + k);
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+      *reinterpret_cast<uint2 *>(Hs + rr * HS + k) = make_uint2(lo, hi);
+    }
   }
   __syncthreads();
 
-  const int ntiles = (V + 15) >> 4;
-  const int t0 = (int)((long long)ntiles * y / P);
-  const int t1 = (int)((long long)ntiles * (y + 1) / P);
+  const int ntV = (V + 15) >> 4;
+  const int ntU = W1 ? (r + 15) >> 4 : 0;
+  const int T = ntV + ntU;
+  const int t0 = (int)((long long)T * y / P);
+  const int t1 = (int)((long long)T * (y + 1) / P);
   const int nt = t1 - t0;
+  const int nch = d >> 7;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, g = lane >> 4;
   const uint16_t *hp = Hs + lr * HS + g * 32;
 
   float vals[K1_TPW][4];
 #pragma unroll
-  for (int i = 0; i < K1_TPW; i += 2) {
-    const int ltA = wave + K1_WAVES * i;
-    const int ltB = ltA + K1_WAVES;
-    if (ltA < nt) {
-      const int ltB2 = ltB < nt ? ltB : ltA;
-      const int vA = min((t0 + ltA) * 16 + lr, V - 1);
-      const int vB = min((t0 + ltB2) * 16 + lr, V - 1);
-      const uint4 *pa = reinterpret_cast<const uint4 *>(W + (size_t)vA * d + g * 32);
-      const uint4 *pb = reinterpret_cast<const uint4 *>(W + (size_t)vB * d + g * 32);
-      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
-      uint4 ca[4], cb[4];
+  for (int i = 0; i < K1_TPW; i += TPI) {
+    const int lt0 = wave + K1_WAVES * i;
+    if (lt0 < nt) {
+      const uint4 *ptr[TPI];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { ca[j] = pa[j]; cb[j] = pb[j]; }
-      for (int kc = 0; kc < d; kc += 128) {
-        uint4 na[4], nb[4];
-        if (kc + 128 < d) {
+      for (int u = 0; u < TPI; ++u) {
+        const int lt = lt0 + K1_WAVES * u < nt ? lt0 + K1_WAVES * u : lt0;
+        const int tt = t0 + lt;
+        const uint16_t *rp = tt < ntV ? W + (size_t)min(tt * 16 + lr, V - 1) * d
+                                      : W1 + (size_t)min((tt - ntV) * 16 + lr, r - 1) * ldw1;
+        ptr[u] = reinterpret_cast<const uint4 *>(rp + g * 32);
+      }
+      f32x4 acc[TPI];
+      uint4 ring[PF][TPI][4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) { na[j] = pa[(kc + 128) / 8 + j]; nb[j] = pb[(kc + 128) / 8 + j]; }
+      for (int u = 0; u < TPI; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pp = 0; pp < PF; ++pp)
+        if (pp < nch) {
+#pragma unroll
+          for (int u = 0; u < TPI; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ring[pp][u][j] = ptr[u][pp * 16 + j];
         }
-        const uint4 *h4 = reinterpret_cast<const uint4 *>(hp + kc);
+      for (int c0 = 0; c0 < nch; c0 += PF) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8 hb = as_bf16x8(h4[j]);
-          accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca[j]), hb, accA, 0, 0, 0);
-          accB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cb[j]), hb, accB, 0, 0, 0);
-        }
-        if (kc + 128 < d) {
+        for (int pp = 0; pp < PF; ++pp) {
+          const int c = c0 + pp;
+          if (c < nch) {
+            const uint4 *h4 = reinterpret_cast<const uint4 *>(hp + c * 128);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) { ca[j] = na[j]; cb[j] = nb[j]; }
+            for (int j = 0; j < 4; ++j) {
+              const bf16x8 hb = as_bf16x8(h4[j]);
+#pragma unroll
+              for (int u = 0; u < TPI; ++u)
+                acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[pp][u][j]), hb,
+                                                                 acc[u], 0, 0, 0);
+            }
+            if (c + PF < nch) {
+#pragma unroll
+              for (int u = 0; u < TPI; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ring[pp][u][j] = ptr[u][(c + PF) * 16 + j];
+            }
+          }
         }
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) { vals[i][t] = accA[t]; vals[i + 1][t] = accB[t]; }
+      for (int u = 0; u < TPI; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vals[i + u][t] = acc[u][t];
     }
   }
   __syncthreads();  // every wave is done with Hs: re-use it for the logits
@@ -144,17 +185,24 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
     for (int i = 0; i < K1_TPW; ++i) {
       const int lt = wave + K1_WAVES * i;
       if (lt < nt) {
+        const int tt = t0 + lt;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int c = lt * 16 + 4 * g + t;
-          const int v = t0 * 16 + c;
-          if (v < V) Ls[lr * LSTR + c] = vals[i][t] + (bias ? bias[v] : 0.f);
+          if (tt < ntV) {
+            const int c = lt * 16 + 4 * g + t;
+            const int v = t0 * 16 + c;
+            if (v < V) Ls[lr * LSTR + c] = vals[i][t] + (bias ? bias[v] : 0.f);
+          } else {
+            const int uc = (tt - ntV) * 16 + 4 * g + t;
+            if (uc < r) uH[(size_t)(row0 + lr) * r + uc] = vals[i][t];
+          }
         }
       }
     }
   }
   __syncthreads();
-  const int ncols = min(nt * 16, V - t0 * 16);
+  const int vend = min(min(t1, ntV) * 16, V);
+  const int ncols = vend > t0 * 16 ? vend - t0 * 16 : 0;
   wg_topm_epilogue<K1_MAXCOLS>(Ls, LSTR, ncols, t0 * 16, nrow, M,
                                part + ((size_t)row0 * P + y) * M, (size_t)P * M);
 }
@@ -186,82 +234,71 @@ __global__ __launch_bounds__(K1F_THREADS) void k1_lmhead_f32(
                                 part + ((size_t)row0 * P + y) * M, (size_t)P * M);
 }
 
-// K1b: one workgroup per row merges that row's P partial lists.  A lower
-// bound on the row's M-th best key is the largest M-th key of any partial
-// list; only keys at or above it can be in the result.
-constexpr int K1B_THREADS = 256;
-constexpr int K1B_CAP = 2048;
+// K1b: one workgroup per row merges that row's P partial lists (each sorted
+// best-first, padded with empty keys to Mp = next_pow2(M)) by a bitonic
+// tournament: for two descending lists A and B, max(A[k], B[Mp-1-k]) holds
+// the Mp best keys of A and B as a bitonic sequence, which a half-cleaner
+// cascade sorts back into descending order.  Lists are paired level by level
+// in LDS (no data movement: at level l the live lists sit at slots that are
+// multiples of 2^l); with more lists than fit, batches of G-1 lists are
+// reduced together with the running result in slot 0.
+constexpr int K1B_THREADS = 512;
+constexpr int K1B_CAP = 16384;   // keys in LDS (128 KiB)
 
 __global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
     const uint64_t *__restrict__ part, int P, int M, int32_t *__restrict__ C,
     float *__restrict__ Cl) {
-  __shared__ uint64_t cand[K1B_CAP];
-  __shared__ int32_t dummy[K1B_CAP];
-  __shared__ uint64_t red[K1B_THREADS / 64];
-  __shared__ int cnt;
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint64_t *L = reinterpret_cast<uint64_t *>(smem);
+  const int row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const uint64_t *pk = part + (size_t)row * P * M;
-  const int total = P * M;
-
-  uint64_t t = 0;
-  for (int p = tid; p < P; p += K1B_THREADS) {
-    const uint64_t k = pk[(size_t)p * M + M - 1];
-    t = k > t ? k : t;
-  }
-  t = group_max_u64<64>(t);
-  if (lane == 0) red[wave] = t;
-  if (tid == 0) cnt = 0;
-  __syncthreads();
-  t = red[0];
-  for (int w = 1; w < K1B_THREADS / 64; ++w) t = red[w] > t ? red[w] : t;
-  if (t == 0) t = 1;  // never admit empty slots
-  for (int i = tid; i < total; i += K1B_THREADS) {
-    const uint64_t k = pk[i];
-    if (k >= t) {
-      const int pos = atomicAdd(&cnt, 1);
-      if (pos < K1B_CAP) cand[pos] = k;
+  const int Mp = next_pow2(M);
+  const int lm = __builtin_ctz((unsigned)Mp);         // log2(Mp)
+  const int G = K1B_CAP >> lm;                         // lists per batch (power of two, >= 2)
+  for (int i = tid; i < Mp; i += nt) L[i] = 0ull;     // running result, slot 0
+  for (int p0 = 0; p0 < P; p0 += G - 1) {
+    const int nl = min(G - 1, P - p0);                 // fresh lists in this batch
+    const int nslots = next_pow2(nl + 1);
+    for (int i = Mp + tid; i < (nslots << lm); i += nt) {
+      const int sl = (i >> lm) - 1, k = i & (Mp - 1);
+      L[i] = (sl < nl && k < M) ? pk[(size_t)(p0 + sl) * M + k] : 0ull;
     }
-  }
-  __syncthreads();
-  const int n = cnt;
-  if (n <= K1B_CAP) {
-    const int np2 = next_pow2(n > M ? n : M);
-    for (int i = n + tid; i < np2; i += K1B_THREADS) cand[i] = 0;
     __syncthreads();
-    block_bitonic_desc(cand, dummy, np2);
-    for (int j = tid; j < M; j += K1B_THREADS) {
-      const uint64_t k = cand[j];
-      C[(size_t)row * M + j] = k ? (int32_t)key_tie(k) : -1;
-      Cl[(size_t)row * M + j] = key_val(k);
-    }
-  } else {
-    // Many keys above the bound: take the M best one at a time.
-    uint64_t prev = ~0ull;
-    for (int j = 0; j < M; ++j) {
-      uint64_t b = 0;
-      for (int i = tid; i < total; i += K1B_THREADS) {
-        const uint64_t k = pk[i];
-        b = (k < prev && k > b) ? k : b;
+    for (int ls = 0; (1 << ls) < nslots; ++ls) {
+      const int npairs = nslots >> (ls + 1);
+      const int pshift = ls + 1 + lm;                  // log2 of a pair's span in keys
+      // max against the reversed partner: bitonic, holds the best Mp
+      for (int i = tid; i < (npairs << lm); i += nt) {
+        const int pr = i >> lm, k = i & (Mp - 1);
+        uint64_t *A = L + ((size_t)pr << pshift);
+        const uint64_t *Bv = A + ((size_t)1 << (ls + lm));
+        const uint64_t a = A[k], b = Bv[Mp - 1 - k];
+        A[k] = a > b ? a : b;
       }
-      b = group_max_u64<64>(b);
       __syncthreads();
-      if (lane == 0) red[wave] = b;
-      __syncthreads();
-      b = red[0];
-      for (int w = 1; w < K1B_THREADS / 64; ++w) b = red[w] > b ? red[w] : b;
-      if (tid == 0) {
-        C[(size_t)row * M + j] = b ? (int32_t)key_tie(b) : -1;
-        Cl[(size_t)row * M + j] = key_val(b);
+      for (int lj = lm - 1; lj >= 0; --lj) {
+        const int j = 1 << lj;
+        for (int i = tid; i < (npairs << (lm - 1)); i += nt) {
+          const int pr = i >> (lm - 1), h = i & ((Mp >> 1) - 1);
+          uint64_t *A = L + ((size_t)pr << pshift);
+          const int lo = ((h >> lj) << (lj + 1)) | (h & (j - 1)), hi = lo + j;
+          const uint64_t a = A[lo], b = A[hi];
+          if (a < b) { A[lo] = b; A[hi] = a; }
+        }
+        __syncthreads();
       }
-      prev = b;
     }
+  }
+  for (int j = tid; j < M; j += nt) {
+    const uint64_t k = L[j];
+    C[(size_t)row * M + j] = k ? (int32_t)key_tie(k) : -1;
+    Cl[(size_t)row * M + j] = key_val(k);
   }
 }
 
 // ----------------------------------------------------------------- host side
-int lmhead_partitions(int V, int wtype) {
-  const int ntiles = (V + 15) / 16;
+int lmhead_partitions(int V, int wtype, int extra_tiles) {
+  const int ntiles = (V + 15) / 16 + (wtype == WT_BF16 ? extra_tiles : 0);
   const int per_wg = wtype == WT_BF16 ? K1_MAXCOLS / 16 : K1F_MAXCOLS / 16;
   int P = (ntiles + per_wg - 1) / per_wg;   // enough slices to fit the LDS
   if (P < 256) P = ntiles < 256 ? ntiles : 256;   // at least one per CU
@@ -276,17 +313,21 @@ size_t lmhead_smem(int d, int wtype) {
 }
 
 hipError_t lmhead_prepare(int wtype, size_t smem) {
-  if (wtype != WT_BF16) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k1_lmhead_bf16),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k1b_topm_merge),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)(K1B_CAP * sizeof(uint64_t)));
+  if (e != hipSuccess || wtype != WT_BF16) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k1_lmhead_bf16<K1_TPI, K1_PF>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
 }
 
 hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st) {
   dim3 grid((a.rows + 15) / 16, a.P);
   if (a.wtype == WT_BF16) {
-    hipLaunchKernelGGL(k1_lmhead_bf16, grid, dim3(K1_WAVES * 64), lmhead_smem(a.d, a.wtype), st,
-                       a.H, a.rows, a.d, static_cast<const uint16_t *>(a.W), a.V, a.bias, a.M,
-                       a.part);
+    hipLaunchKernelGGL((k1_lmhead_bf16<K1_TPI, K1_PF>), grid, dim3(K1_WAVES * 64),
+                       lmhead_smem(a.d, a.wtype), st, a.H, a.rows, a.d,
+                       static_cast<const uint16_t *>(a.W), a.V, a.bias, a.M, a.part,
+                       static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH);
   } else {
     hipLaunchKernelGGL(k1_lmhead_f32, grid, dim3(K1F_THREADS), 0, st, a.H, a.rows, a.d,
                        static_cast<const float *>(a.W), a.V, a.bias, a.M, a.part);
@@ -296,7 +337,8 @@ hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st) {
 
 hipError_t launch_topm_merge(const uint64_t *part, int P, int M, int rows, int32_t *C,
                              float *Cl, hipStream_t st) {
-  hipLaunchKernelGGL(k1b_topm_merge, dim3(rows), dim3(K1B_THREADS), 0, st, part, P, M, C, Cl);
+  const size_t sm = (size_t)K1B_CAP * sizeof(uint64_t);
+  hipLaunchKernelGGL(k1b_topm_merge, dim3(rows), dim3(K1B_THREADS), sm, st, part, P, M, C, Cl);
   return hipGetLastError();
 }
 

@@ -18,8 +18,11 @@ struct LMHeadArgs {
   const float *bias;   // [V] or null
   int M, P;
   uint64_t *part;      // [rows, P, M]
+  const void *W1;      // bf16 only: W1[:, :d] rows ride along -> uH (or null)
+  int ldw1, r;
+  float *uH;           // [rows, r]
 };
-int lmhead_partitions(int V, int wtype);
+int lmhead_partitions(int V, int wtype, int extra_tiles);
 size_t lmhead_smem(int d, int wtype);
 hipError_t lmhead_prepare(int wtype, size_t smem);
 hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st);
@@ -39,6 +42,8 @@ struct GemmArgs {
   float *Y; int ldy;
 };
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
+hipError_t skinny_prepare(size_t lds_max);
+void gemm_set_lds_max(size_t bytes);
 // GRU gates: gi, gh = input/state projections incl. biases ([R, 3s]); if gh
 // is null the previous state is zero and the state part equals b_hh.
 hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh,
@@ -48,6 +53,7 @@ hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh,
 // ---- per-depth kernels
 struct TreeBufs {
   int NT;              // superarbol nodes per request (root included)
+  int V;               // vocabulary size (root tokens are clamped into [0, V))
   int Wmax;            // survivor slots per request
   int32_t *n_tok, *n_par, *n_dep;   // [b, NT]
   float *n_score;                   // [b, NT]
@@ -75,6 +81,29 @@ hipError_t launch_topb_emit(int b, int NT, int B, float beta, int Bmax,
                             int32_t *n_nodes, hipStream_t st);
 size_t topb_smem(int NT, int B);
 hipError_t topb_prepare(size_t smem);
+
+// ---- persistent depth loop (small batches) and its correction tables
+struct PersistArgs {
+  int b, D, M, K, W, s, e, V;
+  const void *W_ih, *W_hh, *Emb;
+  const float *b_ih, *b_hh;
+  const int32_t *C, *root;
+  const float *G, *g;
+  float *S0, *S1, *part, *gitab;
+  uint32_t *flags;
+  uint32_t epoch0;
+  TreeBufs t;
+};
+bool persist_eligible(int b, int D, int M, int K, int W, int s, int e, int r, int wtype,
+                      size_t lds_max);
+size_t persist_flag_words(int s);
+size_t persist_part_floats(int s);
+size_t persist_gitab_floats(int s, int D);
+hipError_t persist_prepare(int s);
+hipError_t launch_corr_tables(int rows, int M, int D, int r, int s, int d, int ldw1,
+                              const void *W2, const void *W1, const int32_t *C, const float *Cl,
+                              const float *uH, float *G, float *g, hipStream_t st);
+hipError_t launch_depth_persistent(const PersistArgs &a, hipStream_t st);
 hipError_t corr_logits_prepare(int wtype, size_t smem);
 
 }  // namespace dtree

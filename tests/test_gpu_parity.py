@@ -61,6 +61,21 @@ def test_random_small_shapes(gpu_lib, seed):
     check_config(synth.make_inputs(cfg, seed), cfg, f"small {seed}", max_tie_frac=0.25)
 
 
+@pytest.mark.parametrize("seed,d,e,s,r,D,M,K,W,B,batch", [
+    (0, 128, 128, 128, 32, 5, 32, 4, 8, 40, 1),
+    (1, 256, 384, 128, 64, 8, 64, 8, 8, 100, 2),
+    (2, 512, 128, 256, 16, 6, 16, 3, 16, 60, 4),
+    (3, 128, 256, 384, 48, 4, 128, 8, 8, 90, 8),
+    (4, 384, 128, 128, 256, 7, 33, 5, 12, 77, 3),
+])
+def test_mfma_product_paths(gpu_lib, seed, d, e, s, r, D, M, K, W, B, batch):
+    """bf16 shapes whose products run on the MFMA kernels (contraction
+    widths multiple of 128, at most 64 activation rows)."""
+    cfg = synth.custom_config(cfg_id=8000 + seed, d=d, V=4000 + 17 * seed, e=e, s=s, r=r,
+                              D=D, M=M, K=K, W=W, B=B, beta=-0.05, batch=batch, wtype="bf16")
+    check_config(synth.make_inputs(cfg, seed), cfg, f"mfma {seed}", max_tie_frac=0.34)
+
+
 def test_caps_larger_than_round(gpu_lib):
     cfg = synth.CONFIGS["tiny"].with_(batch=2)
     check_config(synth.make_inputs(cfg, 7), cfg, "tiny caps>params",
@@ -75,3 +90,20 @@ def test_determinism(gpu_lib):
         for q in range(cfg.batch):
             for k in ("tok", "parent", "depth", "score", "mask"):
                 assert np.array_equal(o[q][k], outs[0][q][k])
+
+
+@pytest.mark.parametrize("seed,d,e,s,r,D,M,K,W,B,batch,beta", [
+    (0, 128, 128, 128, 32, 5, 32, 4, 8, 40, 1, -0.05),
+    (1, 256, 256, 256, 64, 9, 16, 3, 5, 60, 2, 0.0),
+    (2, 128, 384, 128, 16, 1, 8, 2, 4, 3, 1, -0.1),
+    (3, 256, 128, 384, 48, 7, 64, 1, 1, 7, 1, -0.2),
+    (4, 128, 128, 128, 256, 12, 32, 8, 16, 120, 1, -0.01),
+    (5, 384, 256, 128, 128, 6, 20, 4, 8, 50, 2, -0.05),
+    (6, 128, 128, 1024, 256, 16, 32, 4, 8, 64, 1, -0.05),
+])
+def test_persistent_depth_loop(gpu_lib, seed, d, e, s, r, D, M, K, W, B, batch, beta):
+    """Shapes that run the depth loop as one cooperative persistent kernel
+    (bf16, GRU sizes multiple of 128, few branches per depth)."""
+    cfg = synth.custom_config(cfg_id=9000 + seed, d=d, V=3000 + 31 * seed, e=e, s=s, r=r,
+                              D=D, M=M, K=K, W=W, B=B, beta=beta, batch=batch, wtype="bf16")
+    check_config(synth.make_inputs(cfg, seed), cfg, f"persistent {seed}", max_tie_frac=0.5)
