@@ -33,7 +33,7 @@ struct Ws {
   int32_t *surv_hist = nullptr, *gidx_tok = nullptr, *gidx_par = nullptr, *sel = nullptr;
   uint32_t *status = nullptr;
   // persistent depth loop: correction tables, partial sums, arrival flags
-  float *G = nullptr, *g = nullptr, *pk_part = nullptr, *gitab = nullptr;
+  float *G = nullptr, *g = nullptr, *pk_part = nullptr, *gitab = nullptr, *pk_terms = nullptr;
   uint32_t *flags = nullptr;
 };
 
@@ -106,7 +106,7 @@ void free_ws(Ws &ws) {
   void *ptrs[] = {ws.part, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.u, ws.ell, ws.gi, ws.gh,
                   ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
-                  ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.flags};
+                  ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.flags};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   ws = Ws();
@@ -219,6 +219,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
     A(alloc(&ws.g, (size_t)ctx->pk_rows));
     A(alloc(&ws.pk_part, persist_part_floats(s)));
     A(alloc(&ws.gitab, persist_gitab_floats(s, c.max_D)));
+    A(alloc(&ws.pk_terms, 2 * persist_terms_floats(s)));
     A(alloc(&ws.flags, persist_flag_words(s)));
     if (e == hipSuccess) A(hipMemset(ws.flags, 0, persist_flag_words(s) * 4));
     if (e == hipSuccess) A(hipDeviceSynchronize());
@@ -313,7 +314,8 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
                                    ws.uH, ws.G, ws.g, st));
     prof_mark(ctx, 3, st);
     PersistArgs pa{batch, D, M, K, W, s, w.e, w.V, w.W_ih, w.W_hh, w.Emb, w.b_ih, w.b_hh,
-                   ws.C, root, ws.G, ws.g, ws.S[0], ws.S[1], ws.pk_part, ws.gitab, ws.flags,
+                   ws.C, root, ws.G, ws.g, ws.pk_terms, ws.pk_terms + persist_terms_floats(s),
+                   ws.pk_part, ws.gitab, ws.flags,
                    ctx->epoch, tb};
     HIPCHK(ctx, launch_depth_persistent(pa, st));
     ctx->epoch += (uint32_t)D + 1u;

@@ -4,20 +4,23 @@
 // the corrected logits of candidate j for a branch with state S are
 //   ell_j = Cl_j + W2[C_j] . (uH + W1[:, d:] S) = g_j + G_j . S,
 // with g = Cl + W2[C] uH and G = W2[C] W1[:, d:] fixed for the round once the
-// Top-M candidates are known (k_corr_tables).  The hidden units of the GRU
-// are split over the persistent workgroups (16 units each, their W_hh rows
-// resident in LDS, their W_ih rows in registers); after a GRU step every
-// workgroup publishes, for every new
-// branch, its partial sum of G_j . S over its own units, and raises its
-// arrival flag.  Once every flag is up, every workgroup adds the partials in
-// the same fixed order and runs the same selection (log-softmax over M,
-// Top-K per branch, Top-W per request; DARTree page, Methodology 1), so one
-// grid-wide hand-off per depth suffices.  While waiting, each workgroup
-// computes the GRU input projections of its units for the next depth's
-// candidates (the survivors' tokens are among them).
+// Top-M candidates are known (k_corr_tables).
+//
+// The GRU's hidden units are split over the workgroups of one cooperative
+// launch.  Producers (8 units each, their W_ih rows in registers) compute the
+// input projections W_ih Emb[tok] + b_ih of the root tokens and of every
+// depth's candidates ahead of time; nothing they do waits on anyone.
+// Consumers (32 units each, their W_hh rows in registers) run the depth loop:
+// after a GRU step each publishes, for every new branch, its partial sum of
+// G_j . S over its own units and raises its arrival flag; once every flag is
+// up, every consumer adds the partials in the same fixed order and runs the
+// same selection (log-softmax over M, Top-K per branch, Top-W per request;
+// DARTree page, Methodology 1), so one grid-wide hand-off per depth suffices.
 //
 // GRU products run on MFMA: weights are the A operand, activations the B
 // operand; the fp32 state is split exactly into three bf16 terms.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -73,12 +76,17 @@ __global__ __launch_bounds__(256) void k_corr_tables(int rows, int M, int D, int
     const uint4 bv = *reinterpret_cast<const uint4 *>(w1t + (wave * 16 + lr) * KS + ks * 32 + gq * 8);
     acc = mfma(a, bv, acc);
   }
-  // lane holds D[row 4 gq + t][column wave*16 + lr]
+  // lane holds D[row 4 gq + t][column wave*16 + lr]; G is stored
+  // [request * D + depth][state unit][candidate] so that a run of state units
+  // of one depth is one contiguous block
   const int n = n0 + wave * 16 + lr;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int row = row0 + 4 * gq + t;
-    if (row < rows && n < s) G[(size_t)row * s + n] = acc[t];
+    if (row < rows && n < s) {
+      const int qd = row / M, jj = row - qd * M;
+      G[((size_t)qd * s + n) * M + jj] = acc[t];
+    }
   }
   if (blockIdx.x == 0) {
     for (int rr = wave; rr < 16; rr += 4) {
@@ -96,39 +104,44 @@ __global__ __launch_bounds__(256) void k_corr_tables(int rows, int M, int D, int
 // ---------------------------------------------------------------- persistent
 constexpr int PK_WAVES = 8;
 constexpr int PK_THREADS = PK_WAVES * 64;
-constexpr int PK_UW = 16;           // hidden units per workgroup
-constexpr int PK_GR = 3 * PK_UW;    // gate rows per workgroup (r, z, n blocks)
+constexpr int PK_CU = 32;           // units per consumer
+constexpr int PK_PU = 8;            // units per producer
+constexpr int PK_PPC = PK_CU / PK_PU;   // producers feeding one consumer
 constexpr int PK_ROWS = 16;         // max expanded branches (all requests) per depth
 constexpr int PK_MAXC = 32;         // max candidates (all requests) per depth
 constexpr int PK_MAXZ = 512;        // max children (all requests) per depth
 constexpr int PK_MAXELL = 512;      // max branches x candidates (all requests)
-constexpr int PK_KSW = 10;          // W_ih k-steps (32 wide) held per wave: e <= 2560
-constexpr int PK_HKS = 4;           // W_hh k-steps per wave: s <= 1024
+constexpr int PK_MAXD = 31;         // max depth
+constexpr int PK_KSW = 10;          // W_ih k-steps (32 wide) per producer wave: e <= 2560
+constexpr int PK_HKS = 4;           // W_hh k-steps per consumer wave: s <= 1024
+constexpr int PK_SMAX = 32 * PK_HKS * 8;   // largest state size
+constexpr int PK_SLOTS = 3 * PK_ROWS;      // (term, branch) columns of the state fragments
 constexpr unsigned PK_SPIN = 1u << 20;
 
 struct PKLayout {
-  size_t whh, red, gic, ghs, ell, ex, lpkey, snew, ckey, clex, cmeta, gs, ctok, gtab, sinfo,
+  size_t red, stage, gis, gsl, ghs, bhh, ell, ex, lpkey, snew, ckey, clex, cmeta, ctok, sinfo,
       finfo, misc, total;
 };
 
-__host__ __device__ inline PKLayout pk_layout(int s) {
+__host__ __device__ inline PKLayout pk_layout() {
   PKLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += (bytes + 15) & ~(size_t)15; return at; };
-  L.whh = take((size_t)PK_GR * (s + 8) * 2);
-  L.red = take((size_t)PK_WAVES * 3 * 16 * 16 * 4);
-  L.gic = take((size_t)PK_MAXC * PK_GR * 4);
-  L.ghs = take((size_t)3 * 16 * 16 * 4);
+  // per-wave MFMA tiles; before them, the current branches' state fragments
+  L.red = take(std::max((size_t)PK_WAVES * 6 * 16 * 16 * 4, (size_t)(PK_SMAX / 32) * PK_SLOTS * 64));
+  L.stage = take((size_t)PK_WAVES * PK_MAXELL * 4);   // partial sums, 8 groups of consumers
+  L.gis = take((size_t)PK_MAXC * 3 * PK_CU * 4);      // input part of this depth's candidates
+  L.gsl = take((size_t)PK_MAXC * PK_CU * 4);          // G slice of the next depth
+  L.ghs = take((size_t)6 * 16 * 16 * 4);              // state part of the current branches
+  L.bhh = take((size_t)3 * PK_CU * 4);
   L.ell = take((size_t)PK_MAXELL * 4);
   L.ex = take((size_t)PK_MAXELL * 4);
   L.lpkey = take((size_t)PK_MAXELL * 8);
-  L.snew = take((size_t)2 * PK_ROWS * PK_UW * 4);
+  L.snew = take((size_t)2 * PK_ROWS * PK_CU * 4);
   L.ckey = take((size_t)PK_MAXZ * 8);
   L.clex = take((size_t)PK_MAXZ * 4);
   L.cmeta = take((size_t)PK_MAXZ * 4);
-  L.gs = take((size_t)PK_MAXC * PK_UW * 4);
-  L.ctok = take((size_t)2 * PK_MAXC * 4);
-  L.gtab = take((size_t)PK_MAXC * 4);
+  L.ctok = take((size_t)PK_MAXC * 4);
   L.sinfo = take((size_t)PK_ROWS * 8 * 4);
   L.finfo = take((size_t)PK_ROWS * 4 * 4);
   L.misc = take(64 * 4);
@@ -137,46 +150,87 @@ __host__ __device__ inline PKLayout pk_layout(int s) {
 }
 
 struct PKParams {
-  int b, D, M, K, W, s, e, V, NWG;
+  int b, D, M, K, W, s, e, V, NC, NP;
   const uint16_t *W_ih, *W_hh, *Emb;
   const float *b_ih, *b_hh;
   const int32_t *C, *root;
   const float *G, *g;
-  float *S0, *S1;        // [b * Wmax, s]
-  float *part;           // [2][NWG][PK_MAXELL]
-  uint32_t *flags;       // [NWG * 64]
+  uint16_t *T0, *T1;     // published states: [s/32 k-steps][48 slots][32] bf16
+  float *part;           // [2][NC][PK_MAXELL]
+  float *gitab;          // [D slots][PK_MAXC][3s]: slot 0 roots, slot t+1 depth t
+  uint32_t *flags;       // [(NC + NP) * 64]: consumer arrivals, then producer slots
   uint32_t epoch0;
   TreeBufs t;
 };
 
-// Hand-off between the persistent workgroups.  Everything another workgroup
-// reads is stored with agent-scope relaxed atomic stores (pk_put), which are
-// coherent across the XCDs without writing back whole L2 caches; each thread
-// waits until its stores have completed before the workgroup raises its flag.
-// The reader polls the flags, then one agent-scope acquire fence makes its
-// plain loads see those values.
+// Hand-off between workgroups.  Everything another workgroup reads is stored
+// with agent-scope relaxed atomic stores (pk_put), which are coherent across
+// the XCDs without writing back whole L2 caches; each thread waits until its
+// stores have completed before the workgroup raises its flag.  Readers poll
+// the flags and then read the published values with device-coherent loads
+// (pk_get, pk_get4, and the copies below with the same cache policy), which
+// miss in the XCD-private caches, so no cache-wide invalidation is needed.
+constexpr int PK_COHERENT = 16;   // cache-policy bits of a device-coherent load
 __device__ __forceinline__ void pk_put(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__device__ __forceinline__ void pk_arrive(uint32_t *flags, uint32_t epoch) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&flags[blockIdx.x * 64], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float pk_get(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Device-coherent 16-byte load at byte offset off of a buffer (reads past the
+// buffer's size return zeros).
+typedef unsigned pk_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pk_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ float4 pk_get4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const pk_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, PK_COHERENT);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
 }
 
-// Returns false if some workgroup failed to arrive within the spin limit
-// (status bit 1 is then set and the caller leaves the loop).
-__device__ __forceinline__ bool pk_wait(uint32_t *flags, int nwg, uint32_t epoch, uint32_t *status,
-                                        int *bad) {
+// Copies nchunk 16-byte chunks straight from global memory into LDS (no
+// registers in between): chunk ci lands at dst + 4 ci and comes from src(ci);
+// AUX is the loads' cache policy.  Wave w issues copy instructions w,
+// w + PK_WAVES, ...; each covers 64 chunks, lanes past nchunk copy chunk 0
+// again into the destination's tail, so dst must hold nchunk rounded up to 64
+// chunks.
+template <int AUX, class F>
+__device__ __forceinline__ void pk_dma(float *dst, int nchunk, F src) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ninstr = (nchunk + 63) >> 6;
+  for (int in = wave; in < ninstr; in += PK_WAVES) {
+    const int ci = in * 64 + lane;
+    __builtin_amdgcn_global_load_lds(src(ci < nchunk ? ci : 0),
+                                     (__attribute__((address_space(3))) void *)(dst + in * 256),
+                                     16, 0, AUX);
+  }
+}
+
+__device__ __forceinline__ void pk_raise(uint32_t *flag, uint32_t epoch) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Threads i < n poll flags[i * 64] >= epoch, threads 64 .. 64 + npf - 1 poll
+// pf[(i - 64) * 64] >= pepoch; false if any wait exceeded the spin limit
+// (status bit 1 is then set and the caller leaves).
+__device__ __forceinline__ bool pk_wait(const uint32_t *flags, int n, uint32_t epoch,
+                                        const uint32_t *pf, int npf, uint32_t pepoch,
+                                        uint32_t *status, int *bad) {
   if (threadIdx.x == 0) *bad = 0;
   __syncthreads();
-  if (threadIdx.x < nwg) {
-    unsigned n = 0;
-    while (__hip_atomic_load(&flags[threadIdx.x * 64], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-           epoch) {
-      if (++n > PK_SPIN) {
+  const uint32_t *f = nullptr;
+  uint32_t want = 0;
+  const int tid = threadIdx.x;
+  if (tid < n) { f = flags + tid * 64; want = epoch; }
+  else if (tid >= 64 && tid < 64 + npf) { f = pf + (tid - 64) * 64; want = pepoch; }
+  if (f) {
+    unsigned k = 0;
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+      if (++k > PK_SPIN) {
         atomicOr(status, 2u);
         *bad = 1;
         break;
@@ -185,52 +239,7 @@ __device__ __forceinline__ bool pk_wait(uint32_t *flags, int nwg, uint32_t epoch
     }
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return *bad == 0;
-}
-
-// GRU input projection of this workgroup's 48 gate rows for nrow (<= 16)
-// token rows: out[row][gr] = W_ih[gate row] . Emb[tok(row)] + b_ih.  The
-// weights sit in registers (k-step ks = wave + 8 i covers k in
-// [32 ks, 32 ks + 32), lane group g its 8 consecutive k); the eight waves'
-// partial sums over their k-steps are added in LDS.
-__device__ void pk_gi(const PKParams &p, const uint4 (&wr)[PK_KSW][3], const int32_t *toks,
-                      int nrow, float *red, float *out) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lr = lane & 15, g = lane >> 4;
-  const int j0 = blockIdx.x * PK_UW, nks = p.e >> 5;
-  const bool live = lr < nrow;
-  const uint16_t *xrow = p.Emb + (size_t)toks[live ? lr : 0] * p.e + g * 8;
-  uint4 xb[PK_KSW];
-#pragma unroll
-  for (int i = 0; i < PK_KSW; ++i) {
-    const int ks = wave + PK_WAVES * i;
-    xb[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (ks < nks && live) xb[i] = *reinterpret_cast<const uint4 *>(xrow + ks * 32);
-  }
-  f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int i = 0; i < PK_KSW; ++i) {
-    const int ks = wave + PK_WAVES * i;
-    if (ks < nks) {
-#pragma unroll
-      for (int m = 0; m < 3; ++m) acc[m] = mfma(wr[i][m], xb[i], acc[m]);
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < 3; ++m)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) red[((wave * 3 + m) * 16 + 4 * g + t) * 16 + lr] = acc[m][t];
-  __syncthreads();
-  for (int i = threadIdx.x; i < nrow * PK_GR; i += blockDim.x) {
-    const int row = i / PK_GR, gr = i - row * PK_GR;
-    const int m = gr / PK_UW, u = gr - m * PK_UW;
-    float v = p.b_ih ? p.b_ih[m * p.s + j0 + u] : 0.f;
-#pragma unroll
-    for (int wv = 0; wv < PK_WAVES; ++wv) v += red[((wv * 3 + m) * 16 + u) * 16 + row];
-    out[i] = v;
-  }
-  __syncthreads();
 }
 
 __device__ __forceinline__ uint4 pack_bf16x8(const uint16_t (&h)[8]) {
@@ -238,104 +247,225 @@ __device__ __forceinline__ uint4 pack_bf16x8(const uint16_t (&h)[8]) {
                     h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
 }
 
-__global__ __launch_bounds__(PK_THREADS) void k_depth_persistent(PKParams p) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const PKLayout L = pk_layout(p.s);
-  uint16_t *whh = reinterpret_cast<uint16_t *>(smem + L.whh);
-  float *red = reinterpret_cast<float *>(smem + L.red);
-  float *gic = reinterpret_cast<float *>(smem + L.gic);      // [cand][48] input part
-  float *ghs = reinterpret_cast<float *>(smem + L.ghs);      // [3][16 units][16 rows]
-  float *ell = reinterpret_cast<float *>(smem + L.ell);
-  float *ex = reinterpret_cast<float *>(smem + L.ex);
-  uint64_t *lpkey = reinterpret_cast<uint64_t *>(smem + L.lpkey);
-  float *snew = reinterpret_cast<float *>(smem + L.snew);    // [2][16 rows][16 units]
-  uint64_t *ckey = reinterpret_cast<uint64_t *>(smem + L.ckey);
-  uint32_t *clex = reinterpret_cast<uint32_t *>(smem + L.clex);
-  int32_t *cmeta = reinterpret_cast<int32_t *>(smem + L.cmeta);
-  float *gsl = reinterpret_cast<float *>(smem + L.gs);       // [cand][16] G slice
-  int32_t *ctok = reinterpret_cast<int32_t *>(smem + L.ctok); // [2][cand]
-  float *gtab = reinterpret_cast<float *>(smem + L.gtab);    // [cand]
-  int32_t *sinfo = reinterpret_cast<int32_t *>(smem + L.sinfo);
-  int32_t *finfo = reinterpret_cast<int32_t *>(smem + L.finfo);
-  int *misc = reinterpret_cast<int *>(smem + L.misc);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int lr = lane & 15, g = lane >> 4;
-  const int w = blockIdx.x, j0 = w * PK_UW;
-  const int s = p.s, KS = s + 8, M = p.M, b = p.b, D = p.D, K = p.K;
-  const int nks_h = s >> 5;
-  const bool leader = w == 0;
-  const int bM = b * M;
+// Published states.  A state row h of the current branches enters the W_hh
+// products as the exact three-term bf16 split h = hi + mid + lo; term t of
+// branch row r is column slot t * rp + r of the MFMA B operand (rp = 5, 8 or
+// 16 by the number of branches, so that the 3 x rows columns fill as few
+// 16-column passes as possible).  The owner of state units 32 c .. 32 c + 31
+// writes k-step c: [k-step][slot][32 units] in bf16, so a consumer copies the
+// whole table with one contiguous transfer and every lane reads its fragment
+// (slot pass * 16 + lane % 16, units 8 (lane / 16) ..) as 16 contiguous bytes.
+__host__ __device__ inline int pk_rp(int rows) { return rows <= 5 ? 5 : rows <= 8 ? 8 : 16; }
+__host__ __device__ inline int pk_npass(int rows) { return rows <= 5 ? 1 : rows <= 8 ? 2 : 3; }
 
-  // weights of this workgroup's 16 units: W_hh rows -> LDS, W_ih rows -> registers
-  {
-    const int per_row = s >> 3, total = PK_GR * per_row;
-#pragma unroll 8
-    for (int i = tid; i < total; i += blockDim.x) {
-      const int row = i / per_row, k8 = (i - row * per_row) * 8;
-      const int m = row / PK_UW, u = row - m * PK_UW;
-      *reinterpret_cast<uint4 *>(whh + row * KS + k8) =
-          *reinterpret_cast<const uint4 *>(p.W_hh + (size_t)(m * s + j0 + u) * s + k8);
+__device__ __forceinline__ void split3(float x, uint16_t &hi, uint16_t &mi, uint16_t &lo) {
+  hi = f32_to_bf16_rne(x);
+  const float r1 = x - bf16_bits_to_f32(hi);
+  mi = f32_to_bf16_rne(r1);
+  lo = f32_to_bf16_rne(r1 - bf16_bits_to_f32(mi));
+}
+
+// Publishes state value h of branch row `row` (of `rows`) and unit u (0..31,
+// lanes of a pair u, u ^ 1 both active) of consumer c into table T.
+__device__ __forceinline__ void pk_put_state(uint16_t *T, int c, int rows, int row, int u, float h) {
+  uint16_t t3[3];
+  split3(h, t3[0], t3[1], t3[2]);
+  const int rp = pk_rp(rows), np = pk_npass(rows);
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const uint32_t mine = t3[t];
+    const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1);
+    if ((u & 1) == 0) {
+      uint32_t *dst = reinterpret_cast<uint32_t *>(T + ((size_t)(c * np * 16 + t * rp + row) * 32 + u));
+      __hip_atomic_store(dst, mine | (other << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  uint4 wr[PK_KSW][3];
-  {
-    const int nks = p.e >> 5;
+}
+
+// Visits n values ld(0..n-1) with op, loading 8 at a time back to back
+// before their first use (a scheduling barrier keeps the loads together, so
+// the LDS latency is paid once per 8 values); the order of op is fixed.
+template <class T, class Ld, class Op>
+__device__ __forceinline__ void pk_scan(int n, Ld ld, Op op) {
+  int j = 0;
+  for (; j + 8 <= n; j += 8) {
+    T v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = ld(j + k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) op(v[k]);
+  }
+  for (; j < n; ++j) op(ld(j));
+}
+
+// ---- producer: GRU input projections of every table slot for 8 units.
+// A tiles: tile 0 rows 0-7 gate r, rows 8-15 gate z; tile 1 rows 0-7 gate n
+// (rows 8-15 zero).  B tiles: 16 token rows each, both in flight at once.
+__device__ void pk_producer(const PKParams &p, uint8_t *smem) {
+  const PKLayout L = pk_layout();
+  float *red = reinterpret_cast<float *>(smem + L.red);        // [8][2 mt][2 nt][16 col][16 arow]
+  float *bih = reinterpret_cast<float *>(smem + L.bhh);        // [3][8]
+  int32_t *toks = reinterpret_cast<int32_t *>(smem + L.stage); // [slot][PK_MAXC]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int pidx = blockIdx.x - p.NC, j0 = pidx * PK_PU, s = p.s, nks = p.e >> 5;
+  const int b = p.b, M = p.M, D = p.D;
+  uint32_t *myflag = p.flags + (size_t)(p.NC + pidx) * 64;
+  uint4 wr[PK_KSW][2];
+#pragma unroll
+  for (int i = 0; i < PK_KSW; ++i) {
+    const int ks = wave + PK_WAVES * i;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int gate = mt * 2 + (lr >> 3);
+      wr[i][mt] = make_uint4(0u, 0u, 0u, 0u);
+      if (ks < nks && gate < 3)
+        wr[i][mt] = *reinterpret_cast<const uint4 *>(
+            p.W_ih + (size_t)(gate * s + j0 + (lr & 7)) * p.e + ks * 32 + g * 8);
+    }
+  }
+  if (tid < 3 * PK_PU) bih[tid] = p.b_ih ? p.b_ih[(tid / PK_PU) * s + j0 + tid % PK_PU] : 0.f;
+  for (int i = tid; i < D * PK_MAXC; i += blockDim.x) {
+    const int slot = i / PK_MAXC, row = i - slot * PK_MAXC;
+    int tk = 0;
+    if (slot == 0) {
+      if (row < b) tk = min(max(p.root[row], 0), p.V - 1);
+    } else if (row < b * M) {
+      tk = max(p.C[((size_t)(row / M) * D + slot - 1) * M + (row % M)], 0);
+    }
+    toks[i] = tk;
+  }
+  __syncthreads();
+  for (int slot = 0; slot < D; ++slot) {
+    const int nrow = slot == 0 ? b : b * M;
+    const int nnt = nrow > 16 ? 2 : 1;
+    uint4 xb[2][PK_KSW];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int xr = min(nt * 16 + lr, nrow - 1);
+      const uint16_t *xrow = p.Emb + (size_t)toks[slot * PK_MAXC + xr] * p.e + g * 8;
+#pragma unroll
+      for (int i = 0; i < PK_KSW; ++i) {
+        const int ks = wave + PK_WAVES * i;
+        xb[nt][i] = make_uint4(0u, 0u, 0u, 0u);
+        if (ks < nks && nt < nnt) xb[nt][i] = *reinterpret_cast<const uint4 *>(xrow + ks * 32);
+      }
+    }
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) { acc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f}; acc[mt][1] = acc[mt][0]; }
 #pragma unroll
     for (int i = 0; i < PK_KSW; ++i) {
       const int ks = wave + PK_WAVES * i;
+      if (ks < nks) {
 #pragma unroll
-      for (int m = 0; m < 3; ++m) {
-        wr[i][m] = make_uint4(0u, 0u, 0u, 0u);
-        if (ks < nks)
-          wr[i][m] = *reinterpret_cast<const uint4 *>(p.W_ih + (size_t)(m * s + j0 + lr) * p.e +
-                                                       ks * 32 + g * 8);
+        for (int mt = 0; mt < 2; ++mt) {
+          acc[mt][0] = mfma(wr[i][mt], xb[0][i], acc[mt][0]);
+          acc[mt][1] = mfma(wr[i][mt], xb[1][i], acc[mt][1]);
+        }
       }
     }
-  }
-  // root state: the GRU consumes each request's last verified token from h = 0
-  for (int q = tid; q < b; q += blockDim.x) ctok[PK_MAXC + q] = min(max(p.root[q], 0), p.V - 1);
-  for (int i = tid; i < bM * PK_UW; i += blockDim.x) {
-    const int cj = i / PK_UW, u = i - cj * PK_UW, q = cj / M, jj = cj - q * M;
-    gsl[i] = p.G[((size_t)(q * D + 0) * M + jj) * s + j0 + u];
-  }
-  __syncthreads();
-  pk_gi(p, wr, ctok + PK_MAXC, b, red, gic);
-  float *Scur = p.S0, *Snext = p.S1;
-  float *sn_cur = snew, *sn_nxt = snew + PK_ROWS * PK_UW;
-  for (int i = tid; i < b * PK_UW; i += blockDim.x) {
-    const int q = i / PK_UW, u = i - q * PK_UW;
-    const float *a = gic + q * PK_GR;
-    const float cr = p.b_hh ? p.b_hh[j0 + u] : 0.f;
-    const float cz = p.b_hh ? p.b_hh[s + j0 + u] : 0.f;
-    const float cn = p.b_hh ? p.b_hh[2 * s + j0 + u] : 0.f;
-    const float r = 1.f / (1.f + expf(-(a[u] + cr)));
-    const float z = 1.f / (1.f + expf(-(a[PK_UW + u] + cz)));
-    const float n = tanhf(a[2 * PK_UW + u] + r * cn);
-    const float h = (1.f - z) * n;
-    sn_cur[q * PK_UW + u] = h;
-    pk_put(Scur + (size_t)q * s + j0 + u, h);
-  }
-  __syncthreads();
-  // partial corrected logits of depth 0 over this workgroup's units
-  for (int i = tid; i < bM; i += blockDim.x) {
-    const int q = i / M;
-    float acc = 0.f;
+    // lane holds D[arow 4g + t][col lr]; stored as one 16-byte run per lane
 #pragma unroll
-    for (int u = 0; u < PK_UW; ++u) acc += gsl[i * PK_UW + u] * sn_cur[q * PK_UW + u];
-    pk_put(p.part + (size_t)w * PK_MAXELL + i, acc);
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        *reinterpret_cast<f32x4 *>(red + ((((wave * 2 + mt) * 2 + nt) * 16 + lr) * 16 + 4 * g)) =
+            acc[mt][nt];
+    __syncthreads();
+    float *out = p.gitab + (size_t)slot * PK_MAXC * 3 * s;
+    for (int i = tid; i < nrow * 3 * PK_PU; i += blockDim.x) {
+      const int row = i / (3 * PK_PU), gr = i - row * 3 * PK_PU;
+      const int m = gr / PK_PU, u = gr - m * PK_PU;
+      const int mt = m >> 1, arow = (m & 1) * 8 + u, nt = row >> 4, col = row & 15;
+      float v = bih[gr];
+#pragma unroll
+      for (int wv = 0; wv < PK_WAVES; ++wv)
+        v += red[(((wv * 2 + mt) * 2 + nt) * 16 + col) * 16 + arow];
+      pk_put(out + (size_t)row * 3 * s + m * s + j0 + u, v);
+    }
+    pk_raise(myflag, p.epoch0 + slot + 1);
+  }
+}
+
+// ---- consumer: the depth loop
+__device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
+  const PKLayout L = pk_layout();
+  float *red = reinterpret_cast<float *>(smem + L.red);      // [8][6 mt][16 row][16 unit]
+  const uint16_t *sfr = reinterpret_cast<const uint16_t *>(red);   // state fragments, before red
+  float *stage = reinterpret_cast<float *>(smem + L.stage);  // [group][entries]
+  float *gis = reinterpret_cast<float *>(smem + L.gis);      // [cand][3][32]
+  float *gsl = reinterpret_cast<float *>(smem + L.gsl);      // [request][32 units][M]
+  float *ghs = reinterpret_cast<float *>(smem + L.ghs);      // [6 mt][16 rows][16 units]
+  float *bhh = reinterpret_cast<float *>(smem + L.bhh);      // [gate][32 units]
+  float *ell = reinterpret_cast<float *>(smem + L.ell);
+  float *ex = reinterpret_cast<float *>(smem + L.ex);
+  uint64_t *lpkey = reinterpret_cast<uint64_t *>(smem + L.lpkey);
+  float *snew = reinterpret_cast<float *>(smem + L.snew);    // [2][16 rows][32 units]
+  uint64_t *ckey = reinterpret_cast<uint64_t *>(smem + L.ckey);
+  uint32_t *clex = reinterpret_cast<uint32_t *>(smem + L.clex);
+  int32_t *cmeta = reinterpret_cast<int32_t *>(smem + L.cmeta);
+  int32_t *ctok = reinterpret_cast<int32_t *>(smem + L.ctok);
+  int32_t *sinfo = reinterpret_cast<int32_t *>(smem + L.sinfo);
+  int32_t *finfo = reinterpret_cast<int32_t *>(smem + L.finfo);
+  int *misc = reinterpret_cast<int *>(smem + L.misc);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int c = blockIdx.x, j0 = c * PK_CU;
+  const int s = p.s, M = p.M, b = p.b, D = p.D, K = p.K, bM = b * M, nks = s >> 5;
+  uint32_t *cflags = p.flags;
+  const uint32_t *pflags = p.flags + (size_t)(p.NC + PK_PPC * c) * 64;   // this consumer's producers
+
+  // W_hh rows of this workgroup's 32 units, as MFMA A fragments: tile mt =
+  // gate * 2 + half covers gate rows gate*s + j0 + half*16 + (0..15)
+  uint4 wh[PK_HKS][6];
+#pragma unroll
+  for (int i = 0; i < PK_HKS; ++i) {
+    const int ks = wave + PK_WAVES * i;
+#pragma unroll
+    for (int mt = 0; mt < 6; ++mt) {
+      wh[i][mt] = make_uint4(0u, 0u, 0u, 0u);
+      if (ks < nks)
+        wh[i][mt] = *reinterpret_cast<const uint4 *>(
+            p.W_hh + (size_t)((mt >> 1) * s + j0 + (mt & 1) * 16 + lr) * s + ks * 32 + g * 8);
+    }
+  }
+  uint16_t *Tcur = p.T0, *Tnext = p.T1;
+  float *sn_cur = snew, *sn_nxt = snew + PK_ROWS * PK_CU;
+  if (tid < 3 * PK_CU) bhh[tid] = p.b_hh ? p.b_hh[(tid / PK_CU) * s + j0 + tid % PK_CU] : 0.f;
+  for (int i = tid; i < b * PK_CU * M; i += blockDim.x) {
+    const int q = i / (PK_CU * M), rem = i - q * PK_CU * M;
+    gsl[i] = p.G[((size_t)(q * D + 0) * s + j0) * M + rem];
   }
   for (int q = tid; q < b; q += blockDim.x) {
     finfo[q * 4 + 0] = 0;                       // node id
     finfo[q * 4 + 1] = 0;                       // lexicographic rank
     finfo[q * 4 + 2] = __float_as_int(0.f);     // score
   }
-  for (int i = tid; i < bM; i += blockDim.x)
-    ctok[i] = max(p.C[((size_t)(i / M) * D + 0) * M + (i % M)], 0);
-  pk_arrive(p.flags, p.epoch0 + 1);
-  // while the others arrive: input projections of depth 0's candidates
-  pk_gi(p, wr, ctok, min(bM, 16), red, gic);
-  if (bM > 16) pk_gi(p, wr, ctok + 16, bM - 16, red, gic + 16 * PK_GR);
-  if (!pk_wait(p.flags, p.NWG, p.epoch0 + 1, p.t.status, misc)) return;
+  // root state from slot 0 (h = 0, so the state part is b_hh)
+  if (!pk_wait(cflags, 0, 0u, pflags, PK_PPC, p.epoch0 + 1, p.t.status, misc)) return;
+  for (int i = tid; i < b * PK_CU; i += blockDim.x) {
+    const int q = i / PK_CU, u = i - q * PK_CU;
+    const float *a = p.gitab + (size_t)q * 3 * s + j0 + u;
+    const float ar = pk_get(a), az = pk_get(a + s), an = pk_get(a + 2 * s);
+    const float r = 1.f / (1.f + expf(-(ar + bhh[u])));
+    const float z = 1.f / (1.f + expf(-(az + bhh[PK_CU + u])));
+    const float n = tanhf(an + r * bhh[2 * PK_CU + u]);
+    const float h = (1.f - z) * n;
+    sn_cur[q * PK_CU + u] = h;
+    pk_put_state(Tcur, c, b, q, u, h);
+  }
+  __syncthreads();
+  for (int i = tid; i < bM; i += blockDim.x) {
+    const int q = i / M, j = i - q * M;
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < PK_CU; ++u) acc += gsl[(q * PK_CU + u) * M + j] * sn_cur[q * PK_CU + u];
+    pk_put(p.part + (size_t)c * PK_MAXELL + i, acc);
+  }
+  pk_raise(cflags + c * 64, p.epoch0 + 1);
+  if (!pk_wait(cflags, p.NC, p.epoch0 + 1, pflags, PK_PPC, p.epoch0 + (D > 1 ? 2 : 1),
+               p.t.status, misc))
+    return;
 
   int A = 1, off = 1;   // branches expanded at this depth; node id of its first child
   for (int dd = 0; dd < D; ++dd) {
@@ -344,67 +474,118 @@ __global__ __launch_bounds__(PK_THREADS) void k_depth_persistent(PKParams p) {
     const int An = Z < p.W ? Z : p.W;
     const int E = rows * M;
     const bool more = dd + 1 < D;
-    const float *pp = p.part + (size_t)(dd & 1) * p.NWG * PK_MAXELL;
-    // ---- one round trip: partial sums, tables, states of the current branches
-    // two threads per entry (workgroups [0,32) and [32,64)) when E <= 256,
-    // else one thread per entry in two batches; summed in a fixed order
-    const bool act = tid < E;
-    const bool split = E <= PK_THREADS / 2;
-    const int ent = split ? (tid & (PK_THREADS / 2 - 1)) : tid;
-    const int vhalf = split ? (tid >> 8) * 32 : 0;
-    const bool lact = ent < E;
-    float x[32];
+    const float *pp = p.part + (size_t)(dd & 1) * p.NC * PK_MAXELL;
+    // ---- one round trip: partial sums of every consumer into registers; the
+    // tables of the next depth and the current branches' states straight into
+    // LDS.  Thread (eq, sg) takes consumers 4 sg .. 4 sg + 3 of entries
+    // 4 eq .. 4 eq + 3 (entries 256+ in a second pass).
+    const __amdgpu_buffer_rsrc_t prs = pk_rsrc(pp, (uint32_t)(p.NC * PK_MAXELL * 4));
+    const int eq = tid & 63, sg = tid >> 6;
+    float4 xs[4];
 #pragma unroll
-    for (int v = 0; v < 32; ++v)
-      x[v] = (lact && vhalf + v < p.NWG) ? pp[(size_t)(vhalf + v) * PK_MAXELL + ent] : 0.f;
+    for (int v = 0; v < 4; ++v) {
+      xs[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (4 * eq < E && 4 * sg + v < p.NC)
+        xs[v] = pk_get4(prs, (uint32_t)(((4 * sg + v) * PK_MAXELL + 4 * eq) * 4));
+    }
+    if (more) {
+      pk_dma<PK_COHERENT>(red, nks * pk_npass(rows) * 64,
+                          [&](int ci) { return reinterpret_cast<const float *>(Tcur + 8 * ci); });
+      const float *gtab = p.gitab + (size_t)(dd + 1) * PK_MAXC * 3 * s + j0;
+      pk_dma<PK_COHERENT>(gis, bM * 24, [&](int ci) {
+        const int rw = ci >> 3, cj = rw / 3;
+        return gtab + (size_t)cj * 3 * s + (rw - 3 * cj) * s + (ci & 7) * 4;
+      });
+      const int qc = 8 * M;   // chunks per request: 32 units x M candidates
+      pk_dma<0>(gsl, b * qc, [&](int ci) {
+        const int q = ci / qc;
+        return p.G + ((size_t)(q * D + dd + 1) * s + j0) * M + 4 * (ci - q * qc);
+      });
+    }
     float gval = 0.f;
-    if (act) gval = p.g[((size_t)(tid / (A * M)) * D + dd) * M + (tid % M)];
-    if (tid < bM) {
-      ctok[tid] = max(p.C[((size_t)(tid / M) * D + dd) * M + (tid % M)], 0);
-      if (dd + 1 < D) ctok[PK_MAXC + tid] = max(p.C[((size_t)(tid / M) * D + dd + 1) * M + (tid % M)], 0);
-    }
-    float gv = 0.f;
-    if (more && tid < bM * PK_UW) {
-      const int cj = tid / PK_UW, u = tid - cj * PK_UW, q = cj / M, jj = cj - q * M;
-      gv = p.G[((size_t)(q * D + dd + 1) * M + jj) * s + j0 + u];
-    }
-    {
-      float part_sum = 0.f;
+    if (tid < E) gval = p.g[((size_t)(tid / (A * M)) * D + dd) * M + (tid % M)];
+    // raw token, clamped only after the loads above have landed
+    const int tc = min(tid, bM - 1);
+    const int tokraw = p.C[((size_t)(tc / M) * D + dd) * M + (tc % M)];
+    for (int half = 0;; ++half) {
+      if (4 * eq + 256 * half < E) {
+        float4 t = xs[0];
 #pragma unroll
-      for (int v = 0; v < 32; ++v) part_sum += x[v];
-      if (!split && lact) {
-#pragma unroll
-        for (int v = 0; v < 32; ++v)
-          x[v] = 32 + v < p.NWG ? pp[(size_t)(32 + v) * PK_MAXELL + ent] : 0.f;
-#pragma unroll
-        for (int v = 0; v < 32; ++v) part_sum += x[v];
+        for (int v = 1; v < 4; ++v) { t.x += xs[v].x; t.y += xs[v].y; t.z += xs[v].z; t.w += xs[v].w; }
+        *reinterpret_cast<float4 *>(stage + sg * PK_MAXELL + 4 * eq + 256 * half) = t;
       }
-      if (split && tid >= PK_THREADS / 2 && lact) ex[ent] = part_sum;   // upper half
-      __syncthreads();
-      if (act) ell[tid] = gval + (split ? part_sum + ex[tid] : part_sum);
-    }
-    if (more && tid < bM * PK_UW) gsl[tid] = gv;
-    // states of the current branches: loaded now, in flight during the selection
-    float4 sf[PK_HKS][2];
+      if (half == 1 || E <= 256) break;
 #pragma unroll
-    for (int i = 0; i < PK_HKS; ++i) {
-      const int ks = wave + PK_WAVES * i;
-      sf[i][0] = make_float4(0.f, 0.f, 0.f, 0.f);
-      sf[i][1] = sf[i][0];
-      if (more && ks < nks_h && lr < rows) {
-        const float *sp = Scur + (size_t)lr * s + ks * 32 + g * 8;
-        sf[i][0] = *reinterpret_cast<const float4 *>(sp);
-        sf[i][1] = *reinterpret_cast<const float4 *>(sp + 4);
+      for (int v = 0; v < 4; ++v) {
+        xs[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (4 * eq + 256 < E && 4 * sg + v < p.NC)
+          xs[v] = pk_get4(prs, (uint32_t)(((4 * sg + v) * PK_MAXELL + 256 + 4 * eq) * 4));
       }
     }
+    if (tid < bM) ctok[tid] = max(tokraw, 0);
+    __builtin_amdgcn_s_waitcnt(0);   // direct-to-LDS copies have landed
+    __syncthreads();
+    // ---- state projection of every current branch (MFMA over the published
+    // three-term splits; see pk_put_state)
+    const int rp = pk_rp(rows);
+    if (more) {
+      const int npass = pk_npass(rows);
+      f32x4 acc[6];
+#pragma unroll
+      for (int mt = 0; mt < 6; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < PK_HKS; ++i) {
+        const int ks = wave + PK_WAVES * i;
+        if (ks < nks) {
+          for (int ps = 0; ps < npass; ++ps) {
+            // slots past the 3 x rp used ones share their columns with used
+            // slots of earlier passes, so they must contribute zero
+            uint4 bf = make_uint4(0u, 0u, 0u, 0u);
+            if (ps * 16 + lr < 3 * rp)
+              bf = *reinterpret_cast<const uint4 *>(sfr + ((ks * npass + ps) * 16 + lr) * 32 + g * 8);
+#pragma unroll
+            for (int mt = 0; mt < 6; ++mt) acc[mt] = mfma(wh[i][mt], bf, acc[mt]);
+          }
+        }
+      }
+      __syncthreads();   // every wave has read the staged states red overwrites
+      // lane holds D[unit 4g + t][column lr]: one 16-byte run per lane
+#pragma unroll
+      for (int mt = 0; mt < 6; ++mt)
+        *reinterpret_cast<f32x4 *>(red + ((wave * 6 + mt) * 16 + lr) * 16 + 4 * g) = acc[mt];
+    }
+    __syncthreads();
+    if (tid < E) {
+      float v = 0.f;   // consumer groups in a fixed order
+      pk_scan<float>(PK_WAVES, [&](int q) { return stage[q * PK_MAXELL + tid]; },
+                     [&](float x) { v += x; });
+      ell[tid] = gval + v;
+    }
+    if (more) {
+      for (int i = tid; i < 6 * 16 * rows; i += blockDim.x) {
+        const int mt = i / (16 * rows), rem = i - mt * 16 * rows, row = rem >> 4, u = rem & 15;
+        float v = bhh[(mt >> 1) * PK_CU + (mt & 1) * 16 + u];
+        for (int col = row; col < 16; col += rp) {
+          float w8[PK_WAVES];
+#pragma unroll
+          for (int wv = 0; wv < PK_WAVES; ++wv) w8[wv] = red[((wv * 6 + mt) * 16 + col) * 16 + u];
+#pragma unroll
+          for (int wv = 0; wv < PK_WAVES; ++wv) v += w8[wv];
+        }
+        ghs[(mt * 16 + row) * 16 + u] = v;
+      }
+    }
+    __syncthreads();
     // ---- selection, one thread per (branch, candidate): log-softmax over M
+    const bool act = tid < E;
     float lval = 0.f, mx = -INFINITY;
     int row = 0, jj = 0;
     if (act) {
       row = tid / M;
       jj = tid - row * M;
       lval = ell[tid];
-      for (int j = 0; j < M; ++j) mx = fmaxf(mx, ell[row * M + j]);
+      const float *er = ell + row * M;
+      pk_scan<float>(M, [&](int j) { return er[j]; }, [&](float x) { mx = fmaxf(mx, x); });
       ex[tid] = expf(lval - mx);
     }
     __syncthreads();
@@ -412,25 +593,26 @@ __global__ __launch_bounds__(PK_THREADS) void k_depth_persistent(PKParams p) {
     float lp = 0.f;
     if (act) {
       float sum = 0.f;
-      for (int j = 0; j < M; ++j) sum += ex[row * M + j];
+      const float *xr = ex + row * M;
+      pk_scan<float>(M, [&](int j) { return xr[j]; }, [&](float x) { sum += x; });
       lp = lval - (mx + logf(sum));
-      const int q = row / A;
-      mykey = make_key(lp, (uint32_t)ctok[q * M + jj]);
+      mykey = make_key(lp, (uint32_t)ctok[(row / A) * M + jj]);
       lpkey[tid] = mykey;
     }
     __syncthreads();
     // Top-K children of each branch (log-prob desc, token asc) by rank
     if (act) {
       int rank = 0;
-      for (int j = 0; j < M; ++j) rank += lpkey[row * M + j] > mykey;
+      const uint64_t *kr = lpkey + row * M;
+      pk_scan<uint64_t>(M, [&](int j) { return kr[j]; }, [&](uint64_t x) { rank += x > mykey; });
       if (rank < K) {
         const int q = row / A, a = row - q * A;
-        const int c = q * Z + a * K + rank;
+        const int cc = q * Z + a * K + rank;
         const float sc = __fadd_rn(__int_as_float(finfo[row * 4 + 2]), lp);
         const uint32_t lex = ((uint32_t)finfo[row * 4 + 1] << 18) | (uint32_t)ctok[q * M + jj];
-        ckey[c] = make_key(sc, lex);
-        clex[c] = lex;
-        cmeta[c] = jj;
+        ckey[cc] = make_key(sc, lex);
+        clex[cc] = lex;
+        cmeta[cc] = jj;
       }
     }
     __syncthreads();
@@ -438,8 +620,9 @@ __global__ __launch_bounds__(PK_THREADS) void k_depth_persistent(PKParams p) {
     if (tid < b * Z) {
       const int q = tid / Z, z = tid - q * Z;
       const uint64_t kc = ckey[tid];
+      const uint64_t *kq = ckey + q * Z;
       int rank = 0;
-      for (int c2 = 0; c2 < Z; ++c2) rank += ckey[q * Z + c2] > kc;
+      pk_scan<uint64_t>(Z, [&](int c2) { return kq[c2]; }, [&](uint64_t x) { rank += x > kc; });
       if (rank < An) {
         int32_t *si = sinfo + (q * An + rank) * 8;
         si[0] = off + z;                        // node id
@@ -454,147 +637,110 @@ __global__ __launch_bounds__(PK_THREADS) void k_depth_persistent(PKParams p) {
       const int q = tid / An;
       const uint32_t li = (uint32_t)sinfo[tid * 8 + 4];
       int rank = 0;
-      for (int j = 0; j < An; ++j) rank += (uint32_t)sinfo[(q * An + j) * 8 + 4] < li;
+      pk_scan<uint32_t>(An, [&](int j) { return (uint32_t)sinfo[(q * An + j) * 8 + 4]; },
+                        [&](uint32_t x) { rank += x < li; });
       sinfo[tid * 8 + 6] = rank;
     }
     __syncthreads();
-    // ---- state projection of every current branch (three-term split of S)
-    if (more) {
-      f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int i = 0; i < PK_HKS; ++i) {
-        const int ks = wave + PK_WAVES * i;
-        if (ks < nks_h) {
-          const float xs[8] = {sf[i][0].x, sf[i][0].y, sf[i][0].z, sf[i][0].w,
-                               sf[i][1].x, sf[i][1].y, sf[i][1].z, sf[i][1].w};
-          uint16_t hh[8], mi[8], lo[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            hh[q] = f32_to_bf16_rne(xs[q]);
-            const float r1 = xs[q] - bf16_bits_to_f32(hh[q]);
-            mi[q] = f32_to_bf16_rne(r1);
-            lo[q] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(mi[q]));
-          }
-          const uint4 bh = pack_bf16x8(hh), bm = pack_bf16x8(mi), bl = pack_bf16x8(lo);
-#pragma unroll
-          for (int m = 0; m < 3; ++m) {
-            const uint4 a = *reinterpret_cast<const uint4 *>(whh + (m * PK_UW + lr) * KS + ks * 32 + g * 8);
-            acc[m] = mfma(a, bh, acc[m]);
-            acc[m] = mfma(a, bm, acc[m]);
-            acc[m] = mfma(a, bl, acc[m]);
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < 3; ++m)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) red[((wave * 3 + m) * 16 + 4 * g + t) * 16 + lr] = acc[m][t];
-    }
-    __syncthreads();
-    if (more) {
-      for (int i = tid; i < 3 * 16 * rows; i += blockDim.x) {
-        const int m = i / (16 * rows), rem = i - m * 16 * rows, u = rem / rows, row = rem - u * rows;
-        float v = p.b_hh ? p.b_hh[m * s + j0 + u] : 0.f;
-#pragma unroll
-        for (int wv = 0; wv < PK_WAVES; ++wv) v += red[((wv * 3 + m) * 16 + u) * 16 + row];
-        ghs[(m * 16 + u) * 16 + row] = v;
-      }
-    }
-    __syncthreads();
-    // node records of this depth (written once, by one workgroup); global
-    // stores are issued only right before the arrival fence, which waits for them
-    const int Zc = Z, offc = off, Ac = A, Anc = An;
-    auto write_records = [&]() {
-      if (!leader) return;
-      for (int c = tid; c < b * Zc; c += blockDim.x) {
-        const int q = c / Zc, z = c - q * Zc;
-        const size_t id = (size_t)q * p.t.NT + offc + z;
-        p.t.n_tok[id] = (int32_t)(clex[c] & 0x3FFFFu);
-        p.t.n_par[id] = finfo[(q * Ac + z / K) * 4 + 0];
+    // node records of this depth, split over the consumers (read by the
+    // emission kernel after this one ends)
+    {
+      const int per = (b * Z + p.NC - 1) / p.NC;
+      for (int cc = c * per + tid; cc < min(b * Z, (c + 1) * per); cc += blockDim.x) {
+        const int q = cc / Z, z = cc - q * Z;
+        const size_t id = (size_t)q * p.t.NT + off + z;
+        p.t.n_tok[id] = (int32_t)(clex[cc] & 0x3FFFFu);
+        p.t.n_par[id] = finfo[(q * A + z / K) * 4 + 0];
         p.t.n_dep[id] = dd + 1;
-        p.t.n_score[id] = key_val(ckey[c]);
-        p.t.n_lex[id] = clex[c];
+        p.t.n_score[id] = key_val(ckey[cc]);
+        p.t.n_lex[id] = clex[cc];
       }
-      for (int i = tid; i < b * Anc; i += blockDim.x) {
-        const int q = i / Anc, rk = i - q * Anc;
+      for (int i = c + p.NC * tid; i < b * An; i += p.NC * blockDim.x) {
+        const int q = i / An, rk = i - q * An;
         p.t.surv_hist[((size_t)q * (D + 1) + dd + 1) * p.t.Wmax + rk] = sinfo[i * 8 + 0];
       }
-    };
-    if (!more) {
-      write_records();
-      break;
     }
+    if (!more) break;
+    __syncthreads();   // node records above read finfo, rewritten below
 
-    // ---- GRU step of the survivors for this workgroup's units
+    // ---- GRU step of the survivors for this workgroup's 32 units
     const int nrow = b * An;
-    if (tid < nrow * PK_UW) {
-      const int i = tid / PK_UW, u = tid - i * PK_UW;
+    if (tid < nrow * PK_CU) {
+      const int i = tid / PK_CU, u = tid - i * PK_CU;
       const int q = i / An;
       const int pr = sinfo[i * 8 + 1], jc = sinfo[i * 8 + 3];
-      const float *a = gic + (q * M + jc) * PK_GR;
-      const float h = sn_cur[pr * PK_UW + u];
-      const float r = 1.f / (1.f + expf(-(a[u] + ghs[(0 * 16 + u) * 16 + pr])));
-      const float z = 1.f / (1.f + expf(-(a[PK_UW + u] + ghs[(1 * 16 + u) * 16 + pr])));
-      const float n = tanhf(a[2 * PK_UW + u] + r * ghs[(2 * 16 + u) * 16 + pr]);
+      const float *a = gis + (q * M + jc) * 3 * PK_CU;
+      const int half = u >> 4, ul = u & 15;
+      const float h = sn_cur[pr * PK_CU + u];
+      const float r = 1.f / (1.f + expf(-(a[u] + ghs[((0 + half) * 16 + pr) * 16 + ul])));
+      const float z = 1.f / (1.f + expf(-(a[PK_CU + u] + ghs[((2 + half) * 16 + pr) * 16 + ul])));
+      const float n = tanhf(a[2 * PK_CU + u] + r * ghs[((4 + half) * 16 + pr) * 16 + ul]);
       const float hn = (1.f - z) * n + z * h;
-      sn_nxt[i * PK_UW + u] = hn;
-    }
-    write_records();
-    __syncthreads();
-    // new states and partial corrected logits of depth dd+1 over this
-    // workgroup's units (the frontier update waits for the records above)
-    if (tid < nrow * PK_UW) {
-      const int i = tid / PK_UW, u = tid - i * PK_UW;
-      pk_put(Snext + (size_t)i * s + j0 + u, sn_nxt[i * PK_UW + u]);
-    }
-    float *pn = p.part + ((size_t)((dd + 1) & 1) * p.NWG + w) * PK_MAXELL;
-    if (tid < nrow * M) {
-      const int i = tid / M, j = tid - i * M, q = i / An;
-      float acc = 0.f;
-#pragma unroll
-      for (int u = 0; u < PK_UW; ++u) acc += gsl[(q * M + j) * PK_UW + u] * sn_nxt[i * PK_UW + u];
-      pk_put(pn + tid, acc);
+      sn_nxt[i * PK_CU + u] = hn;
+      pk_put_state(Tnext, c, nrow, i, u, hn);
     }
     for (int i = tid; i < nrow; i += blockDim.x) {
       finfo[i * 4 + 0] = sinfo[i * 8 + 0];
       finfo[i * 4 + 1] = sinfo[i * 8 + 6];
       finfo[i * 4 + 2] = sinfo[i * 8 + 5];
     }
-    pk_arrive(p.flags, p.epoch0 + dd + 2);
-    // while waiting: input projections of depth dd+1's candidates
-    if (dd + 2 < D) {
-      pk_gi(p, wr, ctok + PK_MAXC, min(bM, 16), red, gic);
-      if (bM > 16) pk_gi(p, wr, ctok + PK_MAXC + 16, bM - 16, red, gic + 16 * PK_GR);
+    __syncthreads();
+    // partial corrected logits of depth dd+1 over this workgroup's units
+    float *pn = p.part + ((size_t)((dd + 1) & 1) * p.NC + c) * PK_MAXELL;
+    if (tid < nrow * M) {
+      const int i = tid / M, j = tid - i * M, q = i / An;
+      const float *gq = gsl + q * PK_CU * M + j;
+      const float *sq = sn_nxt + i * PK_CU;
+      float acc = 0.f;
+#pragma unroll
+      for (int u0 = 0; u0 < PK_CU; u0 += 8) {
+        float gv[8], sv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { gv[k] = gq[(u0 + k) * M]; sv[k] = sq[u0 + k]; }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += gv[k] * sv[k];
+      }
+      pk_put(pn + tid, acc);
     }
-    if (!pk_wait(p.flags, p.NWG, p.epoch0 + dd + 2, p.t.status, misc)) return;
-    float *tmp = Scur; Scur = Snext; Snext = tmp;
+    pk_raise(cflags + c * 64, p.epoch0 + dd + 2);
+    // producer slot dd + 2 holds the candidates of depth dd + 1
+    const uint32_t pe = p.epoch0 + (dd + 2 < D ? dd + 3 : D);
+    if (!pk_wait(cflags, p.NC, p.epoch0 + dd + 2, pflags, PK_PPC, pe, p.t.status, misc)) return;
+    uint16_t *tmp = Tcur; Tcur = Tnext; Tnext = tmp;
     float *tn = sn_cur; sn_cur = sn_nxt; sn_nxt = tn;
     off += Z;
     A = An;
   }
 }
 
+__global__ __launch_bounds__(PK_THREADS) void k_depth_persistent(PKParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  if ((int)blockIdx.x < p.NC) pk_consumer(p, smem);
+  else pk_producer(p, smem);
+}
+
 // ---------------------------------------------------------------- host side
 bool persist_eligible(int b, int D, int M, int K, int W, int s, int e, int r, int wtype,
                       size_t lds_max) {
-  if (wtype != WT_BF16 || s % 128 || e % 128 || s % PK_UW) return false;
-  if (s > 32 * PK_HKS * PK_WAVES || e > 32 * PK_KSW * PK_WAVES || D > 31) return false;
-  if (s / PK_UW > 64) return false;   // grid-wide hand-offs get slow past 64 workgroups
+  if (wtype != WT_BF16 || s % 128 || e % 128) return false;
+  if (s > 32 * PK_HKS * PK_WAVES || e > 32 * PK_KSW * PK_WAVES || D > PK_MAXD) return false;
   if (b * W > PK_ROWS || b * M > PK_MAXC || (long long)b * W * M > PK_MAXELL) return false;
   if ((long long)b * W * K > PK_MAXZ) return false;
   if (r > 512) return false;   // the correction-table tile must fit in LDS
-  return pk_layout(s).total <= lds_max;
+  return pk_layout().total <= lds_max;
 }
 
-size_t persist_flag_words(int s) { return (size_t)(s / PK_UW) * 64; }
-size_t persist_part_floats(int s) { return (size_t)2 * (s / PK_UW) * PK_MAXELL; }
-size_t persist_gitab_floats(int s, int D) { (void)s; (void)D; return 16; }
+size_t persist_flag_words(int s) { return (size_t)(s / PK_CU + s / PK_PU) * 64; }
+size_t persist_part_floats(int s) { return (size_t)2 * (s / PK_CU) * PK_MAXELL; }
+size_t persist_gitab_floats(int s, int D) { return (size_t)D * PK_MAXC * 3 * s; }
+size_t persist_terms_floats(int s) { return (size_t)(s / 32) * PK_SLOTS * 32 / 2; }
 
 hipError_t persist_prepare(int s) {
-  if (s % PK_UW) return hipSuccess;
+  (void)s;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_depth_persistent),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)pk_layout(s).total);
+                                     (int)pk_layout().total);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_corr_tables),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ct_smem(512));
@@ -612,19 +758,23 @@ hipError_t launch_corr_tables(int rows, int M, int D, int r, int s, int d, int l
 }
 
 hipError_t launch_depth_persistent(const PersistArgs &a, hipStream_t st) {
+  if (a.s % 128 || a.D < 1 || a.D > PK_MAXD) return hipErrorInvalidValue;
   PKParams p{};
   p.b = a.b; p.D = a.D; p.M = a.M; p.K = a.K; p.W = a.W; p.s = a.s; p.e = a.e; p.V = a.V;
-  p.NWG = a.s / PK_UW;
+  p.NC = a.s / PK_CU;
+  p.NP = a.s / PK_PU;
   p.W_ih = static_cast<const uint16_t *>(a.W_ih);
   p.W_hh = static_cast<const uint16_t *>(a.W_hh);
   p.Emb = static_cast<const uint16_t *>(a.Emb);
   p.b_ih = a.b_ih; p.b_hh = a.b_hh; p.C = a.C; p.root = a.root; p.G = a.G; p.g = a.g;
-  p.S0 = a.S0; p.S1 = a.S1; p.part = a.part; p.flags = a.flags; p.epoch0 = a.epoch0;
+  p.T0 = reinterpret_cast<uint16_t *>(a.T0);
+  p.T1 = reinterpret_cast<uint16_t *>(a.T1);
+  p.part = a.part; p.gitab = a.gitab; p.flags = a.flags;
+  p.epoch0 = a.epoch0;
   p.t = a.t;
   void *args[] = {&p};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_depth_persistent),
-                                    dim3(p.NWG), dim3(PK_THREADS), args, pk_layout(a.s).total, st);
+                                    dim3(p.NC + p.NP), dim3(PK_THREADS), args, pk_layout().total, st);
 }
 
 }  // namespace dtree
-

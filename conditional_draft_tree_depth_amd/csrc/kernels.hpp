@@ -89,7 +89,8 @@ struct PersistArgs {
   const float *b_ih, *b_hh;
   const int32_t *C, *root;
   const float *G, *g;
-  float *S0, *S1, *part, *gitab;
+  float *T0, *T1;        // published states (persist_terms_floats each)
+  float *part, *gitab;
   uint32_t *flags;
   uint32_t epoch0;
   TreeBufs t;
@@ -99,6 +100,7 @@ bool persist_eligible(int b, int D, int M, int K, int W, int s, int e, int r, in
 size_t persist_flag_words(int s);
 size_t persist_part_floats(int s);
 size_t persist_gitab_floats(int s, int D);
+size_t persist_terms_floats(int s);
 hipError_t persist_prepare(int s);
 hipError_t launch_corr_tables(int rows, int M, int D, int r, int s, int d, int ldw1,
                               const void *W2, const void *W1, const int32_t *C, const float *Cl,
