@@ -40,13 +40,14 @@ __device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
 // rank r (zero-padded to a multiple of 32).  The workgroups of column block 0
 // also produce g = Cl + W2[C] . uH (one wave per row, fp32).
 constexpr int CT_NB = 64;   // state columns per workgroup
+constexpr int CT_THREADS = 256;
 
 __host__ __device__ inline size_t ct_smem(int r) {
   const int rp = (r + 31) & ~31;
   return (size_t)(CT_NB + 16) * (rp + 8) * 2;
 }
 
-__global__ __launch_bounds__(256) void k_corr_tables(int rows, int M, int D, int r, int s, int d,
+__global__ __launch_bounds__(CT_THREADS) void k_corr_tables(int rows, int M, int D, int r, int s, int d,
                                                      int ldw1, const uint16_t *__restrict__ W2,
                                                      const uint16_t *__restrict__ W1,
                                                      const int32_t *__restrict__ C,
@@ -58,11 +59,11 @@ __global__ __launch_bounds__(256) void k_corr_tables(int rows, int M, int D, int
   uint16_t *w1t = reinterpret_cast<uint16_t *>(smem);          // [CT_NB][KS]: W1[k][d + n0 + n]
   uint16_t *w2s = w1t + CT_NB * KS;                            // [16][KS]:   W2[C[row]][k]
   const int row0 = blockIdx.y * 16, n0 = blockIdx.x * CT_NB, tid = threadIdx.x;
-  for (int i = tid; i < rp * CT_NB; i += blockDim.x) {
+  for (int i = tid; i < rp * CT_NB; i += CT_THREADS) {
     const int k = i / CT_NB, n = i - k * CT_NB;
     w1t[n * KS + k] = (k < r && n0 + n < s) ? W1[(size_t)k * ldw1 + d + n0 + n] : (uint16_t)0;
   }
-  for (int i = tid; i < 16 * rp; i += blockDim.x) {
+  for (int i = tid; i < 16 * rp; i += CT_THREADS) {
     const int rr = i / rp, k = i - rr * rp, row = row0 + rr;
     uint16_t v = 0;
     if (row < rows && k < r) v = W2[(size_t)(C[row] < 0 ? 0 : C[row]) * r + k];
@@ -247,6 +248,34 @@ __device__ __forceinline__ uint4 pack_bf16x8(const uint16_t (&h)[8]) {
                     h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
 }
 
+// Exact x / d for 0 <= x < 2^16 and 1 <= d < 2^16 with one high multiply:
+// m = floor(2^32 / d) + 1 exceeds 2^32 / d by less than 1 / d per unit of x.
+struct PkDiv {
+  uint32_t m;   // 0 stands for d == 1
+  __device__ explicit PkDiv(uint32_t d) : m(d == 1 ? 0u : 0xFFFFFFFFu / d + 1u) {}
+  __device__ __forceinline__ int operator()(int x) const {
+    return m ? (int)__umulhi((uint32_t)x, m) : x;
+  }
+};
+
+// Lane exchange within rows of 16 lanes (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ int pk_dpp(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+// All-reduce of v over aligned groups of n lanes (n a power of two <= 64);
+// every lane of a group ends with the same bits for a commutative op.
+template <class Op>
+__device__ __forceinline__ float pk_group_reduce(float v, int n, Op op) {
+  if (n >= 2) v = op(v, __int_as_float(pk_dpp<0xB1>(__float_as_int(v))));    // lane ^ 1
+  if (n >= 4) v = op(v, __int_as_float(pk_dpp<0x4E>(__float_as_int(v))));    // lane ^ 2
+  if (n >= 8) v = op(v, __int_as_float(pk_dpp<0x141>(__float_as_int(v))));   // 7 - lane in 8
+  if (n >= 16) v = op(v, __int_as_float(pk_dpp<0x140>(__float_as_int(v))));  // 15 - lane in 16
+  if (n >= 32) v = op(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+  if (n >= 64) v = op(v, __shfl_xor(v, 32));
+  return v;
+}
+
 // Published states.  A state row h of the current branches enters the W_hh
 // products as the exact three-term bf16 split h = hi + mid + lo; term t of
 // branch row r is column slot t * rp + r of the MFMA B operand (rp = 5, 8 or
@@ -274,7 +303,7 @@ __device__ __forceinline__ void pk_put_state(uint16_t *T, int c, int rows, int r
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
     const uint32_t mine = t3[t];
-    const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1);
+    const uint32_t other = (uint32_t)pk_dpp<0xB1>((int)mine);   // unit u ^ 1
     if ((u & 1) == 0) {
       uint32_t *dst = reinterpret_cast<uint32_t *>(T + ((size_t)(c * np * 16 + t * rp + row) * 32 + u));
       __hip_atomic_store(dst, mine | (other << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -325,7 +354,7 @@ __device__ void pk_producer(const PKParams &p, uint8_t *smem) {
     }
   }
   if (tid < 3 * PK_PU) bih[tid] = p.b_ih ? p.b_ih[(tid / PK_PU) * s + j0 + tid % PK_PU] : 0.f;
-  for (int i = tid; i < D * PK_MAXC; i += blockDim.x) {
+  for (int i = tid; i < D * PK_MAXC; i += PK_THREADS) {
     const int slot = i / PK_MAXC, row = i - slot * PK_MAXC;
     int tk = 0;
     if (slot == 0) {
@@ -374,7 +403,7 @@ __device__ void pk_producer(const PKParams &p, uint8_t *smem) {
             acc[mt][nt];
     __syncthreads();
     float *out = p.gitab + (size_t)slot * PK_MAXC * 3 * s;
-    for (int i = tid; i < nrow * 3 * PK_PU; i += blockDim.x) {
+    for (int i = tid; i < nrow * 3 * PK_PU; i += PK_THREADS) {
       const int row = i / (3 * PK_PU), gr = i - row * 3 * PK_PU;
       const int m = gr / PK_PU, u = gr - m * PK_PU;
       const int mt = m >> 1, arow = (m & 1) * 8 + u, nt = row >> 4, col = row & 15;
@@ -432,18 +461,18 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
   uint16_t *Tcur = p.T0, *Tnext = p.T1;
   float *sn_cur = snew, *sn_nxt = snew + PK_ROWS * PK_CU;
   if (tid < 3 * PK_CU) bhh[tid] = p.b_hh ? p.b_hh[(tid / PK_CU) * s + j0 + tid % PK_CU] : 0.f;
-  for (int i = tid; i < b * PK_CU * M; i += blockDim.x) {
+  for (int i = tid; i < b * PK_CU * M; i += PK_THREADS) {
     const int q = i / (PK_CU * M), rem = i - q * PK_CU * M;
     gsl[i] = p.G[((size_t)(q * D + 0) * s + j0) * M + rem];
   }
-  for (int q = tid; q < b; q += blockDim.x) {
+  for (int q = tid; q < b; q += PK_THREADS) {
     finfo[q * 4 + 0] = 0;                       // node id
     finfo[q * 4 + 1] = 0;                       // lexicographic rank
     finfo[q * 4 + 2] = __float_as_int(0.f);     // score
   }
   // root state from slot 0 (h = 0, so the state part is b_hh)
   if (!pk_wait(cflags, 0, 0u, pflags, PK_PPC, p.epoch0 + 1, p.t.status, misc)) return;
-  for (int i = tid; i < b * PK_CU; i += blockDim.x) {
+  for (int i = tid; i < b * PK_CU; i += PK_THREADS) {
     const int q = i / PK_CU, u = i - q * PK_CU;
     const float *a = p.gitab + (size_t)q * 3 * s + j0 + u;
     const float ar = pk_get(a), az = pk_get(a + s), an = pk_get(a + 2 * s);
@@ -455,7 +484,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     pk_put_state(Tcur, c, b, q, u, h);
   }
   __syncthreads();
-  for (int i = tid; i < bM; i += blockDim.x) {
+  for (int i = tid; i < bM; i += PK_THREADS) {
     const int q = i / M, j = i - q * M;
     float acc = 0.f;
 #pragma unroll
@@ -467,6 +496,9 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
                p.t.status, misc))
     return;
 
+  // (branch row, candidate) of this thread's entry; the entries are row-major
+  const int row0 = tid / M, jj0 = tid - row0 * M;
+  const PkDiv divK(K), divQC(8 * M), divNC(p.NC);
   int A = 1, off = 1;   // branches expanded at this depth; node id of its first child
   for (int dd = 0; dd < D; ++dd) {
     const int rows = b * A;
@@ -474,6 +506,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     const int An = Z < p.W ? Z : p.W;
     const int E = rows * M;
     const bool more = dd + 1 < D;
+    const PkDiv divA(A), divZ(Z), divAn(An);
     const float *pp = p.part + (size_t)(dd & 1) * p.NC * PK_MAXELL;
     // ---- one round trip: partial sums of every consumer into registers; the
     // tables of the next depth and the current branches' states straight into
@@ -498,15 +531,15 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       });
       const int qc = 8 * M;   // chunks per request: 32 units x M candidates
       pk_dma<0>(gsl, b * qc, [&](int ci) {
-        const int q = ci / qc;
+        const int q = divQC(ci);
         return p.G + ((size_t)(q * D + dd + 1) * s + j0) * M + 4 * (ci - q * qc);
       });
     }
     float gval = 0.f;
-    if (tid < E) gval = p.g[((size_t)(tid / (A * M)) * D + dd) * M + (tid % M)];
+    if (tid < E) gval = p.g[((size_t)divA(row0) * D + dd) * M + jj0];
     // raw token, clamped only after the loads above have landed
-    const int tc = min(tid, bM - 1);
-    const int tokraw = p.C[((size_t)(tc / M) * D + dd) * M + (tc % M)];
+    const int tq = tid < bM ? row0 : b - 1, tj = tid < bM ? jj0 : M - 1;
+    const int tokraw = p.C[((size_t)tq * D + dd) * M + tj];
     for (int half = 0;; ++half) {
       if (4 * eq + 256 * half < E) {
         float4 t = xs[0];
@@ -526,13 +559,14 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     __builtin_amdgcn_s_waitcnt(0);   // direct-to-LDS copies have landed
     __syncthreads();
     // ---- state projection of every current branch (MFMA over the published
-    // three-term splits; see pk_put_state)
+    // three-term splits; see pk_put_state).  Only issued here: the selection
+    // below runs while the matrix cores work, the sums are used after it.
     const int rp = pk_rp(rows);
+    f32x4 acc[6];
+#pragma unroll
+    for (int mt = 0; mt < 6; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (more) {
       const int npass = pk_npass(rows);
-      f32x4 acc[6];
-#pragma unroll
-      for (int mt = 0; mt < 6; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < PK_HKS; ++i) {
         const int ks = wave + PK_WAVES * i;
@@ -548,65 +582,59 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
           }
         }
       }
-      __syncthreads();   // every wave has read the staged states red overwrites
-      // lane holds D[unit 4g + t][column lr]: one 16-byte run per lane
-#pragma unroll
-      for (int mt = 0; mt < 6; ++mt)
-        *reinterpret_cast<f32x4 *>(red + ((wave * 6 + mt) * 16 + lr) * 16 + 4 * g) = acc[mt];
     }
-    __syncthreads();
     if (tid < E) {
       float v = 0.f;   // consumer groups in a fixed order
       pk_scan<float>(PK_WAVES, [&](int q) { return stage[q * PK_MAXELL + tid]; },
                      [&](float x) { v += x; });
       ell[tid] = gval + v;
     }
-    if (more) {
-      for (int i = tid; i < 6 * 16 * rows; i += blockDim.x) {
-        const int mt = i / (16 * rows), rem = i - mt * 16 * rows, row = rem >> 4, u = rem & 15;
-        float v = bhh[(mt >> 1) * PK_CU + (mt & 1) * 16 + u];
-        for (int col = row; col < 16; col += rp) {
-          float w8[PK_WAVES];
-#pragma unroll
-          for (int wv = 0; wv < PK_WAVES; ++wv) w8[wv] = red[((wv * 6 + mt) * 16 + col) * 16 + u];
-#pragma unroll
-          for (int wv = 0; wv < PK_WAVES; ++wv) v += w8[wv];
-        }
-        ghs[(mt * 16 + row) * 16 + u] = v;
+    __syncthreads();
+    // ---- selection, one thread per (branch, candidate): log-softmax over M.
+    // When M is a power of two a branch's M candidates are M aligned lanes of
+    // one wave: max and sum are lane butterflies (every lane of a group gets
+    // the same bits) and the group needs no workgroup barrier.
+    const bool act = tid < E;
+    const bool lanes = (M & (M - 1)) == 0;
+    const int row = row0, jj = jj0;
+    const float lval = act ? ell[tid] : 0.f;
+    float mx = -INFINITY, sum = 0.f;
+    if (lanes) {
+      mx = pk_group_reduce(lval, M, [](float a, float b2) { return fmaxf(a, b2); });
+      sum = pk_group_reduce(expf(lval - mx), M, [](float a, float b2) { return a + b2; });
+    } else {
+      if (act) {
+        const float *er = ell + row * M;
+        pk_scan<float>(M, [&](int j) { return er[j]; }, [&](float x) { mx = fmaxf(mx, x); });
+        ex[tid] = expf(lval - mx);
+      }
+      __syncthreads();
+      if (act) {
+        const float *xr = ex + row * M;
+        pk_scan<float>(M, [&](int j) { return xr[j]; }, [&](float x) { sum += x; });
       }
     }
-    __syncthreads();
-    // ---- selection, one thread per (branch, candidate): log-softmax over M
-    const bool act = tid < E;
-    float lval = 0.f, mx = -INFINITY;
-    int row = 0, jj = 0;
-    if (act) {
-      row = tid / M;
-      jj = tid - row * M;
-      lval = ell[tid];
-      const float *er = ell + row * M;
-      pk_scan<float>(M, [&](int j) { return er[j]; }, [&](float x) { mx = fmaxf(mx, x); });
-      ex[tid] = expf(lval - mx);
-    }
-    __syncthreads();
     uint64_t mykey = 0ull;
     float lp = 0.f;
     if (act) {
-      float sum = 0.f;
-      const float *xr = ex + row * M;
-      pk_scan<float>(M, [&](int j) { return xr[j]; }, [&](float x) { sum += x; });
       lp = lval - (mx + logf(sum));
-      mykey = make_key(lp, (uint32_t)ctok[(row / A) * M + jj]);
+      mykey = make_key(lp, (uint32_t)ctok[divA(row) * M + jj]);
       lpkey[tid] = mykey;
     }
-    __syncthreads();
+    if (lanes) {
+      // LDS accesses of one wave take effect in issue order
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      __syncthreads();
+    }
     // Top-K children of each branch (log-prob desc, token asc) by rank
     if (act) {
       int rank = 0;
       const uint64_t *kr = lpkey + row * M;
       pk_scan<uint64_t>(M, [&](int j) { return kr[j]; }, [&](uint64_t x) { rank += x > mykey; });
       if (rank < K) {
-        const int q = row / A, a = row - q * A;
+        const int q = divA(row), a = row - q * A;
         const int cc = q * Z + a * K + rank;
         const float sc = __fadd_rn(__int_as_float(finfo[row * 4 + 2]), lp);
         const uint32_t lex = ((uint32_t)finfo[row * 4 + 1] << 18) | (uint32_t)ctok[q * M + jj];
@@ -618,7 +646,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     __syncthreads();
     // Top-W survivors of each request (score desc, token path asc) by rank
     if (tid < b * Z) {
-      const int q = tid / Z, z = tid - q * Z;
+      const int q = divZ(tid), z = tid - q * Z;
       const uint64_t kc = ckey[tid];
       const uint64_t *kq = ckey + q * Z;
       int rank = 0;
@@ -626,7 +654,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       if (rank < An) {
         int32_t *si = sinfo + (q * An + rank) * 8;
         si[0] = off + z;                        // node id
-        si[1] = q * A + z / K;                  // parent's row among the current branches
+        si[1] = q * A + divK(z);                // parent's row among the current branches
         si[3] = cmeta[tid];                     // candidate index
         si[4] = (int32_t)clex[tid];
         si[5] = __float_as_int(key_val(kc));    // score
@@ -634,7 +662,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     }
     __syncthreads();
     if (tid < b * An) {
-      const int q = tid / An;
+      const int q = divAn(tid);
       const uint32_t li = (uint32_t)sinfo[tid * 8 + 4];
       int rank = 0;
       pk_scan<uint32_t>(An, [&](int j) { return (uint32_t)sinfo[(q * An + j) * 8 + 4]; },
@@ -645,29 +673,48 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     // node records of this depth, split over the consumers (read by the
     // emission kernel after this one ends)
     {
-      const int per = (b * Z + p.NC - 1) / p.NC;
-      for (int cc = c * per + tid; cc < min(b * Z, (c + 1) * per); cc += blockDim.x) {
-        const int q = cc / Z, z = cc - q * Z;
+      const int per = divNC(b * Z + p.NC - 1);
+      for (int cc = c * per + tid; cc < min(b * Z, (c + 1) * per); cc += PK_THREADS) {
+        const int q = divZ(cc), z = cc - q * Z;
         const size_t id = (size_t)q * p.t.NT + off + z;
         p.t.n_tok[id] = (int32_t)(clex[cc] & 0x3FFFFu);
-        p.t.n_par[id] = finfo[(q * A + z / K) * 4 + 0];
+        p.t.n_par[id] = finfo[(q * A + divK(z)) * 4 + 0];
         p.t.n_dep[id] = dd + 1;
         p.t.n_score[id] = key_val(ckey[cc]);
         p.t.n_lex[id] = clex[cc];
       }
-      for (int i = c + p.NC * tid; i < b * An; i += p.NC * blockDim.x) {
-        const int q = i / An, rk = i - q * An;
+      for (int i = c + p.NC * tid; i < b * An; i += p.NC * PK_THREADS) {
+        const int q = divAn(i), rk = i - q * An;
         p.t.surv_hist[((size_t)q * (D + 1) + dd + 1) * p.t.Wmax + rk] = sinfo[i * 8 + 0];
       }
     }
     if (!more) break;
-    __syncthreads();   // node records above read finfo, rewritten below
+    // the fragment table under red was read before the barriers above
+    // lane holds D[unit 4g + t][column lr]: one 16-byte run per lane
+#pragma unroll
+    for (int mt = 0; mt < 6; ++mt)
+      *reinterpret_cast<f32x4 *>(red + ((wave * 6 + mt) * 16 + lr) * 16 + 4 * g) = acc[mt];
+    __syncthreads();
+    const PkDiv div16r(16 * rows);
+    for (int i = tid; i < 6 * 16 * rows; i += PK_THREADS) {
+      const int mt = div16r(i), rem = i - mt * 16 * rows, row = rem >> 4, u = rem & 15;
+      float v = bhh[(mt >> 1) * PK_CU + (mt & 1) * 16 + u];
+      for (int col = row; col < 16; col += rp) {
+        float w8[PK_WAVES];
+#pragma unroll
+        for (int wv = 0; wv < PK_WAVES; ++wv) w8[wv] = red[((wv * 6 + mt) * 16 + col) * 16 + u];
+#pragma unroll
+        for (int wv = 0; wv < PK_WAVES; ++wv) v += w8[wv];
+      }
+      ghs[(mt * 16 + row) * 16 + u] = v;
+    }
+    __syncthreads();   // also: node records above read finfo, rewritten below
 
     // ---- GRU step of the survivors for this workgroup's 32 units
     const int nrow = b * An;
     if (tid < nrow * PK_CU) {
       const int i = tid / PK_CU, u = tid - i * PK_CU;
-      const int q = i / An;
+      const int q = divAn(i);
       const int pr = sinfo[i * 8 + 1], jc = sinfo[i * 8 + 3];
       const float *a = gis + (q * M + jc) * 3 * PK_CU;
       const int half = u >> 4, ul = u & 15;
@@ -679,7 +726,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       sn_nxt[i * PK_CU + u] = hn;
       pk_put_state(Tnext, c, nrow, i, u, hn);
     }
-    for (int i = tid; i < nrow; i += blockDim.x) {
+    for (int i = tid; i < nrow; i += PK_THREADS) {
       finfo[i * 4 + 0] = sinfo[i * 8 + 0];
       finfo[i * 4 + 1] = sinfo[i * 8 + 6];
       finfo[i * 4 + 2] = sinfo[i * 8 + 5];
@@ -688,7 +735,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     // partial corrected logits of depth dd+1 over this workgroup's units
     float *pn = p.part + ((size_t)((dd + 1) & 1) * p.NC + c) * PK_MAXELL;
     if (tid < nrow * M) {
-      const int i = tid / M, j = tid - i * M, q = i / An;
+      const int i = row0, j = jj0, q = divAn(i);
       const float *gq = gsl + q * PK_CU * M + j;
       const float *sq = sn_nxt + i * PK_CU;
       float acc = 0.f;
@@ -751,7 +798,7 @@ hipError_t launch_corr_tables(int rows, int M, int D, int r, int s, int d, int l
                               const float *uH, float *G, float *g, hipStream_t st) {
   dim3 grid((s + CT_NB - 1) / CT_NB, (rows + 15) / 16);
   const size_t sm = ct_smem(r);
-  hipLaunchKernelGGL(k_corr_tables, grid, dim3(256), sm, st, rows, M, D, r, s, d, ldw1,
+  hipLaunchKernelGGL(k_corr_tables, grid, dim3(CT_THREADS), sm, st, rows, M, D, r, s, d, ldw1,
                      static_cast<const uint16_t *>(W2), static_cast<const uint16_t *>(W1), C, Cl,
                      uH, G, g);
   return hipGetLastError();
