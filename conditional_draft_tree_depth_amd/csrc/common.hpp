@@ -47,23 +47,57 @@ __device__ __forceinline__ uint32_t key_tie(uint64_t k) {
 __device__ __forceinline__ float key_val(uint64_t k) { return ord_f32((uint32_t)(k >> 32)); }
 
 // ---------------------------------------------------------------- wave ops
+// Lane exchanges inside rows of 16 lanes go through DPP (no LDS round trip):
+// 0xB1 = lane ^ 1, 0x4E = lane ^ 2, 0x141 = 7 - lane within 8, 0x140 =
+// 15 - lane within 16; across rows, ds_swizzle 0x401F = lane ^ 16 within 32.
+// For an all-reduce any partner in the other half of a group will do.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int STEP>
+__device__ __forceinline__ uint32_t xchg_u32(uint32_t v) {   // partner for group size 2 STEP
+  if constexpr (STEP == 1) return dpp_u32<0xB1>(v);
+  else if constexpr (STEP == 2) return dpp_u32<0x4E>(v);
+  else if constexpr (STEP == 4) return dpp_u32<0x141>(v);
+  else if constexpr (STEP == 8) return dpp_u32<0x140>(v);
+  else if constexpr (STEP == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+  else return (uint32_t)__shfl_xor((int)v, 32);
+}
+template <int STEP>
+__device__ __forceinline__ float xchg_f32(float v) {
+  return __uint_as_float(xchg_u32<STEP>(__float_as_uint(v)));
+}
+template <int STEP>
+__device__ __forceinline__ uint64_t xchg_u64(uint64_t v) {
+  return ((uint64_t)xchg_u32<STEP>((uint32_t)(v >> 32)) << 32) | xchg_u32<STEP>((uint32_t)v);
+}
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, xchg_f32<1>(v));
+  v = fmaxf(v, xchg_f32<2>(v));
+  v = fmaxf(v, xchg_f32<4>(v));
+  v = fmaxf(v, xchg_f32<8>(v));
+  v = fmaxf(v, xchg_f32<16>(v));
+  return fmaxf(v, xchg_f32<32>(v));
 }
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += xchg_f32<1>(v);
+  v += xchg_f32<2>(v);
+  v += xchg_f32<4>(v);
+  v += xchg_f32<8>(v);
+  v += xchg_f32<16>(v);
+  return v + xchg_f32<32>(v);
 }
+// max over aligned groups of WIDTH lanes (a power of two <= 64)
 template <int WIDTH>
 __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = WIDTH / 2; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor((unsigned long long)v, o, WIDTH);
-    v = w > v ? w : v;
-  }
+  uint64_t w;
+  if constexpr (WIDTH >= 2) { w = xchg_u64<1>(v); v = w > v ? w : v; }
+  if constexpr (WIDTH >= 4) { w = xchg_u64<2>(v); v = w > v ? w : v; }
+  if constexpr (WIDTH >= 8) { w = xchg_u64<4>(v); v = w > v ? w : v; }
+  if constexpr (WIDTH >= 16) { w = xchg_u64<8>(v); v = w > v ? w : v; }
+  if constexpr (WIDTH >= 32) { w = xchg_u64<16>(v); v = w > v ? w : v; }
+  if constexpr (WIDTH >= 64) { w = xchg_u64<32>(v); v = w > v ? w : v; }
   return v;
 }
 

@@ -34,6 +34,9 @@ constexpr int K1_MAXCOLS = K1_WAVES * K1_TPW * 16;  // 1024 tokens per WG
 #ifndef K1_PF
 #define K1_PF 4       // k chunks prefetched per tile
 #endif
+#ifndef K1_CL
+#define K1_CL 0       // lane-contiguous k layout
+#endif
 constexpr int K1F_THREADS = 256;            // fp32 path
 constexpr int K1F_MAXCOLS = 256;
 
@@ -41,8 +44,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 
 // Each half-wave takes one row of the staged logits Ls[row][0..ncols) and
 // writes that row's M best keys (value desc, token asc), best first, to
-// out[row * ostride + m].  Keys within a row are distinct (distinct tokens),
-// so the m-th best is the largest key strictly below the (m-1)-th.
+// out[row * ostride + m].  Keys within a row are distinct (distinct tokens).
+// Every lane keeps its own best EPI_T keys in a short sorted list; each of
+// the M rounds takes the half-wave maximum of the list heads and the winning
+// lane pops its head.  A lane whose list runs dry refills it with its next
+// best keys (those below the last one it gave).
+constexpr int EPI_T = 4;
 template <int MAXC>
 __device__ void wg_topm_epilogue(const float *Ls, int lstride, int ncols, int col0,
                                  int nrow, int M, uint64_t *out, size_t ostride) {
@@ -53,29 +60,49 @@ __device__ void wg_topm_epilogue(const float *Ls, int lstride, int ncols, int co
     const int r = rb + (lane >> 5);
     const bool active = r < nrow;
     uint64_t keys[KPL];
-    uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
       const int c = hl + 32 * i;
       uint64_t k = 0;
       if (active && c < ncols) k = make_key(Ls[r * lstride + c], (uint32_t)(col0 + c));
       keys[i] = k;
-      best = k > best ? k : best;
     }
-    for (int m = 0; m < M; ++m) {
-      const uint64_t top = group_max_u64<32>(best);
-      if (active && hl == 0) out[(size_t)r * ostride + m] = top;
-      if (best == top && top != 0) {
-        uint64_t nb = 0;
+    // best EPI_T keys below `below`, descending (insertion network)
+    uint64_t loc[EPI_T];
+    auto refill = [&](uint64_t below) {
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) {
-          const uint64_t k = keys[i];
-          nb = (k < top && k > nb) ? k : nb;
+      for (int t = 0; t < EPI_T; ++t) loc[t] = 0;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        uint64_t x = keys[i] < below ? keys[i] : 0ull;
+#pragma unroll
+        for (int t = 0; t < EPI_T; ++t) {
+          const uint64_t hi = x > loc[t] ? x : loc[t];
+          x = x > loc[t] ? loc[t] : x;
+          loc[t] = hi;
         }
-        best = nb;
+      }
+    };
+    refill(~0ull);
+    for (int m = 0; m < M; ++m) {
+      const uint64_t top = group_max_u64<32>(loc[0]);
+      if (active && hl == 0) out[(size_t)r * ostride + m] = top;
+      if (loc[0] == top && top != 0) {
+#pragma unroll
+        for (int t = 0; t + 1 < EPI_T; ++t) loc[t] = loc[t + 1];
+        loc[EPI_T - 1] = 0;
+        if (loc[0] == 0) refill(top);
       }
     }
   }
+}
+
+// LDS of the bf16 kernel: the hidden rows [16][d + 8] bf16, later re-used
+// for the logits [16][K1_MAXCOLS] fp32; then the slice's bias.
+__host__ __device__ inline size_t lmhead_smem_body(int d) {
+  const size_t hs = (size_t)16 * (d + 8) * 2;
+  const size_t ls = (size_t)16 * K1_MAXCOLS * 4;
+  return ((hs > ls ? hs : ls) + 15) & ~(size_t)15;
 }
 
 // Tiles [0, ntV) are 16-token slabs of W_lm; when W1 is given, tiles
@@ -83,7 +110,7 @@ __device__ void wg_topm_epilogue(const float *Ls, int lstride, int ncols, int co
 // path-independent projection uH = W1[:, :d] Hq for the same rows (the same
 // B operand), written straight to uH.  A wave keeps TPI tiles in flight and
 // PF 128-wide k chunks of each prefetched in registers.
-template <int TPI, int PF>
+template <int TPI, int PF, int CL>
 __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
     const float *__restrict__ H, int rows, int d, const uint16_t *__restrict__ W, int V,
     const float *__restrict__ bias, int M, uint64_t *__restrict__ part,
@@ -95,11 +122,54 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
   const int HS = d + 8;  // bf16 elements per LDS row (16-byte skew)
   uint16_t *Hs = reinterpret_cast<uint16_t *>(smem);
 
+  const int ntV = (V + 15) >> 4;
+  const int ntU = W1 ? (r + 15) >> 4 : 0;
+  const int T = ntV + ntU;
+  const int t0 = (int)((long long)T * y / P);
+  const int t1 = (int)((long long)T * (y + 1) / P);
+  const int nt = t1 - t0;
+  const int nch = d >> 7;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, g = lane >> 4;
+  // CL: lane group g takes k = 32 j + 8 g + (0..7) of MFMA j (a row's four
+  // lanes read 64 contiguous bytes per load); else k = 32 g + 8 j + (0..7)
+  const uint16_t *hp = Hs + lr * HS + g * (CL ? 8 : 32);
+  const uint4 *ptr[TPI];
+  uint4 ring[PF][TPI][4];
+  // pointers of the tiles lt0 + K1_WAVES u and the first PF chunks of them
+  auto start_tiles = [&](int lt0) {
+#pragma unroll
+    for (int u = 0; u < TPI; ++u) {
+      const int lt = lt0 + K1_WAVES * u < nt ? lt0 + K1_WAVES * u : lt0;
+      const int tt = t0 + lt;
+      const uint16_t *rp = tt < ntV ? W + (size_t)min(tt * 16 + lr, V - 1) * d
+                                    : W1 + (size_t)min((tt - ntV) * 16 + lr, r - 1) * ldw1;
+      ptr[u] = reinterpret_cast<const uint4 *>(rp + g * (CL ? 8 : 32));
+    }
+#pragma unroll
+    for (int pp = 0; pp < PF; ++pp)
+      if (pp < nch) {
+#pragma unroll
+        for (int u = 0; u < TPI; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ring[pp][u][j] = ptr[u][pp * 16 + j * (CL ? 4 : 1)];
+      }
+  };
+  // the first tiles' loads are in flight while the hidden rows are staged
+  if (wave < nt) start_tiles(wave);
+
+  // bias of this slice's vocabulary columns, staged once (behind the larger
+  // of the hidden-row and logit buffers)
+  float *bs = reinterpret_cast<float *>(smem + lmhead_smem_body(d));
+  {
+    const int c0 = t0 * 16, nc = min(min(t1, ntV) * 16, V) - c0;
+    for (int c = threadIdx.x; c < nc; c += K1_WAVES * 64) bs[c] = bias ? bias[c0 + c] : 0.f;
+  }
   // Hq = bf16_rne(H) for the 16 rows of this block (zeros past `rows`)
   {
     const int q4 = d >> 2;   // float4 per row
 #pragma unroll 4
-    for (int i = threadIdx.x; i < 16 * q4; i += blockDim.x) {
+    for (int i = threadIdx.x; i < 16 * q4; i += K1_WAVES * 64) {
       const int rr = i / q4, k = (i - rr * q4) * 4;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (rr < nrow) v = *reinterpret_cast<const float4 *>(H + (size_t)(row0 + rr) * d + k);
@@ -110,43 +180,15 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
   }
   __syncthreads();
 
-  const int ntV = (V + 15) >> 4;
-  const int ntU = W1 ? (r + 15) >> 4 : 0;
-  const int T = ntV + ntU;
-  const int t0 = (int)((long long)T * y / P);
-  const int t1 = (int)((long long)T * (y + 1) / P);
-  const int nt = t1 - t0;
-  const int nch = d >> 7;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lr = lane & 15, g = lane >> 4;
-  const uint16_t *hp = Hs + lr * HS + g * 32;
-
   float vals[K1_TPW][4];
 #pragma unroll
   for (int i = 0; i < K1_TPW; i += TPI) {
     const int lt0 = wave + K1_WAVES * i;
     if (lt0 < nt) {
-      const uint4 *ptr[TPI];
-#pragma unroll
-      for (int u = 0; u < TPI; ++u) {
-        const int lt = lt0 + K1_WAVES * u < nt ? lt0 + K1_WAVES * u : lt0;
-        const int tt = t0 + lt;
-        const uint16_t *rp = tt < ntV ? W + (size_t)min(tt * 16 + lr, V - 1) * d
-                                      : W1 + (size_t)min((tt - ntV) * 16 + lr, r - 1) * ldw1;
-        ptr[u] = reinterpret_cast<const uint4 *>(rp + g * 32);
-      }
+      if (i > 0) start_tiles(lt0);
       f32x4 acc[TPI];
-      uint4 ring[PF][TPI][4];
 #pragma unroll
       for (int u = 0; u < TPI; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int pp = 0; pp < PF; ++pp)
-        if (pp < nch) {
-#pragma unroll
-          for (int u = 0; u < TPI; ++u)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ring[pp][u][j] = ptr[u][pp * 16 + j];
-        }
       for (int c0 = 0; c0 < nch; c0 += PF) {
 #pragma unroll
         for (int pp = 0; pp < PF; ++pp) {
@@ -155,7 +197,7 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
             const uint4 *h4 = reinterpret_cast<const uint4 *>(hp + c * 128);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const bf16x8 hb = as_bf16x8(h4[j]);
+              const bf16x8 hb = as_bf16x8(h4[j * (CL ? 4 : 1)]);
 #pragma unroll
               for (int u = 0; u < TPI; ++u)
                 acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[pp][u][j]), hb,
@@ -165,7 +207,7 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
 #pragma unroll
               for (int u = 0; u < TPI; ++u)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) ring[pp][u][j] = ptr[u][(c + PF) * 16 + j];
+                for (int j = 0; j < 4; ++j) ring[pp][u][j] = ptr[u][(c + PF) * 16 + j * (CL ? 4 : 1)];
             }
           }
         }
@@ -191,7 +233,7 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
           if (tt < ntV) {
             const int c = lt * 16 + 4 * g + t;
             const int v = t0 * 16 + c;
-            if (v < V) Ls[lr * LSTR + c] = vals[i][t] + (bias ? bias[v] : 0.f);
+            if (v < V) Ls[lr * LSTR + c] = vals[i][t] + bs[c];
           } else {
             const int uc = (tt - ntV) * 16 + 4 * g + t;
             if (uc < r) uH[(size_t)(row0 + lr) * r + uc] = vals[i][t];
@@ -307,9 +349,7 @@ int lmhead_partitions(int V, int wtype, int extra_tiles) {
 
 size_t lmhead_smem(int d, int wtype) {
   if (wtype != WT_BF16) return 0;
-  const size_t hs = (size_t)16 * (d + 8) * 2;
-  const size_t ls = (size_t)16 * K1_MAXCOLS * 4;
-  return hs > ls ? hs : ls;
+  return lmhead_smem_body(d) + (size_t)K1_MAXCOLS * 4;
 }
 
 hipError_t lmhead_prepare(int wtype, size_t smem) {
@@ -317,14 +357,14 @@ hipError_t lmhead_prepare(int wtype, size_t smem) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)(K1B_CAP * sizeof(uint64_t)));
   if (e != hipSuccess || wtype != WT_BF16) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k1_lmhead_bf16<K1_TPI, K1_PF>),
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k1_lmhead_bf16<K1_TPI, K1_PF, K1_CL>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
 }
 
 hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st) {
   dim3 grid((a.rows + 15) / 16, a.P);
   if (a.wtype == WT_BF16) {
-    hipLaunchKernelGGL((k1_lmhead_bf16<K1_TPI, K1_PF>), grid, dim3(K1_WAVES * 64),
+    hipLaunchKernelGGL((k1_lmhead_bf16<K1_TPI, K1_PF, K1_CL>), grid, dim3(K1_WAVES * 64),
                        lmhead_smem(a.d, a.wtype), st, a.H, a.rows, a.d,
                        static_cast<const uint16_t *>(a.W), a.V, a.bias, a.M, a.part,
                        static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH);

@@ -258,21 +258,16 @@ struct PkDiv {
   }
 };
 
-// Lane exchange within rows of 16 lanes (no LDS round trip).
-template <int CTRL>
-__device__ __forceinline__ int pk_dpp(int v) {
-  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
-}
 // All-reduce of v over aligned groups of n lanes (n a power of two <= 64);
 // every lane of a group ends with the same bits for a commutative op.
 template <class Op>
 __device__ __forceinline__ float pk_group_reduce(float v, int n, Op op) {
-  if (n >= 2) v = op(v, __int_as_float(pk_dpp<0xB1>(__float_as_int(v))));    // lane ^ 1
-  if (n >= 4) v = op(v, __int_as_float(pk_dpp<0x4E>(__float_as_int(v))));    // lane ^ 2
-  if (n >= 8) v = op(v, __int_as_float(pk_dpp<0x141>(__float_as_int(v))));   // 7 - lane in 8
-  if (n >= 16) v = op(v, __int_as_float(pk_dpp<0x140>(__float_as_int(v))));  // 15 - lane in 16
-  if (n >= 32) v = op(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
-  if (n >= 64) v = op(v, __shfl_xor(v, 32));
+  if (n >= 2) v = op(v, xchg_f32<1>(v));
+  if (n >= 4) v = op(v, xchg_f32<2>(v));
+  if (n >= 8) v = op(v, xchg_f32<4>(v));
+  if (n >= 16) v = op(v, xchg_f32<8>(v));
+  if (n >= 32) v = op(v, xchg_f32<16>(v));
+  if (n >= 64) v = op(v, xchg_f32<32>(v));
   return v;
 }
 
@@ -303,7 +298,7 @@ __device__ __forceinline__ void pk_put_state(uint16_t *T, int c, int rows, int r
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
     const uint32_t mine = t3[t];
-    const uint32_t other = (uint32_t)pk_dpp<0xB1>((int)mine);   // unit u ^ 1
+    const uint32_t other = xchg_u32<1>(mine);   // unit u ^ 1
     if ((u & 1) == 0) {
       uint32_t *dst = reinterpret_cast<uint32_t *>(T + ((size_t)(c * np * 16 + t * rp + row) * 32 + u));
       __hip_atomic_store(dst, mine | (other << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
