@@ -37,6 +37,7 @@ constexpr int K1_MAXCOLS = K1_WAVES * K1_TPW * 16;  // 1024 tokens per WG
 #ifndef K1_CL
 #define K1_CL 0       // lane-contiguous k layout
 #endif
+constexpr int K1_GROUP = 16;                // workgroups per first-level merge
 constexpr int K1F_THREADS = 256;            // fp32 path
 constexpr int K1F_MAXCOLS = 256;
 
@@ -86,7 +87,9 @@ __device__ void wg_topm_epilogue(const float *Ls, int lstride, int ncols, int co
     refill(~0ull);
     for (int m = 0; m < M; ++m) {
       const uint64_t top = group_max_u64<32>(loc[0]);
-      if (active && hl == 0) out[(size_t)r * ostride + m] = top;
+      if (active && hl == 0)   // read by another workgroup: device-coherent store
+        __hip_atomic_store(out + (size_t)r * ostride + m, top, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       if (loc[0] == top && top != 0) {
 #pragma unroll
         for (int t = 0; t + 1 < EPI_T; ++t) loc[t] = loc[t + 1];
@@ -95,6 +98,60 @@ __device__ void wg_topm_epilogue(const float *Ls, int lstride, int ncols, int co
       }
     }
   }
+}
+
+// Top-M merge of at most 16 sorted lists per row.  For each of nr rows,
+// lists 0 .. nl-1 (descending, M keys, 0 = empty) sit at src + row * rstride
+// + list * lstride (written by other workgroups: read with device-coherent
+// loads) and are staged in LDS.  Sixteen lanes take a row, one list each,
+// with the list's next four keys in registers; each of the M rounds takes
+// the 16-lane maximum (DPP only) and the winning lane pops its head and
+// fetches the key four places further on from LDS.  emit(row, m, key) gets
+// the row's m-th best key.  At most 4 * waves rows per call; all threads of
+// the block call it.
+constexpr int K1_MLISTS = 16;
+template <class Emit>
+__device__ void lds_merge_lists(uint64_t *L, const uint64_t *src, size_t rstride, int lstride,
+                                int nl, int nr, int M, Emit emit) {
+  const int tid = threadIdx.x;
+  constexpr int NT = K1_WAVES * 64;
+  const int tot = nr * K1_MLISTS * M;
+  for (int i0 = tid; i0 < tot; i0 += 8 * NT) {   // 8 loads in flight per thread
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * NT, rl = i / M, k = i - rl * M, row = rl / K1_MLISTS;
+      const int l = rl - row * K1_MLISTS;
+      v[u] = 0ull;
+      if (i < tot && l < nl)
+        v[u] = __hip_atomic_load(src + row * rstride + (size_t)l * lstride + k, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u * NT < tot) L[i0 + u * NT] = v[u];
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int row = wave * 4 + (lane >> 4), li = lane & 15;
+  const bool act = row < nr;
+  const uint64_t *lst = L + ((size_t)(act ? row : 0) * K1_MLISTS + li) * M;
+  uint64_t buf[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) buf[t] = (act && t < M) ? lst[t] : 0ull;
+  int cur = 0;   // index of buf[0] in the list
+  for (int m = 0; m < M; ++m) {
+    const uint64_t top = group_max_u64<16>(buf[0]);
+    if (act && li == 0) emit(row, m, top);
+    if (buf[0] == top && top != 0) {
+      buf[0] = buf[1];
+      buf[1] = buf[2];
+      buf[2] = buf[3];
+      ++cur;
+      buf[3] = cur + 3 < M ? lst[cur + 3] : 0ull;
+    }
+  }
+  __syncthreads();
 }
 
 // LDS of the bf16 kernel: the hidden rows [16][d + 8] bf16, later re-used
@@ -114,7 +171,9 @@ template <int TPI, int PF, int CL>
 __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
     const float *__restrict__ H, int rows, int d, const uint16_t *__restrict__ W, int V,
     const float *__restrict__ bias, int M, uint64_t *__restrict__ part,
-    const uint16_t *__restrict__ W1, int ldw1, int r, float *__restrict__ uH) {
+    const uint16_t *__restrict__ W1, int ldw1, int r, float *__restrict__ uH,
+    uint32_t *__restrict__ cnt, uint64_t *__restrict__ part2, int32_t *__restrict__ C,
+    float *__restrict__ Cl) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int P = gridDim.y, y = blockIdx.y;
   const int row0 = blockIdx.x * 16;
@@ -247,6 +306,54 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
   const int ncols = vend > t0 * 16 ? vend - t0 * 16 : 0;
   wg_topm_epilogue<K1_MAXCOLS>(Ls, LSTR, ncols, t0 * 16, nrow, M,
                                part + ((size_t)row0 * P + y) * M, (size_t)P * M);
+  if (!cnt) return;
+
+  // Fused merge.  Workgroups y come in groups of K1_GROUP; the last one of a
+  // group to finish (counted by an ever-growing counter: every round adds the
+  // group size) merges the group's lists into part2, and the last group
+  // merger of this row block merges the groups' lists into C / Cl.  Lists
+  // travel through device-coherent stores and loads; each thread's stores
+  // have completed before its workgroup counts itself in.
+  const int NG = (P + K1_GROUP - 1) / K1_GROUP, grp = y / K1_GROUP;
+  const int gsz = min(K1_GROUP, P - grp * K1_GROUP);
+  uint32_t *cb = cnt + (size_t)blockIdx.x * (NG + 1);
+  int *flag = reinterpret_cast<int *>(bs);
+  uint64_t *L = reinterpret_cast<uint64_t *>(smem);
+  // rows per merge call: the staged lists fit in LDS, 4 rows per wave
+  const int rpb = min(4 * K1_WAVES, max(1, (int)(lmhead_smem_body(d) / 8) / (K1_MLISTS * M)));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(cb + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag[0] = (old + 1) % (uint32_t)gsz == 0;
+  }
+  __syncthreads();
+  if (!flag[0]) return;
+  for (int rb = 0; rb < nrow; rb += rpb) {
+    const int nr = min(rpb, nrow - rb);
+    lds_merge_lists(L, part + ((size_t)(row0 + rb) * P + grp * K1_GROUP) * M, (size_t)P * M, M,
+                    gsz, nr, M, [&](int rr, int m, uint64_t key) {
+                      __hip_atomic_store(part2 + ((size_t)(row0 + rb + rr) * NG + grp) * M + m, key,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    });
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(cb + NG, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag[0] = (old + 1) % (uint32_t)NG == 0;
+  }
+  __syncthreads();
+  if (!flag[0]) return;
+  for (int rb = 0; rb < nrow; rb += rpb) {
+    const int nr = min(rpb, nrow - rb);
+    lds_merge_lists(L, part2 + (size_t)(row0 + rb) * NG * M, (size_t)NG * M, M, NG, nr, M,
+                    [&](int rr, int m, uint64_t key) {
+                      const size_t o = (size_t)(row0 + rb + rr) * M + m;
+                      C[o] = key ? (int32_t)key_tie(key) : -1;
+                      Cl[o] = key_val(key);
+                    });
+  }
 }
 
 // fp32 weights: plain VALU dot products (small workloads only).
@@ -347,6 +454,12 @@ int lmhead_partitions(int V, int wtype, int extra_tiles) {
   return P;
 }
 
+bool lmhead_fused_merge(int P, int M, int d, int wtype) {
+  if (wtype != WT_BF16 || (P + K1_GROUP - 1) / K1_GROUP > K1_MLISTS) return false;
+  return (size_t)K1_MLISTS * M * 8 <= lmhead_smem_body(d);
+}
+int lmhead_groups(int P) { return (P + K1_GROUP - 1) / K1_GROUP; }
+
 size_t lmhead_smem(int d, int wtype) {
   if (wtype != WT_BF16) return 0;
   return lmhead_smem_body(d) + (size_t)K1_MAXCOLS * 4;
@@ -367,7 +480,8 @@ hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((k1_lmhead_bf16<K1_TPI, K1_PF, K1_CL>), grid, dim3(K1_WAVES * 64),
                        lmhead_smem(a.d, a.wtype), st, a.H, a.rows, a.d,
                        static_cast<const uint16_t *>(a.W), a.V, a.bias, a.M, a.part,
-                       static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH);
+                       static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH, a.cnt, a.part2,
+                       a.C, a.Cl);
   } else {
     hipLaunchKernelGGL(k1_lmhead_f32, grid, dim3(K1F_THREADS), 0, st, a.H, a.rows, a.d,
                        static_cast<const float *>(a.W), a.V, a.bias, a.M, a.part);

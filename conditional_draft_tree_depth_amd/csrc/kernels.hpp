@@ -21,7 +21,15 @@ struct LMHeadArgs {
   const void *W1;      // bf16 only: W1[:, :d] rows ride along -> uH (or null)
   int ldw1, r;
   float *uH;           // [rows, r]
+  // bf16 only, when lmhead_fused_merge(): the kernel also merges the lists
+  // into C / Cl (else null and launch_topm_merge does it)
+  uint32_t *cnt;       // [row blocks][lmhead_groups(P) + 1], zeroed once, never reset
+  uint64_t *part2;     // [rows, lmhead_groups(P), M]
+  int32_t *C;          // [rows, M]
+  float *Cl;           // [rows, M]
 };
+bool lmhead_fused_merge(int P, int M, int d, int wtype);
+int lmhead_groups(int P);
 int lmhead_partitions(int V, int wtype, int extra_tiles);
 size_t lmhead_smem(int d, int wtype);
 hipError_t lmhead_prepare(int wtype, size_t smem);
