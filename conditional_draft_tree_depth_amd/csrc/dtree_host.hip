@@ -35,6 +35,7 @@ struct Ws {
   uint32_t *status = nullptr;
   // persistent depth loop: correction tables, partial sums, arrival flags
   float *G = nullptr, *g = nullptr, *pk_part = nullptr, *gitab = nullptr, *pk_terms = nullptr;
+  uint16_t *w1t = nullptr;   // W1[:, d:]^T, padded (correction tables)
   uint32_t *flags = nullptr;
 };
 
@@ -107,7 +108,7 @@ void free_ws(Ws &ws) {
   void *ptrs[] = {ws.part, ws.part2, ws.k1cnt, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.u, ws.ell, ws.gi, ws.gh,
                   ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
-                  ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.flags};
+                  ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   ws = Ws();
@@ -216,7 +217,9 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   A(alloc(&ws.sel, (size_t)c.max_batch * c.max_B));
   A(alloc(&ws.status, 1));
   // the persistent depth loop needs bf16 weights and MFMA-friendly GRU sizes
-  ctx->pk = w->wtype == DTREE_BF16 && s % 128 == 0 && w->e % 128 == 0 &&
+  auto al16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  ctx->pk = w->wtype == DTREE_BF16 && s % 128 == 0 && w->e % 128 == 0 && al16(w->Emb) &&
+            al16(w->W_ih) && al16(w->W_hh) && al16(w->W2) &&
             persist_eligible(1, c.max_D, 1, 1, 1, s, w->e, r, WT_BF16, ctx->lds_max);
   if (ctx->pk) {
     const int cand = c.max_batch * c.max_M < 64 ? c.max_batch * c.max_M : 64;
@@ -226,6 +229,8 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
     A(alloc(&ws.pk_part, persist_part_floats(s)));
     A(alloc(&ws.gitab, persist_gitab_floats(s, c.max_D)));
     A(alloc(&ws.pk_terms, 2 * persist_terms_floats(s)));
+    A(alloc(&ws.w1t, corr_w1t_elems(s, r)));
+    if (e == hipSuccess) A(launch_transpose_w1s(w->W1, r, s, w->d, w->d + s, ws.w1t, nullptr));
     A(alloc(&ws.flags, persist_flag_words(s)));
     if (e == hipSuccess) A(hipMemset(ws.flags, 0, persist_flag_words(s) * 4));
     if (e == hipSuccess) A(hipDeviceSynchronize());
@@ -278,6 +283,19 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   const size_t esz = wt == WT_BF16 ? 2 : 4;
   ctx->has_round = false;
 
+  // round start (done inside the LM-head kernel)
+  TreeBufs tb{};
+  tb.NT = ctx->NTcap;
+  tb.V = w.V;
+  tb.Wmax = c.max_W;
+  tb.n_tok = ws.n_tok; tb.n_par = ws.n_par; tb.n_dep = ws.n_dep;
+  tb.n_score = ws.n_score; tb.n_lex = ws.n_lex;
+  tb.surv_hist = ws.surv_hist; tb.gidx_tok = ws.gidx_tok; tb.gidx_par = ws.gidx_par;
+  tb.sel = ws.sel; tb.status = ws.status;
+  int cur = 0;
+  tb.surv_node = ws.surv[0]; tb.surv_rank = ws.rank[0];
+  tb.nsurv_node = ws.surv[1]; tb.nsurv_rank = ws.rank[1];
+
   // K1 + K1b: candidate tables
   prof_mark(ctx, 0, st);
   // bf16: the LM-head kernel also produces uH = W1[:, :d] . Hq (same operand)
@@ -286,7 +304,7 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   const bool fuse_merge = lmhead_fused_merge(ctx->P, M, d, wt);
   LMHeadArgs la{H, rows, d, w.W_lm, wt, w.V, w.lm_bias, M, ctx->P, ws.part,
                 fuse_uH ? w.W1 : nullptr, d + s, r, ws.uH,
-                fuse_merge ? ws.k1cnt : nullptr, ws.part2, ws.C, ws.Cl};
+                fuse_merge ? ws.k1cnt : nullptr, ws.part2, ws.C, ws.Cl, root, batch, D + 1, tb};
   HIPCHK(ctx, launch_lmhead(la, st));
   prof_mark(ctx, 1, st);
   if (!fuse_merge) HIPCHK(ctx, launch_topm_merge(ws.part, ctx->P, M, rows, ws.C, ws.Cl, st));
@@ -299,18 +317,6 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
     HIPCHK(ctx, launch_gemm(g, st));
   }
 
-  TreeBufs tb{};
-  tb.NT = ctx->NTcap;
-  tb.V = w.V;
-  tb.Wmax = c.max_W;
-  tb.n_tok = ws.n_tok; tb.n_par = ws.n_par; tb.n_dep = ws.n_dep;
-  tb.n_score = ws.n_score; tb.n_lex = ws.n_lex;
-  tb.surv_hist = ws.surv_hist; tb.gidx_tok = ws.gidx_tok; tb.gidx_par = ws.gidx_par;
-  tb.sel = ws.sel; tb.status = ws.status;
-  int cur = 0;
-  tb.surv_node = ws.surv[0]; tb.surv_rank = ws.rank[0];
-  tb.nsurv_node = ws.surv[1]; tb.nsurv_rank = ws.rank[1];
-  HIPCHK(ctx, launch_init_round(batch, root, tb, D + 1, st));
 
   const bool pk = ctx->pk && batch * M <= 64 && batch * D * M <= ctx->pk_rows &&
                   persist_eligible(batch, D, M, K, W, s, w.e, r, wt, ctx->lds_max);
@@ -318,8 +324,8 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   if (pk) {
     // correction tables G = W2[C] W1[:, d:], g = Cl + W2[C] uH, then the
     // whole depth loop as one cooperative launch
-    HIPCHK(ctx, launch_corr_tables(batch * D * M, M, D, r, s, d, d + s, w.W2, w.W1, ws.C, ws.Cl,
-                                   ws.uH, ws.G, ws.g, st));
+    HIPCHK(ctx, launch_corr_tables(batch * D * M, M, r, s, w.W2, ws.w1t, ws.C, ws.Cl, ws.uH,
+                                   ws.G, ws.g, st));
     prof_mark(ctx, 3, st);
     PersistArgs pa{batch, D, M, K, W, s, w.e, w.V, w.W_ih, w.W_hh, w.Emb, w.b_ih, w.b_hh,
                    ws.C, root, ws.G, ws.g, ws.pk_terms, ws.pk_terms + persist_terms_floats(s),

@@ -16,33 +16,6 @@ constexpr int SEL_THREADS = 256;
 constexpr int SEL_MAXZ = 1024;   // children per request and depth
 constexpr int SEL_MAXW = 512;
 
-__global__ void k_init_round(int b, const int32_t *__restrict__ root, TreeBufs t, int Dp1) {
-  const int q = blockIdx.x;
-  for (int i = threadIdx.x; i < Dp1 * t.Wmax; i += blockDim.x)
-    t.surv_hist[(size_t)q * Dp1 * t.Wmax + i] = -1;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const size_t n0 = (size_t)q * t.NT;
-    const int32_t rt = root[q] < 0 ? 0 : (root[q] >= t.V ? t.V - 1 : root[q]);
-    t.n_tok[n0] = rt;
-    t.n_par[n0] = -1;
-    t.n_dep[n0] = 0;
-    t.n_score[n0] = 0.f;
-    t.n_lex[n0] = 0u;
-    t.surv_node[(size_t)q * t.Wmax] = 0;
-    t.surv_rank[(size_t)q * t.Wmax] = 0;
-    t.surv_hist[(size_t)q * Dp1 * t.Wmax] = 0;
-    t.gidx_tok[q] = rt;
-    if (q == 0) *t.status = 0u;
-  }
-}
-
-hipError_t launch_init_round(int b, const int32_t *root, const TreeBufs &t, int Dp1,
-                             hipStream_t st) {
-  hipLaunchKernelGGL(k_init_round, dim3(b), dim3(256), 0, st, b, root, t, Dp1);
-  return hipGetLastError();
-}
-
 // Corrected logits of the depth's candidates for every expanded branch:
 //   ell[a][j] = Cl[j] + W2[C[j]] . u_a
 // ("Resumen Técnico: Domino", Methodology 2: L = L_base + Delta L with the

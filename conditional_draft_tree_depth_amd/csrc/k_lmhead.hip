@@ -173,9 +173,11 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
     const float *__restrict__ bias, int M, uint64_t *__restrict__ part,
     const uint16_t *__restrict__ W1, int ldw1, int r, float *__restrict__ uH,
     uint32_t *__restrict__ cnt, uint64_t *__restrict__ part2, int32_t *__restrict__ C,
-    float *__restrict__ Cl) {
+    float *__restrict__ Cl, const int32_t *__restrict__ root, int b, int Dp1, TreeBufs tb) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int P = gridDim.y, y = blockIdx.y;
+  if (root && blockIdx.x == 0)
+    for (int q = y; q < b; q += P) init_round_request(q, root, tb, Dp1, threadIdx.x, K1_WAVES * 64);
   const int row0 = blockIdx.x * 16;
   const int nrow = min(16, rows - row0);
   const int HS = d + 8;  // bf16 elements per LDS row (16-byte skew)
@@ -359,9 +361,12 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
 // fp32 weights: plain VALU dot products (small workloads only).
 __global__ __launch_bounds__(K1F_THREADS) void k1_lmhead_f32(
     const float *__restrict__ H, int rows, int d, const float *__restrict__ W, int V,
-    const float *__restrict__ bias, int M, uint64_t *__restrict__ part) {
+    const float *__restrict__ bias, int M, uint64_t *__restrict__ part,
+    const int32_t *__restrict__ root, int b, int Dp1, TreeBufs tb) {
   __shared__ float Ls[16 * K1F_MAXCOLS];
   const int P = gridDim.y, y = blockIdx.y;
+  if (root && blockIdx.x == 0)
+    for (int q = y; q < b; q += P) init_round_request(q, root, tb, Dp1, threadIdx.x, K1F_THREADS);
   const int row0 = blockIdx.x * 16;
   const int nrow = min(16, rows - row0);
   const int ntiles = (V + 15) >> 4;
@@ -481,10 +486,11 @@ hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st) {
                        lmhead_smem(a.d, a.wtype), st, a.H, a.rows, a.d,
                        static_cast<const uint16_t *>(a.W), a.V, a.bias, a.M, a.part,
                        static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH, a.cnt, a.part2,
-                       a.C, a.Cl);
+                       a.C, a.Cl, a.root, a.b, a.Dp1, a.t);
   } else {
     hipLaunchKernelGGL(k1_lmhead_f32, grid, dim3(K1F_THREADS), 0, st, a.H, a.rows, a.d,
-                       static_cast<const float *>(a.W), a.V, a.bias, a.M, a.part);
+                       static_cast<const float *>(a.W), a.V, a.bias, a.M, a.part, a.root, a.b,
+                       a.Dp1, a.t);
   }
   return hipGetLastError();
 }

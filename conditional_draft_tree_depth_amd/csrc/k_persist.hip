@@ -35,52 +35,46 @@ __device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
 
 // ---------------------------------------------------------------- tables
 // One workgroup: 16 candidate rows (flattened (request, depth, j)) x 64 state
-// columns, on MFMA: A = the candidates' W2 rows, B = W1[:, d + n] (staged
-// transposed in LDS so each lane reads 8 consecutive k), fp32 sums over the
-// rank r (zero-padded to a multiple of 32).  The workgroups of column block 0
-// also produce g = Cl + W2[C] . uH (one wave per row, fp32).
+// columns, on MFMA with fragments read straight from global memory: A = the
+// candidates' W2 rows (gathered by token), B = W1t rows, W1t = W1[:, d:]^T
+// zero-padded to a multiple of 32 in the rank (made once per context), fp32
+// sums over the rank.  The workgroups of column block 0 also produce
+// g = Cl + W2[C] . uH (one wave per row, fp32).
 constexpr int CT_NB = 64;   // state columns per workgroup
 constexpr int CT_THREADS = 256;
+constexpr int CT_MAXKS = 16;   // rank <= 512
 
-__host__ __device__ inline size_t ct_smem(int r) {
-  const int rp = (r + 31) & ~31;
-  return (size_t)(CT_NB + 16) * (rp + 8) * 2;
-}
-
-__global__ __launch_bounds__(CT_THREADS) void k_corr_tables(int rows, int M, int D, int r, int s, int d,
-                                                     int ldw1, const uint16_t *__restrict__ W2,
-                                                     const uint16_t *__restrict__ W1,
+__global__ __launch_bounds__(CT_THREADS) void k_corr_tables(int rows, int M, int r, int s,
+                                                     const uint16_t *__restrict__ W2,
+                                                     const uint16_t *__restrict__ W1t,
                                                      const int32_t *__restrict__ C,
                                                      const float *__restrict__ Cl,
                                                      const float *__restrict__ uH,
                                                      float *__restrict__ G, float *__restrict__ g) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const int rp = (r + 31) & ~31, KS = rp + 8;
-  uint16_t *w1t = reinterpret_cast<uint16_t *>(smem);          // [CT_NB][KS]: W1[k][d + n0 + n]
-  uint16_t *w2s = w1t + CT_NB * KS;                            // [16][KS]:   W2[C[row]][k]
+  const int rp = (r + 31) & ~31, nks = rp >> 5;
   const int row0 = blockIdx.y * 16, n0 = blockIdx.x * CT_NB, tid = threadIdx.x;
-  for (int i = tid; i < rp * CT_NB; i += CT_THREADS) {
-    const int k = i / CT_NB, n = i - k * CT_NB;
-    w1t[n * KS + k] = (k < r && n0 + n < s) ? W1[(size_t)k * ldw1 + d + n0 + n] : (uint16_t)0;
-  }
-  for (int i = tid; i < 16 * rp; i += CT_THREADS) {
-    const int rr = i / rp, k = i - rr * rp, row = row0 + rr;
-    uint16_t v = 0;
-    if (row < rows && k < r) v = W2[(size_t)(C[row] < 0 ? 0 : C[row]) * r + k];
-    w2s[rr * KS + k] = v;
-  }
-  __syncthreads();
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, gq = lane >> 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int ks = 0; ks < rp / 32; ++ks) {
-    const uint4 a = *reinterpret_cast<const uint4 *>(w2s + lr * KS + ks * 32 + gq * 8);
-    const uint4 bv = *reinterpret_cast<const uint4 *>(w1t + (wave * 16 + lr) * KS + ks * 32 + gq * 8);
-    acc = mfma(a, bv, acc);
+  const int arow = row0 + lr;
+  const int tok = arow < rows ? max(C[arow], 0) : -1;
+  const int n = n0 + wave * 16 + lr;
+  uint4 a[CT_MAXKS], bv[CT_MAXKS];
+#pragma unroll
+  for (int ks = 0; ks < CT_MAXKS; ++ks) {
+    const int k = ks * 32 + gq * 8;
+    a[ks] = make_uint4(0u, 0u, 0u, 0u);
+    bv[ks] = a[ks];
+    if (ks < nks) {
+      if (tok >= 0 && k < r) a[ks] = *reinterpret_cast<const uint4 *>(W2 + (size_t)tok * r + k);
+      if (n < s) bv[ks] = *reinterpret_cast<const uint4 *>(W1t + (size_t)n * rp + k);
+    }
   }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < CT_MAXKS; ++ks)
+    if (ks < nks) acc = mfma(a[ks], bv[ks], acc);
   // lane holds D[row 4 gq + t][column wave*16 + lr]; G is stored
   // [request * D + depth][state unit][candidate] so that a run of state units
   // of one depth is one contiguous block
-  const int n = n0 + wave * 16 + lr;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int row = row0 + 4 * gq + t;
@@ -90,16 +84,27 @@ __global__ __launch_bounds__(CT_THREADS) void k_corr_tables(int rows, int M, int
     }
   }
   if (blockIdx.x == 0) {
-    for (int rr = wave; rr < 16; rr += 4) {
+    for (int rr = wave; rr < 16; rr += CT_THREADS / 64) {
       const int row = row0 + rr;
       if (row >= rows) continue;
+      const uint16_t *w2 = W2 + (size_t)max(C[row], 0) * r;
       const float *uh = uH + (size_t)(row / M) * r;   // row / M = request * D + depth
       float part = 0.f;
-      for (int k = lane; k < r; k += 64) part += bf16_bits_to_f32(w2s[rr * KS + k]) * uh[k];
+      for (int k = lane; k < r; k += 64) part += bf16_bits_to_f32(w2[k]) * uh[k];
       part = wave_sum_f32(part);
       if (lane == 0) g[row] = Cl[row] + part;
     }
   }
+}
+
+// W1t[n][k] = W1[k][d + n] for k < r, zero for r <= k < rp
+__global__ void k_transpose_w1s(const uint16_t *__restrict__ W1, int r, int s, int d, int ldw1,
+                                uint16_t *__restrict__ W1t) {
+  const int rp = (r + 31) & ~31;
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i >= (size_t)s * rp) return;
+  const int n = (int)(i / rp), k = (int)(i - (size_t)n * rp);
+  W1t[i] = k < r ? W1[(size_t)k * ldw1 + d + n] : (uint16_t)0;
 }
 
 // ---------------------------------------------------------------- persistent
@@ -769,7 +774,7 @@ bool persist_eligible(int b, int D, int M, int K, int W, int s, int e, int r, in
   if (s > 32 * PK_HKS * PK_WAVES || e > 32 * PK_KSW * PK_WAVES || D > PK_MAXD) return false;
   if (b * W > PK_ROWS || b * M > PK_MAXC || (long long)b * W * M > PK_MAXELL) return false;
   if ((long long)b * W * K > PK_MAXZ) return false;
-  if (r > 512) return false;   // the correction-table tile must fit in LDS
+  if (r > 32 * CT_MAXKS || r % 8) return false;   // correction-table fragments
   return pk_layout().total <= lds_max;
 }
 
@@ -780,21 +785,27 @@ size_t persist_terms_floats(int s) { return (size_t)(s / 32) * PK_SLOTS * 32 / 2
 
 hipError_t persist_prepare(int s) {
   (void)s;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_depth_persistent),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)pk_layout().total);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_corr_tables),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ct_smem(512));
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_depth_persistent),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)pk_layout().total);
 }
 
-hipError_t launch_corr_tables(int rows, int M, int D, int r, int s, int d, int ldw1,
-                              const void *W2, const void *W1, const int32_t *C, const float *Cl,
-                              const float *uH, float *G, float *g, hipStream_t st) {
+size_t corr_w1t_elems(int s, int r) { return (size_t)s * ((r + 31) & ~31); }
+
+hipError_t launch_transpose_w1s(const void *W1, int r, int s, int d, int ldw1, void *W1t,
+                                hipStream_t st) {
+  const size_t n = corr_w1t_elems(s, r);
+  hipLaunchKernelGGL(k_transpose_w1s, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const uint16_t *>(W1), r, s, d, ldw1,
+                     static_cast<uint16_t *>(W1t));
+  return hipGetLastError();
+}
+
+hipError_t launch_corr_tables(int rows, int M, int r, int s, const void *W2, const void *W1t,
+                              const int32_t *C, const float *Cl, const float *uH, float *G,
+                              float *g, hipStream_t st) {
   dim3 grid((s + CT_NB - 1) / CT_NB, (rows + 15) / 16);
-  const size_t sm = ct_smem(r);
-  hipLaunchKernelGGL(k_corr_tables, grid, dim3(CT_THREADS), sm, st, rows, M, D, r, s, d, ldw1,
-                     static_cast<const uint16_t *>(W2), static_cast<const uint16_t *>(W1), C, Cl,
+  hipLaunchKernelGGL(k_corr_tables, grid, dim3(CT_THREADS), 0, st, rows, M, r, s,
+                     static_cast<const uint16_t *>(W2), static_cast<const uint16_t *>(W1t), C, Cl,
                      uH, G, g);
   return hipGetLastError();
 }

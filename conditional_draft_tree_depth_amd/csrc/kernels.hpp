@@ -7,6 +7,43 @@ namespace dtree {
 
 enum { WT_F32 = 0, WT_BF16 = 1 };
 
+struct TreeBufs {
+  int NT;              // superarbol nodes per request (root included)
+  int V;               // vocabulary size (root tokens are clamped into [0, V))
+  int Wmax;            // survivor slots per request
+  int32_t *n_tok, *n_par, *n_dep;   // [b, NT]
+  float *n_score;                   // [b, NT]
+  uint32_t *n_lex;                  // [b, NT] (parent lexrank << 18) | token
+  int32_t *surv_node, *surv_rank;   // [b, Wmax] current expanded nodes
+  int32_t *nsurv_node, *nsurv_rank; // [b, Wmax] next depth
+  int32_t *surv_hist;               // [b, D+1, Wmax]
+  int32_t *gidx_tok, *gidx_par;     // [b * Wmax] gathers for the GRU step
+  int32_t *sel;                     // [b, Bmax]
+  uint32_t *status;                 // device status bits
+};
+
+// Start of a round for request q (called by one workgroup per request before
+// anything reads the tree buffers): empty survivor history, the root node
+// (its token clamped into [0, V)) as the only expanded branch.
+__device__ inline void init_round_request(int q, const int32_t *root, const TreeBufs &t, int Dp1,
+                                          int tid, int nt) {
+  for (int i = tid; i < Dp1 * t.Wmax; i += nt)
+    t.surv_hist[(size_t)q * Dp1 * t.Wmax + i] = i == 0 ? 0 : -1;
+  if (tid == 0) {
+    const size_t n0 = (size_t)q * t.NT;
+    const int32_t rt = root[q] < 0 ? 0 : (root[q] >= t.V ? t.V - 1 : root[q]);
+    t.n_tok[n0] = rt;
+    t.n_par[n0] = -1;
+    t.n_dep[n0] = 0;
+    t.n_score[n0] = 0.f;
+    t.n_lex[n0] = 0u;
+    t.surv_node[(size_t)q * t.Wmax] = 0;
+    t.surv_rank[(size_t)q * t.Wmax] = 0;
+    t.gidx_tok[q] = rt;
+    if (q == 0) *t.status = 0u;
+  }
+}
+
 // ---- K1: base logits Hq . W_lm^T + bias with a fused per-workgroup Top-M.
 // Writes part[row][p][0..M) = the M best keys of vocabulary slice p for that
 // row, best first (0 = empty).  P slices per row.
@@ -27,6 +64,10 @@ struct LMHeadArgs {
   uint64_t *part2;     // [rows, lmhead_groups(P), M]
   int32_t *C;          // [rows, M]
   float *Cl;           // [rows, M]
+  // round start (init_round_request for q < b), done by the first workgroups
+  const int32_t *root;
+  int b, Dp1;
+  TreeBufs t;
 };
 bool lmhead_fused_merge(int P, int M, int d, int wtype);
 int lmhead_groups(int P);
@@ -59,22 +100,6 @@ hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh,
                               const int32_t *pidx, float *Snew, hipStream_t st);
 
 // ---- per-depth kernels
-struct TreeBufs {
-  int NT;              // superarbol nodes per request (root included)
-  int V;               // vocabulary size (root tokens are clamped into [0, V))
-  int Wmax;            // survivor slots per request
-  int32_t *n_tok, *n_par, *n_dep;   // [b, NT]
-  float *n_score;                   // [b, NT]
-  uint32_t *n_lex;                  // [b, NT] (parent lexrank << 18) | token
-  int32_t *surv_node, *surv_rank;   // [b, Wmax] current expanded nodes
-  int32_t *nsurv_node, *nsurv_rank; // [b, Wmax] next depth
-  int32_t *surv_hist;               // [b, D+1, Wmax]
-  int32_t *gidx_tok, *gidx_par;     // [b * Wmax] gathers for the GRU step
-  int32_t *sel;                     // [b, Bmax]
-  uint32_t *status;                 // device status bits
-};
-hipError_t launch_init_round(int b, const int32_t *root, const TreeBufs &t,
-                             int Dp1, hipStream_t st);
 hipError_t launch_corr_logits(int b, int A, int M, int r, int D, int delta,
                               const void *W2, int wtype, const int32_t *C,
                               const float *Cl, const float *u, float *ell,
@@ -110,9 +135,13 @@ size_t persist_part_floats(int s);
 size_t persist_gitab_floats(int s, int D);
 size_t persist_terms_floats(int s);
 hipError_t persist_prepare(int s);
-hipError_t launch_corr_tables(int rows, int M, int D, int r, int s, int d, int ldw1,
-                              const void *W2, const void *W1, const int32_t *C, const float *Cl,
-                              const float *uH, float *G, float *g, hipStream_t st);
+// W1t = W1[:, d:]^T zero-padded to [s, (r + 31) & ~31] bf16 (made once)
+size_t corr_w1t_elems(int s, int r);
+hipError_t launch_transpose_w1s(const void *W1, int r, int s, int d, int ldw1, void *W1t,
+                                hipStream_t st);
+hipError_t launch_corr_tables(int rows, int M, int r, int s, const void *W2, const void *W1t,
+                              const int32_t *C, const float *Cl, const float *uH, float *G,
+                              float *g, hipStream_t st);
 hipError_t launch_depth_persistent(const PersistArgs &a, hipStream_t st);
 hipError_t corr_logits_prepare(int wtype, size_t smem);
 

@@ -71,7 +71,11 @@ typedef enum { DTREE_F32 = 0, DTREE_BF16 = 1 } dtree_dtype;
 
 /* Shared drafter weights, PyTorch module layouts, row-major, device memory.
  * Matrices are stored as `wtype` (bf16 = raw 16-bit patterns).  Biases are
- * fp32 and may be NULL (read as zeros).                                      */
+ * fp32 and may be NULL (read as zeros).  The context borrows the weights:
+ * they must stay valid and unchanged while it exists (it also keeps a
+ * transposed copy of W1[:, d:] made by dtree_create).  With bf16 weights,
+ * 16-byte aligned W_ih, W_hh, Emb and W2 let the depth loop run as a single
+ * persistent kernel when the shapes allow it.                                */
 typedef struct {
   int32_t d;   /* hidden size of H                                          */
   int32_t V;   /* vocabulary size, <= 262144                                 */
