@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen3_4b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy a 256 MiB device buffer three times (a kernel of known "
+                         "traffic, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -119,6 +122,13 @@ def main():
     rnd = runner.Round(wd, cfg.wtype, caps, cfg.batch, cfg.D, cfg.M, cfg.K, cfg.W, cfg.B,
                        cfg.beta)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         rnd.run(H, root)
     torch.cuda.synchronize()
