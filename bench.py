@@ -70,7 +70,7 @@ def counters_traffic(workload, per_launch_div=1):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inputs, budget_s=15.0, max_rounds=5):
+def cpu_baseline(cfg, inputs, budget_s=12.0, max_rounds=50):
     """The CPU oracle as it stands, timed on this host on whole rounds of the
     same workload (at least one, stopping once ~budget_s has been spent)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))

@@ -125,8 +125,8 @@ constexpr int PK_SLOTS = 3 * PK_ROWS;      // (term, branch) columns of the stat
 constexpr unsigned PK_SPIN = 1u << 20;
 
 struct PKLayout {
-  size_t red, stage, gis, gsl, ghs, bhh, ell, ex, lpkey, snew, ckey, clex, cmeta, ctok, sinfo,
-      finfo, misc, total;
+  size_t red, stage, gis, gsl, ghs, bhh, ell, ex, lpkey, snew, ckey, clex, cmeta, cpar, ctok,
+      sinfo, finfo, misc, total;
 };
 
 __host__ __device__ inline PKLayout pk_layout() {
@@ -147,6 +147,7 @@ __host__ __device__ inline PKLayout pk_layout() {
   L.ckey = take((size_t)PK_MAXZ * 8);
   L.clex = take((size_t)PK_MAXZ * 4);
   L.cmeta = take((size_t)PK_MAXZ * 4);
+  L.cpar = take((size_t)PK_MAXZ * 4);
   L.ctok = take((size_t)PK_MAXC * 4);
   L.sinfo = take((size_t)PK_ROWS * 8 * 4);
   L.finfo = take((size_t)PK_ROWS * 4 * 4);
@@ -434,6 +435,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
   uint64_t *ckey = reinterpret_cast<uint64_t *>(smem + L.ckey);
   uint32_t *clex = reinterpret_cast<uint32_t *>(smem + L.clex);
   int32_t *cmeta = reinterpret_cast<int32_t *>(smem + L.cmeta);
+  int32_t *cpar = reinterpret_cast<int32_t *>(smem + L.cpar);   // children's parent node ids
   int32_t *ctok = reinterpret_cast<int32_t *>(smem + L.ctok);
   int32_t *sinfo = reinterpret_cast<int32_t *>(smem + L.sinfo);
   int32_t *finfo = reinterpret_cast<int32_t *>(smem + L.finfo);
@@ -641,6 +643,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
         ckey[cc] = make_key(sc, lex);
         clex[cc] = lex;
         cmeta[cc] = jj;
+        cpar[cc] = finfo[row * 4 + 0];
       }
     }
     __syncthreads();
@@ -671,14 +674,15 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     }
     __syncthreads();
     // node records of this depth, split over the consumers (read by the
-    // emission kernel after this one ends)
-    {
+    // emission kernel after this one ends); written while waiting for the
+    // next hand-off, from LDS that stays put until the next selection
+    auto write_records = [&]() {
       const int per = divNC(b * Z + p.NC - 1);
       for (int cc = c * per + tid; cc < min(b * Z, (c + 1) * per); cc += PK_THREADS) {
         const int q = divZ(cc), z = cc - q * Z;
         const size_t id = (size_t)q * p.t.NT + off + z;
         p.t.n_tok[id] = (int32_t)(clex[cc] & 0x3FFFFu);
-        p.t.n_par[id] = finfo[(q * A + divK(z)) * 4 + 0];
+        p.t.n_par[id] = cpar[cc];
         p.t.n_dep[id] = dd + 1;
         p.t.n_score[id] = key_val(ckey[cc]);
         p.t.n_lex[id] = clex[cc];
@@ -687,8 +691,11 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
         const int q = divAn(i), rk = i - q * An;
         p.t.surv_hist[((size_t)q * (D + 1) + dd + 1) * p.t.Wmax + rk] = sinfo[i * 8 + 0];
       }
+    };
+    if (!more) {
+      write_records();
+      break;
     }
-    if (!more) break;
     // the fragment table under red was read before the barriers above
     // lane holds D[unit 4g + t][column lr]: one 16-byte run per lane
 #pragma unroll
@@ -708,7 +715,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       }
       ghs[(mt * 16 + row) * 16 + u] = v;
     }
-    __syncthreads();   // also: node records above read finfo, rewritten below
+    __syncthreads();
 
     // ---- GRU step of the survivors for this workgroup's 32 units
     const int nrow = b * An;
@@ -751,6 +758,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       pk_put(pn + tid, acc);
     }
     pk_raise(cflags + c * 64, p.epoch0 + dd + 2);
+    write_records();
     // producer slot dd + 2 holds the candidates of depth dd + 1
     const uint32_t pe = p.epoch0 + (dd + 2 < D ? dd + 3 : D);
     if (!pk_wait(cflags, p.NC, p.epoch0 + dd + 2, pflags, PK_PPC, pe, p.t.status, misc)) return;
