@@ -22,8 +22,7 @@ namespace {
 thread_local std::string g_create_err;
 
 struct Ws {
-  uint64_t *part = nullptr, *part2 = nullptr;
-  uint32_t *k1cnt = nullptr;
+  uint64_t *part = nullptr;
   int32_t *C = nullptr;
   float *Cl = nullptr, *uH = nullptr, *S[2] = {nullptr, nullptr}, *u = nullptr;
   float *ell = nullptr, *gi = nullptr, *gh = nullptr;
@@ -56,6 +55,7 @@ struct dtree_ctx {
   dtree_caps caps{};
   int P = 0, NTcap = 0;
   size_t k1_smem = 0, lds_max = 0;
+  int k1_ring = 0;
   Ws ws;
   std::string err;
   bool has_round = false;
@@ -105,7 +105,7 @@ hipError_t alloc(T **p, size_t n) {
 }
 
 void free_ws(Ws &ws) {
-  void *ptrs[] = {ws.part, ws.part2, ws.k1cnt, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.u, ws.ell, ws.gi, ws.gh,
+  void *ptrs[] = {ws.part, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.u, ws.ell, ws.gi, ws.gh,
                   ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
                   ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags};
@@ -171,7 +171,8 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   ctx->NTcap = NTcap;
   ctx->lds_max = prop.sharedMemPerBlock;
   ctx->P = lmhead_partitions(w->V, w->wtype, (w->r + 15) / 16);
-  ctx->k1_smem = lmhead_smem(w->d, w->wtype);
+  ctx->k1_ring = lmhead_ring(w->d, w->wtype, ctx->lds_max);
+  ctx->k1_smem = lmhead_smem(w->d, w->wtype, ctx->k1_ring);
   const size_t cl_smem = corr_logits_smem(c.max_W, c.max_M, w->r, w->wtype);
   const size_t tb_smem = topb_smem(NTcap, c.max_B);
   auto reject = [&](dtree_status s, const std::string &m) {
@@ -191,10 +192,6 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   auto A = [&](hipError_t x) { if (e == hipSuccess) e = x; };
   A(alloc(&ws.part, rows * ctx->P * c.max_M));
   // counters of the merge fused into the LM-head kernel: only ever grow
-  const size_t nrb = (rows + 15) / 16, ng = lmhead_groups(ctx->P);
-  A(alloc(&ws.part2, rows * ng * c.max_M));
-  A(alloc(&ws.k1cnt, nrb * (ng + 1)));
-  if (e == hipSuccess) A(hipMemset(ws.k1cnt, 0, nrb * (ng + 1) * sizeof(uint32_t)));
   A(alloc(&ws.C, rows * c.max_M));
   A(alloc(&ws.Cl, rows * c.max_M));
   A(alloc(&ws.uH, rows * r));
@@ -239,7 +236,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
     free_ws(ws);
     return reject(DTREE_E_NOMEM, std::string("workspace: ") + hipGetErrorString(e));
   }
-  hipError_t pe = lmhead_prepare(w->wtype, ctx->k1_smem);
+  hipError_t pe = lmhead_prepare(w->wtype, ctx->k1_ring, ctx->k1_smem);
   if (pe == hipSuccess) pe = corr_logits_prepare(w->wtype, cl_smem);
   if (pe == hipSuccess) pe = topb_prepare(tb_smem);
   if (pe == hipSuccess) pe = skinny_prepare(ctx->lds_max);
@@ -301,13 +298,12 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   // bf16: the LM-head kernel also produces uH = W1[:, :d] . Hq (same operand)
   const bool fuse_uH = wt == WT_BF16 && (d + s) % 8 == 0 &&
                        reinterpret_cast<uintptr_t>(w.W1) % 16 == 0;
-  const bool fuse_merge = lmhead_fused_merge(ctx->P, M, d, wt);
   LMHeadArgs la{H, rows, d, w.W_lm, wt, w.V, w.lm_bias, M, ctx->P, ws.part,
                 fuse_uH ? w.W1 : nullptr, d + s, r, ws.uH,
-                fuse_merge ? ws.k1cnt : nullptr, ws.part2, ws.C, ws.Cl, root, batch, D + 1, tb};
+                root, batch, D + 1, tb, ctx->k1_ring};
   HIPCHK(ctx, launch_lmhead(la, st));
   prof_mark(ctx, 1, st);
-  if (!fuse_merge) HIPCHK(ctx, launch_topm_merge(ws.part, ctx->P, M, rows, ws.C, ws.Cl, st));
+  HIPCHK(ctx, launch_topm_merge(ws.part, ctx->P, M, rows, ws.C, ws.Cl, st));
   prof_mark(ctx, 2, st);
   // K2: uH = W1[:, :d] . Hq for every (request, depth), when not fused above
   GemmArgs g{};

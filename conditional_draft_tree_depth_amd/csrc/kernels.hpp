@@ -58,22 +58,17 @@ struct LMHeadArgs {
   const void *W1;      // bf16 only: W1[:, :d] rows ride along -> uH (or null)
   int ldw1, r;
   float *uH;           // [rows, r]
-  // bf16 only, when lmhead_fused_merge(): the kernel also merges the lists
-  // into C / Cl (else null and launch_topm_merge does it)
-  uint32_t *cnt;       // [row blocks][lmhead_groups(P) + 1], zeroed once, never reset
-  uint64_t *part2;     // [rows, lmhead_groups(P), M]
-  int32_t *C;          // [rows, M]
-  float *Cl;           // [rows, M]
   // round start (init_round_request for q < b), done by the first workgroups
   const int32_t *root;
   int b, Dp1;
   TreeBufs t;
+  int ring;            // bf16: LDS ring depth from lmhead_ring (0 = register path)
 };
-bool lmhead_fused_merge(int P, int M, int d, int wtype);
-int lmhead_groups(int P);
 int lmhead_partitions(int V, int wtype, int extra_tiles);
-size_t lmhead_smem(int d, int wtype);
-hipError_t lmhead_prepare(int wtype, size_t smem);
+// LDS ring depth of the bf16 kernel that fits lds_max (0: register path)
+int lmhead_ring(int d, int wtype, size_t lds_max);
+size_t lmhead_smem(int d, int wtype, int ring);
+hipError_t lmhead_prepare(int wtype, int ring, size_t smem);
 hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st);
 // ---- K1b: merge the P partial lists of each row into C (tokens), Cl (logits)
 hipError_t launch_topm_merge(const uint64_t *part, int P, int M, int rows,
