@@ -1,13 +1,13 @@
 """Throughput of one draft-tree round on one MI355X.
 
-A step is one ``dtree_build_round`` call: base-logit GEMM with fused Top-M
-and merge, prologue, the whole depth loop and the global Top-B with mask
+A step is one ``dtree_build_round`` call: base-logit GEMM with fused
+per-slice Top-M, the merge of the slices, prologue, the whole depth loop and the global Top-B with mask
 emission, from device-resident H and root tokens to device-resident outputs,
 for one batch of synthetic inputs (seeded, shapes of the named workload).
 
 Prints ONE JSON line (rank 0).  ``value`` comes from K timed steps with
 nothing else on the stream.  ``roofline`` is for the dominant kernel (the
-LM-head GEMM with its fused Top-M and merge), timed over a second pass of K
+LM-head GEMM with its fused per-slice Top-M), timed over a second pass of K
 steps with HIP events recorded by the library around each stage on the
 round's own stream; ``cpu_baseline`` times the CPU oracle on a bounded sample
 of the same workload.
@@ -179,7 +179,7 @@ def main():
                    "r": cfg.r, "D": cfg.D, "M": cfg.M, "K": cfg.K, "W": cfg.W, "B": cfg.B,
                    "beta": cfg.beta, "batch": cfg.batch, "weights": cfg.wtype},
         "roofline": {"bound": "hbm",
-                     "kernel": "k1_lmhead_bf16 (LM-head GEMM + fused Top-M and merge)",
+                     "kernel": "k1_lmhead_bf16 (LM-head GEMM + fused per-slice Top-M)",
                      "achieved": k1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": k1_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": cnt["k1_bytes"], "us_per_launch": k1_ms * 1e3},

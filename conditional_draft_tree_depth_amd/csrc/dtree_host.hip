@@ -180,6 +180,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
     return fail(nullptr, s, m);
   };
   if (ctx->k1_smem > ctx->lds_max) return reject(DTREE_E_SHAPE, "d too large for the LM-head LDS tile");
+  if (topm_merge_smem(ctx->P) > 131072) return reject(DTREE_E_SHAPE, "vocabulary too large for the Top-M merge");
   if (cl_smem > ctx->lds_max) return reject(DTREE_E_SHAPE, "max_M * r + max_W * r too large for LDS");
   if (tb_smem > ctx->lds_max) return reject(DTREE_E_SHAPE, "superarbol too large for the Top-B LDS sort");
 
@@ -190,7 +191,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   const int s = w->s, r = w->r;
   hipError_t e = hipSuccess;
   auto A = [&](hipError_t x) { if (e == hipSuccess) e = x; };
-  A(alloc(&ws.part, rows * ctx->P * c.max_M));
+  A(alloc(&ws.part, rows * ctx->P * K1_LSTRIDE));
   // counters of the merge fused into the LM-head kernel: only ever grow
   A(alloc(&ws.C, rows * c.max_M));
   A(alloc(&ws.Cl, rows * c.max_M));

@@ -17,6 +17,8 @@
 // k per 128-wide chunk (64-byte row segments of W_lm).  A workgroup owns a
 // contiguous slice of tiles; after its GEMM it re-uses the LDS of the hidden
 // rows to stage its logits and extracts each row's best M keys.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -34,65 +36,79 @@ constexpr int K1F_MAXCOLS = 256;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// ---- per-row Top-M of the staged logits (one row per half-wave)
+// ---- per-row candidate lists of the staged logits (one row per half-wave)
+//
+// Every workgroup leaves, for each of its rows, a list at part + row *
+// rstride: K1_LCAP key slots, then tau, head and count.  The list holds
+// `count` keys (any order) that include the slice's M best, every slice key
+// >= tau is in it, at least min(M, slice size) slice keys are >= tau (so the
+// row's M-th best key is >= tau), and head is the slice's best key.
 
-// u64 exchange with lane ^ J inside groups of 32 lanes
+// u32 exchange with lane ^ J inside groups of 32 lanes
 template <int J>
-__device__ __forceinline__ uint64_t xor_u64(uint64_t v) {
-  auto x32 = [](uint32_t u) -> uint32_t {
-    if constexpr (J == 1) return dpp_u32<0xB1>(u);
-    else if constexpr (J == 2) return dpp_u32<0x4E>(u);
-    else if constexpr (J == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x101F);
-    else if constexpr (J == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x201F);
-    else return (uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x401F);
-  };
-  return ((uint64_t)x32((uint32_t)(v >> 32)) << 32) | x32((uint32_t)v);
+__device__ __forceinline__ uint32_t xor_u32(uint32_t u) {
+  if constexpr (J == 1) return dpp_u32<0xB1>(u);
+  else if constexpr (J == 2) return dpp_u32<0x4E>(u);
+  else if constexpr (J == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x101F);
+  else if constexpr (J == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x201F);
+  else return (uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x401F);
 }
 
-// Bitonic sort (descending) of 32 NR keys held NR per lane by a half-wave,
-// element e = 32 h + lane in register h.  Merge step (K, J): e is compared
-// with e ^ J; blocks with (e & K) == 0 are ordered descending.
+// Bitonic sort (descending) of 32 NR values held NR per lane by a half-wave,
+// element e = NR lane + h in register h (NR a power of two): the low index
+// bits stay inside a lane, so fewer steps need a lane exchange.  Merge step
+// (K, J): e is compared with e ^ J; blocks with (e & K) == 0 are ordered
+// descending.
 template <int NR, int K, int J>
-__device__ __forceinline__ void bitonic_step(uint64_t (&v)[NR], int hl) {
-  if constexpr (J >= 32) {
-    constexpr int HJ = J / 32;
+__device__ __forceinline__ void bitonic_step(uint32_t (&v)[NR], int hl) {
+  if constexpr (J < NR) {
 #pragma unroll
     for (int h = 0; h < NR; ++h) {
-      if ((h & HJ) == 0) {
-        const uint64_t a = v[h], b = v[h | HJ];
-        const bool desc = ((32 * h + hl) & K) == 0;
-        const bool sw = desc ? a < b : a > b;
-        v[h] = sw ? b : a;
-        v[h | HJ] = sw ? a : b;
+      if ((h & J) == 0) {
+        const uint32_t a = v[h], b = v[h | J];
+        const bool desc = ((NR * hl + h) & K) == 0;
+        v[h] = desc ? max(a, b) : min(a, b);
+        v[h | J] = desc ? min(a, b) : max(a, b);
       }
     }
   } else {
+    constexpr int LJ = J / NR;
 #pragma unroll
     for (int h = 0; h < NR; ++h) {
-      const uint64_t o = xor_u64<J>(v[h]);
-      const bool keepmax = ((hl & J) == 0) == (((32 * h + hl) & K) == 0);
-      v[h] = keepmax ? (o > v[h] ? o : v[h]) : (o < v[h] ? o : v[h]);
+      const uint32_t o = xor_u32<LJ>(v[h]);
+      const bool keepmax = ((hl & LJ) == 0) == (((NR * hl + h) & K) == 0);
+      v[h] = keepmax ? max(o, v[h]) : min(o, v[h]);
     }
   }
   if constexpr (J > 1) bitonic_step<NR, K, J / 2>(v, hl);
 }
 template <int NR, int K>
-__device__ __forceinline__ void bitonic_sort32(uint64_t (&v)[NR], int hl) {
+__device__ __forceinline__ void bitonic_sort32(uint32_t (&v)[NR], int hl) {
   bitonic_step<NR, K, K / 2>(v, hl);
   if constexpr (K < 32 * NR) bitonic_sort32<NR, 2 * K>(v, hl);
 }
-
-// the lane's NR best keys, descending (insertion network)
-template <int KPL, int NR>
-__device__ __forceinline__ void lane_best(const uint64_t (&keys)[KPL], uint64_t below,
-                                          uint64_t (&v)[NR]) {
+// element e of the sorted values (all lanes of the half-wave get it)
+template <int NR>
+__device__ __forceinline__ uint32_t bitonic_elem(const uint32_t (&v)[NR], int e) {
+  uint32_t x = v[0];
 #pragma unroll
-  for (int t = 0; t < NR; ++t) v[t] = 0;
+  for (int h = 1; h < NR; ++h)
+    if ((e & (NR - 1)) == h) x = v[h];
+  return (uint32_t)__shfl((int)x, (int)(threadIdx.x & 32) + e / NR);
+}
+
+// the lane's EPI_T best keys below `below`, descending (insertion network)
+constexpr int EPI_T = 4;
+template <int KPL>
+__device__ __forceinline__ void lane_best(const uint64_t (&keys)[KPL], uint64_t below,
+                                          uint64_t (&v)[EPI_T]) {
+#pragma unroll
+  for (int t = 0; t < EPI_T; ++t) v[t] = 0;
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     uint64_t x = keys[i] < below ? keys[i] : 0ull;
 #pragma unroll
-    for (int t = 0; t < NR; ++t) {
+    for (int t = 0; t < EPI_T; ++t) {
       const uint64_t hi = x > v[t] ? x : v[t];
       x = x > v[t] ? v[t] : x;
       v[t] = hi;
@@ -100,114 +116,102 @@ __device__ __forceinline__ void lane_best(const uint64_t (&keys)[KPL], uint64_t 
   }
 }
 
-// Each lane holds KPL keys of the row (0 = empty; keys of a row are
-// distinct).  S = the NR best keys of every lane (32 NR >= M of them); tau,
-// the M-th largest key of S, has at least M keys of the row at or above it,
-// so the row's M best are among the keys >= tau, usually only a few more
-// than M.  Those are compacted into cand (the row's own LDS, already read)
-// and each one's rank among them is counted.  Returns false, having written
-// nothing, when more than min(32 CAP, capmax) keys reach tau.
-template <int KPL, int NR, int CAP>
-__device__ __forceinline__ bool row_topm_fast(const uint64_t (&keys)[KPL], int hl, bool active,
-                                              int M, uint64_t *cand, int capmax, uint64_t *outr) {
-  uint64_t v[NR];
-  lane_best<KPL, NR>(keys, ~0ull, v);
-  bitonic_sort32<NR, 2>(v, hl);
-  uint64_t x = v[0];
-#pragma unroll
-  for (int h = 1; h < NR; ++h)
-    if (((M - 1) >> 5) == h) x = v[h];
-  const int src = (int)(threadIdx.x & 32) + ((M - 1) & 31);
-  const uint64_t tau = ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(x >> 32), src) << 32) |
-                       (uint32_t)__shfl((int)(uint32_t)x, src);
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) cnt += (keys[i] >= tau && keys[i] != 0ull) ? 1 : 0;
-  // inclusive prefix of the counts over the half-wave, and its total
-  int incl = cnt, tot = cnt, y;
-  y = (int)dpp_u32<0xB1>((uint32_t)tot); if (hl & 1) incl += y; tot += y;
-  y = (int)dpp_u32<0x4E>((uint32_t)tot); if (hl & 2) incl += y; tot += y;
-  y = __builtin_amdgcn_ds_swizzle(tot, 0x101F); if (hl & 4) incl += y; tot += y;
-  y = __builtin_amdgcn_ds_swizzle(tot, 0x201F); if (hl & 8) incl += y; tot += y;
-  y = __builtin_amdgcn_ds_swizzle(tot, 0x401F); if (hl & 16) incl += y; tot += y;
-  if (tot > 32 * CAP || tot > capmax) return false;
-  if (active) {
-    int pos = incl - cnt;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i)
-      if (keys[i] >= tau && keys[i] != 0ull) cand[pos++] = keys[i];
-  }
-  uint64_t mine[CAP];
-  int rk[CAP];
-#pragma unroll
-  for (int w = 0; w < CAP; ++w) {
-    mine[w] = hl + 32 * w < tot ? cand[hl + 32 * w] : 0ull;
-    rk[w] = 0;
-  }
-  for (int j = 0; j < tot; j += 8) {
-    uint64_t c[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) c[u] = j + u < tot ? cand[j + u] : 0ull;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int w = 0; w < CAP; ++w) rk[w] += c[u] > mine[w] ? 1 : 0;
-  }
-  if (active) {
-#pragma unroll
-    for (int w = 0; w < CAP; ++w)
-      if (hl + 32 * w < tot && rk[w] < M) outr[rk[w]] = mine[w];
-    for (int m = tot + hl; m < M; m += 32) outr[m] = 0ull;
-  }
-  return true;
-}
-
-// The same result by M rounds of a half-wave maximum over the lanes' sorted
-// lists of their best EPI_T keys; the winning lane pops its head, and a lane
-// whose list runs dry refills it with its next best keys.
-constexpr int EPI_T = 4;
-template <int KPL>
-__device__ __forceinline__ void row_topm_rounds(const uint64_t (&keys)[KPL], int hl, bool active,
-                                                int M, uint64_t *outr) {
-  uint64_t loc[EPI_T];
-  lane_best<KPL, EPI_T>(keys, ~0ull, loc);
-  for (int m = 0; m < M; ++m) {
-    const uint64_t top = group_max_u64<32>(loc[0]);
-    if (active && hl == 0) outr[m] = top;
-    if (loc[0] == top && top != 0) {
-#pragma unroll
-      for (int t = 0; t + 1 < EPI_T; ++t) loc[t] = loc[t + 1];
-      loc[EPI_T - 1] = 0;
-      if (loc[0] == 0) lane_best<KPL, EPI_T>(keys, top, loc);
-    }
-  }
-}
-
-// Each half-wave takes one row of the staged logits Ls[row][0..ncols) and
-// writes that row's M best keys (value desc, token asc), best first, to
-// out[row * ostride + m] (0 = empty).  The row's LDS is scratch afterwards.
+// Each lane holds KPL ordered values of the row (hv, 0 = empty) for columns
+// hl + 32 i.  Fast path (M <= 64): S = every lane's two best values; tau,
+// the M-th largest of S, has at least M keys of the row at or above it, so
+// the row's M best are among the keys with value >= tau, usually only a few
+// more than M.  Those are written unsorted.  With more than K1_LCAP of them
+// (ties) or M > 64, the row's exact M best are written instead, by M rounds
+// of a half-wave maximum over the lanes' sorted short lists (a lane whose
+// list runs dry refills it with its next best keys).
 template <int MAXC>
-__device__ __forceinline__ void wg_topm_epilogue(float *Ls, int lstride, int ncols, int col0,
-                                                 int nrow, int M, uint64_t *out, size_t ostride) {
+__device__ __forceinline__ void wg_topm_epilogue(const float *Ls, int lstride, int ncols,
+                                                 int col0, int nrow, int M, uint64_t *out,
+                                                 size_t rstride) {
   constexpr int KPL = MAXC / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6, hl = lane & 31;
   for (int rb = wave * 2; rb < nrow; rb += 2 * nw) {
     const int r = rb + (lane >> 5);
     const bool active = r < nrow;
-    uint64_t keys[KPL];
+    uint32_t hv[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
       const int c = hl + 32 * i;
-      uint64_t k = 0;
-      if (active && c < ncols) k = make_key(Ls[r * lstride + c], (uint32_t)(col0 + c));
-      keys[i] = k;
+      hv[i] = (active && c < ncols) ? f32_ord(Ls[r * lstride + c]) : 0u;
     }
-    uint64_t *cand = reinterpret_cast<uint64_t *>(Ls + r * lstride);
-    uint64_t *outr = out + (size_t)r * ostride;
-    const int capmax = lstride / 2;
-    const bool done = M <= 64 && row_topm_fast<KPL, 2, 4>(keys, hl, active, M, cand, capmax, outr);
-    if (!done) row_topm_rounds<KPL>(keys, hl, active, M, outr);
+    auto key_of = [&](int i) -> uint64_t {
+      return ((uint64_t)hv[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(col0 + hl + 32 * i));
+    };
+    uint64_t *outr = out + (size_t)r * rstride;
+    bool done = false;
+    if (M <= 64) {
+      uint32_t sv[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        sv[1] = max(sv[1], min(sv[0], hv[i]));
+        sv[0] = max(sv[0], hv[i]);
+      }
+      bitonic_sort32<2, 2>(sv, hl);
+      const uint32_t tau = bitonic_elem<2>(sv, M - 1);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) cnt += (hv[i] >= tau && hv[i] != 0u) ? 1 : 0;
+      // inclusive prefix of the counts over the half-wave, and its total
+      int incl = cnt, tot = cnt, y;
+      y = (int)dpp_u32<0xB1>((uint32_t)tot); if (hl & 1) incl += y; tot += y;
+      y = (int)dpp_u32<0x4E>((uint32_t)tot); if (hl & 2) incl += y; tot += y;
+      y = __builtin_amdgcn_ds_swizzle(tot, 0x101F); if (hl & 4) incl += y; tot += y;
+      y = __builtin_amdgcn_ds_swizzle(tot, 0x201F); if (hl & 8) incl += y; tot += y;
+      y = __builtin_amdgcn_ds_swizzle(tot, 0x401F); if (hl & 16) incl += y; tot += y;
+      if (tot <= K1_LCAP) {
+        if (active) {
+          int pos = incl - cnt;
+          uint64_t best = 0;
+#pragma unroll
+          for (int i = 0; i < KPL; ++i)
+            if (hv[i] >= tau && hv[i] != 0u) {
+              const uint64_t k = key_of(i);
+              outr[pos++] = k;
+              best = k > best ? k : best;
+            }
+          const uint64_t head = group_max_u64<32>(best);
+          if (hl == 0) {
+            outr[K1_LCAP] = (uint64_t)tau << 32;
+            outr[K1_LCAP + 1] = head;
+            outr[K1_LCAP + 2] = (uint64_t)tot;
+          }
+        }
+        done = true;
+      }
+    }
+    if (!done) {
+      uint64_t keys[KPL];
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) keys[i] = hv[i] ? key_of(i) : 0ull;
+      uint64_t loc[EPI_T];
+      lane_best<KPL>(keys, ~0ull, loc);
+      uint64_t first = 0, last = 0;
+      int nz = 0;
+      for (int m = 0; m < M; ++m) {
+        const uint64_t top = group_max_u64<32>(loc[0]);
+        if (active && hl == 0) outr[m] = top;
+        if (m == 0) first = top;
+        last = top;
+        nz += top != 0 ? 1 : 0;
+        if (loc[0] == top && top != 0) {
+#pragma unroll
+          for (int t = 0; t + 1 < EPI_T; ++t) loc[t] = loc[t + 1];
+          loc[EPI_T - 1] = 0;
+          if (loc[0] == 0) lane_best<KPL>(keys, top, loc);
+        }
+      }
+      if (active && hl == 0) {
+        outr[K1_LCAP] = nz == M ? last : 0ull;
+        outr[K1_LCAP + 1] = first;
+        outr[K1_LCAP + 2] = (uint64_t)nz;
+      }
+    }
   }
 }
 
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
   const int vend = min(min(t1, ntV) * 16, V);
   const int ncols = vend > t0 * 16 ? vend - t0 * 16 : 0;
   wg_topm_epilogue<K1_MAXCOLS>(Ls, LSTR, ncols, t0 * 16, nrow, M,
-                               part + ((size_t)row0 * P + y) * M, (size_t)P * M);
+                               part + ((size_t)row0 * P + y) * K1_LSTRIDE, (size_t)P * K1_LSTRIDE);
 }
 
 // fp32 weights: plain VALU dot products (small workloads only).
@@ -467,135 +471,161 @@ __global__ __launch_bounds__(K1F_THREADS) void k1_lmhead_f32(
   }
   __syncthreads();
   wg_topm_epilogue<K1F_MAXCOLS>(Ls, K1F_MAXCOLS, ncols, col0, nrow, M,
-                                part + ((size_t)row0 * P + y) * M, (size_t)P * M);
+                                part + ((size_t)row0 * P + y) * K1_LSTRIDE, (size_t)P * K1_LSTRIDE);
 }
 
-// K1b: one workgroup per row merges that row's P partial lists (each sorted
-// best first, M keys, 0 = empty) into the row's M best.
+// K1b: one workgroup per row selects the row's M best keys from its P lists.
 //
-// Every list holds M keys at least as large as its M-th, and the M largest
-// list heads are M distinct keys, so the row's M best are all >= tau, the
-// larger of the largest M-th key of a list and the M-th largest head.
-// Usually only a few more than M keys qualify: they are gathered in LDS and each one's rank
-// among them is counted.  With more than K1B_FAST of them, the lists are
-// merged by a bitonic tournament instead: for two descending lists A and B,
-// max(A[k], B[Mp-1-k]) holds the Mp best keys of A and B as a bitonic
-// sequence (Mp = next_pow2(M), lists padded with empty keys), which a
-// half-cleaner cascade sorts back into descending order.  Lists are paired
-// level by level in LDS (at level l the live lists sit at slots that are
-// multiples of 2^l); with more lists than fit, batches of G-1 lists are
-// reduced together with the running result in slot 0.
+// Each list guarantees that the row's M-th best key is >= its tau; M heads
+// are M distinct keys, so the M-th largest value among 64 (M > 64: 128) of
+// the heads is a bound as well.  tau, the largest of these bounds, can only be reached in lists
+// whose head reaches it (at most M of them), and usually by only a few more
+// than M keys: those are gathered in LDS and each one's rank among them is
+// counted.  If more than K1B_FAST keys pass (heavy ties), the exact M-th
+// best key is found first by bisection over counts (the largest x with at
+// least M listed keys >= x, between tau and the best head; every key the
+// row's M best could be is listed), leaving exactly M keys to rank.
 constexpr int K1B_THREADS = 512;
-constexpr int K1B_CAP = 16384;   // tournament: keys in LDS (128 KiB)
-constexpr int K1B_FAST = 2048;   // gathered candidates
+constexpr int K1B_FAST = 2048;   // gathered keys
+constexpr int K1B_UNROLL = 8;
+
+size_t topm_merge_smem(int P) {
+  return (size_t)K1B_FAST * 8 + (size_t)P * 8 + (size_t)P * 4 * 2;
+}
 
 __global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
     const uint64_t *__restrict__ part, int P, int M, int32_t *__restrict__ C,
     float *__restrict__ Cl) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ uint64_t red[K1B_THREADS / 64];
-  __shared__ int ncand;
-  uint64_t *L = reinterpret_cast<uint64_t *>(smem);
+  __shared__ int redi[K1B_THREADS / 64];
+  __shared__ int ncand, nlive;
+  uint64_t *cand = reinterpret_cast<uint64_t *>(smem);                 // [K1B_FAST]
+  uint64_t *heads = cand + K1B_FAST;                                   // [P]
+  int *cnt = reinterpret_cast<int *>(heads + P);                       // [P]
+  int *live = cnt + P;                                                 // [P]
   const int row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
-  const uint64_t *pk = part + (size_t)row * P * M;
-  {
-    uint64_t t = 0;
-    for (int l = tid; l < P; l += nt) {
-      const uint64_t v = pk[(size_t)l * M + M - 1];
-      t = v > t ? v : t;
+  const int lane = tid & 63, wave = tid >> 6, nwv = nt >> 6;
+  const uint64_t *base = part + (size_t)row * P * K1_LSTRIDE;
+  auto block_max = [&](uint64_t v) -> uint64_t {
+    v = group_max_u64<64>(v);
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    uint64_t m = 0;
+    for (int w = 0; w < nwv; ++w) m = red[w] > m ? red[w] : m;
+    return m;
+  };
+  auto block_sum = [&](int c) -> int {
+    c += (int)xchg_u32<1>((uint32_t)c);
+    c += (int)xchg_u32<2>((uint32_t)c);
+    c += (int)xchg_u32<4>((uint32_t)c);
+    c += (int)xchg_u32<8>((uint32_t)c);
+    c += (int)xchg_u32<16>((uint32_t)c);
+    c += (int)xchg_u32<32>((uint32_t)c);
+    __syncthreads();
+    if (lane == 0) redi[wave] = c;
+    __syncthreads();
+    int tot = 0;
+    for (int w = 0; w < nwv; ++w) tot += redi[w];
+    return tot;
+  };
+
+  uint64_t t = 0;
+  for (int l = tid; l < P; l += nt) {
+    const uint64_t *m = base + (size_t)l * K1_LSTRIDE + K1_LCAP;
+    const uint64_t tl = m[0];
+    heads[l] = m[1];
+    cnt[l] = (int)min(m[2], (uint64_t)K1_LCAP);
+    t = tl > t ? tl : t;
+  }
+  if (tid == 0) { ncand = 0; nlive = 0; }
+  __syncthreads();
+  if (wave == 0 && M <= P) {
+    // 32 NR distinct heads (the best of the lists l = slot mod 32 NR), sorted
+    // by value: at least M keys reach the M-th largest value among them
+    const int hl = lane & 31;
+    auto bound = [&](auto nr) -> uint64_t {
+      constexpr int NR = decltype(nr)::value;
+      uint32_t v[NR];
+#pragma unroll
+      for (int h = 0; h < NR; ++h) {
+        uint64_t b = 0;
+        for (int l = NR * hl + h; l < P; l += 32 * NR) b = heads[l] > b ? heads[l] : b;
+        v[h] = (uint32_t)(b >> 32);
+      }
+      bitonic_sort32<NR, 2>(v, hl);
+      return (uint64_t)bitonic_elem<NR>(v, M - 1) << 32;
+    };
+    const uint64_t th = M <= 64 ? bound(std::integral_constant<int, 2>())
+                                : bound(std::integral_constant<int, 4>());
+    t = th > t ? th : t;
+  }
+  const uint64_t tau = block_max(t);
+  uint64_t hmax = 0;
+  for (int l = tid; l < P; l += nt) {
+    const uint64_t h = heads[l];
+    if (h >= tau && h != 0ull && cnt[l] > 0) live[atomicAdd(&nlive, 1)] = l;
+    hmax = h > hmax ? h : hmax;
+  }
+  hmax = block_max(hmax);   // (its barriers also publish live / nlive)
+  const int nslot = nlive * K1_LCAP;
+
+  // f(key) for every key of the live lists
+  auto sweep = [&](auto &&fn) {
+    for (int i0 = tid; i0 < nslot; i0 += K1B_UNROLL * nt) {
+      uint64_t v[K1B_UNROLL];
+#pragma unroll
+      for (int u = 0; u < K1B_UNROLL; ++u) {
+        const int i = i0 + u * nt;
+        v[u] = 0ull;
+        if (i < nslot) {
+          const int l = live[i / K1_LCAP], k = i % K1_LCAP;
+          if (k < cnt[l]) v[u] = base[(size_t)l * K1_LSTRIDE + k];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < K1B_UNROLL; ++u) fn(v[u]);
     }
-    // the lists' heads are distinct keys too: the M-th largest head is
-    // another lower bound of the row's M-th key (0 if fewer than M heads)
-    uint64_t *heads = L;
-    for (int l = tid; l < P; l += nt) heads[l] = pk[(size_t)l * M];
+  };
+  auto gather = [&](uint64_t thr) {
+    sweep([&](uint64_t v) {
+      if (v >= thr && v != 0ull) {
+        const int at = atomicAdd(&ncand, 1);
+        if (at < K1B_FAST) cand[at] = v;
+      }
+    });
+    __syncthreads();
+  };
+  gather(tau);
+  int n = ncand;
+  if (n > K1B_FAST) {
+    // count(>= lo) >= M > count(>= hi)
+    uint64_t lo = tau, hi = hmax + 1;
+    while (hi - lo > 1) {
+      const uint64_t mid = lo + (hi - lo) / 2;
+      int c = 0;
+      sweep([&](uint64_t v) { c += (v >= mid && v != 0ull) ? 1 : 0; });
+      if (block_sum(c) >= M) lo = mid; else hi = mid;
+    }
+    __syncthreads();
     if (tid == 0) ncand = 0;
     __syncthreads();
-    if (M <= P) {
-      for (int l = tid; l < P; l += nt) {
-        const uint64_t h = heads[l];
-        int rk = 0;
-        for (int j = 0; j < P; ++j) rk += heads[j] > h ? 1 : 0;
-        if (rk == M - 1 && h > t) t = h;
-      }
-    }
-    t = group_max_u64<64>(t);
-    if ((tid & 63) == 0) red[tid >> 6] = t;
-    __syncthreads();
-    uint64_t tau = 0;
-    for (int w = 0; w < nt / 64; ++w) tau = red[w] > tau ? red[w] : tau;
-    const int tot = P * M;
-    for (int i0 = tid; i0 < tot; i0 += 8 * nt) {
-      uint64_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = i0 + u * nt < tot ? pk[i0 + u * nt] : 0ull;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (v[u] >= tau && v[u] != 0ull) {
-          const int at = atomicAdd(&ncand, 1);
-          if (at < K1B_FAST) L[at] = v[u];
-        }
-    }
-    __syncthreads();
-    const int n = ncand;
-    if (n <= K1B_FAST) {
-      for (int i = tid; i < n; i += nt) {
-        const uint64_t k = L[i];
-        int rk = 0;
-        for (int j = 0; j < n; ++j) rk += L[j] > k ? 1 : 0;
-        if (rk < M) {
-          C[(size_t)row * M + rk] = (int32_t)key_tie(k);
-          Cl[(size_t)row * M + rk] = key_val(k);
-        }
-      }
-      for (int m = n + tid; m < M; m += nt) {
-        C[(size_t)row * M + m] = -1;
-        Cl[(size_t)row * M + m] = key_val(0ull);
-      }
-      return;
-    }
-    __syncthreads();
+    gather(lo);
+    n = min(ncand, K1B_FAST);
   }
-  const int Mp = next_pow2(M);
-  const int lm = __builtin_ctz((unsigned)Mp);         // log2(Mp)
-  const int G = K1B_CAP >> lm;                         // lists per batch (power of two, >= 2)
-  for (int i = tid; i < Mp; i += nt) L[i] = 0ull;     // running result, slot 0
-  for (int p0 = 0; p0 < P; p0 += G - 1) {
-    const int nl = min(G - 1, P - p0);                 // fresh lists in this batch
-    const int nslots = next_pow2(nl + 1);
-    for (int i = Mp + tid; i < (nslots << lm); i += nt) {
-      const int sl = (i >> lm) - 1, k = i & (Mp - 1);
-      L[i] = (sl < nl && k < M) ? pk[(size_t)(p0 + sl) * M + k] : 0ull;
-    }
-    __syncthreads();
-    for (int ls = 0; (1 << ls) < nslots; ++ls) {
-      const int npairs = nslots >> (ls + 1);
-      const int pshift = ls + 1 + lm;                  // log2 of a pair's span in keys
-      // max against the reversed partner: bitonic, holds the best Mp
-      for (int i = tid; i < (npairs << lm); i += nt) {
-        const int pr = i >> lm, k = i & (Mp - 1);
-        uint64_t *A = L + ((size_t)pr << pshift);
-        const uint64_t *Bv = A + ((size_t)1 << (ls + lm));
-        const uint64_t a = A[k], b = Bv[Mp - 1 - k];
-        A[k] = a > b ? a : b;
-      }
-      __syncthreads();
-      for (int lj = lm - 1; lj >= 0; --lj) {
-        const int j = 1 << lj;
-        for (int i = tid; i < (npairs << (lm - 1)); i += nt) {
-          const int pr = i >> (lm - 1), h = i & ((Mp >> 1) - 1);
-          uint64_t *A = L + ((size_t)pr << pshift);
-          const int lo = ((h >> lj) << (lj + 1)) | (h & (j - 1)), hi = lo + j;
-          const uint64_t a = A[lo], b = A[hi];
-          if (a < b) { A[lo] = b; A[hi] = a; }
-        }
-        __syncthreads();
-      }
+  for (int i = tid; i < n; i += nt) {
+    const uint64_t k = cand[i];
+    int rk = 0;
+    for (int j = 0; j < n; ++j) rk += cand[j] > k ? 1 : 0;
+    if (rk < M) {
+      C[(size_t)row * M + rk] = (int32_t)key_tie(k);
+      Cl[(size_t)row * M + rk] = key_val(k);
     }
   }
-  for (int j = tid; j < M; j += nt) {
-    const uint64_t k = L[j];
-    C[(size_t)row * M + j] = k ? (int32_t)key_tie(k) : -1;
-    Cl[(size_t)row * M + j] = key_val(k);
+  for (int m = n + tid; m < M; m += nt) {
+    C[(size_t)row * M + m] = -1;
+    Cl[(size_t)row * M + m] = key_val(0ull);
   }
 }
 
@@ -626,8 +656,7 @@ static const void *k1_fn() { return reinterpret_cast<const void *>(&k1_lmhead_bf
 
 hipError_t lmhead_prepare(int wtype, int ring, size_t smem) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k1b_topm_merge),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)(K1B_CAP * sizeof(uint64_t)));
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
   if (e != hipSuccess || wtype != WT_BF16) return e;
   const void *fn = ring == 2 ? k1_fn<2>() : ring == 1 ? k1_fn<1>() : k1_fn<0>();
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -655,7 +684,7 @@ hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st) {
 
 hipError_t launch_topm_merge(const uint64_t *part, int P, int M, int rows, int32_t *C,
                              float *Cl, hipStream_t st) {
-  const size_t sm = (size_t)K1B_CAP * sizeof(uint64_t);
+  const size_t sm = topm_merge_smem(P);
   hipLaunchKernelGGL(k1b_topm_merge, dim3(rows), dim3(K1B_THREADS), sm, st, part, P, M, C, Cl);
   return hipGetLastError();
 }

@@ -44,9 +44,14 @@ __device__ inline void init_round_request(int q, const int32_t *root, const Tree
   }
 }
 
-// ---- K1: base logits Hq . W_lm^T + bias with a fused per-workgroup Top-M.
-// Writes part[row][p][0..M) = the M best keys of vocabulary slice p for that
-// row, best first (0 = empty).  P slices per row.
+// ---- K1: base logits Hq . W_lm^T + bias with a fused per-workgroup Top-M
+// pre-selection.  For every row and vocabulary slice p (P slices per row)
+// it writes the list part[row][p][0 .. K1_LSTRIDE): up to K1_LCAP keys (any
+// order) that include the slice's M best, then tau, head and count: every
+// slice key >= tau is among the `count` keys, at least min(M, slice size)
+// slice keys are >= tau, head is the slice's best key.
+constexpr int K1_LCAP = 128;
+constexpr int K1_LSTRIDE = K1_LCAP + 4;
 struct LMHeadArgs {
   const float *H;      // [rows, d] fp32
   int rows, d;
@@ -54,7 +59,7 @@ struct LMHeadArgs {
   int wtype, V;
   const float *bias;   // [V] or null
   int M, P;
-  uint64_t *part;      // [rows, P, M]
+  uint64_t *part;      // [rows, P, K1_LSTRIDE]
   const void *W1;      // bf16 only: W1[:, :d] rows ride along -> uH (or null)
   int ldw1, r;
   float *uH;           // [rows, r]
@@ -70,7 +75,8 @@ int lmhead_ring(int d, int wtype, size_t lds_max);
 size_t lmhead_smem(int d, int wtype, int ring);
 hipError_t lmhead_prepare(int wtype, int ring, size_t smem);
 hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st);
-// ---- K1b: merge the P partial lists of each row into C (tokens), Cl (logits)
+// ---- K1b: the M best keys of each row from its P lists -> C (tokens), Cl (logits)
+size_t topm_merge_smem(int P);
 hipError_t launch_topm_merge(const uint64_t *part, int P, int M, int rows,
                              int32_t *C, float *Cl, hipStream_t st);
 

@@ -107,3 +107,26 @@ def test_persistent_depth_loop(gpu_lib, seed, d, e, s, r, D, M, K, W, B, batch, 
     cfg = synth.custom_config(cfg_id=9000 + seed, d=d, V=3000 + 31 * seed, e=e, s=s, r=r,
                               D=D, M=M, K=K, W=W, B=B, beta=beta, batch=batch, wtype="bf16")
     check_config(synth.make_inputs(cfg, seed), cfg, f"persistent {seed}", max_tie_frac=0.5)
+
+
+@pytest.mark.parametrize("wtype,M,mode", [
+    ("bf16", 32, "equal"), ("bf16", 64, "equal"), ("bf16", 128, "equal"),
+    ("bf16", 32, "groups"), ("bf16", 64, "groups"), ("f32", 32, "equal"),
+    ("f32", 64, "groups"),
+])
+def test_tied_base_logits(gpu_lib, wtype, M, mode):
+    """Exact ties in the base logits (W_lm = 0, so the logits are the bias):
+    the Top-M table breaks them by token, and slices with more tied keys
+    than a candidate list holds take the exact per-slice path."""
+    V = 40000 if wtype == "bf16" else 6000
+    cfg = synth.custom_config(cfg_id=9500 + M, d=128 if wtype == "bf16" else 32, V=V, e=64,
+                              s=64, r=32, D=4, M=M, K=4, W=8, B=60, beta=-0.05, batch=2,
+                              wtype=wtype)
+    x = synth.make_inputs(cfg, 3)
+    x["weights"]["W_lm"] = np.zeros_like(x["weights"]["W_lm"])
+    if mode == "equal":
+        x["weights"]["bias"] = np.zeros(V, np.float32)
+    else:
+        perm = np.random.default_rng(5).permutation(V)
+        x["weights"]["bias"] = (-0.25 * np.floor(perm / 97.0)).astype(np.float32)
+    check_config(x, cfg, f"tied {wtype} M={M} {mode}", max_tie_frac=0.0)
