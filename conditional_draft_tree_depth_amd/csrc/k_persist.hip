@@ -494,10 +494,17 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     pk_put(p.part + (size_t)c * PK_MAXELL + i, acc);
   }
   pk_raise(cflags + c * 64, p.epoch0 + 1);
-  if (!pk_wait(cflags, p.NC, p.epoch0 + 1, pflags, PK_PPC, p.epoch0 + (D > 1 ? 2 : 1),
-               p.t.status, misc))
-    return;
+  // (the producers' next slot is waited for only where depth 0 first needs it)
+  if (!pk_wait(cflags, p.NC, p.epoch0 + 1, pflags, 0, 0u, p.t.status, misc)) return;
 
+  // input projections of table slot `slot` (this workgroup's units) into LDS
+  auto load_gis = [&](int slot) {
+    const float *gtab = p.gitab + (size_t)slot * PK_MAXC * 3 * s + j0;
+    pk_dma<PK_COHERENT>(gis, bM * 24, [&](int ci) {
+      const int rw = ci >> 3, cj = rw / 3;
+      return gtab + (size_t)cj * 3 * s + (rw - 3 * cj) * s + (ci & 7) * 4;
+    });
+  };
   // (branch row, candidate) of this thread's entry; the entries are row-major
   const int row0 = tid / M, jj0 = tid - row0 * M;
   const PkDiv divK(K), divQC(8 * M), divNC(p.NC);
@@ -526,11 +533,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     if (more) {
       pk_dma<PK_COHERENT>(red, nks * pk_npass(rows) * 64,
                           [&](int ci) { return reinterpret_cast<const float *>(Tcur + 8 * ci); });
-      const float *gtab = p.gitab + (size_t)(dd + 1) * PK_MAXC * 3 * s + j0;
-      pk_dma<PK_COHERENT>(gis, bM * 24, [&](int ci) {
-        const int rw = ci >> 3, cj = rw / 3;
-        return gtab + (size_t)cj * 3 * s + (rw - 3 * cj) * s + (ci & 7) * 4;
-      });
+      if (dd > 0) load_gis(dd + 1);
       const int qc = 8 * M;   // chunks per request: 32 units x M candidates
       pk_dma<0>(gsl, b * qc, [&](int ci) {
         const int q = divQC(ci);
@@ -696,6 +699,11 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       write_records();
       break;
     }
+    // depth 0: the producers' slot 1 was not needed before the GRU step
+    if (dd == 0) {
+      if (!pk_wait(cflags, 0, 0u, pflags, PK_PPC, p.epoch0 + 2, p.t.status, misc)) return;
+      load_gis(1);
+    }
     // the fragment table under red was read before the barriers above
     // lane holds D[unit 4g + t][column lr]: one 16-byte run per lane
 #pragma unroll
@@ -715,6 +723,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       }
       ghs[(mt * 16 + row) * 16 + u] = v;
     }
+    if (dd == 0) __builtin_amdgcn_s_waitcnt(0);   // the copy of slot 1 has landed
     __syncthreads();
 
     // ---- GRU step of the survivors for this workgroup's 32 units
