@@ -20,6 +20,7 @@
 // GRU products run on MFMA: weights are the A operand, activations the B
 // operand; the fp32 state is split exactly into three bf16 terms.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -282,9 +283,11 @@ __device__ __forceinline__ float pk_group_reduce(float v, int n, Op op) {
 // branch row r is column slot t * rp + r of the MFMA B operand (rp = 5, 8 or
 // 16 by the number of branches, so that the 3 x rows columns fill as few
 // 16-column passes as possible).  The owner of state units 32 c .. 32 c + 31
-// writes k-step c: [k-step][slot][32 units] in bf16, so a consumer copies the
-// whole table with one contiguous transfer and every lane reads its fragment
-// (slot pass * 16 + lane % 16, units 8 (lane / 16) ..) as 16 contiguous bytes.
+// writes k-step c: [k-step][3 rp slots][32 units] in bf16, so a consumer
+// copies the whole table with one contiguous transfer and every lane reads
+// its fragment (slot pass * 16 + lane % 16, units 8 (lane / 16) ..) as 16
+// contiguous bytes.  Pass p column j accumulates slot 16 p + j, so the terms
+// of row r end up in columns r, r + rp and r + 2 rp (mod 16).
 __host__ __device__ inline int pk_rp(int rows) { return rows <= 5 ? 5 : rows <= 8 ? 8 : 16; }
 __host__ __device__ inline int pk_npass(int rows) { return rows <= 5 ? 1 : rows <= 8 ? 2 : 3; }
 
@@ -300,13 +303,13 @@ __device__ __forceinline__ void split3(float x, uint16_t &hi, uint16_t &mi, uint
 __device__ __forceinline__ void pk_put_state(uint16_t *T, int c, int rows, int row, int u, float h) {
   uint16_t t3[3];
   split3(h, t3[0], t3[1], t3[2]);
-  const int rp = pk_rp(rows), np = pk_npass(rows);
+  const int rp = pk_rp(rows);
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
     const uint32_t mine = t3[t];
     const uint32_t other = xchg_u32<1>(mine);   // unit u ^ 1
     if ((u & 1) == 0) {
-      uint32_t *dst = reinterpret_cast<uint32_t *>(T + ((size_t)(c * np * 16 + t * rp + row) * 32 + u));
+      uint32_t *dst = reinterpret_cast<uint32_t *>(T + ((size_t)(c * 3 * rp + t * rp + row) * 32 + u));
       __hip_atomic_store(dst, mine | (other << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -531,7 +534,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
         xs[v] = pk_get4(prs, (uint32_t)(((4 * sg + v) * PK_MAXELL + 4 * eq) * 4));
     }
     if (more) {
-      pk_dma<PK_COHERENT>(red, nks * pk_npass(rows) * 64,
+      pk_dma<PK_COHERENT>(red, nks * 3 * pk_rp(rows) * 4,
                           [&](int ci) { return reinterpret_cast<const float *>(Tcur + 8 * ci); });
       if (dd > 0) load_gis(dd + 1);
       const int qc = 8 * M;   // chunks per request: 32 units x M candidates
@@ -572,20 +575,34 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     for (int mt = 0; mt < 6; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (more) {
       const int npass = pk_npass(rows);
+      // fragments of k-step i + 1 are read while those of k-step i feed the
+      // matrix cores; slots past the 3 x rp used ones share their columns
+      // with used slots of earlier passes, so they must contribute zero
+      auto frags = [&](int i, uint4 (&f)[3]) {
+        const int ks = wave + PK_WAVES * i;
+#pragma unroll
+        for (int ps = 0; ps < 3; ++ps) {
+          const bool ok = ks < nks && ps < npass && ps * 16 + lr < 3 * rp;
+          const uint4 v = *reinterpret_cast<const uint4 *>(
+              sfr + (ok ? (ks * 3 * rp + ps * 16 + lr) * 32 + g * 8 : 0));
+          f[ps] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+        }
+      };
+      uint4 fc[3], fn[3];
+      frags(0, fc);
 #pragma unroll
       for (int i = 0; i < PK_HKS; ++i) {
-        const int ks = wave + PK_WAVES * i;
-        if (ks < nks) {
-          for (int ps = 0; ps < npass; ++ps) {
-            // slots past the 3 x rp used ones share their columns with used
-            // slots of earlier passes, so they must contribute zero
-            uint4 bf = make_uint4(0u, 0u, 0u, 0u);
-            if (ps * 16 + lr < 3 * rp)
-              bf = *reinterpret_cast<const uint4 *>(sfr + ((ks * npass + ps) * 16 + lr) * 32 + g * 8);
+        if (i + 1 < PK_HKS) frags(i + 1, fn);
+        if (wave + PK_WAVES * i < nks) {
 #pragma unroll
-            for (int mt = 0; mt < 6; ++mt) acc[mt] = mfma(wh[i][mt], bf, acc[mt]);
-          }
+          for (int ps = 0; ps < 3; ++ps)
+            if (ps < npass) {
+#pragma unroll
+              for (int mt = 0; mt < 6; ++mt) acc[mt] = mfma(wh[i][mt], fc[ps], acc[mt]);
+            }
         }
+#pragma unroll
+        for (int ps = 0; ps < 3; ++ps) fc[ps] = fn[ps];
       }
     }
     if (tid < E) {
@@ -705,22 +722,42 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       load_gis(1);
     }
     // the fragment table under red was read before the barriers above
-    // lane holds D[unit 4g + t][column lr]: one 16-byte run per lane
+    // lane holds D[unit 4g + t][column lr]; the lanes of columns r, r + rp
+    // and r + 2 rp (mod 16) add up row r's terms first, then every row is
+    // one 16-byte run per lane
+    // (DPP row_ror:n gives lane l the value of lane l - n mod 16)
+    auto put_rows = [&](auto variant) {
+      constexpr int RV = decltype(variant)::value;
+      auto ror = [](float x, auto n) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + decltype(n)::value,
+                                                       0xF, 0xF, false));
+      };
 #pragma unroll
-    for (int mt = 0; mt < 6; ++mt)
-      *reinterpret_cast<f32x4 *>(red + ((wave * 6 + mt) * 16 + lr) * 16 + 4 * g) = acc[mt];
+      for (int mt = 0; mt < 6; ++mt) {
+        f32x4 v = acc[mt];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if constexpr (RV == 8) v[t] += ror(v[t], std::integral_constant<int, 8>());
+          if constexpr (RV == 5)
+            v[t] += ror(v[t], std::integral_constant<int, 11>()) + ror(v[t], std::integral_constant<int, 6>());
+        }
+        if (lr < rows)
+          *reinterpret_cast<f32x4 *>(red + ((wave * 6 + mt) * 16 + lr) * 16 + 4 * g) = v;
+      }
+    };
+    if (rp == 8) put_rows(std::integral_constant<int, 8>());
+    else if (rp == 5) put_rows(std::integral_constant<int, 5>());
+    else put_rows(std::integral_constant<int, 16>());
     __syncthreads();
     const PkDiv div16r(16 * rows);
     for (int i = tid; i < 6 * 16 * rows; i += PK_THREADS) {
       const int mt = div16r(i), rem = i - mt * 16 * rows, row = rem >> 4, u = rem & 15;
       float v = bhh[(mt >> 1) * PK_CU + (mt & 1) * 16 + u];
-      for (int col = row; col < 16; col += rp) {
-        float w8[PK_WAVES];
+      float w8[PK_WAVES];
 #pragma unroll
-        for (int wv = 0; wv < PK_WAVES; ++wv) w8[wv] = red[((wv * 6 + mt) * 16 + col) * 16 + u];
+      for (int wv = 0; wv < PK_WAVES; ++wv) w8[wv] = red[((wv * 6 + mt) * 16 + row) * 16 + u];
 #pragma unroll
-        for (int wv = 0; wv < PK_WAVES; ++wv) v += w8[wv];
-      }
+      for (int wv = 0; wv < PK_WAVES; ++wv) v += w8[wv];
       ghs[(mt * 16 + row) * 16 + u] = v;
     }
     if (dd == 0) __builtin_amdgcn_s_waitcnt(0);   // the copy of slot 1 has landed
