@@ -35,6 +35,7 @@ struct Ws {
   // persistent depth loop: correction tables, partial sums, arrival flags
   float *G = nullptr, *g = nullptr, *pk_part = nullptr, *gitab = nullptr, *pk_terms = nullptr;
   uint16_t *w1t = nullptr;   // W1[:, d:]^T, padded (correction tables)
+  uint16_t *hb = nullptr;    // bf16 hidden rows of the round (LM-head kernel)
   uint32_t *flags = nullptr;
 };
 
@@ -105,7 +106,7 @@ hipError_t alloc(T **p, size_t n) {
 }
 
 void free_ws(Ws &ws) {
-  void *ptrs[] = {ws.part, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.u, ws.ell, ws.gi, ws.gh,
+  void *ptrs[] = {ws.part, ws.hb, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.u, ws.ell, ws.gi, ws.gh,
                   ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
                   ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags};
@@ -196,6 +197,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   A(alloc(&ws.C, rows * c.max_M));
   A(alloc(&ws.Cl, rows * c.max_M));
   A(alloc(&ws.uH, rows * r));
+  A(alloc(&ws.hb, (size_t)((rows + 15) / 16 * 16) * w->d));
   A(alloc(&ws.S[0], bw * s));
   A(alloc(&ws.S[1], bw * s));
   A(alloc(&ws.u, bw * r));
@@ -301,7 +303,7 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
                        reinterpret_cast<uintptr_t>(w.W1) % 16 == 0;
   LMHeadArgs la{H, rows, d, w.W_lm, wt, w.V, w.lm_bias, M, ctx->P, ws.part,
                 fuse_uH ? w.W1 : nullptr, d + s, r, ws.uH,
-                root, batch, D + 1, tb, ctx->k1_ring};
+                root, batch, D + 1, tb, ctx->k1_ring, ws.hb};
   HIPCHK(ctx, launch_lmhead(la, st));
   prof_mark(ctx, 1, st);
   HIPCHK(ctx, launch_topm_merge(ws.part, ctx->P, M, rows, ws.C, ws.Cl, st));

@@ -251,17 +251,14 @@ __device__ __forceinline__ void k1_wait_vm(int n) {   // vmcnt <= n (n <= 63)
 // its own row's A fragments straight into registers, K1_PF chunks ahead.
 template <int RING>
 __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
-    const float *__restrict__ H, int rows, int d, const uint16_t *__restrict__ W, int V,
+    const uint16_t *__restrict__ Hb, int rows, int d, const uint16_t *__restrict__ W, int V,
     const float *__restrict__ bias, int M, uint64_t *__restrict__ part,
-    const uint16_t *__restrict__ W1, int ldw1, int r, float *__restrict__ uH,
-    const int32_t *__restrict__ root, int b, int Dp1, TreeBufs tb) {
+    const uint16_t *__restrict__ W1, int ldw1, int r, float *__restrict__ uH) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int P = gridDim.y, y = blockIdx.y;
-  if (root && blockIdx.x == 0)
-    for (int q = y; q < b; q += P) init_round_request(q, root, tb, Dp1, threadIdx.x, K1_WAVES * 64);
   const int row0 = blockIdx.x * 16;
   const int nrow = min(16, rows - row0);
-  const int HS = d + 8;  // bf16 elements per LDS row (16-byte skew)
+  const int cpr = d >> 3;   // 16-byte chunks per hidden row (a multiple of 16)
   uint16_t *Hs = reinterpret_cast<uint16_t *>(smem);
 
   const int ntV = (V + 15) >> 4;
@@ -311,7 +308,9 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
   };
   // ---- register state (RING == 0): lane group g takes k = 32 g + 8 j + (0..7)
   // of MFMA j in each 128-wide chunk
-  const uint16_t *hp = Hs + lr * HS + g * (RING > 0 ? 8 : 32);
+  // this lane's hidden row in LDS (B operand), 16-byte chunks, swizzled
+  const uint4 *hrow = reinterpret_cast<const uint4 *>(smem) + lr * cpr;
+  const int hsw = lr & 7;
   const uint4 *ptr = nullptr;
   uint4 regs[RING > 0 ? 1 : K1_PF][4];
   auto reg_start = [&](int i) {
@@ -340,27 +339,19 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
     const int c0 = t0 * 16, nc = min(min(t1, ntV) * 16, V) - c0;
     for (int c = threadIdx.x; c < nc; c += K1_WAVES * 64) bs[c] = bias ? bias[c0 + c] : 0.f;
   }
-  // Hq = bf16_rne(H) for the 16 rows of this block (zeros past `rows`)
+  // the 16 rounded hidden rows of this block (k1_stage_hidden) straight
+  // into LDS, 1 KiB per copy instruction; 16-byte chunk j of row q is stored
+  // at chunk j ^ (q & 7) of the row, so the B-fragment reads (16 rows, same
+  // chunk) hit distinct banks
   {
-    // all of a thread's loads in flight at once (16 per batch)
-    const int q4 = d >> 2;   // float4 per row
-    constexpr int NB = 16, NTH = K1_WAVES * 64;
-    for (int i0 = threadIdx.x; i0 < 16 * q4; i0 += NB * NTH) {
-      float4 v[NB];
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int i = i0 + u * NTH, rr = i / q4, k = (i - rr * q4) * 4;
-        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < 16 * q4 && rr < nrow) v[u] = *reinterpret_cast<const float4 *>(H + (size_t)(row0 + rr) * d + k);
-      }
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int i = i0 + u * NTH, rr = i / q4, k = (i - rr * q4) * 4;
-        const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[u].x) | ((uint32_t)f32_to_bf16_rne(v[u].y) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[u].z) | ((uint32_t)f32_to_bf16_rne(v[u].w) << 16);
-        if (i < 16 * q4) *reinterpret_cast<uint2 *>(Hs + rr * HS + k) = make_uint2(lo, hi);
-      }
+    const uint4 *src = reinterpret_cast<const uint4 *>(Hb + (size_t)row0 * d);
+    for (int in = wave; in < (16 * cpr) >> 6; in += K1_WAVES) {
+      const int ci = in * 64 + lane, rr = ci / cpr, j = ci - rr * cpr;
+      __builtin_amdgcn_global_load_lds(src + rr * cpr + (j ^ (rr & 7)),
+                                       (__attribute__((address_space(3))) void *)(Hs + in * 512),
+                                       16, 0, 0);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
   }
   __syncthreads();
 
@@ -374,12 +365,11 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
           const int z = i * nch + c;
           k1_wait_vm(z + RING - 1 < Z ? 4 * (RING - 1) : 0);
           const uint4 *buf = ring + (z % RING) * (K1_CHUNK / 16) + lr * 16;
-          const uint4 *h4 = reinterpret_cast<const uint4 *>(hp + c * 128);
           uint4 av[4], hv[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             av[j] = buf[(4 * j + g) ^ lr];
-            hv[j] = h4[4 * j];
+            hv[j] = hrow[c * 16 + ((4 * j + g) ^ hsw)];
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -396,11 +386,11 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
           for (int pp = 0; pp < K1_PF; ++pp) {
             const int c = c0 + pp;
             if (c < nch) {
-              const uint4 *h4 = reinterpret_cast<const uint4 *>(hp + c * 128);
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(regs[pp][j]),
-                                                             as_bf16x8(h4[j]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(regs[pp][j]), as_bf16x8(hrow[c * 16 + ((4 * g + j) ^ hsw)]), acc, 0,
+                    0, 0);
               if (c + K1_PF < nch) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) regs[pp][j] = ptr[(c + K1_PF) * 16 + j];
@@ -629,6 +619,29 @@ __global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
   }
 }
 
+// Round start for the bf16 path: Hb = bf16_rne(H) with rows padded to a
+// multiple of 16 by zeros (the LM-head kernel copies it into LDS as is), and
+// init_round_request for every request.
+__global__ __launch_bounds__(256) void k1_stage_hidden(const float *__restrict__ H, int rows,
+                                                       int rows_pad, int d,
+                                                       uint16_t *__restrict__ Hb,
+                                                       const int32_t *__restrict__ root, int b,
+                                                       int Dp1, TreeBufs tb) {
+  const int q4 = d >> 2;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;   // one float4 each
+  if (i < rows_pad * q4) {
+    const int rr = i / q4, k = (i - rr * q4) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (rr < rows) v = *reinterpret_cast<const float4 *>(H + (size_t)rr * d + k);
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+    *reinterpret_cast<uint2 *>(Hb + (size_t)rr * d + k) = make_uint2(lo, hi);
+  }
+  if (root)
+    for (int q = blockIdx.x; q < b; q += gridDim.x)
+      init_round_request(q, root, tb, Dp1, threadIdx.x, blockDim.x);
+}
+
 // ----------------------------------------------------------------- host side
 int lmhead_partitions(int V, int wtype, int extra_tiles) {
   const int ntiles = (V + 15) / 16 + (wtype == WT_BF16 ? extra_tiles : 0);
@@ -665,11 +678,14 @@ hipError_t lmhead_prepare(int wtype, int ring, size_t smem) {
 hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st) {
   dim3 grid((a.rows + 15) / 16, a.P);
   if (a.wtype == WT_BF16) {
+    const int rows_pad = (a.rows + 15) & ~15, n4 = rows_pad * (a.d >> 2);
+    hipLaunchKernelGGL(k1_stage_hidden, dim3((n4 + 255) / 256), dim3(256), 0, st, a.H, a.rows,
+                       rows_pad, a.d, a.Hb, a.root, a.b, a.Dp1, a.t);
     const size_t sm = lmhead_smem(a.d, a.wtype, a.ring);
-#define K1_LAUNCH(RING)                                                                         \
-  hipLaunchKernelGGL((k1_lmhead_bf16<RING>), grid, dim3(K1_WAVES * 64), sm, st, a.H, a.rows, a.d, \
-                     static_cast<const uint16_t *>(a.W), a.V, a.bias, a.M, a.part,               \
-                     static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH, a.root, a.b, a.Dp1, a.t)
+#define K1_LAUNCH(RING)                                                                          \
+  hipLaunchKernelGGL((k1_lmhead_bf16<RING>), grid, dim3(K1_WAVES * 64), sm, st, a.Hb, a.rows, a.d, \
+                     static_cast<const uint16_t *>(a.W), a.V, a.bias, a.M, a.part,                \
+                     static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH)
     if (a.ring == 2) K1_LAUNCH(2);
     else if (a.ring == 1) K1_LAUNCH(1);
     else K1_LAUNCH(0);

@@ -68,6 +68,7 @@ struct LMHeadArgs {
   int b, Dp1;
   TreeBufs t;
   int ring;            // bf16: LDS ring depth from lmhead_ring (0 = register path)
+  uint16_t *Hb;        // bf16: [rows rounded up to 16, d] rounded hidden rows (workspace)
 };
 int lmhead_partitions(int V, int wtype, int extra_tiles);
 // LDS ring depth of the bf16 kernel that fits lds_max (0: register path)
