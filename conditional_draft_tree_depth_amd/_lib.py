@@ -16,7 +16,7 @@ STATUS = {0: "DTREE_OK", 1: "DTREE_E_ARG", 2: "DTREE_E_SHAPE", 3: "DTREE_E_DTYPE
           4: "DTREE_E_DEVICE", 5: "DTREE_E_NOMEM", 6: "DTREE_E_HIP", 7: "DTREE_E_STATE"}
 EXPORTS = ("dtree_create", "dtree_build_round", "dtree_superarbol_nodes",
            "dtree_get_trace", "dtree_profile_enable", "dtree_profile_read",
-           "dtree_last_error", "dtree_destroy")
+           "dtree_set_persistent_launch", "dtree_last_error", "dtree_destroy")
 NSTAGES = 5
 STAGES = ("lmhead_topm", "topm_merge", "prologue", "depth_loop", "topb_emit")
 
@@ -81,6 +81,8 @@ def load(path=LIB_PATH):
     lib.dtree_profile_enable.restype = c_i32
     lib.dtree_profile_read.argtypes = [c_vp, P(c_f32), P(c_i32)]
     lib.dtree_profile_read.restype = c_i32
+    lib.dtree_set_persistent_launch.argtypes = [c_vp, c_i32, c_i32]
+    lib.dtree_set_persistent_launch.restype = c_i32
     lib.dtree_last_error.argtypes = [c_vp]
     lib.dtree_last_error.restype = ctypes.c_char_p
     lib.dtree_destroy.argtypes = [c_vp]
@@ -176,3 +178,8 @@ def dtree_last_error(ctx=None):
 
 def dtree_destroy(ctx):
     _check("dtree_destroy", load().dtree_destroy(ctx))
+
+
+def dtree_set_persistent_launch(ctx, cooperative, spin_limit=0):
+    _check("dtree_set_persistent_launch",
+           load().dtree_set_persistent_launch(ctx, int(cooperative), int(spin_limit)), ctx)

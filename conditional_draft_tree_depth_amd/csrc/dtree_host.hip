@@ -66,6 +66,12 @@ struct dtree_ctx {
   // epoch of the next round (flags only ever grow, so they need no reset)
   bool pk = false;
   int pk_rows = 0;
+  // persistent depth loop: plain launches until one of its waits runs out
+  // (it then stores 1 to *pk_fail, host memory the kernel writes through
+  // pk_fail_dev); from then on cooperative launches
+  bool pk_coop = false;
+  uint32_t *pk_fail = nullptr, *pk_fail_dev = nullptr;
+  uint32_t pk_spin = 0;   // 0: the kernel's default limit
   uint32_t epoch = 0;
   // stage timing: kProfRounds rounds x (DTREE_NSTAGES + 1) events
   bool prof = false;
@@ -233,10 +239,17 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
     if (e == hipSuccess) A(launch_transpose_w1s(w->W1, r, s, w->d, w->d + s, ws.w1t, nullptr));
     A(alloc(&ws.flags, persist_flag_words(s)));
     if (e == hipSuccess) A(hipMemset(ws.flags, 0, persist_flag_words(s) * 4));
+    if (e == hipSuccess) A(hipHostMalloc(reinterpret_cast<void **>(&ctx->pk_fail), sizeof(uint32_t),
+                                         hipHostMallocMapped));
+    if (e == hipSuccess) {
+      *ctx->pk_fail = 0u;
+      A(hipHostGetDevicePointer(reinterpret_cast<void **>(&ctx->pk_fail_dev), ctx->pk_fail, 0));
+    }
     if (e == hipSuccess) A(hipDeviceSynchronize());
   }
   if (e != hipSuccess) {
     free_ws(ws);
+    if (ctx->pk_fail) (void)hipHostFree(ctx->pk_fail);
     return reject(DTREE_E_NOMEM, std::string("workspace: ") + hipGetErrorString(e));
   }
   hipError_t pe = lmhead_prepare(w->wtype, ctx->k1_ring, ctx->k1_smem);
@@ -273,6 +286,17 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   if (!(p->beta <= 0.0f)) return fail(ctx, DTREE_E_ARG, "beta must be <= 0 (and not NaN)");
   if (std::isinf(p->beta)) return fail(ctx, DTREE_E_ARG, "beta must be finite");
 
+  // an earlier round's depth-loop kernel could not have all its workgroups
+  // resident at once (the device was shared): that round failed (status bit
+  // 1); report it here, loudly, and use cooperative launches from now on
+  if (ctx->pk_fail && __atomic_load_n(ctx->pk_fail, __ATOMIC_ACQUIRE)) {
+    __atomic_store_n(ctx->pk_fail, 0u, __ATOMIC_RELEASE);
+    ctx->pk_coop = true;
+    return fail(ctx, DTREE_E_HIP,
+                "an earlier round's depth loop could not run all its workgroups at once; its "
+                "outputs are invalid; later rounds use cooperative launches");
+  }
+
   DeviceGuard dg(ctx->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dtree_weights &w = ctx->w;
@@ -283,7 +307,7 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   const size_t esz = wt == WT_BF16 ? 2 : 4;
   ctx->has_round = false;
 
-  // round start (done inside the LM-head kernel)
+  // round start (done by the first kernel of the round)
   TreeBufs tb{};
   tb.NT = ctx->NTcap;
   tb.V = w.V;
@@ -328,9 +352,9 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
     prof_mark(ctx, 3, st);
     PersistArgs pa{batch, D, M, K, W, s, w.e, w.V, w.W_ih, w.W_hh, w.Emb, w.b_ih, w.b_hh,
                    ws.C, root, ws.G, ws.g, ws.pk_terms, ws.pk_terms + persist_terms_floats(s),
-                   ws.pk_part, ws.gitab, ws.flags,
+                   ws.pk_part, ws.gitab, ws.flags, ctx->pk_fail_dev, ctx->pk_spin,
                    ctx->epoch, tb};
-    HIPCHK(ctx, launch_depth_persistent(pa, st));
+    HIPCHK(ctx, launch_depth_persistent(pa, ctx->pk_coop, st));
     ctx->epoch += (uint32_t)D + 1u;
     for (int dd = 0; dd < D; ++dd) {
       off += A * K;
@@ -458,6 +482,17 @@ extern "C" dtree_status dtree_profile_read(dtree_ctx *ctx, float *ms, int32_t *r
   return DTREE_OK;
 }
 
+extern "C" dtree_status dtree_set_persistent_launch(dtree_ctx *ctx, int32_t cooperative,
+                                                    int32_t spin_limit) {
+  if (!ctx) return DTREE_E_ARG;
+  ctx->err.clear();
+  if (cooperative != 0 && cooperative != 1) return fail(ctx, DTREE_E_ARG, "cooperative must be 0 or 1");
+  if (spin_limit < 0) return fail(ctx, DTREE_E_ARG, "spin_limit must be >= 0");
+  ctx->pk_coop = cooperative == 1;
+  ctx->pk_spin = (uint32_t)spin_limit;
+  return DTREE_OK;
+}
+
 extern "C" const char *dtree_last_error(const dtree_ctx *ctx) {
   return ctx ? ctx->err.c_str() : g_create_err.c_str();
 }
@@ -467,6 +502,7 @@ extern "C" dtree_status dtree_destroy(dtree_ctx *ctx) {
   {
     DeviceGuard dg(ctx->device);
     free_ws(ctx->ws);
+    if (ctx->pk_fail) (void)hipHostFree(ctx->pk_fail);
     if (ctx->prof_ev) {
       for (int i = 0; i < kProfRounds * (DTREE_NSTAGES + 1); ++i) (void)hipEventDestroy(ctx->prof_ev[i]);
       delete[] ctx->prof_ev;

@@ -167,6 +167,8 @@ struct PKParams {
   float *part;           // [2][NC][PK_MAXELL]
   float *gitab;          // [D slots][PK_MAXC][3s]: slot 0 roots, slot t+1 depth t
   uint32_t *flags;       // [(NC + NP) * 64]: consumer arrivals, then producer slots
+  uint32_t *host_fail;   // host-visible word, set when a wait ran out (or null)
+  uint32_t spin;         // polls before a wait gives up
   uint32_t epoch0;
   TreeBufs t;
 };
@@ -224,10 +226,13 @@ __device__ __forceinline__ void pk_raise(uint32_t *flag, uint32_t epoch) {
 
 // Threads i < n poll flags[i * 64] >= epoch, threads 64 .. 64 + npf - 1 poll
 // pf[(i - 64) * 64] >= pepoch; false if any wait exceeded the spin limit
-// (status bit 1 is then set and the caller leaves).
+// (status bit 1 is then set, 1 is stored to the host-visible word host_fail,
+// and the caller leaves).  A wait can only run out if some workgroup of the
+// grid never became resident next to the waiting ones.
 __device__ __forceinline__ bool pk_wait(const uint32_t *flags, int n, uint32_t epoch,
                                         const uint32_t *pf, int npf, uint32_t pepoch,
-                                        uint32_t *status, int *bad) {
+                                        uint32_t *status, uint32_t *host_fail, unsigned spin,
+                                        int *bad) {
   if (threadIdx.x == 0) *bad = 0;
   __syncthreads();
   const uint32_t *f = nullptr;
@@ -238,8 +243,9 @@ __device__ __forceinline__ bool pk_wait(const uint32_t *flags, int n, uint32_t e
   if (f) {
     unsigned k = 0;
     while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
-      if (++k > PK_SPIN) {
+      if (++k > spin) {
         atomicOr(status, 2u);
+        if (host_fail) __hip_atomic_store(host_fail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         *bad = 1;
         break;
       }
@@ -476,7 +482,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     finfo[q * 4 + 2] = __float_as_int(0.f);     // score
   }
   // root state from slot 0 (h = 0, so the state part is b_hh)
-  if (!pk_wait(cflags, 0, 0u, pflags, PK_PPC, p.epoch0 + 1, p.t.status, misc)) return;
+  if (!pk_wait(cflags, 0, 0u, pflags, PK_PPC, p.epoch0 + 1, p.t.status, p.host_fail, p.spin, misc)) return;
   for (int i = tid; i < b * PK_CU; i += PK_THREADS) {
     const int q = i / PK_CU, u = i - q * PK_CU;
     const float *a = p.gitab + (size_t)q * 3 * s + j0 + u;
@@ -498,7 +504,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
   }
   pk_raise(cflags + c * 64, p.epoch0 + 1);
   // (the producers' next slot is waited for only where depth 0 first needs it)
-  if (!pk_wait(cflags, p.NC, p.epoch0 + 1, pflags, 0, 0u, p.t.status, misc)) return;
+  if (!pk_wait(cflags, p.NC, p.epoch0 + 1, pflags, 0, 0u, p.t.status, p.host_fail, p.spin, misc)) return;
 
   // input projections of table slot `slot` (this workgroup's units) into LDS
   auto load_gis = [&](int slot) {
@@ -718,7 +724,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     }
     // depth 0: the producers' slot 1 was not needed before the GRU step
     if (dd == 0) {
-      if (!pk_wait(cflags, 0, 0u, pflags, PK_PPC, p.epoch0 + 2, p.t.status, misc)) return;
+      if (!pk_wait(cflags, 0, 0u, pflags, PK_PPC, p.epoch0 + 2, p.t.status, p.host_fail, p.spin, misc)) return;
       load_gis(1);
     }
     // the fragment table under red was read before the barriers above
@@ -807,7 +813,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     write_records();
     // producer slot dd + 2 holds the candidates of depth dd + 1
     const uint32_t pe = p.epoch0 + (dd + 2 < D ? dd + 3 : D);
-    if (!pk_wait(cflags, p.NC, p.epoch0 + dd + 2, pflags, PK_PPC, pe, p.t.status, misc)) return;
+    if (!pk_wait(cflags, p.NC, p.epoch0 + dd + 2, pflags, PK_PPC, pe, p.t.status, p.host_fail, p.spin, misc)) return;
     uint16_t *tmp = Tcur; Tcur = Tnext; Tnext = tmp;
     float *tn = sn_cur; sn_cur = sn_nxt; sn_nxt = tn;
     off += Z;
@@ -864,7 +870,7 @@ hipError_t launch_corr_tables(int rows, int M, int r, int s, const void *W2, con
   return hipGetLastError();
 }
 
-hipError_t launch_depth_persistent(const PersistArgs &a, hipStream_t st) {
+hipError_t launch_depth_persistent(const PersistArgs &a, bool cooperative, hipStream_t st) {
   if (a.s % 128 || a.D < 1 || a.D > PK_MAXD) return hipErrorInvalidValue;
   PKParams p{};
   p.b = a.b; p.D = a.D; p.M = a.M; p.K = a.K; p.W = a.W; p.s = a.s; p.e = a.e; p.V = a.V;
@@ -878,7 +884,19 @@ hipError_t launch_depth_persistent(const PersistArgs &a, hipStream_t st) {
   p.T1 = reinterpret_cast<uint16_t *>(a.T1);
   p.part = a.part; p.gitab = a.gitab; p.flags = a.flags;
   p.epoch0 = a.epoch0;
+  p.host_fail = a.host_fail;
+  p.spin = a.spin ? a.spin : PK_SPIN;
   p.t = a.t;
+  // Every workgroup needs a whole CU (LDS) and all of them must run at once.
+  // A plain launch onto an otherwise idle device places them all; the flag
+  // waits detect the case where they could not be (see pk_wait), and the
+  // caller then switches to cooperative launches, which guarantee it at a
+  // higher launch cost.
+  if (!cooperative) {
+    hipLaunchKernelGGL(k_depth_persistent, dim3(p.NC + p.NP), dim3(PK_THREADS), pk_layout().total,
+                       st, p);
+    return hipGetLastError();
+  }
   void *args[] = {&p};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_depth_persistent),
                                     dim3(p.NC + p.NP), dim3(PK_THREADS), args, pk_layout().total, st);

@@ -127,6 +127,8 @@ struct PersistArgs {
   float *T0, *T1;        // published states (persist_terms_floats each)
   float *part, *gitab;
   uint32_t *flags;
+  uint32_t *host_fail;   // device address of a host-visible word (or null)
+  uint32_t spin;         // polls before a wait gives up (0: the default)
   uint32_t epoch0;
   TreeBufs t;
 };
@@ -144,7 +146,7 @@ hipError_t launch_transpose_w1s(const void *W1, int r, int s, int d, int ldw1, v
 hipError_t launch_corr_tables(int rows, int M, int r, int s, const void *W2, const void *W1t,
                               const int32_t *C, const float *Cl, const float *uH, float *G,
                               float *g, hipStream_t st);
-hipError_t launch_depth_persistent(const PersistArgs &a, hipStream_t st);
+hipError_t launch_depth_persistent(const PersistArgs &a, bool cooperative, hipStream_t st);
 hipError_t corr_logits_prepare(int wtype, size_t smem);
 
 }  // namespace dtree

@@ -136,12 +136,32 @@ dtree_status dtree_create(const dtree_weights *w, const dtree_caps *caps,
  * lexicographically ascending, so parent[i] < i.  Slots past n_nodes hold
  * tok/parent/depth = -1, score = -inf and zero mask rows and columns.
  * H and root must stay valid until the stream work completes.  A context is
- * not reentrant: calls on one context must not overlap.                     */
+ * not reentrant: calls on one context must not overlap.
+ * With bf16 weights and small batches the depth loop runs as one persistent
+ * kernel whose workgroups wait on each other (each needs a whole CU).  It is
+ * launched like any other kernel; should its workgroups not all become
+ * resident together (another stream holding CUs for a long time), its waits
+ * run out after a bounded time, that round's status gets bit 1, the next
+ * dtree_build_round on the context returns DTREE_E_HIP without enqueueing
+ * anything, and every later round uses cooperative launches, which
+ * guarantee co-residency at a higher launch cost (about 18 us on MI355X).   */
 dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
                                int32_t batch, const float *H,
                                const int32_t *root, int32_t *tok,
                                int32_t *parent, int32_t *depth, float *score,
                                uint8_t *mask, int32_t *n_nodes, void *stream);
+
+/* Launch of the persistent depth loop (see dtree_build_round).
+ *   cooperative  0: plain launches (the default; a context switches itself to
+ *                cooperative launches after a round whose waits ran out),
+ *                1: cooperative launches from now on
+ *   spin_limit   polls before a wait between its workgroups gives up and the
+ *                round fails with status bit 1; 0 restores the default
+ *                (about a second); tests use a tiny value to exercise the
+ *                failure report without a stalled GPU
+ * Takes effect from the next round; DTREE_E_ARG for other values.          */
+dtree_status dtree_set_persistent_launch(dtree_ctx *ctx, int32_t cooperative,
+                                         int32_t spin_limit);
 
 /* Number of superarbol nodes (root included) a round with `p` builds per
  * request, or -1 if p is invalid.  Pure host arithmetic.                     */
@@ -160,7 +180,10 @@ typedef struct {
   int32_t *sel;        /* [B]    selected node ids in selection order, -1 pad */
   int32_t n_sa;        /* out: superarbol nodes incl. root                   */
   int32_t status;      /* out: device status bits (0 = fine; bit 0: the
-                          selection was not closed under parents)           */
+                          selection was not closed under parents; bit 1:
+                          the persistent depth loop could not run all its
+                          workgroups at once, the round's outputs are
+                          invalid)                                          */
 } dtree_trace;
 dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace *out);
 

@@ -130,3 +130,50 @@ def test_tied_base_logits(gpu_lib, wtype, M, mode):
         perm = np.random.default_rng(5).permutation(V)
         x["weights"]["bias"] = (-0.25 * np.floor(perm / 97.0)).astype(np.float32)
     check_config(x, cfg, f"tied {wtype} M={M} {mode}", max_tie_frac=0.0)
+
+
+def test_persistent_launch_modes(gpu_lib):
+    """The persistent depth loop builds the same round with plain and with
+    cooperative launches.  A round whose waits run out (forced from the host
+    with a one-poll spin limit, so every kernel still ends normally) reports
+    status bit 1, the next call fails loudly, and the context then uses
+    cooperative launches and builds correct rounds again."""
+    import torch
+    from conditional_draft_tree_depth_amd import _lib, runner
+    cfg = synth.custom_config(cfg_id=9100, d=128, V=3000, e=128, s=128, r=32, D=5, M=32, K=4,
+                              W=8, B=40, beta=-0.05, batch=1, wtype="bf16")
+    x = synth.make_inputs(cfg, 0)
+    wd, H, root = runner.to_device(x)
+    rnd = runner.Round(wd, cfg.wtype, caps_for(cfg), cfg.batch, cfg.D, cfg.M, cfg.K, cfg.W,
+                       cfg.B, cfg.beta)
+    keys = ("tok", "parent", "depth", "score", "mask")
+    try:
+        rnd.run(H, root)
+        torch.cuda.synchronize()
+        plain = rnd.outputs()
+        assert rnd.trace(0)["status"] == 0
+        _lib.dtree_set_persistent_launch(rnd.ctx, 1)
+        rnd.run(H, root)
+        torch.cuda.synchronize()
+        coop = rnd.outputs()
+        for k in keys:
+            assert np.array_equal(plain[0][k], coop[0][k]), k
+        print("[gpu] forcing a wait to run out (one poll)", flush=True)
+        _lib.dtree_set_persistent_launch(rnd.ctx, 0, 1)
+        rnd.run(H, root)
+        torch.cuda.synchronize()
+        assert rnd.trace(0)["status"] & 2
+        _lib.dtree_set_persistent_launch(rnd.ctx, 0, 0)
+        with pytest.raises(_lib.DTreeError):
+            rnd.run(H, root)
+        rnd.run(H, root)
+        torch.cuda.synchronize()
+        again = rnd.outputs()
+        assert rnd.trace(0)["status"] == 0
+        for k in keys:
+            assert np.array_equal(plain[0][k], again[0][k]), k
+        with pytest.raises(_lib.DTreeError):
+            _lib.dtree_set_persistent_launch(rnd.ctx, 2)
+    finally:
+        rnd.close()
+    check_config(x, cfg, "persistent launch modes", max_tie_frac=0.0)
