@@ -8,8 +8,9 @@ for one batch of synthetic inputs (seeded, shapes of the named workload).
 Prints ONE JSON line (rank 0).  ``value`` comes from K timed steps with
 nothing else on the stream.  ``roofline`` is for the dominant kernel (the
 LM-head GEMM with its fused per-slice Top-M), timed over a second pass of K
-steps with HIP events recorded by the library around each stage on the
-round's own stream; ``cpu_baseline`` times the CPU oracle on a bounded sample
+steps with HIP events on the round's own stream (the library records them
+between stages; the LM-head kernel's pair is taken at the kernel's own start
+and end, as a kernel trace measures it); ``cpu_baseline`` times the CPU oracle on a bounded sample
 of the same workload.
 """
 import argparse

@@ -17,8 +17,8 @@ STATUS = {0: "DTREE_OK", 1: "DTREE_E_ARG", 2: "DTREE_E_SHAPE", 3: "DTREE_E_DTYPE
 EXPORTS = ("dtree_create", "dtree_build_round", "dtree_superarbol_nodes",
            "dtree_get_trace", "dtree_profile_enable", "dtree_profile_read",
            "dtree_set_persistent_launch", "dtree_last_error", "dtree_destroy")
-NSTAGES = 5
-STAGES = ("lmhead_topm", "topm_merge", "prologue", "depth_loop", "topb_emit")
+NSTAGES = 6
+STAGES = ("round_start", "lmhead_topm", "topm_merge", "prologue", "depth_loop", "topb_emit")
 
 c_i32, c_vp, c_f32 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
 

@@ -328,10 +328,15 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   LMHeadArgs la{H, rows, d, w.W_lm, wt, w.V, w.lm_bias, M, ctx->P, ws.part,
                 fuse_uH ? w.W1 : nullptr, d + s, r, ws.uH,
                 root, batch, D + 1, tb, ctx->k1_ring, ws.hb};
-  HIPCHK(ctx, launch_lmhead(la, st));
-  prof_mark(ctx, 1, st);
+  HIPCHK(ctx, launch_stage_hidden(la, st));
+  // the LM-head stage is timed by the kernel's own start and end (no marker
+  // packets around it)
+  hipEvent_t k1ev[2] = {nullptr, nullptr};
+  if (ctx->prof && ctx->prof_n < kProfRounds)
+    for (int i = 0; i < 2; ++i) k1ev[i] = ctx->prof_ev[ctx->prof_n * (DTREE_NSTAGES + 1) + 1 + i];
+  HIPCHK(ctx, launch_lmhead(la, st, k1ev[0], k1ev[1]));
   HIPCHK(ctx, launch_topm_merge(ws.part, ctx->P, M, rows, ws.C, ws.Cl, st));
-  prof_mark(ctx, 2, st);
+  prof_mark(ctx, 3, st);
   // K2: uH = W1[:, :d] . Hq for every (request, depth), when not fused above
   GemmArgs g{};
   if (!fuse_uH) {
@@ -349,7 +354,7 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
     // whole depth loop as one cooperative launch
     HIPCHK(ctx, launch_corr_tables(batch * D * M, M, r, s, w.W2, ws.w1t, ws.C, ws.Cl, ws.uH,
                                    ws.G, ws.g, st));
-    prof_mark(ctx, 3, st);
+    prof_mark(ctx, 4, st);
     PersistArgs pa{batch, D, M, K, W, s, w.e, w.V, w.W_ih, w.W_hh, w.Emb, w.b_ih, w.b_hh,
                    ws.C, root, ws.G, ws.g, ws.pk_terms, ws.pk_terms + persist_terms_floats(s),
                    ws.pk_part, ws.gitab, ws.flags, ctx->pk_fail_dev, ctx->pk_spin,
@@ -366,7 +371,7 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
                  w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
     HIPCHK(ctx, launch_gemm(g, st));
     HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, w.b_hh, nullptr, nullptr, ws.S[0], st));
-    prof_mark(ctx, 3, st);
+    prof_mark(ctx, 4, st);
     for (int dd = 0; dd < D; ++dd) {
       // u = uH[req, dd] + W1[:, d:] . S  for every expanded branch
       g = GemmArgs{batch * A, r, s, ws.S[sc], WT_F32, s, nullptr, 0,
@@ -395,10 +400,10 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
     }
   }
   const int NT = off;
-  prof_mark(ctx, 4, st);
+  prof_mark(ctx, 5, st);
   HIPCHK(ctx, launch_topb_emit(batch, NT, B, p->beta, c.max_B, tb, tok, parent, depth, score,
                                mask, n_nodes, st));
-  prof_mark(ctx, 5, st);
+  prof_mark(ctx, 6, st);
   if (ctx->prof && ctx->prof_n < kProfRounds) ++ctx->prof_n;
   ctx->has_round = true;
   ctx->last = *p;

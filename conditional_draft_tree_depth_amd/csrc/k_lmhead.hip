@@ -17,6 +17,7 @@
 // k per 128-wide chunk (64-byte row segments of W_lm).  A workgroup owns a
 // contiguous slice of tiles; after its GEMM it re-uses the LDS of the hidden
 // rows to stage its logits and extracts each row's best M keys.
+#include <hip/hip_ext.h>
 #include <type_traits>
 
 #include "common.hpp"
@@ -675,26 +676,32 @@ hipError_t lmhead_prepare(int wtype, int ring, size_t smem) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
 }
 
-hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st) {
+hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid((a.rows + 15) / 16, a.P);
   if (a.wtype == WT_BF16) {
-    const int rows_pad = (a.rows + 15) & ~15, n4 = rows_pad * (a.d >> 2);
-    hipLaunchKernelGGL(k1_stage_hidden, dim3((n4 + 255) / 256), dim3(256), 0, st, a.H, a.rows,
-                       rows_pad, a.d, a.Hb, a.root, a.b, a.Dp1, a.t);
     const size_t sm = lmhead_smem(a.d, a.wtype, a.ring);
-#define K1_LAUNCH(RING)                                                                          \
-  hipLaunchKernelGGL((k1_lmhead_bf16<RING>), grid, dim3(K1_WAVES * 64), sm, st, a.Hb, a.rows, a.d, \
-                     static_cast<const uint16_t *>(a.W), a.V, a.bias, a.M, a.part,                \
-                     static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH)
+#define K1_LAUNCH(RING)                                                                           \
+  hipExtLaunchKernelGGL((k1_lmhead_bf16<RING>), grid, dim3(K1_WAVES * 64), (uint32_t)sm, st, ev0,  \
+                        ev1, 0u, (const uint16_t *)a.Hb, a.rows, a.d,                              \
+                        static_cast<const uint16_t *>(a.W), a.V, a.bias, a.M, a.part,              \
+                        static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH)
     if (a.ring == 2) K1_LAUNCH(2);
     else if (a.ring == 1) K1_LAUNCH(1);
     else K1_LAUNCH(0);
 #undef K1_LAUNCH
   } else {
-    hipLaunchKernelGGL(k1_lmhead_f32, grid, dim3(K1F_THREADS), 0, st, a.H, a.rows, a.d,
-                       static_cast<const float *>(a.W), a.V, a.bias, a.M, a.part, a.root, a.b,
-                       a.Dp1, a.t);
+    hipExtLaunchKernelGGL(k1_lmhead_f32, grid, dim3(K1F_THREADS), 0u, st, ev0, ev1, 0u, a.H,
+                          a.rows, a.d, static_cast<const float *>(a.W), a.V, a.bias, a.M, a.part,
+                          a.root, a.b, a.Dp1, a.t);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_hidden(const LMHeadArgs &a, hipStream_t st) {
+  if (a.wtype != WT_BF16) return hipSuccess;   // the fp32 kernel starts the round itself
+  const int rows_pad = (a.rows + 15) & ~15, n4 = rows_pad * (a.d >> 2);
+  hipLaunchKernelGGL(k1_stage_hidden, dim3((n4 + 255) / 256), dim3(256), 0, st, a.H, a.rows,
+                     rows_pad, a.d, a.Hb, a.root, a.b, a.Dp1, a.t);
   return hipGetLastError();
 }
 

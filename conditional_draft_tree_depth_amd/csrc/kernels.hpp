@@ -75,7 +75,11 @@ int lmhead_partitions(int V, int wtype, int extra_tiles);
 int lmhead_ring(int d, int wtype, size_t lds_max);
 size_t lmhead_smem(int d, int wtype, int ring);
 hipError_t lmhead_prepare(int wtype, int ring, size_t smem);
-hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st);
+// bf16: round start (k1_stage_hidden: Hb, init_round_request); before launch_lmhead
+hipError_t launch_stage_hidden(const LMHeadArgs &a, hipStream_t st);
+// ev0 / ev1 (or null): events that take the kernel's own start and end times
+hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st, hipEvent_t ev0 = nullptr,
+                         hipEvent_t ev1 = nullptr);
 // ---- K1b: the M best keys of each row from its P lists -> C (tokens), Cl (logits)
 size_t topm_merge_smem(int P);
 hipError_t launch_topm_merge(const uint64_t *part, int P, int M, int rows,

@@ -189,15 +189,16 @@ dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace *out);
 
 /* Stage timing with HIP events recorded on the round's own stream.  When
  * enabled, every round records events between its stages:
- *   0 base-logit GEMM with fused Top-M   1 Top-M merge
- *   2 path-independent prologue (uH, root GRU state)
- *   3 depth loop (correction, selection, GRU, all depths)
- *   4 global Top-B, canonical order and mask
+ *   0 round start (bf16: hidden rows rounded once; empty with fp32 weights)
+ *   1 base-logit GEMM with fused per-slice Top-M   2 Top-M merge
+ *   3 path-independent prologue (uH, correction tables or root GRU state)
+ *   4 depth loop (correction, selection, GRU, all depths)
+ *   5 global Top-B, canonical order and mask
  * dtree_profile_read synchronises, writes the summed milliseconds of each
  * stage over the rounds recorded since dtree_profile_enable(ctx, 1) to
  * ms[0..DTREE_NSTAGES) and the round count to *rounds, and clears them.
  * At most 4096 rounds are recorded; later rounds are not timed.            */
-#define DTREE_NSTAGES 5
+#define DTREE_NSTAGES 6
 dtree_status dtree_profile_enable(dtree_ctx *ctx, int enable);
 dtree_status dtree_profile_read(dtree_ctx *ctx, float *ms, int32_t *rounds);
 
