@@ -10,9 +10,10 @@
 // tree-attention verification uses ("Resumen Técnico: DominoTree", Main
 // components 5).  The closure is checked; a violation sets status bit 0.
 //
-// One workgroup per request.  Selection: up to TB_THREADS nodes, the rank of
-// every node among all keys is counted directly (a few threads per node, no
-// sort); larger superarbols are sorted (bitonic).  The mask comes from each
+// One workgroup per request.  Selection: up to TB_RANK_MAX nodes, the rank
+// of every node among all keys is counted directly (a few threads per node);
+// larger superarbols find the B-th largest key by radix passes and rank only
+// the selected keys among themselves.  The mask comes from each
 // selected node's ancestor at every depth: j is an ancestor-or-self of i iff
 // depth(j) <= depth(i) and i's ancestor at depth(j) is j.
 #include "common.hpp"
@@ -22,11 +23,24 @@ namespace dtree {
 
 constexpr int TB_THREADS = 1024;
 constexpr int TB_MAXDEP = 32;   // depths 0 .. 31
+constexpr int TB_RANK_MAX = 256;   // superarbols up to this size: rank counting
+
+// inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within rows
+// of 16 lanes, then the row ends broadcast into the later rows)
+__device__ __forceinline__ int wave_scan_add(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31, rows 2, 3
+  return v;
+}
 
 // LDS: keys (selection), later the canonical scratch, then the ancestor
 // table; ids (sorted order or selection ranks); the rest.
 struct TBLayout {
-  size_t keys, ids, map, onode, opar, odep, canon, total;
+  size_t keys, ids, map, onode, opar, odep, canon, hist, skey, total;
 };
 
 __host__ __device__ inline TBLayout tb_layout(int NT, int B) {
@@ -45,6 +59,8 @@ __host__ __device__ inline TBLayout tb_layout(int NT, int B) {
   L.opar = take((size_t)N * 4);
   L.odep = take((size_t)N * 4);
   L.canon = take((size_t)N * 4);
+  L.hist = take((size_t)(256 + 8) * 4);   // radix histogram, then scalars
+  L.skey = take((size_t)N * 8);           // selected keys (radix path)
   L.total = o;
   return L;
 }
@@ -93,7 +109,74 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
   __syncthreads();
 
   // the selected nodes in selection order: onode[1 + rank] (keys are distinct)
-  if (Nsa <= TB_THREADS) {
+  if (Nsa > TB_RANK_MAX) {
+    // The Bsel-th largest key by radix passes of 8 bits, most significant
+    // first: each pass counts the digits of the keys that still match the
+    // prefix found so far and keeps the digit where the count from the top
+    // reaches the number of keys still wanted.  The keys >= it are exactly
+    // the selection; their order comes from ranks among them.
+    uint32_t *hist = reinterpret_cast<uint32_t *>(smem + L.hist);
+    int *ctl = reinterpret_cast<int *>(hist + 256);
+    uint64_t *skey = reinterpret_cast<uint64_t *>(smem + L.skey);
+    const int lane = tid & 63;
+    uint64_t prefix = 0, pmask = 0;
+    int need = Bsel;
+    for (int b = tid; b < 256; b += TB_THREADS) hist[b] = 0u;
+    __syncthreads();
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int i = tid; i < Nsa; i += TB_THREADS) {
+        const uint64_t k = keys[i];
+        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // lane l: digits 255 - 4l .. 252 - 4l (counts from the top), then
+        // clears them for the next pass
+        uint32_t c[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = hist[255 - 4 * lane - j];
+          hist[255 - 4 * lane - j] = 0u;
+          sum += c[j];
+        }
+        uint32_t before = (uint32_t)wave_scan_add((int)sum) - sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (before < (uint32_t)need && before + c[j] >= (uint32_t)need) {
+            ctl[0] = 255 - 4 * lane - j;
+            ctl[1] = (int)before;
+            ctl[2] = (int)c[j];
+          }
+          before += c[j];
+        }
+      }
+      __syncthreads();
+      prefix |= (uint64_t)(uint32_t)ctl[0] << shift;
+      pmask |= 0xFFull << shift;
+      need -= ctl[1];
+      // every key left in this digit's bucket is wanted: the selection is
+      // the keys whose masked value reaches the prefix
+      if (ctl[2] == need) break;
+    }
+    __syncthreads();
+    if (tid == 0) ctl[2] = 0;
+    __syncthreads();
+    for (int i = tid; i < Nsa; i += TB_THREADS)
+      if ((keys[i] & pmask) >= prefix) {
+        const int at = atomicAdd(&ctl[2], 1);
+        if (at < Bsel) {   // (exactly Bsel: the keys are distinct)
+          skey[at] = keys[i];
+          ids[at] = i + 1;
+        }
+      }
+    __syncthreads();
+    for (int i = tid; i < Bsel; i += TB_THREADS) {
+      const uint64_t k = skey[i];
+      int rk = 0;
+      for (int j = 0; j < Bsel; ++j) rk += skey[j] > k ? 1 : 0;
+      if (rk < Bsel) onode[1 + rk] = ids[i];
+    }
+  } else {
     int tpn = 1;   // threads per node, a power of two
     while (tpn * 2 * Nsa <= TB_THREADS && tpn < 16) tpn *= 2;
     const int i = tid / tpn, part = tid & (tpn - 1);
@@ -119,9 +202,6 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
     __syncthreads();
     for (int i2 = tid; i2 < Nsa; i2 += TB_THREADS)
       if (rank[i2] < Bsel) onode[1 + rank[i2]] = i2 + 1;
-  } else {
-    block_bitonic_desc(keys, ids, npad);
-    for (int i2 = tid; i2 < Bsel; i2 += TB_THREADS) onode[1 + i2] = ids[i2];
   }
   __syncthreads();
 
