@@ -478,7 +478,8 @@ __global__ __launch_bounds__(K1F_THREADS) void k1_lmhead_f32(
 // row's M best could be is listed), leaving exactly M keys to rank.
 constexpr int K1B_THREADS = 512;
 constexpr int K1B_FAST = 2048;   // gathered keys
-constexpr int K1B_UNROLL = 8;
+constexpr int K1B_UNROLL = 8;   // live lists per wave in flight
+static_assert(K1_LCAP <= 128, "a list's keys are two per lane");
 
 size_t topm_merge_smem(int P) {
   return (size_t)K1B_FAST * 8 + (size_t)P * 8 + (size_t)P * 4 * 2;
@@ -560,23 +561,28 @@ __global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
     hmax = h > hmax ? h : hmax;
   }
   hmax = block_max(hmax);   // (its barriers also publish live / nlive)
-  const int nslot = nlive * K1_LCAP;
 
   // f(key) for every key of the live lists
+  // f(key) for every key of the live lists: wave w takes lists w, w + 8, ...
+  // (K1B_UNROLL of them at once), lane l their keys l and l + 64
   auto sweep = [&](auto &&fn) {
-    for (int i0 = tid; i0 < nslot; i0 += K1B_UNROLL * nt) {
-      uint64_t v[K1B_UNROLL];
+    for (int l0 = wave; l0 < nlive; l0 += nwv * K1B_UNROLL) {
+      uint64_t v[K1B_UNROLL][2];
 #pragma unroll
       for (int u = 0; u < K1B_UNROLL; ++u) {
-        const int i = i0 + u * nt;
-        v[u] = 0ull;
-        if (i < nslot) {
-          const int l = live[i / K1_LCAP], k = i % K1_LCAP;
-          if (k < cnt[l]) v[u] = base[(size_t)l * K1_LSTRIDE + k];
+        const int li = l0 + u * nwv;
+        const int l = li < nlive ? live[li] : 0, c = li < nlive ? cnt[l] : 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = lane + 64 * h;
+          v[u][h] = k < c ? base[(size_t)l * K1_LSTRIDE + k] : 0ull;
         }
       }
 #pragma unroll
-      for (int u = 0; u < K1B_UNROLL; ++u) fn(v[u]);
+      for (int u = 0; u < K1B_UNROLL; ++u) {
+        fn(v[u][0]);
+        fn(v[u][1]);
+      }
     }
   };
   auto gather = [&](uint64_t thr) {
