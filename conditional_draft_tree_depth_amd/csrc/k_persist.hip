@@ -39,7 +39,7 @@ __device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
 // columns, on MFMA with fragments read straight from global memory: A = the
 // candidates' W2 rows (gathered by token), B = W1t rows, W1t = W1[:, d:]^T
 // zero-padded to a multiple of 32 in the rank (made once per context), fp32
-// sums over the rank.  The workgroups of column block 0 also produce
+// sums over the rank.  The first waves of the row block also produce
 // g = Cl + W2[C] . uH (one wave per row, fp32).
 constexpr int CT_NB = 64;   // state columns per workgroup
 constexpr int CT_THREADS = 256;
@@ -84,17 +84,17 @@ __global__ __launch_bounds__(CT_THREADS) void k_corr_tables(int rows, int M, int
       G[((size_t)qd * s + n) * M + jj] = acc[t];
     }
   }
-  if (blockIdx.x == 0) {
-    for (int rr = wave; rr < 16; rr += CT_THREADS / 64) {
-      const int row = row0 + rr;
-      if (row >= rows) continue;
-      const uint16_t *w2 = W2 + (size_t)max(C[row], 0) * r;
-      const float *uh = uH + (size_t)(row / M) * r;   // row / M = request * D + depth
-      float part = 0.f;
-      for (int k = lane; k < r; k += 64) part += bf16_bits_to_f32(w2[k]) * uh[k];
-      part = wave_sum_f32(part);
-      if (lane == 0) g[row] = Cl[row] + part;
-    }
+  // g: one wave per row, spread over the column blocks of this row block
+  for (int rr = blockIdx.x * (CT_THREADS / 64) + wave; rr < 16;
+       rr += gridDim.x * (CT_THREADS / 64)) {
+    const int row = row0 + rr;
+    if (row >= rows) break;
+    const uint16_t *w2 = W2 + (size_t)max(C[row], 0) * r;
+    const float *uh = uH + (size_t)(row / M) * r;   // row / M = request * D + depth
+    float part = 0.f;
+    for (int k = lane; k < r; k += 64) part += bf16_bits_to_f32(w2[k]) * uh[k];
+    part = wave_sum_f32(part);
+    if (lane == 0) g[row] = Cl[row] + part;
   }
 }
 
