@@ -95,6 +95,23 @@ def cpu_baseline(cfg, inputs, budget_s=12.0, max_rounds=50):
                       f"superarbol, global Top-B, emission; literal-heap check off), {el:.1f} s"}
 
 
+def _per_round_us(torch, stream, run, n, before=None):
+    """p10 / p50 / p90 of n single rounds, each between its own event pair."""
+    evs = []
+    for _ in range(n):
+        if before is not None:
+            before()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    q = lambda f: us[min(len(us) - 1, int(f * (len(us) - 1) + 0.5))]
+    return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "rounds": n}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,7 +125,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(requests shard across GPUs with no exchange; see the design notes)",
+              "(requests would shard across GPUs with no exchange between them)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -151,8 +168,28 @@ def main():
     torch.cuda.synchronize()
     stage_ms, nrec = _lib.dtree_profile_read(rnd.ctx)
     _lib.dtree_profile_enable(rnd.ctx, False)
+    # pass 3: per-round latency, an event pair around every round
+    lat = _per_round_us(torch, stream, lambda: rnd.run(H, root), args.steps)
+    # pass 4: cold rounds, a 512 MiB scratch write (which evicts the caches)
+    # before every one of them, timed by its own event pair
+    scratch = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    cold = _per_round_us(torch, stream, lambda: rnd.run(H, root), 20,
+                         before=lambda: scratch.fill_(1.0))
+    del scratch
     out0 = rnd.outputs()[0]
     rnd.close()
+    # a device copy of 1 GiB (read + write) as the achievable streaming rate
+    a = torch.empty(256 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
 
     ms = (t1 - t0) * 1e3 / args.steps
     ev_ms = ev0.elapsed_time(ev1) / args.steps
@@ -187,7 +224,11 @@ def main():
         "round_roofline": {"t_roof_us": t_roof * 1e6, "frac": t_roof / (ms * 1e-3),
                            "bytes": cnt["round_bytes"], "flops": cnt["round_flops"]},
         "stages_us": {k: v * 1e3 / max(nrec, 1) for k, v in stage_ms.items()},
+        "request_rounds_per_s": 1e3 / ms * cfg.batch,
         "event_ms_per_step": ev_ms,
+        "latency_us": lat,
+        "cold_latency_us": cold,
+        "stream_copy_GBps": copy_gbs,
         "tree_nodes": int(out0["n_nodes"]),
         "context": "pages report 3.67 ms -> 2.31 ms per round for their heap-driven "
                    "tree builder on Qwen3-4B (hardware, precision and tree sizes not stated)",
