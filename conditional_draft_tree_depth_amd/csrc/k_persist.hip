@@ -10,7 +10,7 @@
 // launch.  Producers (8 units each, their W_ih rows in registers) compute the
 // input projections W_ih Emb[tok] + b_ih of the root tokens and of every
 // depth's candidates ahead of time; nothing they do waits on anyone.
-// Consumers (32 units each, their W_hh rows in registers) run the depth loop:
+// Consumers (16 units each, their W_hh rows in registers) run the depth loop:
 // after a GRU step each publishes, for every new branch, its partial sum of
 // G_j . S over its own units and raises its arrival flag; once every flag is
 // up, every consumer adds the partials in the same fixed order and runs the
@@ -111,8 +111,13 @@ __global__ void k_transpose_w1s(const uint16_t *__restrict__ W1, int r, int s, i
 // ---------------------------------------------------------------- persistent
 constexpr int PK_WAVES = 8;
 constexpr int PK_THREADS = PK_WAVES * 64;
-constexpr int PK_CU = 32;           // units per consumer
+constexpr int PK_CU = 16;           // units per consumer (16 or 32)
+constexpr int PK_HALF = PK_CU / 16; // 16-unit halves per consumer
+constexpr int PK_NMT = 3 * PK_HALF; // W_hh row tiles per consumer (gates x halves)
+constexpr int PK_XS = 1024 / PK_CU / 8;   // partial-sum vectors per thread (consumers / 8)
 constexpr int PK_PU = 8;            // units per producer
+static_assert(PK_CU == 16 || PK_CU == 32, "consumer width");
+static_assert(1024 / PK_CU <= 64, "pk_wait polls consumer flags with the first wave");
 constexpr int PK_PPC = PK_CU / PK_PU;   // producers feeding one consumer
 constexpr int PK_ROWS = 16;         // max expanded branches (all requests) per depth
 constexpr int PK_MAXC = 32;         // max candidates (all requests) per depth
@@ -135,11 +140,11 @@ __host__ __device__ inline PKLayout pk_layout() {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += (bytes + 15) & ~(size_t)15; return at; };
   // per-wave MFMA tiles; before them, the current branches' state fragments
-  L.red = take(std::max((size_t)PK_WAVES * 6 * 16 * 16 * 4, (size_t)(PK_SMAX / 32) * PK_SLOTS * 64));
+  L.red = take(std::max((size_t)PK_WAVES * PK_NMT * 16 * 16 * 4, (size_t)(PK_SMAX / 32) * PK_SLOTS * 64));
   L.stage = take((size_t)PK_WAVES * PK_MAXELL * 4);   // partial sums, 8 groups of consumers
   L.gis = take((size_t)PK_MAXC * 3 * PK_CU * 4);      // input part of this depth's candidates
   L.gsl = take((size_t)PK_MAXC * PK_CU * 4);          // G slice of the next depth
-  L.ghs = take((size_t)6 * 16 * 16 * 4);              // state part of the current branches
+  L.ghs = take((size_t)PK_NMT * 16 * 16 * 4);         // state part of the current branches
   L.bhh = take((size_t)3 * PK_CU * 4);
   L.ell = take((size_t)PK_MAXELL * 4);
   L.ex = take((size_t)PK_MAXELL * 4);
@@ -288,8 +293,8 @@ __device__ __forceinline__ float pk_group_reduce(float v, int n, Op op) {
 // products as the exact three-term bf16 split h = hi + mid + lo; term t of
 // branch row r is column slot t * rp + r of the MFMA B operand (rp = 5, 8 or
 // 16 by the number of branches, so that the 3 x rows columns fill as few
-// 16-column passes as possible).  The owner of state units 32 c .. 32 c + 31
-// writes k-step c: [k-step][3 rp slots][32 units] in bf16, so a consumer
+// 16-column passes as possible).  State units 32 k .. 32 k + 31 (the units of
+// one or two consumers) form k-step k: [k-step][3 rp slots][32 units] in bf16, so a consumer
 // copies the whole table with one contiguous transfer and every lane reads
 // its fragment (slot pass * 16 + lane % 16, units 8 (lane / 16) ..) as 16
 // contiguous bytes.  Pass p column j accumulates slot 16 p + j, so the terms
@@ -304,8 +309,8 @@ __device__ __forceinline__ void split3(float x, uint16_t &hi, uint16_t &mi, uint
   lo = f32_to_bf16_rne(r1 - bf16_bits_to_f32(mi));
 }
 
-// Publishes state value h of branch row `row` (of `rows`) and unit u (0..31,
-// lanes of a pair u, u ^ 1 both active) of consumer c into table T.
+// Publishes state value h of branch row `row` (of `rows`) and unit u (0 ..
+// PK_CU - 1, lanes of a pair u, u ^ 1 both active) of consumer c into table T.
 __device__ __forceinline__ void pk_put_state(uint16_t *T, int c, int rows, int row, int u, float h) {
   uint16_t t3[3];
   split3(h, t3[0], t3[1], t3[2]);
@@ -315,7 +320,8 @@ __device__ __forceinline__ void pk_put_state(uint16_t *T, int c, int rows, int r
     const uint32_t mine = t3[t];
     const uint32_t other = xchg_u32<1>(mine);   // unit u ^ 1
     if ((u & 1) == 0) {
-      uint32_t *dst = reinterpret_cast<uint32_t *>(T + ((size_t)(c * 3 * rp + t * rp + row) * 32 + u));
+      uint32_t *dst = reinterpret_cast<uint32_t *>(
+          T + ((size_t)((c / (32 / PK_CU)) * 3 * rp + t * rp + row) * 32 + (c % (32 / PK_CU)) * PK_CU + u));
       __hip_atomic_store(dst, mine | (other << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -430,17 +436,17 @@ __device__ void pk_producer(const PKParams &p, uint8_t *smem) {
 // ---- consumer: the depth loop
 __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
   const PKLayout L = pk_layout();
-  float *red = reinterpret_cast<float *>(smem + L.red);      // [8][6 mt][16 row][16 unit]
+  float *red = reinterpret_cast<float *>(smem + L.red);      // [8][PK_NMT mt][16 row][16 unit]
   const uint16_t *sfr = reinterpret_cast<const uint16_t *>(red);   // state fragments, before red
   float *stage = reinterpret_cast<float *>(smem + L.stage);  // [group][entries]
-  float *gis = reinterpret_cast<float *>(smem + L.gis);      // [cand][3][32]
-  float *gsl = reinterpret_cast<float *>(smem + L.gsl);      // [request][32 units][M]
-  float *ghs = reinterpret_cast<float *>(smem + L.ghs);      // [6 mt][16 rows][16 units]
-  float *bhh = reinterpret_cast<float *>(smem + L.bhh);      // [gate][32 units]
+  float *gis = reinterpret_cast<float *>(smem + L.gis);      // [cand][3][PK_CU]
+  float *gsl = reinterpret_cast<float *>(smem + L.gsl);      // [request][PK_CU units][M]
+  float *ghs = reinterpret_cast<float *>(smem + L.ghs);      // [PK_NMT mt][16 rows][16 units]
+  float *bhh = reinterpret_cast<float *>(smem + L.bhh);      // [gate][PK_CU units]
   float *ell = reinterpret_cast<float *>(smem + L.ell);
   float *ex = reinterpret_cast<float *>(smem + L.ex);
   uint64_t *lpkey = reinterpret_cast<uint64_t *>(smem + L.lpkey);
-  float *snew = reinterpret_cast<float *>(smem + L.snew);    // [2][16 rows][32 units]
+  float *snew = reinterpret_cast<float *>(smem + L.snew);    // [2][16 rows][PK_CU units]
   uint64_t *ckey = reinterpret_cast<uint64_t *>(smem + L.ckey);
   uint32_t *clex = reinterpret_cast<uint32_t *>(smem + L.clex);
   int32_t *cmeta = reinterpret_cast<int32_t *>(smem + L.cmeta);
@@ -455,18 +461,18 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
   uint32_t *cflags = p.flags;
   const uint32_t *pflags = p.flags + (size_t)(p.NC + PK_PPC * c) * 64;   // this consumer's producers
 
-  // W_hh rows of this workgroup's 32 units, as MFMA A fragments: tile mt =
-  // gate * 2 + half covers gate rows gate*s + j0 + half*16 + (0..15)
-  uint4 wh[PK_HKS][6];
+  // W_hh rows of this workgroup's units, as MFMA A fragments: tile mt =
+  // gate * PK_HALF + half covers gate rows gate*s + j0 + half*16 + (0..15)
+  uint4 wh[PK_HKS][PK_NMT];
 #pragma unroll
   for (int i = 0; i < PK_HKS; ++i) {
     const int ks = wave + PK_WAVES * i;
 #pragma unroll
-    for (int mt = 0; mt < 6; ++mt) {
+    for (int mt = 0; mt < PK_NMT; ++mt) {
       wh[i][mt] = make_uint4(0u, 0u, 0u, 0u);
       if (ks < nks)
         wh[i][mt] = *reinterpret_cast<const uint4 *>(
-            p.W_hh + (size_t)((mt >> 1) * s + j0 + (mt & 1) * 16 + lr) * s + ks * 32 + g * 8);
+            p.W_hh + (size_t)((mt / PK_HALF) * s + j0 + (mt % PK_HALF) * 16 + lr) * s + ks * 32 + g * 8);
     }
   }
   uint16_t *Tcur = p.T0, *Tnext = p.T1;
@@ -509,14 +515,15 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
   // input projections of table slot `slot` (this workgroup's units) into LDS
   auto load_gis = [&](int slot) {
     const float *gtab = p.gitab + (size_t)slot * PK_MAXC * 3 * s + j0;
-    pk_dma<PK_COHERENT>(gis, bM * 24, [&](int ci) {
-      const int rw = ci >> 3, cj = rw / 3;
-      return gtab + (size_t)cj * 3 * s + (rw - 3 * cj) * s + (ci & 7) * 4;
+    constexpr int CPR = PK_CU / 4;   // 16-byte chunks per gate row of this workgroup's units
+    pk_dma<PK_COHERENT>(gis, bM * 3 * CPR, [&](int ci) {
+      const int rw = ci / CPR, cj = rw / 3;
+      return gtab + (size_t)cj * 3 * s + (rw - 3 * cj) * s + (ci % CPR) * 4;
     });
   };
   // (branch row, candidate) of this thread's entry; the entries are row-major
   const int row0 = tid / M, jj0 = tid - row0 * M;
-  const PkDiv divK(K), divQC(8 * M), divNC(p.NC);
+  const PkDiv divK(K), divQC(PK_CU / 4 * M), divNC(p.NC);
   int A = 1, off = 1;   // branches expanded at this depth; node id of its first child
   for (int dd = 0; dd < D; ++dd) {
     const int rows = b * A;
@@ -528,22 +535,22 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     const float *pp = p.part + (size_t)(dd & 1) * p.NC * PK_MAXELL;
     // ---- one round trip: partial sums of every consumer into registers; the
     // tables of the next depth and the current branches' states straight into
-    // LDS.  Thread (eq, sg) takes consumers 4 sg .. 4 sg + 3 of entries
-    // 4 eq .. 4 eq + 3 (entries 256+ in a second pass).
+    // LDS.  Thread (eq, sg) takes consumers PK_XS sg .. PK_XS sg + PK_XS - 1
+    // of entries 4 eq .. 4 eq + 3 (entries 256+ in a second pass).
     const __amdgpu_buffer_rsrc_t prs = pk_rsrc(pp, (uint32_t)(p.NC * PK_MAXELL * 4));
     const int eq = tid & 63, sg = tid >> 6;
-    float4 xs[4];
+    float4 xs[PK_XS];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < PK_XS; ++v) {
       xs[v] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (4 * eq < E && 4 * sg + v < p.NC)
-        xs[v] = pk_get4(prs, (uint32_t)(((4 * sg + v) * PK_MAXELL + 4 * eq) * 4));
+      if (4 * eq < E && PK_XS * sg + v < p.NC)
+        xs[v] = pk_get4(prs, (uint32_t)(((PK_XS * sg + v) * PK_MAXELL + 4 * eq) * 4));
     }
     if (more) {
       pk_dma<PK_COHERENT>(red, nks * 3 * pk_rp(rows) * 4,
                           [&](int ci) { return reinterpret_cast<const float *>(Tcur + 8 * ci); });
       if (dd > 0) load_gis(dd + 1);
-      const int qc = 8 * M;   // chunks per request: 32 units x M candidates
+      const int qc = PK_CU / 4 * M;   // chunks per request: PK_CU units x M candidates
       pk_dma<0>(gsl, b * qc, [&](int ci) {
         const int q = divQC(ci);
         return p.G + ((size_t)(q * D + dd + 1) * s + j0) * M + 4 * (ci - q * qc);
@@ -558,15 +565,15 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       if (4 * eq + 256 * half < E) {
         float4 t = xs[0];
 #pragma unroll
-        for (int v = 1; v < 4; ++v) { t.x += xs[v].x; t.y += xs[v].y; t.z += xs[v].z; t.w += xs[v].w; }
+        for (int v = 1; v < PK_XS; ++v) { t.x += xs[v].x; t.y += xs[v].y; t.z += xs[v].z; t.w += xs[v].w; }
         *reinterpret_cast<float4 *>(stage + sg * PK_MAXELL + 4 * eq + 256 * half) = t;
       }
       if (half == 1 || E <= 256) break;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
+      for (int v = 0; v < PK_XS; ++v) {
         xs[v] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (4 * eq + 256 < E && 4 * sg + v < p.NC)
-          xs[v] = pk_get4(prs, (uint32_t)(((4 * sg + v) * PK_MAXELL + 256 + 4 * eq) * 4));
+        if (4 * eq + 256 < E && PK_XS * sg + v < p.NC)
+          xs[v] = pk_get4(prs, (uint32_t)(((PK_XS * sg + v) * PK_MAXELL + 256 + 4 * eq) * 4));
       }
     }
     if (tid < bM) ctok[tid] = max(tokraw, 0);
@@ -576,9 +583,9 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     // three-term splits; see pk_put_state).  Only issued here: the selection
     // below runs while the matrix cores work, the sums are used after it.
     const int rp = pk_rp(rows);
-    f32x4 acc[6];
+    f32x4 acc[PK_NMT];
 #pragma unroll
-    for (int mt = 0; mt < 6; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < PK_NMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (more) {
       const int npass = pk_npass(rows);
       // fragments of k-step i + 1 are read while those of k-step i feed the
@@ -604,7 +611,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
           for (int ps = 0; ps < 3; ++ps)
             if (ps < npass) {
 #pragma unroll
-              for (int mt = 0; mt < 6; ++mt) acc[mt] = mfma(wh[i][mt], fc[ps], acc[mt]);
+              for (int mt = 0; mt < PK_NMT; ++mt) acc[mt] = mfma(wh[i][mt], fc[ps], acc[mt]);
             }
         }
 #pragma unroll
@@ -739,7 +746,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
                                                        0xF, 0xF, false));
       };
 #pragma unroll
-      for (int mt = 0; mt < 6; ++mt) {
+      for (int mt = 0; mt < PK_NMT; ++mt) {
         f32x4 v = acc[mt];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -748,7 +755,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
             v[t] += ror(v[t], std::integral_constant<int, 11>()) + ror(v[t], std::integral_constant<int, 6>());
         }
         if (lr < rows)
-          *reinterpret_cast<f32x4 *>(red + ((wave * 6 + mt) * 16 + lr) * 16 + 4 * g) = v;
+          *reinterpret_cast<f32x4 *>(red + ((wave * PK_NMT + mt) * 16 + lr) * 16 + 4 * g) = v;
       }
     };
     if (rp == 8) put_rows(std::integral_constant<int, 8>());
@@ -756,12 +763,12 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     else put_rows(std::integral_constant<int, 16>());
     __syncthreads();
     const PkDiv div16r(16 * rows);
-    for (int i = tid; i < 6 * 16 * rows; i += PK_THREADS) {
+    for (int i = tid; i < PK_NMT * 16 * rows; i += PK_THREADS) {
       const int mt = div16r(i), rem = i - mt * 16 * rows, row = rem >> 4, u = rem & 15;
-      float v = bhh[(mt >> 1) * PK_CU + (mt & 1) * 16 + u];
+      float v = bhh[(mt / PK_HALF) * PK_CU + (mt % PK_HALF) * 16 + u];
       float w8[PK_WAVES];
 #pragma unroll
-      for (int wv = 0; wv < PK_WAVES; ++wv) w8[wv] = red[((wv * 6 + mt) * 16 + row) * 16 + u];
+      for (int wv = 0; wv < PK_WAVES; ++wv) w8[wv] = red[((wv * PK_NMT + mt) * 16 + row) * 16 + u];
 #pragma unroll
       for (int wv = 0; wv < PK_WAVES; ++wv) v += w8[wv];
       ghs[(mt * 16 + row) * 16 + u] = v;
@@ -769,7 +776,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     if (dd == 0) __builtin_amdgcn_s_waitcnt(0);   // the copy of slot 1 has landed
     __syncthreads();
 
-    // ---- GRU step of the survivors for this workgroup's 32 units
+    // ---- GRU step of the survivors for this workgroup's PK_CU units
     const int nrow = b * An;
     if (tid < nrow * PK_CU) {
       const int i = tid / PK_CU, u = tid - i * PK_CU;
@@ -778,9 +785,10 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       const float *a = gis + (q * M + jc) * 3 * PK_CU;
       const int half = u >> 4, ul = u & 15;
       const float h = sn_cur[pr * PK_CU + u];
-      const float r = 1.f / (1.f + expf(-(a[u] + ghs[((0 + half) * 16 + pr) * 16 + ul])));
-      const float z = 1.f / (1.f + expf(-(a[PK_CU + u] + ghs[((2 + half) * 16 + pr) * 16 + ul])));
-      const float n = tanhf(a[2 * PK_CU + u] + r * ghs[((4 + half) * 16 + pr) * 16 + ul]);
+      const float *gh = ghs + (half * 16 + pr) * 16 + ul;   // gate g at + g * PK_HALF * 256
+      const float r = 1.f / (1.f + expf(-(a[u] + gh[0])));
+      const float z = 1.f / (1.f + expf(-(a[PK_CU + u] + gh[PK_HALF * 256])));
+      const float n = tanhf(a[2 * PK_CU + u] + r * gh[2 * PK_HALF * 256]);
       const float hn = (1.f - z) * n + z * h;
       sn_nxt[i * PK_CU + u] = hn;
       pk_put_state(Tnext, c, nrow, i, u, hn);
