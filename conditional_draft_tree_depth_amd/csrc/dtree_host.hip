@@ -188,7 +188,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   };
   if (ctx->k1_smem > ctx->lds_max) return reject(DTREE_E_SHAPE, "d too large for the LM-head LDS tile");
   if (topm_merge_smem(ctx->P) > 131072) return reject(DTREE_E_SHAPE, "vocabulary too large for the Top-M merge");
-  if (cl_smem > ctx->lds_max) return reject(DTREE_E_SHAPE, "max_M * r + max_W * r too large for LDS");
+  if (cl_smem > ctx->lds_max) return reject(DTREE_E_SHAPE, "max_M * r too large for the correction LDS tile");
   if (tb_smem > ctx->lds_max) return reject(DTREE_E_SHAPE, "superarbol too large for the Top-B LDS sort");
 
   DeviceGuard dg(device);

@@ -12,54 +12,85 @@
 
 namespace dtree {
 
-constexpr int SEL_THREADS = 256;
+constexpr int SEL_THREADS = 1024;
 constexpr int SEL_MAXZ = 1024;   // children per request and depth
 constexpr int SEL_MAXW = 512;
+constexpr int CL_BR = 4;         // expanded branches per correction workgroup
 
 // Corrected logits of the depth's candidates for every expanded branch:
 //   ell[a][j] = Cl[j] + W2[C[j]] . u_a
 // ("Resumen Técnico: Domino", Methodology 2: L = L_base + Delta L with the
 // low-rank map back to the vocabulary; "Resumen Técnico: DominoTree", Main
 // components 2: only the r x M slice of W2 for the Top-M candidates is
-// used).  One workgroup per request stages that slice and the branches' u
-// vectors in LDS.
+// used).  One workgroup per (request, group of CL_BR branches) stages that
+// slice and its branches' u vectors in LDS; with bf16 rows of a multiple of
+// 8 the slice moves in 16-byte pieces and every output reads 8 weights at
+// a time.
 template <typename WT>
 __global__ __launch_bounds__(256) void k_corr_logits(int A, int M, int r, int D, int delta,
-                                                     const WT *__restrict__ W2,
+                                                     int vec, const WT *__restrict__ W2,
                                                      const int32_t *__restrict__ C,
                                                      const float *__restrict__ Cl,
                                                      const float *__restrict__ u,
                                                      float *__restrict__ ell) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int q = blockIdx.x;
-  const int rs = r + (sizeof(WT) == 2 ? 2 : 1);   // skewed row stride
+  const int q = blockIdx.x, a0 = blockIdx.y * CL_BR;
+  const int na = min(CL_BR, A - a0);
+  constexpr bool B16 = sizeof(WT) == 2;   // vec: bf16, r % 8 == 0, W2 16-byte aligned
+  const int rs = vec ? r + 8 : r + (B16 ? 2 : 1);   // row stride (skewed when scalar)
   WT *W2s = reinterpret_cast<WT *>(smem);
   size_t w2bytes = ((size_t)M * rs * sizeof(WT) + 15) & ~(size_t)15;
   float *us = reinterpret_cast<float *>(smem + w2bytes);
   const int32_t *toks = C + ((size_t)q * D + delta) * M;
-  for (int i = threadIdx.x; i < M * r; i += blockDim.x) {
-    const int j = i / r, tt = i - j * r;
-    const int tk = toks[j] < 0 ? 0 : toks[j];   // an empty slot never reaches here
-    W2s[j * rs + tt] = W2[(size_t)tk * r + tt];
+  if (vec) {
+    const int r8 = r >> 3;
+    for (int i = threadIdx.x; i < M * r8; i += blockDim.x) {
+      const int j = i / r8, c8 = i - j * r8;
+      const int tk = toks[j] < 0 ? 0 : toks[j];   // an empty slot never reaches here
+      *reinterpret_cast<uint4 *>(W2s + j * rs + 8 * c8) =
+          *reinterpret_cast<const uint4 *>(W2 + (size_t)tk * r + 8 * c8);
+    }
+  } else {
+    for (int i = threadIdx.x; i < M * r; i += blockDim.x) {
+      const int j = i / r, tt = i - j * r;
+      const int tk = toks[j] < 0 ? 0 : toks[j];
+      W2s[j * rs + tt] = W2[(size_t)tk * r + tt];
+    }
   }
-  const float *uq = u + (size_t)q * A * r;
-  for (int i = threadIdx.x; i < A * r; i += blockDim.x) us[i] = uq[i];
+  const float *uq = u + ((size_t)q * A + a0) * r;
+  for (int i = threadIdx.x; i < na * r; i += blockDim.x) us[i] = uq[i];
   __syncthreads();
   const float *clq = Cl + ((size_t)q * D + delta) * M;
-  for (int o = threadIdx.x; o < A * M; o += blockDim.x) {
+  for (int o = threadIdx.x; o < na * M; o += blockDim.x) {
     const int a = o / M, j = o - a * M;
     const WT *w = W2s + j * rs;
     const float *ua = us + a * r;
     float acc = 0.f;
-    for (int tt = 0; tt < r; ++tt) acc += wload(w, tt) * ua[tt];
-    ell[((size_t)q * A + a) * M + j] = clq[j] + acc;
+    if (vec) {
+      for (int c8 = 0; c8 < r; c8 += 8) {
+        const uint4 wv = *reinterpret_cast<const uint4 *>(w + c8);
+        const float4 u0 = *reinterpret_cast<const float4 *>(ua + c8);
+        const float4 u1 = *reinterpret_cast<const float4 *>(ua + c8 + 4);
+        acc += __uint_as_float(wv.x << 16) * u0.x;
+        acc += __uint_as_float(wv.x & 0xFFFF0000u) * u0.y;
+        acc += __uint_as_float(wv.y << 16) * u0.z;
+        acc += __uint_as_float(wv.y & 0xFFFF0000u) * u0.w;
+        acc += __uint_as_float(wv.z << 16) * u1.x;
+        acc += __uint_as_float(wv.z & 0xFFFF0000u) * u1.y;
+        acc += __uint_as_float(wv.w << 16) * u1.z;
+        acc += __uint_as_float(wv.w & 0xFFFF0000u) * u1.w;
+      }
+    } else {
+      for (int tt = 0; tt < r; ++tt) acc += wload(w, tt) * ua[tt];
+    }
+    ell[((size_t)q * A + a0 + a) * M + j] = clq[j] + acc;
   }
 }
 
 size_t corr_logits_smem(int A, int M, int r, int wtype) {
   const size_t es = wtype == WT_BF16 ? 2 : 4;
-  const size_t rs = r + (wtype == WT_BF16 ? 2 : 1);
-  return (((size_t)M * rs * es + 15) & ~(size_t)15) + (size_t)A * r * 4;
+  const size_t rs = wtype == WT_BF16 ? (r % 8 == 0 ? r + 8 : r + 2) : r + 1;
+  return (((size_t)M * rs * es + 15) & ~(size_t)15) + (size_t)(A < CL_BR ? A : CL_BR) * r * 4;
 }
 
 hipError_t corr_logits_prepare(int wtype, size_t smem) {
@@ -74,21 +105,26 @@ hipError_t launch_corr_logits(int b, int A, int M, int r, int D, int delta, cons
                               int wtype, const int32_t *C, const float *Cl, const float *u,
                               float *ell, hipStream_t st) {
   const size_t sm = corr_logits_smem(A, M, r, wtype);
+  const dim3 grid(b, (A + CL_BR - 1) / CL_BR);
+  const int vec = wtype == WT_BF16 && r % 8 == 0 && reinterpret_cast<uintptr_t>(W2) % 16 == 0;
   if (wtype == WT_BF16)
-    hipLaunchKernelGGL(k_corr_logits<uint16_t>, dim3(b), dim3(256), sm, st, A, M, r, D, delta,
+    hipLaunchKernelGGL(k_corr_logits<uint16_t>, grid, dim3(256), sm, st, A, M, r, D, delta, vec,
                        static_cast<const uint16_t *>(W2), C, Cl, u, ell);
   else
-    hipLaunchKernelGGL(k_corr_logits<float>, dim3(b), dim3(256), sm, st, A, M, r, D, delta,
+    hipLaunchKernelGGL(k_corr_logits<float>, grid, dim3(256), sm, st, A, M, r, D, delta, 0,
                        static_cast<const float *>(W2), C, Cl, u, ell);
   return hipGetLastError();
 }
 
 // Selection of one depth for one request (one workgroup each):
-//  1. per expanded branch (one wave each): log-softmax over the M corrected
-//     logits, Top-K children (log-prob desc, token asc), child score =
-//     parent score + log-prob; every child is appended to the superarbol
-//     ("Resumen Técnico: DominoTree", Main components 2; DARTree page,
-//     Methodology 1, scoring by corrected cumulative probability);
+//  0. the expanded branches' node ids, lexicographic ranks and scores are
+//     gathered into LDS once (two dependent loads for all branches at once);
+//  1. per expanded branch (one wave each; the next branch's logits are
+//     loaded while the current one is processed): log-softmax over the M
+//     corrected logits, Top-K children (log-prob desc, token asc), child
+//     score = parent score + log-prob; every child is appended to the
+//     superarbol ("Resumen Técnico: DominoTree", Main components 2; DARTree
+//     page, Methodology 1, scoring by corrected cumulative probability);
 //  2. Top-W of the depth's children by (score desc, token path asc) become
 //     the next expanded branches (DARTree page, Methodology 1, retention);
 //  3. the survivors' lexicographic ranks among themselves, and the gathers
@@ -101,27 +137,48 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
   __shared__ uint64_t ckey[SEL_MAXZ];
   __shared__ uint32_t clex[SEL_MAXZ];
   __shared__ uint32_t slex[SEL_MAXW];
-  const int q = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int32_t pnode[SEL_MAXW];
+  __shared__ uint32_t prank[SEL_MAXW];
+  __shared__ float pscore[SEL_MAXW];
+  __shared__ int32_t ctok[128];
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int nw = blockDim.x >> 6;
   const int32_t *cq = C + ((size_t)q * D + delta) * M;
   const size_t nb = (size_t)q * t.NT;
   const int Z = A * K;
   const int An = Z < W ? Z : W;
 
-  for (int a = wave; a < A; a += nw) {
+  for (int a = tid; a < A; a += blockDim.x) {
     const int p = t.surv_node[(size_t)q * t.Wmax + a];
-    const uint32_t prank = (uint32_t)t.surv_rank[(size_t)q * t.Wmax + a];
-    const float pscore = t.n_score[nb + p];
-    const float *la = ell + ((size_t)q * A + a) * M;
-    const bool h0 = lane < M, h1 = lane + 64 < M;
-    const float l0 = h0 ? la[lane] : -INFINITY;
-    const float l1 = h1 ? la[lane + 64] : -INFINITY;
+    pnode[a] = p;
+    prank[a] = (uint32_t)t.surv_rank[(size_t)q * t.Wmax + a];
+    pscore[a] = t.n_score[nb + p];
+  }
+  for (int j = tid; j < M; j += blockDim.x) ctok[j] = cq[j];
+  const bool h0 = lane < M, h1 = lane + 64 < M;
+  float l0 = -INFINITY, l1 = -INFINITY;
+  if (wave < A) {
+    const float *la = ell + ((size_t)q * A + wave) * M;
+    if (h0) l0 = la[lane];
+    if (h1) l1 = la[lane + 64];
+  }
+  __syncthreads();
+  for (int a = wave; a < A; a += nw) {
+    float n0 = -INFINITY, n1 = -INFINITY;   // the wave's next branch, in flight meanwhile
+    if (a + nw < A) {
+      const float *ln = ell + ((size_t)q * A + a + nw) * M;
+      if (h0) n0 = ln[lane];
+      if (h1) n1 = ln[lane + 64];
+    }
+    const int p = pnode[a];
+    const uint32_t pr = prank[a];
+    const float ps = pscore[a];
     const float m = wave_max_f32(fmaxf(l0, l1));
     const float e = (h0 ? expf(l0 - m) : 0.f) + (h1 ? expf(l1 - m) : 0.f);
     const float lse = m + logf(wave_sum_f32(e));
-    uint64_t k0 = h0 ? make_key(l0 - lse, (uint32_t)cq[lane]) : 0ull;
-    uint64_t k1 = h1 ? make_key(l1 - lse, (uint32_t)cq[lane + 64]) : 0ull;
+    uint64_t k0 = h0 ? make_key(l0 - lse, (uint32_t)ctok[lane]) : 0ull;
+    uint64_t k1 = h1 ? make_key(l1 - lse, (uint32_t)ctok[lane + 64]) : 0ull;
     for (int k = 0; k < K; ++k) {
       const uint64_t top = group_max_u64<64>(k0 > k1 ? k0 : k1);
       if (k0 == top) k0 = 0ull;
@@ -129,8 +186,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
       if (lane == 0) {
         const uint32_t tok = key_tie(top);
         const float lp = key_val(top);
-        const float sc = __fadd_rn(pscore, lp);
-        const uint32_t lex = (prank << 18) | tok;
+        const float sc = __fadd_rn(ps, lp);
+        const uint32_t lex = (pr << 18) | tok;
         const int c = a * K + k;
         const size_t id = nb + off + c;
         t.n_tok[id] = (int32_t)tok;
@@ -142,11 +199,13 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
         clex[c] = lex;
       }
     }
+    l0 = n0;
+    l1 = n1;
   }
   __syncthreads();
 
   // Top-W by rank: keys are distinct (distinct token paths)
-  for (int c = threadIdx.x; c < Z; c += blockDim.x) {
+  for (int c = tid; c < Z; c += blockDim.x) {
     const uint64_t kc = ckey[c];
     int rank = 0;
     for (int c2 = 0; c2 < Z; ++c2) rank += ckey[c2] > kc;
@@ -160,7 +219,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < An; i += blockDim.x) {
+  for (int i = tid; i < An; i += blockDim.x) {
     const uint32_t li = slex[i];
     int rank = 0;
     for (int j = 0; j < An; ++j) rank += slex[j] < li;

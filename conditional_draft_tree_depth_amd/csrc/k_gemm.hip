@@ -85,93 +85,143 @@ __global__ __launch_bounds__(256) void k_gemm_xwT(GemmArgs a) {
   }
 }
 
-// Skinny product on MFMA: at most 16 activation rows per workgroup (rows of
-// the B operand, staged in LDS as bf16), bf16 weight rows streamed from
-// memory as the A operand, 16 weight rows per wave, fp32 accumulation.
+// Row-gathered product on MFMA for bf16 weights: Y = X W^T (+ bias, +
+// addend), any number of activation rows.  One workgroup takes 16 weight
+// rows (the A operand, loaded once into registers) and up to 128 activation
+// rows; its 8 waves split the contraction (wave w takes the 32-wide k-steps
+// w, w + 8, ...), so a 3072 x 2560 weight is streamed by 192 x 8 waves with
+// all of a wave's weight loads in flight at once.  Activation fragments (the
+// B operand) come straight from global memory (they are small and shared
+// by every workgroup, so they stay in L2); the fragments of the next 16-row
+// block are loaded while the current one feeds the matrix cores.  The 8
+// partial sums of every output are added in a fixed order through LDS.
 // fp32 activations that must not be rounded (the GRU state) are split
 // exactly into three bf16 terms x = hi + mid + lo (each term is the bf16
 // rounding of what the previous ones left, so the remainder is below
 // 2^-24 |x|); every term is multiplied by the same weight fragment.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-constexpr int SK_WAVES = 4;
+constexpr int SK_WAVES = 8;       // waves per workgroup (contraction split)
+constexpr int SK_RB = 8;          // 16-row activation blocks per workgroup
+constexpr int SK_KSW_B = 16;      // k-steps per wave, bf16 activations: K <= 4096
+constexpr int SK_KSW_F = 8;       // k-steps per wave, fp32 activations: K <= 2048
 
 __device__ __forceinline__ bf16x8 sk_bf(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f32x4 sk_mfma(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(sk_bf(a), sk_bf(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t sk_pack(uint16_t lo, uint16_t hi) {
+  return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// Term t (0: hi, 1: mid, 2: lo; TERMS == 1: the bf16 rounding) of 8 fp32
+// activations, packed as one B fragment.
+template <int TERMS>
+__device__ __forceinline__ void sk_split(const float4 &x0, const float4 &x1, uint4 (&t)[TERMS]) {
+  const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  uint16_t h[TERMS][8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    h[0][k] = f32_to_bf16_rne(x[k]);
+    if constexpr (TERMS == 3) {
+      const float r1 = x[k] - bf16_bits_to_f32(h[0][k]);
+      h[1][k] = f32_to_bf16_rne(r1);
+      h[2][k] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(h[1][k]));
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < TERMS; ++q)
+    t[q] = make_uint4(sk_pack(h[q][0], h[q][1]), sk_pack(h[q][2], h[q][3]),
+                      sk_pack(h[q][4], h[q][5]), sk_pack(h[q][6], h[q][7]));
+}
 
 template <int TERMS, typename XT>
 __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const int KS = a.Kd + 8;
-  uint16_t *Xs = reinterpret_cast<uint16_t *>(smem);   // [TERMS][16][KS]
-  const XT *X = static_cast<const XT *>(a.X);
-  const int r0 = blockIdx.x * 16;
-  const int nr = min(16, a.R - r0);
-  for (int i = threadIdx.x; i < 16 * a.Kd; i += blockDim.x) {
-    const int rr = i / a.Kd, k = i - rr * a.Kd;
-    uint16_t t0 = 0, t1 = 0, t2 = 0;
-    if (rr < nr) {
-      const size_t xi = (size_t)(a.xidx ? a.xidx[r0 + rr] : r0 + rr) * a.ldx + k;
-      if constexpr (sizeof(XT) == 2) {
-        t0 = X[xi];
-      } else {
-        const float x = X[xi];
-        t0 = f32_to_bf16_rne(x);
-        if constexpr (TERMS == 3) {
-          const float r1 = x - bf16_bits_to_f32(t0);
-          t1 = f32_to_bf16_rne(r1);
-          t2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(t1));
-        }
+  constexpr bool XB = sizeof(XT) == 2;
+  constexpr int KSW = XB ? SK_KSW_B : SK_KSW_F;
+  __shared__ __align__(16) float red[SK_WAVES * SK_RB * 256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16, r0 = blockIdx.y * (16 * SK_RB);
+  const int nrb = min(SK_RB, (a.R - r0 + 15) >> 4);
+  const int nks = a.Kd >> 5;
+  const uint16_t *wrow = static_cast<const uint16_t *>(a.W) + (size_t)min(n0 + lr, a.N - 1) * a.ldw + g * 8;
+  uint4 wa[KSW];
+#pragma unroll
+  for (int i = 0; i < KSW; ++i) {
+    const int ks = wave + SK_WAVES * i;
+    wa[i] = ks < nks ? *reinterpret_cast<const uint4 *>(wrow + ks * 32) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // activation row of lane lr in row block rb (rows past R repeat the last
+  // row; their sums are never stored)
+  auto xrow = [&](int rb) -> size_t {
+    const int row = min(r0 + rb * 16 + lr, a.R - 1);
+    return (size_t)(a.xidx ? a.xidx[row] : row) * a.ldx + g * 8;
+  };
+  if constexpr (XB) {
+    const uint16_t *X = static_cast<const uint16_t *>(a.X);
+    uint4 xc[KSW], xn[KSW];
+    auto load = [&](int rb, uint4 (&xv)[KSW]) {
+      const uint16_t *xp = X + xrow(rb);
+#pragma unroll
+      for (int i = 0; i < KSW; ++i) {
+        const int ks = wave + SK_WAVES * i;
+        xv[i] = ks < nks ? *reinterpret_cast<const uint4 *>(xp + ks * 32) : make_uint4(0u, 0u, 0u, 0u);
       }
+    };
+    load(0, xc);
+    for (int rb = 0; rb < nrb; ++rb) {
+      if (rb + 1 < nrb) load(rb + 1, xn);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < KSW; ++i)
+        if (wave + SK_WAVES * i < nks) acc = sk_mfma(wa[i], xc[i], acc);
+      // lane holds Y[row lr][weight row 4 g + t]
+      *reinterpret_cast<f32x4 *>(red + ((wave * SK_RB + rb) * 16 + lr) * 16 + 4 * g) = acc;
+#pragma unroll
+      for (int i = 0; i < KSW; ++i) xc[i] = xn[i];
     }
-    Xs[rr * KS + k] = t0;
-    if constexpr (TERMS == 3) {
-      Xs[(16 + rr) * KS + k] = t1;
-      Xs[(32 + rr) * KS + k] = t2;
+  } else {
+    const float *X = static_cast<const float *>(a.X);
+    float4 xc[KSW][2], xn[KSW][2];
+    auto load = [&](int rb, float4 (&xv)[KSW][2]) {
+      const float *xp = X + xrow(rb);
+#pragma unroll
+      for (int i = 0; i < KSW; ++i) {
+        const int ks = wave + SK_WAVES * i;
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        xv[i][0] = ks < nks ? *reinterpret_cast<const float4 *>(xp + ks * 32) : z;
+        xv[i][1] = ks < nks ? *reinterpret_cast<const float4 *>(xp + ks * 32 + 4) : z;
+      }
+    };
+    load(0, xc);
+    for (int rb = 0; rb < nrb; ++rb) {
+      if (rb + 1 < nrb) load(rb + 1, xn);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < KSW; ++i)
+        if (wave + SK_WAVES * i < nks) {
+          uint4 t[TERMS];
+          sk_split<TERMS>(xc[i][0], xc[i][1], t);
+#pragma unroll
+          for (int q = 0; q < TERMS; ++q) acc = sk_mfma(wa[i], t[q], acc);
+        }
+      *reinterpret_cast<f32x4 *>(red + ((wave * SK_RB + rb) * 16 + lr) * 16 + 4 * g) = acc;
+#pragma unroll
+      for (int i = 0; i < KSW; ++i) { xc[i][0] = xn[i][0]; xc[i][1] = xn[i][1]; }
     }
   }
   __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lr = lane & 15, g = lane >> 4;
-  const int tile = blockIdx.y * SK_WAVES + wave;
-  if (tile * 16 >= a.N) return;
-  const int n = min(tile * 16 + lr, a.N - 1);
-  const uint16_t *Wt = static_cast<const uint16_t *>(a.W);
-  const uint4 *pw = reinterpret_cast<const uint4 *>(Wt + (size_t)n * a.ldw + g * 32);
-  const uint16_t *hp = Xs + lr * KS + g * 32;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  uint4 cw[4];
+  for (int o = tid; o < nrb * 256; o += SK_WAVES * 64) {
+    const int rb = o >> 8, rr = (o >> 4) & 15, nn = o & 15;
+    const int row = r0 + rb * 16 + rr, n = n0 + nn;
+    float v = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cw[j] = pw[j];
-  for (int kc = 0; kc < a.Kd; kc += 128) {
-    uint4 nw[4];
-    if (kc + 128 < a.Kd) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) nw[j] = pw[(kc + 128) / 8 + j];
+    for (int w = 0; w < SK_WAVES; ++w) v += red[((w * SK_RB + rb) * 16 + rr) * 16 + nn];
+    if (row < a.R && n < a.N) {
+      if (a.bias) v += a.bias[n];
+      if (a.addend) v += a.addend[(size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda + n];
+      a.Y[(size_t)row * a.ldy + n] = v;
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int t = 0; t < TERMS; ++t) {
-        const uint4 xv = *reinterpret_cast<const uint4 *>(hp + t * 16 * KS + kc + 8 * j);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sk_bf(cw[j]), sk_bf(xv), acc, 0, 0, 0);
-      }
-    }
-    if (kc + 128 < a.Kd) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cw[j] = nw[j];
-    }
-  }
-  if (lr >= nr) return;
-  const int row = r0 + lr;
-  const float *add = a.addend ? a.addend + (size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda : nullptr;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int nn = tile * 16 + 4 * g + t;
-    if (nn >= a.N) continue;
-    float v = acc[t];
-    if (a.bias) v += a.bias[nn];
-    if (add) v += add[nn];
-    a.Y[(size_t)row * a.ldy + nn] = v;
   }
 }
 
@@ -179,40 +229,30 @@ static int skinny_terms(const GemmArgs &a) {
   return (a.xtype == WT_F32 && !a.xround) ? 3 : 1;
 }
 
-size_t skinny_smem(int Kd, int terms) { return (size_t)terms * 16 * (Kd + 8) * 2; }
-
-bool skinny_ok(const GemmArgs &a, size_t lds_max) {
-  return a.wtype == WT_BF16 && a.Kd % 128 == 0 && a.ldw % 8 == 0 &&
-         reinterpret_cast<uintptr_t>(a.W) % 16 == 0 && a.R <= 64 &&
-         skinny_smem(a.Kd, skinny_terms(a)) <= lds_max;
+bool skinny_ok(const GemmArgs &a) {
+  if (a.wtype != WT_BF16 || a.Kd % 32 || a.ldw % 8 || reinterpret_cast<uintptr_t>(a.W) % 16)
+    return false;
+  if (reinterpret_cast<uintptr_t>(a.X) % 16) return false;
+  if (a.xtype == WT_BF16) return a.ldx % 8 == 0 && a.Kd <= 32 * SK_WAVES * SK_KSW_B;
+  return a.ldx % 4 == 0 && a.Kd <= 32 * SK_WAVES * SK_KSW_F;
 }
 
-hipError_t skinny_prepare(size_t lds_max) {
-  const void *fns[] = {reinterpret_cast<const void *>(&k_skinny_bf16<1, uint16_t>),
-                       reinterpret_cast<const void *>(&k_skinny_bf16<1, float>),
-                       reinterpret_cast<const void *>(&k_skinny_bf16<3, float>)};
-  for (const void *f : fns) {
-    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
+hipError_t skinny_prepare(size_t) { return hipSuccess; }
 
 static size_t g_lds_max = 65536;
 void gemm_set_lds_max(size_t b) { g_lds_max = b; }
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.R <= 0 || a.N <= 0) return hipSuccess;
-  if (skinny_ok(a, g_lds_max)) {
+  if (skinny_ok(a)) {
     const int terms = skinny_terms(a);
-    dim3 grid((a.R + 15) / 16, ((a.N + 15) / 16 + SK_WAVES - 1) / SK_WAVES);
-    const size_t sm = skinny_smem(a.Kd, terms);
+    dim3 grid((a.N + 15) / 16, (a.R + 16 * SK_RB - 1) / (16 * SK_RB));
     if (a.xtype == WT_BF16)
-      hipLaunchKernelGGL((k_skinny_bf16<1, uint16_t>), grid, dim3(SK_WAVES * 64), sm, st, a);
+      hipLaunchKernelGGL((k_skinny_bf16<1, uint16_t>), grid, dim3(SK_WAVES * 64), 0, st, a);
     else if (terms == 1)
-      hipLaunchKernelGGL((k_skinny_bf16<1, float>), grid, dim3(SK_WAVES * 64), sm, st, a);
+      hipLaunchKernelGGL((k_skinny_bf16<1, float>), grid, dim3(SK_WAVES * 64), 0, st, a);
     else
-      hipLaunchKernelGGL((k_skinny_bf16<3, float>), grid, dim3(SK_WAVES * 64), sm, st, a);
+      hipLaunchKernelGGL((k_skinny_bf16<3, float>), grid, dim3(SK_WAVES * 64), 0, st, a);
     return hipGetLastError();
   }
   dim3 grid((a.N + GT - 1) / GT, (a.R + GT - 1) / GT);
