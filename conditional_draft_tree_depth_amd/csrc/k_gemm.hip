@@ -145,12 +145,12 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a) {
   const int nrb = min(SK_RB, (a.R - r0 + 15) >> 4);
   const int nks = a.Kd >> 5;
   const uint16_t *wrow = static_cast<const uint16_t *>(a.W) + (size_t)min(n0 + lr, a.N - 1) * a.ldw + g * 8;
+  // k-steps past the contraction load the last one again (every load is
+  // unconditional and in bounds) and are skipped at the products
   uint4 wa[KSW];
 #pragma unroll
-  for (int i = 0; i < KSW; ++i) {
-    const int ks = wave + SK_WAVES * i;
-    wa[i] = ks < nks ? *reinterpret_cast<const uint4 *>(wrow + ks * 32) : make_uint4(0u, 0u, 0u, 0u);
-  }
+  for (int i = 0; i < KSW; ++i)
+    wa[i] = *reinterpret_cast<const uint4 *>(wrow + min(wave + SK_WAVES * i, nks - 1) * 32);
   // activation row of lane lr in row block rb (rows past R repeat the last
   // row; their sums are never stored)
   auto xrow = [&](int rb) -> size_t {
@@ -163,10 +163,8 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a) {
     auto load = [&](int rb, uint4 (&xv)[KSW]) {
       const uint16_t *xp = X + xrow(rb);
 #pragma unroll
-      for (int i = 0; i < KSW; ++i) {
-        const int ks = wave + SK_WAVES * i;
-        xv[i] = ks < nks ? *reinterpret_cast<const uint4 *>(xp + ks * 32) : make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int i = 0; i < KSW; ++i)
+        xv[i] = *reinterpret_cast<const uint4 *>(xp + min(wave + SK_WAVES * i, nks - 1) * 32);
     };
     load(0, xc);
     for (int rb = 0; rb < nrb; ++rb) {
@@ -187,10 +185,9 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a) {
       const float *xp = X + xrow(rb);
 #pragma unroll
       for (int i = 0; i < KSW; ++i) {
-        const int ks = wave + SK_WAVES * i;
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        xv[i][0] = ks < nks ? *reinterpret_cast<const float4 *>(xp + ks * 32) : z;
-        xv[i][1] = ks < nks ? *reinterpret_cast<const float4 *>(xp + ks * 32 + 4) : z;
+        const float *pk = xp + min(wave + SK_WAVES * i, nks - 1) * 32;
+        xv[i][0] = *reinterpret_cast<const float4 *>(pk);
+        xv[i][1] = *reinterpret_cast<const float4 *>(pk + 4);
       }
     };
     load(0, xc);

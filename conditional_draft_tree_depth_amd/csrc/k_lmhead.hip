@@ -256,8 +256,20 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
     const float *__restrict__ bias, int M, uint64_t *__restrict__ part,
     const uint16_t *__restrict__ W1, int ldw1, int r, float *__restrict__ uH) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int P = gridDim.y, y = blockIdx.y;
-  const int row0 = blockIdx.x * 16;
+  const int P = gridDim.y, RB = gridDim.x;
+  int y = blockIdx.y, bx = blockIdx.x;
+  // Several 16-row blocks: workgroups are handed to the 8 XCDs in turn, so
+  // task (row block, slice) is renumbered to give each XCD a contiguous run
+  // of tasks in which all row blocks of one slice come one after another;
+  // they run side by side and read the slice's W_lm tiles through that
+  // XCD's L2 instead of each from HBM.
+  if (RB > 1 && (RB * P) % 8 == 0) {
+    const int id = bx + RB * y;
+    const int task = (id & 7) * (RB * P / 8) + (id >> 3);
+    y = task / RB;
+    bx = task - y * RB;
+  }
+  const int row0 = bx * 16;
   const int nrow = min(16, rows - row0);
   const int cpr = d >> 3;   // 16-byte chunks per hidden row (a multiple of 16)
   uint16_t *Hs = reinterpret_cast<uint16_t *>(smem);
