@@ -24,8 +24,11 @@ thread_local std::string g_create_err;
 struct Ws {
   uint64_t *part = nullptr;
   int32_t *C = nullptr;
-  float *Cl = nullptr, *uH = nullptr, *S[2] = {nullptr, nullptr}, *u = nullptr;
-  float *ell = nullptr, *gi = nullptr, *gh = nullptr;
+  float *Cl = nullptr, *uH = nullptr, *S[2] = {nullptr, nullptr};
+  // per depth: [u | W_hh S + b_hh] of every expanded branch, [b * W, r + 3s]
+  float *uh = nullptr;
+  float *ell = nullptr, *gi = nullptr;
+  void *wcat = nullptr;      // [W1[:, d:] ; W_hh], [r + 3s, s] in the weight dtype
   int32_t *n_tok = nullptr, *n_par = nullptr, *n_dep = nullptr;
   float *n_score = nullptr;
   uint32_t *n_lex = nullptr;
@@ -112,7 +115,7 @@ hipError_t alloc(T **p, size_t n) {
 }
 
 void free_ws(Ws &ws) {
-  void *ptrs[] = {ws.part, ws.hb, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.u, ws.ell, ws.gi, ws.gh,
+  void *ptrs[] = {ws.part, ws.hb, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.uh, ws.ell, ws.gi, ws.wcat,
                   ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
                   ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags};
@@ -206,10 +209,15 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   A(alloc(&ws.hb, (size_t)((rows + 15) / 16 * 16) * w->d));
   A(alloc(&ws.S[0], bw * s));
   A(alloc(&ws.S[1], bw * s));
-  A(alloc(&ws.u, bw * r));
+  A(alloc(&ws.uh, bw * (r + 3 * s)));
   A(alloc(&ws.ell, bw * c.max_M));
   A(alloc(&ws.gi, bw * 3 * s));
-  A(alloc(&ws.gh, bw * 3 * s));
+  const size_t esz_w = w->wtype == DTREE_BF16 ? 2 : 4;
+  A(alloc(reinterpret_cast<uint8_t **>(&ws.wcat), (size_t)(r + 3 * s) * s * esz_w));
+  if (e == hipSuccess)
+    A(launch_concat_state_weights(w->W1, w->W_hh, r, s, w->d,
+                                  w->wtype == DTREE_BF16 ? WT_BF16 : WT_F32, ws.wcat, nullptr));
+  if (e == hipSuccess) A(hipDeviceSynchronize());   // rounds may run on any stream
   const size_t nt = (size_t)c.max_batch * NTcap;
   A(alloc(&ws.n_tok, nt));
   A(alloc(&ws.n_par, nt));
@@ -370,26 +378,29 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
     g = GemmArgs{batch, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
                  w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
     HIPCHK(ctx, launch_gemm(g, st));
-    HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, w.b_hh, nullptr, nullptr, ws.S[0], st));
+    HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, 0, w.b_hh, nullptr, nullptr, ws.S[0], st));
     prof_mark(ctx, 4, st);
     for (int dd = 0; dd < D; ++dd) {
-      // u = uH[req, dd] + W1[:, d:] . S  for every expanded branch
-      g = GemmArgs{batch * A, r, s, ws.S[sc], WT_F32, s, nullptr, 0,
-                   static_cast<const uint8_t *>(w.W1) + (size_t)d * esz, wt, d + s, nullptr,
-                   ws.uH, r, A, D, dd, ws.u, r};
+      // for every expanded branch, one product over its state S:
+      //   u = uH[req, dd] + W1[:, d:] . S   (outputs 0 .. r-1)
+      //   W_hh . S + b_hh                  (outputs r .. r+3s-1, the GRU state
+      //                                      part of all of the branch's children)
+      const int ldu = r + 3 * s;
+      g = GemmArgs{batch * A, ldu, s, ws.S[sc], WT_F32, s, nullptr, 0, ws.wcat, wt, s, w.b_hh,
+                   ws.uH, r, A, D, dd, ws.uh, ldu};
+      g.add_n = r;
+      g.bias_n0 = r;
       HIPCHK(ctx, launch_gemm(g, st));
-      HIPCHK(ctx, launch_corr_logits(batch, A, M, r, D, dd, w.W2, wt, ws.C, ws.Cl, ws.u, ws.ell, st));
+      HIPCHK(ctx, launch_corr_logits(batch, A, M, r, D, dd, w.W2, wt, ws.C, ws.Cl, ws.uh, ldu,
+                                     ws.ell, st));
       HIPCHK(ctx, launch_select(batch, A, M, K, W, D, dd, off, ws.C, ws.ell, tb, st));
       const int An = A * K < W ? A * K : W;
       if (dd + 1 < D) {
         g = GemmArgs{batch * An, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
                      w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
         HIPCHK(ctx, launch_gemm(g, st));
-        g = GemmArgs{batch * An, 3 * s, s, ws.S[sc], WT_F32, s, ws.gidx_par, 0, w.W_hh, wt, s,
-                     w.b_hh, nullptr, 0, 1, 0, 0, ws.gh, 3 * s};
-        HIPCHK(ctx, launch_gemm(g, st));
-        HIPCHK(ctx, launch_gru_combine(batch * An, s, ws.gi, ws.gh, nullptr, ws.S[sc], ws.gidx_par,
-                                       ws.S[1 - sc], st));
+        HIPCHK(ctx, launch_gru_combine(batch * An, s, ws.gi, ws.uh + r, ldu, nullptr, ws.S[sc],
+                                       ws.gidx_par, ws.S[1 - sc], st));
         sc = 1 - sc;
       }
       cur = 1 - cur;

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void k_corr_logits(int A, int M, int r, int D,
                                                      int vec, const WT *__restrict__ W2,
                                                      const int32_t *__restrict__ C,
                                                      const float *__restrict__ Cl,
-                                                     const float *__restrict__ u,
+                                                     const float *__restrict__ u, int ldu,
                                                      float *__restrict__ ell) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int q = blockIdx.x, a0 = blockIdx.y * CL_BR;
@@ -57,8 +57,11 @@ __global__ __launch_bounds__(256) void k_corr_logits(int A, int M, int r, int D,
       W2s[j * rs + tt] = W2[(size_t)tk * r + tt];
     }
   }
-  const float *uq = u + ((size_t)q * A + a0) * r;
-  for (int i = threadIdx.x; i < na * r; i += blockDim.x) us[i] = uq[i];
+  const float *uq = u + ((size_t)q * A + a0) * ldu;
+  for (int i = threadIdx.x; i < na * r; i += blockDim.x) {
+    const int a = i / r;
+    us[i] = uq[(size_t)a * ldu + (i - a * r)];
+  }
   __syncthreads();
   const float *clq = Cl + ((size_t)q * D + delta) * M;
   for (int o = threadIdx.x; o < na * M; o += blockDim.x) {
@@ -103,16 +106,16 @@ hipError_t corr_logits_prepare(int wtype, size_t smem) {
 
 hipError_t launch_corr_logits(int b, int A, int M, int r, int D, int delta, const void *W2,
                               int wtype, const int32_t *C, const float *Cl, const float *u,
-                              float *ell, hipStream_t st) {
+                              int ldu, float *ell, hipStream_t st) {
   const size_t sm = corr_logits_smem(A, M, r, wtype);
   const dim3 grid(b, (A + CL_BR - 1) / CL_BR);
   const int vec = wtype == WT_BF16 && r % 8 == 0 && reinterpret_cast<uintptr_t>(W2) % 16 == 0;
   if (wtype == WT_BF16)
     hipLaunchKernelGGL(k_corr_logits<uint16_t>, grid, dim3(256), sm, st, A, M, r, D, delta, vec,
-                       static_cast<const uint16_t *>(W2), C, Cl, u, ell);
+                       static_cast<const uint16_t *>(W2), C, Cl, u, ldu, ell);
   else
     hipLaunchKernelGGL(k_corr_logits<float>, grid, dim3(256), sm, st, A, M, r, D, delta, 0,
-                       static_cast<const float *>(W2), C, Cl, u, ell);
+                       static_cast<const float *>(W2), C, Cl, u, ldu, ell);
   return hipGetLastError();
 }
 

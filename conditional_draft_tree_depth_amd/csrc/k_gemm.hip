@@ -8,6 +8,8 @@
 // rounded to bf16); bf16 weights are widened exactly to fp32; accumulation
 // is fp32.  Tiles: 64 rows x 64 outputs per 256-thread workgroup, 16-wide k
 // chunks staged in LDS.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -78,8 +80,8 @@ __global__ __launch_bounds__(256) void k_gemm_xwT(GemmArgs a) {
       const int n = n0 + tx * 4 + j;
       if (n >= a.N) continue;
       float v = acc[i][j];
-      if (a.bias) v += a.bias[n];
-      if (add) v += add[n];
+      if (a.bias && n >= a.bias_n0) v += a.bias[n - a.bias_n0];
+      if (add && n < a.add_n) v += add[n];
       a.Y[(size_t)row * a.ldy + n] = v;
     }
   }
@@ -136,13 +138,13 @@ __device__ __forceinline__ void sk_split(const float4 &x0, const float4 &x1, uin
 }
 
 template <int TERMS, typename XT>
-__global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a) {
+__global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int RB) {
   constexpr bool XB = sizeof(XT) == 2;
   constexpr int KSW = XB ? SK_KSW_B : SK_KSW_F;
   __shared__ __align__(16) float red[SK_WAVES * SK_RB * 256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 16, r0 = blockIdx.y * (16 * SK_RB);
-  const int nrb = min(SK_RB, (a.R - r0 + 15) >> 4);
+  const int n0 = blockIdx.x * 16, r0 = blockIdx.y * (16 * RB);
+  const int nrb = min(RB, (a.R - r0 + 15) >> 4);
   const int nks = a.Kd >> 5;
   const uint16_t *wrow = static_cast<const uint16_t *>(a.W) + (size_t)min(n0 + lr, a.N - 1) * a.ldw + g * 8;
   // k-steps past the contraction load the last one again (every load is
@@ -215,8 +217,8 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a) {
 #pragma unroll
     for (int w = 0; w < SK_WAVES; ++w) v += red[((w * SK_RB + rb) * 16 + rr) * 16 + nn];
     if (row < a.R && n < a.N) {
-      if (a.bias) v += a.bias[n];
-      if (a.addend) v += a.addend[(size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda + n];
+      if (a.bias && n >= a.bias_n0) v += a.bias[n - a.bias_n0];
+      if (a.addend && n < a.add_n) v += a.addend[(size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda + n];
       a.Y[(size_t)row * a.ldy + n] = v;
     }
   }
@@ -243,13 +245,18 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.R <= 0 || a.N <= 0) return hipSuccess;
   if (skinny_ok(a)) {
     const int terms = skinny_terms(a);
-    dim3 grid((a.N + 15) / 16, (a.R + 16 * SK_RB - 1) / (16 * SK_RB));
+    // row blocks per workgroup: enough workgroups to fill the chip (about
+    // 1024) before a weight tile is reused for more rows
+    const int ncol = (a.N + 15) / 16, nrb = (a.R + 15) / 16;
+    const int groups = std::max(1, std::min(nrb, 1024 / ncol));
+    const int RB = std::min(SK_RB, (nrb + groups - 1) / groups);
+    dim3 grid(ncol, (nrb + RB - 1) / RB);
     if (a.xtype == WT_BF16)
-      hipLaunchKernelGGL((k_skinny_bf16<1, uint16_t>), grid, dim3(SK_WAVES * 64), 0, st, a);
+      hipLaunchKernelGGL((k_skinny_bf16<1, uint16_t>), grid, dim3(SK_WAVES * 64), 0, st, a, RB);
     else if (terms == 1)
-      hipLaunchKernelGGL((k_skinny_bf16<1, float>), grid, dim3(SK_WAVES * 64), 0, st, a);
+      hipLaunchKernelGGL((k_skinny_bf16<1, float>), grid, dim3(SK_WAVES * 64), 0, st, a, RB);
     else
-      hipLaunchKernelGGL((k_skinny_bf16<3, float>), grid, dim3(SK_WAVES * 64), 0, st, a);
+      hipLaunchKernelGGL((k_skinny_bf16<3, float>), grid, dim3(SK_WAVES * 64), 0, st, a, RB);
     return hipGetLastError();
   }
   dim3 grid((a.N + GT - 1) / GT, (a.R + GT - 1) / GT);
@@ -269,7 +276,7 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
 //   h' = (1 - z) n + z h
 // where a = W_ih x + b_ih and c = W_hh h + b_hh.
 __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *__restrict__ gi,
-                                                     const float *__restrict__ gh,
+                                                     const float *__restrict__ gh, int ldgh,
                                                      const float *__restrict__ b_hh,
                                                      const float *__restrict__ Sprev,
                                                      const int32_t *__restrict__ pidx,
@@ -280,9 +287,10 @@ __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *
   const float *a = gi + (size_t)i * 3 * s;
   float cr, cz, cn, h;
   if (gh) {
-    const float *c = gh + (size_t)i * 3 * s;
+    const int pr = pidx ? pidx[i] : i;   // the parent's row: its state and state part
+    const float *c = gh + (size_t)pr * ldgh;
     cr = c[j]; cz = c[s + j]; cn = c[2 * s + j];
-    h = Sprev[(size_t)(pidx ? pidx[i] : i) * s + j];
+    h = Sprev[(size_t)pr * s + j];
   } else {
     cr = b_hh ? b_hh[j] : 0.f;
     cz = b_hh ? b_hh[s + j] : 0.f;
@@ -295,13 +303,40 @@ __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *
   Snew[(size_t)i * s + j] = (1.f - z) * n + z * h;
 }
 
-hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh, const float *b_hh,
-                              const float *Sprev, const int32_t *pidx, float *Snew,
-                              hipStream_t st) {
+hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh, int ldgh,
+                              const float *b_hh, const float *Sprev, const int32_t *pidx,
+                              float *Snew, hipStream_t st) {
   const int n = R * s;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gru_combine, dim3((n + 255) / 256), dim3(256), 0, st, R, s, gi, gh, b_hh,
-                     Sprev, pidx, Snew);
+  hipLaunchKernelGGL(k_gru_combine, dim3((n + 255) / 256), dim3(256), 0, st, R, s, gi, gh, ldgh,
+                     b_hh, Sprev, pidx, Snew);
+  return hipGetLastError();
+}
+
+// Wcat rows n < r: W1[n][d .. d + s); rows r + m: W_hh[m] (made once per
+// context, so that the low-rank head's state part and the GRU's state
+// projection of the same branches are one product)
+template <typename T>
+__global__ void k_concat_state_weights(const T *__restrict__ W1, const T *__restrict__ W_hh,
+                                       int r, int s, int d, T *__restrict__ Wcat) {
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i >= (size_t)(r + 3 * s) * s) return;
+  const int n = (int)(i / s), k = (int)(i - (size_t)n * s);
+  Wcat[i] = n < r ? W1[(size_t)n * (d + s) + d + k] : W_hh[(size_t)(n - r) * s + k];
+}
+
+hipError_t launch_concat_state_weights(const void *W1, const void *W_hh, int r, int s, int d,
+                                       int wtype, void *Wcat, hipStream_t st) {
+  const size_t n = (size_t)(r + 3 * s) * s;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (wtype == WT_BF16)
+    hipLaunchKernelGGL(k_concat_state_weights<uint16_t>, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t *>(W1), static_cast<const uint16_t *>(W_hh), r,
+                       s, d, static_cast<uint16_t *>(Wcat));
+  else
+    hipLaunchKernelGGL(k_concat_state_weights<float>, grid, dim3(256), 0, st,
+                       static_cast<const float *>(W1), static_cast<const float *>(W_hh), r, s, d,
+                       static_cast<float *>(Wcat));
   return hipGetLastError();
 }
 

@@ -86,7 +86,8 @@ hipError_t launch_topm_merge(const uint64_t *part, int P, int M, int rows,
                              int32_t *C, float *Cl, hipStream_t st);
 
 // ---- generic fp32-activation x weight^T product with gathers and epilogue
-// Y[i][n] = sum_k X[xrow(i)][k] * W[n][k] + bias[n] + addend[arow(i)][n]
+// Y[i][n] = sum_k X[xrow(i)][k] * W[n][k] + bias[n - bias_n0] (n >= bias_n0)
+//           + addend[arow(i)][n] (n < add_n)
 // xrow(i) = xidx ? xidx[i] : i ; arow(i) = (i / adiv) * amul + aoff
 struct GemmArgs {
   int R, N, Kd;
@@ -95,20 +96,26 @@ struct GemmArgs {
   const float *bias;
   const float *addend; int lda, adiv, amul, aoff;
   float *Y; int ldy;
+  int add_n = 1 << 30;   // the addend covers outputs n < add_n
+  int bias_n0 = 0;       // the bias covers outputs n >= bias_n0
 };
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
 hipError_t skinny_prepare(size_t lds_max);
 void gemm_set_lds_max(size_t bytes);
 // GRU gates: gi, gh = input/state projections incl. biases ([R, 3s]); if gh
 // is null the previous state is zero and the state part equals b_hh.
-hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh,
+// Row i takes gh row pidx[i] (stride ldgh) and previous state row pidx[i].
+hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh, int ldgh,
                               const float *b_hh, const float *Sprev,
                               const int32_t *pidx, float *Snew, hipStream_t st);
+// Wcat = [W1[:, d:] ; W_hh] as [r + 3s, s] rows in the weight dtype
+hipError_t launch_concat_state_weights(const void *W1, const void *W_hh, int r, int s, int d,
+                                       int wtype, void *Wcat, hipStream_t st);
 
 // ---- per-depth kernels
 hipError_t launch_corr_logits(int b, int A, int M, int r, int D, int delta,
                               const void *W2, int wtype, const int32_t *C,
-                              const float *Cl, const float *u, float *ell,
+                              const float *Cl, const float *u, int ldu, float *ell,
                               hipStream_t st);
 size_t corr_logits_smem(int A, int M, int r, int wtype);
 hipError_t launch_select(int b, int A, int M, int K, int W, int D, int delta,
