@@ -39,6 +39,7 @@ struct Ws {
   float *G = nullptr, *g = nullptr, *pk_part = nullptr, *gitab = nullptr, *pk_terms = nullptr;
   uint16_t *w1t = nullptr;   // W1[:, d:]^T, padded (correction tables)
   uint16_t *hb = nullptr;    // bf16 hidden rows of the round (LM-head kernel)
+  float *logits = nullptr;   // [b * D, V] base logits when 32 or more rows (tiled product)
   uint32_t *flags = nullptr;
 };
 
@@ -118,7 +119,8 @@ void free_ws(Ws &ws) {
   void *ptrs[] = {ws.part, ws.hb, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.uh, ws.ell, ws.gi, ws.wcat,
                   ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
-                  ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags};
+                  ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags,
+                  ws.logits};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   ws = Ws();
@@ -207,6 +209,8 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   A(alloc(&ws.Cl, rows * c.max_M));
   A(alloc(&ws.uH, rows * r));
   A(alloc(&ws.hb, (size_t)((rows + 15) / 16 * 16) * w->d));
+  if (lmhead_tiled_ok((int)rows, w->d, w->wtype == DTREE_BF16 ? WT_BF16 : WT_F32))
+    A(alloc(&ws.logits, rows * (size_t)w->V));
   A(alloc(&ws.S[0], bw * s));
   A(alloc(&ws.S[1], bw * s));
   A(alloc(&ws.uh, bw * (r + 3 * s)));
@@ -331,7 +335,9 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   // K1 + K1b: candidate tables
   prof_mark(ctx, 0, st);
   // bf16: the LM-head kernel also produces uH = W1[:, :d] . Hq (same operand)
-  const bool fuse_uH = wt == WT_BF16 && (d + s) % 8 == 0 &&
+  // 32 or more rows: a tiled product writes the logits, lists from those
+  const bool tiled = ws.logits != nullptr && lmhead_tiled_ok(rows, d, wt);
+  const bool fuse_uH = !tiled && wt == WT_BF16 && (d + s) % 8 == 0 &&
                        reinterpret_cast<uintptr_t>(w.W1) % 16 == 0;
   LMHeadArgs la{H, rows, d, w.W_lm, wt, w.V, w.lm_bias, M, ctx->P, ws.part,
                 fuse_uH ? w.W1 : nullptr, d + s, r, ws.uH,
@@ -342,12 +348,17 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   hipEvent_t k1ev[2] = {nullptr, nullptr};
   if (ctx->prof && ctx->prof_n < kProfRounds)
     for (int i = 0; i < 2; ++i) k1ev[i] = ctx->prof_ev[ctx->prof_n * (DTREE_NSTAGES + 1) + 1 + i];
-  HIPCHK(ctx, launch_lmhead(la, st, k1ev[0], k1ev[1]));
+  if (tiled) HIPCHK(ctx, launch_lmhead_tiled(la, ws.logits, st, k1ev[0], k1ev[1]));
+  else HIPCHK(ctx, launch_lmhead(la, st, k1ev[0], k1ev[1]));
   HIPCHK(ctx, launch_topm_merge(ws.part, ctx->P, M, rows, ws.C, ws.Cl, st));
   prof_mark(ctx, 3, st);
   // K2: uH = W1[:, :d] . Hq for every (request, depth), when not fused above
   GemmArgs g{};
-  if (!fuse_uH) {
+  if (tiled) {   // from the bf16 hidden rows of the round start (= the rounded H)
+    g = GemmArgs{rows, r, d, ws.hb, WT_BF16, d, nullptr, 0, w.W1, wt, d + s,
+                 nullptr, nullptr, 0, 1, 0, 0, ws.uH, r};
+    HIPCHK(ctx, launch_gemm(g, st));
+  } else if (!fuse_uH) {
     g = GemmArgs{rows, r, d, H, WT_F32, d, nullptr, wt == WT_BF16 ? 1 : 0, w.W1, wt, d + s,
                  nullptr, nullptr, 0, 1, 0, 0, ws.uH, r};
     HIPCHK(ctx, launch_gemm(g, st));

@@ -661,6 +661,201 @@ __global__ __launch_bounds__(256) void k1_stage_hidden(const float *__restrict__
       init_round_request(q, root, tb, Dp1, threadIdx.x, blockDim.x);
 }
 
+// ---- many hidden rows (32 or more): the base logits as a tiled MFMA
+// product written to memory, then the same per-slice candidate lists.
+// With b*D rows the vocabulary projection stops being a pure stream of W_lm
+// (128 rows: 128 flop per weight byte, 512 rows: 512), so every workgroup
+// takes a 128-row x 128-token tile and a W_lm tile is read once for all the
+// rows of the tile instead of once per 16-row block.  Operands are staged in
+// LDS, 64-wide k chunks, double-buffered, with the 16-byte chunk c of row q
+// stored at c ^ (q & 7) so that the fragment reads of 16 rows hit distinct
+// banks; each of the 4 waves computes a 64 x 64 quarter (4 x 4 MFMA tiles).
+constexpr int LT_BM = 128, LT_BN = 128, LT_BK = 64, LT_THREADS = 256;
+constexpr int LT_STAGES = 4;                          // LDS ring: 3 k chunks in flight
+constexpr int LT_STAGE_CHUNKS = (LT_BM + LT_BN) * 8;  // 16-byte chunks per stage
+constexpr size_t LT_SMEM = (size_t)LT_STAGES * LT_STAGE_CHUNKS * 16;
+
+__global__ __launch_bounds__(LT_THREADS) void k1_logits_tiled(
+    const uint16_t *__restrict__ Hb, int rows, int rows_pad, int d,
+    const uint16_t *__restrict__ W, int V, const float *__restrict__ bias,
+    float *__restrict__ L) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint4 *ring = reinterpret_cast<uint4 *>(smem);
+  const int ntm = (rows + LT_BM - 1) / LT_BM, ntn = (V + LT_BN - 1) / LT_BN;
+  const int total = ntm * ntn;
+  int task = blockIdx.x;
+  // the row tiles of one token tile run one after another on one XCD
+  // (workgroups are handed to the 8 XCDs in turn), sharing its L2 for W_lm
+  if (total % 8 == 0) task = (task & 7) * (total / 8) + (task >> 3);
+  const int m0 = (task % ntm) * LT_BM, n0 = (task / ntm) * LT_BN;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  // A stage holds 16 copy instructions of hidden rows, then 16 of W_lm rows,
+  // each 64 lanes x 16 bytes straight from global memory into LDS; slot s
+  // (row s >> 3, position s & 7) receives chunk (s & 7) ^ (row & 7) of its
+  // row.  Wave w issues instructions w, w + 4, ..., w + 28.
+  const uint4 *src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = wave + 4 * i, sl = (j & 15) * 64 + lane, row = sl >> 3;
+    const int ch = (sl & 7) ^ (row & 7);
+    const uint16_t *base = j >= 16 ? W + (size_t)min(n0 + row, V - 1) * d
+                                   : Hb + (size_t)min(m0 + row, rows_pad - 1) * d;
+    src[i] = reinterpret_cast<const uint4 *>(base) + ch;
+  }
+  const int nk = d / LT_BK;
+  auto issue = [&](int kc) {
+    uint4 *dst = ring + (kc % LT_STAGES) * LT_STAGE_CHUNKS;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(src[i] + kc * 8,
+                                       (__attribute__((address_space(3))) void *)(dst + (wave + 4 * i) * 64),
+                                       16, 0, 0);
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kc = 0; kc < LT_STAGES - 1 && kc < nk; ++kc) issue(kc);
+  for (int kc = 0; kc < nk; ++kc) {
+    // this wave's copies of chunk kc have landed (the later ones may still
+    // be in flight); the barrier makes every wave's copies visible and
+    // retires every read of the buffer refilled next
+    const int ahead = min(LT_STAGES - 2, nk - 1 - kc);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+    __syncthreads();
+    if (kc + LT_STAGES - 1 < nk) issue(kc + LT_STAGES - 1);
+    const uint4 *As = ring + (kc % LT_STAGES) * LT_STAGE_CHUNKS, *Bs = As + LT_BM * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = 4 * ks + g;
+      uint4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra_ = wm + i * 16 + lr, rb_ = wn + i * 16 + lr;
+        af[i] = As[ra_ * 8 + (ch ^ (ra_ & 7))];
+        bf[i] = Bs[rb_ * 8 + (ch ^ (rb_ & 7))];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[i]), as_bf16x8(bf[j]),
+                                                             acc[i][j], 0, 0, 0);
+    }
+  }
+  // lane holds D[hidden row 4 g + t][token lr] of tile (i, j)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int v = n0 + wn + j * 16 + lr;
+    if (v >= V) continue;
+    const float bv = bias ? bias[v] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int row = m0 + wm + i * 16 + 4 * g + t;
+        if (row < rows) L[(size_t)row * V + v] = acc[i][j][t] + bv;
+      }
+  }
+}
+
+// Exact candidate list for M > 64 (logits in LDS, one row per half-wave):
+// the M-th largest key K of the slice is found by bisection over the 64
+// key bits (keys are distinct, so count(keys >= T) >= M holds exactly for
+// T <= K; each step is one comparison per held key and a half-wave sum);
+// the keys >= K, exactly M of them, are written unsorted with K as the
+// list's bound, the best key and the count (the layout of the fast path).
+// A slice with fewer than M keys writes all of them with a zero bound.
+template <int MAXC>
+__device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int ncols, int col0,
+                                               int nrow, int M, uint64_t *out, size_t rstride) {
+  constexpr int KPL = MAXC / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6, hl = lane & 31;
+  // inclusive prefix (over the half-wave, by lane) of c, and its total
+  auto scan = [&](int c, int &incl, int &tot) {
+    int y;
+    incl = c; tot = c;
+    y = (int)dpp_u32<0xB1>((uint32_t)tot); if (hl & 1) incl += y; tot += y;
+    y = (int)dpp_u32<0x4E>((uint32_t)tot); if (hl & 2) incl += y; tot += y;
+    y = __builtin_amdgcn_ds_swizzle(tot, 0x101F); if (hl & 4) incl += y; tot += y;
+    y = __builtin_amdgcn_ds_swizzle(tot, 0x201F); if (hl & 8) incl += y; tot += y;
+    y = __builtin_amdgcn_ds_swizzle(tot, 0x401F); if (hl & 16) incl += y; tot += y;
+  };
+  for (int rb = wave * 2; rb < nrow; rb += 2 * nw) {
+    const int r = rb + (lane >> 5);
+    const bool active = r < nrow;
+    uint64_t keys[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int c = hl + 32 * i;
+      keys[i] = (active && c < ncols)
+                    ? ((uint64_t)f32_ord(Ls[r * lstride + c]) << 32) |
+                          (uint64_t)(0xFFFFFFFFu - (uint32_t)(col0 + c))
+                    : 0ull;
+    }
+    uint64_t T = 0;
+    if (ncols > M) {
+      for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t cand = T | (1ull << bit);
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) c += keys[i] >= cand ? 1 : 0;
+        int incl, tot;
+        scan(c, incl, tot);
+        if (tot >= M) T = cand;
+      }
+    }
+    const uint64_t lo = T ? T : 1ull;   // key 0 marks an empty column
+    int c = 0;
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (keys[i] >= lo) { ++c; best = keys[i] > best ? keys[i] : best; }
+    int incl, tot;
+    scan(c, incl, tot);
+    const uint64_t head = group_max_u64<32>(best);
+    if (active) {
+      uint64_t *outr = out + (size_t)r * rstride;
+      int pos = incl - c;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i)
+        if (keys[i] >= lo) outr[pos++] = keys[i];
+      if (hl == 0) {
+        outr[K1_LCAP] = T;
+        outr[K1_LCAP + 1] = head;
+        outr[K1_LCAP + 2] = (uint64_t)tot;
+      }
+    }
+  }
+}
+
+// The candidate list of (16-row block, vocabulary slice y) from logits in
+// memory: the slice's logits go to LDS and the LM-head kernel's epilogue
+// runs on them unchanged (slices cover the vocabulary tiles only).
+__global__ __launch_bounds__(K1_WAVES * 64) void k1_lists_from_logits(
+    const float *__restrict__ L, int rows, int V, int M, uint64_t *__restrict__ part) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  float *Ls = reinterpret_cast<float *>(smem);
+  const int P = gridDim.y, y = blockIdx.y, row0 = blockIdx.x * 16;
+  const int nrow = min(16, rows - row0);
+  const int ntV = (V + 15) >> 4;
+  const int t0 = (int)((long long)ntV * y / P), t1 = (int)((long long)ntV * (y + 1) / P);
+  const int c0 = t0 * 16, ncols = max(0, min(t1 * 16, V) - c0);
+  for (int i = threadIdx.x; i < nrow * ncols; i += blockDim.x) {
+    const int rr = i / ncols, c = i - rr * ncols;
+    Ls[rr * K1_MAXCOLS + c] = L[(size_t)(row0 + rr) * V + c0 + c];
+  }
+  __syncthreads();
+  uint64_t *out = part + ((size_t)row0 * P + y) * K1_LSTRIDE;
+  if (M > 64) wg_topm_bisect<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE);
+  else wg_topm_epilogue<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE);
+}
+
 // ----------------------------------------------------------------- host side
 int lmhead_partitions(int V, int wtype, int extra_tiles) {
   const int ntiles = (V + 15) / 16 + (wtype == WT_BF16 ? extra_tiles : 0);
@@ -691,6 +886,9 @@ hipError_t lmhead_prepare(int wtype, int ring, size_t smem) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
   if (e != hipSuccess || wtype != WT_BF16) return e;
   const void *fn = ring == 2 ? k1_fn<2>() : ring == 1 ? k1_fn<1>() : k1_fn<0>();
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k1_logits_tiled),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)LT_SMEM);
+  if (e != hipSuccess) return e;
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
 }
 
@@ -712,6 +910,26 @@ hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st, hipEvent_t ev0, hi
                           a.rows, a.d, static_cast<const float *>(a.W), a.V, a.bias, a.M, a.part,
                           a.root, a.b, a.Dp1, a.t);
   }
+  return hipGetLastError();
+}
+
+bool lmhead_tiled_ok(int rows, int d, int wtype) {
+  return wtype == WT_BF16 && rows >= 32 && d % LT_BK == 0;
+}
+
+hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t st, hipEvent_t ev0,
+                               hipEvent_t ev1) {
+  const int rows_pad = (a.rows + 15) & ~15;
+  const int ntm = (a.rows + LT_BM - 1) / LT_BM, ntn = (a.V + LT_BN - 1) / LT_BN;
+  hipExtLaunchKernelGGL(k1_logits_tiled, dim3(ntm * ntn), dim3(LT_THREADS), (uint32_t)LT_SMEM, st,
+                        ev0, nullptr,
+                        0u, (const uint16_t *)a.Hb, a.rows, rows_pad, a.d,
+                        static_cast<const uint16_t *>(a.W), a.V, a.bias, logits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipExtLaunchKernelGGL(k1_lists_from_logits, dim3(rows_pad / 16, a.P), dim3(K1_WAVES * 64),
+                        (uint32_t)(16 * K1_MAXCOLS * 4), st, nullptr, ev1, 0u,
+                        (const float *)logits, a.rows, a.V, a.M, a.part);
   return hipGetLastError();
 }
 

@@ -82,6 +82,11 @@ hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st, hipEvent_t ev0 = n
                          hipEvent_t ev1 = nullptr);
 // ---- K1b: the M best keys of each row from its P lists -> C (tokens), Cl (logits)
 size_t topm_merge_smem(int P);
+// 32 or more hidden rows (bf16): logits [rows, V] fp32 by a tiled MFMA
+// product, then the same per-slice candidate lists (uH is not produced)
+bool lmhead_tiled_ok(int rows, int d, int wtype);
+hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t st,
+                               hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_topm_merge(const uint64_t *part, int P, int M, int rows,
                              int32_t *C, float *Cl, hipStream_t st);
 
