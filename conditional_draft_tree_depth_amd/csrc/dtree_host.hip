@@ -40,6 +40,7 @@ struct Ws {
   uint16_t *w1t = nullptr;   // W1[:, d:]^T, padded (correction tables)
   uint16_t *hb = nullptr;    // bf16 hidden rows of the round (LM-head kernel)
   float *logits = nullptr;   // [b * D, V] base logits when 32 or more rows (tiled product)
+  uint16_t *S3[2] = {nullptr, nullptr};   // states as three bf16 planes (many branches)
   uint32_t *flags = nullptr;
 };
 
@@ -120,7 +121,7 @@ void free_ws(Ws &ws) {
                   ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
                   ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags,
-                  ws.logits};
+                  ws.logits, ws.S3[0], ws.S3[1]};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   ws = Ws();
@@ -214,6 +215,10 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   A(alloc(&ws.S[0], bw * s));
   A(alloc(&ws.S[1], bw * s));
   A(alloc(&ws.uh, bw * (r + 3 * s)));
+  // 256 or more branches: the state products run as tiled bf16 products over
+  // the three-plane split of the states
+  if (w->wtype == DTREE_BF16 && s % 64 == 0 && bw >= 256)
+    for (int i = 0; i < 2; ++i) A(alloc(&ws.S3[i], bw * 3 * s));
   A(alloc(&ws.ell, bw * c.max_M));
   A(alloc(&ws.gi, bw * 3 * s));
   const size_t esz_w = w->wtype == DTREE_BF16 ? 2 : 4;
@@ -268,6 +273,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   if (pe == hipSuccess) pe = corr_logits_prepare(w->wtype, cl_smem);
   if (pe == hipSuccess) pe = topb_prepare(tb_smem);
   if (pe == hipSuccess) pe = skinny_prepare(ctx->lds_max);
+  if (pe == hipSuccess) pe = gemm_prepare();
   if (pe == hipSuccess && ctx->pk) pe = persist_prepare(s);
   gemm_set_lds_max(ctx->lds_max);
   if (pe != hipSuccess) {
@@ -389,7 +395,8 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
     g = GemmArgs{batch, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
                  w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
     HIPCHK(ctx, launch_gemm(g, st));
-    HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, 0, w.b_hh, nullptr, nullptr, ws.S[0], st));
+    HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, 0, w.b_hh, nullptr, nullptr, ws.S[0],
+                                   ws.S3[0], st));
     prof_mark(ctx, 4, st);
     for (int dd = 0; dd < D; ++dd) {
       // for every expanded branch, one product over its state S:
@@ -399,6 +406,13 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
       const int ldu = r + 3 * s;
       g = GemmArgs{batch * A, ldu, s, ws.S[sc], WT_F32, s, nullptr, 0, ws.wcat, wt, s, w.b_hh,
                    ws.uH, r, A, D, dd, ws.uh, ldu};
+      if (ws.S3[sc] && batch * A >= 256) {   // the state as three bf16 planes
+        g.X = ws.S3[sc];
+        g.xtype = WT_BF16;
+        g.ldx = 3 * s;
+        g.Kd = 3 * s;
+        g.kw = s;
+      }
       g.add_n = r;
       g.bias_n0 = r;
       HIPCHK(ctx, launch_gemm(g, st));
@@ -411,7 +425,7 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
                      w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
         HIPCHK(ctx, launch_gemm(g, st));
         HIPCHK(ctx, launch_gru_combine(batch * An, s, ws.gi, ws.uh + r, ldu, nullptr, ws.S[sc],
-                                       ws.gidx_par, ws.S[1 - sc], st));
+                                       ws.gidx_par, ws.S[1 - sc], ws.S3[1 - sc], st));
         sc = 1 - sc;
       }
       cur = 1 - cur;

@@ -224,6 +224,120 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int R
   }
 }
 
+// Many activation rows (256 or more): bf16 x bf16 product in 128 x 128
+// tiles (activation rows x weight rows), operands staged in a 4-stage LDS
+// ring by direct global-to-LDS copies (3 k chunks of 64 in flight), the
+// 16-byte chunk c of row q at position c ^ (q & 7) so that fragment reads
+// of 16 rows hit distinct banks; each of the 4 waves computes a 64 x 64
+// quarter.  Activation rows are gathered through xidx; the weights' k index
+// runs modulo kw (a three-plane split state meets the same weights three
+// times).  The row tiles of one weight tile run one after another on one
+// XCD, sharing its L2.
+constexpr int GTT_B = 128, GTT_BK = 64, GTT_THREADS = 256, GTT_STAGES = 4;
+constexpr int GTT_STAGE_CHUNKS = 2 * GTT_B * 8;
+constexpr size_t GTT_SMEM = (size_t)GTT_STAGES * GTT_STAGE_CHUNKS * 16;
+
+__global__ __launch_bounds__(GTT_THREADS) void k_gemm_tiled(GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint4 *ring = reinterpret_cast<uint4 *>(smem);
+  const int ntm = (a.R + GTT_B - 1) / GTT_B, ntn = (a.N + GTT_B - 1) / GTT_B;
+  const int total = ntm * ntn;
+  int task = blockIdx.x;
+  if (total % 8 == 0) task = (task & 7) * (total / 8) + (task >> 3);
+  const int m0 = (task % ntm) * GTT_B, n0 = (task / ntm) * GTT_B;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const uint16_t *X = static_cast<const uint16_t *>(a.X);
+  const uint16_t *W = static_cast<const uint16_t *>(a.W);
+  const int nk = a.Kd / GTT_BK, nkw = (a.kw ? a.kw : a.Kd) / GTT_BK;
+  // copy instruction j of a stage: 0..15 activation rows, 16..31 weight rows
+  const uint4 *src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = wave + 4 * i, sl = (j & 15) * 64 + lane, row = sl >> 3;
+    const int ch = (sl & 7) ^ (row & 7);
+    if (j >= 16) {
+      src[i] = reinterpret_cast<const uint4 *>(W + (size_t)min(n0 + row, a.N - 1) * a.ldw) + ch;
+    } else {
+      const int xr = min(m0 + row, a.R - 1);
+      src[i] = reinterpret_cast<const uint4 *>(X + (size_t)(a.xidx ? a.xidx[xr] : xr) * a.ldx) + ch;
+    }
+  }
+  auto issue = [&](int kc) {
+    uint4 *dst = ring + (kc % GTT_STAGES) * GTT_STAGE_CHUNKS;
+    const int kcw = kc % nkw;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = wave + 4 * i;
+      __builtin_amdgcn_global_load_lds(src[i] + (j >= 16 ? kcw : kc) * 8,
+                                       (__attribute__((address_space(3))) void *)(dst + j * 64),
+                                       16, 0, 0);
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kc = 0; kc < GTT_STAGES - 1 && kc < nk; ++kc) issue(kc);
+  for (int kc = 0; kc < nk; ++kc) {
+    const int ahead = min(GTT_STAGES - 2, nk - 1 - kc);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+    __syncthreads();
+    if (kc + GTT_STAGES - 1 < nk) issue(kc + GTT_STAGES - 1);
+    const uint4 *As = ring + (kc % GTT_STAGES) * GTT_STAGE_CHUNKS, *Bs = As + GTT_B * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = 4 * ks + g;
+      uint4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = wm + i * 16 + lr, rb = wn + i * 16 + lr;
+        af[i] = As[ra * 8 + (ch ^ (ra & 7))];
+        bf[i] = Bs[rb * 8 + (ch ^ (rb & 7))];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = sk_mfma(af[i], bf[j], acc[i][j]);
+    }
+  }
+  // lane holds Y[activation row 4 g + t][output lr] of tile (i, j)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn + j * 16 + lr;
+    if (n >= a.N) continue;
+    const float bv = (a.bias && n >= a.bias_n0) ? a.bias[n - a.bias_n0] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int row = m0 + wm + i * 16 + 4 * g + t;
+        if (row >= a.R) continue;
+        float v = acc[i][j][t] + bv;
+        if (a.addend && n < a.add_n)
+          v += a.addend[(size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda + n];
+        a.Y[(size_t)row * a.ldy + n] = v;
+      }
+  }
+}
+
+static bool tiled_ok(const GemmArgs &a) {
+  const int kw = a.kw ? a.kw : a.Kd;
+  auto al16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  const int tiles = ((a.R + GTT_B - 1) / GTT_B) * ((a.N + GTT_B - 1) / GTT_B);
+  return a.R >= 256 && tiles >= 64 && a.wtype == WT_BF16 && a.xtype == WT_BF16 && a.Kd % GTT_BK == 0 &&
+         kw % GTT_BK == 0 && a.Kd % kw == 0 && a.ldx % 8 == 0 && a.ldw % 8 == 0 && al16(a.X) &&
+         al16(a.W);
+}
+
+hipError_t gemm_prepare() {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_tiled),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GTT_SMEM);
+}
+
 static int skinny_terms(const GemmArgs &a) {
   return (a.xtype == WT_F32 && !a.xround) ? 3 : 1;
 }
@@ -243,6 +357,12 @@ void gemm_set_lds_max(size_t b) { g_lds_max = b; }
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.R <= 0 || a.N <= 0) return hipSuccess;
+  if (tiled_ok(a)) {
+    const int total = ((a.R + GTT_B - 1) / GTT_B) * ((a.N + GTT_B - 1) / GTT_B);
+    hipLaunchKernelGGL(k_gemm_tiled, dim3(total), dim3(GTT_THREADS), GTT_SMEM, st, a);
+    return hipGetLastError();
+  }
+  if (a.kw && a.kw != a.Kd) return hipErrorInvalidValue;   // planes need the tiled kernel
   if (skinny_ok(a)) {
     const int terms = skinny_terms(a);
     // row blocks per workgroup: enough workgroups to fill the chip (about
@@ -280,7 +400,8 @@ __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *
                                                      const float *__restrict__ b_hh,
                                                      const float *__restrict__ Sprev,
                                                      const int32_t *__restrict__ pidx,
-                                                     float *__restrict__ Snew) {
+                                                     float *__restrict__ Snew,
+                                                     uint16_t *__restrict__ S3) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= R * s) return;
   const int i = idx / s, j = idx - i * s;
@@ -300,16 +421,26 @@ __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *
   const float r = 1.f / (1.f + expf(-(a[j] + cr)));
   const float z = 1.f / (1.f + expf(-(a[s + j] + cz)));
   const float n = tanhf(a[2 * s + j] + r * cn);
-  Snew[(size_t)i * s + j] = (1.f - z) * n + z * h;
+  const float hn = (1.f - z) * n + z * h;
+  Snew[(size_t)i * s + j] = hn;
+  if (S3) {
+    const uint16_t t0 = f32_to_bf16_rne(hn);
+    const float r1 = hn - bf16_bits_to_f32(t0);
+    const uint16_t t1 = f32_to_bf16_rne(r1);
+    uint16_t *o = S3 + (size_t)i * 3 * s + j;
+    o[0] = t0;
+    o[s] = t1;
+    o[2 * s] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(t1));
+  }
 }
 
 hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh, int ldgh,
                               const float *b_hh, const float *Sprev, const int32_t *pidx,
-                              float *Snew, hipStream_t st) {
+                              float *Snew, uint16_t *S3, hipStream_t st) {
   const int n = R * s;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_gru_combine, dim3((n + 255) / 256), dim3(256), 0, st, R, s, gi, gh, ldgh,
-                     b_hh, Sprev, pidx, Snew);
+                     b_hh, Sprev, pidx, Snew, S3);
   return hipGetLastError();
 }
 

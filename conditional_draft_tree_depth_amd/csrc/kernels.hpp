@@ -103,6 +103,9 @@ struct GemmArgs {
   float *Y; int ldy;
   int add_n = 1 << 30;   // the addend covers outputs n < add_n
   int bias_n0 = 0;       // the bias covers outputs n >= bias_n0
+  int kw = 0;            // bf16 X only: W's k index is k mod kw (0: kw = Kd); a
+                         // state split into three bf16 planes [hi | mid | lo]
+                         // is multiplied by the same weights three times
 };
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
 hipError_t skinny_prepare(size_t lds_max);
@@ -110,9 +113,12 @@ void gemm_set_lds_max(size_t bytes);
 // GRU gates: gi, gh = input/state projections incl. biases ([R, 3s]); if gh
 // is null the previous state is zero and the state part equals b_hh.
 // Row i takes gh row pidx[i] (stride ldgh) and previous state row pidx[i].
+// S3 (or null): the new state also as three bf16 planes, row i = [hi | mid | lo]
+// ([R, 3s]), the exact split hi + mid + lo of every fp32 value.
 hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh, int ldgh,
                               const float *b_hh, const float *Sprev,
-                              const int32_t *pidx, float *Snew, hipStream_t st);
+                              const int32_t *pidx, float *Snew, uint16_t *S3, hipStream_t st);
+hipError_t gemm_prepare();
 // Wcat = [W1[:, d:] ; W_hh] as [r + 3s, s] rows in the weight dtype
 hipError_t launch_concat_state_weights(const void *W1, const void *W_hh, int r, int s, int d,
                                        int wtype, void *Wcat, hipStream_t st);

@@ -67,10 +67,14 @@ def test_random_small_shapes(gpu_lib, seed):
     (2, 512, 128, 256, 16, 6, 16, 3, 16, 60, 4),
     (3, 128, 256, 384, 48, 4, 128, 8, 8, 90, 8),
     (4, 384, 128, 128, 256, 7, 33, 5, 12, 77, 3),
+    # 8 x 32 = 256 expanded branches and 40 hidden rows: tiled products over
+    # the three-plane states, tiled LM head with lists from the logits
+    (5, 256, 128, 128, 64, 5, 64, 8, 32, 200, 8),
+    (6, 128, 192, 256, 32, 4, 128, 4, 64, 150, 6),
 ])
 def test_mfma_product_paths(gpu_lib, seed, d, e, s, r, D, M, K, W, B, batch):
-    """bf16 shapes whose products run on the MFMA kernels (contraction
-    widths multiple of 128, at most 64 activation rows)."""
+    """bf16 shapes whose products run on the MFMA kernels: the row-gathered
+    product, and for many rows the tiled products and tiled LM head."""
     cfg = synth.custom_config(cfg_id=8000 + seed, d=d, V=4000 + 17 * seed, e=e, s=s, r=r,
                               D=D, M=M, K=K, W=W, B=B, beta=-0.05, batch=batch, wtype="bf16")
     check_config(synth.make_inputs(cfg, seed), cfg, f"mfma {seed}", max_tie_frac=0.34)
