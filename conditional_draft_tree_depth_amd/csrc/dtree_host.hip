@@ -406,15 +406,17 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
       const int ldu = r + 3 * s;
       g = GemmArgs{batch * A, ldu, s, ws.S[sc], WT_F32, s, nullptr, 0, ws.wcat, wt, s, w.b_hh,
                    ws.uH, r, A, D, dd, ws.uh, ldu};
-      if (ws.S3[sc] && batch * A >= 256) {   // the state as three bf16 planes
-        g.X = ws.S3[sc];
-        g.xtype = WT_BF16;
-        g.ldx = 3 * s;
-        g.Kd = 3 * s;
-        g.kw = s;
-      }
       g.add_n = r;
       g.bias_n0 = r;
+      if (ws.S3[sc]) {   // the state as three bf16 planes, if a tiled product takes it
+        GemmArgs g3 = g;
+        g3.X = ws.S3[sc];
+        g3.xtype = WT_BF16;
+        g3.ldx = 3 * s;
+        g3.Kd = 3 * s;
+        g3.kw = s;
+        if (gemm_tiled_ok(g3)) g = g3;
+      }
       HIPCHK(ctx, launch_gemm(g, st));
       HIPCHK(ctx, launch_corr_logits(batch, A, M, r, D, dd, w.W2, wt, ws.C, ws.Cl, ws.uh, ldu,
                                      ws.ell, st));

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(GTT_THREADS) void k_gemm_tiled(GemmArgs a) {
   }
 }
 
-static bool tiled_ok(const GemmArgs &a) {
+bool gemm_tiled_ok(const GemmArgs &a) {
   const int kw = a.kw ? a.kw : a.Kd;
   auto al16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   const int tiles = ((a.R + GTT_B - 1) / GTT_B) * ((a.N + GTT_B - 1) / GTT_B);
@@ -357,7 +357,7 @@ void gemm_set_lds_max(size_t b) { g_lds_max = b; }
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.R <= 0 || a.N <= 0) return hipSuccess;
-  if (tiled_ok(a)) {
+  if (gemm_tiled_ok(a)) {
     const int total = ((a.R + GTT_B - 1) / GTT_B) * ((a.N + GTT_B - 1) / GTT_B);
     hipLaunchKernelGGL(k_gemm_tiled, dim3(total), dim3(GTT_THREADS), GTT_SMEM, st, a);
     return hipGetLastError();

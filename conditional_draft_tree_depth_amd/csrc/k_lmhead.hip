@@ -667,11 +667,14 @@ __global__ __launch_bounds__(256) void k1_stage_hidden(const float *__restrict__
 // (128 rows: 128 flop per weight byte, 512 rows: 512), so every workgroup
 // takes a 128-row x 128-token tile and a W_lm tile is read once for all the
 // rows of the tile instead of once per 16-row block.  Operands are staged in
-// LDS, 64-wide k chunks, double-buffered, with the 16-byte chunk c of row q
-// stored at c ^ (q & 7) so that the fragment reads of 16 rows hit distinct
-// banks; each of the 4 waves computes a 64 x 64 quarter (4 x 4 MFMA tiles).
-constexpr int LT_BM = 128, LT_BN = 128, LT_BK = 64, LT_THREADS = 256;
-constexpr int LT_STAGES = 4;                          // LDS ring: 3 k chunks in flight
+// an LDS ring of 64-wide k chunks, with the 16-byte chunk c of row q stored
+// at c ^ (q & 7) so that the fragment reads of 16 rows hit distinct banks;
+// each of the 8 waves computes a 64 x 64 part (4 x 4 MFMA tiles) of the
+// 128 x 256 tile.
+constexpr int LT_BM = 128, LT_BN = 256, LT_BK = 64, LT_THREADS = 512;
+constexpr int LT_WAVES = LT_THREADS / 64;
+constexpr int LT_STAGES = 3;                          // LDS ring: 2 k chunks in flight
+constexpr int LT_NI = (LT_BM + LT_BN) * 8 / 64 / LT_WAVES;   // copies per wave per stage
 constexpr int LT_STAGE_CHUNKS = (LT_BM + LT_BN) * 8;  // 16-byte chunks per stage
 constexpr size_t LT_SMEM = (size_t)LT_STAGES * LT_STAGE_CHUNKS * 16;
 
@@ -689,15 +692,15 @@ __global__ __launch_bounds__(LT_THREADS) void k1_logits_tiled(
   if (total % 8 == 0) task = (task & 7) * (total / 8) + (task >> 3);
   const int m0 = (task % ntm) * LT_BM, n0 = (task / ntm) * LT_BN;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
-  // A stage holds 16 copy instructions of hidden rows, then 16 of W_lm rows,
+  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;   // wn: 0, 64, 128, 192
+  // A stage holds 16 copy instructions of hidden rows, then 32 of W_lm rows,
   // each 64 lanes x 16 bytes straight from global memory into LDS; slot s
   // (row s >> 3, position s & 7) receives chunk (s & 7) ^ (row & 7) of its
-  // row.  Wave w issues instructions w, w + 4, ..., w + 28.
-  const uint4 *src[8];
+  // row.  Wave w issues instructions w, w + 8, ..., w + 40.
+  const uint4 *src[LT_NI];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = wave + 4 * i, sl = (j & 15) * 64 + lane, row = sl >> 3;
+  for (int i = 0; i < LT_NI; ++i) {
+    const int j = wave + LT_WAVES * i, sl = (j >= 16 ? j - 16 : j) * 64 + lane, row = sl >> 3;
     const int ch = (sl & 7) ^ (row & 7);
     const uint16_t *base = j >= 16 ? W + (size_t)min(n0 + row, V - 1) * d
                                    : Hb + (size_t)min(m0 + row, rows_pad - 1) * d;
@@ -707,9 +710,9 @@ __global__ __launch_bounds__(LT_THREADS) void k1_logits_tiled(
   auto issue = [&](int kc) {
     uint4 *dst = ring + (kc % LT_STAGES) * LT_STAGE_CHUNKS;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < LT_NI; ++i)
       __builtin_amdgcn_global_load_lds(src[i] + kc * 8,
-                                       (__attribute__((address_space(3))) void *)(dst + (wave + 4 * i) * 64),
+                                       (__attribute__((address_space(3))) void *)(dst + (wave + LT_WAVES * i) * 64),
                                        16, 0, 0);
   };
   f32x4 acc[4][4];
@@ -722,10 +725,9 @@ __global__ __launch_bounds__(LT_THREADS) void k1_logits_tiled(
     // this wave's copies of chunk kc have landed (the later ones may still
     // be in flight); the barrier makes every wave's copies visible and
     // retires every read of the buffer refilled next
-    const int ahead = min(LT_STAGES - 2, nk - 1 - kc);
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+    static_assert(LT_STAGES == 3 && LT_NI == 6, "copy counts below");
+    if (kc + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): chunk kc + 1 may fly
+    else __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
     __syncthreads();
     if (kc + LT_STAGES - 1 < nk) issue(kc + LT_STAGES - 1);
     const uint4 *As = ring + (kc % LT_STAGES) * LT_STAGE_CHUNKS, *Bs = As + LT_BM * 8;

@@ -119,6 +119,8 @@ hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh, in
                               const float *b_hh, const float *Sprev,
                               const int32_t *pidx, float *Snew, uint16_t *S3, hipStream_t st);
 hipError_t gemm_prepare();
+// true when launch_gemm runs a as a tiled product (many rows, bf16 operands)
+bool gemm_tiled_ok(const GemmArgs &a);
 // Wcat = [W1[:, d:] ; W_hh] as [r + 3s, s] rows in the weight dtype
 hipError_t launch_concat_state_weights(const void *W1, const void *W_hh, int r, int s, int d,
                                        int wtype, void *Wcat, hipStream_t st);
