@@ -70,6 +70,7 @@ struct dtree_ctx {
   // persistent depth loop: available for this context, and the arrival
   // epoch of the next round (flags only ever grow, so they need no reset)
   bool pk = false;
+  bool sel_corr = false;   // correction logits computed inside the selection kernel
   int pk_rows = 0;
   // persistent depth loop: plain launches until one of its waits runs out
   // (it then stores 1 to *pk_fail, host memory the kernel writes through
@@ -274,6 +275,12 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   if (pe == hipSuccess) pe = topb_prepare(tb_smem);
   if (pe == hipSuccess) pe = skinny_prepare(ctx->lds_max);
   if (pe == hipSuccess) pe = gemm_prepare();
+  // correction logits inside the selection kernel: bf16 W2 rows of 16-byte
+  // pieces whose slice (and one u row per wave) fits in LDS
+  ctx->sel_corr = w->wtype == DTREE_BF16 && r % 8 == 0 && r <= 512 &&
+                  reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
+                  select_corr_smem(c.max_M, r) + 24576 <= ctx->lds_max;
+  if (pe == hipSuccess && ctx->sel_corr) pe = select_corr_prepare(select_corr_smem(c.max_M, r));
   if (pe == hipSuccess && ctx->pk) pe = persist_prepare(s);
   gemm_set_lds_max(ctx->lds_max);
   if (pe != hipSuccess) {
@@ -418,9 +425,16 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
         if (gemm_tiled_ok(g3)) g = g3;
       }
       HIPCHK(ctx, launch_gemm(g, st));
-      HIPCHK(ctx, launch_corr_logits(batch, A, M, r, D, dd, w.W2, wt, ws.C, ws.Cl, ws.uh, ldu,
-                                     ws.ell, st));
-      HIPCHK(ctx, launch_select(batch, A, M, K, W, D, dd, off, ws.C, ws.ell, tb, st));
+      // (with many branches x candidates per request the separate correction
+      // kernel spreads that work over more workgroups)
+      if (ctx->sel_corr && A * M <= 2048) {
+        HIPCHK(ctx, launch_select_corr(batch, A, M, K, W, D, dd, off, r, w.W2, ws.C, ws.Cl, ws.uh,
+                                       ldu, tb, st));
+      } else {
+        HIPCHK(ctx, launch_corr_logits(batch, A, M, r, D, dd, w.W2, wt, ws.C, ws.Cl, ws.uh, ldu,
+                                       ws.ell, st));
+        HIPCHK(ctx, launch_select(batch, A, M, K, W, D, dd, off, ws.C, ws.ell, tb, st));
+      }
       const int An = A * K < W ? A * K : W;
       if (dd + 1 < D) {
         g = GemmArgs{batch * An, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,

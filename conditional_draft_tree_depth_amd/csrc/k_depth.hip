@@ -230,6 +230,179 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
   }
 }
 
+// The same selection with the corrected logits computed in place (bf16 W2,
+// r a multiple of 8): the r x M slice of W2 for the depth's candidates is
+// staged in LDS once per request, and the wave of each expanded branch
+// forms ell[j] = Cl[j] + W2[C[j]] . u_a for its M candidates (in the order
+// of k_corr_logits) before the log-softmax, so the logits never leave the
+// workgroup.
+__global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K, int W, int D,
+                                                             int delta, int off, int r,
+                                                             const uint16_t *__restrict__ W2,
+                                                             const int32_t *__restrict__ C,
+                                                             const float *__restrict__ Cl,
+                                                             const float *__restrict__ u, int ldu,
+                                                             TreeBufs t) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ uint64_t ckey[SEL_MAXZ];
+  __shared__ uint32_t clex[SEL_MAXZ];
+  __shared__ uint32_t slex[SEL_MAXW];
+  __shared__ int32_t pnode[SEL_MAXW];
+  __shared__ uint32_t prank[SEL_MAXW];
+  __shared__ float pscore[SEL_MAXW];
+  __shared__ int32_t ctok[128];
+  __shared__ float clv[128];
+  const int rs = r + 8;
+  uint16_t *W2s = reinterpret_cast<uint16_t *>(smem);                    // [M][r + 8]
+  float *ubuf = reinterpret_cast<float *>(smem + (((size_t)M * rs * 2 + 15) & ~(size_t)15));
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  const int32_t *cq = C + ((size_t)q * D + delta) * M;
+  const size_t nb = (size_t)q * t.NT;
+  const int Z = A * K;
+  const int An = Z < W ? Z : W;
+
+  for (int a = tid; a < A; a += blockDim.x) {
+    const int p = t.surv_node[(size_t)q * t.Wmax + a];
+    pnode[a] = p;
+    prank[a] = (uint32_t)t.surv_rank[(size_t)q * t.Wmax + a];
+    pscore[a] = t.n_score[nb + p];
+  }
+  for (int j = tid; j < M; j += blockDim.x) {
+    ctok[j] = cq[j];
+    clv[j] = Cl[((size_t)q * D + delta) * M + j];
+  }
+  const int r8 = r >> 3;
+  for (int i = tid; i < M * r8; i += blockDim.x) {
+    const int j = i / r8, c8 = i - j * r8;
+    const int tk = cq[j] < 0 ? 0 : cq[j];   // an empty slot never reaches here
+    *reinterpret_cast<uint4 *>(W2s + j * rs + 8 * c8) =
+        *reinterpret_cast<const uint4 *>(W2 + (size_t)tk * r + 8 * c8);
+  }
+  __syncthreads();
+  const bool h0 = lane < M, h1 = lane + 64 < M;
+  float *ub = ubuf + wave * r;
+  // u row of the wave's next branch, in registers (r <= 512), loaded while
+  // the current branch is processed
+  float un[8];
+  auto load_u = [&](int a) {
+    const float *ua = u + ((size_t)q * A + a) * ldu;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (lane + 64 * i < r) un[i] = ua[lane + 64 * i];
+  };
+  if (wave < A) load_u(wave);
+  for (int a = wave; a < A; a += nw) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (lane + 64 * i < r) ub[lane + 64 * i] = un[i];
+    if (a + nw < A) load_u(a + nw);
+    // LDS accesses of one wave take effect in issue order
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float acc0 = 0.f, acc1 = 0.f;
+    const uint16_t *w0 = W2s + (h0 ? lane : 0) * rs, *w1 = W2s + (h1 ? lane + 64 : 0) * rs;
+    for (int c8 = 0; c8 < r; c8 += 8) {
+      const float4 u0 = *reinterpret_cast<const float4 *>(ub + c8);
+      const float4 u1 = *reinterpret_cast<const float4 *>(ub + c8 + 4);
+      const uint4 wa = *reinterpret_cast<const uint4 *>(w0 + c8);
+      acc0 += __uint_as_float(wa.x << 16) * u0.x;
+      acc0 += __uint_as_float(wa.x & 0xFFFF0000u) * u0.y;
+      acc0 += __uint_as_float(wa.y << 16) * u0.z;
+      acc0 += __uint_as_float(wa.y & 0xFFFF0000u) * u0.w;
+      acc0 += __uint_as_float(wa.z << 16) * u1.x;
+      acc0 += __uint_as_float(wa.z & 0xFFFF0000u) * u1.y;
+      acc0 += __uint_as_float(wa.w << 16) * u1.z;
+      acc0 += __uint_as_float(wa.w & 0xFFFF0000u) * u1.w;
+      if (h1) {
+        const uint4 wb = *reinterpret_cast<const uint4 *>(w1 + c8);
+        acc1 += __uint_as_float(wb.x << 16) * u0.x;
+        acc1 += __uint_as_float(wb.x & 0xFFFF0000u) * u0.y;
+        acc1 += __uint_as_float(wb.y << 16) * u0.z;
+        acc1 += __uint_as_float(wb.y & 0xFFFF0000u) * u0.w;
+        acc1 += __uint_as_float(wb.z << 16) * u1.x;
+        acc1 += __uint_as_float(wb.z & 0xFFFF0000u) * u1.y;
+        acc1 += __uint_as_float(wb.w << 16) * u1.z;
+        acc1 += __uint_as_float(wb.w & 0xFFFF0000u) * u1.w;
+      }
+    }
+    const float l0 = h0 ? clv[lane] + acc0 : -INFINITY;
+    const float l1 = h1 ? clv[lane + 64] + acc1 : -INFINITY;
+    // every lane's reads of ub are done before the next branch refills it
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const int p = pnode[a];
+    const uint32_t pr = prank[a];
+    const float ps = pscore[a];
+    const float m = wave_max_f32(fmaxf(l0, l1));
+    const float e = (h0 ? expf(l0 - m) : 0.f) + (h1 ? expf(l1 - m) : 0.f);
+    const float lse = m + logf(wave_sum_f32(e));
+    uint64_t k0 = h0 ? make_key(l0 - lse, (uint32_t)ctok[lane]) : 0ull;
+    uint64_t k1 = h1 ? make_key(l1 - lse, (uint32_t)ctok[lane + 64]) : 0ull;
+    for (int k = 0; k < K; ++k) {
+      const uint64_t top = group_max_u64<64>(k0 > k1 ? k0 : k1);
+      if (k0 == top) k0 = 0ull;
+      if (k1 == top) k1 = 0ull;
+      if (lane == 0) {
+        const uint32_t tok = key_tie(top);
+        const float lp = key_val(top);
+        const float sc = __fadd_rn(ps, lp);
+        const uint32_t lex = (pr << 18) | tok;
+        const int c = a * K + k;
+        const size_t id = nb + off + c;
+        t.n_tok[id] = (int32_t)tok;
+        t.n_par[id] = p;
+        t.n_dep[id] = delta + 1;
+        t.n_score[id] = sc;
+        t.n_lex[id] = lex;
+        ckey[c] = make_key(sc, lex);
+        clex[c] = lex;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Top-W by rank: keys are distinct (distinct token paths)
+  for (int c = tid; c < Z; c += blockDim.x) {
+    const uint64_t kc = ckey[c];
+    int rank = 0;
+    for (int c2 = 0; c2 < Z; ++c2) rank += ckey[c2] > kc;
+    if (rank < An) {
+      const size_t sl = (size_t)q * t.Wmax + rank;
+      t.nsurv_node[sl] = off + c;
+      slex[rank] = clex[c];
+      t.gidx_tok[(size_t)q * An + rank] = (int32_t)(clex[c] & 0x3FFFFu);
+      t.gidx_par[(size_t)q * An + rank] = q * A + c / K;
+      t.surv_hist[((size_t)q * (D + 1) + delta + 1) * t.Wmax + rank] = off + c;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < An; i += blockDim.x) {
+    const uint32_t li = slex[i];
+    int rank = 0;
+    for (int j = 0; j < An; ++j) rank += slex[j] < li;
+    t.nsurv_rank[(size_t)q * t.Wmax + i] = rank;
+  }
+}
+
+size_t select_corr_smem(int M, int r) {
+  return (((size_t)M * (r + 8) * 2 + 15) & ~(size_t)15) + (size_t)(SEL_THREADS / 64) * r * 4;
+}
+
+hipError_t select_corr_prepare(size_t smem) {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_select_corr),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+}
+
+hipError_t launch_select_corr(int b, int A, int M, int K, int W, int D, int delta, int off, int r,
+                              const void *W2, const int32_t *C, const float *Cl, const float *u,
+                              int ldu, const TreeBufs &t, hipStream_t st) {
+  hipLaunchKernelGGL(k_select_corr, dim3(b), dim3(SEL_THREADS), select_corr_smem(M, r), st, A, M,
+                     K, W, D, delta, off, r, static_cast<const uint16_t *>(W2), C, Cl, u, ldu, t);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(int b, int A, int M, int K, int W, int D, int delta, int off,
                          const int32_t *C, const float *ell, const TreeBufs &t,
                          hipStream_t st) {
