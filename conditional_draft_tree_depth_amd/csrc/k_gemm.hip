@@ -137,10 +137,9 @@ __device__ __forceinline__ void sk_split(const float4 &x0, const float4 &x1, uin
                       sk_pack(h[q][4], h[q][5]), sk_pack(h[q][6], h[q][7]));
 }
 
-template <int TERMS, typename XT>
+template <int TERMS, typename XT, int KSW>
 __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int RB) {
   constexpr bool XB = sizeof(XT) == 2;
-  constexpr int KSW = XB ? SK_KSW_B : SK_KSW_F;
   __shared__ __align__(16) float red[SK_WAVES * SK_RB * 256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16, r0 = blockIdx.y * (16 * RB);
@@ -371,12 +370,20 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
     const int groups = std::max(1, std::min(nrb, 1024 / ncol));
     const int RB = std::min(SK_RB, (nrb + groups - 1) / groups);
     dim3 grid(ncol, (nrb + RB - 1) / RB);
-    if (a.xtype == WT_BF16)
-      hipLaunchKernelGGL((k_skinny_bf16<1, uint16_t>), grid, dim3(SK_WAVES * 64), 0, st, a, RB);
-    else if (terms == 1)
-      hipLaunchKernelGGL((k_skinny_bf16<1, float>), grid, dim3(SK_WAVES * 64), 0, st, a, RB);
-    else
-      hipLaunchKernelGGL((k_skinny_bf16<3, float>), grid, dim3(SK_WAVES * 64), 0, st, a, RB);
+    // register arrays sized to the contraction: short ones leave room for a
+    // second workgroup per CU
+    const bool shortk = a.Kd <= 32 * SK_WAVES * (a.xtype == WT_BF16 ? 8 : 4);
+    const dim3 blk(SK_WAVES * 64);
+    if (a.xtype == WT_BF16) {
+      if (shortk) hipLaunchKernelGGL((k_skinny_bf16<1, uint16_t, 8>), grid, blk, 0, st, a, RB);
+      else hipLaunchKernelGGL((k_skinny_bf16<1, uint16_t, SK_KSW_B>), grid, blk, 0, st, a, RB);
+    } else if (terms == 1) {
+      if (shortk) hipLaunchKernelGGL((k_skinny_bf16<1, float, 4>), grid, blk, 0, st, a, RB);
+      else hipLaunchKernelGGL((k_skinny_bf16<1, float, SK_KSW_F>), grid, blk, 0, st, a, RB);
+    } else {
+      if (shortk) hipLaunchKernelGGL((k_skinny_bf16<3, float, 4>), grid, blk, 0, st, a, RB);
+      else hipLaunchKernelGGL((k_skinny_bf16<3, float, SK_KSW_F>), grid, blk, 0, st, a, RB);
+    }
     return hipGetLastError();
   }
   dim3 grid((a.N + GT - 1) / GT, (a.R + GT - 1) / GT);
