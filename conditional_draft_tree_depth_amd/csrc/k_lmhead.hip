@@ -766,10 +766,14 @@ __global__ __launch_bounds__(LT_THREADS) void k1_logits_tiled(
 }
 
 // Exact candidate list for M > 64 (logits in LDS, one row per half-wave):
-// the M-th largest key K of the slice is found by bisection over the 64
-// key bits (keys are distinct, so count(keys >= T) >= M holds exactly for
+// the M-th largest key K of the slice is found by bisection, first over the
+// 32 bits of the ordered value (the M-th largest value v), then, where more
+// than M keys reach v, over the 32-bit tie field among the keys whose value
+// is v (keys are distinct, so count(keys >= T) >= M holds exactly for
 // T <= K; each step is one comparison per held key and a half-wave sum);
-// the keys >= K, exactly M of them, are written unsorted with K as the
+// where exactly M keys reach v, K is the one of value v with the smallest
+// tie field.
+// The keys >= K, exactly M of them, are written unsorted with K as the
 // list's bound, the best key and the count (the layout of the fast path).
 // A slice with fewer than M keys writes all of them with a zero bound.
 template <int MAXC>
@@ -788,36 +792,61 @@ __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int
     y = __builtin_amdgcn_ds_swizzle(tot, 0x201F); if (hl & 8) incl += y; tot += y;
     y = __builtin_amdgcn_ds_swizzle(tot, 0x401F); if (hl & 16) incl += y; tot += y;
   };
+  auto total = [&](int c) { int incl, tot; scan(c, incl, tot); return tot; };
   for (int rb = wave * 2; rb < nrow; rb += 2 * nw) {
     const int r = rb + (lane >> 5);
     const bool active = r < nrow;
-    uint64_t keys[KPL];
+    uint32_t hv[KPL];   // ordered values, 0 = empty column
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
       const int c = hl + 32 * i;
-      keys[i] = (active && c < ncols)
-                    ? ((uint64_t)f32_ord(Ls[r * lstride + c]) << 32) |
-                          (uint64_t)(0xFFFFFFFFu - (uint32_t)(col0 + c))
-                    : 0ull;
+      hv[i] = (active && c < ncols) ? f32_ord(Ls[r * lstride + c]) : 0u;
     }
-    uint64_t T = 0;
+    auto tie_of = [&](int i) { return 0xFFFFFFFFu - (uint32_t)(col0 + hl + 32 * i); };
+    uint64_t T = 0;   // the M-th largest key (0: fewer than M keys)
     if (ncols > M) {
-      for (int bit = 63; bit >= 0; --bit) {
-        const uint64_t cand = T | (1ull << bit);
+      uint32_t tv = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = tv | (1u << bit);
         int c = 0;
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) c += keys[i] >= cand ? 1 : 0;
-        int incl, tot;
-        scan(c, incl, tot);
-        if (tot >= M) T = cand;
+        for (int i = 0; i < KPL; ++i) c += hv[i] >= cand ? 1 : 0;
+        if (total(c) >= M) tv = cand;
       }
+      int cgt = 0, cge = 0;
+      uint64_t ntie = 0;   // largest complemented tie among the keys of value tv
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        cgt += hv[i] > tv ? 1 : 0;
+        cge += hv[i] >= tv ? 1 : 0;
+        if (hv[i] == tv) ntie = max(ntie, (uint64_t)(0xFFFFFFFFu - tie_of(i)));
+      }
+      const int need = M - total(cgt);   // keys of value tv that belong in the list
+      const int nge = total(cge);
+      uint32_t tt;
+      if (__all(!active || nge == M)) {
+        // (every row of the wave) all keys of value tv belong: K has the smallest tie
+        tt = 0xFFFFFFFFu - (uint32_t)group_max_u64<32>(ntie);
+      } else {
+        tt = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = tt | (1u << bit);
+          int c = 0;
+#pragma unroll
+          for (int i = 0; i < KPL; ++i) c += (hv[i] == tv && tie_of(i) >= cand) ? 1 : 0;
+          if (total(c) >= need) tt = cand;
+        }
+      }
+      T = ((uint64_t)tv << 32) | tt;
     }
     const uint64_t lo = T ? T : 1ull;   // key 0 marks an empty column
     int c = 0;
     uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i)
-      if (keys[i] >= lo) { ++c; best = keys[i] > best ? keys[i] : best; }
+    for (int i = 0; i < KPL; ++i) {
+      const uint64_t k = hv[i] ? ((uint64_t)hv[i] << 32) | tie_of(i) : 0ull;
+      if (k >= lo) { ++c; best = k > best ? k : best; }
+    }
     int incl, tot;
     scan(c, incl, tot);
     const uint64_t head = group_max_u64<32>(best);
@@ -825,8 +854,10 @@ __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int
       uint64_t *outr = out + (size_t)r * rstride;
       int pos = incl - c;
 #pragma unroll
-      for (int i = 0; i < KPL; ++i)
-        if (keys[i] >= lo) outr[pos++] = keys[i];
+      for (int i = 0; i < KPL; ++i) {
+        const uint64_t k = hv[i] ? ((uint64_t)hv[i] << 32) | tie_of(i) : 0ull;
+        if (k >= lo) outr[pos++] = k;
+      }
       if (hl == 0) {
         outr[K1_LCAP] = T;
         outr[K1_LCAP + 1] = head;
