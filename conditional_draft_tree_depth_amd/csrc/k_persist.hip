@@ -618,21 +618,24 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
         for (int ps = 0; ps < 3; ++ps) fc[ps] = fn[ps];
       }
     }
-    if (tid < E) {
-      float v = 0.f;   // consumer groups in a fixed order
-      pk_scan<float>(PK_WAVES, [&](int q) { return stage[q * PK_MAXELL + tid]; },
-                     [&](float x) { v += x; });
-      ell[tid] = gval + v;
-    }
-    __syncthreads();
     // ---- selection, one thread per (branch, candidate): log-softmax over M.
     // When M is a power of two a branch's M candidates are M aligned lanes of
     // one wave: max and sum are lane butterflies (every lane of a group gets
-    // the same bits) and the group needs no workgroup barrier.
+    // the same bits), each thread keeps its own logit in a register and the
+    // group needs no workgroup barrier.
     const bool act = tid < E;
     const bool lanes = (M & (M - 1)) == 0;
+    float ev = 0.f;
+    if (act) {
+      float v = 0.f;   // consumer groups in a fixed order
+      pk_scan<float>(PK_WAVES, [&](int q) { return stage[q * PK_MAXELL + tid]; },
+                     [&](float x) { v += x; });
+      ev = gval + v;
+      if (!lanes) ell[tid] = ev;
+    }
+    if (!lanes) __syncthreads();
     const int row = row0, jj = jj0;
-    const float lval = act ? ell[tid] : 0.f;
+    const float lval = ev;
     float mx = -INFINITY, sum = 0.f;
     if (lanes) {
       mx = pk_group_reduce(lval, M, [](float a, float b2) { return fmaxf(a, b2); });
