@@ -279,7 +279,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   // pieces whose slice (and one u row per wave) fits in LDS
   ctx->sel_corr = w->wtype == DTREE_BF16 && r % 8 == 0 && r <= 512 &&
                   reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
-                  select_corr_smem(c.max_M, r) + 24576 <= ctx->lds_max;
+                  select_corr_smem(c.max_M, r) + 40960 <= ctx->lds_max;
   if (pe == hipSuccess && ctx->sel_corr) pe = select_corr_prepare(select_corr_smem(c.max_M, r));
   if (pe == hipSuccess && ctx->pk) pe = persist_prepare(s);
   gemm_set_lds_max(ctx->lds_max);

@@ -119,13 +119,39 @@ hipError_t launch_corr_logits(int b, int A, int M, int r, int D, int delta, cons
   return hipGetLastError();
 }
 
+// Ranks of one branch's candidates, held by one wave (lane l: candidate l
+// in k0, candidate l + 64 in k1; keys are distinct): the keys go through
+// the wave's LDS row wk and every lane counts the larger ones.
+__device__ __forceinline__ void branch_ranks(uint64_t k0, uint64_t k1, bool h0, bool h1, int M,
+                                             uint64_t *wk, int lane, int &r0, int &r1) {
+  if (h0) wk[lane] = k0;
+  if (h1) wk[lane + 64] = k1;
+  // LDS accesses of one wave take effect in issue order
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  r0 = 0;
+  r1 = 0;
+  int j = 0;
+  for (; j + 8 <= M; j += 8) {
+    uint64_t v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = wk[j + t];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) { r0 += v[t] > k0; r1 += v[t] > k1; }
+  }
+  for (; j < M; ++j) { const uint64_t v = wk[j]; r0 += v > k0; r1 += v > k1; }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Selection of one depth for one request (one workgroup each):
 //  0. the expanded branches' node ids, lexicographic ranks and scores are
 //     gathered into LDS once (two dependent loads for all branches at once);
 //  1. per expanded branch (one wave each; the next branch's logits are
 //     loaded while the current one is processed): log-softmax over the M
-//     corrected logits, Top-K children (log-prob desc, token asc), child
-//     score = parent score + log-prob; every child is appended to the
+//     corrected logits, Top-K children (log-prob desc, token asc) by rank
+//     counting, child score = parent score + log-prob; every child is
+//     appended to the
 //     superarbol ("Resumen Técnico: DominoTree", Main components 2; DARTree
 //     page, Methodology 1, scoring by corrected cumulative probability);
 //  2. Top-W of the depth's children by (score desc, token path asc) become
@@ -144,6 +170,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
   __shared__ uint32_t prank[SEL_MAXW];
   __shared__ float pscore[SEL_MAXW];
   __shared__ int32_t ctok[128];
+  __shared__ uint64_t wkeys[(SEL_THREADS / 64) * 128];   // one row of keys per wave
   const int q = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int nw = blockDim.x >> 6;
@@ -180,18 +207,21 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
     const float m = wave_max_f32(fmaxf(l0, l1));
     const float e = (h0 ? expf(l0 - m) : 0.f) + (h1 ? expf(l1 - m) : 0.f);
     const float lse = m + logf(wave_sum_f32(e));
-    uint64_t k0 = h0 ? make_key(l0 - lse, (uint32_t)ctok[lane]) : 0ull;
-    uint64_t k1 = h1 ? make_key(l1 - lse, (uint32_t)ctok[lane + 64]) : 0ull;
-    for (int k = 0; k < K; ++k) {
-      const uint64_t top = group_max_u64<64>(k0 > k1 ? k0 : k1);
-      if (k0 == top) k0 = 0ull;
-      if (k1 == top) k1 = 0ull;
-      if (lane == 0) {
-        const uint32_t tok = key_tie(top);
-        const float lp = key_val(top);
+    const uint64_t k0 = h0 ? make_key(l0 - lse, (uint32_t)ctok[lane]) : 0ull;
+    const uint64_t k1 = h1 ? make_key(l1 - lse, (uint32_t)ctok[lane + 64]) : 0ull;
+    // Top-K by rank; each selected candidate's lane writes its child
+    int r0, r1;
+    branch_ranks(k0, k1, h0, h1, M, wkeys + wave * 128, lane, r0, r1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t kk = h ? k1 : k0;
+      const int rk = h ? r1 : r0;
+      if ((h ? h1 : h0) && rk < K) {
+        const uint32_t tok = key_tie(kk);
+        const float lp = key_val(kk);
         const float sc = __fadd_rn(ps, lp);
         const uint32_t lex = (pr << 18) | tok;
-        const int c = a * K + k;
+        const int c = a * K + rk;
         const size_t id = nb + off + c;
         t.n_tok[id] = (int32_t)tok;
         t.n_par[id] = p;
@@ -252,6 +282,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K
   __shared__ float pscore[SEL_MAXW];
   __shared__ int32_t ctok[128];
   __shared__ float clv[128];
+  __shared__ uint64_t wkeys[(SEL_THREADS / 64) * 128];   // one row of keys per wave
   const int rs = r + 8;
   uint16_t *W2s = reinterpret_cast<uint16_t *>(smem);                    // [M][r + 8]
   float *ubuf = reinterpret_cast<float *>(smem + (((size_t)M * rs * 2 + 15) & ~(size_t)15));
@@ -338,18 +369,21 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K
     const float m = wave_max_f32(fmaxf(l0, l1));
     const float e = (h0 ? expf(l0 - m) : 0.f) + (h1 ? expf(l1 - m) : 0.f);
     const float lse = m + logf(wave_sum_f32(e));
-    uint64_t k0 = h0 ? make_key(l0 - lse, (uint32_t)ctok[lane]) : 0ull;
-    uint64_t k1 = h1 ? make_key(l1 - lse, (uint32_t)ctok[lane + 64]) : 0ull;
-    for (int k = 0; k < K; ++k) {
-      const uint64_t top = group_max_u64<64>(k0 > k1 ? k0 : k1);
-      if (k0 == top) k0 = 0ull;
-      if (k1 == top) k1 = 0ull;
-      if (lane == 0) {
-        const uint32_t tok = key_tie(top);
-        const float lp = key_val(top);
+    const uint64_t k0 = h0 ? make_key(l0 - lse, (uint32_t)ctok[lane]) : 0ull;
+    const uint64_t k1 = h1 ? make_key(l1 - lse, (uint32_t)ctok[lane + 64]) : 0ull;
+    // Top-K by rank; each selected candidate's lane writes its child
+    int r0, r1;
+    branch_ranks(k0, k1, h0, h1, M, wkeys + wave * 128, lane, r0, r1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t kk = h ? k1 : k0;
+      const int rk = h ? r1 : r0;
+      if ((h ? h1 : h0) && rk < K) {
+        const uint32_t tok = key_tie(kk);
+        const float lp = key_val(kk);
         const float sc = __fadd_rn(ps, lp);
         const uint32_t lex = (pr << 18) | tok;
-        const int c = a * K + k;
+        const int c = a * K + rk;
         const size_t id = nb + off + c;
         t.n_tok[id] = (int32_t)tok;
         t.n_par[id] = p;
