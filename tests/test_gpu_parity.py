@@ -31,7 +31,7 @@ def test_golden_fixture_on_gpu(gpu_lib, name):
     check_invariants(out, p["B"])
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(240))
 def test_tiny_seeds_exact(gpu_lib, seed):
     cfg = synth.CONFIGS["tiny"]
     check_config(synth.make_inputs(cfg, seed), cfg, f"tiny seed {seed}", max_tie_frac=0.0)
