@@ -52,7 +52,7 @@ import numpy as np
 __all__ = [
     "bf16_round", "decode", "OracleWeights", "base_logits", "top_m",
     "gru_cell", "log_softmax", "build_superarbol", "select_global_top_b",
-    "select_literal_heap", "emit_tree", "build_round",
+    "select_literal_heap", "emit_tree", "build_round", "SCORINGS",
 ]
 
 
@@ -181,17 +181,30 @@ def _key(score, depth, beta, store):
     return float(score) + float(beta) * float(depth)
 
 
-def build_superarbol(Hq_req, root_tok, Lb_req, W, D, M, K, Wd, store="f32"):
+SCORINGS = ("conditional", "marginal")
+
+
+def build_superarbol(Hq_req, root_tok, Lb_req, W, D, M, K, Wd, store="f32",
+                     scoring="conditional"):
     """Depth-wise construction of one request's superarbol.
 
     DARTree page, Methodology 1, with the Domino head as the corrected
     drafter (Domino page, Methodology 2) and the Top-M restriction
     (DominoTree page, Main components 2).
 
+    scoring="marginal" scores every branch with the path-independent base
+    logits alone (Delta L = 0, no GRU state): the uncorrected, DDTree-style
+    scoring that the pages compare against with the same drafter and tree
+    construction (DominoTree page, Evaluation, the conditionality ablation;
+    DARTree page, Results, DDTree as the marginal baseline).
+
     Hq_req: [D, d] rounded hidden states; Lb_req: [D, V] base logits.
     Wd is the branch width W (the name W is taken by the weights).
     Returns a dict with the node table and the per-depth intermediates.
     """
+    if scoring not in SCORINGS:
+        raise ValueError(f"scoring must be one of {SCORINGS}")
+    marginal = scoring == "marginal"
     st = _storer(store)
     C = np.empty((D, M), dtype=np.int64)
     Cl = np.empty((D, M), dtype=np.float64)
@@ -203,13 +216,17 @@ def build_superarbol(Hq_req, root_tok, Lb_req, W, D, M, K, Wd, store="f32"):
     tok, par, dep, score, path = [int(root_tok)], [-1], [0], [0.0], [()]
     kids = [[]]
     # the block starts with the last verified token: the GRU consumes it first
-    S = gru_cell(W.emb_rows([root_tok]), np.zeros((1, W.s)), W, store)
+    S = None if marginal else gru_cell(W.emb_rows([root_tok]), np.zeros((1, W.s)), W, store)
     frontier = [0]
     per_depth = []
     for dd in range(D):
         A = len(frontier)
-        u = st(uH[dd][None, :] + S @ W.W1_S.T)                   # [A, r]
-        ell = st(Cl[dd][None, :] + u @ W.w2_rows(C[dd]).T)      # [A, M]
+        if marginal:
+            u = None
+            ell = np.repeat(Cl[dd][None, :], A, axis=0)           # [A, M]
+        else:
+            u = st(uH[dd][None, :] + S @ W.W1_S.T)               # [A, r]
+            ell = st(Cl[dd][None, :] + u @ W.w2_rows(C[dd]).T)  # [A, M]
         lp = log_softmax(ell, store)                             # [A, M]
         children = []
         for a, p in enumerate(frontier):
@@ -229,7 +246,7 @@ def build_superarbol(Hq_req, root_tok, Lb_req, W, D, M, K, Wd, store="f32"):
         surv = sorted(children, key=lambda n: (-score[n], path[n]))[:Wd]
         per_depth.append(dict(frontier=list(frontier), u=u, ell=ell, lp=lp,
                               children=children, survivors=surv))
-        if dd + 1 < D:
+        if dd + 1 < D and not marginal:
             slot = {p: a for a, p in enumerate(frontier)}
             S = gru_cell(W.emb_rows([tok[c] for c in surv]),
                          S[[slot[par[c]] for c in surv]], W, store)
@@ -306,11 +323,13 @@ def emit_tree(sa, sel, B):
                 n_nodes=n_nodes, order=order)
 
 
-def build_round(inputs, D, M, K, W, B, beta, store="f32", check_heap=True):
+def build_round(inputs, D, M, K, W, B, beta, store="f32", check_heap=True,
+                scoring="conditional"):
     """Whole round for every request of ``inputs`` (as drawn by ``synth``).
 
     Returns per-request outputs (tok, parent, depth, score, mask, n_nodes)
-    and the superarbol trace used by the checkers.
+    and the superarbol trace used by the checkers.  ``scoring`` as in
+    ``build_superarbol``.
     """
     wts, wtype = inputs["weights"], inputs["wtype"]
     H = np.asarray(inputs["H"], dtype=np.float32)
@@ -323,7 +342,7 @@ def build_round(inputs, D, M, K, W, B, beta, store="f32", check_heap=True):
     reqs = []
     for q in range(b):
         sa = build_superarbol(Hq[q], int(inputs["root"][q]), Lb[q], Wo,
-                              D, M, K, W, store)
+                              D, M, K, W, store, scoring)
         sel = select_global_top_b(sa, B, beta, store)
         if check_heap:
             pops = select_literal_heap(sa, B, beta, store)

@@ -87,3 +87,22 @@ class Brute:
             S = self.step_state(S, t)
         lp = self.child_logprobs(len(path), S)
         return {t: float(lp[j]) for j, t in enumerate(self.C[len(path)])}, score
+
+    def enumerate_marginal(self):
+        """{path tuple: cumulative score} for every path of length 1..D when
+        every branch is scored by the base logits alone (no correction): the
+        closed form sum over depths of log_softmax(Lb[dd][C[dd]]) at the
+        path's tokens."""
+        lps = [torch.log_softmax(self.Lb[dd][self.C[dd]], dim=0) for dd in range(self.D)]
+        out = {}
+
+        def rec(path, score, dd):
+            if dd == self.D:
+                return
+            for j, t in enumerate(self.C[dd]):
+                p2 = path + (t,)
+                out[p2] = score + float(lps[dd][j])
+                rec(p2, out[p2], dd + 1)
+
+        rec((), 0.0, 0)
+        return out

@@ -311,3 +311,73 @@ def test_golden_fixture(name):
     assert out["depth"][:n].tolist() == exp["depth"]
     assert np.max(np.abs(out["score"][:n] - np.array(exp["score"]))) < g["score_tol"]
     assert out["mask"][:n, :n].tolist() == exp["mask"]
+
+
+# ------------------------------------------------------- marginal scoring
+def _check_marginal(x, cfg):
+    res = _run(x, cfg, store="f64", scoring="marginal")[0]
+    sa = res["sa"]
+    bf = Brute(x, 0, cfg.D, cfg.M)
+    allp = bf.enumerate_marginal()
+    assert [list(c) for c in sa["C"]] == [list(c) for c in bf.C]
+    for n in range(1, len(sa["tok"])):
+        assert abs(sa["score"][n] - allp[sa["path"][n]]) < 1e-10
+    for dd, pdp in enumerate(sa["per_depth"]):
+        lp = torch.log_softmax(bf.Lb[dd][bf.C[dd]], dim=0).tolist()
+        want = [t for _, t in sorted(zip(lp, bf.C[dd]), key=lambda z: (-z[0], z[1]))[:cfg.K]]
+        for p in pdp["frontier"]:
+            assert [sa["tok"][c] for c in sa["kids"][p]] == want
+        ch = pdp["children"]
+        surv = sorted(ch, key=lambda n: (-allp[sa["path"][n]], sa["path"][n]))[:cfg.W]
+        assert set(surv) == set(pdp["survivors"])
+    return res
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_marginal_scoring_tiny(seed):
+    """Marginal (uncorrected) scoring: every node's score is the closed form
+    sum of the per-depth log-softmax of the base logits at its tokens, every
+    branch of a depth gets the same Top-K children, survivors are the Top-W."""
+    cfg = synth.CONFIGS["tiny"]
+    _check_marginal(synth.make_inputs(cfg, seed), cfg)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_marginal_scoring_random_shapes(seed):
+    cfg, x = _rand_tiny(100 + seed, "bf16" if seed % 2 else "f32")
+    _check_marginal(x, cfg)
+
+
+def test_marginal_equals_zero_correction():
+    """Marginal scoring builds the same tree as conditional scoring with a
+    zero correction head (W2 = 0 makes Delta L vanish on every path)."""
+    for seed in range(4):
+        cfg = synth.CONFIGS["tiny"]
+        x = synth.make_inputs(cfg, seed)
+        a = _run(x, cfg, store="f64", scoring="marginal")[0]
+        x["weights"]["W2"] = np.zeros_like(x["weights"]["W2"])
+        b = _run(x, cfg, store="f64")[0]
+        for k in ("tok", "parent", "depth"):
+            assert list(a[k]) == list(b[k])
+        assert np.max(np.abs(np.asarray(a["score"]) - np.asarray(b["score"]))) < 1e-12
+        assert np.array_equal(a["mask"], b["mask"])
+
+
+def test_marginal_unpruned_top_b_over_all_paths():
+    """K = M, W >= M^(D-1) with marginal scoring: the Top-B over all token
+    paths by the closed-form marginal score (DDTree's best-first tree)."""
+    for seed in range(4):
+        cfg = synth.custom_config(cfg_id=4100, d=16, V=40, e=8, s=8, r=4, D=3, M=4, K=4,
+                                  W=16, B=20, beta=-0.2)
+        x = synth.make_inputs(cfg, seed)
+        res = _run(x, cfg, store="f64", scoring="marginal")[0]
+        allp = Brute(x, 0, cfg.D, cfg.M).enumerate_marginal()
+        ranked = sorted(allp, key=lambda p: (-(allp[p] + cfg.beta * len(p)), len(p), p))
+        sa = res["sa"]
+        assert {sa["path"][n] for n in res["sel"]} == set(ranked[:cfg.B])
+
+
+def test_unknown_scoring_rejected():
+    cfg = synth.CONFIGS["tiny"]
+    with pytest.raises(ValueError):
+        _run(synth.make_inputs(cfg, 0), cfg, scoring="markov")
