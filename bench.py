@@ -71,7 +71,7 @@ def counters_traffic(workload, per_launch_div=1):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inputs, budget_s=12.0, max_rounds=50):
+def cpu_baseline(cfg, inputs, budget_s=12.0, max_rounds=50, scoring="conditional"):
     """The CPU oracle as it stands, timed on this host on whole rounds of the
     same workload (at least one, stopping once ~budget_s has been spent)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -84,7 +84,8 @@ def cpu_baseline(cfg, inputs, budget_s=12.0, max_rounds=50):
         pass
     n, t0 = 0, time.perf_counter()
     while True:
-        O.build_round(inputs, cfg.D, cfg.M, cfg.K, cfg.W, cfg.B, cfg.beta, check_heap=False)
+        O.build_round(inputs, cfg.D, cfg.M, cfg.K, cfg.W, cfg.B, cfg.beta, check_heap=False,
+                      scoring=scoring)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= max_rounds:
@@ -119,6 +120,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen3_4b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scoring", default="conditional", choices=["conditional", "marginal"],
+                    help="conditional (the method) or marginal (uncorrected base-logit "
+                         "scoring, the pages' comparison)")
     ap.add_argument("--cold-rounds", type=int, default=0,
                     help="also time this many rounds, each after a 1 GiB device read that "
                          "evicts the caches (cold_latency_us)")
@@ -141,7 +145,7 @@ def main():
     wd, H, root = runner.to_device(inputs)
     caps = (cfg.batch, cfg.D, cfg.M, cfg.K, cfg.W, cfg.B)
     rnd = runner.Round(wd, cfg.wtype, caps, cfg.batch, cfg.D, cfg.M, cfg.K, cfg.W, cfg.B,
-                       cfg.beta)
+                       cfg.beta, scoring=args.scoring)
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
@@ -222,7 +226,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "d": cfg.d, "V": cfg.V, "e": cfg.e, "s": cfg.s,
                    "r": cfg.r, "D": cfg.D, "M": cfg.M, "K": cfg.K, "W": cfg.W, "B": cfg.B,
-                   "beta": cfg.beta, "batch": cfg.batch, "weights": cfg.wtype},
+                   "beta": cfg.beta, "batch": cfg.batch, "weights": cfg.wtype,
+                   "scoring": args.scoring},
         "roofline": {"bound": "hbm",
                      "kernel": "k1_lmhead_bf16 (LM-head GEMM + fused per-slice Top-M)",
                      "achieved": k1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -242,7 +247,7 @@ def main():
     if cold is not None:
         line["cold_latency_us"] = cold
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, inputs)
+        line["cpu_baseline"] = cpu_baseline(cfg, inputs, scoring=args.scoring)
     print(json.dumps(line), flush=True)
 
 

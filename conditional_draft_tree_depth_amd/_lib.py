@@ -16,7 +16,8 @@ STATUS = {0: "DTREE_OK", 1: "DTREE_E_ARG", 2: "DTREE_E_SHAPE", 3: "DTREE_E_DTYPE
           4: "DTREE_E_DEVICE", 5: "DTREE_E_NOMEM", 6: "DTREE_E_HIP", 7: "DTREE_E_STATE"}
 EXPORTS = ("dtree_create", "dtree_build_round", "dtree_superarbol_nodes",
            "dtree_get_trace", "dtree_profile_enable", "dtree_profile_read",
-           "dtree_set_persistent_launch", "dtree_last_error", "dtree_destroy")
+           "dtree_set_persistent_launch", "dtree_set_scoring", "dtree_last_error",
+           "dtree_destroy")
 NSTAGES = 6
 STAGES = ("round_start", "lmhead_topm", "topm_merge", "prologue", "depth_loop", "topb_emit")
 
@@ -83,6 +84,8 @@ def load(path=LIB_PATH):
     lib.dtree_profile_read.restype = c_i32
     lib.dtree_set_persistent_launch.argtypes = [c_vp, c_i32, c_i32]
     lib.dtree_set_persistent_launch.restype = c_i32
+    lib.dtree_set_scoring.argtypes = [c_vp, c_i32]
+    lib.dtree_set_scoring.restype = c_i32
     lib.dtree_last_error.argtypes = [c_vp]
     lib.dtree_last_error.restype = ctypes.c_char_p
     lib.dtree_destroy.argtypes = [c_vp]
@@ -183,3 +186,13 @@ def dtree_destroy(ctx):
 def dtree_set_persistent_launch(ctx, cooperative, spin_limit=0):
     _check("dtree_set_persistent_launch",
            load().dtree_set_persistent_launch(ctx, int(cooperative), int(spin_limit)), ctx)
+
+
+SCORE_CONDITIONAL, SCORE_MARGINAL = 0, 1
+SCORINGS = {"conditional": SCORE_CONDITIONAL, "marginal": SCORE_MARGINAL}
+
+
+def dtree_set_scoring(ctx, scoring):
+    """scoring: "conditional" / "marginal" (or the DTREE_SCORE_* value)."""
+    code = SCORINGS[scoring] if isinstance(scoring, str) else int(scoring)
+    _check("dtree_set_scoring", load().dtree_set_scoring(ctx, code), ctx)

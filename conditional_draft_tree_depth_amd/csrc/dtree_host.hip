@@ -71,6 +71,7 @@ struct dtree_ctx {
   // epoch of the next round (flags only ever grow, so they need no reset)
   bool pk = false;
   bool sel_corr = false;   // correction logits computed inside the selection kernel
+  int scoring = DTREE_SCORE_CONDITIONAL;
   int pk_rows = 0;
   // persistent depth loop: plain launches until one of its waits runs out
   // (it then stores 1 to *pk_fail, host memory the kernel writes through
@@ -378,10 +379,25 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   }
 
 
-  const bool pk = ctx->pk && batch * M <= 64 && batch * D * M <= ctx->pk_rows &&
+  const bool marginal = ctx->scoring == DTREE_SCORE_MARGINAL;
+  const bool pk = !marginal && ctx->pk && batch * M <= 64 && batch * D * M <= ctx->pk_rows &&
                   persist_eligible(batch, D, M, K, W, s, w.e, r, wt, ctx->lds_max);
   int A = 1, off = 1, sc = 0;
-  if (pk) {
+  if (marginal) {
+    // every branch of a depth is scored by the depth's base logits Cl
+    // (no correction, no GRU state): the selection reads the same row of Cl
+    // for all of a request's branches
+    prof_mark(ctx, 4, st);
+    for (int dd = 0; dd < D; ++dd) {
+      HIPCHK(ctx, launch_select(batch, A, M, K, W, D, dd, off, ws.C, ws.Cl + (size_t)dd * M,
+                                (long)D * M, 0, tb, st));
+      cur = 1 - cur;
+      tb.surv_node = ws.surv[cur]; tb.surv_rank = ws.rank[cur];
+      tb.nsurv_node = ws.surv[1 - cur]; tb.nsurv_rank = ws.rank[1 - cur];
+      off += A * K;
+      A = A * K < W ? A * K : W;
+    }
+  } else if (pk) {
     // correction tables G = W2[C] W1[:, d:], g = Cl + W2[C] uH, then the
     // whole depth loop as one cooperative launch
     HIPCHK(ctx, launch_corr_tables(batch * D * M, M, r, s, w.W2, ws.w1t, ws.C, ws.Cl, ws.uH,
@@ -433,7 +449,8 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
       } else {
         HIPCHK(ctx, launch_corr_logits(batch, A, M, r, D, dd, w.W2, wt, ws.C, ws.Cl, ws.uh, ldu,
                                        ws.ell, st));
-        HIPCHK(ctx, launch_select(batch, A, M, K, W, D, dd, off, ws.C, ws.ell, tb, st));
+        HIPCHK(ctx, launch_select(batch, A, M, K, W, D, dd, off, ws.C, ws.ell, (long)A * M, M, tb,
+                                  st));
       }
       const int An = A * K < W ? A * K : W;
       if (dd + 1 < D) {
@@ -547,6 +564,15 @@ extern "C" dtree_status dtree_set_persistent_launch(dtree_ctx *ctx, int32_t coop
   if (spin_limit < 0) return fail(ctx, DTREE_E_ARG, "spin_limit must be >= 0");
   ctx->pk_coop = cooperative == 1;
   ctx->pk_spin = (uint32_t)spin_limit;
+  return DTREE_OK;
+}
+
+extern "C" dtree_status dtree_set_scoring(dtree_ctx *ctx, int32_t scoring) {
+  if (!ctx) return DTREE_E_ARG;
+  ctx->err.clear();
+  if (scoring != DTREE_SCORE_CONDITIONAL && scoring != DTREE_SCORE_MARGINAL)
+    return fail(ctx, DTREE_E_ARG, "scoring must be DTREE_SCORE_CONDITIONAL or DTREE_SCORE_MARGINAL");
+  ctx->scoring = scoring;
   return DTREE_OK;
 }
 

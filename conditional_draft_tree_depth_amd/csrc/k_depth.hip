@@ -161,8 +161,8 @@ __device__ __forceinline__ void branch_ranks(uint64_t k0, uint64_t k1, bool h0, 
 __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int W, int D,
                                                         int delta, int off,
                                                         const int32_t *__restrict__ C,
-                                                        const float *__restrict__ ell,
-                                                        TreeBufs t) {
+                                                        const float *__restrict__ ell, long ldq,
+                                                        int lda, TreeBufs t) {
   __shared__ uint64_t ckey[SEL_MAXZ];
   __shared__ uint32_t clex[SEL_MAXZ];
   __shared__ uint32_t slex[SEL_MAXW];
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
   const bool h0 = lane < M, h1 = lane + 64 < M;
   float l0 = -INFINITY, l1 = -INFINITY;
   if (wave < A) {
-    const float *la = ell + ((size_t)q * A + wave) * M;
+    const float *la = ell + q * ldq + (size_t)wave * lda;
     if (h0) l0 = la[lane];
     if (h1) l1 = la[lane + 64];
   }
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
   for (int a = wave; a < A; a += nw) {
     float n0 = -INFINITY, n1 = -INFINITY;   // the wave's next branch, in flight meanwhile
     if (a + nw < A) {
-      const float *ln = ell + ((size_t)q * A + a + nw) * M;
+      const float *ln = ell + q * ldq + (size_t)(a + nw) * lda;
       if (h0) n0 = ln[lane];
       if (h1) n1 = ln[lane + 64];
     }
@@ -438,10 +438,10 @@ hipError_t launch_select_corr(int b, int A, int M, int K, int W, int D, int delt
 }
 
 hipError_t launch_select(int b, int A, int M, int K, int W, int D, int delta, int off,
-                         const int32_t *C, const float *ell, const TreeBufs &t,
-                         hipStream_t st) {
+                         const int32_t *C, const float *ell, long ldq, int lda,
+                         const TreeBufs &t, hipStream_t st) {
   hipLaunchKernelGGL(k_select, dim3(b), dim3(SEL_THREADS), 0, st, A, M, K, W, D, delta, off, C,
-                     ell, t);
+                     ell, ldq, lda, t);
   return hipGetLastError();
 }
 

@@ -131,8 +131,9 @@ hipError_t launch_corr_logits(int b, int A, int M, int r, int D, int delta,
                               const float *Cl, const float *u, int ldu, float *ell,
                               hipStream_t st);
 size_t corr_logits_smem(int A, int M, int r, int wtype);
+// branch a of request q reads its M logits at ell + q * ldq + a * lda
 hipError_t launch_select(int b, int A, int M, int K, int W, int D, int delta,
-                         int off, const int32_t *C, const float *ell,
+                         int off, const int32_t *C, const float *ell, long ldq, int lda,
                          const TreeBufs &t, hipStream_t st);
 // selection with the correction logits computed in place (bf16 W2, 16-byte
 // aligned, r % 8 == 0; dynamic LDS select_corr_smem(M, r))

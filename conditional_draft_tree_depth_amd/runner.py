@@ -20,11 +20,14 @@ def to_device(inputs, device="cuda"):
 class Round:
     """One context + output buffers for a fixed (batch, params)."""
 
-    def __init__(self, dev_weights, wtype, caps, batch, D, M, K, W, B, beta, device=0):
+    def __init__(self, dev_weights, wtype, caps, batch, D, M, K, W, B, beta, device=0,
+                 scoring="conditional"):
         import torch
         self.p = _lib.params(D, M, K, W, B, beta)
         self.batch = batch
         self.ctx = _lib.dtree_create(dev_weights, wtype, caps, device)
+        if scoring != "conditional":
+            _lib.dtree_set_scoring(self.ctx, scoring)
         self.weights = dev_weights   # keep the borrowed weights alive
         N = B + 1
         dev = f"cuda:{device}"

@@ -163,6 +163,23 @@ dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
 dtree_status dtree_set_persistent_launch(dtree_ctx *ctx, int32_t cooperative,
                                          int32_t spin_limit);
 
+/* How the children of every expanded branch are scored (for the context's
+ * later rounds):
+ *   DTREE_SCORE_CONDITIONAL (0, the default): corrected logits
+ *       L_base + Delta L, Delta L from the low-rank head over [H_i ; S] with
+ *       the branch's own GRU state S ("Resumen Técnico: Domino",
+ *       Methodology 2; DARTree page, Methodology 1);
+ *   DTREE_SCORE_MARGINAL (1): the path-independent base logits alone
+ *       (Delta L = 0, no GRU state), the uncorrected DDTree-style scoring the
+ *       pages compare against with the same drafter and tree construction
+ *       ("Resumen Técnico: DominoTree", Evaluation, the conditionality
+ *       ablation).  Everything else in the round is unchanged: Top-M per
+ *       depth, log-softmax over M, Top-K, Top-W, global Top-B, mask.
+ * DTREE_E_ARG for other values.                                            */
+#define DTREE_SCORE_CONDITIONAL 0
+#define DTREE_SCORE_MARGINAL 1
+dtree_status dtree_set_scoring(dtree_ctx *ctx, int32_t scoring);
+
 /* Number of superarbol nodes (root included) a round with `p` builds per
  * request, or -1 if p is invalid.  Pure host arithmetic.                     */
 int32_t dtree_superarbol_nodes(const dtree_params *p);

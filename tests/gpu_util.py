@@ -16,12 +16,12 @@ def caps_for(cfg, **over):
     return (c["max_batch"], c["max_D"], c["max_M"], c["max_K"], c["max_W"], c["max_B"])
 
 
-def gpu_round(inputs, cfg, caps=None, beta=None, runs=1):
+def gpu_round(inputs, cfg, caps=None, beta=None, runs=1, scoring="conditional"):
     from conditional_draft_tree_depth_amd import runner
     import torch
     wd, H, root = runner.to_device(inputs)
     rnd = runner.Round(wd, cfg.wtype, caps or caps_for(cfg), cfg.batch, cfg.D, cfg.M, cfg.K,
-                       cfg.W, cfg.B, cfg.beta if beta is None else beta)
+                       cfg.W, cfg.B, cfg.beta if beta is None else beta, scoring=scoring)
     try:
         outs = []
         for _ in range(runs):
@@ -34,12 +34,12 @@ def gpu_round(inputs, cfg, caps=None, beta=None, runs=1):
     return outs if runs > 1 else outs[0], traces
 
 
-def check_config(inputs, cfg, label, max_tie_frac=0.0, caps=None):
+def check_config(inputs, cfg, label, max_tie_frac=0.0, caps=None, scoring="conditional"):
     """GPU round vs oracle on every request; returns the tie descriptions."""
     print(f"[gpu] {label}: batch={cfg.batch} D={cfg.D} M={cfg.M} K={cfg.K} W={cfg.W} "
-          f"B={cfg.B} beta={cfg.beta} wtype={cfg.wtype}", flush=True)
-    gouts, gtrs = gpu_round(inputs, cfg, caps)
-    orcs = O.build_round(inputs, cfg.D, cfg.M, cfg.K, cfg.W, cfg.B, cfg.beta)
+          f"B={cfg.B} beta={cfg.beta} wtype={cfg.wtype} scoring={scoring}", flush=True)
+    gouts, gtrs = gpu_round(inputs, cfg, caps, scoring=scoring)
+    orcs = O.build_round(inputs, cfg.D, cfg.M, cfg.K, cfg.W, cfg.B, cfg.beta, scoring=scoring)
     prm = dict(D=cfg.D, M=cfg.M, K=cfg.K, W=cfg.W, B=cfg.B, beta=cfg.beta)
     ties = []
     for q in range(cfg.batch):

@@ -55,6 +55,7 @@ def test_create_rejects_bad_arguments_before_device():
     assert lib.dtree_create(None, ctypes.byref(caps), 0, ctypes.byref(ctx)) == 1
     assert lib.dtree_destroy(None) == 0
     assert lib.dtree_build_round(None, None, 1, *([None] * 9)) == 1
+    assert lib.dtree_set_scoring(None, 0) == 1
 
 
 def test_binding_refuses_missing_library(tmp_path):
