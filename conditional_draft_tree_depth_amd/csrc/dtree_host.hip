@@ -274,7 +274,6 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   hipError_t pe = lmhead_prepare(w->wtype, ctx->k1_ring, ctx->k1_smem);
   if (pe == hipSuccess) pe = corr_logits_prepare(w->wtype, cl_smem);
   if (pe == hipSuccess) pe = topb_prepare(tb_smem);
-  if (pe == hipSuccess) pe = skinny_prepare(ctx->lds_max);
   if (pe == hipSuccess) pe = gemm_prepare();
   // correction logits inside the selection kernel: bf16 W2 rows of 16-byte
   // pieces whose slice (and one u row per wave) fits in LDS
@@ -283,7 +282,6 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
                   select_corr_smem(c.max_M, r) + 40960 <= ctx->lds_max;
   if (pe == hipSuccess && ctx->sel_corr) pe = select_corr_prepare(select_corr_smem(c.max_M, r));
   if (pe == hipSuccess && ctx->pk) pe = persist_prepare(s);
-  gemm_set_lds_max(ctx->lds_max);
   if (pe != hipSuccess) {
     free_ws(ws);
     return reject(DTREE_E_HIP, std::string("kernel attributes: ") + hipGetErrorString(pe));

@@ -1,13 +1,16 @@
-// Row-gathered products with fp32 activations and stored (bf16/fp32) weights,
-// and the GRU cell.
+// Row-gathered products of activations and stored (bf16/fp32) weights, and
+// the GRU cell.
 //
 // Used for the path-independent projection uH = W1[:, :d] Hq, the per-branch
 // part W1[:, d:] S of the low-rank head ("Resumen Técnico: Domino",
 // Methodology 2: [H_i ; S_{i-1}] is projected to rank r), and the GRU input
-// and state projections.  Activations stay fp32 (the GRU state is never
-// rounded to bf16); bf16 weights are widened exactly to fp32; accumulation
-// is fp32.  Tiles: 64 rows x 64 outputs per 256-thread workgroup, 16-wide k
-// chunks staged in LDS.
+// and state projections.  fp32 activations are never rounded to bf16 (the
+// GRU state enters the matrix cores as an exact three-term bf16 split);
+// accumulation is fp32.  Three kernels: bf16 weights with fewer than 256
+// rows, a contraction split over 8 waves (k_skinny_bf16); bf16 operands
+// with many rows, 128 x 128 tiles (k_gemm_tiled); anything else, a plain
+// tiled VALU product (k_gemm_xwT: 64 x 64 outputs per 256-thread
+// workgroup, 16-wide k chunks staged in LDS).
 #include <algorithm>
 
 #include "common.hpp"
@@ -349,10 +352,7 @@ bool skinny_ok(const GemmArgs &a) {
   return a.ldx % 4 == 0 && a.Kd <= 32 * SK_WAVES * SK_KSW_F;
 }
 
-hipError_t skinny_prepare(size_t) { return hipSuccess; }
 
-static size_t g_lds_max = 65536;
-void gemm_set_lds_max(size_t b) { g_lds_max = b; }
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.R <= 0 || a.N <= 0) return hipSuccess;

@@ -108,8 +108,6 @@ struct GemmArgs {
                          // is multiplied by the same weights three times
 };
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
-hipError_t skinny_prepare(size_t lds_max);
-void gemm_set_lds_max(size_t bytes);
 // GRU gates: gi, gh = input/state projections incl. biases ([R, 3s]); if gh
 // is null the previous state is zero and the state part equals b_hh.
 // Row i takes gh row pidx[i] (stride ldgh) and previous state row pidx[i].
