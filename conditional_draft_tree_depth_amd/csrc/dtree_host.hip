@@ -383,15 +383,10 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   int A = 1, off = 1, sc = 0;
   if (marginal) {
     // every branch of a depth is scored by the depth's base logits Cl
-    // (no correction, no GRU state): the selection reads the same row of Cl
-    // for all of a request's branches
+    // (no correction, no GRU state): the whole depth loop is one kernel
     prof_mark(ctx, 4, st);
+    HIPCHK(ctx, launch_select_marginal(batch, M, K, W, D, ws.C, ws.Cl, tb, st));
     for (int dd = 0; dd < D; ++dd) {
-      HIPCHK(ctx, launch_select(batch, A, M, K, W, D, dd, off, ws.C, ws.Cl + (size_t)dd * M,
-                                (long)D * M, 0, tb, st));
-      cur = 1 - cur;
-      tb.surv_node = ws.surv[cur]; tb.surv_rank = ws.rank[cur];
-      tb.nsurv_node = ws.surv[1 - cur]; tb.nsurv_rank = ws.rank[1 - cur];
       off += A * K;
       A = A * K < W ? A * K : W;
     }

@@ -144,6 +144,21 @@ __device__ __forceinline__ void branch_ranks(uint64_t k0, uint64_t k1, bool h0, 
   __builtin_amdgcn_wave_barrier();
 }
 
+// Number of the n keys in LDS greater than kc (8 loads in flight at a time).
+template <class T>
+__device__ __forceinline__ int count_greater(const T *keys, int n, T kc) {
+  int r = 0, j = 0;
+  for (; j + 8 <= n; j += 8) {
+    T v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = keys[j + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r += v[u] > kc;
+  }
+  for (; j < n; ++j) r += keys[j] > kc;
+  return r;
+}
+
 // Selection of one depth for one request (one workgroup each):
 //  0. the expanded branches' node ids, lexicographic ranks and scores are
 //     gathered into LDS once (two dependent loads for all branches at once);
@@ -240,8 +255,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
   // Top-W by rank: keys are distinct (distinct token paths)
   for (int c = tid; c < Z; c += blockDim.x) {
     const uint64_t kc = ckey[c];
-    int rank = 0;
-    for (int c2 = 0; c2 < Z; ++c2) rank += ckey[c2] > kc;
+    const int rank = count_greater<uint64_t>(ckey, Z, kc);
     if (rank < An) {
       const size_t sl = (size_t)q * t.Wmax + rank;
       t.nsurv_node[sl] = off + c;
@@ -254,8 +268,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
   __syncthreads();
   for (int i = tid; i < An; i += blockDim.x) {
     const uint32_t li = slex[i];
-    int rank = 0;
-    for (int j = 0; j < An; ++j) rank += slex[j] < li;
+    const int rank = An - 1 - count_greater<uint32_t>(slex, An, li);   // lex keys are distinct
     t.nsurv_rank[(size_t)q * t.Wmax + i] = rank;
   }
 }
@@ -400,8 +413,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K
   // Top-W by rank: keys are distinct (distinct token paths)
   for (int c = tid; c < Z; c += blockDim.x) {
     const uint64_t kc = ckey[c];
-    int rank = 0;
-    for (int c2 = 0; c2 < Z; ++c2) rank += ckey[c2] > kc;
+    const int rank = count_greater<uint64_t>(ckey, Z, kc);
     if (rank < An) {
       const size_t sl = (size_t)q * t.Wmax + rank;
       t.nsurv_node[sl] = off + c;
@@ -414,8 +426,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K
   __syncthreads();
   for (int i = tid; i < An; i += blockDim.x) {
     const uint32_t li = slex[i];
-    int rank = 0;
-    for (int j = 0; j < An; ++j) rank += slex[j] < li;
+    const int rank = An - 1 - count_greater<uint32_t>(slex, An, li);   // lex keys are distinct
     t.nsurv_rank[(size_t)q * t.Wmax + i] = rank;
   }
 }
@@ -434,6 +445,102 @@ hipError_t launch_select_corr(int b, int A, int M, int K, int W, int D, int delt
                               int ldu, const TreeBufs &t, hipStream_t st) {
   hipLaunchKernelGGL(k_select_corr, dim3(b), dim3(SEL_THREADS), select_corr_smem(M, r), st, A, M,
                      K, W, D, delta, off, r, static_cast<const uint16_t *>(W2), C, Cl, u, ldu, t);
+  return hipGetLastError();
+}
+
+// The whole depth loop under marginal scoring, one workgroup per request:
+// with no correction every branch of a depth sees the same M log-probs (the
+// log-softmax of the depth's base logits), so the depth's ranks are found
+// once; each expanded branch a gets children a * K + k, k < K, with the
+// candidate of rank k and score fp32(score(a) + lp); then the Top-W
+// survivors and their lexicographic ranks, carried to the next depth in LDS.
+// Same rules and tie-breaks as k_select (DARTree page, Methodology 1;
+// "Resumen Técnico: DominoTree", Main components 2).
+__global__ __launch_bounds__(SEL_THREADS) void k_select_marginal(int M, int K, int W, int D,
+                                                                 const int32_t *__restrict__ C,
+                                                                 const float *__restrict__ Cl,
+                                                                 TreeBufs t) {
+  __shared__ uint64_t ckey[SEL_MAXZ];
+  __shared__ uint32_t clex[SEL_MAXZ];
+  __shared__ uint32_t slex[SEL_MAXW];
+  __shared__ int32_t pnode[2][SEL_MAXW];
+  __shared__ uint32_t prank[2][SEL_MAXW];
+  __shared__ float pscore[2][SEL_MAXW];
+  __shared__ int32_t ktok[128];     // the depth's candidates by rank: token
+  __shared__ float klp[128];        //   and log-prob
+  __shared__ uint64_t wkeys[128];
+  __shared__ int32_t ctab[32 * 128];   // every depth's candidates (D <= 31, M <= 128)
+  __shared__ float ltab[32 * 128];     //   and their base logits
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t nb = (size_t)q * t.NT;
+  for (int i = tid; i < D * M; i += blockDim.x) {
+    ctab[i] = C[(size_t)q * D * M + i];
+    ltab[i] = Cl[(size_t)q * D * M + i];
+  }
+  if (tid == 0) { pnode[0][0] = 0; prank[0][0] = 0u; pscore[0][0] = 0.f; }
+  __syncthreads();
+  int A = 1, off = 1, cur = 0;
+  for (int dd = 0; dd < D; ++dd) {
+    const int Z = A * K, An = Z < W ? Z : W;
+    if (wave == 0) {
+      const int32_t *cq = ctab + dd * M;
+      const float *lq = ltab + dd * M;
+      const bool h0 = lane < M, h1 = lane + 64 < M;
+      const float l0 = h0 ? lq[lane] : -INFINITY, l1 = h1 ? lq[lane + 64] : -INFINITY;
+      const int32_t t0 = h0 ? cq[lane] : 0, t1 = h1 ? cq[lane + 64] : 0;
+      const float m = wave_max_f32(fmaxf(l0, l1));
+      const float e = (h0 ? expf(l0 - m) : 0.f) + (h1 ? expf(l1 - m) : 0.f);
+      const float lse = m + logf(wave_sum_f32(e));
+      const uint64_t k0 = h0 ? make_key(l0 - lse, (uint32_t)t0) : 0ull;
+      const uint64_t k1 = h1 ? make_key(l1 - lse, (uint32_t)t1) : 0ull;
+      int r0, r1;
+      branch_ranks(k0, k1, h0, h1, M, wkeys, lane, r0, r1);
+      if (h0 && r0 < K) { ktok[r0] = t0; klp[r0] = key_val(k0); }
+      if (h1 && r1 < K) { ktok[r1] = t1; klp[r1] = key_val(k1); }
+    }
+    __syncthreads();
+    for (int c = tid; c < Z; c += blockDim.x) {
+      const int a = c / K, k = c - a * K;
+      const uint32_t tok = (uint32_t)ktok[k];
+      const float sc = __fadd_rn(pscore[cur][a], klp[k]);
+      const uint32_t lex = (prank[cur][a] << 18) | tok;
+      const size_t id = nb + off + c;
+      t.n_tok[id] = (int32_t)tok;
+      t.n_par[id] = pnode[cur][a];
+      t.n_dep[id] = dd + 1;
+      t.n_score[id] = sc;
+      t.n_lex[id] = lex;
+      ckey[c] = make_key(sc, lex);
+      clex[c] = lex;
+    }
+    __syncthreads();
+    // Top-W by rank: keys are distinct (distinct token paths)
+    for (int c = tid; c < Z; c += blockDim.x) {
+      const uint64_t kc = ckey[c];
+      const int rank = count_greater<uint64_t>(ckey, Z, kc);
+      if (rank < An) {
+        pnode[cur ^ 1][rank] = off + c;
+        pscore[cur ^ 1][rank] = key_val(kc);
+        slex[rank] = clex[c];
+        t.surv_hist[((size_t)q * (D + 1) + dd + 1) * t.Wmax + rank] = off + c;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < An; i += blockDim.x) {
+      const uint32_t li = slex[i];
+      const int rank = An - 1 - count_greater<uint32_t>(slex, An, li);   // lex keys are distinct
+      prank[cur ^ 1][i] = (uint32_t)rank;
+    }
+    __syncthreads();
+    cur ^= 1;
+    off += Z;
+    A = An;
+  }
+}
+
+hipError_t launch_select_marginal(int b, int M, int K, int W, int D, const int32_t *C,
+                                  const float *Cl, const TreeBufs &t, hipStream_t st) {
+  hipLaunchKernelGGL(k_select_marginal, dim3(b), dim3(SEL_THREADS), 0, st, M, K, W, D, C, Cl, t);
   return hipGetLastError();
 }
 

@@ -129,6 +129,9 @@ hipError_t launch_corr_logits(int b, int A, int M, int r, int D, int delta,
                               const float *Cl, const float *u, int ldu, float *ell,
                               hipStream_t st);
 size_t corr_logits_smem(int A, int M, int r, int wtype);
+// marginal scoring: the whole depth loop, one workgroup per request
+hipError_t launch_select_marginal(int b, int M, int K, int W, int D, const int32_t *C,
+                                  const float *Cl, const TreeBufs &t, hipStream_t st);
 // branch a of request q reads its M logits at ell + q * ldq + a * lda
 hipError_t launch_select(int b, int A, int M, int K, int W, int D, int delta,
                          int off, const int32_t *C, const float *ell, long ldq, int lda,
