@@ -34,6 +34,11 @@ struct Ws {
   uint32_t *n_lex = nullptr;
   int32_t *surv[2] = {nullptr, nullptr}, *rank[2] = {nullptr, nullptr};
   int32_t *surv_hist = nullptr, *gidx_tok = nullptr, *gidx_par = nullptr, *sel = nullptr;
+  // GRU input projections of every candidate of every depth ([b * D * M, 3s],
+  // multi-kernel loop with at most 4096 candidates per round) and each
+  // survivor's row in it
+  float *gi_all = nullptr;
+  int32_t *gidx_cand = nullptr;
   uint32_t *status = nullptr;
   // persistent depth loop: correction tables, partial sums, arrival flags
   float *G = nullptr, *g = nullptr, *pk_part = nullptr, *gitab = nullptr, *pk_terms = nullptr;
@@ -123,7 +128,7 @@ void free_ws(Ws &ws) {
                   ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
                   ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags,
-                  ws.logits, ws.S3[0], ws.S3[1]};
+                  ws.logits, ws.S3[0], ws.S3[1], ws.gi_all, ws.gidx_cand};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   ws = Ws();
@@ -239,6 +244,10 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   A(alloc(&ws.surv_hist, (size_t)c.max_batch * (c.max_D + 1) * c.max_W));
   A(alloc(&ws.gidx_tok, bw));
   A(alloc(&ws.gidx_par, bw));
+  if (w->wtype == DTREE_BF16 && rows * c.max_M <= 4096) {
+    A(alloc(&ws.gi_all, rows * c.max_M * 3 * s));
+    A(alloc(&ws.gidx_cand, bw));
+  }
   A(alloc(&ws.sel, (size_t)c.max_batch * c.max_B));
   A(alloc(&ws.status, 1));
   // the persistent depth loop needs bf16 weights and MFMA-friendly GRU sizes
@@ -279,7 +288,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   // pieces whose slice (and one u row per wave) fits in LDS
   ctx->sel_corr = w->wtype == DTREE_BF16 && r % 8 == 0 && r <= 512 &&
                   reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
-                  select_corr_smem(c.max_M, r) + 40960 <= ctx->lds_max;
+                  select_corr_smem(c.max_M, r) + 45056 <= ctx->lds_max;
   if (pe == hipSuccess && ctx->sel_corr) pe = select_corr_prepare(select_corr_smem(c.max_M, r));
   if (pe == hipSuccess && ctx->pk) pe = persist_prepare(s);
   if (pe != hipSuccess) {
@@ -411,8 +420,18 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
     g = GemmArgs{batch, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
                  w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
     HIPCHK(ctx, launch_gemm(g, st));
-    HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, 0, w.b_hh, nullptr, nullptr, ws.S[0],
-                                   ws.S3[0], st));
+    HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, nullptr, 0, w.b_hh, nullptr, nullptr,
+                                   ws.S[0], ws.S3[0], st));
+    // the GRU input projection depends on the token only: with few enough
+    // candidates it is made for all of them at once, and each survivor's
+    // GRU step reads its candidate's row
+    const bool precomp = ws.gi_all && batch * D * M <= 4096;
+    if (precomp) {
+      g = GemmArgs{batch * D * M, 3 * s, w.e, w.Emb, wt, w.e, ws.C, 0, w.W_ih, wt, w.e,
+                   w.b_ih, nullptr, 0, 1, 0, 0, ws.gi_all, 3 * s};
+      HIPCHK(ctx, launch_gemm(g, st));
+      tb.gidx_cand = ws.gidx_cand;
+    }
     prof_mark(ctx, 4, st);
     for (int dd = 0; dd < D; ++dd) {
       // for every expanded branch, one product over its state S:
@@ -447,11 +466,14 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
       }
       const int An = A * K < W ? A * K : W;
       if (dd + 1 < D) {
-        g = GemmArgs{batch * An, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
-                     w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
-        HIPCHK(ctx, launch_gemm(g, st));
-        HIPCHK(ctx, launch_gru_combine(batch * An, s, ws.gi, ws.uh + r, ldu, nullptr, ws.S[sc],
-                                       ws.gidx_par, ws.S[1 - sc], ws.S3[1 - sc], st));
+        if (!precomp) {
+          g = GemmArgs{batch * An, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
+                       w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
+          HIPCHK(ctx, launch_gemm(g, st));
+        }
+        HIPCHK(ctx, launch_gru_combine(batch * An, s, precomp ? ws.gi_all : ws.gi,
+                                       precomp ? ws.gidx_cand : nullptr, ws.uh + r, ldu, nullptr,
+                                       ws.S[sc], ws.gidx_par, ws.S[1 - sc], ws.S3[1 - sc], st));
         sc = 1 - sc;
       }
       cur = 1 - cur;

@@ -186,6 +186,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
   __shared__ float pscore[SEL_MAXW];
   __shared__ int32_t ctok[128];
   __shared__ uint64_t wkeys[(SEL_THREADS / 64) * 128];   // one row of keys per wave
+  __shared__ int16_t cidx[SEL_MAXZ];                      // children's candidate index
   const int q = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int nw = blockDim.x >> 6;
@@ -245,6 +246,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
         t.n_lex[id] = lex;
         ckey[c] = make_key(sc, lex);
         clex[c] = lex;
+        cidx[c] = (int16_t)(lane + 64 * h);
       }
     }
     l0 = n0;
@@ -262,6 +264,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
       slex[rank] = clex[c];
       t.gidx_tok[(size_t)q * An + rank] = (int32_t)(clex[c] & 0x3FFFFu);
       t.gidx_par[(size_t)q * An + rank] = q * A + c / K;
+      if (t.gidx_cand) t.gidx_cand[(size_t)q * An + rank] = (q * D + delta) * M + cidx[c];
       t.surv_hist[((size_t)q * (D + 1) + delta + 1) * t.Wmax + rank] = off + c;
     }
   }
@@ -296,6 +299,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K
   __shared__ int32_t ctok[128];
   __shared__ float clv[128];
   __shared__ uint64_t wkeys[(SEL_THREADS / 64) * 128];   // one row of keys per wave
+  __shared__ int16_t cidx[SEL_MAXZ];                      // children's candidate index
   const int rs = r + 8;
   uint16_t *W2s = reinterpret_cast<uint16_t *>(smem);                    // [M][r + 8]
   float *ubuf = reinterpret_cast<float *>(smem + (((size_t)M * rs * 2 + 15) & ~(size_t)15));
@@ -405,6 +409,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K
         t.n_lex[id] = lex;
         ckey[c] = make_key(sc, lex);
         clex[c] = lex;
+        cidx[c] = (int16_t)(lane + 64 * h);
       }
     }
   }
@@ -420,6 +425,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K
       slex[rank] = clex[c];
       t.gidx_tok[(size_t)q * An + rank] = (int32_t)(clex[c] & 0x3FFFFu);
       t.gidx_par[(size_t)q * An + rank] = q * A + c / K;
+      if (t.gidx_cand) t.gidx_cand[(size_t)q * An + rank] = (q * D + delta) * M + cidx[c];
       t.surv_hist[((size_t)q * (D + 1) + delta + 1) * t.Wmax + rank] = off + c;
     }
   }

@@ -403,6 +403,7 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
 //   h' = (1 - z) n + z h
 // where a = W_ih x + b_ih and c = W_hh h + b_hh.
 __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *__restrict__ gi,
+                                                     const int32_t *__restrict__ gidx,
                                                      const float *__restrict__ gh, int ldgh,
                                                      const float *__restrict__ b_hh,
                                                      const float *__restrict__ Sprev,
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= R * s) return;
   const int i = idx / s, j = idx - i * s;
-  const float *a = gi + (size_t)i * 3 * s;
+  const float *a = gi + (size_t)(gidx ? gidx[i] : i) * 3 * s;
   float cr, cz, cn, h;
   if (gh) {
     const int pr = pidx ? pidx[i] : i;   // the parent's row: its state and state part
@@ -441,13 +442,13 @@ __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *
   }
 }
 
-hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh, int ldgh,
-                              const float *b_hh, const float *Sprev, const int32_t *pidx,
-                              float *Snew, uint16_t *S3, hipStream_t st) {
+hipError_t launch_gru_combine(int R, int s, const float *gi, const int32_t *gidx,
+                              const float *gh, int ldgh, const float *b_hh, const float *Sprev,
+                              const int32_t *pidx, float *Snew, uint16_t *S3, hipStream_t st) {
   const int n = R * s;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gru_combine, dim3((n + 255) / 256), dim3(256), 0, st, R, s, gi, gh, ldgh,
-                     b_hh, Sprev, pidx, Snew, S3);
+  hipLaunchKernelGGL(k_gru_combine, dim3((n + 255) / 256), dim3(256), 0, st, R, s, gi, gidx, gh,
+                     ldgh, b_hh, Sprev, pidx, Snew, S3);
   return hipGetLastError();
 }
 

@@ -18,6 +18,8 @@ struct TreeBufs {
   int32_t *nsurv_node, *nsurv_rank; // [b, Wmax] next depth
   int32_t *surv_hist;               // [b, D+1, Wmax]
   int32_t *gidx_tok, *gidx_par;     // [b * Wmax] gathers for the GRU step
+  int32_t *gidx_cand;               // [b * Wmax] survivor's candidate row (q D + depth) M + j,
+                                    // written when not null
   int32_t *sel;                     // [b, Bmax]
   uint32_t *status;                 // device status bits
 };
@@ -110,10 +112,12 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
 // GRU gates: gi, gh = input/state projections incl. biases ([R, 3s]); if gh
 // is null the previous state is zero and the state part equals b_hh.
-// Row i takes gh row pidx[i] (stride ldgh) and previous state row pidx[i].
+// Row i takes gi row gidx[i] (i if gidx is null), gh row pidx[i] (stride
+// ldgh) and previous state row pidx[i].
 // S3 (or null): the new state also as three bf16 planes, row i = [hi | mid | lo]
 // ([R, 3s]), the exact split hi + mid + lo of every fp32 value.
-hipError_t launch_gru_combine(int R, int s, const float *gi, const float *gh, int ldgh,
+hipError_t launch_gru_combine(int R, int s, const float *gi, const int32_t *gidx,
+                              const float *gh, int ldgh,
                               const float *b_hh, const float *Sprev,
                               const int32_t *pidx, float *Snew, uint16_t *S3, hipStream_t st);
 hipError_t gemm_prepare();
