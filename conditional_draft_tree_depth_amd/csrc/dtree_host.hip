@@ -8,6 +8,7 @@
 //   for each depth: u = uH + W1[:, d:] S, corrected logits of the M
 //       candidates, selection, GRU step of the survivors  (k_gemm/k_depth)
 //   K4  global Top-B, canonical order, mask      (k_topb.hip)
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -34,11 +35,17 @@ struct Ws {
   uint32_t *n_lex = nullptr;
   int32_t *surv[2] = {nullptr, nullptr}, *rank[2] = {nullptr, nullptr};
   int32_t *surv_hist = nullptr, *gidx_tok = nullptr, *gidx_par = nullptr, *sel = nullptr;
-  // GRU input projections of every candidate of every depth ([b * D * M, 3s],
-  // multi-kernel loop with at most 4096 candidates per round) and each
-  // survivor's row in it
+  // GRU input projections of the round's candidates, made before the
+  // multi-kernel depth loop: one row per distinct token (or per candidate
+  // when few), [min(b D M, V), 3s]; each survivor's candidate row; the
+  // distinct-token tables (first row per token [V], representatives' positions,
+  // distinct tokens, candidate row -> distinct position, count)
   float *gi_all = nullptr;
   int32_t *gidx_cand = nullptr;
+  uint64_t *first_row = nullptr;
+  int32_t *cidx_tmp = nullptr, *uniq = nullptr, *rowmap = nullptr, *ucount = nullptr,
+          *lpos = nullptr, *btot = nullptr;
+  size_t gi_rows = 0;
   uint32_t *status = nullptr;
   // persistent depth loop: correction tables, partial sums, arrival flags
   float *G = nullptr, *g = nullptr, *pk_part = nullptr, *gitab = nullptr, *pk_terms = nullptr;
@@ -77,6 +84,7 @@ struct dtree_ctx {
   bool pk = false;
   bool sel_corr = false;   // correction logits computed inside the selection kernel
   int scoring = DTREE_SCORE_CONDITIONAL;
+  uint32_t tok_epoch = 0;   // distinct-token tables: grows by one per round that uses them
   int pk_rows = 0;
   // persistent depth loop: plain launches until one of its waits runs out
   // (it then stores 1 to *pk_fail, host memory the kernel writes through
@@ -128,7 +136,8 @@ void free_ws(Ws &ws) {
                   ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
                   ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags,
-                  ws.logits, ws.S3[0], ws.S3[1], ws.gi_all, ws.gidx_cand};
+                  ws.logits, ws.S3[0], ws.S3[1], ws.gi_all, ws.gidx_cand, ws.first_row,
+                  ws.cidx_tmp, ws.uniq, ws.rowmap, ws.ucount, ws.lpos, ws.btot};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   ws = Ws();
@@ -244,9 +253,19 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   A(alloc(&ws.surv_hist, (size_t)c.max_batch * (c.max_D + 1) * c.max_W));
   A(alloc(&ws.gidx_tok, bw));
   A(alloc(&ws.gidx_par, bw));
-  if (w->wtype == DTREE_BF16 && rows * c.max_M <= 4096) {
-    A(alloc(&ws.gi_all, rows * c.max_M * 3 * s));
+  if (w->wtype == DTREE_BF16) {
+    const size_t ncand = rows * c.max_M;
+    ws.gi_rows = ncand < (size_t)w->V ? ncand : (size_t)w->V;
+    A(alloc(&ws.gi_all, ws.gi_rows * 3 * s));
     A(alloc(&ws.gidx_cand, bw));
+    A(alloc(&ws.first_row, (size_t)w->V));
+    A(alloc(&ws.cidx_tmp, ncand));
+    A(alloc(&ws.uniq, ws.gi_rows));
+    A(alloc(&ws.rowmap, ncand));
+    A(alloc(&ws.ucount, 1));
+    A(alloc(&ws.lpos, ncand));
+    A(alloc(&ws.btot, ncand / 256 + 1));
+    if (e == hipSuccess) A(hipMemset(ws.first_row, 0, (size_t)w->V * 8));
   }
   A(alloc(&ws.sel, (size_t)c.max_batch * c.max_B));
   A(alloc(&ws.status, 1));
@@ -420,18 +439,34 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
     g = GemmArgs{batch, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
                  w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
     HIPCHK(ctx, launch_gemm(g, st));
-    HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, nullptr, 0, w.b_hh, nullptr, nullptr,
-                                   ws.S[0], ws.S3[0], st));
-    // the GRU input projection depends on the token only: with few enough
-    // candidates it is made for all of them at once, and each survivor's
-    // GRU step reads its candidate's row
-    const bool precomp = ws.gi_all && batch * D * M <= 4096;
-    if (precomp) {
-      g = GemmArgs{batch * D * M, 3 * s, w.e, w.Emb, wt, w.e, ws.C, 0, w.W_ih, wt, w.e,
+    HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, nullptr, nullptr, 0, w.b_hh, nullptr,
+                                   nullptr, ws.S[0], ws.S3[0], st));
+    // the GRU input projection depends on the token only: it is made once
+    // per distinct token of the round's candidates (a tiled product whose row
+    // count is read on the device), or once per candidate when they are few,
+    // and each survivor's GRU step reads its token's row
+    const int ncand = batch * D * M;
+    int precomp = 0;   // 0: per depth, 1: per candidate, 2: per distinct token
+    GemmArgs gu{};
+    if (ws.gi_all) {
+      gu = GemmArgs{(int)std::min((size_t)ncand, ws.gi_rows), 3 * s, w.e, w.Emb, wt, w.e, ws.uniq,
+                    0, w.W_ih, wt, w.e, w.b_ih, nullptr, 0, 1, 0, 0, ws.gi_all, 3 * s};
+      gu.Rdev = ws.ucount;
+      // (finding the distinct tokens costs five small launches: worth it
+      // with many candidates, whose tokens repeat across depths and requests)
+      if (ncand > 2048 && ncand <= 262144 && gemm_rdev_ok(gu)) precomp = 2;
+      else if ((size_t)ncand <= ws.gi_rows && ncand <= 4096) precomp = 1;
+    }
+    if (precomp == 2) {
+      HIPCHK(ctx, launch_token_dedupe(ncand, ws.C, ws.first_row, ++ctx->tok_epoch, ws.lpos,
+                                      ws.btot, ws.cidx_tmp, ws.uniq, ws.rowmap, ws.ucount, st));
+      HIPCHK(ctx, launch_gemm(gu, st));
+    } else if (precomp == 1) {
+      g = GemmArgs{ncand, 3 * s, w.e, w.Emb, wt, w.e, ws.C, 0, w.W_ih, wt, w.e,
                    w.b_ih, nullptr, 0, 1, 0, 0, ws.gi_all, 3 * s};
       HIPCHK(ctx, launch_gemm(g, st));
-      tb.gidx_cand = ws.gidx_cand;
     }
+    if (precomp) tb.gidx_cand = ws.gidx_cand;
     prof_mark(ctx, 4, st);
     for (int dd = 0; dd < D; ++dd) {
       // for every expanded branch, one product over its state S:
@@ -472,7 +507,8 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
           HIPCHK(ctx, launch_gemm(g, st));
         }
         HIPCHK(ctx, launch_gru_combine(batch * An, s, precomp ? ws.gi_all : ws.gi,
-                                       precomp ? ws.gidx_cand : nullptr, ws.uh + r, ldu, nullptr,
+                                       precomp ? ws.gidx_cand : nullptr,
+                                       precomp == 2 ? ws.rowmap : nullptr, ws.uh + r, ldu, nullptr,
                                        ws.S[sc], ws.gidx_par, ws.S[1 - sc], ws.S3[1 - sc], st));
         sc = 1 - sc;
       }

@@ -146,7 +146,9 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int R
   __shared__ __align__(16) float red[SK_WAVES * SK_RB * 256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16, r0 = blockIdx.y * (16 * RB);
-  const int nrb = min(RB, (a.R - r0 + 15) >> 4);
+  const int R = a.Rdev ? min(*a.Rdev, a.R) : a.R;   // rows past the device count: no work
+  if (r0 >= R) return;
+  const int nrb = min(RB, (R - r0 + 15) >> 4);
   const int nks = a.Kd >> 5;
   const uint16_t *wrow = static_cast<const uint16_t *>(a.W) + (size_t)min(n0 + lr, a.N - 1) * a.ldw + g * 8;
   // k-steps past the contraction load the last one again (every load is
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int R
   // activation row of lane lr in row block rb (rows past R repeat the last
   // row; their sums are never stored)
   auto xrow = [&](int rb) -> size_t {
-    const int row = min(r0 + rb * 16 + lr, a.R - 1);
+    const int row = min(r0 + rb * 16 + lr, R - 1);
     return (size_t)(a.xidx ? a.xidx[row] : row) * a.ldx + g * 8;
   };
   if constexpr (XB) {
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int R
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < SK_WAVES; ++w) v += red[((w * SK_RB + rb) * 16 + rr) * 16 + nn];
-    if (row < a.R && n < a.N) {
+    if (row < R && n < a.N) {
       if (a.bias && n >= a.bias_n0) v += a.bias[n - a.bias_n0];
       if (a.addend && n < a.add_n) v += a.addend[(size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda + n];
       a.Y[(size_t)row * a.ldy + n] = v;
@@ -247,6 +249,8 @@ __global__ __launch_bounds__(GTT_THREADS) void k_gemm_tiled(GemmArgs a) {
   int task = blockIdx.x;
   if (total % 8 == 0) task = (task & 7) * (total / 8) + (task >> 3);
   const int m0 = (task % ntm) * GTT_B, n0 = (task / ntm) * GTT_B;
+  const int R = a.Rdev ? min(*a.Rdev, a.R) : a.R;   // rows past the device count: no work
+  if (m0 >= R) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
   const uint16_t *X = static_cast<const uint16_t *>(a.X);
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(GTT_THREADS) void k_gemm_tiled(GemmArgs a) {
     if (j >= 16) {
       src[i] = reinterpret_cast<const uint4 *>(W + (size_t)min(n0 + row, a.N - 1) * a.ldw) + ch;
     } else {
-      const int xr = min(m0 + row, a.R - 1);
+      const int xr = min(m0 + row, R - 1);
       src[i] = reinterpret_cast<const uint4 *>(X + (size_t)(a.xidx ? a.xidx[xr] : xr) * a.ldx) + ch;
     }
   }
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(GTT_THREADS) void k_gemm_tiled(GemmArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int row = m0 + wm + i * 16 + 4 * g + t;
-        if (row >= a.R) continue;
+        if (row >= R) continue;
         float v = acc[i][j][t] + bv;
         if (a.addend && n < a.add_n)
           v += a.addend[(size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda + n];
@@ -354,14 +358,22 @@ bool skinny_ok(const GemmArgs &a) {
 
 
 
+bool gemm_rdev_ok(const GemmArgs &a) {
+  return (a.R <= 8192 && skinny_ok(a)) || gemm_tiled_ok(a);
+}
+
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.R <= 0 || a.N <= 0) return hipSuccess;
-  if (gemm_tiled_ok(a)) {
+  // a device row count up to 8192 rows: the contraction-split kernel, whose
+  // workgroups past the count leave at once, keeps every wave busy
+  const bool skinny_first = a.Rdev && a.R <= 8192 && skinny_ok(a);
+  if (!skinny_first && gemm_tiled_ok(a)) {
     const int total = ((a.R + GTT_B - 1) / GTT_B) * ((a.N + GTT_B - 1) / GTT_B);
     hipLaunchKernelGGL(k_gemm_tiled, dim3(total), dim3(GTT_THREADS), GTT_SMEM, st, a);
     return hipGetLastError();
   }
   if (a.kw && a.kw != a.Kd) return hipErrorInvalidValue;   // planes need the tiled kernel
+  if (a.Rdev && !skinny_ok(a)) return hipErrorInvalidValue;  // device row counts need MFMA kernels
   if (skinny_ok(a)) {
     const int terms = skinny_terms(a);
     // row blocks per workgroup: enough workgroups to fill the chip (about
@@ -404,6 +416,7 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
 // where a = W_ih x + b_ih and c = W_hh h + b_hh.
 __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *__restrict__ gi,
                                                      const int32_t *__restrict__ gidx,
+                                                     const int32_t *__restrict__ gmap,
                                                      const float *__restrict__ gh, int ldgh,
                                                      const float *__restrict__ b_hh,
                                                      const float *__restrict__ Sprev,
@@ -413,7 +426,9 @@ __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= R * s) return;
   const int i = idx / s, j = idx - i * s;
-  const float *a = gi + (size_t)(gidx ? gidx[i] : i) * 3 * s;
+  int gr = gidx ? gidx[i] : i;
+  if (gmap) gr = gmap[gr];
+  const float *a = gi + (size_t)gr * 3 * s;
   float cr, cz, cn, h;
   if (gh) {
     const int pr = pidx ? pidx[i] : i;   // the parent's row: its state and state part
@@ -443,12 +458,13 @@ __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *
 }
 
 hipError_t launch_gru_combine(int R, int s, const float *gi, const int32_t *gidx,
-                              const float *gh, int ldgh, const float *b_hh, const float *Sprev,
-                              const int32_t *pidx, float *Snew, uint16_t *S3, hipStream_t st) {
+                              const int32_t *gmap, const float *gh, int ldgh, const float *b_hh,
+                              const float *Sprev, const int32_t *pidx, float *Snew, uint16_t *S3,
+                              hipStream_t st) {
   const int n = R * s;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gru_combine, dim3((n + 255) / 256), dim3(256), 0, st, R, s, gi, gidx, gh,
-                     ldgh, b_hh, Sprev, pidx, Snew, S3);
+  hipLaunchKernelGGL(k_gru_combine, dim3((n + 255) / 256), dim3(256), 0, st, R, s, gi, gidx, gmap,
+                     gh, ldgh, b_hh, Sprev, pidx, Snew, S3);
   return hipGetLastError();
 }
 
@@ -476,6 +492,96 @@ hipError_t launch_concat_state_weights(const void *W1, const void *W_hh, int r, 
     hipLaunchKernelGGL(k_concat_state_weights<float>, grid, dim3(256), 0, st,
                        static_cast<const float *>(W1), static_cast<const float *>(W_hh), r, s, d,
                        static_cast<float *>(Wcat));
+  return hipGetLastError();
+}
+
+// ---- distinct tokens (the GRU input projection depends on the token only)
+// first[tok] holds (epoch << 32) | (2^32 - 1 - row) for the token's first row
+// of the current round (a 64-bit maximum, so entries of earlier rounds lose
+// and the table never needs clearing); row i represents its token when it is
+// that first row.  Representatives get consecutive positions in row order.
+constexpr int TD_B = 256;   // rows per block of the scans
+
+__device__ __forceinline__ uint64_t td_tag(uint32_t epoch, int row) {
+  return ((uint64_t)epoch << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row);
+}
+
+__global__ void k_token_mark(int n, const int32_t *__restrict__ tok, unsigned long long *first,
+                             uint32_t epoch) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) atomicMax(first + tok[i], (unsigned long long)td_tag(epoch, i));
+}
+
+// positions of the representatives inside each block of TD_B rows, and the
+// block totals
+__global__ __launch_bounds__(TD_B) void k_token_scan(int n, const int32_t *__restrict__ tok,
+                                                     const unsigned long long *__restrict__ first,
+                                                     uint32_t epoch, int32_t *lpos,
+                                                     int32_t *btot) {
+  __shared__ int sc[TD_B];
+  const int tid = threadIdx.x, i = blockIdx.x * TD_B + tid;
+  const int f = (i < n && first[tok[i]] == td_tag(epoch, i)) ? 1 : 0;
+  sc[tid] = f;
+  __syncthreads();
+  for (int off = 1; off < TD_B; off <<= 1) {   // inclusive scan (Hillis-Steele)
+    const int v = tid >= off ? sc[tid - off] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  if (i < n) lpos[i] = f ? sc[tid] - 1 : -1;
+  if (tid == TD_B - 1) btot[blockIdx.x] = sc[tid];
+}
+
+// exclusive scan of the block totals (one workgroup, nb <= 1024 blocks) and
+// the number of distinct tokens
+__global__ __launch_bounds__(1024) void k_token_bases(int nb, int32_t *btot, int32_t *count) {
+  __shared__ int sc[1024];
+  const int tid = threadIdx.x;
+  const int v0 = tid < nb ? btot[tid] : 0;
+  sc[tid] = v0;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? sc[tid - off] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  if (tid < nb) btot[tid] = sc[tid] - v0;
+  if (tid == 1023) *count = sc[tid];
+}
+
+__global__ void k_token_place(int n, const int32_t *__restrict__ tok,
+                              const int32_t *__restrict__ lpos, const int32_t *__restrict__ bbase,
+                              int32_t *cidx, int32_t *uniq) {
+  const int i = blockIdx.x * TD_B + threadIdx.x;
+  if (i >= n || lpos[i] < 0) return;
+  const int pos = bbase[blockIdx.x] + lpos[i];
+  cidx[i] = pos;
+  uniq[pos] = tok[i];
+}
+
+__global__ void k_token_map(int n, const int32_t *__restrict__ tok,
+                            const unsigned long long *__restrict__ first,
+                            const int32_t *__restrict__ cidx, int32_t *rowmap) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int rep = (int)(0xFFFFFFFFu - (uint32_t)first[tok[i]]);
+  rowmap[i] = cidx[rep];
+}
+
+hipError_t launch_token_dedupe(int n, const int32_t *tok, void *first, uint32_t epoch,
+                               int32_t *lpos, int32_t *btot, int32_t *cidx, int32_t *uniq,
+                               int32_t *rowmap, int32_t *count, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int nb = (n + TD_B - 1) / TD_B;
+  if (nb > 1024) return hipErrorInvalidValue;
+  auto *f = static_cast<unsigned long long *>(first);
+  hipLaunchKernelGGL(k_token_mark, dim3(nb), dim3(TD_B), 0, st, n, tok, f, epoch);
+  hipLaunchKernelGGL(k_token_scan, dim3(nb), dim3(TD_B), 0, st, n, tok, f, epoch, lpos, btot);
+  hipLaunchKernelGGL(k_token_bases, dim3(1), dim3(1024), 0, st, nb, btot, count);
+  hipLaunchKernelGGL(k_token_place, dim3(nb), dim3(TD_B), 0, st, n, tok, lpos, btot, cidx, uniq);
+  hipLaunchKernelGGL(k_token_map, dim3(nb), dim3(TD_B), 0, st, n, tok, f, cidx, rowmap);
   return hipGetLastError();
 }
 

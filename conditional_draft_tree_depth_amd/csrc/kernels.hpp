@@ -105,6 +105,8 @@ struct GemmArgs {
   float *Y; int ldy;
   int add_n = 1 << 30;   // the addend covers outputs n < add_n
   int bias_n0 = 0;       // the bias covers outputs n >= bias_n0
+  const int32_t *Rdev = nullptr;   // tiled product only: the row count read on the
+                                   // device (R is then its upper bound)
   int kw = 0;            // bf16 X only: W's k index is k mod kw (0: kw = Kd); a
                          // state split into three bf16 planes [hi | mid | lo]
                          // is multiplied by the same weights three times
@@ -112,17 +114,26 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
 // GRU gates: gi, gh = input/state projections incl. biases ([R, 3s]); if gh
 // is null the previous state is zero and the state part equals b_hh.
-// Row i takes gi row gidx[i] (i if gidx is null), gh row pidx[i] (stride
-// ldgh) and previous state row pidx[i].
+// Row i takes gi row gidx[i] (i if gidx is null; mapped through gmap when
+// given), gh row pidx[i] (stride ldgh) and previous state row pidx[i].
 // S3 (or null): the new state also as three bf16 planes, row i = [hi | mid | lo]
 // ([R, 3s]), the exact split hi + mid + lo of every fp32 value.
 hipError_t launch_gru_combine(int R, int s, const float *gi, const int32_t *gidx,
-                              const float *gh, int ldgh,
+                              const int32_t *gmap, const float *gh, int ldgh,
                               const float *b_hh, const float *Sprev,
                               const int32_t *pidx, float *Snew, uint16_t *S3, hipStream_t st);
 hipError_t gemm_prepare();
+// Distinct tokens of tok[0..n) (n <= 262144): uniq[0..*count) in order of
+// first occurrence, rowmap[i] = position of tok[i] in uniq.  first [V] u64
+// starts zeroed; epoch must grow from round to round (>= 1); lpos, cidx [n]
+// and btot [n / 256 + 1] are scratch.
+hipError_t launch_token_dedupe(int n, const int32_t *tok, void *first, uint32_t epoch,
+                               int32_t *lpos, int32_t *btot, int32_t *cidx, int32_t *uniq,
+                               int32_t *rowmap, int32_t *count, hipStream_t st);
 // true when launch_gemm runs a as a tiled product (many rows, bf16 operands)
 bool gemm_tiled_ok(const GemmArgs &a);
+// true when launch_gemm accepts a device row count (a.Rdev) for a
+bool gemm_rdev_ok(const GemmArgs &a);
 // Wcat = [W1[:, d:] ; W_hh] as [r + 3s, s] rows in the weight dtype
 hipError_t launch_concat_state_weights(const void *W1, const void *W_hh, int r, int s, int d,
                                        int wtype, void *Wcat, hipStream_t st);
