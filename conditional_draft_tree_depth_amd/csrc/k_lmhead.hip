@@ -870,6 +870,7 @@ __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int
 // The candidate list of (16-row block, vocabulary slice y) from logits in
 // memory: the slice's logits go to LDS and the LM-head kernel's epilogue
 // runs on them unchanged (slices cover the vocabulary tiles only).
+template <bool BISECT>
 __global__ __launch_bounds__(K1_WAVES * 64) void k1_lists_from_logits(
     const float *__restrict__ L, int rows, int V, int M, uint64_t *__restrict__ part) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -885,8 +886,10 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lists_from_logits(
   }
   __syncthreads();
   uint64_t *out = part + ((size_t)row0 * P + y) * K1_LSTRIDE;
-  if (M > 64) wg_topm_bisect<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE);
-  else wg_topm_epilogue<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE);
+  if constexpr (BISECT)
+    wg_topm_bisect<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE);
+  else
+    wg_topm_epilogue<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE);
 }
 
 // ----------------------------------------------------------------- host side
@@ -960,9 +963,15 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
                         static_cast<const uint16_t *>(a.W), a.V, a.bias, logits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipExtLaunchKernelGGL(k1_lists_from_logits, dim3(rows_pad / 16, a.P), dim3(K1_WAVES * 64),
-                        (uint32_t)(16 * K1_MAXCOLS * 4), st, nullptr, ev1, 0u,
-                        (const float *)logits, a.rows, a.V, a.M, a.part);
+  // (exact lists for M > 64: a kernel of its own, with fewer registers)
+  if (a.M > 64)
+    hipExtLaunchKernelGGL(k1_lists_from_logits<true>, dim3(rows_pad / 16, a.P),
+                          dim3(K1_WAVES * 64), (uint32_t)(16 * K1_MAXCOLS * 4), st, nullptr, ev1,
+                          0u, (const float *)logits, a.rows, a.V, a.M, a.part);
+  else
+    hipExtLaunchKernelGGL(k1_lists_from_logits<false>, dim3(rows_pad / 16, a.P),
+                          dim3(K1_WAVES * 64), (uint32_t)(16 * K1_MAXCOLS * 4), st, nullptr, ev1,
+                          0u, (const float *)logits, a.rows, a.V, a.M, a.part);
   return hipGetLastError();
 }
 
