@@ -13,16 +13,17 @@
 // One workgroup per request.  Selection: up to TB_RANK_MAX nodes, the rank
 // of every node among all keys is counted directly (a few threads per node);
 // larger superarbols find the B-th largest key by radix passes and rank only
-// the selected keys among themselves.  The mask comes from each
-// selected node's ancestor at every depth: j is an ancestor-or-self of i iff
-// depth(j) <= depth(i) and i's ancestor at depth(j) is j.
+// the selected keys among themselves.  The mask is built as a bitmap in
+// LDS, band of rows by band: each emitted node walks its parent chain and
+// sets its row's bits, then the band is written out with aligned 16-byte
+// stores (single bytes only where a band's edge is unaligned).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace dtree {
 
 constexpr int TB_THREADS = 1024;
-constexpr int TB_MAXDEP = 32;   // depths 0 .. 31
+constexpr int TB_MAXDEP = 32;   // depths 0 .. 31: a parent chain has at most 32 nodes
 constexpr int TB_RANK_MAX = 256;   // superarbols up to this size: rank counting
 
 // inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within rows
@@ -37,10 +38,65 @@ __device__ __forceinline__ int wave_scan_add(int v) {
   return v;
 }
 
-// LDS: keys (selection), later the canonical scratch, then the ancestor
-// table; ids (sorted order or selection ranks); the rest.
+// threads per element for the rank counts: a power of two up to 16 with
+// all elements in one pass when they fit
+__device__ __forceinline__ int split_width(int n) {
+  int tpn = 1;
+  while (tpn * 2 * n <= TB_THREADS && tpn < 16) tpn *= 2;
+  return tpn;
+}
+
+// part `part` of tpn of the count of a[0..n) ordered before x (greater if
+// GREATER, else smaller).  a is 16-byte aligned and the parts start at
+// multiples of 8 elements, so groups of 8 come in as 16-byte LDS reads.
+template <bool GREATER, typename T>
+__device__ __forceinline__ int count_split(const T *a, int n, T x, int part, int tpn) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit keys");
+  const int per = ((n + tpn - 1) / tpn + 7) & ~7, j0 = part * per, j1 = min(n, j0 + per);
+  int cnt = 0, j = j0;
+  for (; j + 8 <= j1; j += 8) {
+    constexpr int NV = 8 * (int)sizeof(T) / 16;
+    uint4 raw[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) raw[u] = reinterpret_cast<const uint4 *>(a + j)[u];
+    uint32_t w[4 * NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      w[4 * u] = raw[u].x; w[4 * u + 1] = raw[u].y; w[4 * u + 2] = raw[u].z; w[4 * u + 3] = raw[u].w;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      T v;
+      if constexpr (sizeof(T) == 8) v = ((uint64_t)w[2 * u + 1] << 32) | w[2 * u];
+      else v = w[u];
+      cnt += GREATER ? (v > x) : (v < x);
+    }
+  }
+  for (; j < j1; ++j) cnt += GREATER ? (a[j] > x) : (a[j] < x);
+  return cnt;
+}
+
+// sum over the tpn adjacent lanes of an element (every lane of the wave
+// takes part)
+__device__ __forceinline__ int sum_adjacent(int cnt, int tpn) {
+  if (tpn >= 2) cnt += (int)xchg_u32<1>((uint32_t)cnt);
+  if (tpn >= 4) cnt += (int)xchg_u32<2>((uint32_t)cnt);
+  if (tpn >= 8) cnt += (int)xchg_u32<4>((uint32_t)cnt);
+  if (tpn >= 16) cnt += (int)xchg_u32<8>((uint32_t)cnt);
+  return cnt;
+}
+
+// low 4 bits of b as 4 bytes of 0/1 (bit k -> byte k): the product puts a
+// copy of bit k at bit 7m + k of term m, and only m = k lands on bit 8m
+__device__ __forceinline__ uint32_t spread4(uint32_t b) {
+  return ((b & 15u) * 0x00204081u) & 0x01010101u;
+}
+
+// LDS: keys (selection), later the canonical scratch, then the mask bitmap
+// of one band of rows; ids (sorted order or selection ranks); the rest.
 struct TBLayout {
-  size_t keys, ids, map, onode, opar, odep, canon, hist, skey, total;
+  size_t keys, ids, map, onode, opar, canon, hist, skey, total;
+  int band_rows;   // mask rows per bitmap band
 };
 
 __host__ __device__ inline TBLayout tb_layout(int NT, int B) {
@@ -51,13 +107,16 @@ __host__ __device__ inline TBLayout tb_layout(int NT, int B) {
   TBLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += (bytes + 15) & ~(size_t)15; return at; };
-  const size_t kb = (size_t)npad * 8, ab = (size_t)N * TB_MAXDEP * 2;
-  L.keys = take(kb > ab ? kb : ab);
+  // at least 64 bytes per emitted row: bands of at least 512 rows
+  const size_t kb = (size_t)npad * 8, ab = (size_t)N * 64 + 64;
+  const size_t rb = kb > ab ? kb : ab;
+  L.keys = take(rb);
+  const size_t bits = rb * 8 - 64;   // two spare words for the 16-bit reads
+  L.band_rows = (int)(bits / (size_t)N < (size_t)N ? bits / (size_t)N : (size_t)N);
   L.ids = take((size_t)npad * 4);
   L.map = take((size_t)NT * 2);
   L.onode = take((size_t)N * 4);
   L.opar = take((size_t)N * 4);
-  L.odep = take((size_t)N * 4);
   L.canon = take((size_t)N * 4);
   L.hist = take((size_t)(256 + 8) * 4);   // radix histogram, then scalars
   L.skey = take((size_t)N * 8);           // selected keys (radix path)
@@ -89,21 +148,39 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
   int16_t *map = reinterpret_cast<int16_t *>(smem + L.map);       // [NT] node -> out index
   int32_t *onode = reinterpret_cast<int32_t *>(smem + L.onode);   // [N] out -> node
   int32_t *opar_s = reinterpret_cast<int32_t *>(smem + L.opar);   // [N]
-  int32_t *odep_s = reinterpret_cast<int32_t *>(smem + L.odep);   // [N]
   uint32_t *canon = reinterpret_cast<uint32_t *>(smem + L.canon); // [N] (depth, path) keys
-  int16_t *anc = reinterpret_cast<int16_t *>(smem + L.keys);      // [N][TB_MAXDEP], last
+  uint32_t *bm = reinterpret_cast<uint32_t *>(smem + L.keys);     // mask bitmap band, last
 
   // selection keys: fp32 key = score + beta*depth, rounded after each op
-  for (int i = tid; i < npad; i += TB_THREADS) {
-    uint64_t k = 0;
-    if (i < Nsa) {
-      const int n = i + 1;
-      const int dep = t.n_dep[nb + n];
-      const float key = __fadd_rn(t.n_score[nb + n], __fmul_rn(beta, (float)dep));
-      k = make_key(key, ((uint32_t)dep << 27) | t.n_lex[nb + n]);
+  // (the node fields of up to 8 strides loaded before any is used)
+  constexpr int KB_UNROLL = 8;
+  for (int i0 = tid; i0 < npad; i0 += TB_THREADS * KB_UNROLL) {
+    int dep[KB_UNROLL];
+    float sc[KB_UNROLL];
+    uint32_t lex[KB_UNROLL];
+#pragma unroll
+    for (int u = 0; u < KB_UNROLL; ++u) {
+      const int i = i0 + u * TB_THREADS;
+      dep[u] = 0; sc[u] = 0.f; lex[u] = 0u;
+      if (i < Nsa) {
+        dep[u] = t.n_dep[nb + i + 1];
+        sc[u] = t.n_score[nb + i + 1];
+        lex[u] = t.n_lex[nb + i + 1];
+      }
     }
-    keys[i] = k;
-    ids[i] = i + 1;
+#pragma unroll
+    for (int u = 0; u < KB_UNROLL; ++u) {
+      const int i = i0 + u * TB_THREADS;
+      if (i < npad) {
+        uint64_t k = 0;
+        if (i < Nsa) {
+          const float key = __fadd_rn(sc[u], __fmul_rn(beta, (float)dep[u]));
+          k = make_key(key, ((uint32_t)dep[u] << 27) | lex[u]);
+        }
+        keys[i] = k;
+        ids[i] = i + 1;
+      }
+    }
   }
   for (int i = tid; i < NT; i += TB_THREADS) map[i] = -1;
   __syncthreads();
@@ -124,9 +201,21 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
     for (int b = tid; b < 256; b += TB_THREADS) hist[b] = 0u;
     __syncthreads();
     for (int shift = 56; shift >= 0; shift -= 8) {
-      for (int i = tid; i < Nsa; i += TB_THREADS) {
-        const uint64_t k = keys[i];
-        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      // the keys' leading digits are mostly equal (scores of one range):
+      // the lanes sharing the first active lane's digit add once, together
+      for (int i0 = tid - lane; i0 < Nsa; i0 += TB_THREADS) {
+        const int i = i0 + lane;
+        const uint64_t k = i < Nsa ? keys[i] : 0ull;
+        const bool act = i < Nsa && (k & pmask) == prefix;
+        const uint32_t dg = (uint32_t)(k >> shift) & 255u;
+        const uint64_t live = __ballot(act);
+        if (live) {
+          const int lead = (int)__builtin_ctzll(live);
+          const uint32_t ld = (uint32_t)__shfl((int)dg, lead);
+          const uint64_t same = __ballot(act && dg == ld);
+          if (lane == lead) atomicAdd(&hist[ld], (uint32_t)__popcll(same));
+          if (act && dg != ld) atomicAdd(&hist[dg], 1u);
+        }
       }
       __syncthreads();
       if (tid < 64) {
@@ -170,34 +259,21 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
         }
       }
     __syncthreads();
-    for (int i = tid; i < Bsel; i += TB_THREADS) {
-      const uint64_t k = skey[i];
-      int rk = 0;
-      for (int j = 0; j < Bsel; ++j) rk += skey[j] > k ? 1 : 0;
-      if (rk < Bsel) onode[1 + rk] = ids[i];
+    const int tpn = split_width(Bsel);
+    const int part = tid & (tpn - 1);
+    for (int base = 0; base < Bsel; base += TB_THREADS / tpn) {
+      const int i = base + tid / tpn;
+      const uint64_t k = i < Bsel ? skey[i] : 0ull;
+      int rk = i < Bsel ? count_split<true>(skey, Bsel, k, part, tpn) : 0;
+      rk = sum_adjacent(rk, tpn);
+      if (i < Bsel && part == 0 && rk < Bsel) onode[1 + rk] = ids[i];
     }
   } else {
-    int tpn = 1;   // threads per node, a power of two
-    while (tpn * 2 * Nsa <= TB_THREADS && tpn < 16) tpn *= 2;
+    const int tpn = split_width(Nsa);   // Nsa <= TB_RANK_MAX: one pass
     const int i = tid / tpn, part = tid & (tpn - 1);
     const uint64_t ki = i < Nsa ? keys[i] : 0ull;
-    int cnt = 0;
-    const int per = (Nsa + tpn - 1) / tpn, j0 = part * per, j1 = min(Nsa, j0 + per);
-    int j = j0;
-    for (; j + 8 <= j1; j += 8) {
-      uint64_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = keys[j + u];
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) cnt += v[u] > ki;
-    }
-    for (; j < j1; ++j) cnt += keys[j] > ki;
-    // the tpn threads of a node are adjacent lanes
-    if (tpn >= 2) cnt += (int)xchg_u32<1>((uint32_t)cnt);
-    if (tpn >= 4) cnt += (int)xchg_u32<2>((uint32_t)cnt);
-    if (tpn >= 8) cnt += (int)xchg_u32<4>((uint32_t)cnt);
-    if (tpn >= 16) cnt += (int)xchg_u32<8>((uint32_t)cnt);
+    int cnt = i < Nsa ? count_split<true>(keys, Nsa, ki, part, tpn) : 0;
+    cnt = sum_adjacent(cnt, tpn);
     if (i < Nsa && part == 0) rank[i] = cnt;
     __syncthreads();
     for (int i2 = tid; i2 < Nsa; i2 += TB_THREADS)
@@ -214,13 +290,20 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
   for (int i = Bsel + tid; i < Bmax; i += TB_THREADS) t.sel[(size_t)q * Bmax + i] = -1;
   __syncthreads();
   // canonical position of each selected node (the keys are no longer needed)
-  for (int i = tid; i < Bsel; i += TB_THREADS) {
-    const uint32_t ci = canon[i];
-    int rk = 0;
-    for (int j = 0; j < Bsel; ++j) rk += canon[j] < ci;
-    const int n = onode[1 + i];
-    cpos[i] = make_int2(n, 1 + rk);
-    map[n] = (int16_t)(1 + rk);
+  {
+    const int tpn = split_width(Bsel);
+    const int part = tid & (tpn - 1);
+    for (int base = 0; base < Bsel; base += TB_THREADS / tpn) {
+      const int i = base + tid / tpn;
+      const uint32_t ci = i < Bsel ? canon[i] : 0u;
+      int rk = i < Bsel ? count_split<false>(canon, Bsel, ci, part, tpn) : 0;
+      rk = sum_adjacent(rk, tpn);
+      if (i < Bsel && part == 0) {
+        const int n = onode[1 + i];
+        cpos[i] = make_int2(n, 1 + rk);
+        map[n] = (int16_t)(1 + rk);
+      }
+    }
   }
   __syncthreads();
   for (int i = tid; i < Bsel; i += TB_THREADS) onode[cpos[i].y] = cpos[i].x;
@@ -244,38 +327,48 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
       odep[o] = dn;
       oscore[o] = t.n_score[nb + n];
       opar_s[i] = pi;
-      odep_s[i] = min(dn, TB_MAXDEP - 1);
     } else {
       otok[o] = -1; opar[o] = -1; odep[o] = -1; oscore[o] = -INFINITY;
       opar_s[i] = -1;
-      odep_s[i] = -1;
     }
   }
   if (tid == 0) on_nodes[q] = nn;
-  for (int i = tid; i < N * TB_MAXDEP; i += TB_THREADS) anc[i] = -1;
   __syncthreads();
 
-  // ancestor of every emitted node at each depth on its path (parents come
-  // first in canonical order, so the walk ends at the root)
-  for (int i = tid; i < nn; i += TB_THREADS) {
-    int x = i, steps = 0;
-    while (x >= 0 && steps < TB_MAXDEP) {
-      anc[i * TB_MAXDEP + odep_s[x]] = (int16_t)x;
-      x = x > 0 ? opar_s[x] : -1;
-      ++steps;
-    }
-  }
-  __syncthreads();
-  // mask[i][j] = 1 iff j is i or an ancestor of i
+  // mask[i][j] = 1 iff j is i or an ancestor of i: bands of rows as bitmaps
+  // (bit (i - r0) * N + j), every emitted node setting its chain's bits
+  // (parents come first in canonical order, so each walk ends at the root)
   uint8_t *mq = omask + (size_t)q * N * N;
-  for (int e = tid; e < N * N; e += TB_THREADS) {
-    const int i = e / N, j = e - i * N;
-    uint8_t v = 0;
-    if (i < nn && j < nn) {
-      const int dj = odep_s[j];
-      v = (dj <= odep_s[i] && anc[i * TB_MAXDEP + dj] == j) ? 1 : 0;
+  for (int r0 = 0; r0 < N; r0 += L.band_rows) {
+    const int r1 = min(N, r0 + L.band_rows);
+    const int nbits = (r1 - r0) * N;
+    const int nw = (nbits + 31) / 32 + 1;
+    for (int w = tid; w < nw; w += TB_THREADS) bm[w] = 0u;
+    __syncthreads();
+    for (int i = r0 + tid; i < min(r1, nn); i += TB_THREADS) {
+      const int row = (i - r0) * N;
+      int x = i, steps = 0;
+      while (x >= 0 && steps < TB_MAXDEP) {
+        atomicOr(&bm[(row + x) >> 5], 1u << ((row + x) & 31));
+        x = x > 0 ? opar_s[x] : -1;
+        ++steps;
+      }
     }
-    mq[e] = v;
+    __syncthreads();
+    uint8_t *g = mq + (size_t)r0 * N;
+    const int head = min(nbits, (int)((16u - ((uint32_t)reinterpret_cast<uintptr_t>(g) & 15u)) & 15u));
+    const int nchunk = (nbits - head) >> 4;
+    const int tail = head + (nchunk << 4);
+    for (int c = tid; c < nchunk; c += TB_THREADS) {
+      const int p = head + (c << 4), w = p >> 5;
+      const uint32_t b16 = __builtin_amdgcn_alignbit(bm[w + 1], bm[w], (uint32_t)(p & 31));
+      *reinterpret_cast<uint4 *>(g + p) = make_uint4(spread4(b16), spread4(b16 >> 4),
+                                                     spread4(b16 >> 8), spread4(b16 >> 12));
+    }
+    for (int e = tid; e < head; e += TB_THREADS) g[e] = (uint8_t)((bm[e >> 5] >> (e & 31)) & 1u);
+    for (int e = tail + tid; e < nbits; e += TB_THREADS)
+      g[e] = (uint8_t)((bm[e >> 5] >> (e & 31)) & 1u);
+    __syncthreads();   // the next band reuses the bitmap
   }
 }
 
