@@ -125,6 +125,55 @@ __device__ inline void block_bitonic_desc(uint64_t *keys, int32_t *vals, int n) 
   }
 }
 
+// ---------------------------------------------------------------- rank counts
+// threads per element when nt threads count ranks of n elements: a power of
+// two up to 16, all elements in one pass when they fit
+__device__ __forceinline__ int split_width(int n, int nt) {
+  int tpn = 1;
+  while (tpn * 2 * n <= nt && tpn < 16) tpn *= 2;
+  return tpn;
+}
+
+// part `part` of tpn of the count of a[0..n) ordered before x (greater if
+// GREATER, else smaller).  a is 16-byte aligned and the parts start at
+// multiples of 8 elements, so groups of 8 come in as 16-byte LDS reads.
+template <bool GREATER, typename T>
+__device__ __forceinline__ int count_split(const T *a, int n, T x, int part, int tpn) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit keys");
+  const int per = ((n + tpn - 1) / tpn + 7) & ~7, j0 = part * per, j1 = min(n, j0 + per);
+  int cnt = 0, j = j0;
+  for (; j + 8 <= j1; j += 8) {
+    constexpr int NV = 8 * (int)sizeof(T) / 16;
+    uint4 raw[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) raw[u] = reinterpret_cast<const uint4 *>(a + j)[u];
+    uint32_t w[4 * NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      w[4 * u] = raw[u].x; w[4 * u + 1] = raw[u].y; w[4 * u + 2] = raw[u].z; w[4 * u + 3] = raw[u].w;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      T v;
+      if constexpr (sizeof(T) == 8) v = ((uint64_t)w[2 * u + 1] << 32) | w[2 * u];
+      else v = w[u];
+      cnt += GREATER ? (v > x) : (v < x);
+    }
+  }
+  for (; j < j1; ++j) cnt += GREATER ? (a[j] > x) : (a[j] < x);
+  return cnt;
+}
+
+// sum over the tpn adjacent lanes of an element (every lane of the wave
+// takes part)
+__device__ __forceinline__ int sum_adjacent(int cnt, int tpn) {
+  if (tpn >= 2) cnt += (int)xchg_u32<1>((uint32_t)cnt);
+  if (tpn >= 4) cnt += (int)xchg_u32<2>((uint32_t)cnt);
+  if (tpn >= 8) cnt += (int)xchg_u32<4>((uint32_t)cnt);
+  if (tpn >= 16) cnt += (int)xchg_u32<8>((uint32_t)cnt);
+  return cnt;
+}
+
 __device__ __forceinline__ int next_pow2(int n) {
   int p = 1;
   while (p < n) p <<= 1;

@@ -480,8 +480,9 @@ __global__ __launch_bounds__(K1F_THREADS) void k1_lmhead_f32(
 // K1b: one workgroup per row selects the row's M best keys from its P lists.
 //
 // Each list guarantees that the row's M-th best key is >= its tau; M heads
-// are M distinct keys, so the M-th largest value among 64 (M > 64: 128) of
-// the heads is a bound as well.  tau, the largest of these bounds, can only be reached in lists
+// are M distinct keys, so the M-th largest value among 64 (M > 32: 256) of
+// the heads (the best of the lists l = slot mod 64 or 256) is a bound as
+// well; the larger sort costs more than it saves for small M.  tau, the largest of these bounds, can only be reached in lists
 // whose head reaches it (at most M of them), and usually by only a few more
 // than M keys: those are gathered in LDS and each one's rank among them is
 // counted.  If more than K1B_FAST keys pass (heavy ties), the exact M-th
@@ -561,8 +562,8 @@ __global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
       bitonic_sort32<NR, 2>(v, hl);
       return (uint64_t)bitonic_elem<NR>(v, M - 1) << 32;
     };
-    const uint64_t th = M <= 64 ? bound(std::integral_constant<int, 2>())
-                                : bound(std::integral_constant<int, 4>());
+    const uint64_t th = M <= 32 ? bound(std::integral_constant<int, 2>())
+                                : bound(std::integral_constant<int, 8>());
     t = th > t ? th : t;
   }
   const uint64_t tau = block_max(t);
@@ -623,11 +624,14 @@ __global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
     gather(lo);
     n = min(ncand, K1B_FAST);
   }
-  for (int i = tid; i < n; i += nt) {
-    const uint64_t k = cand[i];
-    int rk = 0;
-    for (int j = 0; j < n; ++j) rk += cand[j] > k ? 1 : 0;
-    if (rk < M) {
+  // rank of each gathered key among them (keys are distinct)
+  const int tpn = split_width(n, nt), sub = tid & (tpn - 1);
+  for (int b0 = 0; b0 < n; b0 += nt / tpn) {
+    const int i = b0 + tid / tpn;
+    const uint64_t k = i < n ? cand[i] : 0ull;
+    int rk = i < n ? count_split<true>(cand, n, k, sub, tpn) : 0;
+    rk = sum_adjacent(rk, tpn);
+    if (i < n && sub == 0 && rk < M) {
       C[(size_t)row * M + rk] = (int32_t)key_tie(k);
       Cl[(size_t)row * M + rk] = key_val(k);
     }
