@@ -218,7 +218,10 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
       const uint64_t k = i < Bsel ? skey[i] : 0ull;
       int rk = i < Bsel ? count_split<true>(skey, Bsel, k, part, tpn) : 0;
       rk = sum_adjacent(rk, tpn);
-      if (i < Bsel && part == 0 && rk < Bsel) onode[1 + rk] = ids[i];
+      if (i < Bsel && part == 0 && rk < Bsel) {
+        onode[1 + rk] = ids[i];
+        canon[rk] = key_tie(k);
+      }
     }
   } else {
     const int tpn = split_width(Nsa, TB_THREADS);   // Nsa <= TB_RANK_MAX: one pass
@@ -229,19 +232,27 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
     if (i < Nsa && part == 0) rank[i] = cnt;
     __syncthreads();
     for (int i2 = tid; i2 < Nsa; i2 += TB_THREADS)
-      if (rank[i2] < Bsel) onode[1 + rank[i2]] = i2 + 1;
+      if (rank[i2] < Bsel) {
+        onode[1 + rank[i2]] = i2 + 1;
+        canon[rank[i2]] = key_tie(keys[i2]);
+      }
   }
   __syncthreads();
 
-  // canonical order of the selected nodes: (depth, lexicographic path)
-  for (int i = tid; i < Bsel; i += TB_THREADS) {
-    const int n = onode[1 + i];
-    canon[i] = ((uint32_t)t.n_dep[nb + n] << 27) | t.n_lex[nb + n];
-    t.sel[(size_t)q * Bmax + i] = n;
+  // canonical order of the selected nodes: (depth, lexicographic path), the
+  // tie field of their keys (canon, in selection order); the node fields of
+  // each thread's first selected node load while the positions are counted
+  int my_par = 0, my_tok = 0;
+  float my_sc = 0.f;
+  if (tid < Bsel) {
+    const int n = onode[1 + tid];
+    my_par = t.n_par[nb + n];
+    my_tok = t.n_tok[nb + n];
+    my_sc = t.n_score[nb + n];
   }
+  for (int i = tid; i < Bsel; i += TB_THREADS) t.sel[(size_t)q * Bmax + i] = onode[1 + i];
   for (int i = Bsel + tid; i < Bmax; i += TB_THREADS) t.sel[(size_t)q * Bmax + i] = -1;
-  __syncthreads();
-  // canonical position of each selected node (the keys are no longer needed)
+  if (tid == 0) map[0] = 0;
   {
     const int tpn = split_width(Bsel, TB_THREADS);
     const int part = tid & (tpn - 1);
@@ -258,33 +269,42 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
     }
   }
   __syncthreads();
-  for (int i = tid; i < Bsel; i += TB_THREADS) onode[cpos[i].y] = cpos[i].x;
-  if (tid == 0) { map[0] = 0; onode[0] = 0; }
-  __syncthreads();
 
-  // outputs, parent re-indexing and the closure check
-  for (int i = tid; i < N; i += TB_THREADS) {
-    const size_t o = (size_t)q * N + i;
-    if (i < nn) {
-      const int n = onode[i];
-      const int pn = t.n_par[nb + n];
-      int pi = -1;
-      if (i > 0) {
-        pi = map[pn];
-        if (pi < 0) atomicOr(t.status, 1u);
-      }
-      const int dn = t.n_dep[nb + n];
-      otok[o] = t.n_tok[nb + n];
-      opar[o] = pi;
-      odep[o] = dn;
-      oscore[o] = t.n_score[nb + n];
-      opar_s[i] = pi;
-    } else {
-      otok[o] = -1; opar[o] = -1; odep[o] = -1; oscore[o] = -INFINITY;
-      opar_s[i] = -1;
-    }
+  // outputs at the canonical positions, parent re-indexing and the closure
+  // check (slot 0: the root)
+  if (tid == 0) {
+    const size_t o = (size_t)q * N;
+    otok[o] = t.n_tok[nb];
+    opar[o] = -1;
+    odep[o] = t.n_dep[nb];
+    oscore[o] = t.n_score[nb];
+    opar_s[0] = -1;
+    on_nodes[q] = nn;
   }
-  if (tid == 0) on_nodes[q] = nn;
+  for (int i = tid; i < Bsel; i += TB_THREADS) {
+    int pn = my_par, tok = my_tok;
+    float sc = my_sc;
+    if (i >= TB_THREADS) {
+      const int n = cpos[i].x;
+      pn = t.n_par[nb + n];
+      tok = t.n_tok[nb + n];
+      sc = t.n_score[nb + n];
+    }
+    const int pos = cpos[i].y;
+    const int pi = map[pn];
+    if (pi < 0) atomicOr(t.status, 1u);
+    const size_t o = (size_t)q * N + pos;
+    otok[o] = tok;
+    opar[o] = pi;
+    odep[o] = (int32_t)(canon[i] >> 27);
+    oscore[o] = sc;
+    opar_s[pos] = pi;
+  }
+  for (int i = nn + tid; i < N; i += TB_THREADS) {
+    const size_t o = (size_t)q * N + i;
+    otok[o] = -1; opar[o] = -1; odep[o] = -1; oscore[o] = -INFINITY;
+    opar_s[i] = -1;
+  }
   __syncthreads();
 
   // mask[i][j] = 1 iff j is i or an ancestor of i: bands of rows as bitmaps

@@ -181,3 +181,13 @@ def test_persistent_launch_modes(gpu_lib):
     finally:
         rnd.close()
     check_config(x, cfg, "persistent launch modes", max_tie_frac=0.0)
+
+
+@pytest.mark.parametrize("B,beta", [(1200, -0.02), (1500, 0.0)])
+def test_large_tree_budget(gpu_lib, B, beta):
+    """Budgets past one workgroup's threads: 1364 superarbol nodes, B = 1200
+    (three mask bands of rows, rank counts over several passes, emitted nodes
+    past the 1024th) and B = 1500 (every node selected, empty tail slots)."""
+    cfg = synth.custom_config(cfg_id=9700 + B, d=64, V=600, e=16, s=16, r=8, D=6, M=8, K=4,
+                              W=128, B=B, beta=beta, batch=2, wtype="f32")
+    check_config(synth.make_inputs(cfg, 3), cfg, f"large budget B={B}", max_tie_frac=0.0)
