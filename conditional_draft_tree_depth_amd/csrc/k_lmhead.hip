@@ -884,9 +884,53 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lists_from_logits(
   const int ntV = (V + 15) >> 4;
   const int t0 = (int)((long long)ntV * y / P), t1 = (int)((long long)ntV * (y + 1) / P);
   const int c0 = t0 * 16, ncols = max(0, min(t1 * 16, V) - c0);
-  for (int i = threadIdx.x; i < nrow * ncols; i += blockDim.x) {
-    const int rr = i / ncols, c = i - rr * ncols;
-    Ls[rr * K1_MAXCOLS + c] = L[(size_t)(row0 + rr) * V + c0 + c];
+  // the slice's logits into LDS, up to LU loads per thread in flight (16-byte
+  // ones when every row segment starts 16-byte aligned: V % 4 == 0, c0 and
+  // ncols multiples of 4)
+  constexpr int LU = 8;
+  const int nt = blockDim.x;
+  if ((V & 3) == 0) {
+    const int nq = ncols >> 2, n4 = nrow * nq;
+    for (int i0 = threadIdx.x; i0 < n4; i0 += nt * LU) {
+      float4 v[LU];
+#pragma unroll
+      for (int u = 0; u < LU; ++u) {
+        const int i = i0 + u * nt;
+        if (i < n4) {
+          const int rr = i / nq, c = (i - rr * nq) * 4;
+          v[u] = *reinterpret_cast<const float4 *>(L + (size_t)(row0 + rr) * V + c0 + c);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < LU; ++u) {
+        const int i = i0 + u * nt;
+        if (i < n4) {
+          const int rr = i / nq, c = (i - rr * nq) * 4;
+          *reinterpret_cast<float4 *>(Ls + rr * K1_MAXCOLS + c) = v[u];
+        }
+      }
+    }
+  } else {
+    const int n1 = nrow * ncols;
+    for (int i0 = threadIdx.x; i0 < n1; i0 += nt * LU) {
+      float v[LU];
+#pragma unroll
+      for (int u = 0; u < LU; ++u) {
+        const int i = i0 + u * nt;
+        if (i < n1) {
+          const int rr = i / ncols, c = i - rr * ncols;
+          v[u] = L[(size_t)(row0 + rr) * V + c0 + c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < LU; ++u) {
+        const int i = i0 + u * nt;
+        if (i < n1) {
+          const int rr = i / ncols, c = i - rr * ncols;
+          Ls[rr * K1_MAXCOLS + c] = v[u];
+        }
+      }
+    }
   }
   __syncthreads();
   uint64_t *out = part + ((size_t)row0 * P + y) * K1_LSTRIDE;

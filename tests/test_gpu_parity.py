@@ -71,6 +71,10 @@ def test_random_small_shapes(gpu_lib, seed):
     # the three-plane states, tiled LM head with lists from the logits
     (5, 256, 128, 128, 64, 5, 64, 8, 32, 200, 8),
     (6, 128, 192, 256, 32, 4, 128, 4, 64, 150, 6),
+    # 32 hidden rows and M > 64: exact lists by bisection from the logits,
+    # V odd (4-byte logit loads) and V % 4 == 0 (16-byte loads)
+    (7, 128, 128, 128, 32, 4, 128, 4, 16, 120, 8),
+    (8, 256, 128, 128, 32, 4, 96, 4, 16, 120, 8),
 ])
 def test_mfma_product_paths(gpu_lib, seed, d, e, s, r, D, M, K, W, B, batch):
     """bf16 shapes whose products run on the MFMA kernels: the row-gathered
