@@ -892,21 +892,19 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lists_from_logits(
   if ((V & 3) == 0) {
     const int nq = ncols >> 2, n4 = nrow * nq;
     for (int i0 = threadIdx.x; i0 < n4; i0 += nt * LU) {
-      float4 v[LU];
+      f32x4 v[LU];
 #pragma unroll
       for (int u = 0; u < LU; ++u) {
-        const int i = i0 + u * nt;
-        if (i < n4) {
-          const int rr = i / nq, c = (i - rr * nq) * 4;
-          v[u] = *reinterpret_cast<const float4 *>(L + (size_t)(row0 + rr) * V + c0 + c);
-        }
+        const int i = min(i0 + u * nt, n4 - 1);   // (a repeated load past the end)
+        const int rr = i / nq, c = (i - rr * nq) * 4;
+        v[u] = *reinterpret_cast<const f32x4 *>(L + (size_t)(row0 + rr) * V + c0 + c);
       }
 #pragma unroll
       for (int u = 0; u < LU; ++u) {
         const int i = i0 + u * nt;
         if (i < n4) {
           const int rr = i / nq, c = (i - rr * nq) * 4;
-          *reinterpret_cast<float4 *>(Ls + rr * K1_MAXCOLS + c) = v[u];
+          *reinterpret_cast<f32x4 *>(Ls + rr * K1_MAXCOLS + c) = v[u];
         }
       }
     }
@@ -916,11 +914,9 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lists_from_logits(
       float v[LU];
 #pragma unroll
       for (int u = 0; u < LU; ++u) {
-        const int i = i0 + u * nt;
-        if (i < n1) {
-          const int rr = i / ncols, c = i - rr * ncols;
-          v[u] = L[(size_t)(row0 + rr) * V + c0 + c];
-        }
+        const int i = min(i0 + u * nt, n1 - 1);
+        const int rr = i / ncols, c = i - rr * ncols;
+        v[u] = L[(size_t)(row0 + rr) * V + c0 + c];
       }
 #pragma unroll
       for (int u = 0; u < LU; ++u) {
