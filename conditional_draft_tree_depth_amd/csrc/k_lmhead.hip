@@ -874,13 +874,16 @@ __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int
 // The candidate list of (16-row block, vocabulary slice y) from logits in
 // memory: the slice's logits go to LDS and the LM-head kernel's epilogue
 // runs on them unchanged (slices cover the vocabulary tiles only).
+// 8 rows (4 waves) per workgroup: two or more workgroups per CU, so that one
+// workgroup's loads overlap another's selection
+constexpr int LS_ROWS = 8;
 template <bool BISECT>
-__global__ __launch_bounds__(K1_WAVES * 64) void k1_lists_from_logits(
+__global__ __launch_bounds__(LS_ROWS / 2 * 64) void k1_lists_from_logits(
     const float *__restrict__ L, int rows, int V, int M, uint64_t *__restrict__ part) {
   extern __shared__ __align__(16) uint8_t smem[];
   float *Ls = reinterpret_cast<float *>(smem);
-  const int P = gridDim.y, y = blockIdx.y, row0 = blockIdx.x * 16;
-  const int nrow = min(16, rows - row0);
+  const int P = gridDim.y, y = blockIdx.y, row0 = blockIdx.x * LS_ROWS;
+  const int nrow = min(LS_ROWS, rows - row0);
   const int ntV = (V + 15) >> 4;
   const int t0 = (int)((long long)ntV * y / P), t1 = (int)((long long)ntV * (y + 1) / P);
   const int c0 = t0 * 16, ncols = max(0, min(t1 * 16, V) - c0);
@@ -1009,12 +1012,12 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
   if (e != hipSuccess) return e;
   // (exact lists for M > 64: a kernel of its own, with fewer registers)
   if (a.M > 64)
-    hipExtLaunchKernelGGL(k1_lists_from_logits<true>, dim3(rows_pad / 16, a.P),
-                          dim3(K1_WAVES * 64), (uint32_t)(16 * K1_MAXCOLS * 4), st, nullptr, ev1,
+    hipExtLaunchKernelGGL(k1_lists_from_logits<true>, dim3((a.rows + LS_ROWS - 1) / LS_ROWS, a.P),
+                          dim3(LS_ROWS / 2 * 64), (uint32_t)(LS_ROWS * K1_MAXCOLS * 4), st, nullptr, ev1,
                           0u, (const float *)logits, a.rows, a.V, a.M, a.part);
   else
-    hipExtLaunchKernelGGL(k1_lists_from_logits<false>, dim3(rows_pad / 16, a.P),
-                          dim3(K1_WAVES * 64), (uint32_t)(16 * K1_MAXCOLS * 4), st, nullptr, ev1,
+    hipExtLaunchKernelGGL(k1_lists_from_logits<false>, dim3((a.rows + LS_ROWS - 1) / LS_ROWS, a.P),
+                          dim3(LS_ROWS / 2 * 64), (uint32_t)(LS_ROWS * K1_MAXCOLS * 4), st, nullptr, ev1,
                           0u, (const float *)logits, a.rows, a.V, a.M, a.part);
   return hipGetLastError();
 }
