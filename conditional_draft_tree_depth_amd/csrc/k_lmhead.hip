@@ -776,7 +776,9 @@ __global__ __launch_bounds__(LT_THREADS) void k1_logits_tiled(
 // is v (keys are distinct, so count(keys >= T) >= M holds exactly for
 // T <= K; each step is one comparison per held key and a half-wave sum);
 // where exactly M keys reach v, K is the one of value v with the smallest
-// tie field.
+// tie field.  The value search stops early once a step's count is exactly M
+// (for every row of the wave): that value, with tie field 0, bounds exactly
+// the M best keys, and it is the list's bound instead of K.
 // The keys >= K, exactly M of them, are written unsorted with K as the
 // list's bound, the best key and the count (the layout of the fast path).
 // A slice with fewer than M keys writes all of them with a zero bound.
@@ -809,13 +811,20 @@ __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int
     auto tie_of = [&](int i) { return 0xFFFFFFFFu - (uint32_t)(col0 + hl + 32 * i); };
     uint64_t T = 0;   // the M-th largest key (0: fewer than M keys)
     if (ncols > M) {
+      // (a step whose count is exactly M has found a value bound with
+      // exactly M keys at or above it: once every row of the wave has one,
+      // the search stops and that bound is the list's)
       uint32_t tv = 0;
+      bool sep = false;
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = tv | (1u << bit);
         int c = 0;
 #pragma unroll
         for (int i = 0; i < KPL; ++i) c += hv[i] >= cand ? 1 : 0;
-        if (total(c) >= M) tv = cand;
+        const int tc = total(c);
+        if (tc >= M) tv = cand;
+        sep = sep || tc == M;
+        if (__all(!active || sep)) break;
       }
       int cgt = 0, cge = 0;
       uint64_t ntie = 0;   // largest complemented tie among the keys of value tv
@@ -841,7 +850,7 @@ __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int
           if (total(c) >= need) tt = cand;
         }
       }
-      T = ((uint64_t)tv << 32) | tt;
+      T = sep ? (uint64_t)tv << 32 : ((uint64_t)tv << 32) | tt;
     }
     const uint64_t lo = T ? T : 1ull;   // key 0 marks an empty column
     int c = 0;
