@@ -7,8 +7,10 @@ for one batch of synthetic inputs (seeded, shapes of the named workload).
 
 Prints ONE JSON line (rank 0).  ``value`` comes from K timed steps with
 nothing else on the stream.  ``roofline`` is for the dominant kernel (the
-LM-head GEMM with its fused per-slice Top-M), timed over a second pass of K
-steps with HIP events on the round's own stream (the library records them
+LM-head kernel the workload runs: the streaming GEMM with its fused
+per-slice Top-M, or the tiled product with 32 or more hidden rows, against
+the HBM or MFMA peak its arithmetic intensity puts it under), timed over a
+second pass of K steps with HIP events on the round's own stream (the library records them
 between stages; the LM-head kernel's pair is taken at the kernel's own start
 and end, as a kernel trace measures it); ``cpu_baseline`` times the CPU oracle on a bounded sample
 of the same workload.
@@ -52,15 +54,59 @@ def algorithmic_counts(cfg):
                 round_flops=round_flops)
 
 
+def dominant_kernel(cfg):
+    """The LM-head kernel this workload runs, the roofline that binds it and
+    its algorithmic work per launch (one launch covers the whole vocabulary
+    for all b * D hidden rows).
+
+    Fewer than 32 hidden rows: the streaming kernel with the fused per-slice
+    Top-M (the logits never leave the chip): HBM-bound, bytes = W_lm + bias
+    + H.  32 or more rows (bf16): the tiled product writing the logits; its
+    arithmetic intensity 2 rows d V / (2 V d + 2 rows d + 4 rows V) decides
+    the bound against the ridge of the published peaks."""
+    es = 2 if cfg.wtype == "bf16" else 4
+    rows = cfg.batch * cfg.D
+    d, V = cfg.d, cfg.V
+    if cfg.wtype == "bf16" and rows >= 32 and d % 64 == 0:
+        flops = 2 * rows * d * V
+        nbytes = 2 * V * d + 2 * rows * d + 4 * V + 4 * rows * V
+        ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if flops / nbytes >= ridge:
+            return dict(kernel="k1_logits_tiled", label="tiled bf16 MFMA LM-head product",
+                        bound="mfma", work=flops, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                        scale=1e12)
+        return dict(kernel="k1_logits_tiled", label="tiled bf16 MFMA LM-head product",
+                    bound="hbm", work=nbytes, peak=HBM_PEAK_GBS, unit="GB/s", scale=1e9)
+    name = "k1_lmhead_bf16" if cfg.wtype == "bf16" else "k1_lmhead_f32"
+    return dict(kernel=name, label="LM-head GEMM + fused per-slice Top-M", bound="hbm",
+                work=es * V * d + 4 * V + 4 * rows * d, peak=HBM_PEAK_GBS, unit="GB/s",
+                scale=1e9)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _src_sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counters_traffic(workload, per_launch_div=1):
-    """HBM bytes of the LM-head kernel from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"k1_lmhead_{workload}_counters.json")
+def counters_traffic(workload, kernel="k1_lmhead_bf16"):
+    """HBM bytes per launch of the LM-head kernel from the committed
+    rocprofv3 counter summary of this workload, if it was taken on the
+    current kernel source; else None."""
+    stem = {"k1_lmhead_bf16": "k1_lmhead", "k1_logits_tiled": "k1_logits_tiled"}.get(kernel)
+    if stem is None:
+        return None
+    path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -90,7 +136,9 @@ def cpu_baseline(cfg, inputs, budget_s=12.0, max_rounds=50, scoring="conditional
         el = time.perf_counter() - t0
         if el >= budget_s or n >= max_rounds:
             break
-    return {"value": n / el, "unit": "rounds/s", "cores": threads or len(os.sched_getaffinity(0)),
+    return {"value": n / el, "unit": "rounds/s",
+            "cores": threads or len(os.sched_getaffinity(0)),
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{n} full {cfg.name} round(s) (numpy float64 oracle: LM head, "
                       f"superarbol, global Top-B, emission; literal-heap check off), {el:.1f} s"}
@@ -206,8 +254,9 @@ def main():
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     cnt = algorithmic_counts(cfg)
     k1_ms = stage_ms["lmhead_topm"] / max(nrec, 1)
-    k1_gbs = cnt["k1_bytes"] / (k1_ms * 1e-3) / 1e9
-    traffic = counters_traffic(cfg.name)
+    dk = dominant_kernel(cfg)
+    k1_rate = dk["work"] / (k1_ms * 1e-3) / dk["scale"]
+    traffic = counters_traffic(cfg.name, dk["kernel"])
     t_roof = max(cnt["round_bytes"] / (HBM_PEAK_GBS * 1e9),
                  cnt["round_flops"] / (BF16_PEAK_TFLOPS * 1e12))
     line = {
@@ -228,11 +277,13 @@ def main():
                    "r": cfg.r, "D": cfg.D, "M": cfg.M, "K": cfg.K, "W": cfg.W, "B": cfg.B,
                    "beta": cfg.beta, "batch": cfg.batch, "weights": cfg.wtype,
                    "scoring": args.scoring},
-        "roofline": {"bound": "hbm",
-                     "kernel": "k1_lmhead_bf16 (LM-head GEMM + fused per-slice Top-M)",
-                     "achieved": k1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": k1_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "bytes_per_launch": cnt["k1_bytes"], "us_per_launch": k1_ms * 1e3},
+        "roofline": {"bound": dk["bound"],
+                     "kernel": f"{dk['kernel']} ({dk['label']})",
+                     "achieved": k1_rate, "peak": dk["peak"], "unit": dk["unit"],
+                     "frac": k1_rate / dk["peak"], "traffic": traffic,
+                     ("bytes_per_launch" if dk["bound"] == "hbm" else "flops_per_launch"):
+                         dk["work"],
+                     "us_per_launch": k1_ms * 1e3},
         "round_roofline": {"t_roof_us": t_roof * 1e6, "frac": t_roof / (ms * 1e-3),
                            "bytes": cnt["round_bytes"], "flops": cnt["round_flops"]},
         "stages_us": {k: v * 1e3 / max(nrec, 1) for k, v in stage_ms.items()},

@@ -458,7 +458,9 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
       else if ((size_t)ncand <= ws.gi_rows && ncand <= 4096) precomp = 1;
     }
     if (precomp == 2) {
-      HIPCHK(ctx, launch_token_dedupe(ncand, ws.C, ws.first_row, ++ctx->tok_epoch, ws.lpos,
+      // the epoch runs 1 .. 2^32 - 1, then starts again at 1 (which clears the table)
+      if (++ctx->tok_epoch == 0u) ctx->tok_epoch = 1u;
+      HIPCHK(ctx, launch_token_dedupe(ncand, ws.C, ws.first_row, w.V, ctx->tok_epoch, ws.lpos,
                                       ws.btot, ws.cidx_tmp, ws.uniq, ws.rowmap, ws.ucount, st));
       HIPCHK(ctx, launch_gemm(gu, st));
     } else if (precomp == 1) {

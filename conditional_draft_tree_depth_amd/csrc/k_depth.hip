@@ -1,4 +1,4 @@
-// Per-depth kernels of the depth-wise build (DARTree page, Methodology 1):
+// Per-depth kernels of the depth-wise build (DARTree page, Metodología 1):
 // batched correction of every active branch, per-branch log-softmax and
 // Top-K children, and the Top-W survivors of the depth.
 //
@@ -19,7 +19,7 @@ constexpr int CL_BR = 4;         // expanded branches per correction workgroup
 
 // Corrected logits of the depth's candidates for every expanded branch:
 //   ell[a][j] = Cl[j] + W2[C[j]] . u_a
-// ("Resumen Técnico: Domino", Methodology 2: L = L_base + Delta L with the
+// ("Resumen Técnico: Domino", Metodología 2: L = L_base + Delta L with the
 // low-rank map back to the vocabulary; "Resumen Técnico: DominoTree", Main
 // components 2: only the r x M slice of W2 for the Top-M candidates is
 // used).  One workgroup per (request, group of CL_BR branches) stages that
@@ -167,10 +167,10 @@ __device__ __forceinline__ int count_greater(const T *keys, int n, T kc) {
 //     corrected logits, Top-K children (log-prob desc, token asc) by rank
 //     counting, child score = parent score + log-prob; every child is
 //     appended to the
-//     superarbol ("Resumen Técnico: DominoTree", Main components 2; DARTree
-//     page, Methodology 1, scoring by corrected cumulative probability);
+//     superarbol ("Resumen Técnico: DominoTree", Componentes Principales 2; DARTree
+//     page, Metodología 1, scoring by corrected cumulative probability);
 //  2. Top-W of the depth's children by (score desc, token path asc) become
-//     the next expanded branches (DARTree page, Methodology 1, retention);
+//     the next expanded branches (DARTree page, Metodología 1, retention);
 //  3. the survivors' lexicographic ranks among themselves, and the gathers
 //     the GRU step needs (token and parent state slot).
 __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int W, int D,
@@ -460,8 +460,8 @@ hipError_t launch_select_corr(int b, int A, int M, int K, int W, int D, int delt
 // once; each expanded branch a gets children a * K + k, k < K, with the
 // candidate of rank k and score fp32(score(a) + lp); then the Top-W
 // survivors and their lexicographic ranks, carried to the next depth in LDS.
-// Same rules and tie-breaks as k_select (DARTree page, Methodology 1;
-// "Resumen Técnico: DominoTree", Main components 2).
+// Same rules and tie-breaks as k_select (DARTree page, Metodología 1;
+// "Resumen Técnico: DominoTree", Componentes Principales 2).
 __global__ __launch_bounds__(SEL_THREADS) void k_select_marginal(int M, int K, int W, int D,
                                                                  const int32_t *__restrict__ C,
                                                                  const float *__restrict__ Cl,

@@ -3,7 +3,7 @@
 //
 // Used for the path-independent projection uH = W1[:, :d] Hq, the per-branch
 // part W1[:, d:] S of the low-rank head ("Resumen Técnico: Domino",
-// Methodology 2: [H_i ; S_{i-1}] is projected to rank r), and the GRU input
+// Metodología 2: [H_i ; S_{i-1}] is projected to rank r), and the GRU input
 // and state projections.  fp32 activations are never rounded to bf16 (the
 // GRU state enters the matrix cores as an exact three-term bf16 split);
 // accumulation is fp32.  Three kernels: bf16 weights with fewer than 256
@@ -570,13 +570,23 @@ __global__ void k_token_map(int n, const int32_t *__restrict__ tok,
   rowmap[i] = cidx[rep];
 }
 
-hipError_t launch_token_dedupe(int n, const int32_t *tok, void *first, uint32_t epoch,
+__global__ void k_zero_u64(unsigned long long *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
+hipError_t launch_token_dedupe(int n, const int32_t *tok, void *first, int V, uint32_t epoch,
                                int32_t *lpos, int32_t *btot, int32_t *cidx, int32_t *uniq,
                                int32_t *rowmap, int32_t *count, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   const int nb = (n + TD_B - 1) / TD_B;
   if (nb > 1024) return hipErrorInvalidValue;
   auto *f = static_cast<unsigned long long *>(first);
+  // epoch 1 starts a new cycle of the 32-bit epoch: tags left by the last
+  // cycle would outrank it, so the table is cleared first (a kernel, so the
+  // round stays free of memset nodes under graph capture)
+  if (epoch == 1u)
+    hipLaunchKernelGGL(k_zero_u64, dim3((V + 255) / 256), dim3(256), 0, st, f, V);
   hipLaunchKernelGGL(k_token_mark, dim3(nb), dim3(TD_B), 0, st, n, tok, f, epoch);
   hipLaunchKernelGGL(k_token_scan, dim3(nb), dim3(TD_B), 0, st, n, tok, f, epoch, lpos, btot);
   hipLaunchKernelGGL(k_token_bases, dim3(1), dim3(1024), 0, st, nb, btot, count);

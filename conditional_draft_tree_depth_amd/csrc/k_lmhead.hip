@@ -2,10 +2,10 @@
 //
 // Base logits L_base = Hq . W_lm^T (+ bias) come from the backbone's shared
 // hidden states through the frozen target LM head ("Resumen Técnico:
-// Domino", Methodology 1); they are path-independent, so one pass serves
-// every branch ("Resumen Técnico: DominoTree", Main components 1).  Only the
+// Domino", Metodología 1); they are path-independent, so one pass serves
+// every branch ("Resumen Técnico: DominoTree", Componentes Principales 1).  Only the
 // Top-M of each row is kept ("Resumen Técnico: DominoTree", Main
-// components 2; DARTree page, Methodology 1, candidate selection): the
+// components 2; DARTree page, Metodología 1, candidate selection): the
 // vocabulary-wide logits are never written to memory.
 //
 // bf16 path: every wave multiplies 16-token tiles of W_lm (MFMA A operand,
@@ -1013,8 +1013,10 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
                                hipEvent_t ev1) {
   const int rows_pad = (a.rows + 15) & ~15;
   const int ntm = (a.rows + LT_BM - 1) / LT_BM, ntn = (a.V + LT_BN - 1) / LT_BN;
+  // the kernel's own start and end events time the product alone (the list
+  // kernel falls into the next stage)
   hipExtLaunchKernelGGL(k1_logits_tiled, dim3(ntm * ntn), dim3(LT_THREADS), (uint32_t)LT_SMEM, st,
-                        ev0, nullptr,
+                        ev0, ev1,
                         0u, (const uint16_t *)a.Hb, a.rows, rows_pad, a.d,
                         static_cast<const uint16_t *>(a.W), a.V, a.bias, logits);
   hipError_t e = hipGetLastError();
@@ -1022,11 +1024,11 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
   // (exact lists for M > 64: a kernel of its own, with fewer registers)
   if (a.M > 64)
     hipExtLaunchKernelGGL(k1_lists_from_logits<true>, dim3((a.rows + LS_ROWS - 1) / LS_ROWS, a.P),
-                          dim3(LS_ROWS / 2 * 64), (uint32_t)(LS_ROWS * K1_MAXCOLS * 4), st, nullptr, ev1,
+                          dim3(LS_ROWS / 2 * 64), (uint32_t)(LS_ROWS * K1_MAXCOLS * 4), st, nullptr, nullptr,
                           0u, (const float *)logits, a.rows, a.V, a.M, a.part);
   else
     hipExtLaunchKernelGGL(k1_lists_from_logits<false>, dim3((a.rows + LS_ROWS - 1) / LS_ROWS, a.P),
-                          dim3(LS_ROWS / 2 * 64), (uint32_t)(LS_ROWS * K1_MAXCOLS * 4), st, nullptr, ev1,
+                          dim3(LS_ROWS / 2 * 64), (uint32_t)(LS_ROWS * K1_MAXCOLS * 4), st, nullptr, nullptr,
                           0u, (const float *)logits, a.rows, a.V, a.M, a.part);
   return hipGetLastError();
 }

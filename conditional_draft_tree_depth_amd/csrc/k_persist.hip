@@ -1,6 +1,6 @@
 // Depth loop of the depth-wise build as ONE persistent kernel (small batches).
 //
-// The low-rank head is linear ("Resumen Técnico: Domino", Methodology 2), so
+// The low-rank head is linear ("Resumen Técnico: Domino", Metodología 2), so
 // the corrected logits of candidate j for a branch with state S are
 //   ell_j = Cl_j + W2[C_j] . (uH + W1[:, d:] S) = g_j + G_j . S,
 // with g = Cl + W2[C] uH and G = W2[C] W1[:, d:] fixed for the round once the
@@ -15,7 +15,7 @@
 // G_j . S over its own units and raises its arrival flag; once every flag is
 // up, every consumer adds the partials in the same fixed order and runs the
 // same selection (log-softmax over M, Top-K per branch, Top-W per request;
-// DARTree page, Methodology 1), so one grid-wide hand-off per depth suffices.
+// DARTree page, Metodología 1), so one grid-wide hand-off per depth suffices.
 //
 // GRU products run on MFMA: weights are the A operand, activations the B
 // operand; the fp32 state is split exactly into three bf16 terms.
@@ -230,7 +230,7 @@ __device__ __forceinline__ void pk_raise(uint32_t *flag, uint32_t epoch) {
 }
 
 // Threads i < n poll flags[i * 64] >= epoch, threads 64 .. 64 + npf - 1 poll
-// pf[(i - 64) * 64] >= pepoch; false if any wait exceeded the spin limit
+// pf[(i - 64) * 64] >= pepoch (">=" modulo 2^32: the epoch wraps); false if any wait exceeded the spin limit
 // (status bit 1 is then set, 1 is stored to the host-visible word host_fail,
 // and the caller leaves).  A wait can only run out if some workgroup of the
 // grid never became resident next to the waiting ones.
@@ -247,7 +247,8 @@ __device__ __forceinline__ bool pk_wait(const uint32_t *flags, int n, uint32_t e
   else if (tid >= 64 && tid < 64 + npf) { f = pf + (tid - 64) * 64; want = pepoch; }
   if (f) {
     unsigned k = 0;
-    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+    // flags and epochs are 32-bit counters that wrap: compare by difference
+    while ((int32_t)(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - want) < 0) {
       if (++k > spin) {
         atomicOr(status, 2u);
         if (host_fail) __hip_atomic_store(host_fail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

@@ -1,14 +1,14 @@
 // K4: deferred pruning and the compact verification tree.
 //
-// DARTree page, Methodology 2: after the superarbol is built, ONE global
+// DARTree page, Metodología 2: after the superarbol is built, ONE global
 // Top-B over all its materialised prefixes (root excluded) replaces the
 // sequential best-first heap; with a non-positive depth bonus beta the key
 // score + beta * depth never increases from a node to its children, which
 // is why (Lemma 1) the selected set equals the heap's and is closed under
 // parents.  The selected nodes are emitted in canonical order (depth, then
 // token path), parents re-indexed, with the ancestor-or-self mask that
-// tree-attention verification uses ("Resumen Técnico: DominoTree", Main
-// components 5).  The closure is checked; a violation sets status bit 0.
+// tree-attention verification uses ("Resumen Técnico: DominoTree",
+// Componentes Principales 5).  The closure is checked; a violation sets status bit 0.
 //
 // One workgroup per request.  Selection: up to TB_RANK_MAX nodes, the rank
 // of every node among all keys is counted directly (a few threads per node);
@@ -279,7 +279,9 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
     odep[o] = t.n_dep[nb];
     oscore[o] = t.n_score[nb];
     opar_s[0] = -1;
-    on_nodes[q] = nn;
+    // a round whose persistent depth loop could not run (status bit 1)
+    // marks itself: n_nodes = 0
+    on_nodes[q] = (*t.status & 2u) ? 0 : nn;
   }
   for (int i = tid; i < Bsel; i += TB_THREADS) {
     int pn = my_par, tok = my_tok;

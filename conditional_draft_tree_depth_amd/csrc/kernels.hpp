@@ -124,10 +124,11 @@ hipError_t launch_gru_combine(int R, int s, const float *gi, const int32_t *gidx
                               const int32_t *pidx, float *Snew, uint16_t *S3, hipStream_t st);
 hipError_t gemm_prepare();
 // Distinct tokens of tok[0..n) (n <= 262144): uniq[0..*count) in order of
-// first occurrence, rowmap[i] = position of tok[i] in uniq.  first [V] u64
-// starts zeroed; epoch must grow from round to round (>= 1); lpos, cidx [n]
-// and btot [n / 256 + 1] are scratch.
-hipError_t launch_token_dedupe(int n, const int32_t *tok, void *first, uint32_t epoch,
+// first occurrence, rowmap[i] = position of tok[i] in uniq.  first [V] u64;
+// epoch must grow by one from round to round, starting at 1 (and again at 1
+// after it wraps: epoch 1 clears first); lpos, cidx [n] and btot
+// [n / 256 + 1] are scratch.
+hipError_t launch_token_dedupe(int n, const int32_t *tok, void *first, int V, uint32_t epoch,
                                int32_t *lpos, int32_t *btot, int32_t *cidx, int32_t *uniq,
                                int32_t *rowmap, int32_t *count, hipStream_t st);
 // true when launch_gemm runs a as a tiled product (many rows, bf16 operands)

@@ -3,18 +3,18 @@
  * construction on an AMD Instinct MI355X (gfx950).
  *
  * The operation (pages cited by title and section):
- *   * "Resumen Técnico: Domino", Methodology 1 and 2: base logits
+ *   * "Resumen Técnico: Domino", Metodología 1 and 2: base logits
  *     L_base = H . W_lm (+ bias) from the shared hidden states H of the draft
  *     block; a GRU folds the embeddings of the preceding draft tokens into a
  *     causal state S; a low-rank head maps [H_i ; S_{i-1}] to rank r (W1) and
  *     back to vocabulary space (W2) giving Delta L_i; L = L_base + Delta L.
- *   * "Resumen Técnico: DominoTree", Main components 1, 2 and 5: children are
+ *   * "Resumen Técnico: DominoTree", Componentes Principales 1, 2 and 5: children are
  *     scored by the path's own correction; the correction is restricted to
  *     the Top-M marginal candidates of each depth (an r x M slice of W2)
  *     before the Top-k children are kept; verification uses tree attention
  *     with an ancestor-only mask.
  *   * "DARTree: Speculative Diffusion Decoding with Autoregressive Draft
- *     Trees", Methodology 1 and 2: the tree grows depth by depth; every
+ *     Trees", Metodología 1 and 2: the tree grows depth by depth; every
  *     active branch of a depth is corrected in one batch with its own prefix
  *     state; extensions are scored by corrected cumulative log-probability;
  *     the W best branches are kept and their states carried forward; the
@@ -141,10 +141,14 @@ dtree_status dtree_create(const dtree_weights *w, const dtree_caps *caps,
  * kernel whose workgroups wait on each other (each needs a whole CU).  It is
  * launched like any other kernel; should its workgroups not all become
  * resident together (another stream holding CUs for a long time), its waits
- * run out after a bounded time, that round's status gets bit 1, the next
- * dtree_build_round on the context returns DTREE_E_HIP without enqueueing
- * anything, and every later round uses cooperative launches, which
- * guarantee co-residency at a higher launch cost (about 18 us on MI355X).   */
+ * run out after a bounded time and that round fails: its n_nodes are 0 (a
+ * valid round has n_nodes >= 1, so a failed round marks itself in its own
+ * outputs even when rounds are queued back to back), its status gets bit 1,
+ * the next dtree_build_round on the context returns DTREE_E_HIP without
+ * enqueueing anything (once the failed round has run: the flag is read
+ * without synchronising), and every later round uses cooperative launches,
+ * which guarantee co-residency at a higher launch cost (about 18 us on
+ * MI355X).                                                                  */
 dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
                                int32_t batch, const float *H,
                                const int32_t *root, int32_t *tok,
@@ -168,13 +172,13 @@ dtree_status dtree_set_persistent_launch(dtree_ctx *ctx, int32_t cooperative,
  *   DTREE_SCORE_CONDITIONAL (0, the default): corrected logits
  *       L_base + Delta L, Delta L from the low-rank head over [H_i ; S] with
  *       the branch's own GRU state S ("Resumen Técnico: Domino",
- *       Methodology 2; DARTree page, Methodology 1);
+ *       Metodología 2; DARTree page, Metodología 1);
  *   DTREE_SCORE_MARGINAL (1): the path-independent base logits alone
  *       (Delta L = 0, no GRU state), the uncorrected DDTree-style scoring the
  *       pages compare against with the same drafter and tree construction
- *       ("Resumen Técnico: DominoTree", Evaluation, the conditionality
- *       ablation).  Everything else in the round is unchanged: Top-M per
- *       depth, log-softmax over M, Top-K, Top-W, global Top-B, mask.
+ *       ("Resumen Técnico: DominoTree", Contribuciones Clave, the ablation of
+ *       conditionality).  Everything else in the round is unchanged: Top-M
+ *       per depth, log-softmax over M, Top-K, Top-W, global Top-B, mask.
  * DTREE_E_ARG for other values.                                            */
 #define DTREE_SCORE_CONDITIONAL 0
 #define DTREE_SCORE_MARGINAL 1
@@ -207,7 +211,10 @@ dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace *out);
 /* Stage timing with HIP events recorded on the round's own stream.  When
  * enabled, every round records events between its stages:
  *   0 round start (bf16: hidden rows rounded once; empty with fp32 weights)
- *   1 base-logit GEMM with fused per-slice Top-M   2 Top-M merge
+ *   1 base-logit GEMM with fused per-slice Top-M (32 or more hidden rows:
+ *     the logits product alone, timed by the kernel's own start and end)
+ *   2 Top-M merge (32 or more hidden rows: the per-slice lists built from
+ *     the logits, then the merge)
  *   3 path-independent prologue (uH, correction tables or root GRU state)
  *   4 depth loop (correction, selection, GRU, all depths)
  *   5 global Top-B, canonical order and mask

@@ -106,3 +106,41 @@ class Brute:
 
         rec((), 0.0, 0)
         return out
+
+    def enumerate_markov(self):
+        """{path tuple: cumulative score} for every path of length 1..D under
+        the first-order (Markov) correction: the children of a node are
+        scored with the state the GRU reaches from a zero state after the
+        node's own last token alone (the root's token for the root)."""
+        zero = torch.zeros(self.s, dtype=torch.float64)
+        out = {}
+
+        def rec(path, last_tok, score, dd):
+            if dd == self.D:
+                return
+            lp = self.child_logprobs(dd, self.step_state(zero, last_tok))
+            for j, t in enumerate(self.C[dd]):
+                p2 = path + (t,)
+                out[p2] = score + float(lp[j])
+                rec(p2, t, out[p2], dd + 1)
+
+        rec((), self.root, 0.0, 0)
+        return out
+
+    def kary_tree(self, K, markov=False):
+        """{path: score} of the unpruned K-ary tree of depth D: every node's
+        children are the Top-K (log-prob desc, token asc) of its M one-token
+        extensions, scores recomputed from scratch along each path."""
+        allp = self.enumerate_markov() if markov else self.enumerate()
+        out = {}
+
+        def rec(path, dd):
+            if dd == self.D:
+                return
+            ext = {t: allp[path + (t,)] for t in self.C[dd]}
+            for t in sorted(ext, key=lambda t: (-ext[t], t))[:K]:
+                out[path + (t,)] = ext[t]
+                rec(path + (t,), dd + 1)
+
+        rec((), 0)
+        return out

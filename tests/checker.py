@@ -3,16 +3,27 @@
 Parity rule: tree structure (tokens, parents, depths, mask, node count) must
 be identical, scores within ``tol`` (1e-4 absolute, fp32 log-prob), and a
 selection may differ only where the competing values are within ``tol`` of
-the oracle's cutoff.  The two sides are compared stage by stage using the
-library's debug trace (candidate tables, superarbol, expanded nodes per
-depth, selected set), matching nodes by token path.  At the first stage
-whose sets differ, every differing item must sit within ``tol`` of the
-oracle's cutoff value (a tolerated near-tie); from there on the two runs
-legitimately diverge, so the rest of that request is checked for validity
-only (output invariants and self-consistency with its own trace).  The
-oracle never receives anything computed on the GPU.
+the oracle's cutoff (the DominoTree page, Resultados Experimentales: the
+method is exact except for floating-point tie-breaking).
+
+How a near-tie is handled.  The oracle records every selection decision of
+its own run (Top-M per depth, Top-K per expanded branch, Top-W per depth,
+the global Top-B) with the band of items within ``tol`` of its cutoff,
+computed from its own values only.  Its admissible alternatives at a
+decision are the sets X with  sure <= X <= sure | band,  |X| = n.  The
+checker walks the GPU's debug trace stage by stage in the order the round
+makes its decisions.  At the first decision where the GPU kept a different
+set, that set must be one of the oracle's admissible alternatives there;
+the oracle then builds the round again along that alternative -- all of its
+arithmetic its own -- and the walk restarts.  When every decision agrees,
+the whole tree is compared element by element: every superarbol node's
+score, the selected set, and the emitted tokens, parents, depths, mask and
+scores, to the last node.  Each followed alternative is reported as a
+tolerated tie with its stage and its distance from the cutoff.
 """
 import numpy as np
+
+from oracle import dtree_oracle as O
 
 
 class Mismatch(AssertionError):
@@ -56,108 +67,125 @@ def check_invariants(out, B, where=""):
         raise Mismatch(f"{where}not in canonical order")
 
 
-def _tie_ok(vals_by_item, diff, cutoff, tol):
-    return all(abs(vals_by_item[x] - cutoff) <= tol for x in diff)
+class _Gpu:
+    """The GPU round of one request, indexed by token path."""
+
+    def __init__(self, gout, gtr, B, where):
+        check_invariants(gout, B, where)
+        if gtr["status"] != 0:
+            raise Mismatch(f"{where}device status {gtr['status']}")
+        self.paths = _paths(gtr["node_tok"], gtr["node_parent"])
+        if len(set(self.paths)) != len(self.paths):
+            raise Mismatch(f"{where}GPU superarbol repeats a token path")
+        self.id = {p: i for i, p in enumerate(self.paths)}
+        self.score = {self.paths[i]: float(gtr["node_score"][i]) for i in range(1, len(self.paths))}
+        self.kids = {}
+        for i in range(1, len(self.paths)):
+            self.kids.setdefault(self.paths[i][:-1], []).append(self.paths[i])
+        self.C = [set(int(t) for t in row) for row in gtr["C"]]
+        self.Cl = gtr["Cl"]
+        self.Ctok = gtr["C"]
+        self.surv = [{self.paths[i] for i in row if i >= 0} for row in gtr["surv"]]
+        self.sel = {self.paths[int(x)] for x in gtr["sel"] if x >= 0}
+        # the emitted tree must be the GPU's own selection in canonical order
+        n = int(gout["n_nodes"])
+        if n != len(self.sel) + 1:
+            raise Mismatch(f"{where}n_nodes {n} vs {len(self.sel)} selected")
+        out_paths = _paths(gout["tok"][:n], gout["parent"][:n])
+        if set(out_paths[1:]) != self.sel:
+            raise Mismatch(f"{where}output is not the GPU's own selection")
+        for i in range(1, n):
+            if gout["score"][i] != np.float32(self.score[out_paths[i]]):
+                raise Mismatch(f"{where}output score differs from trace at {i}")
 
 
-def compare_request(gout, gtr, orc, prm, tol=1e-4, where=""):
-    """gout: GPU outputs of one request; gtr: its trace; orc: the oracle's
-    result for that request.  Returns a dict {'exact': bool, 'tie': str}."""
-    D, M, K, W, B = prm["D"], prm["M"], prm["K"], prm["W"], prm["B"]
+def _first_divergence(g, orc, prm, tol, where):
+    """(decision key, GPU's set) of the first decision where the GPU kept a
+    different set than the oracle's build, or None.  Values that are not
+    decisions (base logits, scores) must agree within tol on the way."""
+    D = prm["D"]
     sa = orc["sa"]
-    check_invariants(gout, B, where)
-    if gtr["status"] != 0:
-        raise Mismatch(f"{where}device status {gtr['status']}")
-
-    # GPU output must be the GPU's own selection in canonical order
-    gpaths = _paths(gtr["node_tok"], gtr["node_parent"])
-    n = int(gout["n_nodes"])
-    sel_ids = [int(x) for x in gtr["sel"] if x >= 0]
-    if n != len(sel_ids) + 1:
-        raise Mismatch(f"{where}n_nodes {n} vs {len(sel_ids)} selected")
-    out_paths = _paths(gout["tok"][:n], gout["parent"][:n])
-    if set(out_paths[1:]) != {gpaths[i] for i in sel_ids}:
-        raise Mismatch(f"{where}output is not the GPU's own selection")
-    gscore = {gpaths[i]: float(gtr["node_score"][i]) for i in range(1, len(gpaths))}
-    for i in range(1, n):
-        if gout["score"][i] != np.float32(gscore[out_paths[i]]):
-            raise Mismatch(f"{where}output score differs from trace at {i}")
-
-    # stage 1: candidate tables
+    Lb = orc["Lb"]
     for dd in range(D):
-        gs, os_ = set(gtr["C"][dd].tolist()), set(int(t) for t in sa["C"][dd])
-        lbt, lbv = orc["lb_sorted"][dd]
-        lb = {int(t): float(v) for t, v in zip(lbt, lbv)}
-        for j, t in enumerate(gtr["C"][dd]):
-            if int(t) in lb and abs(float(gtr["Cl"][dd][j]) - lb[int(t)]) > tol:
+        for j, t in enumerate(g.Ctok[dd]):
+            if abs(float(g.Cl[dd][j]) - float(Lb[dd][int(t)])) > tol:
                 raise Mismatch(f"{where}base logit of token {t} at depth {dd}")
-        if gs != os_:
-            diff = gs ^ os_
-            if not all(t in lb for t in diff) or not _tie_ok(lb, diff, float(sa["Cl"][dd][M - 1]), tol):
-                raise Mismatch(f"{where}candidates at depth {dd} differ beyond tolerance: {diff}")
-            return {"exact": False, "tie": f"top-M at depth {dd}"}
-
-    # stage 2: depth by depth
-    opath_id = {p: i for i, p in enumerate(sa["path"])}
-    gpath_id = {p: i for i, p in enumerate(gpaths)}
-    gkids = {}
-    for i in range(1, len(gpaths)):
-        gkids.setdefault(int(gtr["node_parent"][i]), []).append(i)
-    if set(gpaths) - set(opath_id):
-        extra = set(gpaths) - set(opath_id)
-    else:
-        extra = set()
+        if g.C[dd] != set(int(t) for t in sa["C"][dd]):
+            return ("M", dd), g.C[dd]
     for dd in range(D):
         pdp = sa["per_depth"][dd]
-        g_front = {gpaths[i] for i in gtr["surv"][dd] if i >= 0}
         o_front = {sa["path"][i] for i in pdp["frontier"]}
-        if g_front != o_front:
-            raise Mismatch(f"{where}expanded set at depth {dd} differs without a recorded tie")
-        for a, p in enumerate(pdp["frontier"]):
-            ppath = sa["path"][p]
+        if g.surv[dd] != o_front:
+            raise Mismatch(f"{where}expanded set at depth {dd} differs without a decision")
+        for p in pdp["frontier"]:
+            pp = sa["path"][p]
+            g_k = {c[-1] for c in g.kids.get(pp, [])}
             o_k = {sa["tok"][c] for c in sa["kids"][p]}
-            g_k = {gpaths[c][-1] for c in gkids.get(gpath_id[ppath], [])}
             if g_k != o_k:
-                lpm = {int(t): float(v) for t, v in zip(sa["C"][dd], pdp["lp"][a])}
-                order = sorted(lpm.values(), reverse=True)
-                if not _tie_ok(lpm, g_k ^ o_k, order[K - 1], tol):
-                    raise Mismatch(f"{where}children of {ppath} differ beyond tolerance")
-                return {"exact": False, "tie": f"top-K at depth {dd}"}
+                return ("K", dd, pp), g_k
         for c in pdp["children"]:
             cp = sa["path"][c]
-            if abs(gscore[cp] - sa["score"][c]) > tol:
-                raise Mismatch(f"{where}score of {cp}: gpu {gscore[cp]} oracle {sa['score'][c]}")
-        g_surv = {gpaths[i] for i in gtr["surv"][dd + 1] if i >= 0}
+            if cp not in g.score:
+                raise Mismatch(f"{where}GPU lacks superarbol node {cp}")
+            if abs(g.score[cp] - sa["score"][c]) > tol:
+                raise Mismatch(f"{where}score of {cp}: gpu {g.score[cp]} oracle {sa['score'][c]}")
         o_surv = {sa["path"][i] for i in pdp["survivors"]}
-        if g_surv != o_surv:
-            osc = {sa["path"][c]: sa["score"][c] for c in pdp["children"]}
-            cut = sorted(osc.values(), reverse=True)[len(o_surv) - 1]
-            if not _tie_ok(osc, g_surv ^ o_surv, cut, tol):
-                raise Mismatch(f"{where}survivors at depth {dd + 1} differ beyond tolerance")
-            return {"exact": False, "tie": f"top-W at depth {dd + 1}"}
-    if extra:
-        raise Mismatch(f"{where}GPU superarbol has paths the oracle lacks: {sorted(extra)[:3]}")
-    if len(gpaths) != len(sa["path"]):
-        raise Mismatch(f"{where}superarbol sizes {len(gpaths)} vs {len(sa['path'])}")
-
-    # stage 3: global Top-B
-    g_sel = {gpaths[i] for i in sel_ids}
+        if g.surv[dd + 1] != o_surv:
+            return ("W", dd + 1), g.surv[dd + 1]
+    if set(g.paths) != set(sa["path"]):
+        extra = sorted(set(g.paths) ^ set(sa["path"]))[:3]
+        raise Mismatch(f"{where}superarbols differ: {extra}")
     o_sel = {sa["path"][i] for i in orc["sel"]}
-    if g_sel != o_sel:
-        beta = np.float32(prm["beta"])
-        okey = {sa["path"][i]: float(np.float32(sa["score"][i]) + np.float32(beta * np.float32(sa["depth"][i])))
-                for i in range(1, len(sa["path"]))}
-        cut = okey[sa["path"][orc["sel"][-1]]]
-        if not _tie_ok(okey, g_sel ^ o_sel, cut, tol):
-            raise Mismatch(f"{where}selected set differs beyond tolerance")
-        return {"exact": False, "tie": "top-B"}
+    if g.sel != o_sel:
+        return ("B",), g.sel
+    return None
 
-    # stage 4: identical structure, scores within tolerance
+
+def _tie_info(key, d, gset):
+    diff = set(gset) ^ set(d["default"])
+    return {"stage": key[0], "depth": key[1] if len(key) > 1 else None,
+            "band": len(d["band"]), "swapped": len(diff) // 2}
+
+
+def compare_request(gout, gtr, prep, q, prm, tol=O.TIE_TOL, where="", scoring="conditional",
+                    max_ties=64):
+    """gout: GPU outputs of request q; gtr: its trace; prep: the oracle's
+    ``prepare_round`` of the same inputs.  Returns
+    {'exact': bool, 'ties': [...], 'ambiguous': int, 'nodes': int}."""
+    D, M, K, W, B, beta = prm["D"], prm["M"], prm["K"], prm["W"], prm["B"], prm["beta"]
+    g = _Gpu(gout, gtr, B, where)
+    script, ties = {}, []
+    while True:
+        orc = O.build_request(prep, q, D, M, K, W, B, beta, check_heap=not script,
+                              scoring=scoring, script=script, tol=tol)
+        div = _first_divergence(g, orc, prm, tol, where)
+        if div is None:
+            break
+        key, gset = div
+        d = orc["sa"]["decisions"].get(key)
+        if d is None:
+            raise Mismatch(f"{where}decision {key}: GPU kept {sorted(gset)[:4]}, oracle has no choice")
+        if not (len(gset) == d["n"] and d["sure"] <= gset <= (d["sure"] | d["band"])):
+            raise Mismatch(f"{where}decision {key} differs beyond tolerance: "
+                           f"{sorted(set(gset) ^ d['default'])[:4]}")
+        ties.append(_tie_info(key, d, gset))
+        if len(ties) > max_ties:
+            raise Mismatch(f"{where}more than {max_ties} tolerated ties")
+        script[key] = set(gset)
+
+    # every decision agrees: the whole tree element by element
+    sa = orc["sa"]
+    for n in range(1, len(sa["path"])):
+        if abs(g.score[sa["path"][n]] - sa["score"][n]) > tol:
+            raise Mismatch(f"{where}score of {sa['path'][n]}")
+    n = int(gout["n_nodes"])
+    if n != orc["n_nodes"]:
+        raise Mismatch(f"{where}n_nodes {n} vs {orc['n_nodes']}")
     for k in ("tok", "parent", "depth", "mask"):
         if not np.array_equal(gout[k], orc[k]):
             raise Mismatch(f"{where}{k} differs")
-    if n != orc["n_nodes"]:
-        raise Mismatch(f"{where}n_nodes differs")
     if np.max(np.abs(gout["score"][:n] - orc["score"][:n])) > tol:
         raise Mismatch(f"{where}scores differ by more than {tol}")
-    return {"exact": True, "tie": ""}
+    amb = sum(1 for d in sa["decisions"].values() if d["ambiguous"])
+    return {"exact": not ties, "ties": ties, "ambiguous": amb, "nodes": n,
+            "superarbol": len(sa["path"])}

@@ -42,3 +42,17 @@ def test_counter_traffic_follows_the_kernel_source(monkeypatch):
     monkeypatch.setattr(bench, "_src_sha", lambda p: "0" * 16)
     assert bench.counters_traffic("qwen3_4b") is None
     assert bench.counters_traffic("no_such_workload") is None
+
+
+def test_dominant_kernel_follows_the_path_each_workload_runs():
+    import synth
+    bench = _bench_module()
+    k = {n: bench.dominant_kernel(c) for n, c in synth.CONFIGS.items()}
+    assert k["qwen3_4b"]["kernel"] == "k1_lmhead_bf16" and k["qwen3_4b"]["bound"] == "hbm"
+    assert k["wide"]["kernel"] == "k1_lmhead_bf16"
+    # 128 hidden rows: the tiled product, 128 flop per weight byte, HBM-bound
+    assert k["qwen3_8b_x8"]["kernel"] == "k1_logits_tiled" and k["qwen3_8b_x8"]["bound"] == "hbm"
+    # 512 hidden rows: past the ridge of the published peaks, MFMA-bound
+    assert k["stress_b0"]["bound"] == "mfma" and k["stress_b0"]["unit"] == "TFLOP/s"
+    c = synth.CONFIGS["stress_b0"]
+    assert k["stress_b0"]["work"] == 2 * c.batch * c.D * c.d * c.V

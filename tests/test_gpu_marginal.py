@@ -13,8 +13,8 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("seed", range(20))
 def test_marginal_tiny_exact(gpu_lib, seed):
     cfg = synth.CONFIGS["tiny"]
-    check_config(synth.make_inputs(cfg, seed), cfg, f"marginal tiny {seed}", max_tie_frac=0.0,
-                 scoring="marginal")
+    check_config(synth.make_inputs(cfg, seed), cfg, f"marginal tiny {seed}", scoring="marginal",
+                 seed=seed)
 
 
 @pytest.mark.parametrize("seed,wtype,d,V,M,K,W,B,D,batch", [
@@ -26,15 +26,15 @@ def test_marginal_tiny_exact(gpu_lib, seed):
 def test_marginal_shapes(gpu_lib, seed, wtype, d, V, M, K, W, B, D, batch):
     cfg = synth.custom_config(cfg_id=9500 + seed, d=d, V=V, e=64, s=64, r=32, D=D, M=M, K=K, W=W,
                               B=B, beta=-0.05, batch=batch, wtype=wtype)
-    check_config(synth.make_inputs(cfg, seed), cfg, f"marginal shape {seed}", max_tie_frac=0.34,
-                 scoring="marginal")
+    check_config(synth.make_inputs(cfg, seed), cfg, f"marginal shape {seed}", max_ties_per_request=2,
+                 scoring="marginal", seed=seed)
 
 
 @pytest.mark.parametrize("name", ["qwen3_4b", "wide", "qwen3_8b_x8"])
 def test_marginal_full_size(gpu_lib, name):
     cfg = synth.CONFIGS[name]
-    check_config(synth.make_inputs(cfg, 0), cfg, f"marginal {name}",
-                 max_tie_frac=1.0 if cfg.batch == 1 else 0.25, scoring="marginal")
+    check_config(synth.make_inputs(cfg, 0), cfg, f"marginal {name}", max_ties_per_request=2,
+                 scoring="marginal", seed=0)
 
 
 def test_scoring_switch_on_one_context(gpu_lib):
@@ -51,14 +51,15 @@ def test_scoring_switch_on_one_context(gpu_lib):
     rnd = runner.Round(wd, cfg.wtype, caps_for(cfg), cfg.batch, cfg.D, cfg.M, cfg.K, cfg.W,
                        cfg.B, cfg.beta, scoring="marginal")
     prm = dict(D=cfg.D, M=cfg.M, K=cfg.K, W=cfg.W, B=cfg.B, beta=cfg.beta)
+    prep = O.prepare_round(x, cfg.D)
     try:
         for mode in ("marginal", "conditional", "marginal", "conditional"):
             _lib.dtree_set_scoring(rnd.ctx, mode)
             rnd.run(H, root)
             torch.cuda.synchronize()
             out = rnd.outputs()[0]
-            orc = O.build_round(x, cfg.D, cfg.M, cfg.K, cfg.W, cfg.B, cfg.beta, scoring=mode)[0]
-            res = compare_request(out, rnd.trace(0), orc, prm, where=f"switch {mode}: ")
+            res = compare_request(out, rnd.trace(0), prep, 0, prm, where=f"switch {mode}: ",
+                                  scoring=mode)
             assert res["exact"], res
         with pytest.raises(_lib.DTreeError):
             _lib.dtree_set_scoring(rnd.ctx, 7)

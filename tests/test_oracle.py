@@ -3,7 +3,7 @@
 Each test checks the oracle against something it does not compute itself:
 a library routine the step reduces to, an independent brute-force walk over
 every token path, the hand-worked fixtures, the set equality of Lemma 1
-(DARTree page, Methodology 2), closed-form special cases, and invariants.
+(DARTree page, Metodología 2), closed-form special cases, and invariants.
 """
 import math
 
@@ -380,4 +380,185 @@ def test_marginal_unpruned_top_b_over_all_paths():
 def test_unknown_scoring_rejected():
     cfg = synth.CONFIGS["tiny"]
     with pytest.raises(ValueError):
-        _run(synth.make_inputs(cfg, 0), cfg, scoring="markov")
+        _run(synth.make_inputs(cfg, 0), cfg, scoring="no_such_scoring")
+
+
+# ------------------------------------------------------- Markov scoring
+def _check_markov(x, cfg):
+    res = _run(x, cfg, store="f64", scoring="markov")[0]
+    sa = res["sa"]
+    bf = Brute(x, 0, cfg.D, cfg.M)
+    allp = bf.enumerate_markov()
+    assert [list(c) for c in sa["C"]] == [list(c) for c in bf.C]
+    for n in range(1, len(sa["tok"])):
+        assert abs(sa["score"][n] - allp[sa["path"][n]]) < 1e-10
+    for dd, pdp in enumerate(sa["per_depth"]):
+        for p in pdp["frontier"]:
+            pth = sa["path"][p]
+            ext = {t: allp[pth + (t,)] - (allp[pth] if pth else 0.0) for t in bf.C[dd]}
+            want = sorted(ext, key=lambda t: (-ext[t], t))[:cfg.K]
+            assert [sa["tok"][c] for c in sa["kids"][p]] == want
+        ch = pdp["children"]
+        surv = sorted(ch, key=lambda n: (-allp[sa["path"][n]], sa["path"][n]))[:cfg.W]
+        assert set(surv) == set(pdp["survivors"])
+    return res
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_markov_scoring_tiny(seed):
+    """Markov (parent-token-only) scoring: every node's score equals the sum
+    over its path of log-probs recomputed by an independent enumerator that
+    runs the GRU one step from a zero state on each node's last token."""
+    cfg = synth.CONFIGS["tiny"]
+    _check_markov(synth.make_inputs(cfg, seed), cfg)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_markov_scoring_random_shapes(seed):
+    cfg, x = _rand_tiny(300 + seed, "bf16" if seed % 2 else "f32")
+    _check_markov(x, cfg)
+
+
+def test_markov_children_depend_on_depth_and_token_only():
+    """Two expanded branches of one depth ending in the same token get the
+    same log-probs under Markov scoring; conditional scoring tells them
+    apart (their GRU states differ)."""
+    cfg = synth.custom_config(cfg_id=4200, d=16, V=12, e=8, s=8, r=4, D=3, M=3, K=3, W=9,
+                              B=30, beta=0.0)
+    seen = 0
+    for seed in range(6):
+        x = synth.make_inputs(cfg, seed)
+        for scoring in ("markov", "conditional"):
+            sa = _run(x, cfg, store="f64", scoring=scoring)[0]["sa"]
+            pdp = sa["per_depth"][2]
+            by_tok = {}
+            for a, p in enumerate(pdp["frontier"]):
+                by_tok.setdefault(sa["tok"][p], []).append(pdp["lp"][a])
+            for rows in by_tok.values():
+                for r in rows[1:]:
+                    same = np.array_equal(r, rows[0])
+                    assert same == (scoring == "markov")
+                    seen += scoring == "markov"
+    assert seen > 0
+
+
+def test_markov_unpruned_top_b_over_all_paths():
+    for seed in range(4):
+        cfg = synth.custom_config(cfg_id=4300, d=16, V=40, e=8, s=8, r=4, D=3, M=4, K=4,
+                                  W=16, B=20, beta=-0.1)
+        x = synth.make_inputs(cfg, seed)
+        res = _run(x, cfg, store="f64", scoring="markov")[0]
+        allp = Brute(x, 0, cfg.D, cfg.M).enumerate_markov()
+        ranked = sorted(allp, key=lambda p: (-(allp[p] + cfg.beta * len(p)), len(p), p))
+        sa = res["sa"]
+        assert {sa["path"][n] for n in res["sel"]} == set(ranked[:cfg.B])
+
+
+# ------------------------------------------------ sequential best-first heap
+def _heap(x, cfg, store="f64", scoring="conditional", B=None):
+    prep = O.prepare_round(x, cfg.D, store)
+    return O.build_heap_tree(prep, 0, cfg.D, cfg.M, cfg.K, cfg.B if B is None else B,
+                             cfg.beta, scoring=scoring)
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("scoring", ["conditional", "markov"])
+def test_heap_builder_vs_brute_force(seed, scoring):
+    """DominoTree's best-first builder selects the Top-B (key desc, depth
+    asc, path asc) of the unpruned K-ary tree in which every node's children
+    are the Top-K of its M extensions; brute force rebuilds that tree with
+    every score recomputed from the root."""
+    cfg, x = _rand_tiny(500 + seed, "bf16" if seed % 2 else "f32")
+    cfg = cfg.with_(beta=min(cfg.beta, 0.0))
+    res = _heap(x, cfg, scoring=scoring)
+    tree = Brute(x, 0, cfg.D, cfg.M).kary_tree(cfg.K, markov=scoring == "markov")
+    ranked = sorted(tree, key=lambda p: (-(tree[p] + cfg.beta * len(p)), len(p), p))
+    sa = res["sa"]
+    got = [sa["path"][n] for n in res["sel"]]
+    assert set(got) == set(ranked[:cfg.B])
+    for n in res["sel"]:
+        assert abs(sa["score"][n] - tree[sa["path"][n]]) < 1e-10
+    # pops come out in the selection order itself
+    assert got == ranked[:len(got)]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_heap_builder_equals_unpruned_depthwise_build(seed):
+    """With W >= K^(D-1) the depth-wise build prunes nothing, so by Lemma 1
+    its global Top-B is the heap's pop set: same tree, same scores."""
+    cfg = synth.custom_config(cfg_id=4400, d=24, V=60, e=8, s=12, r=6, D=4, M=5, K=3,
+                              W=27, B=25, beta=[0.0, -0.05, -0.3][seed % 3],
+                              wtype="bf16" if seed % 2 else "f32")
+    x = synth.make_inputs(cfg, seed)
+    a = _heap(x, cfg, store="f32")
+    b = _run(x, cfg, store="f32")[0]
+    for k in ("tok", "parent", "depth", "mask"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["n_nodes"] == b["n_nodes"]
+    assert np.max(np.abs(a["score"][:a["n_nodes"]] - b["score"][:b["n_nodes"]])) < 1e-6
+
+
+def test_heap_builder_chain_special_case():
+    """K = 1 (one child per popped node): the heap grows the greedy corrected
+    chain, the same tree as the depth-wise build with K = W = 1."""
+    for seed in range(5):
+        cfg = synth.CONFIGS["tiny"].with_(K=1, W=1)
+        x = synth.make_inputs(cfg, seed)
+        a = _heap(x, cfg, store="f64")
+        b = _run(x, cfg, store="f64")[0]
+        assert a["tok"].tolist() == b["tok"].tolist()
+        assert a["n_nodes"] == min(cfg.B, cfg.D) + 1
+
+
+# ---------------------------------------------- decisions and alternatives
+def test_default_script_reproduces_the_round():
+    """Scripting every decision with its own default selection changes
+    nothing; with tol = 0 and no exact ties no decision is ambiguous."""
+    cfg = synth.CONFIGS["tiny"]
+    for seed in range(5):
+        x = synth.make_inputs(cfg, seed)
+        prep = O.prepare_round(x, cfg.D)
+        a = O.build_request(prep, 0, cfg.D, cfg.M, cfg.K, cfg.W, cfg.B, cfg.beta, tol=0.0)
+        decs = a["sa"]["decisions"]
+        assert ("B",) in decs and ("W", 3) in decs and ("M", 0) in decs
+        assert not any(d["ambiguous"] for d in decs.values())
+        script = {k: d["default"] for k, d in decs.items()}
+        b = O.build_request(prep, 0, cfg.D, cfg.M, cfg.K, cfg.W, cfg.B, cfg.beta,
+                            script=script, tol=0.0)
+        for k in ("tok", "parent", "depth", "score", "mask"):
+            assert np.array_equal(a[k], b[k])
+
+
+def test_exact_tie_alternative_is_admissible_and_builds_a_valid_tree():
+    """The width-tie fixture has two children with exactly equal scores at
+    the Top-W cutoff: the decision is ambiguous, the other choice is an
+    admissible alternative the oracle builds itself (a different, valid
+    tree), and a set outside the band is refused."""
+    g, x, exp = fixtures_io.load("width_tie")
+    p = g["params"]
+    prep = O.prepare_round(x, p["D"])
+    a = O.build_request(prep, 0, p["D"], p["M"], p["K"], p["W"], p["B"], p["beta"])
+    amb = [k for k, d in a["sa"]["decisions"].items() if d["ambiguous"]]
+    wkeys = [k for k in amb if k[0] == "W"]
+    assert wkeys
+    k = wkeys[0]
+    d = a["sa"]["decisions"][k]
+    alts = [X for X in _subsets(d["band"], d["n"] - len(d["sure"]))]
+    assert len(alts) >= 2
+    other = next(set(d["sure"]) | set(X) for X in alts
+                 if set(d["sure"]) | set(X) != d["default"])
+    b = O.build_request(prep, 0, p["D"], p["M"], p["K"], p["W"], p["B"], p["beta"],
+                        script={k: other}, check_heap=False)
+    sa = b["sa"]
+    assert {sa["path"][n] for n in sa["per_depth"][k[1] - 1]["survivors"]} == other
+    assert not np.array_equal(a["tok"], b["tok"]) or not np.array_equal(a["parent"], b["parent"])
+    outside = set(d["default"])
+    outside.discard(next(iter(outside - set(d["sure"]))))
+    with pytest.raises(O.NotAdmissible):
+        O.build_request(prep, 0, p["D"], p["M"], p["K"], p["W"], p["B"], p["beta"],
+                        script={k: outside})
+
+
+def _subsets(items, n):
+    import itertools
+    return [set(c) for c in itertools.combinations(sorted(items), n)]
