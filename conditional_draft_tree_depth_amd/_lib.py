@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(HERE, "libdtree.so")
 DTREE_F32, DTREE_BF16 = 0, 1
 STATUS = {0: "DTREE_OK", 1: "DTREE_E_ARG", 2: "DTREE_E_SHAPE", 3: "DTREE_E_DTYPE",
           4: "DTREE_E_DEVICE", 5: "DTREE_E_NOMEM", 6: "DTREE_E_HIP", 7: "DTREE_E_STATE"}
-EXPORTS = ("dtree_create", "dtree_build_round", "dtree_superarbol_nodes",
+EXPORTS = ("dtree_create", "dtree_build_round", "dtree_build_round_static",
+           "dtree_superarbol_nodes",
            "dtree_get_trace", "dtree_profile_enable", "dtree_profile_read",
            "dtree_set_persistent_launch", "dtree_set_scoring", "dtree_last_error",
            "dtree_destroy")
@@ -74,6 +75,9 @@ def load(path=LIB_PATH):
     lib.dtree_build_round.argtypes = [c_vp, P(dtree_params), c_i32, c_vp, c_vp, c_vp, c_vp,
                                       c_vp, c_vp, c_vp, c_vp, c_vp]
     lib.dtree_build_round.restype = c_i32
+    lib.dtree_build_round_static.argtypes = [P(dtree_weights), P(dtree_params), c_i32, c_vp,
+                                             c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.dtree_build_round_static.restype = c_i32
     lib.dtree_superarbol_nodes.argtypes = [P(dtree_params)]
     lib.dtree_superarbol_nodes.restype = c_i32
     lib.dtree_get_trace.argtypes = [c_vp, c_i32, P(dtree_trace)]
@@ -112,19 +116,25 @@ def dtree_superarbol_nodes(p):
     return load().dtree_superarbol_nodes(ctypes.byref(p))
 
 
-def dtree_create(weights, wtype, caps, device=0):
-    """weights: dict of contiguous device tensors (W_lm, bias, Emb, W_ih, W_hh,
-    b_ih, b_hh, W1, W2); bf16 matrices as torch.bfloat16 or int16 views.
-    Returns an opaque context handle (c_void_p)."""
-    lib = load()
+def weights_struct(weights, wtype):
+    """dtree_weights of a dict of contiguous device tensors (W_lm, bias, Emb,
+    W_ih, W_hh, b_ih, b_hh, W1, W2); bf16 matrices as torch.bfloat16 or int16
+    views."""
     W_lm, W1 = weights["W_lm"], weights["W1"]
     V, d = W_lm.shape
     s = weights["W_hh"].shape[1]
-    w = dtree_weights(d, V, weights["Emb"].shape[1], s, W1.shape[0],
-                      DTREE_BF16 if wtype == "bf16" else DTREE_F32,
-                      _ptr(W_lm), _ptr(weights.get("bias")), _ptr(weights["Emb"]),
-                      _ptr(weights["W_ih"]), _ptr(weights["W_hh"]), _ptr(weights.get("b_ih")),
-                      _ptr(weights.get("b_hh")), _ptr(W1), _ptr(weights["W2"]))
+    return dtree_weights(d, V, weights["Emb"].shape[1], s, W1.shape[0],
+                         DTREE_BF16 if wtype == "bf16" else DTREE_F32,
+                         _ptr(W_lm), _ptr(weights.get("bias")), _ptr(weights["Emb"]),
+                         _ptr(weights["W_ih"]), _ptr(weights["W_hh"]), _ptr(weights.get("b_ih")),
+                         _ptr(weights.get("b_hh")), _ptr(W1), _ptr(weights["W2"]))
+
+
+def dtree_create(weights, wtype, caps, device=0):
+    """weights: dict of contiguous device tensors (see weights_struct).
+    Returns an opaque context handle (c_void_p)."""
+    lib = load()
+    w = weights_struct(weights, wtype)
     c = dtree_caps(*caps) if not isinstance(caps, dtree_caps) else caps
     ctx = ctypes.c_void_p()
     _check("dtree_create", lib.dtree_create(ctypes.byref(w), ctypes.byref(c), device,
@@ -143,6 +153,20 @@ def dtree_build_round(ctx, p, batch, H, root, tok, parent, depth, score, mask, n
                                     _ptr(tok), _ptr(parent), _ptr(depth), _ptr(score),
                                     _ptr(mask), _ptr(n_nodes), ctypes.c_void_p(stream)),
            ctx)
+
+
+def dtree_build_round_static(weights, wtype, p, batch, H, root, tok, parent, depth, score,
+                             mask, n_nodes, stream=None):
+    """The allocation-free round (no context): weights as for dtree_create."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    w = weights_struct(weights, wtype)
+    _check("dtree_build_round_static",
+           load().dtree_build_round_static(ctypes.byref(w), ctypes.byref(p), batch, _ptr(H),
+                                           _ptr(root), _ptr(tok), _ptr(parent), _ptr(depth),
+                                           _ptr(score), _ptr(mask), _ptr(n_nodes),
+                                           ctypes.c_void_p(stream)))
 
 
 def dtree_get_trace(ctx, req, p, batch_nodes):

@@ -12,7 +12,9 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "dtree.h"
 #include "kernels.hpp"
@@ -97,12 +99,25 @@ struct dtree_ctx {
   bool prof = false;
   int prof_n = 0;
   hipEvent_t *prof_ev = nullptr;
+  // errors go here instead of err when set (a context on the stack of the
+  // allocation-free entry point: no host allocation for the message)
+  char *err_buf = nullptr;
+  size_t err_cap = 0;
 };
 
 static constexpr int kProfRounds = 4096;
+static const char *g_static_err_text();
 
 static dtree_status fail(dtree_ctx *c, dtree_status s, const std::string &m) {
-  if (c) c->err = m; else g_create_err = m;
+  if (c && c->err_buf) std::snprintf(c->err_buf, c->err_cap, "%s", m.c_str());
+  else if (c) c->err = m;
+  else g_create_err = m;
+  return s;
+}
+static dtree_status fail(dtree_ctx *c, dtree_status s, const char *m) {
+  if (c && c->err_buf) std::snprintf(c->err_buf, c->err_cap, "%s", m);
+  else if (c) c->err = m;
+  else g_create_err = m;
   return s;
 }
 
@@ -299,16 +314,18 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
     if (ctx->pk_fail) (void)hipHostFree(ctx->pk_fail);
     return reject(DTREE_E_NOMEM, std::string("workspace: ") + hipGetErrorString(e));
   }
-  hipError_t pe = lmhead_prepare(w->wtype, ctx->k1_ring, ctx->k1_smem);
-  if (pe == hipSuccess) pe = corr_logits_prepare(w->wtype, cl_smem);
-  if (pe == hipSuccess) pe = topb_prepare(tb_smem);
+  // (every kernel may use up to the device's LDS per workgroup: contexts and
+  // allocation-free calls of other sizes never lower each other's limits)
+  hipError_t pe = lmhead_prepare(w->wtype, ctx->k1_ring, ctx->lds_max);
+  if (pe == hipSuccess) pe = corr_logits_prepare(w->wtype, ctx->lds_max);
+  if (pe == hipSuccess) pe = topb_prepare(ctx->lds_max);
   if (pe == hipSuccess) pe = gemm_prepare();
   // correction logits inside the selection kernel: bf16 W2 rows of 16-byte
   // pieces whose slice (and one u row per wave) fits in LDS
   ctx->sel_corr = w->wtype == DTREE_BF16 && r % 8 == 0 && r <= 512 &&
                   reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
                   select_corr_smem(c.max_M, r) + 45056 <= ctx->lds_max;
-  if (pe == hipSuccess && ctx->sel_corr) pe = select_corr_prepare(select_corr_smem(c.max_M, r));
+  if (pe == hipSuccess && ctx->sel_corr) pe = select_corr_prepare(ctx->lds_max);
   if (pe == hipSuccess && ctx->pk) pe = persist_prepare(s);
   if (pe != hipSuccess) {
     free_ws(ws);
@@ -317,6 +334,11 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   *out = ctx;
   return DTREE_OK;
 }
+
+static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t batch,
+                                  const float *H, const int32_t *root, int32_t *tok,
+                                  int32_t *parent, int32_t *depth, float *score, uint8_t *mask,
+                                  int32_t *n_nodes, hipStream_t st);
 
 extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p, int32_t batch,
                                           const float *H, const int32_t *root, int32_t *tok,
@@ -350,7 +372,17 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   }
 
   DeviceGuard dg(ctx->device);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  return enqueue_round(ctx, p, batch, H, root, tok, parent, depth, score, mask, n_nodes,
+                       static_cast<hipStream_t>(stream));
+}
+
+// The kernels of one round, enqueued on st (arguments already checked).
+static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t batch,
+                                  const float *H, const int32_t *root, int32_t *tok,
+                                  int32_t *parent, int32_t *depth, float *score, uint8_t *mask,
+                                  int32_t *n_nodes, hipStream_t st) {
+  const dtree_caps &c = ctx->caps;
+  const int D = p->D, M = p->M, K = p->K, W = p->W, B = p->B;
   const dtree_weights &w = ctx->w;
   Ws &ws = ctx->ws;
   const int rows = batch * D;
@@ -476,20 +508,32 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
       //   W_hh . S + b_hh                  (outputs r .. r+3s-1, the GRU state
       //                                      part of all of the branch's children)
       const int ldu = r + 3 * s;
-      g = GemmArgs{batch * A, ldu, s, ws.S[sc], WT_F32, s, nullptr, 0, ws.wcat, wt, s, w.b_hh,
-                   ws.uH, r, A, D, dd, ws.uh, ldu};
-      g.add_n = r;
-      g.bias_n0 = r;
-      if (ws.S3[sc]) {   // the state as three bf16 planes, if a tiled product takes it
-        GemmArgs g3 = g;
-        g3.X = ws.S3[sc];
-        g3.xtype = WT_BF16;
-        g3.ldx = 3 * s;
-        g3.Kd = 3 * s;
-        g3.kw = s;
-        if (gemm_tiled_ok(g3)) g = g3;
+      if (ws.wcat) {
+        g = GemmArgs{batch * A, ldu, s, ws.S[sc], WT_F32, s, nullptr, 0, ws.wcat, wt, s, w.b_hh,
+                     ws.uH, r, A, D, dd, ws.uh, ldu};
+        g.add_n = r;
+        g.bias_n0 = r;
+        if (ws.S3[sc]) {   // the state as three bf16 planes, if a tiled product takes it
+          GemmArgs g3 = g;
+          g3.X = ws.S3[sc];
+          g3.xtype = WT_BF16;
+          g3.ldx = 3 * s;
+          g3.Kd = 3 * s;
+          g3.kw = s;
+          if (gemm_tiled_ok(g3)) g = g3;
+        }
+        HIPCHK(ctx, launch_gemm(g, st));
+      } else {
+        // no concatenated copy (allocation-free calls): the same two
+        // products straight from W1[:, d:] and W_hh
+        g = GemmArgs{batch * A, r, s, ws.S[sc], WT_F32, s, nullptr, 0,
+                     static_cast<const uint8_t *>(w.W1) + (size_t)d * esz, wt, d + s, nullptr,
+                     ws.uH, r, A, D, dd, ws.uh, ldu};
+        HIPCHK(ctx, launch_gemm(g, st));
+        g = GemmArgs{batch * A, 3 * s, s, ws.S[sc], WT_F32, s, nullptr, 0, w.W_hh, wt, s, w.b_hh,
+                     nullptr, 0, 1, 0, 0, ws.uh + r, ldu};
+        HIPCHK(ctx, launch_gemm(g, st));
       }
-      HIPCHK(ctx, launch_gemm(g, st));
       // (with many branches x candidates per request the separate correction
       // kernel spreads that work over more workgroups)
       if (ctx->sel_corr && A * M <= 2048) {
@@ -630,7 +674,8 @@ extern "C" dtree_status dtree_set_scoring(dtree_ctx *ctx, int32_t scoring) {
 }
 
 extern "C" const char *dtree_last_error(const dtree_ctx *ctx) {
-  return ctx ? ctx->err.c_str() : g_create_err.c_str();
+  if (ctx) return ctx->err.c_str();
+  return g_create_err.empty() ? g_static_err_text() : g_create_err.c_str();
 }
 
 extern "C" dtree_status dtree_destroy(dtree_ctx *ctx) {
@@ -647,3 +692,192 @@ extern "C" dtree_status dtree_destroy(dtree_ctx *ctx) {
   delete ctx;
   return DTREE_OK;
 }
+
+// ---------------------------------------------------------------- allocation-free rounds
+//
+// dtree_build_round_static: one round with no context.  Its whole workspace
+// lives in `scratch`, a file-scope device array of kStaticScratch bytes (each
+// device the library runs on holds its own copy until the process ends).  In
+// host code `scratch` names a host-side stand-in, so the array's device
+// address is taken once per device with hipGetSymbolAddress and only that
+// address is used.  Calls on one device share the array: calls whose work
+// overlaps on the device race (one stream, or synchronised streams, per
+// device); every buffer a round reads is written earlier in the same round
+// (the round-start kernel clears the survivor history and the status word).
+static constexpr size_t kStaticScratch = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratch];
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct StaticDevice {
+  bool ready = false;
+  bool gfx950 = false;
+  size_t lds_max = 0;
+  void *scratch = nullptr;   // device address of this device's `scratch`
+};
+StaticDevice g_static_dev[kMaxDevices];
+std::mutex g_static_mu;
+thread_local char g_static_err[256];
+
+dtree_status static_fail(dtree_status s, const char *m) {
+  std::snprintf(g_static_err, sizeof g_static_err, "%s", m);
+  g_create_err.clear();
+  return s;
+}
+}  // namespace
+
+// The workspace of a round sized exactly for p and batch, carved from base
+// (256-byte aligned pieces); returns the bytes it needs (nothing is written
+// when base is null).
+static size_t static_layout(const dtree_weights &w, const dtree_params &p, int batch, int P,
+                            int NT, uint8_t *base, Ws &ws) {
+  size_t off = 0;
+  auto take = [&](auto **ptr, size_t n) {
+    using T = std::remove_pointer_t<std::remove_reference_t<decltype(*ptr)>>;
+    const size_t at = (off + 255) & ~(size_t)255;
+    off = at + (n ? n : 1) * sizeof(T);
+    if (base) *ptr = reinterpret_cast<T *>(base + at);
+  };
+  const size_t rows = (size_t)batch * p.D, bw = (size_t)batch * p.W;
+  const int s = w.s, r = w.r;
+  take(&ws.part, rows * P * K1_LSTRIDE);
+  take(&ws.C, rows * p.M);
+  take(&ws.Cl, rows * p.M);
+  take(&ws.uH, rows * r);
+  take(&ws.hb, (rows + 15) / 16 * 16 * (size_t)w.d);
+  take(&ws.S[0], bw * s);
+  take(&ws.S[1], bw * s);
+  take(&ws.uh, bw * (r + 3 * s));
+  take(&ws.ell, bw * p.M);
+  take(&ws.gi, bw * 3 * s);
+  const size_t nt = (size_t)batch * NT;
+  take(&ws.n_tok, nt);
+  take(&ws.n_par, nt);
+  take(&ws.n_dep, nt);
+  take(&ws.n_score, nt);
+  take(&ws.n_lex, nt);
+  for (int i = 0; i < 2; ++i) { take(&ws.surv[i], bw); take(&ws.rank[i], bw); }
+  take(&ws.surv_hist, (size_t)batch * (p.D + 1) * p.W);
+  take(&ws.gidx_tok, bw);
+  take(&ws.gidx_par, bw);
+  take(&ws.sel, (size_t)batch * p.B);
+  take(&ws.status, 1);
+  return off;
+}
+
+extern "C" dtree_status dtree_build_round_static(const dtree_weights *w, const dtree_params *p,
+                                                 int32_t batch, const float *H,
+                                                 const int32_t *root, int32_t *tok,
+                                                 int32_t *parent, int32_t *depth, float *score,
+                                                 uint8_t *mask, int32_t *n_nodes, void *stream) {
+  g_static_err[0] = '\0';
+  if (!w || !p) return static_fail(DTREE_E_ARG, "null weights or params");
+  if (!H || !root || !tok || !parent || !depth || !score || !mask || !n_nodes)
+    return static_fail(DTREE_E_ARG, "null input or output pointer");
+  if (w->wtype != DTREE_F32 && w->wtype != DTREE_BF16)
+    return static_fail(DTREE_E_DTYPE, "wtype must be DTREE_F32 or DTREE_BF16");
+  if (w->d < 1 || w->V < 1 || w->e < 1 || w->s < 1 || w->r < 1)
+    return static_fail(DTREE_E_ARG, "d, V, e, s, r must be >= 1");
+  if (w->V > (1 << 18)) return static_fail(DTREE_E_SHAPE, "V must be <= 262144");
+  if (!w->W_lm || !w->Emb || !w->W_ih || !w->W_hh || !w->W1 || !w->W2)
+    return static_fail(DTREE_E_ARG, "null weight pointer");
+  if (w->wtype == DTREE_BF16) {
+    if (w->d % 128) return static_fail(DTREE_E_SHAPE, "bf16 weights need d % 128 == 0");
+    if (reinterpret_cast<uintptr_t>(w->W_lm) % 16)
+      return static_fail(DTREE_E_ARG, "W_lm must be 16-byte aligned");
+  }
+  const int D = p->D, M = p->M, K = p->K, W = p->W, B = p->B;
+  if (batch < 1) return static_fail(DTREE_E_ARG, "batch must be >= 1");
+  if (D < 1 || D > 31) return static_fail(DTREE_E_ARG, "D outside [1, 31]");
+  if (M < 1 || M > 128 || M > w->V) return static_fail(DTREE_E_ARG, "M outside [1, min(128, V)]");
+  if (K < 1 || K > M) return static_fail(DTREE_E_ARG, "K outside [1, M]");
+  if (W < 1 || W > 512 || (long long)W * K > 1024)
+    return static_fail(DTREE_E_ARG, "W outside [1, 512] or W * K > 1024");
+  if (B < 1) return static_fail(DTREE_E_ARG, "B must be >= 1");
+  if (!(p->beta <= 0.0f)) return static_fail(DTREE_E_ARG, "beta must be <= 0 (and not NaN)");
+  if (std::isinf(p->beta)) return static_fail(DTREE_E_ARG, "beta must be finite");
+  const int NT = superarbol_nodes(D, K, W);
+  if (NT < 0 || NT > 8192) return static_fail(DTREE_E_SHAPE, "superarbol exceeds 8192 nodes");
+  const int P = lmhead_partitions(w->V, w->wtype, (w->r + 15) / 16);
+  Ws ws;
+  const size_t need = static_layout(*w, *p, batch, P, NT, nullptr, ws);
+  if (need > kStaticScratch) {
+    char m[160];
+    std::snprintf(m, sizeof m, "round workspace of %zu bytes exceeds the %zu-byte static scratch",
+                  need, kStaticScratch);
+    return static_fail(DTREE_E_SHAPE, m);
+  }
+
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return static_fail(DTREE_E_DEVICE, "no current HIP device");
+  StaticDevice &sd = g_static_dev[dev];
+  {
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    if (!sd.ready) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return static_fail(DTREE_E_DEVICE, "device query failed");
+      sd.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+      sd.lds_max = prop.sharedMemPerBlock;
+      if (sd.gfx950) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) {
+          char m[128];
+          std::snprintf(m, sizeof m, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+          return static_fail(DTREE_E_HIP, m);
+        }
+        sd.scratch = ptr;
+        hipError_t pe = hipSuccess;
+        for (int ring = 0; ring <= 2 && pe == hipSuccess; ++ring)
+          pe = lmhead_prepare(WT_BF16, ring, sd.lds_max);
+        if (pe == hipSuccess) pe = corr_logits_prepare(WT_BF16, sd.lds_max);
+        if (pe == hipSuccess) pe = corr_logits_prepare(WT_F32, sd.lds_max);
+        if (pe == hipSuccess) pe = topb_prepare(sd.lds_max);
+        if (pe == hipSuccess) pe = gemm_prepare();
+        if (pe == hipSuccess) pe = select_corr_prepare(sd.lds_max);
+        if (pe != hipSuccess) {
+          char m[128];
+          std::snprintf(m, sizeof m, "kernel attributes: %s", hipGetErrorString(pe));
+          return static_fail(DTREE_E_HIP, m);
+        }
+      }
+      sd.ready = true;
+    }
+  }
+  if (!sd.gfx950) return static_fail(DTREE_E_DEVICE, "needs a gfx950 device");
+
+  // the kernels' own limits, as dtree_create checks them
+  const int ring = lmhead_ring(w->d, w->wtype, sd.lds_max);
+  const size_t k1_smem = lmhead_smem(w->d, w->wtype, ring);
+  if (k1_smem > sd.lds_max) return static_fail(DTREE_E_SHAPE, "d too large for the LM-head LDS tile");
+  if (topm_merge_smem(P) > 131072)
+    return static_fail(DTREE_E_SHAPE, "vocabulary too large for the Top-M merge");
+  if (corr_logits_smem(W, M, w->r, w->wtype) > sd.lds_max)
+    return static_fail(DTREE_E_SHAPE, "M * r too large for the correction LDS tile");
+  if (topb_smem(NT, B) > sd.lds_max)
+    return static_fail(DTREE_E_SHAPE, "superarbol too large for the Top-B LDS sort");
+
+  // a context on the stack: workspace in scratch, no persistent depth loop,
+  // no derived weight copies, no stage events
+  dtree_ctx ctx;
+  ctx.device = dev;
+  ctx.w = *w;
+  ctx.caps = dtree_caps{batch, D, M, K, W, B};
+  ctx.P = P;
+  ctx.NTcap = NT;
+  ctx.k1_ring = ring;
+  ctx.k1_smem = k1_smem;
+  ctx.lds_max = sd.lds_max;
+  static_layout(*w, *p, batch, P, NT, static_cast<uint8_t *>(sd.scratch), ctx.ws);
+  ctx.sel_corr = w->wtype == DTREE_BF16 && w->r % 8 == 0 && w->r <= 512 &&
+                 reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
+                 select_corr_smem(M, w->r) + 45056 <= sd.lds_max;
+  ctx.err_buf = g_static_err;
+  ctx.err_cap = sizeof g_static_err;
+  return enqueue_round(&ctx, p, batch, H, root, tok, parent, depth, score, mask, n_nodes,
+                       static_cast<hipStream_t>(stream));
+}
+
+static const char *g_static_err_text() { return g_static_err; }

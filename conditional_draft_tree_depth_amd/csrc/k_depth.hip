@@ -96,12 +96,10 @@ size_t corr_logits_smem(int A, int M, int r, int wtype) {
   return (((size_t)M * rs * es + 15) & ~(size_t)15) + (size_t)(A < CL_BR ? A : CL_BR) * r * 4;
 }
 
-hipError_t corr_logits_prepare(int wtype, size_t smem) {
+hipError_t corr_logits_prepare(int wtype, size_t lds_bytes) {
   if (wtype == WT_BF16)
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_corr_logits<uint16_t>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_corr_logits<float>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    return set_lds_limit(reinterpret_cast<const void *>(&k_corr_logits<uint16_t>), lds_bytes);
+  return set_lds_limit(reinterpret_cast<const void *>(&k_corr_logits<float>), lds_bytes);
 }
 
 hipError_t launch_corr_logits(int b, int A, int M, int r, int D, int delta, const void *W2,
@@ -441,9 +439,8 @@ size_t select_corr_smem(int M, int r) {
   return (((size_t)M * (r + 8) * 2 + 15) & ~(size_t)15) + (size_t)(SEL_THREADS / 64) * r * 4;
 }
 
-hipError_t select_corr_prepare(size_t smem) {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_select_corr),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+hipError_t select_corr_prepare(size_t lds_bytes) {
+  return set_lds_limit(reinterpret_cast<const void *>(&k_select_corr), lds_bytes);
 }
 
 hipError_t launch_select_corr(int b, int A, int M, int K, int W, int D, int delta, int off, int r,

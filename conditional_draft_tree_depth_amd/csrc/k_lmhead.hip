@@ -973,7 +973,7 @@ int lmhead_ring(int d, int wtype, size_t lds_max) {
 template <int RING>
 static const void *k1_fn() { return reinterpret_cast<const void *>(&k1_lmhead_bf16<RING>); }
 
-hipError_t lmhead_prepare(int wtype, int ring, size_t smem) {
+hipError_t lmhead_prepare(int wtype, int ring, size_t lds_bytes) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k1b_topm_merge),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
   if (e != hipSuccess || wtype != WT_BF16) return e;
@@ -981,7 +981,7 @@ hipError_t lmhead_prepare(int wtype, int ring, size_t smem) {
   e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k1_logits_tiled),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)LT_SMEM);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  return set_lds_limit(fn, lds_bytes);
 }
 
 hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {

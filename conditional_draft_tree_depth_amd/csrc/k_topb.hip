@@ -348,9 +348,8 @@ __global__ __launch_bounds__(TB_THREADS) void k_topb_emit(int NT, int B, float b
 
 size_t topb_smem(int NT, int B) { return tb_layout(NT, B).total; }
 
-hipError_t topb_prepare(size_t smem) {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_topb_emit),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+hipError_t topb_prepare(size_t lds_bytes) {
+  return set_lds_limit(reinterpret_cast<const void *>(&k_topb_emit), lds_bytes);
 }
 
 hipError_t launch_topb_emit(int b, int NT, int B, float beta, int Bmax, const TreeBufs &t,

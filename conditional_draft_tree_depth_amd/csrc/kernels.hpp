@@ -7,6 +7,17 @@ namespace dtree {
 
 enum { WT_F32 = 0, WT_BF16 = 1 };
 
+// Lets kernel fn use up to lds_bytes of LDS per workgroup in all: its limit
+// for dynamic LDS is lds_bytes less the kernel's own static LDS.
+inline hipError_t set_lds_limit(const void *fn, size_t lds_bytes) {
+  hipFuncAttributes fa;
+  hipError_t e = hipFuncGetAttributes(&fa, fn);
+  if (e != hipSuccess) return e;
+  const size_t st = fa.sharedSizeBytes;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)(lds_bytes > st ? lds_bytes - st : 0));
+}
+
 struct TreeBufs {
   int NT;              // superarbol nodes per request (root included)
   int V;               // vocabulary size (root tokens are clamped into [0, V))
@@ -76,7 +87,8 @@ int lmhead_partitions(int V, int wtype, int extra_tiles);
 // LDS ring depth of the bf16 kernel that fits lds_max (0: register path)
 int lmhead_ring(int d, int wtype, size_t lds_max);
 size_t lmhead_smem(int d, int wtype, int ring);
-hipError_t lmhead_prepare(int wtype, int ring, size_t smem);
+// every prepare call lets its kernels use up to lds_bytes of LDS in all
+hipError_t lmhead_prepare(int wtype, int ring, size_t lds_bytes);
 // bf16: round start (k1_stage_hidden: Hb, init_round_request); before launch_lmhead
 hipError_t launch_stage_hidden(const LMHeadArgs &a, hipStream_t st);
 // ev0 / ev1 (or null): events that take the kernel's own start and end times
@@ -155,7 +167,7 @@ hipError_t launch_select(int b, int A, int M, int K, int W, int D, int delta,
 // selection with the correction logits computed in place (bf16 W2, 16-byte
 // aligned, r % 8 == 0; dynamic LDS select_corr_smem(M, r))
 size_t select_corr_smem(int M, int r);
-hipError_t select_corr_prepare(size_t smem);
+hipError_t select_corr_prepare(size_t lds_bytes);
 hipError_t launch_select_corr(int b, int A, int M, int K, int W, int D, int delta, int off, int r,
                               const void *W2, const int32_t *C, const float *Cl, const float *u,
                               int ldu, const TreeBufs &t, hipStream_t st);
@@ -164,7 +176,7 @@ hipError_t launch_topb_emit(int b, int NT, int B, float beta, int Bmax,
                             int32_t *depth, float *score, uint8_t *mask,
                             int32_t *n_nodes, hipStream_t st);
 size_t topb_smem(int NT, int B);
-hipError_t topb_prepare(size_t smem);
+hipError_t topb_prepare(size_t lds_bytes);
 
 // ---- persistent depth loop (small batches) and its correction tables
 struct PersistArgs {
@@ -196,6 +208,6 @@ hipError_t launch_corr_tables(int rows, int M, int r, int s, const void *W2, con
                               const int32_t *C, const float *Cl, const float *uH, float *G,
                               float *g, hipStream_t st);
 hipError_t launch_depth_persistent(const PersistArgs &a, bool cooperative, hipStream_t st);
-hipError_t corr_logits_prepare(int wtype, size_t smem);
+hipError_t corr_logits_prepare(int wtype, size_t lds_bytes);
 
 }  // namespace dtree

@@ -155,6 +155,30 @@ dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
                                int32_t *parent, int32_t *depth, float *score,
                                uint8_t *mask, int32_t *n_nodes, void *stream);
 
+/* dtree_build_round for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): one round with no context, with the same arguments and
+ * outputs as dtree_build_round (weights as for dtree_create; the params are
+ * their own caps).  The round's whole workspace comes from one fixed array
+ * inside the library, 16 MiB on each device the library runs on (held from
+ * the first call until the process ends); nothing is allocated: no
+ * hipMalloc, hipFree or allocating library routine.  A round whose
+ * workspace exceeds 16 MiB returns DTREE_E_SHAPE before anything is
+ * enqueued (the Qwen3-4B shape with one request needs about 5 MiB: the
+ * per-slice candidate lists of the LM head dominate).  The depth loop runs
+ * as one product, correction, selection and GRU step per depth (never the
+ * persistent kernel), with no distinct-token or tiled paths.  All calls on
+ * one device share that array, which keeps the last call's contents: calls
+ * whose work overlaps on the device race (use one stream per device, or
+ * order the streams).  Asynchronous on `stream`; argument errors return
+ * before anything is enqueued; dtree_last_error(NULL) describes the last
+ * failure of this call on the calling thread.                              */
+dtree_status dtree_build_round_static(const dtree_weights *w, const dtree_params *p,
+                                      int32_t batch, const float *H, const int32_t *root,
+                                      int32_t *tok, int32_t *parent, int32_t *depth,
+                                      float *score, uint8_t *mask, int32_t *n_nodes,
+                                      void *stream);
+
 /* Launch of the persistent depth loop (see dtree_build_round).
  *   cooperative  0: plain launches (the default; a context switches itself to
  *                cooperative launches after a round whose waits ran out),

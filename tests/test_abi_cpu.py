@@ -66,3 +66,18 @@ def test_binding_refuses_missing_library(tmp_path):
             _lib.load(str(tmp_path / "nope.so"))
     finally:
         _lib._lib = saved
+
+
+def test_static_round_refuses_oversized_workspace_before_device():
+    """The allocation-free round sizes its workspace on the host and refuses
+    one beyond its fixed device array before touching a device."""
+    lib = _lib.load()
+    w = _lib.dtree_weights(4096, 151936, 4096, 1024, 256, 1, *([ctypes.c_void_p(256)] * 9))
+    p = _lib.params(16, 32, 4, 16, 128, -0.05)
+    ptrs = [ctypes.c_void_p(256)] * 8
+    code = lib.dtree_build_round_static(ctypes.byref(w), ctypes.byref(p), 8, *ptrs, None)
+    assert code == 2   # DTREE_E_SHAPE
+    assert b"static scratch" in lib.dtree_last_error(None)
+    assert lib.dtree_build_round_static(None, ctypes.byref(p), 1, *ptrs, None) == 1
+    p.beta = 0.5
+    assert lib.dtree_build_round_static(ctypes.byref(w), ctypes.byref(p), 1, *ptrs, None) == 1
