@@ -168,9 +168,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen3_4b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--scoring", default="conditional", choices=["conditional", "marginal"],
-                    help="conditional (the method) or marginal (uncorrected base-logit "
-                         "scoring, the pages' comparison)")
+    ap.add_argument("--scoring", default="conditional",
+                    choices=["conditional", "marginal", "markov"],
+                    help="conditional (the method), marginal (uncorrected base-logit "
+                         "scoring, the pages' comparison) or markov (parent-token-only "
+                         "correction)")
     ap.add_argument("--cold-rounds", type=int, default=0,
                     help="also time this many rounds, each after a 1 GiB device read that "
                          "evicts the caches (cold_latency_us)")

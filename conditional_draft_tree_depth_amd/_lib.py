@@ -212,11 +212,12 @@ def dtree_set_persistent_launch(ctx, cooperative, spin_limit=0):
            load().dtree_set_persistent_launch(ctx, int(cooperative), int(spin_limit)), ctx)
 
 
-SCORE_CONDITIONAL, SCORE_MARGINAL = 0, 1
-SCORINGS = {"conditional": SCORE_CONDITIONAL, "marginal": SCORE_MARGINAL}
+SCORE_CONDITIONAL, SCORE_MARGINAL, SCORE_MARKOV = 0, 1, 2
+SCORINGS = {"conditional": SCORE_CONDITIONAL, "marginal": SCORE_MARGINAL,
+            "markov": SCORE_MARKOV}
 
 
 def dtree_set_scoring(ctx, scoring):
-    """scoring: "conditional" / "marginal" (or the DTREE_SCORE_* value)."""
+    """scoring: "conditional" / "marginal" / "markov" (or the DTREE_SCORE_* value)."""
     code = SCORINGS[scoring] if isinstance(scoring, str) else int(scoring)
     _check("dtree_set_scoring", load().dtree_set_scoring(ctx, code), ctx)

@@ -438,6 +438,9 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
 
 
   const bool marginal = ctx->scoring == DTREE_SCORE_MARGINAL;
+  // Markov scoring: each survivor's GRU step starts from a zero state, so
+  // the W_hh product of the branches is not needed
+  const bool markov = ctx->scoring == DTREE_SCORE_MARKOV;
   const bool pk = !marginal && ctx->pk && batch * M <= 64 && batch * D * M <= ctx->pk_rows &&
                   persist_eligible(batch, D, M, K, W, s, w.e, r, wt, ctx->lds_max);
   int A = 1, off = 1, sc = 0;
@@ -459,7 +462,7 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
     PersistArgs pa{batch, D, M, K, W, s, w.e, w.V, w.W_ih, w.W_hh, w.Emb, w.b_ih, w.b_hh,
                    ws.C, root, ws.G, ws.g, ws.pk_terms, ws.pk_terms + persist_terms_floats(s),
                    ws.pk_part, ws.gitab, ws.flags, ctx->pk_fail_dev, ctx->pk_spin,
-                   ctx->epoch, tb};
+                   ctx->epoch, tb, markov ? 1 : 0};
     HIPCHK(ctx, launch_depth_persistent(pa, ctx->pk_coop, st));
     ctx->epoch += (uint32_t)D + 1u;
     for (int dd = 0; dd < D; ++dd) {
@@ -508,7 +511,7 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
       //   W_hh . S + b_hh                  (outputs r .. r+3s-1, the GRU state
       //                                      part of all of the branch's children)
       const int ldu = r + 3 * s;
-      if (ws.wcat) {
+      if (ws.wcat && !markov) {
         g = GemmArgs{batch * A, ldu, s, ws.S[sc], WT_F32, s, nullptr, 0, ws.wcat, wt, s, w.b_hh,
                      ws.uH, r, A, D, dd, ws.uh, ldu};
         g.add_n = r;
@@ -530,9 +533,11 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
                      static_cast<const uint8_t *>(w.W1) + (size_t)d * esz, wt, d + s, nullptr,
                      ws.uH, r, A, D, dd, ws.uh, ldu};
         HIPCHK(ctx, launch_gemm(g, st));
-        g = GemmArgs{batch * A, 3 * s, s, ws.S[sc], WT_F32, s, nullptr, 0, w.W_hh, wt, s, w.b_hh,
-                     nullptr, 0, 1, 0, 0, ws.uh + r, ldu};
-        HIPCHK(ctx, launch_gemm(g, st));
+        if (!markov) {
+          g = GemmArgs{batch * A, 3 * s, s, ws.S[sc], WT_F32, s, nullptr, 0, w.W_hh, wt, s,
+                       w.b_hh, nullptr, 0, 1, 0, 0, ws.uh + r, ldu};
+          HIPCHK(ctx, launch_gemm(g, st));
+        }
       }
       // (with many branches x candidates per request the separate correction
       // kernel spreads that work over more workgroups)
@@ -554,8 +559,10 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
         }
         HIPCHK(ctx, launch_gru_combine(batch * An, s, precomp ? ws.gi_all : ws.gi,
                                        precomp ? ws.gidx_cand : nullptr,
-                                       precomp == 2 ? ws.rowmap : nullptr, ws.uh + r, ldu, nullptr,
-                                       ws.S[sc], ws.gidx_par, ws.S[1 - sc], ws.S3[1 - sc], st));
+                                       precomp == 2 ? ws.rowmap : nullptr,
+                                       markov ? nullptr : ws.uh + r, ldu,
+                                       markov ? w.b_hh : nullptr, markov ? nullptr : ws.S[sc],
+                                       ws.gidx_par, ws.S[1 - sc], ws.S3[1 - sc], st));
         sc = 1 - sc;
       }
       cur = 1 - cur;
@@ -667,8 +674,10 @@ extern "C" dtree_status dtree_set_persistent_launch(dtree_ctx *ctx, int32_t coop
 extern "C" dtree_status dtree_set_scoring(dtree_ctx *ctx, int32_t scoring) {
   if (!ctx) return DTREE_E_ARG;
   ctx->err.clear();
-  if (scoring != DTREE_SCORE_CONDITIONAL && scoring != DTREE_SCORE_MARGINAL)
-    return fail(ctx, DTREE_E_ARG, "scoring must be DTREE_SCORE_CONDITIONAL or DTREE_SCORE_MARGINAL");
+  if (scoring != DTREE_SCORE_CONDITIONAL && scoring != DTREE_SCORE_MARGINAL &&
+      scoring != DTREE_SCORE_MARKOV)
+    return fail(ctx, DTREE_E_ARG,
+                "scoring must be DTREE_SCORE_CONDITIONAL, DTREE_SCORE_MARGINAL or DTREE_SCORE_MARKOV");
   ctx->scoring = scoring;
   return DTREE_OK;
 }

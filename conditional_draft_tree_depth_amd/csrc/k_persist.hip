@@ -175,6 +175,7 @@ struct PKParams {
   uint32_t *host_fail;   // host-visible word, set when a wait ran out (or null)
   uint32_t spin;         // polls before a wait gives up
   uint32_t epoch0;
+  int markov;            // nonzero: every GRU step starts from a zero state
   TreeBufs t;
 };
 
@@ -587,7 +588,8 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
     f32x4 acc[PK_NMT];
 #pragma unroll
     for (int mt = 0; mt < PK_NMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (more) {
+    // (zero-state steps: the product is zero and the state part is b_hh)
+    if (more && !p.markov) {
       const int npass = pk_npass(rows);
       // fragments of k-step i + 1 are read while those of k-step i feed the
       // matrix cores; slots past the 3 x rp used ones share their columns
@@ -788,7 +790,7 @@ __device__ void pk_consumer(const PKParams &p, uint8_t *smem) {
       const int pr = sinfo[i * 8 + 1], jc = sinfo[i * 8 + 3];
       const float *a = gis + (q * M + jc) * 3 * PK_CU;
       const int half = u >> 4, ul = u & 15;
-      const float h = sn_cur[pr * PK_CU + u];
+      const float h = p.markov ? 0.f : sn_cur[pr * PK_CU + u];
       const float *gh = ghs + (half * 16 + pr) * 16 + ul;   // gate g at + g * PK_HALF * 256
       const float r = 1.f / (1.f + expf(-(a[u] + gh[0])));
       const float z = 1.f / (1.f + expf(-(a[PK_CU + u] + gh[PK_HALF * 256])));
@@ -896,6 +898,7 @@ hipError_t launch_depth_persistent(const PersistArgs &a, bool cooperative, hipSt
   p.T1 = reinterpret_cast<uint16_t *>(a.T1);
   p.part = a.part; p.gitab = a.gitab; p.flags = a.flags;
   p.epoch0 = a.epoch0;
+  p.markov = a.markov;
   p.host_fail = a.host_fail;
   p.spin = a.spin ? a.spin : PK_SPIN;
   p.t = a.t;

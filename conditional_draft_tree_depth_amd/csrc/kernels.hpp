@@ -192,6 +192,7 @@ struct PersistArgs {
   uint32_t spin;         // polls before a wait gives up (0: the default)
   uint32_t epoch0;
   TreeBufs t;
+  int markov;            // nonzero: zero-state GRU steps (no W_hh product)
 };
 bool persist_eligible(int b, int D, int M, int K, int W, int s, int e, int r, int wtype,
                       size_t lds_max);

@@ -202,10 +202,19 @@ dtree_status dtree_set_persistent_launch(dtree_ctx *ctx, int32_t cooperative,
  *       pages compare against with the same drafter and tree construction
  *       ("Resumen Técnico: DominoTree", Contribuciones Clave, the ablation of
  *       conditionality).  Everything else in the round is unchanged: Top-M
- *       per depth, log-softmax over M, Top-K, Top-W, global Top-B, mask.
+ *       per depth, log-softmax over M, Top-K, Top-W, global Top-B, mask;
+ *   DTREE_SCORE_MARKOV (2): a first-order correction that conditions on the
+ *       parent token only (DARTree page, Resultados Experimentales,
+ *       Ablación: the method also helps the DSpark drafter, whose
+ *       correction head is Markov).  Reading taken: a branch's causal state
+ *       is the GRU applied to its last token from a zero state,
+ *       S = GRU(Emb[token], 0) (the root's state is the same as in
+ *       conditional scoring); the low-rank head and the rest of the round
+ *       are unchanged.
  * DTREE_E_ARG for other values.                                            */
 #define DTREE_SCORE_CONDITIONAL 0
 #define DTREE_SCORE_MARGINAL 1
+#define DTREE_SCORE_MARKOV 2
 dtree_status dtree_set_scoring(dtree_ctx *ctx, int32_t scoring);
 
 /* Number of superarbol nodes (root included) a round with `p` builds per
