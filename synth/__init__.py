@@ -8,3 +8,4 @@ sides always see identical values.
 """
 from .configs import CONFIGS, Config, config_by_name  # noqa: F401
 from .inputs import make_inputs, custom_config  # noqa: F401
+from .attn import ATTN_CONFIGS, AttnConfig, make_attn_inputs, random_parents  # noqa: F401
