@@ -30,10 +30,11 @@ import numpy as np
 
 __all__ = ["ancestor_mask", "tree_attention", "parity_bound", "ATTN_REL_TOL"]
 
-# A kernel that rounds the softmax weights to bf16 (relative error <= 2^-9)
-# before the weighted sum of V and accumulates in fp32 over at most a few
-# thousand keys stays within  2^-9 * absw + (fp32 accumulation) of O.
-ATTN_REL_TOL = 2.0 ** -9 + 2.5e-4
+# A kernel that rounds the softmax weights to bf16 (8-bit significand: unit
+# roundoff 2^-8, so relative error <= 2^-8) before the weighted sum of V and
+# accumulates in fp32 over at most a few thousand keys stays within
+# 2^-8 * absw + (fp32 accumulation) of O.
+ATTN_REL_TOL = 2.0 ** -8 + 2.5e-4
 ATTN_ABS_TOL = 1e-5
 
 
