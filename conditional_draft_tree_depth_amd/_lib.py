@@ -18,7 +18,7 @@ EXPORTS = ("dtree_create", "dtree_build_round", "dtree_build_round_static",
            "dtree_superarbol_nodes",
            "dtree_get_trace", "dtree_profile_enable", "dtree_profile_read",
            "dtree_set_persistent_launch", "dtree_set_scoring", "dtree_last_error",
-           "dtree_destroy")
+           "dtree_destroy", "dtree_tree_attention_workspace", "dtree_tree_attention")
 NSTAGES = 6
 STAGES = ("round_start", "lmhead_topm", "topm_merge", "prologue", "depth_loop", "topb_emit")
 
@@ -46,6 +46,14 @@ class dtree_trace(ctypes.Structure):
     _fields_ = [("C", c_vp), ("Cl", c_vp), ("node_tok", c_vp), ("node_parent", c_vp),
                 ("node_score", c_vp), ("surv", c_vp), ("sel", c_vp), ("n_sa", c_i32),
                 ("status", c_i32)]
+
+
+class dtree_attn_args(ctypes.Structure):
+    _fields_ = [("batch", c_i32), ("n_max", c_i32), ("Hq", c_i32), ("Hkv", c_i32),
+                ("dh", c_i32), ("L_cap", c_i32), ("Q", c_vp), ("K", c_vp), ("V", c_vp),
+                ("prefix_len", c_vp), ("n_nodes", c_vp), ("mask", c_vp), ("scale", c_f32),
+                ("O", c_vp), ("splits", c_i32), ("workspace", c_vp),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class DTreeError(RuntimeError):
@@ -94,6 +102,10 @@ def load(path=LIB_PATH):
     lib.dtree_last_error.restype = ctypes.c_char_p
     lib.dtree_destroy.argtypes = [c_vp]
     lib.dtree_destroy.restype = c_i32
+    lib.dtree_tree_attention_workspace.argtypes = [P(dtree_attn_args), P(ctypes.c_size_t)]
+    lib.dtree_tree_attention_workspace.restype = c_i32
+    lib.dtree_tree_attention.argtypes = [P(dtree_attn_args), c_vp]
+    lib.dtree_tree_attention.restype = c_i32
     _lib = lib
     return lib
 
@@ -221,3 +233,32 @@ def dtree_set_scoring(ctx, scoring):
     """scoring: "conditional" / "marginal" / "markov" (or the DTREE_SCORE_* value)."""
     code = SCORINGS[scoring] if isinstance(scoring, str) else int(scoring)
     _check("dtree_set_scoring", load().dtree_set_scoring(ctx, code), ctx)
+
+
+def attn_args(Q, K, V, prefix_len, n_nodes, mask, scale, O, splits=0, workspace=None):
+    """dtree_attn_args of device tensors: Q [b, n_max, Hq, dh] and K, V
+    [b, Hkv, L_cap, dh] bf16 (torch.bfloat16 or int16 views), prefix_len and
+    n_nodes [b] int32, mask [b, n_max, n_max] uint8, O [b, n_max, Hq, dh] fp32."""
+    b, n_max, Hq, dh = Q.shape
+    Hkv, L_cap = K.shape[1], K.shape[2]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return dtree_attn_args(b, n_max, Hq, Hkv, dh, L_cap, _ptr(Q), _ptr(K), _ptr(V),
+                           _ptr(prefix_len), _ptr(n_nodes), _ptr(mask), float(scale), _ptr(O),
+                           int(splits), _ptr(workspace), nbytes)
+
+
+def dtree_tree_attention_workspace(a):
+    """Workspace bytes a dtree_attn_args needs (0: none)."""
+    n = ctypes.c_size_t(0)
+    _check("dtree_tree_attention_workspace",
+           load().dtree_tree_attention_workspace(ctypes.byref(a), ctypes.byref(n)))
+    return n.value
+
+
+def dtree_tree_attention(a, stream=None):
+    """Enqueue one tree-attention call (see dtree.h)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    _check("dtree_tree_attention",
+           load().dtree_tree_attention(ctypes.byref(a), ctypes.c_void_p(stream)))

@@ -890,3 +890,87 @@ extern "C" dtree_status dtree_build_round_static(const dtree_weights *w, const d
 }
 
 static const char *g_static_err_text() { return g_static_err; }
+
+// ---------------------------------------------------------------------------
+// tree-attention verification
+
+static dtree_status attn_check(const dtree_attn_args *a, int *splits) {
+  if (!a) return static_fail(DTREE_E_ARG, "null arguments");
+  if (a->batch < 1 || a->n_max < 1) return static_fail(DTREE_E_ARG, "batch and n_max must be >= 1");
+  if (a->n_max > 4096) return static_fail(DTREE_E_SHAPE, "n_max must be <= 4096");
+  if (a->dh != 64 && a->dh != 128) return static_fail(DTREE_E_SHAPE, "dh must be 64 or 128");
+  if (a->Hkv < 1 || a->Hq < 1 || a->Hq % a->Hkv)
+    return static_fail(DTREE_E_SHAPE, "Hq must be a positive multiple of Hkv");
+  if (a->Hq / a->Hkv > 64) return static_fail(DTREE_E_SHAPE, "Hq / Hkv must be <= 64");
+  if (a->L_cap < a->n_max) return static_fail(DTREE_E_SHAPE, "L_cap must be >= n_max");
+  if ((long long)a->batch * a->Hkv * a->L_cap * a->dh >= (1LL << 40) ||
+      (long long)a->batch * a->n_max * a->Hq * a->dh >= (1LL << 31))
+    return static_fail(DTREE_E_SHAPE, "tensors too large");
+  if (!(std::isfinite(a->scale) && a->scale > 0.f))
+    return static_fail(DTREE_E_ARG, "scale must be finite and > 0");
+  if (a->splits < 0 || a->splits > 256) return static_fail(DTREE_E_ARG, "splits outside [0, 256]");
+  const long long rb = ((long long)a->n_max * (a->Hq / a->Hkv) + 63) / 64;
+  const int S = dtree::tree_attn_splits(a->batch, a->n_max, a->Hq, a->Hkv, a->L_cap, a->splits);
+  if (rb * a->Hkv * a->batch * S >= (1LL << 31))
+    return static_fail(DTREE_E_SHAPE, "grid too large");
+  *splits = S;
+  return DTREE_OK;
+}
+
+extern "C" dtree_status dtree_tree_attention_workspace(const dtree_attn_args *a, size_t *bytes) {
+  g_static_err[0] = '\0';
+  if (!bytes) return static_fail(DTREE_E_ARG, "null output pointer");
+  int S = 1;
+  const dtree_status st = attn_check(a, &S);
+  if (st != DTREE_OK) return st;
+  *bytes = dtree::tree_attn_workspace(a->batch, a->n_max, a->Hq, a->Hkv, a->dh, S);
+  return DTREE_OK;
+}
+
+namespace {
+int g_attn_arch[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+}
+
+extern "C" dtree_status dtree_tree_attention(const dtree_attn_args *a, void *stream) {
+  g_static_err[0] = '\0';
+  int S = 1;
+  const dtree_status st = attn_check(a, &S);
+  if (st != DTREE_OK) return st;
+  if (!a->Q || !a->K || !a->V || !a->prefix_len || !a->n_nodes || !a->mask || !a->O)
+    return static_fail(DTREE_E_ARG, "null input or output pointer");
+  if (reinterpret_cast<uintptr_t>(a->Q) % 16 || reinterpret_cast<uintptr_t>(a->K) % 16 ||
+      reinterpret_cast<uintptr_t>(a->V) % 16 || reinterpret_cast<uintptr_t>(a->O) % 16)
+    return static_fail(DTREE_E_ARG, "Q, K, V and O must be 16-byte aligned");
+  const size_t need = dtree::tree_attn_workspace(a->batch, a->n_max, a->Hq, a->Hkv, a->dh, S);
+  if (need && (!a->workspace || a->workspace_bytes < need ||
+               reinterpret_cast<uintptr_t>(a->workspace) % 256)) {
+    char m[160];
+    std::snprintf(m, sizeof m, "needs a 256-byte aligned workspace of %zu bytes", need);
+    return static_fail(DTREE_E_ARG, m);
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return static_fail(DTREE_E_DEVICE, "no current HIP device");
+  int arch = 0;
+  {
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    if (!g_attn_arch[dev]) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return static_fail(DTREE_E_DEVICE, "device query failed");
+      g_attn_arch[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    arch = g_attn_arch[dev];
+  }
+  if (arch < 0) return static_fail(DTREE_E_DEVICE, "needs a gfx950 device");
+  dtree::TreeAttnArgs t{a->batch, a->n_max, a->Hq, a->Hkv, a->dh, a->L_cap, S,
+                        a->Q, a->K, a->V, a->prefix_len, a->n_nodes, a->mask,
+                        a->scale, a->O, a->workspace};
+  const hipError_t e = dtree::launch_tree_attn(t, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    char m[160];
+    std::snprintf(m, sizeof m, "tree attention launch: %s", hipGetErrorString(e));
+    return static_fail(DTREE_E_HIP, m);
+  }
+  return DTREE_OK;
+}

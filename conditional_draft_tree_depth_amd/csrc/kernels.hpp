@@ -211,4 +211,19 @@ hipError_t launch_corr_tables(int rows, int M, int r, int s, const void *W2, con
 hipError_t launch_depth_persistent(const PersistArgs &a, bool cooperative, hipStream_t st);
 hipError_t corr_logits_prepare(int wtype, size_t lds_bytes);
 
+// ---- tree-attention verification (k_attn.hip)
+struct TreeAttnArgs {
+  int batch, n_max, Hq, Hkv, dh, L_cap, splits;
+  const void *Q, *K, *V;
+  const int32_t *prefix_len, *n_nodes;
+  const uint8_t *mask;
+  float scale;
+  float *O;
+  void *workspace;
+};
+// key splits per row block (requested > 0 is taken as is)
+int tree_attn_splits(int batch, int n_max, int Hq, int Hkv, int L_cap, int requested);
+size_t tree_attn_workspace(int batch, int n_max, int Hq, int Hkv, int dh, int splits);
+hipError_t launch_tree_attn(const TreeAttnArgs &a, hipStream_t st);
+
 }  // namespace dtree

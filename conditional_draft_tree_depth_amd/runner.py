@@ -55,3 +55,41 @@ class Round:
         if self.ctx is not None:
             _lib.dtree_destroy(self.ctx)
             self.ctx = None
+
+
+class TreeAttention:
+    """Device buffers for tree-attention calls of one shape: Q, K, V (raw
+    bf16 bits as numpy uint16 or device tensors), per-request lengths, the
+    mask (numpy or a round's device mask), the output and the workspace."""
+
+    def __init__(self, Q, K, V, prefix_len, n_nodes, mask, scale, splits=0, device="cuda"):
+        import torch
+
+        def dev(a, dtype=None):
+            if isinstance(a, torch.Tensor):
+                return a.to(device).contiguous()
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            t = torch.from_numpy(a if dtype is None else a.astype(dtype))
+            return t.to(device)
+
+        self.Q, self.K, self.V = dev(Q), dev(K), dev(V)
+        self.prefix_len = dev(prefix_len, np.int32)
+        self.n_nodes = dev(n_nodes, np.int32)
+        self.mask = dev(mask, np.uint8)
+        self.O = torch.empty(tuple(self.Q.shape), dtype=torch.float32, device=device)
+        self.workspace = None
+        a = _lib.attn_args(self.Q, self.K, self.V, self.prefix_len, self.n_nodes, self.mask,
+                           scale, self.O, splits)
+        need = _lib.dtree_tree_attention_workspace(a)
+        if need:
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        self.args = _lib.attn_args(self.Q, self.K, self.V, self.prefix_len, self.n_nodes,
+                                   self.mask, scale, self.O, splits, self.workspace)
+
+    def run(self, stream=None):
+        _lib.dtree_tree_attention(self.args, stream)
+
+    def output(self):
+        return self.O.cpu().numpy()

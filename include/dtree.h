@@ -259,8 +259,65 @@ dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace *out);
 dtree_status dtree_profile_enable(dtree_ctx *ctx, int enable);
 dtree_status dtree_profile_read(dtree_ctx *ctx, float *ms, int32_t *rounds);
 
+/* ---- tree-attention verification ------------------------------------------
+ * One layer's attention of the target model's verification pass over an
+ * emitted draft tree ("Resumen Técnico: DominoTree", Componentes Principales
+ * 5: tree attention with an ancestor-only mask; "DARTree: Speculative
+ * Diffusion Decoding with Autoregressive Draft Trees", Metodología 2,
+ * verification).  Tree token i of request q attends to the request's
+ * verified prefix and to the tree tokens j with mask[q][i][j] = 1 (its
+ * root-to-node path, itself included, in the round's emitted convention):
+ *
+ *   O[q,i,h] = sum_k softmax_k(scale * Q[q,i,h] . K[q,h/G,k]) V[q,h/G,k]
+ *
+ * over the visible cache positions k: [0, prefix_len[q]) and
+ * prefix_len[q] + j for the visible nodes j.  G = Hq / Hkv query heads share
+ * one KV head (query head h reads KV head h / G).  bf16 inputs, fp32
+ * scores and sums; the softmax weights enter the weighted sum of V rounded
+ * to bf16 (so |O - exact| <= 2^-8 sum_k w_k |V_k| plus fp32 rounding).
+ *
+ * Layouts (all device memory, row-major):
+ *   Q           [batch, n_max, Hq, dh] bf16 (tree token i, head h);
+ *   K, V        [batch, Hkv, L_cap, dh] bf16: the KV cache, prefix at
+ *               positions [0, prefix_len[q]), tree token j at prefix_len[q] + j;
+ *   prefix_len  [batch] int32, n_nodes [batch] int32 (the round's n_nodes);
+ *   mask        [batch, n_max, n_max] uint8 (the round's mask, n_max = B + 1);
+ *   O           [batch, n_max, Hq, dh] fp32, caller-owned; rows i >= n_nodes[q]
+ *               are written as 0.
+ * Only positions below prefix_len[q] + n_nodes[q] are read.  The tree must be
+ * in the round's canonical order (every ancestor before its descendants).
+ * Limits: dh 64 or 128, Hq a multiple of Hkv with Hq / Hkv <= 64,
+ * n_max <= 4096 and <= L_cap; Q, K, V, O 16-byte aligned.
+ * splits: key ranges per block of 64 query rows whose partial results are
+ * merged by a second kernel (0: chosen from the shape to fill the device);
+ * with more than one, a workspace of dtree_tree_attention_workspace() bytes,
+ * 256-byte aligned, caller-owned, is needed (NULL when that size is 0).
+ * Errors: shapes and pointers are checked before anything is enqueued
+ * (DTREE_E_ARG / DTREE_E_SHAPE, DTREE_E_DEVICE off gfx950); text from
+ * dtree_last_error(NULL).  Per-request lengths live on the device and are
+ * checked there: a request with prefix_len < 0, n_nodes outside
+ * [1, n_max] or prefix_len + n_nodes > L_cap reads nothing and gets NaN in
+ * every row of O.  Asynchronous on `stream`; no host synchronisation; no
+ * state kept between calls (calls on different streams are independent if
+ * their workspaces differ).                                                 */
+typedef struct {
+  int32_t batch, n_max, Hq, Hkv, dh, L_cap;
+  const void *Q, *K, *V;
+  const int32_t *prefix_len, *n_nodes;
+  const uint8_t *mask;
+  float scale;        /* > 0, e.g. 1 / sqrt(dh) */
+  float *O;
+  int32_t splits;     /* 0 = automatic */
+  void *workspace;
+  size_t workspace_bytes;
+} dtree_attn_args;
+
+dtree_status dtree_tree_attention_workspace(const dtree_attn_args *a, size_t *bytes);
+dtree_status dtree_tree_attention(const dtree_attn_args *a, void *stream);
+
 /* Text of the last error on this context ("" if none); ctx may be NULL for
- * errors of dtree_create.  Valid until the next call on the context.        */
+ * errors of dtree_create, of the allocation-free round and of the attention
+ * calls.  Valid until the next call on the context.                         */
 const char *dtree_last_error(const dtree_ctx *ctx);
 
 /* Free the workspace.  NULL-safe.  The caller must ensure no enqueued round

@@ -81,3 +81,39 @@ def test_static_round_refuses_oversized_workspace_before_device():
     assert lib.dtree_build_round_static(None, ctypes.byref(p), 1, *ptrs, None) == 1
     p.beta = 0.5
     assert lib.dtree_build_round_static(ctypes.byref(w), ctypes.byref(p), 1, *ptrs, None) == 1
+
+
+def _attn(**over):
+    a = dict(batch=1, n_max=65, Hq=32, Hkv=8, dh=128, L_cap=4161, Q=256, K=256, V=256,
+             prefix_len=256, n_nodes=256, mask=256, scale=0.088, O=256, splits=0, workspace=None,
+             workspace_bytes=0)
+    a.update(over)
+    return _lib.dtree_attn_args(*[a[f] for f, _ in _lib.dtree_attn_args._fields_])
+
+
+def test_attention_workspace_sizes():
+    """Split choice and workspace size are host arithmetic: one block of 64
+    query rows per (request, KV head) at Qwen3-4B needs 13 splits to give
+    about two workgroups per CU; 8 requests of 129 tree tokens need none."""
+    ws = _lib.dtree_tree_attention_workspace
+    rows = 8 * 13 * 320       # Hkv x splits x padded rows (65 nodes x 4 heads -> 320)
+    assert ws(_attn()) == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 8
+    assert ws(_attn(splits=1)) == 0
+    assert ws(_attn(batch=8, n_max=129, L_cap=4225)) == 0
+    rows3 = 8 * 3 * 320
+    assert ws(_attn(splits=3)) == ((rows3 * 128 * 4 + 255) // 256) * 256 + rows3 * 8
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dh=96), 2), (dict(Hq=30), 2), (dict(Hkv=0), 2), (dict(L_cap=10), 2),
+    (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(splits=-1), 1),
+    (dict(batch=0), 1), (dict(n_max=5000, L_cap=9000), 2), (dict(Hq=8 * 65), 2),
+    (dict(Q=None), 1), (dict(O=None), 1), (dict(mask=None), 1), (dict(K=264), 1),
+    (dict(splits=4), 1),                       # needs a workspace
+    (dict(splits=4, workspace=256, workspace_bytes=16), 1),
+])
+def test_attention_rejects_bad_arguments_before_device(over, code):
+    lib = _lib.load()
+    a = _attn(**over)
+    assert lib.dtree_tree_attention(ctypes.byref(a), None) == code
+    assert lib.dtree_last_error(None)
