@@ -161,6 +161,129 @@ def _per_round_us(torch, stream, run, n, before=None):
     return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "rounds": n}
 
 
+def _ancestor_rows(parent, n, n_max):
+    """Ancestor-or-self mask rows of a synthetic tree (bench input only)."""
+    import numpy as np
+    m = np.zeros((n_max, n_max), np.uint8)
+    for i in range(n):
+        if i > 0:
+            m[i] = m[parent[i]]
+        m[i, i] = 1
+    return m
+
+
+def attention_counts(cfg, x, masks):
+    """Algorithmic bytes and flops of one tree-attention call: Q, the K/V
+    rows each request can see (prefix + its tree), the mask, the output;
+    4 dh flops per (query head, visible key) pair (Q.K and the weighted V)."""
+    b, n_max, Hq, dh, Hkv = cfg.batch, cfg.n_max, cfg.Hq, cfg.dh, cfg.Hkv
+    nbytes = 2 * b * n_max * Hq * dh + 4 * b * n_max * Hq * dh + b * n_max * n_max
+    flops = 0
+    for q in range(b):
+        P, n = int(x["prefix_len"][q]), int(x["n_nodes"][q])
+        nbytes += 2 * 2 * Hkv * (P + n) * dh
+        vis = n * P + int(masks[q][:n, :n].sum())
+        flops += 4 * dh * Hq * vis
+    return nbytes, flops
+
+
+def cpu_baseline_attention(cfg, x, masks, budget_s=10.0):
+    """The attention oracle as it stands, on whole calls of the workload."""
+    from oracle import tree_attention as TA
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    n, t0 = 0, time.perf_counter()
+    while True:
+        TA.tree_attention(x["Q"], x["K"], x["V"], x["prefix_len"], x["n_nodes"], masks,
+                          x["scale"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": n / el, "unit": "calls/s",
+            "cores": threads or len(os.sched_getaffinity(0)),
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "kind": "oracle",
+            "sample": f"{n} full {cfg.name} call(s) (numpy float64 oracle), {el:.1f} s"}
+
+
+def bench_attention(args):
+    """One step = one layer's tree-attention call of a verification pass.
+    The steps cycle over `layers` distinct K/V caches (as the layers of one
+    forward pass do), so no call finds its cache in the GPU's caches."""
+    import numpy as np
+    import torch
+    import synth
+    from conditional_draft_tree_depth_amd import _lib, runner
+
+    cfg = synth.ATTN_CONFIGS[args.config]
+    x = synth.make_attn_inputs(cfg, 0)
+    masks = np.stack([_ancestor_rows(x["parent"][q], int(x["n_nodes"][q]), cfg.n_max)
+                      for q in range(cfg.batch)])
+    base = runner.TreeAttention(x["Q"], x["K"], x["V"], x["prefix_len"], x["n_nodes"], masks,
+                                x["scale"], args.splits)
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    calls = [base]
+    for _ in range(args.layers - 1):
+        K = (torch.randn(base.K.shape, device="cuda", generator=gen) * 2).to(torch.bfloat16)
+        V = torch.randn(base.V.shape, device="cuda", generator=gen).to(torch.bfloat16)
+        calls.append(runner.TreeAttention(base.Q, K, V, base.prefix_len, base.n_nodes, base.mask,
+                                          x["scale"], args.splits))
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        calls[i % len(calls)].run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        calls[i % len(calls)].run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    lat = _per_round_us(torch, stream, lambda: calls[0].run(), min(args.steps, 50))
+    nbytes, flops = attention_counts(cfg, x, masks)
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    t_call = ev_ms * 1e-3
+    if flops / nbytes >= ridge:
+        roof = {"bound": "mfma", "achieved": flops / t_call / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "flops_per_launch": flops}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / t_call / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "bytes_per_launch": nbytes}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = ("k_tree_attn + k_tree_attn_merge (one call: the split attention "
+                      "kernel and the merge of its key splits)")
+    t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
+    line = {
+        "metric": "tree-attention verification calls/s (one layer, ancestor mask), "
+                  "% of HBM/MFMA roofline",
+        "value": 1e3 / ms, "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "us_per_call": ms * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "dh": cfg.dh,
+                   "n_max": cfg.n_max, "batch": cfg.batch, "prefix": list(cfg.prefix),
+                   "layers_cycled": len(calls),
+                   "splits": args.splits or "automatic"},
+        "roofline": roof,
+        "call_roofline": {"t_roof_us": t_roof * 1e6, "frac": t_roof / t_call,
+                          "bytes": nbytes, "flops": flops},
+        "event_ms_per_step": ev_ms,
+        "latency_us_same_cache": lat,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_attention(cfg, x, masks)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,12 +302,20 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy a 256 MiB device buffer three times (a kernel of known "
                          "traffic, to scale hardware byte counters)")
+    ap.add_argument("--layers", type=int, default=36,
+                    help="attention workloads: distinct K/V caches cycled over the steps")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="attention workloads: key splits per row block (0: the library's "
+                         "choice)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(requests would shard across GPUs with no exchange between them)",
               file=sys.stderr)
         sys.exit(2)
+    if args.config.startswith("attn_"):
+        bench_attention(args)
+        return
 
     import torch
     import synth

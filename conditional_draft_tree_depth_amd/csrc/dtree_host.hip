@@ -903,6 +903,8 @@ static dtree_status attn_check(const dtree_attn_args *a, int *splits) {
     return static_fail(DTREE_E_SHAPE, "Hq must be a positive multiple of Hkv");
   if (a->Hq / a->Hkv > 64) return static_fail(DTREE_E_SHAPE, "Hq / Hkv must be <= 64");
   if (a->L_cap < a->n_max) return static_fail(DTREE_E_SHAPE, "L_cap must be >= n_max");
+  if ((long long)a->L_cap * a->dh >= (1LL << 30))
+    return static_fail(DTREE_E_SHAPE, "L_cap * dh must be < 2^30 (32-bit byte offsets)");
   if ((long long)a->batch * a->Hkv * a->L_cap * a->dh >= (1LL << 40) ||
       (long long)a->batch * a->n_max * a->Hq * a->dh >= (1LL << 31))
     return static_fail(DTREE_E_SHAPE, "tensors too large");

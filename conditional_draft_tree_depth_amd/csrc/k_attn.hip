@@ -32,6 +32,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -40,15 +41,17 @@ namespace dtree {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int TA_THREADS = 256;
-constexpr int TA_QB = 64;      // query rows per workgroup
-constexpr int TA_KT = 64;      // keys per tile (16 per wave)
-constexpr int TA_KPAD = 8;     // bf16 padding of a K row in LDS
-constexpr int TA_VROW = TA_KT + 4;   // bf16 per V^T row in LDS (4 of padding)
-constexpr int TA_OPAD = 4;     // fp32 padding of an output row in LDS
+constexpr int TA_WROWS = 32;          // query rows per wave (two 16-row q-tiles)
+constexpr int TA_QB = 4 * TA_WROWS;   // query rows per workgroup
+constexpr int TA_KT = 64;             // keys per tile
+constexpr int TA_KPAD = 8;            // bf16 padding of a K row in LDS
+constexpr int TA_VROW = TA_KT + 4;    // bf16 per V^T row in LDS (4 of padding)
+constexpr float TA_TAU = 8.f;         // lazy softmax reference: slack in log2 units
 
 struct TAParams {
   const uint16_t *Q, *K, *V;
@@ -63,12 +66,34 @@ struct TAParams {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// two fp32 values to bf16, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 __device__ __forceinline__ bool request_ok(int P, int n, int n_max, int L_cap) {
   return P >= 0 && n >= 1 && n <= n_max && P <= L_cap - n;
+}
+
+// Max / sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups
+// that hold one query row's keys), with the gfx950 lane-swap instructions:
+// each swap leaves a lane holding its own value and its partner's, in some
+// order; max and + are symmetric, so every lane of the four gets the same bits.
+__device__ __forceinline__ float swap_pair_max(float v, bool x32) {
+  const auto r = x32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                     : __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_pair_sum(float v, bool x32) {
+  const auto r = x32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                     : __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float group4_max(float v) {
+  return swap_pair_max(swap_pair_max(v, false), true);
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  return swap_pair_sum(swap_pair_sum(v, false), true);
 }
 
 // Work item of a linear workgroup id.  Workgroup i runs on XCD i % 8; the
@@ -80,21 +105,16 @@ __device__ __forceinline__ int work_item(int lin, int total) {
 }
 
 template <int DH>
-__global__ __launch_bounds__(TA_THREADS) void k_tree_attn(TAParams p) {
+__global__ __launch_bounds__(TA_THREADS, 2) void k_tree_attn(TAParams p) {
   constexpr int NKS = DH / 32;        // 32-dim k-steps of Q.K
   constexpr int NDT = DH / 16;        // 16-dim output tiles
   constexpr int KROW = DH + TA_KPAD;  // bf16 per K row in LDS
   constexpr int KCH = TA_KT * DH / 8 / TA_THREADS;   // 16-byte K chunks per thread
   constexpr int VQ = 16 * DH / 8;     // (key quad, 8-dim chunk) pairs per tile
-  constexpr int KBYTES = TA_KT * KROW * 2, VBYTES = DH * TA_VROW * 2;
-  constexpr int OBYTES = TA_QB * (DH + TA_OPAD) * 4;
-  // K tile, then the V^T tile; after the loop the same bytes hold the
-  // merged output rows [TA_QB][DH + TA_OPAD] fp32
-  __shared__ __align__(16) uint8_t smem[KBYTES + VBYTES > OBYTES ? KBYTES + VBYTES : OBYTES];
-  __shared__ float mw[4][TA_QB], lw[4][TA_QB];
-  uint16_t *Ks = reinterpret_cast<uint16_t *>(smem);
-  uint16_t *Vt = reinterpret_cast<uint16_t *>(smem + KBYTES);
-  float *Obuf = reinterpret_cast<float *>(smem);
+  // two tile buffers: tile t is read from buffer t & 1 while tile t + 1 is
+  // written into the other one
+  __shared__ __align__(16) uint16_t Ksb[2][TA_KT * KROW];
+  __shared__ __align__(16) uint16_t Vtb[2][DH * TA_VROW];
 
   const int total = p.RB * p.Hkv * p.b * p.S;
   const int w = work_item(blockIdx.x, total);
@@ -143,13 +163,14 @@ __global__ __launch_bounds__(TA_THREADS) void k_tree_attn(TAParams p) {
     return;
   }
 
-  // query fragments (B operand of S^T = K Q^T): lane holds query row lr of
-  // q-tile qt, dims 32 ks + 8 g .. + 8
-  uint4 qf[4][NKS];
-  const uint8_t *mrow[4];
+  // this wave's 32 query rows: fragments of the B operand of S^T = K Q^T
+  // (lane: row lr of q-tile qt, dims 32 ks + 8 g .. + 8) and mask rows
+  const int wr0 = r0 + TA_WROWS * wave;
+  uint4 qf[2][NKS];
+  const uint8_t *mrow[2];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const int r = r0 + 16 * qt + lr;
+  for (int qt = 0; qt < 2; ++qt) {
+    const int r = wr0 + 16 * qt + lr;
     const bool ok = r < nrows;
     const int i = ok ? r / G : 0, hq = kvh * G + (ok ? r % G : 0);
     const uint16_t *src = p.Q + ((size_t)q * p.n_max + i) * ostride + (size_t)hq * DH + 8 * g;
@@ -163,189 +184,237 @@ __global__ __launch_bounds__(TA_THREADS) void k_tree_attn(TAParams p) {
   const uint16_t *Vg = p.V + ((size_t)q * p.Hkv + kvh) * p.L_cap * DH;
   // staged tile in registers: K chunks (key, 8 dims) and V quads (4 keys x 8 dims)
   uint4 kr[KCH], vr[4];
-  auto fetch = [&](int k0) {
+  // Tile loads through buffer descriptors whose size ends at key ke: the
+  // hardware returns zeros for every key at or past ke (partial tiles need
+  // no per-lane test), and each load is one 32-bit offset add.
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(Kg), (short)0, ke * DH * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(Vg), (short)0, ke * DH * 2, 0x00020000);
+  // K chunk u of this thread: key tid / (DH / 8) + u * 256 / (DH / 8), dims
+  // 8 (tid % (DH / 8)) .. + 8, i.e. byte offset kbase + 4096 u; V quad: keys
+  // 4 (tid & 15) + u, dims 8 (tid >> 4) .. + 8
+  const int kbase = (tid / (DH / 8)) * DH * 2 + (tid % (DH / 8)) * 16;
+  const int vbase = 4 * (tid & 15) * DH * 2 + (tid >> 4) * 16;
+  auto ld = [](__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  };
+  auto fetch_tile = [&](int k0) {
+    const int t0 = k0 * DH * 2;
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = tid + TA_THREADS * u, key = c / (DH / 8), col = c % (DH / 8);
-      const int k = k0 + key;
-      kr[u] = k < ke ? *reinterpret_cast<const uint4 *>(Kg + (size_t)k * DH + 8 * col)
-                     : make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < KCH; ++u) kr[u] = ld(krs, t0 + kbase + 4096 * u);
     if (tid < VQ) {
-      const int kq = tid / (DH / 8), col = tid % (DH / 8);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int k = k0 + 4 * kq + u;
-        vr[u] = k < ke ? *reinterpret_cast<const uint4 *>(Vg + (size_t)k * DH + 8 * col)
-                       : make_uint4(0, 0, 0, 0);
-      }
+      for (int u = 0; u < 4; ++u) vr[u] = ld(vrs, t0 + vbase + u * DH * 2);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
+    uint16_t *Ks = Ksb[buf], *Vt = Vtb[buf];
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       const int c = tid + TA_THREADS * u, key = c / (DH / 8), col = c % (DH / 8);
       *reinterpret_cast<uint4 *>(Ks + key * KROW + 8 * col) = kr[u];
     }
     if (tid < VQ) {
-      const int kq = tid / (DH / 8), col = tid % (DH / 8);
-      // V^T rows 8 col + d, keys 4 kq .. 4 kq + 3
-      const uint32_t *v32[4] = {reinterpret_cast<const uint32_t *>(&vr[0]),
-                                reinterpret_cast<const uint32_t *>(&vr[1]),
-                                reinterpret_cast<const uint32_t *>(&vr[2]),
-                                reinterpret_cast<const uint32_t *>(&vr[3])};
+      // V^T rows 8 col + d, keys 4 kq .. 4 kq + 3; the 16 lanes of a row
+      // group write 16 different key quads of one row (distinct banks)
+      const int kq = tid & 15, col = tid >> 4;
+      const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+      const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
+      const uint32_t w2[4] = {vr[2].x, vr[2].y, vr[2].z, vr[2].w};
+      const uint32_t w3[4] = {vr[3].x, vr[3].y, vr[3].z, vr[3].w};
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const int sh = (d & 1) * 16;
-        const uint32_t e0 = (v32[0][d >> 1] >> sh) & 0xFFFFu, e1 = (v32[1][d >> 1] >> sh) & 0xFFFFu;
-        const uint32_t e2 = (v32[2][d >> 1] >> sh) & 0xFFFFu, e3 = (v32[3][d >> 1] >> sh) & 0xFFFFu;
-        *reinterpret_cast<uint2 *>(Vt + (8 * col + d) * TA_VROW + 4 * kq) =
-            make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+      for (int m = 0; m < 4; ++m) {
+        // low halves (dim 2m) and high halves (dim 2m + 1) of the 4 keys
+        *reinterpret_cast<uint2 *>(Vt + (8 * col + 2 * m) * TA_VROW + 4 * kq) =
+            make_uint2(__builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u),
+                       __builtin_amdgcn_perm(w3[m], w2[m], 0x05040100u));
+        *reinterpret_cast<uint2 *>(Vt + (8 * col + 2 * m + 1) * TA_VROW + 4 * kq) =
+            make_uint2(__builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u),
+                       __builtin_amdgcn_perm(w3[m], w2[m], 0x07060302u));
       }
     }
   };
 
-  float m[4], l[4];
-  f32x4 o[NDT][4];
+  // online softmax with a lazily moved reference: the reference m only
+  // moves when a score exceeds it by more than TA_TAU (log2 units), so the
+  // weights 2^(x - m) stay below 2^TA_TAU and rescales are rare
+  float mref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  f32x4 o[2][NDT];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    m[qt] = -INFINITY;
-    l[qt] = 0.f;
+  for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-    for (int nt = 0; nt < NDT; ++nt) o[nt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int nt = 0; nt < NDT; ++nt) o[qt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  fetch(kb);
-  for (int k0 = kb; k0 < ke; k0 += TA_KT) {
-    stage();
-    __syncthreads();
-    if (k0 + TA_KT < ke) fetch(k0 + TA_KT);   // lands while this tile is used
+  // one tile: MASKED tiles hold tree keys or run past ke (the mask and the
+  // bounds are tested per key); the others are full tiles of prefix keys
+  // Tile k0 is in buffer buf; the registers hold tile k0 + TA_KT (if any),
+  // which goes to the other buffer after this tile's products, followed by
+  // the loads of tile k0 + 2 TA_KT and one barrier.  A buffer is rewritten
+  // only after the barrier that ends the tile that read it.
+  auto tile = [&](int k0, int buf, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const uint16_t *Ks = Ksb[buf], *Vt = Vtb[buf];
 
-    // S^T for this wave's 16 keys and the 64 query rows
-    f32x4 sc[4];
+    // S^T: four 16-key blocks x two q-tiles; lane: query lr, keys 16 kb4 + 4 g + t
+    f32x4 sc[2][4];
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) sc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4 *>(Ks + (16 * wave + lr) * KROW + 32 * ks + 8 * g);
+      for (int k4 = 0; k4 < 4; ++k4) sc[qt][k4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K fragments are read from LDS two steps ahead of their products (a
+    // ring of three), so the LDS latency overlaps the matrix cores
+    {
+      constexpr int NF = 4 * NKS;
+      // order: k-step outer, key block inner, so consecutive products go to
+      // different accumulators
+      auto kfrag = [&](int f) {
+        const int ks = f / 4, k4 = f % 4;
+        return *reinterpret_cast<const uint4 *>(Ks + (16 * k4 + lr) * KROW + 32 * ks + 8 * g);
+      };
+      uint4 ring[3];
+      ring[0] = kfrag(0);
+      ring[1] = kfrag(1);
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
-        sc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qf[qt][ks]), sc[qt],
-                                                         0, 0, 0);
-    }
-    // lane: query lr of each q-tile, keys kk0 + t
-    const int kk0 = k0 + 16 * wave + 4 * g;
-    const bool tree = k0 + TA_KT > P;   // the tile holds tree keys (uniform)
-    i16x4 pk[4];
+      for (int f = 0; f < NF; ++f) {
+        if (f + 2 < NF) ring[(f + 2) % 3] = kfrag(f + 2);
+        __builtin_amdgcn_sched_barrier(0);   // keep the read ahead of the products
+        const int ks = f / 4, k4 = f % 4;
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      float v[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int kk = kk0 + t;
-        bool vis = kk < ke;
-        if (tree && vis && kk >= P) vis = mrow[qt][kk - P] != 0;
-        v[t] = vis ? sc[qt][t] * p.scale_log2 : -INFINITY;
+        for (int qt = 0; qt < 2; ++qt)
+          sc[qt][k4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[f % 3]),
+                                                               as_bf16x8(qf[qt][ks]), sc[qt][k4], 0, 0, 0);
       }
-      float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[qt], mx);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = exp2f(m[qt] - mu);
-      float e[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) e[t] = exp2f(v[t] - mu);
-      l[qt] = l[qt] * alpha + ((e[0] + e[1]) + (e[2] + e[3]));
-      m[qt] = mn;
-      if (alpha != 1.f) {
-#pragma unroll
-        for (int nt = 0; nt < NDT; ++nt) o[nt][qt] *= alpha;
-      }
-      const uint32_t lo = pack_bf16(e[0], e[1]), hi = pack_bf16(e[2], e[3]);
-      pk[qt] = __builtin_bit_cast(i16x4, make_uint2(lo, hi));
     }
-    // O^T += V^T P^T over the wave's 16 keys
+    // masked and out-of-range keys get a raw score of -inf
+    const float c2 = p.scale_log2;   // > 0: the max of raw scores scales to the max
+    float x[2][16];   // raw scores q.k
 #pragma unroll
-    for (int nt = 0; nt < NDT; ++nt) {
-      const uint2 a = *reinterpret_cast<const uint2 *>(Vt + (16 * nt + lr) * TA_VROW + 16 * wave + 4 * g);
-      const i16x4 av = __builtin_bit_cast(i16x4, a);
+    for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
-        o[nt][qt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pk[qt], o[nt][qt], 0, 0, 0);
+      for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[qt][4 * k4 + t] = sc[qt][k4][t];
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int kk = k0 + 16 * k4 + 4 * g + t, j = kk - P;
+            const int jc = min(max(j, 0), p.n_max - 1);   // in bounds: load unconditionally
+            const uint32_t mb = mrow[qt][jc];
+            const bool vis = (kk < ke) & ((j < 0) | (mb != 0u));
+            x[qt][4 * k4 + t] = vis ? x[qt][4 * k4 + t] : -INFINITY;
+          }
     }
-    __syncthreads();
-  }
-
-  // ---- merge the four waves: common max, rescale, sum in a fixed order
+    // tile max of each query row: own 16 keys, then the lanes l ^ 16, l ^ 32
+    float mx[2];
+    bool move[2];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    float lt = l[qt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    if (g == 0) {
-      mw[wave][16 * qt + lr] = m[qt];
-      lw[wave][16 * qt + lr] = lt;
+    for (int qt = 0; qt < 2; ++qt) {
+      float m = x[qt][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) m = fmaxf(m, x[qt][e]);
+      mx[qt] = group4_max(m) * c2;
+      move[qt] = mx[qt] > mref[qt] + TA_TAU;
     }
-  }
-  __syncthreads();
-  float fself[4], lsum[4], mall[4];
+    if (__any(move[0] | move[1])) {
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const int row = 16 * qt + lr;
-    float M = fmaxf(fmaxf(mw[0][row], mw[1][row]), fmaxf(mw[2][row], mw[3][row]));
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
+      for (int qt = 0; qt < 2; ++qt)
+        if (move[qt]) {
+          const float alpha = __builtin_amdgcn_exp2f(mref[qt] - mx[qt]);   // 0 while mref = -inf
+          lsum[qt] *= alpha;
 #pragma unroll
-    for (int wv = 0; wv < 4; ++wv) L += lw[wv][row] * exp2f(mw[wv][row] - Mu);
-    fself[qt] = exp2f(m[qt] - Mu);
-    lsum[qt] = L;
-    mall[qt] = M;
-  }
-  constexpr int OROW = DH + TA_OPAD;
-  for (int wv = 0; wv < 3; ++wv) {
-    if (wave == wv) {
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-        for (int nt = 0; nt < NDT; ++nt) {
-          float *dst = Obuf + (16 * qt + lr) * OROW + 16 * nt + 4 * g;
-          f32x4 v = o[nt][qt] * fself[qt];
-          if (wv > 0) v += *reinterpret_cast<const f32x4 *>(dst);
-          *reinterpret_cast<f32x4 *>(dst) = v;
+          for (int nt = 0; nt < NDT; ++nt) o[qt][nt] *= alpha;
+          mref[qt] = mx[qt];
         }
     }
-    __syncthreads();
-  }
-  if (wave != 3) return;
+    uint4 pk[2][2];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const int r = r0 + 16 * qt + lr;
+    for (int qt = 0; qt < 2; ++qt) {
+      const float mu = mref[qt] == -INFINITY ? 0.f : mref[qt];
+      float e[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[qt][k], c2, -mu));
+      float ls = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) ls += e[k];
+      lsum[qt] += ls;
+      // k-step c of O^T += V^T P^T: keys 32 c + 4 g + t and 32 c + 16 + 4 g + t
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        pk[qt][c] = make_uint4(pack_bf16(e[8 * c + 0], e[8 * c + 1]), pack_bf16(e[8 * c + 2], e[8 * c + 3]),
+                               pack_bf16(e[8 * c + 4], e[8 * c + 5]), pack_bf16(e[8 * c + 6], e[8 * c + 7]));
+    }
+    // O^T += V^T P^T (A = V^T rows 16 nt + lr, the same keys in the same
+    // order); V^T fragments two steps ahead of their products, as above
+    {
+      constexpr int NF = 2 * NDT;
+      // order: k-step outer, output tile inner (independent accumulators)
+      auto vfrag = [&](int f) {
+        const int c = f / NDT, nt = f % NDT;
+        const uint16_t *vrow = Vt + (16 * nt + lr) * TA_VROW + 32 * c + 4 * g;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      };
+      uint4 ring[3];
+      ring[0] = vfrag(0);
+      ring[1] = vfrag(1);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if (f + 2 < NF) ring[(f + 2) % 3] = vfrag(f + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const int c = f / NDT, nt = f % NDT;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          o[qt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ring[f % 3]), as_bf16x8(pk[qt][c]),
+                                                              o[qt][nt], 0, 0, 0);
+      }
+    }
+    if (k0 + TA_KT < ke) {
+      stage(buf ^ 1);
+      if (k0 + 2 * TA_KT < ke) fetch_tile(k0 + 2 * TA_KT);
+    }
+    __syncthreads();
+  };
+
+  // full tiles of prefix keys first (the bulk), then the rest
+  const int pe = min(ke, P);
+  const int kplain = pe > kb ? kb + (pe - kb) / TA_KT * TA_KT : kb;
+  fetch_tile(kb);
+  stage(0);
+  if (kb + TA_KT < ke) fetch_tile(kb + TA_KT);
+  __syncthreads();
+  int k0 = kb, buf = 0;
+  for (; k0 < kplain; k0 += TA_KT, buf ^= 1) tile(k0, buf, std::false_type());
+  for (; k0 < ke; k0 += TA_KT, buf ^= 1) tile(k0, buf, std::true_type());
+
+  // ---- this wave's rows: lane holds query wr0 + 16 qt + lr, dims 16 nt + 4 g + t
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float lt = group4_sum(lsum[qt]);
+    const int r = wr0 + 16 * qt + lr;
     if (r >= p.n_max * G) continue;
     const int i = r / G, hq = kvh * G + r % G;
     const bool live = r < nrows;
     if (p.S == 1) {
-      const float inv = 1.f / lsum[qt];
+      const float inv = 1.f / lt;
       float *dst = p.O + ((size_t)q * p.n_max + i) * ostride + (size_t)hq * DH + 4 * g;
 #pragma unroll
-      for (int nt = 0; nt < NDT; ++nt) {
-        const f32x4 acc =
-            *reinterpret_cast<const f32x4 *>(Obuf + (16 * qt + lr) * OROW + 16 * nt + 4 * g) +
-            o[nt][qt] * fself[qt];
-        *reinterpret_cast<f32x4 *>(dst + 16 * nt) = live ? acc * inv : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int nt = 0; nt < NDT; ++nt)
+        *reinterpret_cast<f32x4 *>(dst + 16 * nt) = live ? o[qt][nt] * inv : f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
       float *dst = p.part + (slot + r) * DH + 4 * g;
 #pragma unroll
-      for (int nt = 0; nt < NDT; ++nt) {
-        const f32x4 acc =
-            *reinterpret_cast<const f32x4 *>(Obuf + (16 * qt + lr) * OROW + 16 * nt + 4 * g) +
-            o[nt][qt] * fself[qt];
-        *reinterpret_cast<f32x4 *>(dst + 16 * nt) = acc;
-      }
+      for (int nt = 0; nt < NDT; ++nt) *reinterpret_cast<f32x4 *>(dst + 16 * nt) = o[qt][nt];
       if (g == 0) {
-        p.ml[(slot + r) * 2 + 0] = mall[qt];
-        p.ml[(slot + r) * 2 + 1] = lsum[qt];
+        p.ml[(slot + r) * 2 + 0] = mref[qt];
+        p.ml[(slot + r) * 2 + 1] = lt;
       }
     }
   }

@@ -92,16 +92,16 @@ def _attn(**over):
 
 
 def test_attention_workspace_sizes():
-    """Split choice and workspace size are host arithmetic: one block of 64
-    query rows per (request, KV head) at Qwen3-4B needs 13 splits to give
-    about two workgroups per CU; 8 requests of 129 tree tokens need none."""
+    """Split choice and workspace size are host arithmetic: three blocks of
+    128 query rows per (request, KV head) at Qwen3-4B (65 nodes x 4 heads)
+    take 17 key splits (at least 256 keys each) towards two workgroups per
+    CU; 8 requests of 129 tree tokens (5 blocks per KV head) take 2."""
     ws = _lib.dtree_tree_attention_workspace
-    rows = 8 * 13 * 320       # Hkv x splits x padded rows (65 nodes x 4 heads -> 320)
-    assert ws(_attn()) == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 8
+    size = lambda rows: ((rows * 128 * 4 + 255) // 256) * 256 + rows * 8
+    assert ws(_attn()) == size(8 * 17 * 384)
     assert ws(_attn(splits=1)) == 0
-    assert ws(_attn(batch=8, n_max=129, L_cap=4225)) == 0
-    rows3 = 8 * 3 * 320
-    assert ws(_attn(splits=3)) == ((rows3 * 128 * 4 + 255) // 256) * 256 + rows3 * 8
+    assert ws(_attn(batch=8, n_max=129, L_cap=4225)) == size(8 * 8 * 2 * 640)
+    assert ws(_attn(splits=3)) == size(8 * 3 * 384)
 
 
 @pytest.mark.parametrize("over,code", [
