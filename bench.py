@@ -100,10 +100,13 @@ def _src_sha(path):
 
 
 def counters_traffic(workload, kernel="k1_lmhead_bf16"):
-    """HBM bytes per launch of the LM-head kernel from the committed
-    rocprofv3 counter summary of this workload, if it was taken on the
-    current kernel source; else None."""
-    stem = {"k1_lmhead_bf16": "k1_lmhead", "k1_logits_tiled": "k1_logits_tiled"}.get(kernel)
+    """HBM bytes per launch of the named kernel (per call for the attention
+    kernels: both of its kernels) from the committed rocprofv3 counter
+    summary of this workload, if it was taken on the current kernel source;
+    else None."""
+    stem, src = {"k1_lmhead_bf16": ("k1_lmhead", "k_lmhead.hip"),
+                 "k1_logits_tiled": ("k1_logits_tiled", "k_lmhead.hip"),
+                 "k_tree_attn": ("tree_attn", "k_attn.hip")}.get(kernel, (None, None))
     if stem is None:
         return None
     path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_counters.json")
@@ -111,7 +114,7 @@ def counters_traffic(workload, kernel="k1_lmhead_bf16"):
         return None
     with open(path) as f:
         c = json.load(f)
-    src = os.path.join(ROOT, "conditional_draft_tree_depth_amd", "csrc", "k_lmhead.hip")
+    src = os.path.join(ROOT, "conditional_draft_tree_depth_amd", "csrc", src)
     if c.get("kernel_src_sha") != _src_sha(src):
         return None
     return c.get("hbm_bytes_per_launch")
@@ -226,6 +229,13 @@ def bench_attention(args):
                       for q in range(cfg.batch)])
     base = runner.TreeAttention(x["Q"], x["K"], x["V"], x["prefix_len"], x["n_nodes"], masks,
                                 x["scale"], args.splits)
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     gen = torch.Generator(device="cuda").manual_seed(1234)
     calls = [base]
     for _ in range(args.layers - 1):
@@ -258,7 +268,7 @@ def bench_attention(args):
         roof = {"bound": "hbm", "achieved": nbytes / t_call / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "bytes_per_launch": nbytes}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = counters_traffic(cfg.name, "k_tree_attn")
     roof["kernel"] = ("k_tree_attn + k_tree_attn_merge (one call: the split attention "
                       "kernel and the merge of its key splits)")
     t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))

@@ -461,16 +461,26 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(TAParams p) {
 }  // namespace
 
 int tree_attn_splits(int batch, int n_max, int Hq, int Hkv, int L_cap, int requested) {
-  const int G = Hq / Hkv;
-  const int RB = (n_max * G + TA_QB - 1) / TA_QB;
-  const int cap = (L_cap + 255) / 256;     // at least 256 keys per split
   if (requested > 0) return requested;
-  const long base = (long)batch * Hkv * RB;
-  if (base >= 512) return 1;
-  int S = (int)((512 + base - 1) / base);
-  S = S < cap ? S : cap;
-  S = S > 64 ? 64 : S;
-  return S < 1 ? 1 : S;
+  // Choose the key splits S by a small cost model, in units of one tile's
+  // time: workgroups run two per CU (512 at once), so the kernel takes
+  // ceil(blocks * S / 512) rounds of ceil(tiles / S) tiles, and every split
+  // adds partial outputs for the merge (measured at about half a tile of
+  // time per split at these shapes).  Splits keep at least 256 keys.
+  const int G = Hq / Hkv;
+  const long base = (long)batch * Hkv * ((n_max * G + TA_QB - 1) / TA_QB);
+  const long tiles = (L_cap + TA_KT - 1) / TA_KT;
+  const int cap = (L_cap + 255) / 256;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int S = 1; S <= cap && S <= 64; ++S) {
+    const double cost = (double)((base * S + 511) / 512) * (double)((tiles + S - 1) / S) + 0.5 * S;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  return best;
 }
 
 size_t tree_attn_workspace(int batch, int n_max, int Hq, int Hkv, int dh, int S) {

@@ -92,15 +92,15 @@ def _attn(**over):
 
 
 def test_attention_workspace_sizes():
-    """Split choice and workspace size are host arithmetic: three blocks of
-    128 query rows per (request, KV head) at Qwen3-4B (65 nodes x 4 heads)
-    take 17 key splits (at least 256 keys each) towards two workgroups per
-    CU; 8 requests of 129 tree tokens (5 blocks per KV head) take 2."""
+    """Split choice and workspace size are host arithmetic.  Qwen3-4B (65
+    nodes x 4 heads: three blocks of 128 query rows per KV head, 66 key
+    tiles) takes 11 splits, 8 requests of 129 tree tokens (5 blocks per KV
+    head) take 3, and one split needs no workspace."""
     ws = _lib.dtree_tree_attention_workspace
     size = lambda rows: ((rows * 128 * 4 + 255) // 256) * 256 + rows * 8
-    assert ws(_attn()) == size(8 * 17 * 384)
+    assert ws(_attn()) == size(8 * 11 * 384)
     assert ws(_attn(splits=1)) == 0
-    assert ws(_attn(batch=8, n_max=129, L_cap=4225)) == size(8 * 8 * 2 * 640)
+    assert ws(_attn(batch=8, n_max=129, L_cap=4225)) == size(8 * 8 * 3 * 640)
     assert ws(_attn(splits=3)) == size(8 * 3 * 384)
 
 
