@@ -507,10 +507,14 @@ def build_heap_tree(prep, q, D, M, K, B, beta, scoring="conditional", script=Non
     expanded first, not counted in B); B pops; nodes at depth D are not
     expanded; the queue order is the selection order of the depth-wise
     build (key = score + beta * depth descending, then depth, then token
-    path), so with beta = 0 it is the plain cumulative log-probability.
+    path), so with beta = 0 it is the plain cumulative log-probability; the
+    build stops at the B-th pop without expanding it (its children could
+    never be popped).
 
     Returns the same node table as build_superarbol (every node ever
-    pushed), with sel = the popped nodes in pop order.
+    pushed), with sel = the popped nodes in pop order.  The pop set is a
+    recorded decision ("P",) over every pushed node; a scripted admissible
+    alternative (a set of token paths closed under parents) is popped first.
     """
     if scoring not in ("conditional", "markov"):
         raise ValueError("the heap builder scores conditionally or with the Markov head")
@@ -545,8 +549,13 @@ def build_heap_tree(prep, q, D, M, K, B, beta, scoring="conditional", script=Non
             kids[n].append(nid)
         return kids[n]
 
+    # a scripted pop set (an admissible alternative of the ("P",) decision
+    # below) is popped first, each part in the builder's order
+    forced = set(script[("P",)]) if ("P",) in script else None
+
     def okey(n):
-        return (-_key(score[n], dep[n], beta, store), dep[n], path[n])
+        k = (-_key(score[n], dep[n], beta, store), dep[n], path[n])
+        return k if forced is None else ((0 if path[n] in forced else 1),) + k
 
     state[0] = gru_cell(W.emb_rows([root_tok]), np.zeros((1, W.s)), W, store)
     heap = [(okey(c), c) for c in expand(0, state[0])]
@@ -555,11 +564,23 @@ def build_heap_tree(prep, q, D, M, K, B, beta, scoring="conditional", script=Non
     while len(pops) < B and heap:
         _, n = heapq.heappop(heap)
         pops.append(n)
-        if dep[n] < D:
+        # the B-th pop ends the build: its children could never be popped
+        if dep[n] < D and len(pops) < B:
             h = np.zeros((1, W.s)) if scoring == "markov" else state[par[n]]
             state[n] = gru_cell(W.emb_rows([tok[n]]), h, W, store)
             for c in expand(n, state[n]):
                 heapq.heappush(heap, (okey(c), c))
+    # The pops come out in the builder's order over every pushed node (keys
+    # never grow from a node to its children when beta <= 0), so the popped
+    # set is the first len(pops) pushed nodes in that order: recorded as a
+    # decision with its near-cutoff band, like the global Top-B.
+    nodes = list(range(1, len(tok)))
+    items = [path[n] for n in nodes]
+    keys = [_key(score[n], dep[n], beta, store) for n in nodes]
+    kept = _decide(("P",), items, keys, lambda pth: (len(pth), pth), len(pops), script,
+                   decisions, tol)
+    if set(kept) != {path[n] for n in pops}:
+        raise AssertionError("the pops are not the first pushed nodes in the builder's order")
     sa = dict(tok=tok, parent=par, depth=dep, score=score, path=path, kids=kids, C=C,
               Cl=Cl, uH=uH, decisions=decisions)
     out = emit_tree(sa, pops, B)

@@ -189,3 +189,116 @@ def compare_request(gout, gtr, prep, q, prm, tol=O.TIE_TOL, where="", scoring="c
     amb = sum(1 for d in sa["decisions"].values() if d["ambiguous"])
     return {"exact": not ties, "ties": ties, "ambiguous": amb, "nodes": n,
             "superarbol": len(sa["path"])}
+
+
+# ---------------------------------------------------------------------------
+# the sequential best-first builder
+# ---------------------------------------------------------------------------
+class _GpuHeap:
+    """The GPU heap round of one request: every pushed node by token path,
+    the popped set, the emitted tree (checked against the popped set)."""
+
+    def __init__(self, gout, gtr, B, where):
+        check_invariants(gout, B, where)
+        self.paths = _paths(gtr["node_tok"], gtr["node_parent"])
+        if len(set(self.paths)) != len(self.paths):
+            raise Mismatch(f"{where}GPU heap pushed a token path twice")
+        self.score = {self.paths[i]: float(gtr["node_score"][i]) for i in range(1, len(self.paths))}
+        self.kids = {}
+        for i in range(1, len(self.paths)):
+            self.kids.setdefault(self.paths[i][:-1], set()).add(self.paths[i][-1])
+        self.C = [set(int(t) for t in row) for row in gtr["C"]]
+        self.Cl = gtr["Cl"]
+        self.Ctok = gtr["C"]
+        pops = [int(x) for x in gtr["sel"]]
+        n = 0
+        while n < len(pops) and pops[n] >= 0:
+            n += 1
+        if any(x >= 0 for x in pops[n:]):
+            raise Mismatch(f"{where}pops resume after an empty pop")
+        self.pops = [self.paths[x] for x in pops[:n]]
+        self.popped = set(self.pops)
+        if len(self.popped) != n or () in self.popped:
+            raise Mismatch(f"{where}a node was popped twice, or the root")
+        nn = int(gout["n_nodes"])
+        if nn != n + 1:
+            raise Mismatch(f"{where}n_nodes {nn} vs {n} pops")
+        out_paths = _paths(gout["tok"][:nn], gout["parent"][:nn])
+        if set(out_paths[1:]) != self.popped:
+            raise Mismatch(f"{where}output is not the GPU's own pop set")
+        for i in range(1, nn):
+            if gout["score"][i] != np.float32(self.score[out_paths[i]]):
+                raise Mismatch(f"{where}output score differs from trace at {i}")
+
+
+def _first_heap_divergence(g, orc, D, tol, where):
+    sa = orc["sa"]
+    by_path = {p: i for i, p in enumerate(sa["path"])}
+    for dd in range(D):
+        for j, t in enumerate(g.Ctok[dd]):
+            if abs(float(g.Cl[dd][j]) - float(orc["Lb"][dd][int(t)])) > tol:
+                raise Mismatch(f"{where}base logit of token {t} at depth {dd}")
+        if g.C[dd] != set(int(t) for t in sa["C"][dd]):
+            return ("M", dd), g.C[dd]
+    # expansions of the nodes both builds popped, in the oracle's pop order
+    # (the root first)
+    o_pops = [sa["path"][n] for n in orc["sel"]]
+    for pth in [()] + o_pops:
+        if len(pth) >= D or (pth and pth not in g.popped):
+            continue
+        o_k = {sa["tok"][c] for c in sa["kids"][by_path[pth]]}
+        g_k = g.kids.get(pth, set())
+        if g_k != o_k:
+            return ("K", len(pth), pth), g_k
+        for t in o_k:
+            c = pth + (t,)
+            if abs(g.score[c] - sa["score"][by_path[c]]) > tol:
+                raise Mismatch(f"{where}score of {c}: gpu {g.score[c]} oracle {sa['score'][by_path[c]]}")
+    if g.popped != set(o_pops):
+        return ("P",), g.popped
+    return None
+
+
+def compare_heap_request(gout, gtr, prep, q, prm, tol=O.TIE_TOL, where="",
+                         scoring="conditional", max_ties=64):
+    """One request of a GPU heap-builder round against the oracle's
+    sequential best-first builder, to the last node: candidate sets, every
+    expansion's children, every pushed node's score and the pop set, with
+    near-ties handled as in compare_request (the oracle's own admissible
+    alternatives, then a rebuild along the GPU's choice)."""
+    D, M, K, B, beta = prm["D"], prm["M"], prm["K"], prm["B"], prm["beta"]
+    g = _GpuHeap(gout, gtr, B, where)
+    script, ties = {}, []
+    while True:
+        orc = O.build_heap_tree(prep, q, D, M, K, B, beta, scoring=scoring, script=script, tol=tol)
+        div = _first_heap_divergence(g, orc, D, tol, where)
+        if div is None:
+            break
+        key, gset = div
+        d = orc["sa"]["decisions"].get(key)
+        if d is None:
+            raise Mismatch(f"{where}decision {key}: GPU kept {sorted(gset)[:4]}, oracle has no choice")
+        if not (len(gset) == d["n"] and d["sure"] <= gset <= (d["sure"] | d["band"])):
+            raise Mismatch(f"{where}decision {key} differs beyond tolerance: "
+                           f"{sorted(set(gset) ^ d['default'])[:4]}")
+        ties.append(_tie_info(key, d, gset))
+        if len(ties) > max_ties:
+            raise Mismatch(f"{where}more than {max_ties} tolerated ties")
+        script[key] = set(gset)
+    sa = orc["sa"]
+    if set(g.score) != set(sa["path"][1:]):
+        raise Mismatch(f"{where}pushed nodes differ")
+    for n in range(1, len(sa["path"])):
+        if abs(g.score[sa["path"][n]] - sa["score"][n]) > tol:
+            raise Mismatch(f"{where}score of {sa['path'][n]}")
+    n = int(gout["n_nodes"])
+    if n != orc["n_nodes"]:
+        raise Mismatch(f"{where}n_nodes {n} vs {orc['n_nodes']}")
+    for k in ("tok", "parent", "depth", "mask"):
+        if not np.array_equal(gout[k], orc[k]):
+            raise Mismatch(f"{where}{k} differs")
+    if np.max(np.abs(gout["score"][:n] - orc["score"][:n])) > tol:
+        raise Mismatch(f"{where}scores differ by more than {tol}")
+    amb = sum(1 for d in sa["decisions"].values() if d["ambiguous"])
+    return {"exact": not ties, "ties": ties, "ambiguous": amb, "nodes": n,
+            "superarbol": len(sa["path"])}

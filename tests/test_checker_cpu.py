@@ -103,3 +103,82 @@ def test_planted_mistakes_are_rejected():
             compare_request(*as_gpu(res3, _prm(cfg)), prep, 0, _prm(cfg))
         caught += 1
     assert caught >= 13
+
+
+# ---------------------------------------------------------------------------
+# the heap builder's checker
+# ---------------------------------------------------------------------------
+def heap_as_gpu(res, p):
+    sa = res["sa"]
+    D, B = p["D"], p["B"]
+    sel = np.full(B, -1, np.int32)
+    sel[:len(res["sel"])] = res["sel"]
+    C = np.asarray(sa["C"], np.int32)
+    Cl = np.array([[res["Lb"][dd][t] for t in C[dd]] for dd in range(D)], np.float32)
+    gout = {k: np.array(res[k]) for k in ("tok", "parent", "depth", "score", "mask")}
+    gout["n_nodes"] = res["n_nodes"]
+    gtr = dict(C=C, Cl=Cl, node_tok=np.asarray(sa["tok"], np.int32),
+               node_parent=np.asarray(sa["parent"], np.int32),
+               node_score=np.asarray(sa["score"], np.float32), sel=sel,
+               n_sa=len(sa["tok"]), status=0)
+    return gout, gtr
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_heap_oracle_round_is_exact(seed):
+    from checker import compare_heap_request
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.make_inputs(cfg, seed)
+    prep = O.prepare_round(x, cfg.D)
+    res = O.build_heap_tree(prep, 0, cfg.D, cfg.M, cfg.K, cfg.B, cfg.beta)
+    r = compare_heap_request(*heap_as_gpu(res, _prm(cfg)), prep, 0, _prm(cfg))
+    assert r["exact"] and r["nodes"] == res["n_nodes"]
+
+
+def test_heap_pop_alternative_is_followed():
+    """An exact key tie at the last pop: the other admissible pop set is
+    followed by the oracle and compared to its last node."""
+    from checker import compare_heap_request
+    cfg = synth.custom_config(cfg_id=1500, D=3, M=4, K=2, B=3, beta=0.0)
+    # equal base logits everywhere and no correction: every child of a node
+    # has the same log-prob, so the pop cutoff is a tie
+    x = synth.make_inputs(cfg, 0)
+    x["weights"]["W_lm"] = np.zeros_like(x["weights"]["W_lm"])
+    x["weights"]["bias"] = np.zeros_like(x["weights"]["bias"])
+    x["weights"]["W2"] = np.zeros_like(x["weights"]["W2"])
+    prep = O.prepare_round(x, cfg.D)
+    p = _prm(cfg)
+    a = O.build_heap_tree(prep, 0, cfg.D, cfg.M, cfg.K, cfg.B, cfg.beta)
+    d = a["sa"]["decisions"][("P",)]
+    assert d["ambiguous"]
+    # a closed alternative: swap one popped leaf for a tied unpopped sibling
+    pops = {a["sa"]["path"][n] for n in a["sel"]}
+    leaf = max(pops, key=lambda pth: (len(pth), pth))
+    spare = next(pth for pth in sorted(d["band"] - pops) if pth[:-1] in pops | {()}
+                 and len(pth) == len(leaf))
+    alt = (pops - {leaf}) | {spare}
+    b = O.build_heap_tree(prep, 0, cfg.D, cfg.M, cfg.K, cfg.B, cfg.beta, script={("P",): alt})
+    r = compare_heap_request(*heap_as_gpu(b, p), prep, 0, p)
+    assert not r["exact"] and [t["stage"] for t in r["ties"]] == ["P"]
+    assert {b["sa"]["path"][n] for n in b["sel"]} == alt
+
+
+def test_heap_planted_mistakes_are_rejected():
+    from checker import compare_heap_request
+    cfg = synth.CONFIGS["tiny"]
+    for seed in range(4):
+        x = synth.make_inputs(cfg, seed)
+        prep = O.prepare_round(x, cfg.D)
+        p = _prm(cfg)
+        # the depth-wise round is not the heap round (and vice versa for a
+        # perturbed drafter)
+        x2 = synth.make_inputs(cfg, seed)
+        x2["weights"]["W2"] = x2["weights"]["W2"] * np.float32(1.01)
+        res2 = O.build_heap_tree(O.prepare_round(x2, cfg.D), 0, cfg.D, cfg.M, cfg.K, cfg.B,
+                                 cfg.beta)
+        with pytest.raises(Mismatch):
+            compare_heap_request(*heap_as_gpu(res2, p), prep, 0, p)
+        # Markov scoring instead of conditional
+        res3 = O.build_heap_tree(prep, 0, cfg.D, cfg.M, cfg.K, cfg.B, cfg.beta, scoring="markov")
+        with pytest.raises(Mismatch):
+            compare_heap_request(*heap_as_gpu(res3, p), prep, 0, p)
