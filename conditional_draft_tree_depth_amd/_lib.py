@@ -18,7 +18,8 @@ EXPORTS = ("dtree_create", "dtree_build_round", "dtree_build_round_static",
            "dtree_superarbol_nodes",
            "dtree_get_trace", "dtree_profile_enable", "dtree_profile_read",
            "dtree_set_persistent_launch", "dtree_set_scoring", "dtree_last_error",
-           "dtree_destroy", "dtree_tree_attention_workspace", "dtree_tree_attention")
+           "dtree_destroy", "dtree_tree_attention_workspace", "dtree_tree_attention",
+           "dtree_set_builder", "dtree_heap_nodes")
 NSTAGES = 6
 STAGES = ("round_start", "lmhead_topm", "topm_merge", "prologue", "depth_loop", "topb_emit")
 
@@ -102,6 +103,10 @@ def load(path=LIB_PATH):
     lib.dtree_last_error.restype = ctypes.c_char_p
     lib.dtree_destroy.argtypes = [c_vp]
     lib.dtree_destroy.restype = c_i32
+    lib.dtree_set_builder.argtypes = [c_vp, c_i32]
+    lib.dtree_set_builder.restype = c_i32
+    lib.dtree_heap_nodes.argtypes = [P(dtree_params)]
+    lib.dtree_heap_nodes.restype = c_i32
     lib.dtree_tree_attention_workspace.argtypes = [P(dtree_attn_args), P(ctypes.c_size_t)]
     lib.dtree_tree_attention_workspace.restype = c_i32
     lib.dtree_tree_attention.argtypes = [P(dtree_attn_args), c_vp]
@@ -227,6 +232,20 @@ def dtree_set_persistent_launch(ctx, cooperative, spin_limit=0):
 SCORE_CONDITIONAL, SCORE_MARGINAL, SCORE_MARKOV = 0, 1, 2
 SCORINGS = {"conditional": SCORE_CONDITIONAL, "marginal": SCORE_MARGINAL,
             "markov": SCORE_MARKOV}
+
+
+BUILD_DEPTHWISE, BUILD_HEAP = 0, 1
+BUILDERS = {"depthwise": BUILD_DEPTHWISE, "heap": BUILD_HEAP}
+
+
+def dtree_set_builder(ctx, builder):
+    """builder: "depthwise" / "heap" (or the DTREE_BUILD_* value)."""
+    code = BUILDERS[builder] if isinstance(builder, str) else int(builder)
+    _check("dtree_set_builder", load().dtree_set_builder(ctx, code), ctx)
+
+
+def dtree_heap_nodes(p):
+    return load().dtree_heap_nodes(ctypes.byref(p))
 
 
 def dtree_set_scoring(ctx, scoring):

@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdtree.so")
 OBJDIR = os.path.join(ROOT, "_build")
 SOURCES = ["k_lmhead.hip", "k_gemm.hip", "k_depth.hip", "k_topb.hip", "k_persist.hip",
-           "k_attn.hip", "dtree_host.hip"]
+           "k_attn.hip", "k_heap.hip", "dtree_host.hip"]
 # Packed-fp32 instructions are kept out of the generated code on purpose.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

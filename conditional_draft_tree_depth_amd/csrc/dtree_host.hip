@@ -56,6 +56,7 @@ struct Ws {
   float *logits = nullptr;   // [b * D, V] base logits when 32 or more rows (tiled product)
   uint16_t *S3[2] = {nullptr, nullptr};   // states as three bf16 planes (many branches)
   uint32_t *flags = nullptr;
+  HeapBufs hp;               // sequential best-first builder (allocated on first use)
 };
 
 int superarbol_nodes(int D, int K, int W) {
@@ -79,6 +80,7 @@ struct dtree_ctx {
   Ws ws;
   std::string err;
   bool has_round = false;
+  bool last_heap = false;   // the last round ran the sequential best-first builder
   dtree_params last{};
   int last_batch = 0, last_NT = 0;
   // persistent depth loop: available for this context, and the arrival
@@ -86,6 +88,7 @@ struct dtree_ctx {
   bool pk = false;
   bool sel_corr = false;   // correction logits computed inside the selection kernel
   int scoring = DTREE_SCORE_CONDITIONAL;
+  int builder = DTREE_BUILD_DEPTHWISE;
   uint32_t tok_epoch = 0;   // distinct-token tables: grows by one per round that uses them
   int pk_rows = 0;
   // persistent depth loop: plain launches until one of its waits runs out
@@ -152,7 +155,10 @@ void free_ws(Ws &ws) {
                   ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
                   ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags,
                   ws.logits, ws.S3[0], ws.S3[1], ws.gi_all, ws.gidx_cand, ws.first_row,
-                  ws.cidx_tmp, ws.uniq, ws.rowmap, ws.ucount, ws.lpos, ws.btot};
+                  ws.cidx_tmp, ws.uniq, ws.rowmap, ws.ucount, ws.lpos, ws.btot,
+                  ws.hp.tok, ws.hp.par, ws.hp.dep, ws.hp.cand, ws.hp.slot, ws.hp.score,
+                  ws.hp.popped, ws.hp.nnodes, ws.hp.pops, ws.hp.expanded, ws.hp.S, ws.hp.UH,
+                  ws.hp.gi};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   ws = Ws();
@@ -167,6 +173,12 @@ static void prof_mark(dtree_ctx *ctx, int stage, hipStream_t st) {
 extern "C" int32_t dtree_superarbol_nodes(const dtree_params *p) {
   if (!p || p->D < 1 || p->K < 1 || p->W < 1) return -1;
   return superarbol_nodes(p->D, p->K, p->W);
+}
+
+extern "C" int32_t dtree_heap_nodes(const dtree_params *p) {
+  if (!p || p->K < 1 || p->B < 1) return -1;
+  const long long n = (long long)p->K * (p->B + 1) + 1;
+  return n > (1 << 30) ? -1 : (int32_t)n;
 }
 
 extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *caps, int device,
@@ -359,6 +371,8 @@ extern "C" dtree_status dtree_build_round(dtree_ctx *ctx, const dtree_params *p,
   if (B < 1 || B > c.max_B) return fail(ctx, DTREE_E_ARG, "B outside [1, max_B]");
   if (!(p->beta <= 0.0f)) return fail(ctx, DTREE_E_ARG, "beta must be <= 0 (and not NaN)");
   if (std::isinf(p->beta)) return fail(ctx, DTREE_E_ARG, "beta must be finite");
+  if (ctx->builder == DTREE_BUILD_HEAP && ctx->scoring == DTREE_SCORE_MARGINAL)
+    return fail(ctx, DTREE_E_ARG, "the heap builder scores conditionally or with the Markov head");
 
   // an earlier round's depth-loop kernel could not have all its workgroups
   // resident at once (the device was shared): that round failed (status bit
@@ -441,6 +455,51 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
   // Markov scoring: each survivor's GRU step starts from a zero state, so
   // the W_hh product of the branches is not needed
   const bool markov = ctx->scoring == DTREE_SCORE_MARKOV;
+  if (ctx->builder == DTREE_BUILD_HEAP) {
+    // sequential best-first builder: one heap step and one state product per pop
+    HeapBufs &hp = ws.hp;
+    // GRU input projections of every candidate of the round [b D M, 3s]
+    g = GemmArgs{rows * M, 3 * s, w.e, w.Emb, wt, w.e, ws.C, 0, w.W_ih, wt, w.e, w.b_ih, nullptr,
+                 0, 1, 0, 0, hp.gi, 3 * s};
+    HIPCHK(ctx, launch_gemm(g, st));
+    // root state: the GRU consumes the last verified token from a zero state
+    g = GemmArgs{batch, 3 * s, w.e, w.Emb, wt, w.e, ws.gidx_tok, 0, w.W_ih, wt, w.e,
+                 w.b_ih, nullptr, 0, 1, 0, 0, ws.gi, 3 * s};
+    HIPCHK(ctx, launch_gemm(g, st));
+    HIPCHK(ctx, launch_gru_combine(batch, s, ws.gi, nullptr, nullptr, nullptr, 0, w.b_hh, nullptr,
+                                   nullptr, ws.S[0], nullptr, st));
+    const int ldu = r + 3 * s;
+    const size_t slots = (size_t)hp.Bcap + 1;
+    // [u | W_hh S + b_hh] of one state per request into expansion slot Y
+    auto product = [&](const float *X, int ldx, float *Y) {
+      GemmArgs gp{batch, ldu, s, X, WT_F32, ldx, nullptr, 0, ws.wcat, wt, s, w.b_hh, nullptr,
+                  0, 1, 0, 0, Y, (int)(slots * ldu)};
+      gp.bias_n0 = r;
+      return launch_gemm(gp, st);
+    };
+    HIPCHK(ctx, product(ws.S[0], s, hp.UH));
+    prof_mark(ctx, 4, st);
+    HeapStepArgs ha{batch, 0, B, D, M, K, s, r, markov ? 1 : 0, p->beta, w.W2,
+                    wt == WT_BF16 ? 1 : 0, ws.C, ws.Cl, ws.uH, root, ws.S[0], w.b_hh, hp};
+    for (int t = 0; t < B; ++t) {
+      ha.t = t;
+      HIPCHK(ctx, launch_heap_step(ha, st));
+      if (t + 1 < B)
+        HIPCHK(ctx, product(hp.S + (size_t)(t + 1) * s, (int)(slots * s),
+                            hp.UH + (size_t)(t + 1) * ldu));
+    }
+    prof_mark(ctx, 5, st);
+    HIPCHK(ctx, launch_heap_emit(batch, B, D, hp, tok, parent, depth, score, mask, n_nodes, st));
+    prof_mark(ctx, 6, st);
+    if (ctx->prof && ctx->prof_n < kProfRounds) ++ctx->prof_n;
+    ctx->has_round = true;
+    ctx->last = *p;
+    ctx->last_batch = batch;
+    ctx->last_NT = 0;
+    ctx->last_heap = true;
+    return DTREE_OK;
+  }
+  ctx->last_heap = false;
   const bool pk = !marginal && ctx->pk && batch * M <= 64 && batch * D * M <= ctx->pk_rows &&
                   persist_eligible(batch, D, M, K, W, s, w.e, r, wt, ctx->lds_max);
   int A = 1, off = 1, sc = 0;
@@ -585,6 +644,8 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
   return DTREE_OK;
 }
 
+static dtree_status heap_trace(dtree_ctx *ctx, int32_t req, dtree_trace *o);
+
 extern "C" dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace *o) {
   if (!ctx) return DTREE_E_ARG;
   ctx->err.clear();
@@ -593,6 +654,7 @@ extern "C" dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace
   if (req < 0 || req >= ctx->last_batch) return fail(ctx, DTREE_E_ARG, "req out of range");
   DeviceGuard dg(ctx->device);
   HIPCHK(ctx, hipDeviceSynchronize());
+  if (ctx->last_heap) return heap_trace(ctx, req, o);
   const dtree_params &p = ctx->last;
   const Ws &ws = ctx->ws;
   const size_t cm = (size_t)p.D * p.M;
@@ -613,6 +675,30 @@ extern "C" dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace
   HIPCHK(ctx, hipMemcpy(&st, ws.status, 4, hipMemcpyDeviceToHost));
   o->n_sa = NT;
   o->status = (int32_t)st;
+  return DTREE_OK;
+}
+
+// The heap builder's trace: candidates, every pushed node (push order), the
+// pops in pop order (-1 past the last); no per-depth survivors (-1).
+static dtree_status heap_trace(dtree_ctx *ctx, int32_t req, dtree_trace *o) {
+  const dtree_params &p = ctx->last;
+  const Ws &ws = ctx->ws;
+  const HeapBufs &hp = ws.hp;
+  const size_t cm = (size_t)p.D * p.M;
+  const size_t nb = (size_t)req * hp.NH;
+  int32_t nn = 0;
+  HIPCHK(ctx, hipMemcpy(&nn, hp.nnodes + req, 4, hipMemcpyDeviceToHost));
+  if (o->C) HIPCHK(ctx, hipMemcpy(o->C, ws.C + req * cm, cm * 4, hipMemcpyDeviceToHost));
+  if (o->Cl) HIPCHK(ctx, hipMemcpy(o->Cl, ws.Cl + req * cm, cm * 4, hipMemcpyDeviceToHost));
+  if (o->node_tok) HIPCHK(ctx, hipMemcpy(o->node_tok, hp.tok + nb, (size_t)nn * 4, hipMemcpyDeviceToHost));
+  if (o->node_parent) HIPCHK(ctx, hipMemcpy(o->node_parent, hp.par + nb, (size_t)nn * 4, hipMemcpyDeviceToHost));
+  if (o->node_score) HIPCHK(ctx, hipMemcpy(o->node_score, hp.score + nb, (size_t)nn * 4, hipMemcpyDeviceToHost));
+  if (o->surv) std::fill(o->surv, o->surv + (size_t)(p.D + 1) * p.W, -1);
+  if (o->sel)
+    HIPCHK(ctx, hipMemcpy(o->sel, hp.pops + (size_t)req * hp.Bcap, (size_t)p.B * 4,
+                          hipMemcpyDeviceToHost));
+  o->n_sa = nn;
+  o->status = 0;
   return DTREE_OK;
 }
 
@@ -668,6 +754,53 @@ extern "C" dtree_status dtree_set_persistent_launch(dtree_ctx *ctx, int32_t coop
   if (spin_limit < 0) return fail(ctx, DTREE_E_ARG, "spin_limit must be >= 0");
   ctx->pk_coop = cooperative == 1;
   ctx->pk_spin = (uint32_t)spin_limit;
+  return DTREE_OK;
+}
+
+extern "C" dtree_status dtree_set_builder(dtree_ctx *ctx, int32_t builder) {
+  if (!ctx) return DTREE_E_ARG;
+  ctx->err.clear();
+  if (builder != DTREE_BUILD_DEPTHWISE && builder != DTREE_BUILD_HEAP)
+    return fail(ctx, DTREE_E_ARG, "builder must be DTREE_BUILD_DEPTHWISE or DTREE_BUILD_HEAP");
+  if (builder == DTREE_BUILD_HEAP && !ctx->ws.hp.tok) {
+    const dtree_caps &c = ctx->caps;
+    const int s = ctx->w.s, r = ctx->w.r;
+    const long long NH = (long long)c.max_K * (c.max_B + 1) + 1;
+    if (NH > (1 << 24)) return fail(ctx, DTREE_E_SHAPE, "max_K * (max_B + 1) too large for the heap");
+    if (heap_emit_smem((int)NH, c.max_B) > ctx->lds_max)
+      return fail(ctx, DTREE_E_SHAPE, "max_K * max_B too large for the heap emission's LDS");
+    DeviceGuard dg(ctx->device);
+    HeapBufs &hp = ctx->ws.hp;
+    hp.NH = (int)NH;
+    hp.Bcap = c.max_B;
+    const size_t nodes = (size_t)c.max_batch * NH, slots = (size_t)c.max_batch * (c.max_B + 1);
+    hipError_t e = hipSuccess;
+    auto A = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+    A(alloc(&hp.tok, nodes));
+    A(alloc(&hp.par, nodes));
+    A(alloc(&hp.dep, nodes));
+    A(alloc(&hp.cand, nodes));
+    A(alloc(&hp.slot, nodes));
+    A(alloc(&hp.score, nodes));
+    A(alloc(&hp.popped, nodes));
+    A(alloc(&hp.nnodes, (size_t)c.max_batch));
+    A(alloc(&hp.pops, (size_t)c.max_batch * c.max_B));
+    A(alloc(&hp.expanded, (size_t)c.max_batch * c.max_B));
+    A(alloc(&hp.S, slots * s));
+    A(alloc(&hp.UH, slots * (size_t)(r + 3 * s)));
+    A(alloc(&hp.gi, (size_t)c.max_batch * c.max_D * c.max_M * 3 * s));
+    if (e == hipSuccess) e = heap_prepare(ctx->lds_max);
+    if (e != hipSuccess) {
+      void *ptrs[] = {hp.tok, hp.par, hp.dep, hp.cand, hp.slot, hp.score, hp.popped, hp.nnodes,
+                      hp.pops, hp.expanded, hp.S, hp.UH, hp.gi};
+      for (void *q : ptrs)
+        if (q) (void)hipFree(q);
+      hp = HeapBufs();
+      return fail(ctx, e == hipErrorOutOfMemory ? DTREE_E_NOMEM : DTREE_E_HIP,
+                  std::string("heap builder tables: ") + hipGetErrorString(e));
+    }
+  }
+  ctx->builder = builder;
   return DTREE_OK;
 }
 

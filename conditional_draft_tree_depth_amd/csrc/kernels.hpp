@@ -211,6 +211,38 @@ hipError_t launch_corr_tables(int rows, int M, int r, int s, const void *W2, con
 hipError_t launch_depth_persistent(const PersistArgs &a, bool cooperative, hipStream_t st);
 hipError_t corr_logits_prepare(int wtype, size_t lds_bytes);
 
+// ---- sequential best-first builder (k_heap.hip)
+// Per request: a node table of NH entries (push order, node 0 = the root),
+// the pop sequence and expansion flags of Bcap steps, the GRU state and the
+// state product [u | W_hh S + b_hh] of every expansion slot (Bcap + 1), and
+// the GRU input projections of all candidates [b D M, 3s].
+struct HeapBufs {
+  int NH = 0, Bcap = 0;
+  int32_t *tok = nullptr, *par = nullptr, *dep = nullptr, *cand = nullptr, *slot = nullptr;
+  float *score = nullptr;
+  uint8_t *popped = nullptr;
+  int32_t *nnodes = nullptr, *pops = nullptr, *expanded = nullptr;
+  float *S = nullptr, *UH = nullptr, *gi = nullptr;
+};
+struct HeapStepArgs {
+  int batch, t, B, D, M, K, s, r, markov;
+  float beta;
+  const void *W2;
+  int w2_bf16;
+  const int32_t *C;
+  const float *Cl, *uH;
+  const int32_t *root;
+  const float *S_root, *b_hh;
+  HeapBufs h;
+};
+size_t heap_step_smem(int r, int M);
+size_t heap_emit_smem(int NH, int B);
+hipError_t launch_heap_step(const HeapStepArgs &a, hipStream_t st);
+hipError_t launch_heap_emit(int batch, int B, int D, const HeapBufs &h, int32_t *tok,
+                            int32_t *parent, int32_t *depth, float *score, uint8_t *mask,
+                            int32_t *n_nodes, hipStream_t st);
+hipError_t heap_prepare(size_t lds_bytes);
+
 // ---- tree-attention verification (k_attn.hip)
 struct TreeAttnArgs {
   int batch, n_max, Hq, Hkv, dh, L_cap, splits;

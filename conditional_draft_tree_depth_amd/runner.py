@@ -21,13 +21,16 @@ class Round:
     """One context + output buffers for a fixed (batch, params)."""
 
     def __init__(self, dev_weights, wtype, caps, batch, D, M, K, W, B, beta, device=0,
-                 scoring="conditional"):
+                 scoring="conditional", builder="depthwise"):
         import torch
         self.p = _lib.params(D, M, K, W, B, beta)
         self.batch = batch
         self.ctx = _lib.dtree_create(dev_weights, wtype, caps, device)
         if scoring != "conditional":
             _lib.dtree_set_scoring(self.ctx, scoring)
+        self.builder = builder
+        if builder != "depthwise":
+            _lib.dtree_set_builder(self.ctx, builder)
         self.weights = dev_weights   # keep the borrowed weights alive
         N = B + 1
         dev = f"cuda:{device}"
@@ -49,7 +52,9 @@ class Round:
                 for q in range(self.batch)]
 
     def trace(self, req):
-        return _lib.dtree_get_trace(self.ctx, req, self.p, _lib.dtree_superarbol_nodes(self.p))
+        n = (_lib.dtree_heap_nodes(self.p) if self.builder == "heap"
+             else _lib.dtree_superarbol_nodes(self.p))
+        return _lib.dtree_get_trace(self.ctx, req, self.p, n)
 
     def close(self):
         if self.ctx is not None:

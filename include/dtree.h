@@ -217,9 +217,43 @@ dtree_status dtree_set_persistent_launch(dtree_ctx *ctx, int32_t cooperative,
 #define DTREE_SCORE_MARKOV 2
 dtree_status dtree_set_scoring(dtree_ctx *ctx, int32_t scoring);
 
+/* Which builder grows the tree (for the context's later rounds):
+ *   DTREE_BUILD_DEPTHWISE (0, the default): the depth-wise batched build with
+ *       a fixed-width superarbol and one global Top-B (DARTree page,
+ *       Metodología 1 and 2);
+ *   DTREE_BUILD_HEAP (1): the sequential best-first builder the pages
+ *       compare it with ("Resumen Técnico: DominoTree", Componentes
+ *       Principales 1 and 2; DARTree page, Planteamiento del Problema 3 and
+ *       Resultados Experimentales, Ablación: latency): a max-priority queue
+ *       of nodes keyed like the global Top-B (key = score + beta * depth
+ *       descending, then depth ascending, then token path ascending), seeded
+ *       with the root's Top-K children; each of the B pops runs the GRU one
+ *       step along the popped node's own path and, below depth D, corrects
+ *       the next depth's Top-M candidates with that state and pushes the
+ *       node's Top-K children.  The popped nodes are the tree (emitted in the
+ *       same canonical order, with the same mask).  Candidates per depth,
+ *       log-softmax over M and the tie rules are those of the depth-wise
+ *       build; W is not used.  Every pop is one heap-step kernel and one
+ *       state product on the stream (2 B launches per round, no host
+ *       synchronisation).  Conditional or Markov scoring (a round with
+ *       marginal scoring returns DTREE_E_ARG).
+ * The first switch to the heap builder allocates its tables, sized by the
+ * caps (nodes max_K (max_B + 1) + 1 per request, max_B + 1 states and state
+ * products, the input projections of max_batch max_D max_M candidates):
+ * DTREE_E_NOMEM / DTREE_E_SHAPE if they do not fit.  DTREE_E_ARG for other
+ * values.                                                                  */
+#define DTREE_BUILD_DEPTHWISE 0
+#define DTREE_BUILD_HEAP 1
+dtree_status dtree_set_builder(dtree_ctx *ctx, int32_t builder);
+
 /* Number of superarbol nodes (root included) a round with `p` builds per
  * request, or -1 if p is invalid.  Pure host arithmetic.                     */
 int32_t dtree_superarbol_nodes(const dtree_params *p);
+
+/* Upper bound on the nodes (root included) the heap builder pushes per
+ * request with `p`: K (B + 1) + 1, or -1 if p is invalid.  Pure host
+ * arithmetic.                                                               */
+int32_t dtree_heap_nodes(const dtree_params *p);
 
 /* Debug copy of request `req`'s intermediates of the LAST round, host memory,
  * caller-allocated with the sizes noted (for that round's params).  Any
@@ -239,6 +273,9 @@ typedef struct {
                           workgroups at once, the round's outputs are
                           invalid)                                          */
 } dtree_trace;
+/* After a heap-builder round the node arrays hold every pushed node in push
+ * order (up to dtree_heap_nodes(p) entries: size them for that), sel the
+ * popped node ids in pop order (-1 past the last pop), surv is all -1.      */
 dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace *out);
 
 /* Stage timing with HIP events recorded on the round's own stream.  When
@@ -249,8 +286,9 @@ dtree_status dtree_get_trace(dtree_ctx *ctx, int32_t req, dtree_trace *out);
  *   2 Top-M merge (32 or more hidden rows: the per-slice lists built from
  *     the logits, then the merge)
  *   3 path-independent prologue (uH, correction tables or root GRU state)
- *   4 depth loop (correction, selection, GRU, all depths)
- *   5 global Top-B, canonical order and mask
+ *   4 depth loop (correction, selection, GRU, all depths; heap builder:
+ *     all pops)
+ *   5 global Top-B, canonical order and mask (heap builder: emission)
  * dtree_profile_read synchronises, writes the summed milliseconds of each
  * stage over the rounds recorded since dtree_profile_enable(ctx, 1) to
  * ms[0..DTREE_NSTAGES) and the round count to *rounds, and clears them.

@@ -13,7 +13,7 @@ import numpy as np
 
 import synth
 from oracle import dtree_oracle as O
-from checker import compare_request
+from checker import compare_request, compare_heap_request
 
 
 def caps_for(cfg, **over):
@@ -23,12 +23,14 @@ def caps_for(cfg, **over):
     return (c["max_batch"], c["max_D"], c["max_M"], c["max_K"], c["max_W"], c["max_B"])
 
 
-def gpu_round(inputs, cfg, caps=None, beta=None, runs=1, scoring="conditional"):
+def gpu_round(inputs, cfg, caps=None, beta=None, runs=1, scoring="conditional",
+              builder="depthwise"):
     from conditional_draft_tree_depth_amd import runner
     import torch
     wd, H, root = runner.to_device(inputs)
     rnd = runner.Round(wd, cfg.wtype, caps or caps_for(cfg), cfg.batch, cfg.D, cfg.M, cfg.K,
-                       cfg.W, cfg.B, cfg.beta if beta is None else beta, scoring=scoring)
+                       cfg.W, cfg.B, cfg.beta if beta is None else beta, scoring=scoring,
+                       builder=builder)
     try:
         outs = []
         for _ in range(runs):
@@ -50,18 +52,19 @@ def _log(rec):
 
 
 def check_outputs(inputs, cfg, gouts, gtrs, label, max_ties_per_request=0,
-                  scoring="conditional", seed=None):
+                  scoring="conditional", seed=None, builder="depthwise"):
     """Every request of a GPU round against the oracle (checker.py);
     returns the per-request results."""
     prep = O.prepare_round(inputs, cfg.D)
     prm = dict(D=cfg.D, M=cfg.M, K=cfg.K, W=cfg.W, B=cfg.B, beta=cfg.beta)
+    cmp = compare_heap_request if builder == "heap" else compare_request
     res = []
     for q in range(cfg.batch):
-        r = compare_request(gouts[q], gtrs[q], prep, q, prm, where=f"{label} req {q}: ",
-                            scoring=scoring)
+        r = cmp(gouts[q], gtrs[q], prep, q, prm, where=f"{label} req {q}: ", scoring=scoring)
         res.append(r)
         _log({"label": label, "workload": cfg.name, "seed": seed, "req": q,
-              "scoring": scoring, "ties": r["ties"], "ambiguous": r["ambiguous"],
+              "scoring": scoring, "builder": builder, "ties": r["ties"],
+              "ambiguous": r["ambiguous"],
               "nodes": r["nodes"], "superarbol": r["superarbol"]})
     ties = [(q, t) for q, r in enumerate(res) for t in r["ties"]]
     if ties:
@@ -74,9 +77,11 @@ def check_outputs(inputs, cfg, gouts, gtrs, label, max_ties_per_request=0,
 
 
 def check_config(inputs, cfg, label, max_ties_per_request=0, caps=None,
-                 scoring="conditional", seed=None):
+                 scoring="conditional", seed=None, builder="depthwise"):
     """GPU round vs oracle on every request."""
     print(f"[gpu] {label}: batch={cfg.batch} D={cfg.D} M={cfg.M} K={cfg.K} W={cfg.W} "
-          f"B={cfg.B} beta={cfg.beta} wtype={cfg.wtype} scoring={scoring}", flush=True)
-    gouts, gtrs = gpu_round(inputs, cfg, caps, scoring=scoring)
-    return check_outputs(inputs, cfg, gouts, gtrs, label, max_ties_per_request, scoring, seed)
+          f"B={cfg.B} beta={cfg.beta} wtype={cfg.wtype} scoring={scoring} builder={builder}",
+          flush=True)
+    gouts, gtrs = gpu_round(inputs, cfg, caps, scoring=scoring, builder=builder)
+    return check_outputs(inputs, cfg, gouts, gtrs, label, max_ties_per_request, scoring, seed,
+                         builder)
