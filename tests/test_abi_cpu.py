@@ -117,3 +117,12 @@ def test_attention_rejects_bad_arguments_before_device(over, code):
     a = _attn(**over)
     assert lib.dtree_tree_attention(ctypes.byref(a), None) == code
     assert lib.dtree_last_error(None)
+
+
+def test_heap_node_bound_and_builder_rejections():
+    lib = _lib.load()
+    p = _lib.params(16, 32, 4, 8, 64, -0.05)
+    assert lib.dtree_heap_nodes(ctypes.byref(p)) == 4 * 65 + 1
+    p.B = 0
+    assert lib.dtree_heap_nodes(ctypes.byref(p)) == -1
+    assert lib.dtree_set_builder(None, 1) == 1   # null context
