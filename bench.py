@@ -315,6 +315,8 @@ def main():
     ap.add_argument("--builder", default="depthwise", choices=["depthwise", "heap"],
                     help="depthwise (the method) or heap (the sequential best-first builder "
                          "the pages compare it with)")
+    ap.add_argument("--no-builder-comparison", action="store_true",
+                    help="skip the other builder's timing (profiled runs)")
     ap.add_argument("--layers", type=int, default=36,
                     help="attention workloads: distinct K/V caches cycled over the steps")
     ap.add_argument("--splits", type=int, default=0,
@@ -386,7 +388,7 @@ def main():
     # the pages' comparison on identical inputs: the same context switched to
     # the other builder, timed the same way (fewer rounds)
     cmp = None
-    if args.scoring != "marginal":
+    if args.scoring != "marginal" and not args.no_builder_comparison:
         other = "heap" if args.builder == "depthwise" else "depthwise"
         n_cmp = max(1, min(args.steps, 20))
         _lib.dtree_set_builder(rnd.ctx, other)
