@@ -54,7 +54,7 @@ struct Ws {
   uint16_t *w1t = nullptr;   // W1[:, d:]^T, padded (correction tables)
   uint16_t *hb = nullptr;    // bf16 hidden rows of the round (LM-head kernel)
   float *logits = nullptr;   // [b * D, V] base logits when 32 or more rows (tiled product)
-  uint16_t *S3[2] = {nullptr, nullptr};   // states as three bf16 planes (many branches)
+  uint16_t *S3[2] = {nullptr, nullptr};   // states as bf16 planes (many branches)
   uint32_t *flags = nullptr;
   HeapBufs hp;               // sequential best-first builder (allocated on first use)
 };
@@ -259,9 +259,9 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   A(alloc(&ws.S[1], bw * s));
   A(alloc(&ws.uh, bw * (r + 3 * s)));
   // 256 or more branches: the state products run as tiled bf16 products over
-  // the three-plane split of the states
+  // the bf16 plane split of the states
   if (w->wtype == DTREE_BF16 && s % 64 == 0 && bw >= 256)
-    for (int i = 0; i < 2; ++i) A(alloc(&ws.S3[i], bw * 3 * s));
+    for (int i = 0; i < 2; ++i) A(alloc(&ws.S3[i], bw * STATE_PLANES * s));
   A(alloc(&ws.ell, bw * c.max_M));
   A(alloc(&ws.gi, bw * 3 * s));
   const size_t esz_w = w->wtype == DTREE_BF16 ? 2 : 4;
@@ -575,12 +575,12 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
                      ws.uH, r, A, D, dd, ws.uh, ldu};
         g.add_n = r;
         g.bias_n0 = r;
-        if (ws.S3[sc]) {   // the state as three bf16 planes, if a tiled product takes it
+        if (ws.S3[sc]) {   // the state as bf16 planes, if a tiled product takes it
           GemmArgs g3 = g;
           g3.X = ws.S3[sc];
           g3.xtype = WT_BF16;
-          g3.ldx = 3 * s;
-          g3.Kd = 3 * s;
+          g3.ldx = STATE_PLANES * s;
+          g3.Kd = STATE_PLANES * s;
           g3.kw = s;
           if (gemm_tiled_ok(g3)) g = g3;
         }

@@ -234,8 +234,8 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int R
 // 16-byte chunk c of row q at position c ^ (q & 7) so that fragment reads
 // of 16 rows hit distinct banks; each of the 4 waves computes a 64 x 64
 // quarter.  Activation rows are gathered through xidx; the weights' k index
-// runs modulo kw (a three-plane split state meets the same weights three
-// times).  The row tiles of one weight tile run one after another on one
+// runs modulo kw (a state split into bf16 planes meets the same weights
+// once per plane).  The row tiles of one weight tile run one after another on one
 // XCD, sharing its L2.
 constexpr int GTT_B = 128, GTT_BK = 64, GTT_THREADS = 256, GTT_STAGES = 4;
 constexpr int GTT_STAGE_CHUNKS = 2 * GTT_B * 8;
@@ -450,10 +450,9 @@ __global__ __launch_bounds__(256) void k_gru_combine(int R, int s, const float *
     const uint16_t t0 = f32_to_bf16_rne(hn);
     const float r1 = hn - bf16_bits_to_f32(t0);
     const uint16_t t1 = f32_to_bf16_rne(r1);
-    uint16_t *o = S3 + (size_t)i * 3 * s + j;
+    uint16_t *o = S3 + (size_t)i * STATE_PLANES * s + j;
     o[0] = t0;
     o[s] = t1;
-    o[2 * s] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(t1));
   }
 }
 

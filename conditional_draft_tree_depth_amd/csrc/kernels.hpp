@@ -120,16 +120,18 @@ struct GemmArgs {
   const int32_t *Rdev = nullptr;   // tiled product only: the row count read on the
                                    // device (R is then its upper bound)
   int kw = 0;            // bf16 X only: W's k index is k mod kw (0: kw = Kd); a
-                         // state split into three bf16 planes [hi | mid | lo]
-                         // is multiplied by the same weights three times
+                         // state split into bf16 planes [hi | lo]
+                         // is multiplied by the same weights once per plane
 };
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
 // GRU gates: gi, gh = input/state projections incl. biases ([R, 3s]); if gh
 // is null the previous state is zero and the state part equals b_hh.
 // Row i takes gi row gidx[i] (i if gidx is null; mapped through gmap when
 // given), gh row pidx[i] (stride ldgh) and previous state row pidx[i].
-// S3 (or null): the new state also as three bf16 planes, row i = [hi | mid | lo]
-// ([R, 3s]), the exact split hi + mid + lo of every fp32 value.
+// S3 (or null): the new state also as STATE_PLANES bf16 planes, row i =
+// [hi | lo] ([R, STATE_PLANES s]): hi = bf16(x), lo = bf16(x - hi), so
+// |x - hi - lo| <= 2^-18 |x| for every fp32 value x.
+constexpr int STATE_PLANES = 2;
 hipError_t launch_gru_combine(int R, int s, const float *gi, const int32_t *gidx,
                               const int32_t *gmap, const float *gh, int ldgh,
                               const float *b_hh, const float *Sprev,
