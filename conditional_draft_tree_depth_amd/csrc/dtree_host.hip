@@ -156,9 +156,8 @@ void free_ws(Ws &ws) {
                   ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags,
                   ws.logits, ws.S3[0], ws.S3[1], ws.gi_all, ws.gidx_cand, ws.first_row,
                   ws.cidx_tmp, ws.uniq, ws.rowmap, ws.ucount, ws.lpos, ws.btot,
-                  ws.hp.tok, ws.hp.par, ws.hp.dep, ws.hp.cand, ws.hp.slot, ws.hp.score,
-                  ws.hp.popped, ws.hp.nnodes, ws.hp.pops, ws.hp.expanded, ws.hp.S, ws.hp.UH,
-                  ws.hp.gi};
+                  ws.hp.tok, ws.hp.par, ws.hp.dep, ws.hp.score, ws.hp.gref, ws.hp.pv,
+                  ws.hp.nnodes, ws.hp.pops, ws.hp.ex, ws.hp.S, ws.hp.UH, ws.hp.gi};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   ws = Ws();
@@ -479,7 +478,7 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
     };
     HIPCHK(ctx, product(ws.S[0], s, hp.UH));
     prof_mark(ctx, 4, st);
-    HeapStepArgs ha{batch, 0, B, D, M, K, s, r, markov ? 1 : 0, p->beta, w.W2,
+    HeapStepArgs ha{batch, 0, B, D, M, K, s, r, markov ? 1 : 0, w.V, p->beta, w.W2,
                     wt == WT_BF16 ? 1 : 0, ws.C, ws.Cl, ws.uH, root, ws.S[0], w.b_hh, hp};
     for (int t = 0; t < B; ++t) {
       ha.t = t;
@@ -767,8 +766,9 @@ extern "C" dtree_status dtree_set_builder(dtree_ctx *ctx, int32_t builder) {
     const int s = ctx->w.s, r = ctx->w.r;
     const long long NH = (long long)c.max_K * (c.max_B + 1) + 1;
     if (NH > (1 << 24)) return fail(ctx, DTREE_E_SHAPE, "max_K * (max_B + 1) too large for the heap");
-    if (heap_emit_smem((int)NH, c.max_B) > ctx->lds_max)
-      return fail(ctx, DTREE_E_SHAPE, "max_K * max_B too large for the heap emission's LDS");
+    if (heap_emit_smem((int)NH, c.max_B) > ctx->lds_max ||
+        heap_step_smem((int)NH, c.max_D, c.max_M, ctx->w.r) > ctx->lds_max)
+      return fail(ctx, DTREE_E_SHAPE, "max_K * max_B too large for the heap builder's LDS");
     DeviceGuard dg(ctx->device);
     HeapBufs &hp = ctx->ws.hp;
     hp.NH = (int)NH;
@@ -779,20 +779,19 @@ extern "C" dtree_status dtree_set_builder(dtree_ctx *ctx, int32_t builder) {
     A(alloc(&hp.tok, nodes));
     A(alloc(&hp.par, nodes));
     A(alloc(&hp.dep, nodes));
-    A(alloc(&hp.cand, nodes));
-    A(alloc(&hp.slot, nodes));
     A(alloc(&hp.score, nodes));
-    A(alloc(&hp.popped, nodes));
+    A(alloc(&hp.gref, nodes * 2));
+    A(alloc(&hp.pv, nodes));
     A(alloc(&hp.nnodes, (size_t)c.max_batch));
     A(alloc(&hp.pops, (size_t)c.max_batch * c.max_B));
-    A(alloc(&hp.expanded, (size_t)c.max_batch * c.max_B));
+    A(alloc(&hp.ex, (size_t)c.max_batch * 4));
     A(alloc(&hp.S, slots * s));
     A(alloc(&hp.UH, slots * (size_t)(r + 3 * s)));
     A(alloc(&hp.gi, (size_t)c.max_batch * c.max_D * c.max_M * 3 * s));
     if (e == hipSuccess) e = heap_prepare(ctx->lds_max);
     if (e != hipSuccess) {
-      void *ptrs[] = {hp.tok, hp.par, hp.dep, hp.cand, hp.slot, hp.score, hp.popped, hp.nnodes,
-                      hp.pops, hp.expanded, hp.S, hp.UH, hp.gi};
+      void *ptrs[] = {hp.tok, hp.par, hp.dep, hp.score, hp.gref, hp.pv, hp.nnodes, hp.pops,
+                      hp.ex, hp.S, hp.UH, hp.gi};
       for (void *q : ptrs)
         if (q) (void)hipFree(q);
       hp = HeapBufs();

@@ -218,16 +218,21 @@ hipError_t corr_logits_prepare(int wtype, size_t lds_bytes);
 // the pop sequence and expansion flags of Bcap steps, the GRU state and the
 // state product [u | W_hh S + b_hh] of every expansion slot (Bcap + 1), and
 // the GRU input projections of all candidates [b D M, 3s].
+// Node table of the best-first builder, NH nodes per request in push order.
 struct HeapBufs {
   int NH = 0, Bcap = 0;
-  int32_t *tok = nullptr, *par = nullptr, *dep = nullptr, *cand = nullptr, *slot = nullptr;
+  int32_t *tok = nullptr, *par = nullptr, *dep = nullptr;
   float *score = nullptr;
-  uint8_t *popped = nullptr;
-  int32_t *nnodes = nullptr, *pops = nullptr, *expanded = nullptr;
+  int32_t *gref = nullptr;    // [NH][2]: candidate index at its depth, parent's expansion slot
+  uint64_t *pv = nullptr;     // packed pop value; 0 once popped (and for the root)
+  int32_t *nnodes = nullptr;  // [batch] nodes pushed so far
+  int32_t *pops = nullptr;    // [batch][Bcap] node popped at each step
+  int32_t *ex = nullptr;      // [batch][4] node the next step expands (-1: none), its depth
+                              // and score bits
   float *S = nullptr, *UH = nullptr, *gi = nullptr;
 };
 struct HeapStepArgs {
-  int batch, t, B, D, M, K, s, r, markov;
+  int batch, t, B, D, M, K, s, r, markov, V;
   float beta;
   const void *W2;
   int w2_bf16;
@@ -237,7 +242,7 @@ struct HeapStepArgs {
   const float *S_root, *b_hh;
   HeapBufs h;
 };
-size_t heap_step_smem(int r, int M);
+size_t heap_step_smem(int NH, int D, int M, int r);
 size_t heap_emit_smem(int NH, int B);
 hipError_t launch_heap_step(const HeapStepArgs &a, hipStream_t st);
 hipError_t launch_heap_emit(int batch, int B, int D, const HeapBufs &h, int32_t *tok,

@@ -39,6 +39,21 @@ def test_heap_shapes(gpu_lib, seed, wtype, d, V, s, M, K, B, D, batch, beta):
                  seed=seed, builder="heap")
 
 
+@pytest.mark.parametrize("seed,wtype,s,r,M,K,B,D", [
+    (10, "f32", 30, 30, 5, 2, 30, 3),       # rows not 16-byte multiples: scalar loads
+    (11, "bf16", 40, 36, 12, 3, 40, 5),     # bf16 rows of 72 bytes: scalar loads
+    (12, "bf16", 64, 32, 128, 8, 50, 4),    # the most candidates: two lanes each
+    (13, "bf16", 64, 64, 100, 8, 50, 3),    # 100 candidates, 8 pieces per lane
+])
+def test_heap_load_paths(gpu_lib, seed, wtype, s, r, M, K, B, D):
+    """Shapes on both sides of the 16-byte load path and of the lanes per
+    candidate of the correction dot products."""
+    cfg = synth.custom_config(cfg_id=9700 + seed, d=128, V=2000, e=48, s=s, r=r, D=D, M=M, K=K,
+                              W=4, B=B, beta=-0.05, batch=2, wtype=wtype)
+    check_config(synth.make_inputs(cfg, seed), cfg, f"heap load path {seed}",
+                 max_ties_per_request=2, seed=seed, builder="heap")
+
+
 @pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_8b_x8"])
 def test_heap_full_size(gpu_lib, name):
     cfg = synth.CONFIGS[name]
