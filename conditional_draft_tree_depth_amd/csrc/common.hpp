@@ -180,4 +180,38 @@ __device__ __forceinline__ int next_pow2(int n) {
   return p;
 }
 
+// ---- staged tiles: direct global-to-LDS copies with waits of our own ----
+// The compiler, seeing a copy into LDS in flight, waits for every such copy
+// before any LDS read it cannot prove unrelated (and a workgroup fence
+// waits for all of them), which serialises a multi-stage ring.  The copies
+// below are issued where the compiler does not track them; the kernel
+// waits for its own copies with wait_vm before a bare barrier.
+
+// 16 bytes per lane from g into LDS at byte address lds + 16 * lane (lds
+// is uniform over the wave)
+__device__ __forceinline__ void lds_copy16(const void *g, uint32_t lds) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+// this wave's vector memory operations: at most N still in flight (gfx9
+// encoding, lgkmcnt and expcnt left free)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// workgroup barrier without a memory fence (the compiler keeps memory
+// accesses on their side of it)
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace dtree

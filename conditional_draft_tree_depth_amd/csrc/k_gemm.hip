@@ -230,7 +230,8 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int R
 
 // Many activation rows (256 or more): bf16 x bf16 product in 128 x 128
 // tiles (activation rows x weight rows), operands staged in a 4-stage LDS
-// ring by direct global-to-LDS copies (3 k chunks of 64 in flight), the
+// ring by direct global-to-LDS copies (3 k chunks of 64 in flight while one
+// is read; the copies are tracked by waits of the kernel's own), the
 // 16-byte chunk c of row q at position c ^ (q & 7) so that fragment reads
 // of 16 rows hit distinct banks; each of the 4 waves computes a 64 x 64
 // quarter.  Activation rows are gathered through xidx; the weights' k index
@@ -269,15 +270,16 @@ __global__ __launch_bounds__(GTT_THREADS) void k_gemm_tiled(GemmArgs a) {
       src[i] = reinterpret_cast<const uint4 *>(X + (size_t)(a.xidx ? a.xidx[xr] : xr) * a.ldx) + ch;
     }
   }
+  // chunk kc goes to stage kc % 4; past the last chunk a step re-issues the
+  // last one (read by nobody), so every wait below has the same count
+  const uint32_t ring_lds = lds_addr(smem);
   auto issue = [&](int kc) {
-    uint4 *dst = ring + (kc % GTT_STAGES) * GTT_STAGE_CHUNKS;
-    const int kcw = kc % nkw;
+    const uint32_t dst = ring_lds + (uint32_t)((kc % GTT_STAGES) * GTT_STAGE_CHUNKS * 16);
+    const int kk = min(kc, nk - 1), kcw = kk % nkw;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = wave + 4 * i;
-      __builtin_amdgcn_global_load_lds(src[i] + (j >= 16 ? kcw : kc) * 8,
-                                       (__attribute__((address_space(3))) void *)(dst + j * 64),
-                                       16, 0, 0);
+      lds_copy16(src[i] + (j >= 16 ? kcw : kk) * 8, dst + (uint32_t)(j * 64 * 16));
     }
   };
   f32x4 acc[4][4];
@@ -285,14 +287,17 @@ __global__ __launch_bounds__(GTT_THREADS) void k_gemm_tiled(GemmArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kc = 0; kc < GTT_STAGES - 1 && kc < nk; ++kc) issue(kc);
+  static_assert(GTT_STAGES == 4, "copies in flight below");
+  issue(0);
+  issue(1);
+  issue(2);
   for (int kc = 0; kc < nk; ++kc) {
-    const int ahead = min(GTT_STAGES - 2, nk - 1 - kc);
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
-    __syncthreads();
-    if (kc + GTT_STAGES - 1 < nk) issue(kc + GTT_STAGES - 1);
+    // this wave's copies of chunk kc have landed (kc + 1 and kc + 2 may
+    // still fly); the barrier makes every wave's copies visible and retires
+    // every read of the stage refilled next (it held chunk kc - 1)
+    wait_vm<16>();
+    bare_barrier();
+    issue(kc + 3);
     const uint4 *As = ring + (kc % GTT_STAGES) * GTT_STAGE_CHUNKS, *Bs = As + GTT_B * 8;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -310,6 +315,7 @@ __global__ __launch_bounds__(GTT_THREADS) void k_gemm_tiled(GemmArgs a) {
         for (int j = 0; j < 4; ++j) acc[i][j] = sk_mfma(af[i], bf[j], acc[i][j]);
     }
   }
+  wait_vm<0>();   // no copy outlives the workgroup
   // lane holds Y[activation row 4 g + t][output lr] of tile (i, j)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

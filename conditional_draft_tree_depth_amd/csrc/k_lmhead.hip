@@ -307,11 +307,11 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
   auto ring_issue = [&]() {
     if (zi < Z) {
       uint4 *dst = ring + (zi % (RING > 0 ? RING : 1)) * (K1_CHUNK / 16);
+      // (copies the compiler does not track: it would wait for every one of
+      // them before any ring read, and the ring would no longer overlap)
+      const uint32_t dl = lds_addr(dst);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        __builtin_amdgcn_global_load_lds(rq[k] + ic * 16,
-                                         (__attribute__((address_space(3))) void *)(dst + k * 64),
-                                         16, 0, 0);
+      for (int k = 0; k < 4; ++k) lds_copy16(rq[k] + ic * 16, dl + (uint32_t)(k * 64 * 16));
       ++zi;
       if (++ic == nch) {
         ic = 0;
@@ -669,15 +669,15 @@ __global__ __launch_bounds__(256) void k1_stage_hidden(const float *__restrict__
 // product written to memory, then the same per-slice candidate lists.
 // With b*D rows the vocabulary projection stops being a pure stream of W_lm
 // (128 rows: 128 flop per weight byte, 512 rows: 512), so every workgroup
-// takes a 128-row x 128-token tile and a W_lm tile is read once for all the
+// takes a 128-row x 256-token tile and a W_lm tile is read once for all the
 // rows of the tile instead of once per 16-row block.  Operands are staged in
-// an LDS ring of 64-wide k chunks, with the 16-byte chunk c of row q stored
-// at c ^ (q & 7) so that the fragment reads of 16 rows hit distinct banks;
-// each of the 8 waves computes a 64 x 64 part (4 x 4 MFMA tiles) of the
-// 128 x 256 tile.
+// an LDS ring of 64-wide k chunks (3 stages: 2 chunks in flight while one is
+// read), with the 16-byte chunk c of row q stored at c ^ (q & 7) so that the
+// fragment reads of 16 rows hit distinct banks; each of the 8 waves computes
+// a 64 x 64 part (4 x 4 MFMA tiles) of the 128 x 256 tile.
 constexpr int LT_BM = 128, LT_BN = 256, LT_BK = 64, LT_THREADS = 512;
 constexpr int LT_WAVES = LT_THREADS / 64;
-constexpr int LT_STAGES = 3;                          // LDS ring: 2 k chunks in flight
+constexpr int LT_STAGES = 3;
 constexpr int LT_NI = (LT_BM + LT_BN) * 8 / 64 / LT_WAVES;   // copies per wave per stage
 constexpr int LT_STAGE_CHUNKS = (LT_BM + LT_BN) * 8;  // 16-byte chunks per stage
 constexpr size_t LT_SMEM = (size_t)LT_STAGES * LT_STAGE_CHUNKS * 16;
@@ -687,7 +687,8 @@ __global__ __launch_bounds__(LT_THREADS) void k1_logits_tiled(
     const uint16_t *__restrict__ W, int V, const float *__restrict__ bias,
     float *__restrict__ L) {
   extern __shared__ __align__(16) uint8_t smem[];
-  uint4 *ring = reinterpret_cast<uint4 *>(smem);
+  const uint4 *ring = reinterpret_cast<const uint4 *>(smem);
+  const uint32_t ring_lds = lds_addr(smem);
   const int ntm = (rows + LT_BM - 1) / LT_BM, ntn = (V + LT_BN - 1) / LT_BN;
   const int total = ntm * ntn;
   int task = blockIdx.x;
@@ -711,29 +712,29 @@ __global__ __launch_bounds__(LT_THREADS) void k1_logits_tiled(
     src[i] = reinterpret_cast<const uint4 *>(base) + ch;
   }
   const int nk = d / LT_BK;
+  // chunk kc goes to stage kc % 3; past the last chunk a step re-issues the
+  // last one (read by nobody), so every wait below has the same count
   auto issue = [&](int kc) {
-    uint4 *dst = ring + (kc % LT_STAGES) * LT_STAGE_CHUNKS;
+    const uint32_t dst = ring_lds + (uint32_t)((kc % LT_STAGES) * LT_STAGE_CHUNKS * 16);
+    const int kk = min(kc, nk - 1);
 #pragma unroll
     for (int i = 0; i < LT_NI; ++i)
-      __builtin_amdgcn_global_load_lds(src[i] + kc * 8,
-                                       (__attribute__((address_space(3))) void *)(dst + (wave + LT_WAVES * i) * 64),
-                                       16, 0, 0);
+      lds_copy16(src[i] + kk * 8, dst + (uint32_t)((wave + LT_WAVES * i) * 64 * 16));
   };
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kc = 0; kc < LT_STAGES - 1 && kc < nk; ++kc) issue(kc);
+  issue(0);
+  issue(1);
   for (int kc = 0; kc < nk; ++kc) {
-    // this wave's copies of chunk kc have landed (the later ones may still
-    // be in flight); the barrier makes every wave's copies visible and
-    // retires every read of the buffer refilled next
-    static_assert(LT_STAGES == 3 && LT_NI == 6, "copy counts below");
-    if (kc + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): chunk kc + 1 may fly
-    else __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
-    __syncthreads();
-    if (kc + LT_STAGES - 1 < nk) issue(kc + LT_STAGES - 1);
+    // this wave's copies of chunk kc have landed (those of kc + 1 may still
+    // fly); the barrier makes every wave's copies visible and retires every
+    // read of the stage refilled next (it held chunk kc - 1)
+    wait_vm<LT_NI>();
+    bare_barrier();
+    issue(kc + 2);
     const uint4 *As = ring + (kc % LT_STAGES) * LT_STAGE_CHUNKS, *Bs = As + LT_BM * 8;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -753,6 +754,7 @@ __global__ __launch_bounds__(LT_THREADS) void k1_logits_tiled(
                                                              acc[i][j], 0, 0, 0);
     }
   }
+  wait_vm<0>();   // no copy outlives the workgroup
   // lane holds D[hidden row 4 g + t][token lr] of tile (i, j)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
