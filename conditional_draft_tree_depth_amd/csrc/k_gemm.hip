@@ -8,10 +8,11 @@
 // GRU state enters the matrix cores as an exact three-term bf16 split);
 // accumulation is fp32.  Three kernels: bf16 weights with fewer than 256
 // rows, a contraction split over 8 waves (k_skinny_bf16); bf16 operands
-// with many rows, 128 x 128 tiles (k_gemm_tiled); anything else, a plain
+// with many rows, 256 x 128 or 128 x 128 tiles (k_mm); anything else, a plain
 // tiled VALU product (k_gemm_xwT: 64 x 64 outputs per 256-thread
 // workgroup, 16-wide k chunks staged in LDS).
 #include <algorithm>
+#include <hip/hip_ext.h>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -228,102 +229,105 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int R
   }
 }
 
-// Many activation rows (256 or more): bf16 x bf16 product in 128 x 128
-// tiles (activation rows x weight rows), operands staged in a 4-stage LDS
-// ring by direct global-to-LDS copies (3 k chunks of 64 in flight while one
-// is read; the copies are tracked by waits of the kernel's own), the
-// 16-byte chunk c of row q at position c ^ (q & 7) so that fragment reads
-// of 16 rows hit distinct banks; each of the 4 waves computes a 64 x 64
-// quarter.  Activation rows are gathered through xidx; the weights' k index
-// runs modulo kw (a state split into bf16 planes meets the same weights
-// once per plane).  The row tiles of one weight tile run one after another on one
-// XCD, sharing its L2.
-constexpr int GTT_B = 128, GTT_BK = 64, GTT_THREADS = 256, GTT_STAGES = 4;
-constexpr int GTT_STAGE_CHUNKS = 2 * GTT_B * 8;
-constexpr size_t GTT_SMEM = (size_t)GTT_STAGES * GTT_STAGE_CHUNKS * 16;
-
-__global__ __launch_bounds__(GTT_THREADS) void k_gemm_tiled(GemmArgs a) {
+// Many activation rows (256 or more), bf16 x bf16: WM x WN waves per
+// workgroup, each a (BM/WM) x (BN/WN) block of 16 x 16 MFMA tiles (64 x 64;
+// two waves per SIMD, or two workgroups per CU, so that one wave's fragment
+// reads overlap another's MFMAs).  k chunks of 32: a row's chunk is 64 bytes, four
+// 16-byte pieces, piece c of row q stored at position c ^ h(q), h(q) =
+// ((q >> 1) & 3) ^ ((q >> 3) & 1), which puts the reads of one piece by 16
+// consecutive rows on distinct banks (as 8 lanes of 16 bytes over 128 bytes,
+// and as 16 lanes over 256).  A 4-stage ring: chunk kc is read while three
+// more are in flight; the copies are tracked by the kernel's own waits.
+// Activation rows are gathered through xidx; the weights' k index runs
+// modulo kw (a state split into bf16 planes meets the same weights once per
+// plane); rows past the device count *Rdev do no work.  Tasks run in
+// XCD-contiguous runs, so the row tiles of one weight tile share an L2.
+template <int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) void k_mm(GemmArgs a) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;   // 16 x 16 tiles per wave
+  constexpr int SROWS = BM + BN;              // 64-byte rows per stage
+  constexpr int SBYTES = SROWS * 64;
+  constexpr int NI = SROWS / 16 / NW;         // copy instructions per wave per stage
+  static_assert(SROWS % (16 * NW) == 0 && BM % (16 * NW) == 0, "copy split");
+  constexpr int NIA = BM / 16 / NW;           // ... of which activation rows
   extern __shared__ __align__(16) uint8_t smem[];
-  uint4 *ring = reinterpret_cast<uint4 *>(smem);
-  const int ntm = (a.R + GTT_B - 1) / GTT_B, ntn = (a.N + GTT_B - 1) / GTT_B;
+  const uint4 *ring = reinterpret_cast<const uint4 *>(smem);
+  const uint32_t ring_lds = lds_addr(smem);
+  const int ntm = (a.R + BM - 1) / BM, ntn = (a.N + BN - 1) / BN;
   const int total = ntm * ntn;
-  int task = blockIdx.x;
-  if (total % 8 == 0) task = (task & 7) * (total / 8) + (task >> 3);
-  const int m0 = (task % ntm) * GTT_B, n0 = (task / ntm) * GTT_B;
+  // tasks in XCD-contiguous runs (workgroup i runs on XCD i mod 8): the row
+  // tiles of one weight tile run side by side on one XCD and share its L2
+  const int per = (total + 7) / 8;
+  const int task = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (task >= total) return;
+  const int m0 = (task % ntm) * BM, n0 = (task / ntm) * BN;
   const int R = a.Rdev ? min(*a.Rdev, a.R) : a.R;   // rows past the device count: no work
   if (m0 >= R) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int wm = (wave % WM) * (BM / WM), wn = (wave / WM) * (BN / WN);
   const uint16_t *X = static_cast<const uint16_t *>(a.X);
   const uint16_t *W = static_cast<const uint16_t *>(a.W);
-  const int nk = a.Kd / GTT_BK, nkw = (a.kw ? a.kw : a.Kd) / GTT_BK;
-  // copy instruction j of a stage: 0..15 activation rows, 16..31 weight rows
-  const uint4 *src[8];
+  const int nk = a.Kd / 32, nkw = (a.kw ? a.kw : a.Kd) / 32;
+  auto hsw = [](int q) { return ((q >> 1) & 3) ^ ((q >> 3) & 1); };
+  // copy instruction j = wave + NW i of a stage fills stage rows 16 j ..
+  // 16 j + 15 (activation rows first): lane l -> row 16 j + l / 4, position
+  // l & 3
+  const uint16_t *src[NI];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = wave + 4 * i, sl = (j & 15) * 64 + lane, row = sl >> 3;
-    const int ch = (sl & 7) ^ (row & 7);
-    if (j >= 16) {
-      src[i] = reinterpret_cast<const uint4 *>(W + (size_t)min(n0 + row, a.N - 1) * a.ldw) + ch;
+  for (int i = 0; i < NI; ++i) {
+    const int srow = 16 * (wave + NW * i) + (lane >> 2), pc = (lane & 3) ^ hsw(srow);
+    if (i < NIA) {
+      const int xr = min(m0 + srow, R - 1);
+      src[i] = X + (size_t)(a.xidx ? a.xidx[xr] : xr) * a.ldx + 8 * pc;
     } else {
-      const int xr = min(m0 + row, R - 1);
-      src[i] = reinterpret_cast<const uint4 *>(X + (size_t)(a.xidx ? a.xidx[xr] : xr) * a.ldx) + ch;
+      src[i] = W + (size_t)min(n0 + srow - BM, a.N - 1) * a.ldw + 8 * pc;
     }
   }
   // chunk kc goes to stage kc % 4; past the last chunk a step re-issues the
-  // last one (read by nobody), so every wait below has the same count
-  const uint32_t ring_lds = lds_addr(smem);
+  // last one (read by nobody), so every wait has the same count
   auto issue = [&](int kc) {
-    const uint32_t dst = ring_lds + (uint32_t)((kc % GTT_STAGES) * GTT_STAGE_CHUNKS * 16);
-    const int kk = min(kc, nk - 1), kcw = kk % nkw;
+    const uint32_t dst = ring_lds + (uint32_t)((kc % STAGES) * SBYTES);
+    const int kk = min(kc, nk - 1), kkw = kk % nkw;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = wave + 4 * i;
-      lds_copy16(src[i] + (j >= 16 ? kcw : kk) * 8, dst + (uint32_t)(j * 64 * 16));
-    }
+    for (int i = 0; i < NI; ++i)
+      lds_copy16(src[i] + 32 * (i < NIA ? kk : kkw), dst + (uint32_t)((wave + NW * i) * 1024));
   };
-  f32x4 acc[4][4];
+  const int hl = hsw(lr);   // rows of a fragment read are 16-aligned: h(row) = h(lr)
+  f32x4 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  static_assert(GTT_STAGES == 4, "copies in flight below");
-  issue(0);
-  issue(1);
-  issue(2);
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < STAGES - 1; ++kc) issue(kc);
   for (int kc = 0; kc < nk; ++kc) {
-    // this wave's copies of chunk kc have landed (kc + 1 and kc + 2 may
-    // still fly); the barrier makes every wave's copies visible and retires
-    // every read of the stage refilled next (it held chunk kc - 1)
-    wait_vm<16>();
+    // chunk kc has landed (this wave's copies; the next STAGES - 2 may fly);
+    // after the barrier every wave's copies are visible and the stage of
+    // chunk kc - 1 is free
+    wait_vm<(STAGES - 2) * NI>();
     bare_barrier();
-    issue(kc + 3);
-    const uint4 *As = ring + (kc % GTT_STAGES) * GTT_STAGE_CHUNKS, *Bs = As + GTT_B * 8;
+    issue(kc + STAGES - 1);
+    const uint4 *st = ring + (kc % STAGES) * (SBYTES / 16);
+    uint4 fa[TM], fb[TN];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = 4 * ks + g;
-      uint4 af[4], bf[4];
+    for (int i = 0; i < TM; ++i) fa[i] = st[(wm + 16 * i + lr) * 4 + (g ^ hl)];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra = wm + i * 16 + lr, rb = wn + i * 16 + lr;
-        af[i] = As[ra * 8 + (ch ^ (ra & 7))];
-        bf[i] = Bs[rb * 8 + (ch ^ (rb & 7))];
-      }
+    for (int j = 0; j < TN; ++j) fb[j] = st[(BM + wn + 16 * j + lr) * 4 + (g ^ hl)];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = sk_mfma(af[i], bf[j], acc[i][j]);
-    }
+      for (int j = 0; j < TN; ++j) acc[i][j] = sk_mfma(fa[i], fb[j], acc[i][j]);
   }
   wait_vm<0>();   // no copy outlives the workgroup
   // lane holds Y[activation row 4 g + t][output lr] of tile (i, j)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < TN; ++j) {
     const int n = n0 + wn + j * 16 + lr;
     if (n >= a.N) continue;
     const float bv = (a.bias && n >= a.bias_n0) ? a.bias[n - a.bias_n0] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int row = m0 + wm + i * 16 + 4 * g + t;
@@ -336,19 +340,70 @@ __global__ __launch_bounds__(GTT_THREADS) void k_gemm_tiled(GemmArgs a) {
   }
 }
 
-bool gemm_tiled_ok(const GemmArgs &a) {
-  const int kw = a.kw ? a.kw : a.Kd;
-  auto al16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-  const int tiles = ((a.R + GTT_B - 1) / GTT_B) * ((a.N + GTT_B - 1) / GTT_B);
-  return a.R >= 256 && tiles >= 64 && a.wtype == WT_BF16 && a.xtype == WT_BF16 && a.Kd % GTT_BK == 0 &&
-         kw % GTT_BK == 0 && a.Kd % kw == 0 && a.ldx % 8 == 0 && a.ldw % 8 == 0 && al16(a.X) &&
-         al16(a.W);
+template <int BM, int BN, int STAGES>
+static constexpr size_t mm_smem() { return (size_t)STAGES * (BM + BN) * 64; }
+
+// the largest per-wave block whose tile count still covers most of the
+// 256 CUs (one workgroup per CU)
+void mm_tile(int R, int N, int *bm, int *bn) {
+  static const int cand[2][2] = {{256, 128}, {128, 128}};
+  for (const auto &c : cand) {
+    const long long tiles = (long long)((R + c[0] - 1) / c[0]) * ((N + c[1] - 1) / c[1]);
+    if (tiles >= 200) {
+      *bm = c[0];
+      *bn = c[1];
+      return;
+    }
+  }
+  *bm = 128;
+  *bn = 128;
 }
 
-hipError_t gemm_prepare() {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_tiled),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GTT_SMEM);
+bool mm_ok(const GemmArgs &a) {
+  const int kw = a.kw ? a.kw : a.Kd;
+  auto al16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  return a.wtype == WT_BF16 && a.xtype == WT_BF16 && a.Kd % 32 == 0 && kw % 32 == 0 &&
+         a.Kd % kw == 0 && a.ldx % 8 == 0 && a.ldw % 8 == 0 && al16(a.X) && al16(a.W);
 }
+
+// configurations: (BM, BN, WM, WN)
+#define MM_CONFIGS(X) X(256, 128, 4, 2, 4) X(128, 128, 2, 2, 4)
+
+hipError_t launch_mm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
+                     hipEvent_t ev1) {
+  const int total = ((a.R + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+  const dim3 grid(8 * ((total + 7) / 8));
+#define MM_LAUNCH(BM_, BN_, WM_, WN_, S_)                                                       \
+  if (bm == BM_ && bn == BN_) {                                                                 \
+    hipExtLaunchKernelGGL((k_mm<BM_, BN_, WM_, WN_, S_>), grid, dim3(WM_ * WN_ * 64),           \
+                          (uint32_t)mm_smem<BM_, BN_, S_>(), st, ev0, ev1, 0u, a);              \
+    return hipGetLastError();                                                                   \
+  }
+  MM_CONFIGS(MM_LAUNCH)
+#undef MM_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+static hipError_t mm_prepare() {
+  hipError_t e = hipSuccess;
+#define MM_SET(BM_, BN_, WM_, WN_, S_)                                                          \
+  if (e == hipSuccess)                                                                          \
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_mm<BM_, BN_, WM_, WN_, S_>),      \
+                            hipFuncAttributeMaxDynamicSharedMemorySize,                         \
+                            (int)mm_smem<BM_, BN_, S_>());
+  MM_CONFIGS(MM_SET)
+#undef MM_SET
+  return e;
+}
+
+// Many activation rows (256 or more) and bf16 operands: the tiled product
+// (k_mm), at least 64 tiles of 128 x 128
+bool gemm_tiled_ok(const GemmArgs &a) {
+  const int tiles = ((a.R + 127) / 128) * ((a.N + 127) / 128);
+  return a.R >= 256 && tiles >= 64 && a.Kd % 64 == 0 && mm_ok(a);
+}
+
+hipError_t gemm_prepare() { return mm_prepare(); }
 
 static int skinny_terms(const GemmArgs &a) {
   return (a.xtype == WT_F32 && !a.xround) ? 3 : 1;
@@ -374,9 +429,9 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   // workgroups past the count leave at once, keeps every wave busy
   const bool skinny_first = a.Rdev && a.R <= 8192 && skinny_ok(a);
   if (!skinny_first && gemm_tiled_ok(a)) {
-    const int total = ((a.R + GTT_B - 1) / GTT_B) * ((a.N + GTT_B - 1) / GTT_B);
-    hipLaunchKernelGGL(k_gemm_tiled, dim3(total), dim3(GTT_THREADS), GTT_SMEM, st, a);
-    return hipGetLastError();
+    int bm = 128, bn = 128;
+    mm_tile(a.R, a.N, &bm, &bn);
+    return launch_mm(a, bm, bn, st, nullptr, nullptr);
   }
   if (a.kw && a.kw != a.Kd) return hipErrorInvalidValue;   // planes need the tiled kernel
   if (a.Rdev && !skinny_ok(a)) return hipErrorInvalidValue;  // device row counts need MFMA kernels

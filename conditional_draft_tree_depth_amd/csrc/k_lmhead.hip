@@ -1018,8 +1018,7 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
   // the kernel's own start and end events time the product alone (the list
   // kernel falls into the next stage)
   hipExtLaunchKernelGGL(k1_logits_tiled, dim3(ntm * ntn), dim3(LT_THREADS), (uint32_t)LT_SMEM, st,
-                        ev0, ev1,
-                        0u, (const uint16_t *)a.Hb, a.rows, rows_pad, a.d,
+                        ev0, ev1, 0u, (const uint16_t *)a.Hb, a.rows, rows_pad, a.d,
                         static_cast<const uint16_t *>(a.W), a.V, a.bias, logits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
