@@ -141,28 +141,41 @@ __device__ __forceinline__ void sk_split(const float4 &x0, const float4 &x1, uin
                       sk_pack(h[q][4], h[q][5]), sk_pack(h[q][6], h[q][7]));
 }
 
-template <int TERMS, typename XT, int KSW>
+// CT column tiles of 16 per workgroup: each activation fragment (and its
+// split) is loaded once and multiplied by CT weight fragments, so that
+// CT-fold fewer workgroups re-read the activation rows (RBM row blocks at
+// most, the partial sums of all of them in LDS).
+template <int TERMS, typename XT, int KSW, int CT = 1, int RBM = SK_RB>
 __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int RB) {
   constexpr bool XB = sizeof(XT) == 2;
-  __shared__ __align__(16) float red[SK_WAVES * SK_RB * 256];
+  constexpr int NC = 16 * CT;   // output columns per workgroup
+  __shared__ __align__(16) float red[SK_WAVES * RBM * 16 * NC];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 16, r0 = blockIdx.y * (16 * RB);
+  const int n0 = blockIdx.x * NC, r0 = blockIdx.y * (16 * RB);
   const int R = a.Rdev ? min(*a.Rdev, a.R) : a.R;   // rows past the device count: no work
   if (r0 >= R) return;
   const int nrb = min(RB, (R - r0 + 15) >> 4);
   const int nks = a.Kd >> 5;
-  const uint16_t *wrow = static_cast<const uint16_t *>(a.W) + (size_t)min(n0 + lr, a.N - 1) * a.ldw + g * 8;
   // k-steps past the contraction load the last one again (every load is
   // unconditional and in bounds) and are skipped at the products
-  uint4 wa[KSW];
+  uint4 wa[CT][KSW];
 #pragma unroll
-  for (int i = 0; i < KSW; ++i)
-    wa[i] = *reinterpret_cast<const uint4 *>(wrow + min(wave + SK_WAVES * i, nks - 1) * 32);
+  for (int c = 0; c < CT; ++c) {
+    const uint16_t *wrow =
+        static_cast<const uint16_t *>(a.W) + (size_t)min(n0 + 16 * c + lr, a.N - 1) * a.ldw + g * 8;
+#pragma unroll
+    for (int i = 0; i < KSW; ++i)
+      wa[c][i] = *reinterpret_cast<const uint4 *>(wrow + min(wave + SK_WAVES * i, nks - 1) * 32);
+  }
   // activation row of lane lr in row block rb (rows past R repeat the last
   // row; their sums are never stored)
   auto xrow = [&](int rb) -> size_t {
     const int row = min(r0 + rb * 16 + lr, R - 1);
     return (size_t)(a.xidx ? a.xidx[row] : row) * a.ldx + g * 8;
+  };
+  // lane holds Y[row lr][weight row 4 g + t] of column tile c
+  auto put = [&](int rb, int c, const f32x4 &acc) {
+    *reinterpret_cast<f32x4 *>(red + ((wave * RBM + rb) * 16 + lr) * NC + 16 * c + 4 * g) = acc;
   };
   if constexpr (XB) {
     const uint16_t *X = static_cast<const uint16_t *>(a.X);
@@ -176,12 +189,17 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int R
     load(0, xc);
     for (int rb = 0; rb < nrb; ++rb) {
       if (rb + 1 < nrb) load(rb + 1, xn);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < KSW; ++i)
-        if (wave + SK_WAVES * i < nks) acc = sk_mfma(wa[i], xc[i], acc);
-      // lane holds Y[row lr][weight row 4 g + t]
-      *reinterpret_cast<f32x4 *>(red + ((wave * SK_RB + rb) * 16 + lr) * 16 + 4 * g) = acc;
+        if (wave + SK_WAVES * i < nks) {
+#pragma unroll
+          for (int c = 0; c < CT; ++c) acc[c] = sk_mfma(wa[c][i], xc[i], acc[c]);
+        }
+#pragma unroll
+      for (int c = 0; c < CT; ++c) put(rb, c, acc[c]);
 #pragma unroll
       for (int i = 0; i < KSW; ++i) xc[i] = xn[i];
     }
@@ -200,27 +218,32 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int R
     load(0, xc);
     for (int rb = 0; rb < nrb; ++rb) {
       if (rb + 1 < nrb) load(rb + 1, xn);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < KSW; ++i)
         if (wave + SK_WAVES * i < nks) {
           uint4 t[TERMS];
           sk_split<TERMS>(xc[i][0], xc[i][1], t);
 #pragma unroll
-          for (int q = 0; q < TERMS; ++q) acc = sk_mfma(wa[i], t[q], acc);
+          for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int q = 0; q < TERMS; ++q) acc[c] = sk_mfma(wa[c][i], t[q], acc[c]);
         }
-      *reinterpret_cast<f32x4 *>(red + ((wave * SK_RB + rb) * 16 + lr) * 16 + 4 * g) = acc;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) put(rb, c, acc[c]);
 #pragma unroll
       for (int i = 0; i < KSW; ++i) { xc[i][0] = xn[i][0]; xc[i][1] = xn[i][1]; }
     }
   }
   __syncthreads();
-  for (int o = tid; o < nrb * 256; o += SK_WAVES * 64) {
-    const int rb = o >> 8, rr = (o >> 4) & 15, nn = o & 15;
+  for (int o = tid; o < nrb * 16 * NC; o += SK_WAVES * 64) {
+    const int rb = o / (16 * NC), rr = (o / NC) & 15, nn = o % NC;
     const int row = r0 + rb * 16 + rr, n = n0 + nn;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < SK_WAVES; ++w) v += red[((w * SK_RB + rb) * 16 + rr) * 16 + nn];
+    for (int w = 0; w < SK_WAVES; ++w) v += red[((w * RBM + rb) * 16 + rr) * NC + nn];
     if (row < R && n < a.N) {
       if (a.bias && n >= a.bias_n0) v += a.bias[n - a.bias_n0];
       if (a.addend && n < a.add_n) v += a.addend[(size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda + n];
@@ -437,6 +460,16 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.Rdev && !skinny_ok(a)) return hipErrorInvalidValue;  // device row counts need MFMA kernels
   if (skinny_ok(a)) {
     const int terms = skinny_terms(a);
+    // split fp32 activations, a short contraction and many outputs: four
+    // column tiles per workgroup (each split activation fragment feeds four
+    // weight fragments) when that still makes 128 or more workgroups
+    const int nrb0 = (a.R + 15) / 16, ncol4 = (a.N + 63) / 64;
+    if (a.xtype == WT_F32 && terms == 3 && a.Kd <= 32 * SK_WAVES * 4 &&
+        ncol4 * ((nrb0 + 1) / 2) >= 128) {
+      hipLaunchKernelGGL((k_skinny_bf16<3, float, 4, 4, 2>), dim3(ncol4, (nrb0 + 1) / 2),
+                         dim3(SK_WAVES * 64), 0, st, a, 2);
+      return hipGetLastError();
+    }
     // row blocks per workgroup: enough workgroups to fill the chip (about
     // 1024) before a weight tile is reused for more rows
     const int ncol = (a.N + 15) / 16, nrb = (a.R + 15) / 16;
