@@ -247,7 +247,10 @@ __device__ __forceinline__ void k1_wait_vm(int n) {   // vmcnt <= n (n <= 63)
 // loads that hand each lane a piece of a different row reach much less of
 // the HBM bandwidth).  Buffer slot (row q, 16-byte segment x) holds segment
 // x ^ q, so the MFMA A-fragment reads (16 rows, same segment) hit distinct
-// banks.  The ring runs across tile boundaries.
+// banks.  The ring runs across tile boundaries.  The compiler makes a wave
+// wait for its copies in flight before it reads the ring; the eight waves of
+// a CU cover each other's waits (copies issued out of the compiler's sight,
+// with a wait for one buffer only, measured the same time).
 // RING == 0 (hidden rows too large for a ring beside them): every lane loads
 // its own row's A fragments straight into registers, K1_PF chunks ahead.
 template <int RING>
@@ -307,11 +310,11 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
   auto ring_issue = [&]() {
     if (zi < Z) {
       uint4 *dst = ring + (zi % (RING > 0 ? RING : 1)) * (K1_CHUNK / 16);
-      // (copies the compiler does not track: it would wait for every one of
-      // them before any ring read, and the ring would no longer overlap)
-      const uint32_t dl = lds_addr(dst);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) lds_copy16(rq[k] + ic * 16, dl + (uint32_t)(k * 64 * 16));
+      for (int k = 0; k < 4; ++k)
+        __builtin_amdgcn_global_load_lds(rq[k] + ic * 16,
+                                         (__attribute__((address_space(3))) void *)(dst + k * 64),
+                                         16, 0, 0);
       ++zi;
       if (++ic == nch) {
         ic = 0;
