@@ -390,7 +390,7 @@ bool mm_ok(const GemmArgs &a) {
 }
 
 // configurations: (BM, BN, WM, WN)
-#define MM_CONFIGS(X) X(256, 128, 4, 2, 4) X(128, 128, 2, 2, 4)
+#define MM_CONFIGS(X) X(256, 128, 4, 2, 4) X(128, 128, 2, 2, 4) X(128, 640, 1, 8, 3)
 
 hipError_t launch_mm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
                      hipEvent_t ev1) {
