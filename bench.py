@@ -61,7 +61,8 @@ def dominant_kernel(cfg):
 
     Fewer than 32 hidden rows: the streaming kernel with the fused per-slice
     Top-M (the logits never leave the chip): HBM-bound, bytes = W_lm + bias
-    + H.  32 or more rows (bf16): the tiled product writing the logits; its
+    + H.  32 or more rows (bf16): the tiled product writing the logits
+    (128 x 320 tiles of k_mm up to 128 rows, k1_logits_tiled beyond); its
     arithmetic intensity 2 rows d V / (2 V d + 2 rows d + 4 rows V) decides
     the bound against the ridge of the published peaks."""
     es = 2 if cfg.wtype == "bf16" else 4
@@ -71,12 +72,15 @@ def dominant_kernel(cfg):
         flops = 2 * rows * d * V
         nbytes = 2 * V * d + 2 * rows * d + 4 * V + 4 * rows * V
         ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if rows <= 128:
+            kern, label = "k_mm<128, 320>", "tiled bf16 MFMA LM-head product, 128 x 320 tiles"
+        else:
+            kern, label = "k1_logits_tiled", "tiled bf16 MFMA LM-head product, 128 x 256 tiles"
         if flops / nbytes >= ridge:
-            return dict(kernel="k1_logits_tiled", label="tiled bf16 MFMA LM-head product",
-                        bound="mfma", work=flops, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                        scale=1e12)
-        return dict(kernel="k1_logits_tiled", label="tiled bf16 MFMA LM-head product",
-                    bound="hbm", work=nbytes, peak=HBM_PEAK_GBS, unit="GB/s", scale=1e9)
+            return dict(kernel=kern, label=label, bound="mfma", work=flops,
+                        peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", scale=1e12)
+        return dict(kernel=kern, label=label, bound="hbm", work=nbytes, peak=HBM_PEAK_GBS,
+                    unit="GB/s", scale=1e9)
     name = "k1_lmhead_bf16" if cfg.wtype == "bf16" else "k1_lmhead_f32"
     return dict(kernel=name, label="LM-head GEMM + fused per-slice Top-M", bound="hbm",
                 work=es * V * d + 4 * V + 4 * rows * d, peak=HBM_PEAK_GBS, unit="GB/s",

@@ -253,27 +253,31 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny_bf16(GemmArgs a, int R
 }
 
 // Many activation rows (256 or more), bf16 x bf16: WM x WN waves per
-// workgroup, each a (BM/WM) x (BN/WN) block of 16 x 16 MFMA tiles (64 x 64;
-// two waves per SIMD, or two workgroups per CU, so that one wave's fragment
-// reads overlap another's MFMAs).  k chunks of 32: a row's chunk is 64 bytes, four
-// 16-byte pieces, piece c of row q stored at position c ^ h(q), h(q) =
-// ((q >> 1) & 3) ^ ((q >> 3) & 1), which puts the reads of one piece by 16
-// consecutive rows on distinct banks (as 8 lanes of 16 bytes over 128 bytes,
-// and as 16 lanes over 256).  A 4-stage ring: chunk kc is read while three
-// more are in flight; the copies are tracked by the kernel's own waits.
-// Activation rows are gathered through xidx; the weights' k index runs
-// modulo kw (a state split into bf16 planes meets the same weights once per
-// plane); rows past the device count *Rdev do no work.  Tasks run in
-// XCD-contiguous runs, so the row tiles of one weight tile share an L2.
+// workgroup, each a (BM/WM) x (BN/WN) block of 16 x 16 MFMA tiles (two waves
+// per SIMD, or two workgroups per CU, so that one wave's fragment reads
+// overlap another's MFMAs).  k chunks of 64: a row's chunk is one 128-byte
+// line, eight 16-byte pieces, piece c of row q stored at position c ^ (q & 7)
+// so that the fragment reads of 16 rows hit distinct banks (32-wide chunks,
+// half lines, measured slower: more LDS bank conflicts and, for a streamed
+// operand, the other half of each line fetched again).  A ring of STAGES
+// chunks, STAGES - 1 of them in flight while one is read; the copies are
+// tracked by the kernel's own waits.  Activation rows are gathered through
+// xidx; the weights' k index runs modulo kw (a state split into bf16 planes
+// meets the same weights once per plane); rows past the device count *Rdev
+// do no work.  Tasks run in XCD-contiguous runs, so the row tiles of one
+// weight tile share an L2.
 template <int BM, int BN, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(WM * WN * 64) void k_mm(GemmArgs a) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;   // 16 x 16 tiles per wave
-  constexpr int SROWS = BM + BN;              // 64-byte rows per stage
-  constexpr int SBYTES = SROWS * 64;
-  constexpr int NI = SROWS / 16 / NW;         // copy instructions per wave per stage
-  static_assert(SROWS % (16 * NW) == 0 && BM % (16 * NW) == 0, "copy split");
-  constexpr int NIA = BM / 16 / NW;           // ... of which activation rows
+  constexpr int BK = 64;
+  constexpr int CPR = BK / 8;                 // 16-byte pieces per row and chunk
+  constexpr int RPI = 64 / CPR;               // rows per copy instruction
+  constexpr int SROWS = BM + BN;
+  constexpr int SBYTES = SROWS * BK * 2;
+  constexpr int NI = SROWS / RPI / NW;        // copy instructions per wave per stage
+  static_assert(SROWS % (RPI * NW) == 0 && BM % (RPI * NW) == 0, "copy split");
+  constexpr int NIA = BM / RPI / NW;          // ... of which activation rows
   extern __shared__ __align__(16) uint8_t smem[];
   const uint4 *ring = reinterpret_cast<const uint4 *>(smem);
   const uint32_t ring_lds = lds_addr(smem);
@@ -291,15 +295,15 @@ __global__ __launch_bounds__(WM * WN * 64) void k_mm(GemmArgs a) {
   const int wm = (wave % WM) * (BM / WM), wn = (wave / WM) * (BN / WN);
   const uint16_t *X = static_cast<const uint16_t *>(a.X);
   const uint16_t *W = static_cast<const uint16_t *>(a.W);
-  const int nk = a.Kd / 32, nkw = (a.kw ? a.kw : a.Kd) / 32;
-  auto hsw = [](int q) { return ((q >> 1) & 3) ^ ((q >> 3) & 1); };
-  // copy instruction j = wave + NW i of a stage fills stage rows 16 j ..
-  // 16 j + 15 (activation rows first): lane l -> row 16 j + l / 4, position
-  // l & 3
+  const int nk = a.Kd / BK, nkw = (a.kw ? a.kw : a.Kd) / BK;
+  auto sw = [](int q) { return q & 7; };
+  // copy instruction j = wave + NW i of a stage fills stage rows RPI j ..
+  // RPI j + RPI - 1 (activation rows first): lane l -> row RPI j + l / CPR,
+  // position l % CPR
   const uint16_t *src[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int srow = 16 * (wave + NW * i) + (lane >> 2), pc = (lane & 3) ^ hsw(srow);
+    const int srow = RPI * (wave + NW * i) + lane / CPR, pc = (lane % CPR) ^ sw(srow);
     if (i < NIA) {
       const int xr = min(m0 + srow, R - 1);
       src[i] = X + (size_t)(a.xidx ? a.xidx[xr] : xr) * a.ldx + 8 * pc;
@@ -307,16 +311,16 @@ __global__ __launch_bounds__(WM * WN * 64) void k_mm(GemmArgs a) {
       src[i] = W + (size_t)min(n0 + srow - BM, a.N - 1) * a.ldw + 8 * pc;
     }
   }
-  // chunk kc goes to stage kc % 4; past the last chunk a step re-issues the
-  // last one (read by nobody), so every wait has the same count
+  // chunk kc goes to stage kc % STAGES; past the last chunk a step re-issues
+  // the last one (read by nobody), so every wait has the same count
   auto issue = [&](int kc) {
     const uint32_t dst = ring_lds + (uint32_t)((kc % STAGES) * SBYTES);
     const int kk = min(kc, nk - 1), kkw = kk % nkw;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      lds_copy16(src[i] + 32 * (i < NIA ? kk : kkw), dst + (uint32_t)((wave + NW * i) * 1024));
+      lds_copy16(src[i] + BK * (i < NIA ? kk : kkw), dst + (uint32_t)((wave + NW * i) * 1024));
   };
-  const int hl = hsw(lr);   // rows of a fragment read are 16-aligned: h(row) = h(lr)
+  const int hl = sw(lr);   // rows of a fragment read are 16-aligned: sw(row) = sw(lr)
   f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -332,15 +336,19 @@ __global__ __launch_bounds__(WM * WN * 64) void k_mm(GemmArgs a) {
     bare_barrier();
     issue(kc + STAGES - 1);
     const uint4 *st = ring + (kc % STAGES) * (SBYTES / 16);
-    uint4 fa[TM], fb[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[i] = st[(wm + 16 * i + lr) * 4 + (g ^ hl)];
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int pc = (4 * ks + g) ^ hl;
+      uint4 fa[TM], fb[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[j] = st[(BM + wn + 16 * j + lr) * 4 + (g ^ hl)];
+      for (int i = 0; i < TM; ++i) fa[i] = st[(wm + 16 * i + lr) * CPR + pc];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j) fb[j] = st[(BM + wn + 16 * j + lr) * CPR + pc];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = sk_mfma(fa[i], fb[j], acc[i][j]);
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = sk_mfma(fa[i], fb[j], acc[i][j]);
+    }
   }
   wait_vm<0>();   // no copy outlives the workgroup
   // lane holds Y[activation row 4 g + t][output lr] of tile (i, j)
@@ -364,33 +372,27 @@ __global__ __launch_bounds__(WM * WN * 64) void k_mm(GemmArgs a) {
 }
 
 template <int BM, int BN, int STAGES>
-static constexpr size_t mm_smem() { return (size_t)STAGES * (BM + BN) * 64; }
+static constexpr size_t mm_smem() { return (size_t)STAGES * (BM + BN) * 128; }
 
 // the largest per-wave block whose tile count still covers most of the
 // 256 CUs (one workgroup per CU)
+// the larger tile when it still makes 200 or more tiles (one workgroup per
+// CU), else 128 x 128 (two workgroups per CU)
 void mm_tile(int R, int N, int *bm, int *bn) {
-  static const int cand[2][2] = {{256, 128}, {128, 128}};
-  for (const auto &c : cand) {
-    const long long tiles = (long long)((R + c[0] - 1) / c[0]) * ((N + c[1] - 1) / c[1]);
-    if (tiles >= 200) {
-      *bm = c[0];
-      *bn = c[1];
-      return;
-    }
-  }
-  *bm = 128;
+  const long long big = (long long)((R + 255) / 256) * ((N + 127) / 128);
+  *bm = big >= 200 ? 256 : 128;
   *bn = 128;
 }
 
 bool mm_ok(const GemmArgs &a) {
   const int kw = a.kw ? a.kw : a.Kd;
   auto al16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-  return a.wtype == WT_BF16 && a.xtype == WT_BF16 && a.Kd % 32 == 0 && kw % 32 == 0 &&
+  return a.wtype == WT_BF16 && a.xtype == WT_BF16 && a.Kd % 64 == 0 && kw % 64 == 0 &&
          a.Kd % kw == 0 && a.ldx % 8 == 0 && a.ldw % 8 == 0 && al16(a.X) && al16(a.W);
 }
 
 // configurations: (BM, BN, WM, WN)
-#define MM_CONFIGS(X) X(256, 128, 4, 2, 4) X(128, 128, 2, 2, 4) X(128, 640, 1, 8, 3)
+#define MM_CONFIGS(X) X(256, 128, 4, 2, 3) X(128, 128, 2, 2, 2) X(128, 320, 2, 4, 2)
 
 hipError_t launch_mm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
                      hipEvent_t ev1) {

@@ -1024,9 +1024,9 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
   GemmArgs g{a.rows, a.V, a.d, a.Hb, WT_BF16, a.d, nullptr, 0, a.W, WT_BF16, a.d, a.bias,
              nullptr, 0, 1, 0, 0, logits, a.V};
   if (a.rows <= 128 && mm_ok(g)) {
-    // one row tile: 640-token tiles make one round of workgroups over the
-    // vocabulary (238 tiles at V = 151936) instead of 2.3 rounds of 256
-    e = launch_mm(g, 128, 640, st, ev0, ev1);
+    // one row tile: 320-token tiles make 1.9 rounds of workgroups over the
+    // vocabulary (475 tiles at V = 151936) instead of 2.3 rounds of 256
+    e = launch_mm(g, 128, 320, st, ev0, ev1);
   } else {
     hipExtLaunchKernelGGL(k1_logits_tiled, dim3(ntm * ntn), dim3(LT_THREADS), (uint32_t)LT_SMEM,
                           st, ev0, ev1, 0u, (const uint16_t *)a.Hb, a.rows, rows_pad, a.d,

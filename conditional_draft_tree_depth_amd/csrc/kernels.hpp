@@ -147,9 +147,10 @@ hipError_t launch_token_dedupe(int n, const int32_t *tok, void *first, int V, ui
                                int32_t *rowmap, int32_t *count, hipStream_t st);
 // true when launch_gemm runs a as a tiled product (many rows, bf16 operands)
 bool gemm_tiled_ok(const GemmArgs &a);
-// tiled product (bf16 operands, k a multiple of 32): tile bm x bn in
-// {256 x 128, 128 x 128}, chosen for R x N by mm_tile; ev0/ev1 (or null)
-// are recorded at the kernel's start and end
+// tiled product (bf16 operands, k and kw multiples of 64): tile bm x bn in
+// {256 x 128, 128 x 128} (chosen for R x N by mm_tile) or 128 x 320 (the
+// LM head with one row tile); ev0/ev1 (or null) are recorded at the
+// kernel's start and end
 bool mm_ok(const GemmArgs &a);
 void mm_tile(int R, int N, int *bm, int *bn);
 hipError_t launch_mm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
