@@ -180,6 +180,30 @@ __device__ __forceinline__ int next_pow2(int n) {
   return p;
 }
 
+// Exact three-term bf16 split of 8 fp32 values, each term packed as one
+// 16-byte MFMA fragment: hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi
+// - mid), so x - hi - mid - lo is below 2^-24 |x|; a bf16 weight times each
+// term is exact in fp32.
+__device__ __forceinline__ void split3_bf16(const float (&x)[8], uint4 (&t)[3]) {
+  uint32_t w[3][4];
+#pragma unroll
+  for (int k = 0; k < 8; k += 2) {
+    uint32_t h[3][2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint16_t b0 = f32_to_bf16_rne(x[k + e]);
+      const float r1 = x[k + e] - bf16_bits_to_f32(b0);
+      const uint16_t b1 = f32_to_bf16_rne(r1);
+      const uint16_t b2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(b1));
+      h[0][e] = b0; h[1][e] = b1; h[2][e] = b2;
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) w[q][k / 2] = h[q][0] | (h[q][1] << 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) t[q] = make_uint4(w[q][0], w[q][1], w[q][2], w[q][3]);
+}
+
 // ---- staged tiles: direct global-to-LDS copies with waits of our own ----
 // The compiler, seeing a copy into LDS in flight, waits for every such copy
 // before any LDS read it cannot prove unrelated (and a workgroup fence

@@ -332,7 +332,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   if (pe == hipSuccess) pe = topb_prepare(ctx->lds_max);
   if (pe == hipSuccess) pe = gemm_prepare();
   // correction logits inside the selection kernel: bf16 W2 rows of 16-byte
-  // pieces whose slice (and one u row per wave) fits in LDS
+  // pieces whose slice (and the depth's logits) fits in LDS
   ctx->sel_corr = w->wtype == DTREE_BF16 && r % 8 == 0 && r <= 512 &&
                   reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
                   select_corr_smem(c.max_M, r) + 45056 <= ctx->lds_max;

@@ -17,6 +17,13 @@ constexpr int SEL_MAXZ = 1024;   // children per request and depth
 constexpr int SEL_MAXW = 512;
 constexpr int CL_BR = 4;         // expanded branches per correction workgroup
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+__device__ __forceinline__ f32x4 cl_mfma(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // Corrected logits of the depth's candidates for every expanded branch:
 //   ell[a][j] = Cl[j] + W2[C[j]] . u_a
 // ("Resumen Técnico: Domino", Metodología 2: L = L_base + Delta L with the
@@ -90,6 +97,66 @@ __global__ __launch_bounds__(256) void k_corr_logits(int A, int M, int r, int D,
   }
 }
 
+// The same logits on the matrix cores (bf16 W2 with 16-byte rows, r a
+// multiple of 8): workgroups of 4 waves per (request, 16 branches, 64
+// candidates), one 16 x 16 tile (candidates x branches) per wave.  A wave
+// issues the u values and W2 fragments of up to 8 k steps of 32 at once
+// (straight from memory: W2 rows by candidate token), then splits each
+// lane's 8 u values exactly into three bf16 terms (W2 is bf16, so every
+// product is exact in fp32) and runs the MFMAs.
+constexpr int CLM_KB = 8;   // k steps per batch of loads
+__global__ __launch_bounds__(256) void k_corr_logits_mfma(int A, int M, int r, int D, int delta,
+                                                          const uint16_t *__restrict__ W2,
+                                                          const int32_t *__restrict__ C,
+                                                          const float *__restrict__ Cl,
+                                                          const float *__restrict__ u, int ldu,
+                                                          float *__restrict__ ell) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lr = lane & 15, g = lane >> 4;
+  const int q = blockIdx.x, a = blockIdx.y * 16 + lr, jt = blockIdx.z * 4 + wave;
+  if (jt * 16 >= M) return;   // (no barrier in this kernel)
+  const int32_t *toks = C + ((size_t)q * D + delta) * M;
+  const float *clq = Cl + ((size_t)q * D + delta) * M;
+  const float *ua = u + ((size_t)q * A + min(a, A - 1)) * ldu;
+  const int j = min(jt * 16 + lr, M - 1);
+  const uint16_t *wr = W2 + (size_t)max(toks[j], 0) * r;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < r; k0 += 32 * CLM_KB) {
+    // loads from clamped addresses, always in bounds, then masked: no
+    // branch between them
+    float x[CLM_KB][8];
+    uint4 wa[CLM_KB];
+#pragma unroll
+    for (int st = 0; st < CLM_KB; ++st) {
+      const int kk = k0 + 32 * st + 8 * g;   // r % 8 == 0: 8 elements all in or all out
+      const int kc = min(kk, r - 8);
+      const bool in = kk < r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = ua[kc + e];
+        x[st][e] = (in && a < A) ? v : 0.f;
+      }
+      const uint4 w = *reinterpret_cast<const uint4 *>(wr + kc);
+      wa[st] = in ? w : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int st = 0; st < CLM_KB; ++st) {
+      uint4 t3[3];
+      split3_bf16(x[st], t3);
+#pragma unroll
+      for (int tq = 0; tq < 3; ++tq) acc = cl_mfma(wa[st], t3[tq], acc);
+    }
+  }
+  // lane holds D[candidate 4 g + t][branch lr]
+  if (a < A) {
+    float *eq = ell + ((size_t)q * A + a) * M;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int jj = jt * 16 + 4 * g + tt;
+      if (jj < M) eq[jj] = clq[jj] + acc[tt];
+    }
+  }
+}
+
 size_t corr_logits_smem(int A, int M, int r, int wtype) {
   const size_t es = wtype == WT_BF16 ? 2 : 4;
   const size_t rs = wtype == WT_BF16 ? (r % 8 == 0 ? r + 8 : r + 2) : r + 1;
@@ -108,6 +175,11 @@ hipError_t launch_corr_logits(int b, int A, int M, int r, int D, int delta, cons
   const size_t sm = corr_logits_smem(A, M, r, wtype);
   const dim3 grid(b, (A + CL_BR - 1) / CL_BR);
   const int vec = wtype == WT_BF16 && r % 8 == 0 && reinterpret_cast<uintptr_t>(W2) % 16 == 0;
+  if (vec) {
+    hipLaunchKernelGGL(k_corr_logits_mfma, dim3(b, (A + 15) / 16, (M + 63) / 64), dim3(256), 0, st,
+                       A, M, r, D, delta, static_cast<const uint16_t *>(W2), C, Cl, u, ldu, ell);
+    return hipGetLastError();
+  }
   if (wtype == WT_BF16)
     hipLaunchKernelGGL(k_corr_logits<uint16_t>, grid, dim3(256), sm, st, A, M, r, D, delta, vec,
                        static_cast<const uint16_t *>(W2), C, Cl, u, ldu, ell);
@@ -275,11 +347,13 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
 }
 
 // The same selection with the corrected logits computed in place (bf16 W2,
-// r a multiple of 8): the r x M slice of W2 for the depth's candidates is
-// staged in LDS once per request, and the wave of each expanded branch
-// forms ell[j] = Cl[j] + W2[C[j]] . u_a for its M candidates (in the order
-// of k_corr_logits) before the log-softmax, so the logits never leave the
-// workgroup.
+// r a multiple of 8, A M <= 2048): the r x M slice of W2 for the depth's
+// candidates is staged in LDS once per request, and all logits
+// ell[a][j] = Cl[j] + W2[C[j]] . u_a are formed on the matrix cores into LDS
+// (an M x r by r x A product over the exact three-term split of u) before
+// the per-branch log-softmax, so the logits never leave the workgroup.
+// (Formed by each branch's wave as fp32 dot products on the vector units,
+// they took a wide-tree depth 18.8 us, mostly those products.)
 __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K, int W, int D,
                                                              int delta, int off, int r,
                                                              const uint16_t *__restrict__ W2,
@@ -300,7 +374,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K
   __shared__ int16_t cidx[SEL_MAXZ];                      // children's candidate index
   const int rs = r + 8;
   uint16_t *W2s = reinterpret_cast<uint16_t *>(smem);                    // [M][r + 8]
-  float *ubuf = reinterpret_cast<float *>(smem + (((size_t)M * rs * 2 + 15) & ~(size_t)15));
+  float *ell_s = reinterpret_cast<float *>(smem + (((size_t)M * rs * 2 + 15) & ~(size_t)15));  // [A][M]
   const int q = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int nw = blockDim.x >> 6;
@@ -327,57 +401,60 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K
         *reinterpret_cast<const uint4 *>(W2 + (size_t)tk * r + 8 * c8);
   }
   __syncthreads();
-  const bool h0 = lane < M, h1 = lane + 64 < M;
-  float *ub = ubuf + wave * r;
-  // u row of the wave's next branch, in registers (r <= 512), loaded while
-  // the current branch is processed
-  float un[8];
-  auto load_u = [&](int a) {
-    const float *ua = u + ((size_t)q * A + a) * ldu;
+  // Correction logits of every (branch, candidate) pair on the matrix cores,
+  // one 16 x 16 tile (candidates x branches) per wave at a time:
+  // ell_s[a][j] = Cl[j] + W2[C[j]] . u_a over k steps of 32, u split exactly
+  // into three bf16 terms (W2 is bf16, so every product is exact in fp32).
+  {
+    const int lr = lane & 15, g = lane >> 4;
+    const int ntj = (M + 15) >> 4, nta = (A + 15) >> 4;
+    for (int tile = wave; tile < ntj * nta; tile += nw) {
+      const int jt = tile % ntj, at = tile / ntj;
+      const int j = jt * 16 + lr, a = at * 16 + lr;
+      const uint16_t *wr = W2s + (j < M ? j : 0) * rs;
+      const float *ua = u + ((size_t)q * A + (a < A ? a : 0)) * ldu;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      // up to eight k steps at a time: their u loads are all in flight
+      // together
+      for (int k0 = 0; k0 < r; k0 += 256) {
+        // (loads from clamped addresses, always in bounds, then masked: no
+        // branch between them)
+        float x[8][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (lane + 64 * i < r) un[i] = ua[lane + 64 * i];
-  };
-  if (wave < A) load_u(wave);
-  for (int a = wave; a < A; a += nw) {
+        for (int st = 0; st < 8; ++st) {
+          const int kk = k0 + 32 * st + 8 * g;   // r % 8 == 0: 8 elements all in or all out
+          const bool in = kk < r && a < A;
+          const float *up = ua + min(kk, r - 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (lane + 64 * i < r) ub[lane + 64 * i] = un[i];
-    if (a + nw < A) load_u(a + nw);
-    // LDS accesses of one wave take effect in issue order
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    float acc0 = 0.f, acc1 = 0.f;
-    const uint16_t *w0 = W2s + (h0 ? lane : 0) * rs, *w1 = W2s + (h1 ? lane + 64 : 0) * rs;
-    for (int c8 = 0; c8 < r; c8 += 8) {
-      const float4 u0 = *reinterpret_cast<const float4 *>(ub + c8);
-      const float4 u1 = *reinterpret_cast<const float4 *>(ub + c8 + 4);
-      const uint4 wa = *reinterpret_cast<const uint4 *>(w0 + c8);
-      acc0 += __uint_as_float(wa.x << 16) * u0.x;
-      acc0 += __uint_as_float(wa.x & 0xFFFF0000u) * u0.y;
-      acc0 += __uint_as_float(wa.y << 16) * u0.z;
-      acc0 += __uint_as_float(wa.y & 0xFFFF0000u) * u0.w;
-      acc0 += __uint_as_float(wa.z << 16) * u1.x;
-      acc0 += __uint_as_float(wa.z & 0xFFFF0000u) * u1.y;
-      acc0 += __uint_as_float(wa.w << 16) * u1.z;
-      acc0 += __uint_as_float(wa.w & 0xFFFF0000u) * u1.w;
-      if (h1) {
-        const uint4 wb = *reinterpret_cast<const uint4 *>(w1 + c8);
-        acc1 += __uint_as_float(wb.x << 16) * u0.x;
-        acc1 += __uint_as_float(wb.x & 0xFFFF0000u) * u0.y;
-        acc1 += __uint_as_float(wb.y << 16) * u0.z;
-        acc1 += __uint_as_float(wb.y & 0xFFFF0000u) * u0.w;
-        acc1 += __uint_as_float(wb.z << 16) * u1.x;
-        acc1 += __uint_as_float(wb.z & 0xFFFF0000u) * u1.y;
-        acc1 += __uint_as_float(wb.w << 16) * u1.z;
-        acc1 += __uint_as_float(wb.w & 0xFFFF0000u) * u1.w;
+          for (int e = 0; e < 8; ++e) {
+            const float v = up[e];
+            x[st][e] = in ? v : 0.f;
+          }
+        }
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int kk = k0 + 32 * st + 8 * g;
+          uint4 wa = *reinterpret_cast<const uint4 *>(wr + min(kk, r - 8));
+          if (kk >= r) wa = make_uint4(0u, 0u, 0u, 0u);
+          uint4 t3[3];
+          split3_bf16(x[st], t3);
+#pragma unroll
+          for (int tq = 0; tq < 3; ++tq) acc = cl_mfma(wa, t3[tq], acc);
+        }
+      }
+      // lane holds D[candidate 4 g + t][branch lr]
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int jj = jt * 16 + 4 * g + tt;
+        if (jj < M && a < A) ell_s[a * M + jj] = clv[jj] + acc[tt];
       }
     }
-    const float l0 = h0 ? clv[lane] + acc0 : -INFINITY;
-    const float l1 = h1 ? clv[lane + 64] + acc1 : -INFINITY;
-    // every lane's reads of ub are done before the next branch refills it
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  const bool h0 = lane < M, h1 = lane + 64 < M;
+  for (int a = wave; a < A; a += nw) {
+    const float l0 = h0 ? ell_s[a * M + lane] : -INFINITY;
+    const float l1 = h1 ? ell_s[a * M + lane + 64] : -INFINITY;
     const int p = pnode[a];
     const uint32_t pr = prank[a];
     const float ps = pscore[a];
@@ -436,7 +513,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K
 }
 
 size_t select_corr_smem(int M, int r) {
-  return (((size_t)M * (r + 8) * 2 + 15) & ~(size_t)15) + (size_t)(SEL_THREADS / 64) * r * 4;
+  // W2 rows [M][r + 8] bf16, then the logits [A][M] fp32 (A M <= 2048)
+  return (((size_t)M * (r + 8) * 2 + 15) & ~(size_t)15) + (size_t)2048 * 4;
 }
 
 hipError_t select_corr_prepare(size_t lds_bytes) {
