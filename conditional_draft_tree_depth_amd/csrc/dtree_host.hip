@@ -427,7 +427,10 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
   LMHeadArgs la{H, rows, d, w.W_lm, wt, w.V, w.lm_bias, M, ctx->P, ws.part,
                 fuse_uH ? w.W1 : nullptr, d + s, r, ws.uH,
                 root, batch, D + 1, tb, ctx->k1_ring, ws.hb};
-  HIPCHK(ctx, launch_stage_hidden(la, st));
+  // round start: a kernel of its own ahead of the tiled product (bf16 rows
+  // for it); the streaming kernels round the rows and start the round
+  // themselves
+  if (tiled) HIPCHK(ctx, launch_stage_hidden(la, st));
   // the LM-head stage is timed by the kernel's own start and end (no marker
   // packets around it)
   hipEvent_t k1ev[2] = {nullptr, nullptr};

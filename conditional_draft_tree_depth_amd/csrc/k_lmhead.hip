@@ -255,9 +255,10 @@ __device__ __forceinline__ void k1_wait_vm(int n) {   // vmcnt <= n (n <= 63)
 // its own row's A fragments straight into registers, K1_PF chunks ahead.
 template <int RING>
 __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
-    const uint16_t *__restrict__ Hb, int rows, int d, const uint16_t *__restrict__ W, int V,
+    const float *__restrict__ H, int rows, int d, const uint16_t *__restrict__ W, int V,
     const float *__restrict__ bias, int M, uint64_t *__restrict__ part,
-    const uint16_t *__restrict__ W1, int ldw1, int r, float *__restrict__ uH) {
+    const uint16_t *__restrict__ W1, int ldw1, int r, float *__restrict__ uH,
+    const int32_t *__restrict__ root, int b, int Dp1, TreeBufs tb) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int P = gridDim.y, RB = gridDim.x;
   int y = blockIdx.y, bx = blockIdx.x;
@@ -355,19 +356,41 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
     const int c0 = t0 * 16, nc = min(min(t1, ntV) * 16, V) - c0;
     for (int c = threadIdx.x; c < nc; c += K1_WAVES * 64) bs[c] = bias ? bias[c0 + c] : 0.f;
   }
-  // the 16 rounded hidden rows of this block (k1_stage_hidden) straight
-  // into LDS, 1 KiB per copy instruction; 16-byte chunk j of row q is stored
-  // at chunk j ^ (q & 7) of the row, so the B-fragment reads (16 rows, same
-  // chunk) hit distinct banks
+  // round start: the first workgroup of each slice starts the tree buffers
+  // of its requests (read only by the kernels after this one)
+  if (bx == 0 && root)
+    for (int q = y; q < b; q += P) init_round_request(q, root, tb, Dp1, threadIdx.x, K1_WAVES * 64);
+  // the 16 hidden rows of this block, rounded to bf16 (nearest-even) while
+  // they are staged in LDS (rows past the last are zeros); 16-byte chunk j
+  // of row q is stored at chunk j ^ (q & 7) of the row, so the B-fragment
+  // reads (16 rows, same chunk) hit distinct banks
   {
-    const uint4 *src = reinterpret_cast<const uint4 *>(Hb + (size_t)row0 * d);
-    for (int in = wave; in < (16 * cpr) >> 6; in += K1_WAVES) {
-      const int ci = in * 64 + lane, rr = ci / cpr, j = ci - rr * cpr;
-      __builtin_amdgcn_global_load_lds(src + rr * cpr + (j ^ (rr & 7)),
-                                       (__attribute__((address_space(3))) void *)(Hs + in * 512),
-                                       16, 0, 0);
+    constexpr int HB = 5;   // chunks per thread in flight at a time
+    for (int ci0 = threadIdx.x; ci0 < 16 * cpr; ci0 += HB * K1_WAVES * 64) {
+      float4 v[HB][2];
+#pragma unroll
+      for (int h = 0; h < HB; ++h) {
+        const int ci = ci0 + h * K1_WAVES * 64, rr = ci / cpr, j = ci - rr * cpr;
+        v[h][0] = v[h][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ci < 16 * cpr && row0 + rr < rows) {
+          const float *src = H + (size_t)(row0 + rr) * d + 8 * (j ^ (rr & 7));
+          v[h][0] = *reinterpret_cast<const float4 *>(src);
+          v[h][1] = *reinterpret_cast<const float4 *>(src + 4);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < HB; ++h) {
+        const int ci = ci0 + h * K1_WAVES * 64;
+        if (ci < 16 * cpr) {
+          auto pk = [](float lo, float hi) {
+            return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+          };
+          *reinterpret_cast<uint4 *>(Hs + (size_t)ci * 8) =
+              make_uint4(pk(v[h][0].x, v[h][0].y), pk(v[h][0].z, v[h][0].w),
+                         pk(v[h][1].x, v[h][1].y), pk(v[h][1].z, v[h][1].w));
+        }
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
   }
   __syncthreads();
 
@@ -645,8 +668,8 @@ __global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
   }
 }
 
-// Round start for the bf16 path: Hb = bf16_rne(H) with rows padded to a
-// multiple of 16 by zeros (the LM-head kernel copies it into LDS as is), and
+// Round start ahead of the tiled bf16 product: Hb = bf16_rne(H) with rows
+// padded to a multiple of 16 by zeros (the tiled products read it), and
 // init_round_request for every request.
 __global__ __launch_bounds__(256) void k1_stage_hidden(const float *__restrict__ H, int rows,
                                                        int rows_pad, int d,
@@ -995,9 +1018,10 @@ hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st, hipEvent_t ev0, hi
     const size_t sm = lmhead_smem(a.d, a.wtype, a.ring);
 #define K1_LAUNCH(RING)                                                                           \
   hipExtLaunchKernelGGL((k1_lmhead_bf16<RING>), grid, dim3(K1_WAVES * 64), (uint32_t)sm, st, ev0,  \
-                        ev1, 0u, (const uint16_t *)a.Hb, a.rows, a.d,                              \
+                        ev1, 0u, a.H, a.rows, a.d,                                                 \
                         static_cast<const uint16_t *>(a.W), a.V, a.bias, a.M, a.part,              \
-                        static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH)
+                        static_cast<const uint16_t *>(a.W1), a.ldw1, a.r, a.uH, a.root, a.b,       \
+                        a.Dp1, a.t)
     if (a.ring == 2) K1_LAUNCH(2);
     else if (a.ring == 1) K1_LAUNCH(1);
     else K1_LAUNCH(0);

@@ -76,12 +76,13 @@ struct LMHeadArgs {
   const void *W1;      // bf16 only: W1[:, :d] rows ride along -> uH (or null)
   int ldw1, r;
   float *uH;           // [rows, r]
-  // round start (init_round_request for q < b), done by the first workgroups
+  // round start (init_round_request for q < b): done by the first workgroups
+  // of the streaming kernels, by k1_stage_hidden ahead of the tiled product
   const int32_t *root;
   int b, Dp1;
   TreeBufs t;
   int ring;            // bf16: LDS ring depth from lmhead_ring (0 = register path)
-  uint16_t *Hb;        // bf16: [rows rounded up to 16, d] rounded hidden rows (workspace)
+  uint16_t *Hb;        // bf16, tiled product: [rows rounded up to 16, d] rounded hidden rows
 };
 int lmhead_partitions(int V, int wtype, int extra_tiles);
 // LDS ring depth of the bf16 kernel that fits lds_max (0: register path)
@@ -89,7 +90,9 @@ int lmhead_ring(int d, int wtype, size_t lds_max);
 size_t lmhead_smem(int d, int wtype, int ring);
 // every prepare call lets its kernels use up to lds_bytes of LDS in all
 hipError_t lmhead_prepare(int wtype, int ring, size_t lds_bytes);
-// bf16: round start (k1_stage_hidden: Hb, init_round_request); before launch_lmhead
+// bf16, tiled product: round start (k1_stage_hidden: Hb, init_round_request)
+// before launch_lmhead_tiled; the streaming kernels (launch_lmhead) round the
+// hidden rows and start the round themselves
 hipError_t launch_stage_hidden(const LMHeadArgs &a, hipStream_t st);
 // ev0 / ev1 (or null): events that take the kernel's own start and end times
 hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st, hipEvent_t ev0 = nullptr,

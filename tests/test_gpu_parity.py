@@ -69,13 +69,19 @@ def test_random_small_shapes(gpu_lib, seed):
     (3, 128, 256, 384, 48, 4, 128, 8, 8, 90, 8),
     (4, 384, 128, 128, 256, 7, 33, 5, 12, 77, 3),
     # 8 x 32 = 256 expanded branches and 40 hidden rows: tiled products over
-    # the three-plane states, tiled LM head with lists from the logits
+    # the two-plane states, tiled LM head with lists from the logits
     (5, 256, 128, 128, 64, 5, 64, 8, 32, 200, 8),
     (6, 128, 192, 256, 32, 4, 128, 4, 64, 150, 6),
     # 32 hidden rows and M > 64: exact lists by bisection from the logits,
     # V odd (4-byte logit loads) and V % 4 == 0 (16-byte loads)
     (7, 128, 128, 128, 32, 4, 128, 4, 16, 120, 8),
     (8, 256, 128, 128, 32, 4, 96, 4, 16, 120, 8),
+    # rank 40 (a 32-wide k step and an 8-wide tail) on the matrix-core
+    # correction logits: in the selection kernel up to 2048 branch-candidate
+    # pairs, then 64 x 64 = 4096 in the stand-alone kernel (last depth)
+    (9, 128, 128, 128, 40, 4, 64, 4, 64, 120, 2),
+    # rank 8 (one partial k step), 96 candidates
+    (10, 128, 64, 64, 8, 4, 96, 4, 32, 100, 2),
 ])
 def test_mfma_product_paths(gpu_lib, seed, d, e, s, r, D, M, K, W, B, batch):
     """bf16 shapes whose products run on the MFMA kernels: the row-gathered
