@@ -62,7 +62,7 @@ def dominant_kernel(cfg):
     Fewer than 32 hidden rows: the streaming kernel with the fused per-slice
     Top-M (the logits never leave the chip): HBM-bound, bytes = W_lm + bias
     + H.  32 or more rows (bf16): the tiled product writing the logits
-    (128 x 320 tiles of k_mm up to 128 rows, k1_logits_tiled beyond); its
+    (k_mm_lm, 128 x 320 tiles up to 128 rows, 128 x 256 beyond); its
     arithmetic intensity 2 rows d V / (2 V d + 2 rows d + 4 rows V) decides
     the bound against the ridge of the published peaks."""
     es = 2 if cfg.wtype == "bf16" else 4
@@ -73,9 +73,9 @@ def dominant_kernel(cfg):
         nbytes = 2 * V * d + 2 * rows * d + 4 * V + 4 * rows * V
         ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         if rows <= 128:
-            kern, label = "k_mm<128, 320>", "tiled bf16 MFMA LM-head product, 128 x 320 tiles"
+            kern, label = "k_mm_lm<128, 320>", "tiled bf16 MFMA LM-head product, 128 x 320 tiles"
         else:
-            kern, label = "k1_logits_tiled", "tiled bf16 MFMA LM-head product, 128 x 256 tiles"
+            kern, label = "k_mm_lm<128, 256>", "tiled bf16 MFMA LM-head product, 128 x 256 tiles"
         if flops / nbytes >= ridge:
             return dict(kernel=kern, label=label, bound="mfma", work=flops,
                         peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", scale=1e12)
@@ -109,7 +109,6 @@ def counters_traffic(workload, kernel="k1_lmhead_bf16"):
     summary of this workload, if it was taken on the current kernel source;
     else None."""
     stem, src = {"k1_lmhead_bf16": ("k1_lmhead", "k_lmhead.hip"),
-                 "k1_logits_tiled": ("k1_logits_tiled", "k_lmhead.hip"),
                  "k_tree_attn": ("tree_attn", "k_attn.hip")}.get(kernel, (None, None))
     if stem is None:
         return None

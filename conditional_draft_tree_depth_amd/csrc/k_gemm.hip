@@ -326,15 +326,38 @@ __global__ __launch_bounds__(WM * WN * 64) void k_mm(GemmArgs a) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto epilogue = [&]() {
+    // lane holds Y[activation row 4 g + t][output lr] of tile (i, j)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn + j * 16 + lr;
+      if (n >= a.N) continue;
+      const float bv = (a.bias && n >= a.bias_n0) ? a.bias[n - a.bias_n0] : 0.f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int row = m0 + wm + i * 16 + 4 * g + t;
+          if (row >= R) continue;
+          float v = acc[i][j][t] + bv;
+          if (a.addend && n < a.add_n)
+            v += a.addend[(size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda + n];
+          a.Y[(size_t)row * a.ldy + n] = v;
+        }
+    }
+  };
 #pragma unroll
   for (int kc = 0; kc < STAGES - 1; ++kc) issue(kc);
   for (int kc = 0; kc < nk; ++kc) {
-    // chunk kc has landed (this wave's copies; the next STAGES - 2 may fly);
-    // after the barrier every wave's copies are visible and the stage of
-    // chunk kc - 1 is free
+    // chunk kc has landed (this wave's copies; the next STAGES - 2 may
+    // fly); after the barrier every wave's copies are visible and the
+    // stage of chunk kc - 1 is free
     wait_vm<(STAGES - 2) * NI>();
     bare_barrier();
     issue(kc + STAGES - 1);
+    // (fragments of the next chunk double-buffered and read while this
+    // chunk's MFMAs run measured slower for the stress state product, 58
+    // against 55 us)
     const uint4 *st = ring + (kc % STAGES) * (SBYTES / 16);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
@@ -351,24 +374,136 @@ __global__ __launch_bounds__(WM * WN * 64) void k_mm(GemmArgs a) {
     }
   }
   wait_vm<0>();   // no copy outlives the workgroup
-  // lane holds Y[activation row 4 g + t][output lr] of tile (i, j)
+  epilogue();
+}
+
+// The LM-head product (rows of H against the vocabulary rows of W_lm, no
+// gather, no planes): the same tiles with a ring of its own per operand,
+// 2 stages for the hidden rows (L2 hits) and SB for the weight rows, which
+// stream from HBM, so SB - 1 chunks of them are in flight (the shared ring
+// held 2, and the streamed chunks' latency set the pace).  At step kc the
+// copies of hidden-row chunk kc + 1 and weight chunk kc + SB - 1 are issued;
+// the wait before it leaves only the previous step's weight copies in
+// flight, which makes both of chunk kc's copies land.
+template <int BM, int BN, int WM, int WN, int SB>
+__global__ __launch_bounds__(WM * WN * 64) void k_mm_lm(GemmArgs a) {
+  constexpr int SA = 2;
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  constexpr int BK = 64, CPR = 8, RPI = 8;
+  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
+  constexpr int NA = BM / RPI / NW, NB = BN / RPI / NW;   // copy instructions per wave and chunk
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0 && SB >= 3, "copy split");
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint4 *ringA = reinterpret_cast<const uint4 *>(smem);
+  const uint4 *ringB = reinterpret_cast<const uint4 *>(smem + SA * ABYTES);
+  const uint32_t ldsA = lds_addr(smem), ldsB = ldsA + SA * ABYTES;
+  const int ntm = (a.R + BM - 1) / BM, ntn = (a.N + BN - 1) / BN;
+  const int total = ntm * ntn;
+  const int per = (total + 7) / 8;
+  const int task = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (task >= total) return;
+  const int m0 = (task % ntm) * BM, n0 = (task / ntm) * BN;
+  const int R = a.R;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int wm = (wave % WM) * (BM / WM), wn = (wave / WM) * (BN / WN);
+  const uint16_t *X = static_cast<const uint16_t *>(a.X);
+  const uint16_t *W = static_cast<const uint16_t *>(a.W);
+  const int nk = a.Kd / BK;
+  // copy instruction i of an operand's chunk fills its rows RPI (wave + NW i)
+  // .. + RPI - 1: lane l -> row + l / 8, position l % 8 (chunk c of row q
+  // at position c ^ (q & 7))
+  const uint16_t *srcA[NA], *srcB[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = RPI * (wave + NW * i) + lane / CPR, pc = (lane % CPR) ^ (row & 7);
+    srcA[i] = X + (size_t)min(m0 + row, R - 1) * a.ldx + 8 * pc;
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int row = RPI * (wave + NW * i) + lane / CPR, pc = (lane % CPR) ^ (row & 7);
+    srcB[i] = W + (size_t)min(n0 + row, a.N - 1) * a.ldw + 8 * pc;
+  }
+  // past the last chunk a step re-issues the last one (read by nobody), so
+  // every wait has the same count
+  auto issueA = [&](int kc) {
+    const uint32_t dst = ldsA + (uint32_t)((kc % SA) * ABYTES);
+    const int kk = min(kc, nk - 1);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) lds_copy16(srcA[i] + BK * kk, dst + (uint32_t)((wave + NW * i) * 1024));
+  };
+  auto issueB = [&](int kc) {
+    const uint32_t dst = ldsB + (uint32_t)((kc % SB) * BBYTES);
+    const int kk = min(kc, nk - 1);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) lds_copy16(srcB[i] + BK * kk, dst + (uint32_t)((wave + NW * i) * 1024));
+  };
+  const int hl = lr & 7;
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  issueA(0);
+#pragma unroll
+  for (int kc = 0; kc < SB - 1; ++kc) issueB(kc);
+  for (int kc = 0; kc < nk; ++kc) {
+    // chunk kc of both operands has landed (this wave's copies): at step 0
+    // the weight chunks 1 .. SB - 2 may fly, later the previous step's
+    // weight chunk only
+    if (kc == 0) wait_vm<(SB - 2) * NB>();
+    else wait_vm<NB>();
+    bare_barrier();
+    issueA(kc + 1);
+    issueB(kc + SB - 1);
+    const uint4 *sa = ringA + (kc % SA) * (ABYTES / 16), *sb = ringB + (kc % SB) * (BBYTES / 16);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int pc = (4 * ks + g) ^ hl;
+      uint4 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = sa[(wm + 16 * i + lr) * CPR + pc];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = sb[(wn + 16 * j + lr) * CPR + pc];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = sk_mfma(fa[i], fb[j], acc[i][j]);
+    }
+  }
+  wait_vm<0>();   // no copy outlives the workgroup
+  // lane holds Y[row 4 g + t][output lr] of tile (i, j)
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int n = n0 + wn + j * 16 + lr;
     if (n >= a.N) continue;
-    const float bv = (a.bias && n >= a.bias_n0) ? a.bias[n - a.bias_n0] : 0.f;
+    const float bv = a.bias ? a.bias[n] : 0.f;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int row = m0 + wm + i * 16 + 4 * g + t;
-        if (row >= R) continue;
-        float v = acc[i][j][t] + bv;
-        if (a.addend && n < a.add_n)
-          v += a.addend[(size_t)((row / a.adiv) * a.amul + a.aoff) * a.lda + n];
-        a.Y[(size_t)row * a.ldy + n] = v;
+        if (row < R) a.Y[(size_t)row * a.ldy + n] = acc[i][j][t] + bv;
       }
   }
+}
+template <int BM, int BN, int SB>
+static constexpr size_t mm_lm_smem() { return (size_t)2 * BM * 128 + (size_t)SB * BN * 128; }
+#define MM_LM_CONFIGS(X) X(128, 256, 2, 4, 4) X(128, 320, 2, 4, 3)
+
+hipError_t launch_mm_lm(const GemmArgs &a, int bn, hipStream_t st, hipEvent_t ev0,
+                        hipEvent_t ev1) {
+  const int total = ((a.R + 127) / 128) * ((a.N + bn - 1) / bn);
+  const dim3 grid(8 * ((total + 7) / 8));
+#define MM_LM_LAUNCH(BM_, BN_, WM_, WN_, SB_)                                                   \
+  if (bn == BN_) {                                                                              \
+    hipExtLaunchKernelGGL((k_mm_lm<BM_, BN_, WM_, WN_, SB_>), grid, dim3(WM_ * WN_ * 64),       \
+                          (uint32_t)mm_lm_smem<BM_, BN_, SB_>(), st, ev0, ev1, 0u, a);          \
+    return hipGetLastError();                                                                   \
+  }
+  MM_LM_CONFIGS(MM_LM_LAUNCH)
+#undef MM_LM_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 template <int BM, int BN, int STAGES>
@@ -392,7 +527,7 @@ bool mm_ok(const GemmArgs &a) {
 }
 
 // configurations: (BM, BN, WM, WN)
-#define MM_CONFIGS(X) X(256, 128, 4, 2, 3) X(128, 128, 2, 2, 2) X(128, 320, 2, 4, 2)
+#define MM_CONFIGS(X) X(256, 128, 4, 2, 3) X(128, 128, 2, 2, 2)
 
 hipError_t launch_mm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
                      hipEvent_t ev1) {
@@ -418,6 +553,13 @@ static hipError_t mm_prepare() {
                             (int)mm_smem<BM_, BN_, S_>());
   MM_CONFIGS(MM_SET)
 #undef MM_SET
+#define MM_LM_SET(BM_, BN_, WM_, WN_, SB_)                                                      \
+  if (e == hipSuccess)                                                                          \
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_mm_lm<BM_, BN_, WM_, WN_, SB_>),  \
+                            hipFuncAttributeMaxDynamicSharedMemorySize,                         \
+                            (int)mm_lm_smem<BM_, BN_, SB_>());
+  MM_LM_CONFIGS(MM_LM_SET)
+#undef MM_LM_SET
   return e;
 }
 

@@ -693,110 +693,6 @@ __global__ __launch_bounds__(256) void k1_stage_hidden(const float *__restrict__
 
 // ---- many hidden rows (32 or more): the base logits as a tiled MFMA
 // product written to memory, then the same per-slice candidate lists.
-// With b*D rows the vocabulary projection stops being a pure stream of W_lm
-// (128 rows: 128 flop per weight byte, 512 rows: 512), so every workgroup
-// takes a 128-row x 256-token tile and a W_lm tile is read once for all the
-// rows of the tile instead of once per 16-row block.  Operands are staged in
-// an LDS ring of 64-wide k chunks (3 stages: 2 chunks in flight while one is
-// read), with the 16-byte chunk c of row q stored at c ^ (q & 7) so that the
-// fragment reads of 16 rows hit distinct banks; each of the 8 waves computes
-// a 64 x 64 part (4 x 4 MFMA tiles) of the 128 x 256 tile.
-constexpr int LT_BM = 128, LT_BN = 256, LT_BK = 64, LT_THREADS = 512;
-constexpr int LT_WAVES = LT_THREADS / 64;
-constexpr int LT_STAGES = 3;
-constexpr int LT_NI = (LT_BM + LT_BN) * 8 / 64 / LT_WAVES;   // copies per wave per stage
-constexpr int LT_STAGE_CHUNKS = (LT_BM + LT_BN) * 8;  // 16-byte chunks per stage
-constexpr size_t LT_SMEM = (size_t)LT_STAGES * LT_STAGE_CHUNKS * 16;
-
-__global__ __launch_bounds__(LT_THREADS) void k1_logits_tiled(
-    const uint16_t *__restrict__ Hb, int rows, int rows_pad, int d,
-    const uint16_t *__restrict__ W, int V, const float *__restrict__ bias,
-    float *__restrict__ L) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const uint4 *ring = reinterpret_cast<const uint4 *>(smem);
-  const uint32_t ring_lds = lds_addr(smem);
-  const int ntm = (rows + LT_BM - 1) / LT_BM, ntn = (V + LT_BN - 1) / LT_BN;
-  const int total = ntm * ntn;
-  int task = blockIdx.x;
-  // the row tiles of one token tile run one after another on one XCD
-  // (workgroups are handed to the 8 XCDs in turn), sharing its L2 for W_lm
-  if (total % 8 == 0) task = (task & 7) * (total / 8) + (task >> 3);
-  const int m0 = (task % ntm) * LT_BM, n0 = (task / ntm) * LT_BN;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;   // wn: 0, 64, 128, 192
-  // A stage holds 16 copy instructions of hidden rows, then 32 of W_lm rows,
-  // each 64 lanes x 16 bytes straight from global memory into LDS; slot s
-  // (row s >> 3, position s & 7) receives chunk (s & 7) ^ (row & 7) of its
-  // row.  Wave w issues instructions w, w + 8, ..., w + 40.
-  const uint4 *src[LT_NI];
-#pragma unroll
-  for (int i = 0; i < LT_NI; ++i) {
-    const int j = wave + LT_WAVES * i, sl = (j >= 16 ? j - 16 : j) * 64 + lane, row = sl >> 3;
-    const int ch = (sl & 7) ^ (row & 7);
-    const uint16_t *base = j >= 16 ? W + (size_t)min(n0 + row, V - 1) * d
-                                   : Hb + (size_t)min(m0 + row, rows_pad - 1) * d;
-    src[i] = reinterpret_cast<const uint4 *>(base) + ch;
-  }
-  const int nk = d / LT_BK;
-  // chunk kc goes to stage kc % 3; past the last chunk a step re-issues the
-  // last one (read by nobody), so every wait below has the same count
-  auto issue = [&](int kc) {
-    const uint32_t dst = ring_lds + (uint32_t)((kc % LT_STAGES) * LT_STAGE_CHUNKS * 16);
-    const int kk = min(kc, nk - 1);
-#pragma unroll
-    for (int i = 0; i < LT_NI; ++i)
-      lds_copy16(src[i] + kk * 8, dst + (uint32_t)((wave + LT_WAVES * i) * 64 * 16));
-  };
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  issue(0);
-  issue(1);
-  for (int kc = 0; kc < nk; ++kc) {
-    // this wave's copies of chunk kc have landed (those of kc + 1 may still
-    // fly); the barrier makes every wave's copies visible and retires every
-    // read of the stage refilled next (it held chunk kc - 1)
-    wait_vm<LT_NI>();
-    bare_barrier();
-    issue(kc + 2);
-    const uint4 *As = ring + (kc % LT_STAGES) * LT_STAGE_CHUNKS, *Bs = As + LT_BM * 8;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = 4 * ks + g;
-      uint4 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra_ = wm + i * 16 + lr, rb_ = wn + i * 16 + lr;
-        af[i] = As[ra_ * 8 + (ch ^ (ra_ & 7))];
-        bf[i] = Bs[rb_ * 8 + (ch ^ (rb_ & 7))];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[i]), as_bf16x8(bf[j]),
-                                                             acc[i][j], 0, 0, 0);
-    }
-  }
-  wait_vm<0>();   // no copy outlives the workgroup
-  // lane holds D[hidden row 4 g + t][token lr] of tile (i, j)
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int v = n0 + wn + j * 16 + lr;
-    if (v >= V) continue;
-    const float bv = bias ? bias[v] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int row = m0 + wm + i * 16 + 4 * g + t;
-        if (row < rows) L[(size_t)row * V + v] = acc[i][j][t] + bv;
-      }
-  }
-}
-
 // Exact candidate list for M > 64 (logits in LDS, one row per half-wave):
 // the M-th largest key K of the slice is found by bisection, first over the
 // 32 bits of the ordered value (the M-th largest value v), then, where more
@@ -1006,9 +902,6 @@ hipError_t lmhead_prepare(int wtype, int ring, size_t lds_bytes) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
   if (e != hipSuccess || wtype != WT_BF16) return e;
   const void *fn = ring == 2 ? k1_fn<2>() : ring == 1 ? k1_fn<1>() : k1_fn<0>();
-  e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k1_logits_tiled),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)LT_SMEM);
-  if (e != hipSuccess) return e;
   return set_lds_limit(fn, lds_bytes);
 }
 
@@ -1035,13 +928,11 @@ hipError_t launch_lmhead(const LMHeadArgs &a, hipStream_t st, hipEvent_t ev0, hi
 }
 
 bool lmhead_tiled_ok(int rows, int d, int wtype) {
-  return wtype == WT_BF16 && rows >= 32 && d % LT_BK == 0;
+  return wtype == WT_BF16 && rows >= 32 && d % 64 == 0;
 }
 
 hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t st, hipEvent_t ev0,
                                hipEvent_t ev1) {
-  const int rows_pad = (a.rows + 15) & ~15;
-  const int ntm = (a.rows + LT_BM - 1) / LT_BM, ntn = (a.V + LT_BN - 1) / LT_BN;
   // the kernel's own start and end events time the product alone (the list
   // kernel falls into the next stage)
   hipError_t e;
@@ -1050,12 +941,11 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
   if (a.rows <= 128 && mm_ok(g)) {
     // one row tile: 320-token tiles make 1.9 rounds of workgroups over the
     // vocabulary (475 tiles at V = 151936) instead of 2.3 rounds of 256
-    e = launch_mm(g, 128, 320, st, ev0, ev1);
+    e = launch_mm_lm(g, 320, st, ev0, ev1);
+  } else if (mm_ok(g)) {
+    e = launch_mm_lm(g, 256, st, ev0, ev1);
   } else {
-    hipExtLaunchKernelGGL(k1_logits_tiled, dim3(ntm * ntn), dim3(LT_THREADS), (uint32_t)LT_SMEM,
-                          st, ev0, ev1, 0u, (const uint16_t *)a.Hb, a.rows, rows_pad, a.d,
-                          static_cast<const uint16_t *>(a.W), a.V, a.bias, logits);
-    e = hipGetLastError();
+    return hipErrorInvalidValue;   // lmhead_tiled_ok admits bf16 rows with d % 64 == 0 only
   }
   if (e != hipSuccess) return e;
   // (exact lists for M > 64: a kernel of its own, with fewer registers)

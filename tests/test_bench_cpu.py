@@ -52,10 +52,10 @@ def test_dominant_kernel_follows_the_path_each_workload_runs():
     assert k["wide"]["kernel"] == "k1_lmhead_bf16"
     # 128 hidden rows: the tiled product in 128 x 320 tiles, 128 flop per
     # weight byte, HBM-bound
-    assert k["qwen3_8b_x8"]["kernel"] == "k_mm<128, 320>" and k["qwen3_8b_x8"]["bound"] == "hbm"
+    assert k["qwen3_8b_x8"]["kernel"] == "k_mm_lm<128, 320>" and k["qwen3_8b_x8"]["bound"] == "hbm"
     # 512 hidden rows: 128 x 256 tiles, past the ridge of the published
     # peaks, MFMA-bound
-    assert k["stress_b0"]["kernel"] == "k1_logits_tiled"
+    assert k["stress_b0"]["kernel"] == "k_mm_lm<128, 256>"
     assert k["stress_b0"]["bound"] == "mfma" and k["stress_b0"]["unit"] == "TFLOP/s"
     c = synth.CONFIGS["stress_b0"]
     assert k["stress_b0"]["work"] == 2 * c.batch * c.D * c.d * c.V
