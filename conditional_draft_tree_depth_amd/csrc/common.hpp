@@ -88,6 +88,37 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   v += xchg_f32<16>(v);
   return v + xchg_f32<32>(v);
 }
+// The same maximum and sum with the exchanges across rows and across halves
+// done by the lane-pair swaps (vector ALU only, no LDS round trip); every
+// lane of the wave must be active.  Each swap leaves a lane its own value
+// and its partner's, one in each slot, and the operations are symmetric, so
+// the results are those of wave_max_f32 / wave_sum_f32 bit for bit.
+__device__ __forceinline__ float pair_max_f32(float v, bool x32) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = x32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum_f32(float v, bool x32) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = x32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_max_f32_full(float v) {
+  v = fmaxf(v, xchg_f32<1>(v));
+  v = fmaxf(v, xchg_f32<2>(v));
+  v = fmaxf(v, xchg_f32<4>(v));
+  v = fmaxf(v, xchg_f32<8>(v));
+  return pair_max_f32(pair_max_f32(v, false), true);
+}
+__device__ __forceinline__ float wave_sum_f32_full(float v) {
+  v += xchg_f32<1>(v);
+  v += xchg_f32<2>(v);
+  v += xchg_f32<4>(v);
+  v += xchg_f32<8>(v);
+  return pair_sum_f32(pair_sum_f32(v, false), true);
+}
 // max over aligned groups of WIDTH lanes (a power of two <= 64)
 template <int WIDTH>
 __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {

@@ -31,6 +31,10 @@ struct Ws {
   // per depth: [u | W_hh S + b_hh] of every expanded branch, [b * W, r + 3s]
   float *uh = nullptr;
   float *ell = nullptr, *gi = nullptr;
+  uint64_t *ckey = nullptr;   // per depth: children's selection keys [b * W * K]
+  int32_t *ccand = nullptr;   //   and candidate indices
+  uint32_t *selflag = nullptr; // [b, 64] arrival flags of the batched selection
+  float *sscore[2] = {nullptr, nullptr};   // survivors' scores (batched selection)
   void *wcat = nullptr;      // [W1[:, d:] ; W_hh], [r + 3s, s] in the weight dtype
   int32_t *n_tok = nullptr, *n_par = nullptr, *n_dep = nullptr;
   float *n_score = nullptr;
@@ -87,6 +91,7 @@ struct dtree_ctx {
   // epoch of the next round (flags only ever grow, so they need no reset)
   bool pk = false;
   bool sel_corr = false;   // correction logits computed inside the selection kernel
+  bool sel_batch = false;  // selection over many workgroups (correction logits inside)
   int scoring = DTREE_SCORE_CONDITIONAL;
   int builder = DTREE_BUILD_DEPTHWISE;
   uint32_t tok_epoch = 0;   // distinct-token tables: grows by one per round that uses them
@@ -150,9 +155,9 @@ hipError_t alloc(T **p, size_t n) {
 }
 
 void free_ws(Ws &ws) {
-  void *ptrs[] = {ws.part, ws.hb, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.uh, ws.ell, ws.gi, ws.wcat,
-                  ws.n_tok, ws.n_par, ws.n_dep, ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1],
-                  ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
+  void *ptrs[] = {ws.part, ws.hb, ws.C, ws.Cl, ws.uH, ws.S[0], ws.S[1], ws.uh, ws.ell, ws.ckey,
+                  ws.ccand, ws.selflag, ws.sscore[0], ws.sscore[1], ws.gi, ws.wcat, ws.n_tok, ws.n_par, ws.n_dep,
+                  ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1], ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
                   ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags,
                   ws.logits, ws.S3[0], ws.S3[1], ws.gi_all, ws.gidx_cand, ws.first_row,
                   ws.cidx_tmp, ws.uniq, ws.rowmap, ws.ucount, ws.lpos, ws.btot,
@@ -262,6 +267,10 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   if (w->wtype == DTREE_BF16 && s % 64 == 0 && bw >= 256)
     for (int i = 0; i < 2; ++i) A(alloc(&ws.S3[i], bw * STATE_PLANES * s));
   A(alloc(&ws.ell, bw * c.max_M));
+  A(alloc(&ws.ckey, bw * c.max_K));
+  A(alloc(&ws.ccand, bw * c.max_K));
+  A(alloc(&ws.selflag, (size_t)c.max_batch * 64));
+  for (int i = 0; i < 2; ++i) A(alloc(&ws.sscore[i], bw));
   A(alloc(&ws.gi, bw * 3 * s));
   const size_t esz_w = w->wtype == DTREE_BF16 ? 2 : 4;
   A(alloc(reinterpret_cast<uint8_t **>(&ws.wcat), (size_t)(r + 3 * s) * s * esz_w));
@@ -337,6 +346,10 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
                   reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
                   select_corr_smem(c.max_M, r) + 45056 <= ctx->lds_max;
   if (pe == hipSuccess && ctx->sel_corr) pe = select_corr_prepare(ctx->lds_max);
+  ctx->sel_batch = w->wtype == DTREE_BF16 && r % 8 == 0 && r <= 512 &&
+                   reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
+                   branch_select_smem(r) + 32768 <= ctx->lds_max;
+  if (pe == hipSuccess && ctx->sel_batch) pe = branch_select_prepare(ctx->lds_max);
   if (pe == hipSuccess && ctx->pk) pe = persist_prepare(s);
   if (pe != hipSuccess) {
     free_ws(ws);
@@ -412,10 +425,11 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
   tb.n_tok = ws.n_tok; tb.n_par = ws.n_par; tb.n_dep = ws.n_dep;
   tb.n_score = ws.n_score; tb.n_lex = ws.n_lex;
   tb.surv_hist = ws.surv_hist; tb.gidx_tok = ws.gidx_tok; tb.gidx_par = ws.gidx_par;
-  tb.sel = ws.sel; tb.status = ws.status;
+  tb.sel = ws.sel; tb.status = ws.status; tb.selflag = ws.selflag;
   int cur = 0;
   tb.surv_node = ws.surv[0]; tb.surv_rank = ws.rank[0];
   tb.nsurv_node = ws.surv[1]; tb.nsurv_rank = ws.rank[1];
+  tb.surv_score = ws.sscore[0]; tb.nsurv_score = ws.sscore[1];
 
   // K1 + K1b: candidate tables
   prof_mark(ctx, 0, st);
@@ -602,7 +616,10 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
       }
       // (with many branches x candidates per request the separate correction
       // kernel spreads that work over more workgroups)
-      if (ctx->sel_corr && A * M <= 2048) {
+      if (ctx->sel_batch) {
+        HIPCHK(ctx, launch_branch_select(batch, A, M, K, W, D, dd, off, r, w.W2, ws.C, ws.Cl,
+                                         ws.uh, ldu, tb, ws.ckey, ws.ccand, st));
+      } else if (ctx->sel_corr && A * M <= 2048) {
         HIPCHK(ctx, launch_select_corr(batch, A, M, K, W, D, dd, off, r, w.W2, ws.C, ws.Cl, ws.uh,
                                        ldu, tb, st));
       } else {
@@ -629,6 +646,7 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
       cur = 1 - cur;
       tb.surv_node = ws.surv[cur]; tb.surv_rank = ws.rank[cur];
       tb.nsurv_node = ws.surv[1 - cur]; tb.nsurv_rank = ws.rank[1 - cur];
+      tb.surv_score = ws.sscore[cur]; tb.nsurv_score = ws.sscore[1 - cur];
       off += A * K;
       A = An;
     }
@@ -893,6 +911,10 @@ static size_t static_layout(const dtree_weights &w, const dtree_params &p, int b
   take(&ws.S[1], bw * s);
   take(&ws.uh, bw * (r + 3 * s));
   take(&ws.ell, bw * p.M);
+  take(&ws.ckey, bw * p.K);
+  take(&ws.ccand, bw * p.K);
+  take(&ws.selflag, (size_t)batch * 64);
+  for (int i = 0; i < 2; ++i) take(&ws.sscore[i], bw);
   take(&ws.gi, bw * 3 * s);
   const size_t nt = (size_t)batch * NT;
   take(&ws.n_tok, nt);
@@ -981,6 +1003,7 @@ extern "C" dtree_status dtree_build_round_static(const dtree_weights *w, const d
         if (pe == hipSuccess) pe = topb_prepare(sd.lds_max);
         if (pe == hipSuccess) pe = gemm_prepare();
         if (pe == hipSuccess) pe = select_corr_prepare(sd.lds_max);
+        if (pe == hipSuccess) pe = branch_select_prepare(sd.lds_max);
         if (pe != hipSuccess) {
           char m[128];
           std::snprintf(m, sizeof m, "kernel attributes: %s", hipGetErrorString(pe));
@@ -1018,6 +1041,9 @@ extern "C" dtree_status dtree_build_round_static(const dtree_weights *w, const d
   ctx.sel_corr = w->wtype == DTREE_BF16 && w->r % 8 == 0 && w->r <= 512 &&
                  reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
                  select_corr_smem(M, w->r) + 45056 <= sd.lds_max;
+  ctx.sel_batch = w->wtype == DTREE_BF16 && w->r % 8 == 0 && w->r <= 512 &&
+                  reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
+                  branch_select_smem(w->r) + 32768 <= sd.lds_max;
   ctx.err_buf = g_static_err;
   ctx.err_cap = sizeof g_static_err;
   return enqueue_round(&ctx, p, batch, H, root, tok, parent, depth, score, mask, n_nodes,

@@ -529,6 +529,366 @@ hipError_t launch_select_corr(int b, int A, int M, int K, int W, int D, int delt
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- batched selection
+// The selection of one depth spread over many workgroups (bf16 W2 with
+// 16-byte rows, r a multiple of 8 up to 512, M <= 128):
+//  k_branch_topk, one workgroup per (request, BS_BR expanded branches), one
+//    wave per branch: the branches' correction logits on the matrix cores,
+//    log-softmax over the M candidates and the Top-K children, appended to
+//    the superarbol, each child's (score, token path) key written out;
+//  then the last of a request's workgroups to finish takes the Top-W
+//    survivors among those keys (no second launch: a launch costs several
+//    microseconds here, more than the arrival count and the reload).
+// Same arithmetic, keys and tie-breaks as k_select / k_select_corr
+// ("Resumen Técnico: DominoTree", Componentes Principales 2; DARTree page,
+// Metodología 1).
+constexpr int BS_BR = 16;
+constexpr int SEL_FLAGS = 64;   // arrival flags per request (at least SEL_MAXW / BS_BR)
+
+// Ranks of the K best of a wave's candidates, by log-prob descending and
+// token ascending (the order of make_key(lp, token)); lane l holds
+// candidates l (v0, t0) and l + 64 (v1, t1), absent ones as -inf.  K rounds:
+// the wave-wide maximum of the lanes' best remaining log-probs, the lanes
+// holding it, and among several such lanes the smallest token (tokens of a
+// depth's candidates are distinct).  r0 / r1 = K when not among the K best.
+__device__ __forceinline__ void wave_topk(float v0, uint32_t t0, float v1, uint32_t t1, int K,
+                                          int &r0, int &r1) {
+  const int lane = threadIdx.x & 63;
+  int a0 = K, a1 = K;
+  for (int rk = 0; rk < K; ++rk) {
+    const bool s1 = v1 > v0 || (v1 == v0 && t1 < t0);
+    const float bv = s1 ? v1 : v0;
+    const uint32_t bt = s1 ? t1 : t0;
+    const float m = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__float_as_uint(wave_max_f32_full(bv))));
+    if (m == -INFINITY) break;
+    uint64_t at = __ballot(bv == m);
+    if (__popcll(at) > 1) {   // equal log-probs: the smallest token first
+      uint32_t tt = bv == m ? bt : 0xFFFFFFFFu;
+      tt = min(tt, xchg_u32<1>(tt));
+      tt = min(tt, xchg_u32<2>(tt));
+      tt = min(tt, xchg_u32<4>(tt));
+      tt = min(tt, xchg_u32<8>(tt));
+      tt = min(tt, xchg_u32<16>(tt));
+      tt = min(tt, xchg_u32<32>(tt));
+      at = __ballot(bv == m && bt == tt);
+    }
+    const bool win = lane == (int)__builtin_ctzll(at);
+    a0 = win && !s1 ? rk : a0;
+    a1 = win && s1 ? rk : a1;
+    v0 = win && !s1 ? -INFINITY : v0;
+    v1 = win && s1 ? -INFINITY : v1;
+  }
+  r0 = a0;
+  r1 = a1;
+}
+
+// Top-W of one request's Z = A K children by (score desc, token path asc),
+// by the NT threads of one workgroup.  The An-th largest key is at least tau, the An-th largest among
+// the first m = ceil(An / A) children of every branch (A m >= An keys), so
+// only the keys >= tau are ranked: with full-width depths tau is the weakest
+// of the branches' best children.
+struct TopwLds {
+  uint64_t key[SEL_MAXZ];   // the request's children's keys
+  uint64_t pk[SEL_MAXZ];
+  int16_t cc[SEL_MAXZ];     // their candidate indices
+  int16_t pc[SEL_MAXZ];
+  uint32_t slex[SEL_MAXW];  // survivors by slot: token path
+  int16_t sc[SEL_MAXW];     //   and child index
+  uint64_t tau;
+  int np;
+};
+// (the caller has put the Z keys and candidate indices into L.key / L.cc
+// and cleared L.tau and L.np, all before a barrier)
+template <int NT>
+__device__ void topw_request(int q, int A, int K, int W, int D, int delta, int off, int M,
+                             const TreeBufs &t, TopwLds &L) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int Z = A * K, An = Z < W ? Z : W;
+  if (An < Z) {
+    const int m = (An + A - 1) / A, ns = A * m;
+    for (int i = tid; i < ns; i += NT) L.pk[i] = L.key[(i / m) * K + i % m];
+    __syncthreads();
+    const int tpn = split_width(ns, NT), part = tid & (tpn - 1);
+    for (int b0 = 0; b0 < ns; b0 += NT / tpn) {
+      const int i = b0 + tid / tpn;
+      const uint64_t kc = i < ns ? L.pk[i] : 0ull;
+      int cnt = i < ns ? count_split<true>(L.pk, ns, kc, part, tpn) : 0;
+      cnt = sum_adjacent(cnt, tpn);
+      if (i < ns && part == 0 && cnt == An - 1) L.tau = kc;   // keys are distinct: one thread
+    }
+    __syncthreads();
+  }
+  const uint64_t tau = L.tau;
+  for (int c0 = 0; c0 < Z; c0 += NT) {
+    const int c = c0 + tid;
+    const bool keep = c < Z && L.key[c] >= tau;
+    const uint64_t bal = __ballot(keep);
+    int base = 0;
+    if (lane == 0 && bal) base = atomicAdd(&L.np, __popcll(bal));
+    base = __shfl(base, 0);
+    if (keep) {
+      const int at = base + __popcll(bal & ((1ull << lane) - 1ull));
+      L.pk[at] = L.key[c];
+      L.pc[at] = (int16_t)c;
+    }
+  }
+  __syncthreads();
+  const int np = L.np;
+  const int tpn = split_width(np, NT), part = tid & (tpn - 1);
+  for (int b0 = 0; b0 < np; b0 += NT / tpn) {
+    const int i = b0 + tid / tpn;
+    const uint64_t ki = i < np ? L.pk[i] : 0ull;
+    int rank = i < np ? count_split<true>(L.pk, np, ki, part, tpn) : 0;
+    rank = sum_adjacent(rank, tpn);
+    if (i < np && part == 0 && rank < An) {
+      L.slex[rank] = key_tie(ki);
+      L.sc[rank] = L.pc[i];
+    }
+  }
+  __syncthreads();
+  // the survivors in slot order, in coalesced stores
+  for (int i = tid; i < An; i += NT) {
+    const int c = L.sc[i];
+    const uint64_t ki = L.key[c];
+    const uint32_t li = L.slex[i];
+    const size_t sl = (size_t)q * t.Wmax + i;
+    t.nsurv_node[sl] = off + c;
+    t.nsurv_score[sl] = key_val(ki);
+    t.gidx_tok[(size_t)q * An + i] = (int32_t)(li & 0x3FFFFu);
+    t.gidx_par[(size_t)q * An + i] = q * A + c / K;
+    if (t.gidx_cand) t.gidx_cand[(size_t)q * An + i] = (q * D + delta) * M + L.cc[c];
+    t.surv_hist[((size_t)q * (D + 1) + delta + 1) * t.Wmax + i] = off + c;
+    t.nsurv_rank[sl] = An - 1 - count_greater<uint32_t>(L.slex, An, li);   // lex keys are distinct
+  }
+}
+
+__global__ __launch_bounds__(64 * BS_BR) void k_branch_topk(
+    int A, int M, int K, int W, int D, int delta, int off, int r, int uvec,
+    const uint16_t *__restrict__ W2, const int32_t *__restrict__ C, const float *__restrict__ Cl,
+    const float *__restrict__ u, int ldu, TreeBufs t, uint64_t *__restrict__ ckey,
+    int32_t *__restrict__ ccand) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ float ell_s[BS_BR][128];
+  __shared__ int32_t ctok[128];
+  __shared__ float clv[128];
+  __shared__ int32_t pnode[BS_BR];
+  __shared__ uint32_t prank[BS_BR];
+  __shared__ float pscore[BS_BR];
+  __shared__ __align__(16) TopwLds tw;
+  __shared__ bool last_s;
+  // u's three bf16 terms as B-fragment rows: row tq BS_BR + b for branch b,
+  // row 3 BS_BR all zeros (the unused branch columns); rows zero-padded to
+  // whole chunks of four k steps, so the fragment reads need no masks
+  const int nch = (r + 127) >> 7;   // chunks of four k steps of 32
+  const int rp = nch * 128 + 8;     // row pitch (+8: rows start 16 bytes apart in the banks)
+  uint16_t *us = reinterpret_cast<uint16_t *>(smem);   // [3 BS_BR + 1][rp]
+  const int q = blockIdx.x, a0 = blockIdx.y * BS_BR, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, g = lane >> 4;
+  const size_t cb = ((size_t)q * D + delta) * M;
+  const size_t nb = (size_t)q * t.NT;
+  const int Z = A * K;
+  const int r8 = r >> 3;
+  // this wave's 16 candidates: token, then its W2 row as A fragments (the
+  // token load goes first, so waiting for it leaves the others in flight)
+  const int jt = wave;
+  const bool tile = jt * 16 < M;
+  const int jw = min(jt * 16 + lr, M - 1);
+  const int tokw = max(C[cb + jw], 0);   // an empty slot never reaches here
+  // u of the workgroup's branches, 8 values per thread (BS_BR r / 8 <= 1024
+  // threads), coalesced
+  const int ub = tid / r8, uc = tid - ub * r8;
+  const bool uin = ub < BS_BR && a0 + ub < A;
+  float x[8];
+  {
+    const float *up = u + ((size_t)q * A + (uin ? a0 + ub : a0)) * ldu + (uin ? 8 * uc : 0);
+    if (uvec) {
+      const float4 v0 = reinterpret_cast<const float4 *>(up)[0];
+      const float4 v1 = reinterpret_cast<const float4 *>(up)[1];
+      x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+      x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = up[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = uin ? x[e] : 0.f;
+  }
+  for (int j = tid; j < M; j += blockDim.x) {
+    ctok[j] = C[cb + j];
+    clv[j] = Cl[cb + j];
+  }
+  if (tid < BS_BR && a0 + tid < A) {
+    pnode[tid] = t.surv_node[(size_t)q * t.Wmax + a0 + tid];
+    prank[tid] = (uint32_t)t.surv_rank[(size_t)q * t.Wmax + a0 + tid];
+    pscore[tid] = t.surv_score[(size_t)q * t.Wmax + a0 + tid];
+  }
+  // W2 fragments of every k step (past the row's end: its last piece again,
+  // finite bf16 weights that meet zero B rows)
+  uint4 wa[16];
+  {
+    const uint16_t *wr = W2 + (size_t)tokw * r;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+      if (ch < nch) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          wa[4 * ch + i] = *reinterpret_cast<const uint4 *>(wr + min(128 * ch + 32 * i + 8 * g, r - 8));
+      }
+  }
+  if (ub < BS_BR) {
+    uint4 t3[3];
+    split3_bf16(x, t3);   // exact: W2 is bf16, so every MFMA product below is exact in fp32
+#pragma unroll
+    for (int tq = 0; tq < 3; ++tq)
+      *reinterpret_cast<uint4 *>(us + ((size_t)tq * BS_BR + ub) * rp + 8 * uc) = t3[tq];
+  }
+  {
+    const int padc = (rp - r) >> 3;   // zero 8-element pieces past r in each of the 3 BS_BR rows
+    for (int i = tid; i < 3 * BS_BR * padc + rp / 8; i += blockDim.x) {
+      const int row = i < 3 * BS_BR * padc ? i / padc : 3 * BS_BR;
+      const int col = i < 3 * BS_BR * padc ? r + 8 * (i - row * padc) : 8 * (i - 3 * BS_BR * padc);
+      *reinterpret_cast<uint4 *>(us + (size_t)row * rp + col) = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __syncthreads();
+  // one 16 x 16 tile (candidates x branch columns, BS_BR of them used) per
+  // wave: ell_s[branch][j] = Cl[j] + W2[C[j]] . u_branch, k steps in order,
+  // the B fragments of four steps read at a time
+  if (tile) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t *brow[3];
+#pragma unroll
+    for (int tq = 0; tq < 3; ++tq)
+      brow[tq] = us + (size_t)(lr < BS_BR ? tq * BS_BR + lr : 3 * BS_BR) * rp + 8 * g;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+      if (ch < nch) {
+        uint4 bq[4][3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int tq = 0; tq < 3; ++tq)
+            bq[i][tq] = *reinterpret_cast<const uint4 *>(brow[tq] + 128 * ch + 32 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int tq = 0; tq < 3; ++tq) acc = cl_mfma(wa[4 * ch + i], bq[i][tq], acc);
+      }
+    // lane holds D[candidate 4 g + tt][branch column lr]
+    if (lr < BS_BR) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int jj = jt * 16 + 4 * g + tt;
+        if (jj < M) ell_s[lr][jj] = clv[jj] + acc[tt];
+      }
+    }
+  }
+  __syncthreads();
+  const int a = a0 + wave;
+  if (a < A) {
+    const bool h0 = lane < M, h1 = lane + 64 < M;
+    const float l0 = h0 ? ell_s[wave][lane] : -INFINITY;
+    const float l1 = h1 ? ell_s[wave][lane + 64] : -INFINITY;
+    const uint32_t pr = prank[wave];
+    const float ps = pscore[wave];
+    const float m = wave_max_f32_full(fmaxf(l0, l1));
+    const float e = (h0 ? expf(l0 - m) : 0.f) + (h1 ? expf(l1 - m) : 0.f);
+    const float lse = m + logf(wave_sum_f32_full(e));
+    const float lp0 = h0 ? l0 - lse : -INFINITY, lp1 = h1 ? l1 - lse : -INFINITY;
+    const uint32_t tk0 = h0 ? (uint32_t)ctok[lane] : 0u, tk1 = h1 ? (uint32_t)ctok[lane + 64] : 0u;
+    int r0, r1;
+    wave_topk(lp0, tk0, lp1, tk1, K, r0, r1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rk = h ? r1 : r0;
+      if (rk < K) {
+        const uint32_t tok = h ? tk1 : tk0;
+        const float sc = __fadd_rn(ps, h ? lp1 : lp0);
+        const uint32_t lex = (pr << 18) | tok;
+        const int c = a * K + rk;
+        tw.key[c] = make_key(sc, lex);
+        tw.cc[c] = (int16_t)(lane + 64 * h);
+      }
+    }
+  }
+  if (tid == 0) { tw.tau = 0ull; tw.np = 0; }
+  __syncthreads();
+  // the workgroup's children are nodes off + [c0, c1): their records in
+  // coalesced stores
+  const int c0 = a0 * K, c1 = min(A, a0 + BS_BR) * K;
+  for (int c = c0 + tid; c < c1; c += blockDim.x) {
+    const uint64_t kc = tw.key[c];
+    const uint32_t lex = key_tie(kc);
+    const size_t id = nb + off + c;
+    t.n_tok[id] = (int32_t)(lex & 0x3FFFFu);
+    t.n_par[id] = pnode[c / K - a0];
+    t.n_dep[id] = delta + 1;
+    t.n_score[id] = key_val(kc);
+    t.n_lex[id] = lex;
+  }
+  // Hand-off to the request's last workgroup (several workgroups): wave 0
+  // publishes the workgroup's children keys with device-coherent stores,
+  // waits until they have completed, raises the workgroup's flag (the depth
+  // number plus one; the round start clears the flags) and reads all of the
+  // request's flags.  The workgroup whose flag landed last sees them all
+  // raised and loads the other workgroups' keys; one that raced it may see
+  // them all too and then ranks the same complete keys into the same
+  // outputs.  No workgroup waits for another.
+  if (gridDim.y > 1) {
+    uint32_t *fl = t.selflag + (size_t)q * SEL_FLAGS;
+    const uint32_t ep = (uint32_t)delta + 1u;
+    if (wave == 0) {
+      for (int c = c0 + lane; c < c1; c += 64) {
+        __hip_atomic_store(ckey + (size_t)q * Z + c, tw.key[c], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ccand + (size_t)q * Z + c, (int32_t)tw.cc[c], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      if (lane == 0) {
+        __hip_atomic_store(fl + blockIdx.y, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      const bool up = lane >= (int)gridDim.y ||
+                      __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ep;
+      const bool all = __all(up);
+      if (lane == 0) last_s = all;
+    }
+    __syncthreads();
+    if (!last_s) return;
+    for (int c = tid; c < Z; c += blockDim.x)
+      if (c < c0 || c >= c1) {
+        tw.key[c] = __hip_atomic_load(ckey + (size_t)q * Z + c, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        tw.cc[c] = (int16_t)__hip_atomic_load(ccand + (size_t)q * Z + c, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      }
+    __syncthreads();
+  }
+  topw_request<64 * BS_BR>(q, A, K, W, D, delta, off, M, t, tw);
+}
+
+hipError_t branch_select_prepare(size_t lds_bytes) {
+  return set_lds_limit(reinterpret_cast<const void *>(&k_branch_topk), lds_bytes);
+}
+
+size_t branch_select_smem(int r) { return (size_t)(3 * BS_BR + 1) * (((r + 127) >> 7) * 128 + 8) * 2; }
+
+hipError_t launch_branch_select(int b, int A, int M, int K, int W, int D, int delta, int off,
+                                int r, const void *W2, const int32_t *C, const float *Cl,
+                                const float *u, int ldu, const TreeBufs &t, uint64_t *ckey,
+                                int32_t *ccand, hipStream_t st) {
+  if (r % 8 || r > 512 || M > 128 || A * K > SEL_MAXZ || W > SEL_MAXW ||
+      reinterpret_cast<uintptr_t>(W2) % 16)
+    return hipErrorInvalidValue;
+  const int uvec = ldu % 4 == 0 && reinterpret_cast<uintptr_t>(u) % 16 == 0;
+  hipLaunchKernelGGL(k_branch_topk, dim3(b, (A + BS_BR - 1) / BS_BR), dim3(64 * BS_BR),
+                     branch_select_smem(r), st, A, M, K, W, D, delta, off, r, uvec,
+                     static_cast<const uint16_t *>(W2), C, Cl, u, ldu, t, ckey, ccand);
+  return hipGetLastError();
+}
+
 // The whole depth loop under marginal scoring, one workgroup per request:
 // with no correction every branch of a depth sees the same M log-probs (the
 // log-softmax of the depth's base logits), so the depth's ranks are found

@@ -27,12 +27,14 @@ struct TreeBufs {
   uint32_t *n_lex;                  // [b, NT] (parent lexrank << 18) | token
   int32_t *surv_node, *surv_rank;   // [b, Wmax] current expanded nodes
   int32_t *nsurv_node, *nsurv_rank; // [b, Wmax] next depth
+  float *surv_score, *nsurv_score;  // [b, Wmax] their scores (batched selection only, or null)
   int32_t *surv_hist;               // [b, D+1, Wmax]
   int32_t *gidx_tok, *gidx_par;     // [b * Wmax] gathers for the GRU step
   int32_t *gidx_cand;               // [b * Wmax] survivor's candidate row (q D + depth) M + j,
                                     // written when not null
   int32_t *sel;                     // [b, Bmax]
   uint32_t *status;                 // device status bits
+  uint32_t *selflag;                // [b, 64] arrival flags of the batched selection (or null)
 };
 
 // Start of a round for request q (called by one workgroup per request before
@@ -42,6 +44,8 @@ __device__ inline void init_round_request(int q, const int32_t *root, const Tree
                                           int tid, int nt) {
   for (int i = tid; i < Dp1 * t.Wmax; i += nt)
     t.surv_hist[(size_t)q * Dp1 * t.Wmax + i] = i == 0 ? 0 : -1;
+  if (t.selflag)
+    for (int i = tid; i < 64; i += nt) t.selflag[(size_t)q * 64 + i] = 0u;
   if (tid == 0) {
     const size_t n0 = (size_t)q * t.NT;
     const int32_t rt = root[q] < 0 ? 0 : (root[q] >= t.V ? t.V - 1 : root[q]);
@@ -52,6 +56,7 @@ __device__ inline void init_round_request(int q, const int32_t *root, const Tree
     t.n_lex[n0] = 0u;
     t.surv_node[(size_t)q * t.Wmax] = 0;
     t.surv_rank[(size_t)q * t.Wmax] = 0;
+    if (t.surv_score) t.surv_score[(size_t)q * t.Wmax] = 0.f;
     t.gidx_tok[q] = rt;
     if (q == 0) *t.status = 0u;
   }
@@ -181,6 +186,16 @@ hipError_t launch_select_marginal(int b, int M, int K, int W, int D, const int32
 hipError_t launch_select(int b, int A, int M, int K, int W, int D, int delta,
                          int off, const int32_t *C, const float *ell, long ldq, int lda,
                          const TreeBufs &t, hipStream_t st);
+// selection spread over many workgroups (bf16 W2, 16-byte aligned, r % 8 ==
+// 0, r <= 512, M <= 128): correction logits and Top-K per branch, then Top-W
+// per request; ckey / ccand hold b * A * K child keys and candidate indices,
+// t.selflag b * 64 arrival flags (cleared at the round start)
+size_t branch_select_smem(int r);   // dynamic LDS (beside about 30 KB of static LDS)
+hipError_t branch_select_prepare(size_t lds_bytes);
+hipError_t launch_branch_select(int b, int A, int M, int K, int W, int D, int delta, int off,
+                                int r, const void *W2, const int32_t *C, const float *Cl,
+                                const float *u, int ldu, const TreeBufs &t, uint64_t *ckey,
+                                int32_t *ccand, hipStream_t st);
 // selection with the correction logits computed in place (bf16 W2, 16-byte
 // aligned, r % 8 == 0; dynamic LDS select_corr_smem(M, r))
 size_t select_corr_smem(int M, int r);

@@ -82,6 +82,12 @@ def test_random_small_shapes(gpu_lib, seed):
     (9, 128, 128, 128, 40, 4, 64, 4, 64, 120, 2),
     # rank 8 (one partial k step), 96 candidates
     (10, 128, 64, 64, 8, 4, 96, 4, 32, 100, 2),
+    # batched selection: odd state size (u rows not 16-byte aligned: scalar
+    # loads), rank 24 (one partial k step), 12 survivors from 5 branches
+    # (the Top-W bound over the first 3 children of every branch), ragged M
+    (11, 128, 64, 61, 24, 5, 33, 5, 12, 60, 3),
+    # rank 512 (16 k steps), 128 candidates, 64 survivors of 512 children
+    (12, 128, 128, 128, 512, 4, 128, 8, 64, 200, 2),
 ])
 def test_mfma_product_paths(gpu_lib, seed, d, e, s, r, D, M, K, W, B, batch):
     """bf16 shapes whose products run on the MFMA kernels: the row-gathered
