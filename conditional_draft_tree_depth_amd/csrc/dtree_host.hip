@@ -452,7 +452,18 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
     for (int i = 0; i < 2; ++i) k1ev[i] = ctx->prof_ev[ctx->prof_n * (DTREE_NSTAGES + 1) + 1 + i];
   if (tiled) HIPCHK(ctx, launch_lmhead_tiled(la, ws.logits, st, k1ev[0], k1ev[1]));
   else HIPCHK(ctx, launch_lmhead(la, st, k1ev[0], k1ev[1]));
-  HIPCHK(ctx, launch_topm_merge(ws.part, ctx->P, M, rows, ws.C, ws.Cl, st));
+  // the persistent depth loop's correction tables come with the merge when
+  // the fused kernel fits (decided here, used below)
+  const bool marginal = ctx->scoring == DTREE_SCORE_MARGINAL;
+  const bool pk = !marginal && ctx->builder != DTREE_BUILD_HEAP && ctx->pk && batch * M <= 64 &&
+                  batch * D * M <= ctx->pk_rows &&
+                  persist_eligible(batch, D, M, K, W, s, w.e, r, wt, ctx->lds_max);
+  const bool pk_fused = pk && fuse_uH && topm_tables_ok(M, r, s, w.W2, ws.w1t);
+  if (pk_fused)
+    HIPCHK(ctx, launch_topm_tables(ws.part, ctx->P, M, rows, r, s, w.W2, ws.w1t, ws.uH, ws.C,
+                                   ws.Cl, ws.G, ws.g, st));
+  else
+    HIPCHK(ctx, launch_topm_merge(ws.part, ctx->P, M, rows, ws.C, ws.Cl, st));
   prof_mark(ctx, 3, st);
   // K2: uH = W1[:, :d] . Hq for every (request, depth), when not fused above
   GemmArgs g{};
@@ -467,7 +478,6 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
   }
 
 
-  const bool marginal = ctx->scoring == DTREE_SCORE_MARGINAL;
   // Markov scoring: each survivor's GRU step starts from a zero state, so
   // the W_hh product of the branches is not needed
   const bool markov = ctx->scoring == DTREE_SCORE_MARKOV;
@@ -516,8 +526,6 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
     return DTREE_OK;
   }
   ctx->last_heap = false;
-  const bool pk = !marginal && ctx->pk && batch * M <= 64 && batch * D * M <= ctx->pk_rows &&
-                  persist_eligible(batch, D, M, K, W, s, w.e, r, wt, ctx->lds_max);
   int A = 1, off = 1, sc = 0;
   if (marginal) {
     // every branch of a depth is scored by the depth's base logits Cl
@@ -531,8 +539,9 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
   } else if (pk) {
     // correction tables G = W2[C] W1[:, d:], g = Cl + W2[C] uH, then the
     // whole depth loop as one cooperative launch
-    HIPCHK(ctx, launch_corr_tables(batch * D * M, M, r, s, w.W2, ws.w1t, ws.C, ws.Cl, ws.uH,
-                                   ws.G, ws.g, st));
+    if (!pk_fused)
+      HIPCHK(ctx, launch_corr_tables(batch * D * M, M, r, s, w.W2, ws.w1t, ws.C, ws.Cl, ws.uH,
+                                     ws.G, ws.g, st));
     prof_mark(ctx, 4, st);
     PersistArgs pa{batch, D, M, K, W, s, w.e, w.V, w.W_ih, w.W_hh, w.Emb, w.b_ih, w.b_hh,
                    ws.C, root, ws.G, ws.g, ws.pk_terms, ws.pk_terms + persist_terms_floats(s),

@@ -524,10 +524,15 @@ size_t topm_merge_smem(int P) {
   return (size_t)K1B_FAST * 8 + (size_t)P * 8 + (size_t)P * 4 * 2;
 }
 
-__global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
-    const uint64_t *__restrict__ part, int P, int M, int32_t *__restrict__ C,
-    float *__restrict__ Cl) {
-  extern __shared__ __align__(16) uint8_t smem[];
+// The merge of one row by a workgroup of K1B_THREADS threads (dynamic LDS
+// laid out as topm_merge_smem(P) says).  Once the keys to be ranked are
+// gathered, every thread calls gathered(keys, n) (n of them, in LDS, in no
+// particular order); then out(rank, key, i) is called once for every rank <
+// M, i being the key's position among the gathered ones (key 0 and i = -1
+// for the ranks past the listed keys).
+template <class Gathered, class Out>
+__device__ void topm_merge_row(const uint64_t *__restrict__ part, int P, int M, int row,
+                               uint8_t *smem, Gathered gathered, Out out) {
   __shared__ uint64_t red[K1B_THREADS / 64];
   __shared__ int redi[K1B_THREADS / 64];
   __shared__ int ncand, nlive;
@@ -535,7 +540,7 @@ __global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
   uint64_t *heads = cand + K1B_FAST;                                   // [P]
   int *cnt = reinterpret_cast<int *>(heads + P);                       // [P]
   int *live = cnt + P;                                                 // [P]
-  const int row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x, nt = K1B_THREADS;
   const int lane = tid & 63, wave = tid >> 6, nwv = nt >> 6;
   const uint64_t *base = part + (size_t)row * P * K1_LSTRIDE;
   auto block_max = [&](uint64_t v) -> uint64_t {
@@ -650,6 +655,7 @@ __global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
     gather(lo);
     n = min(ncand, K1B_FAST);
   }
+  gathered(cand, n);
   // rank of each gathered key among them (keys are distinct)
   const int tpn = split_width(n, nt), sub = tid & (tpn - 1);
   for (int b0 = 0; b0 < n; b0 += nt / tpn) {
@@ -657,15 +663,162 @@ __global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
     const uint64_t k = i < n ? cand[i] : 0ull;
     int rk = i < n ? count_split<true>(cand, n, k, sub, tpn) : 0;
     rk = sum_adjacent(rk, tpn);
-    if (i < n && sub == 0 && rk < M) {
-      C[(size_t)row * M + rk] = (int32_t)key_tie(k);
-      Cl[(size_t)row * M + rk] = key_val(k);
+    if (i < n && sub == 0 && rk < M) out(rk, k, i);
+  }
+  for (int m = n + tid; m < M; m += nt) out(m, 0ull, -1);
+}
+
+__global__ __launch_bounds__(K1B_THREADS) void k1b_topm_merge(
+    const uint64_t *__restrict__ part, int P, int M, int32_t *__restrict__ C,
+    float *__restrict__ Cl) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int row = blockIdx.x;
+  // (key 0: token -1, the value of an empty slot)
+  topm_merge_row(part, P, M, row, smem, [](const uint64_t *, int) {},
+                 [&](int rk, uint64_t k, int) {
+                   C[(size_t)row * M + rk] = (int32_t)key_tie(k);
+                   Cl[(size_t)row * M + rk] = key_val(k);
+                 });
+}
+
+// The merge fused with the correction tables of the persistent depth loop
+// (bf16, M <= 64, r <= 256, s a multiple of TT_NB): workgroup (x, row) merges
+// row = request * D + depth and forms
+//   G[row][n][j] = W2[C[j]] . W1t[n]   for its TT_NB state units n
+// on the matrix cores (fp32 sums over the rank).  The W1t fragments are
+// loaded before the merge (they do not depend on it), and the W2 rows of the
+// gathered keys are copied into LDS while they are ranked.  Workgroup 0 of
+// the row writes C and Cl, and forms g[row][j] = Cl[j] + W2[C[j]] . uH[row]
+// on the matrix cores too, against uH split exactly into three bf16 terms
+// (every product exact in fp32; the terms' sums are added hi + mid + lo).
+constexpr int TT_NB = 128;
+constexpr int TT_KS = 8;    // k steps of 32 (rank <= 256)
+constexpr int TT_PF = 96;   // most gathered keys whose W2 rows are copied into LDS (>= 64)
+size_t topm_tables_smem(int P, int r) {
+  return topm_merge_smem(P) + ((size_t)TT_PF * (r / 8) + 64) * 16;
+}
+__global__ __launch_bounds__(K1B_THREADS) void k_topm_tables(
+    const uint64_t *__restrict__ part, int P, int M, int r, int s,
+    const uint16_t *__restrict__ W2, const uint16_t *__restrict__ W1t,
+    const float *__restrict__ uH, int32_t *__restrict__ C, float *__restrict__ Cl,
+    float *__restrict__ G, float *__restrict__ g) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int32_t tok_s[64];
+  __shared__ float cl_s[64];
+  __shared__ int16_t gi_s[64];   // gathered position of each rank (-1: none)
+  __shared__ int pf_s;           // the gathered keys' W2 rows are in LDS
+  __shared__ __align__(16) float uh_s[256];
+  // (past the merge's LDS: K1B_FAST keys, P heads, P counts and P list ids)
+  uint16_t *w2s = reinterpret_cast<uint16_t *>(smem + (size_t)K1B_FAST * 8 + (size_t)P * 16);
+  const int row = blockIdx.y, n0 = blockIdx.x * TT_NB, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, gq = lane >> 4;
+  const int rp = (r + 31) & ~31, nks = rp >> 5, r16 = r >> 3;
+  const bool sw = (r16 & 15) == 0;
+  const int n = n0 + wave * 16 + lr;   // < s (s % TT_NB == 0)
+  uint4 bv[TT_KS];
+#pragma unroll
+  for (int ks = 0; ks < TT_KS; ++ks)
+    if (ks < nks) bv[ks] = *reinterpret_cast<const uint4 *>(W1t + (size_t)n * rp + ks * 32 + gq * 8);
+  const bool gw = blockIdx.x == 0 && wave == 0;
+  if (gw)   // uH[row] into LDS (r / 4 pieces of 16 bytes; r % 8 == 0)
+    lds_copy16(uH + (size_t)row * r + 4 * min(lane, r / 4 - 1), lds_addr(uh_s));
+  // 16-byte piece c of W2 row i (gathered position, or rank) goes to LDS
+  // position i r / 8 + p, p = c (with r a multiple of 128: c ^ (i & 15), so
+  // the A-fragment reads of 16 rows spread over the banks); one copy
+  // instruction per 64 pieces, lanes past the end copying the last piece again
+  auto copy_rows = [&](int nr, auto tok_of) {
+    const int tot = nr * r16;
+    for (int base = wave * 64; base < tot; base += K1B_THREADS) {
+      const int i = min(base + lane, tot - 1), gk = i / r16, pp = i - gk * r16;
+      const int c = sw ? (pp ^ (gk & 15)) : pp;
+      const int tk = tok_of(gk);
+      lds_copy16(W2 + (size_t)(tk < 0 ? 0 : tk) * r + 8 * c, lds_addr(w2s + (size_t)base * 8));
     }
+  };
+  topm_merge_row(
+      part, P, M, row, smem,
+      [&](const uint64_t *cand, int ng) {
+        // the gathered keys' W2 rows, copied while they are ranked
+        const int pf = ng <= TT_PF;
+        if (tid == 0) pf_s = pf;
+        if (pf) copy_rows(ng, [&](int gk) { return (int)key_tie(cand[gk]); });
+      },
+      [&](int rk, uint64_t k, int i) {
+        tok_s[rk] = (int32_t)key_tie(k);
+        cl_s[rk] = key_val(k);
+        gi_s[rk] = (int16_t)i;
+        if (blockIdx.x == 0) {
+          C[(size_t)row * M + rk] = (int32_t)key_tie(k);
+          Cl[(size_t)row * M + rk] = key_val(k);
+        }
+      });
+  __syncthreads();
+  const bool pf = pf_s != 0;
+  if (!pf) copy_rows(M, [&](int j) { return tok_s[j]; });   // (many gathered keys: the M rows by rank)
+  wait_vm<0>();   // this wave's copies have landed; the barrier covers the other waves'
+  __syncthreads();
+  // g's B fragments: column lr < 3 holds term lr of uH[row], the rest zeros
+  uint4 ub[TT_KS];
+  if (gw) {
+#pragma unroll
+    for (int ks = 0; ks < TT_KS; ++ks)
+      if (ks < nks) {
+        const int k = min(ks * 32 + gq * 8, r - 8);
+        const float4 x0 = *reinterpret_cast<const float4 *>(uh_s + k);
+        const float4 x1 = *reinterpret_cast<const float4 *>(uh_s + k + 4);
+        const bool in = ks * 32 + gq * 8 < r;
+        float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = in ? x[e] : 0.f;
+        uint4 t3[3];
+        split3_bf16(x, t3);
+        ub[ks] = lr == 0 ? t3[0] : lr == 1 ? t3[1] : lr == 2 ? t3[2] : make_uint4(0u, 0u, 0u, 0u);
+      }
   }
-  for (int m = n + tid; m < M; m += nt) {
-    C[(size_t)row * M + m] = -1;
-    Cl[(size_t)row * M + m] = key_val(0ull);
-  }
+  // A fragments: the candidates' W2 rows from LDS (up to four 16-row tiles;
+  // W1t is zero-padded past r, so any finite weight may meet the padding;
+  // empty candidate slots are masked at the store)
+  const int nmt = (M + 15) >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+    if (mt < nmt) {
+      const int j = min(mt * 16 + lr, M - 1);
+      const int ri = pf ? max((int)gi_s[j], 0) : j;
+      const uint16_t *wr = w2s + (size_t)ri * r;
+      uint4 a[TT_KS];
+#pragma unroll
+      for (int ks = 0; ks < TT_KS; ++ks)
+        if (ks < nks) {
+          const int c = min(ks * 4 + gq, r16 - 1);
+          a[ks] = *reinterpret_cast<const uint4 *>(wr + 8 * (sw ? c ^ (ri & 15) : c));
+        }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, ag = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < TT_KS; ++ks)
+        if (ks < nks) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[ks]), as_bf16x8(bv[ks]), acc,
+                                                        0, 0, 0);
+          if (gw)
+            ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[ks]), as_bf16x8(ub[ks]), ag,
+                                                         0, 0, 0);
+        }
+      // lane holds D[candidate mt 16 + 4 gq + t][unit n] (and, for g, the
+      // candidate's sum against term lr of uH)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int jj = mt * 16 + 4 * gq + t;
+        if (jj < M) G[((size_t)row * s + n) * M + jj] = tok_s[jj] < 0 ? 0.f : acc[t];
+      }
+      if (gw) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float hi = __shfl(ag[t], gq * 16), mid = __shfl(ag[t], gq * 16 + 1),
+                      lo = __shfl(ag[t], gq * 16 + 2);
+          const int jj = mt * 16 + 4 * gq + t;
+          if (lr == 0 && jj < M) g[(size_t)row * M + jj] = cl_s[jj] + ((hi + mid) + lo);
+        }
+      }
+    }
 }
 
 // Round start ahead of the tiled bf16 product: Hb = bf16_rne(H) with rows
@@ -900,6 +1053,9 @@ static const void *k1_fn() { return reinterpret_cast<const void *>(&k1_lmhead_bf
 hipError_t lmhead_prepare(int wtype, int ring, size_t lds_bytes) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k1b_topm_merge),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_topm_tables),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
   if (e != hipSuccess || wtype != WT_BF16) return e;
   const void *fn = ring == 2 ? k1_fn<2>() : ring == 1 ? k1_fn<1>() : k1_fn<0>();
   return set_lds_limit(fn, lds_bytes);
@@ -965,6 +1121,22 @@ hipError_t launch_stage_hidden(const LMHeadArgs &a, hipStream_t st) {
   const int rows_pad = (a.rows + 15) & ~15, n4 = rows_pad * (a.d >> 2);
   hipLaunchKernelGGL(k1_stage_hidden, dim3((n4 + 255) / 256), dim3(256), 0, st, a.H, a.rows,
                      rows_pad, a.d, a.Hb, a.root, a.b, a.Dp1, a.t);
+  return hipGetLastError();
+}
+
+bool topm_tables_ok(int M, int r, int s, const void *W2, const void *W1t) {
+  return M <= 64 && r % 8 == 0 && r <= 32 * TT_KS && s % TT_NB == 0 &&
+         reinterpret_cast<uintptr_t>(W2) % 16 == 0 && reinterpret_cast<uintptr_t>(W1t) % 16 == 0;
+}
+
+hipError_t launch_topm_tables(const uint64_t *part, int P, int M, int rows, int r, int s,
+                              const void *W2, const void *W1t, const float *uH, int32_t *C,
+                              float *Cl, float *G, float *g, hipStream_t st) {
+  if (!topm_tables_ok(M, r, s, W2, W1t)) return hipErrorInvalidValue;
+  const size_t sm = topm_tables_smem(P, r);
+  hipLaunchKernelGGL(k_topm_tables, dim3(s / TT_NB, rows), dim3(K1B_THREADS), sm, st, part, P, M,
+                     r, s, static_cast<const uint16_t *>(W2), static_cast<const uint16_t *>(W1t),
+                     uH, C, Cl, G, g);
   return hipGetLastError();
 }
 

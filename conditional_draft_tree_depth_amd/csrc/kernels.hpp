@@ -109,6 +109,12 @@ size_t topm_merge_smem(int P);
 bool lmhead_tiled_ok(int rows, int d, int wtype);
 hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t st,
                                hipEvent_t ev0, hipEvent_t ev1);
+// the merge fused with the correction tables of the persistent depth loop
+// (G [rows][s][M], g [rows][M]; W1t as launch_corr_tables takes it)
+bool topm_tables_ok(int M, int r, int s, const void *W2, const void *W1t);
+hipError_t launch_topm_tables(const uint64_t *part, int P, int M, int rows, int r, int s,
+                              const void *W2, const void *W1t, const float *uH, int32_t *C,
+                              float *Cl, float *G, float *g, hipStream_t st);
 hipError_t launch_topm_merge(const uint64_t *part, int P, int M, int rows,
                              int32_t *C, float *Cl, hipStream_t st);
 
