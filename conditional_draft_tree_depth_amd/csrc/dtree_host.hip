@@ -90,7 +90,6 @@ struct dtree_ctx {
   // persistent depth loop: available for this context, and the arrival
   // epoch of the next round (flags only ever grow, so they need no reset)
   bool pk = false;
-  bool sel_corr = false;   // correction logits computed inside the selection kernel
   bool sel_batch = false;  // selection over many workgroups (correction logits inside)
   int scoring = DTREE_SCORE_CONDITIONAL;
   int builder = DTREE_BUILD_DEPTHWISE;
@@ -340,12 +339,8 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
   if (pe == hipSuccess) pe = corr_logits_prepare(w->wtype, ctx->lds_max);
   if (pe == hipSuccess) pe = topb_prepare(ctx->lds_max);
   if (pe == hipSuccess) pe = gemm_prepare();
-  // correction logits inside the selection kernel: bf16 W2 rows of 16-byte
-  // pieces whose slice (and the depth's logits) fits in LDS
-  ctx->sel_corr = w->wtype == DTREE_BF16 && r % 8 == 0 && r <= 512 &&
-                  reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
-                  select_corr_smem(c.max_M, r) + 45056 <= ctx->lds_max;
-  if (pe == hipSuccess && ctx->sel_corr) pe = select_corr_prepare(ctx->lds_max);
+  // correction logits inside the (batched) selection kernel: bf16 W2 rows
+  // of 16-byte pieces
   ctx->sel_batch = w->wtype == DTREE_BF16 && r % 8 == 0 && r <= 512 &&
                    reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
                    branch_select_smem(r) + 32768 <= ctx->lds_max;
@@ -623,14 +618,12 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
           HIPCHK(ctx, launch_gemm(g, st));
         }
       }
-      // (with many branches x candidates per request the separate correction
-      // kernel spreads that work over more workgroups)
+      // correction logits, log-softmax, Top-K and Top-W: one kernel over 16
+      // branches per workgroup (bf16 W2), else the logits and the selection
+      // as two kernels
       if (ctx->sel_batch) {
         HIPCHK(ctx, launch_branch_select(batch, A, M, K, W, D, dd, off, r, w.W2, ws.C, ws.Cl,
                                          ws.uh, ldu, tb, ws.ckey, ws.ccand, st));
-      } else if (ctx->sel_corr && A * M <= 2048) {
-        HIPCHK(ctx, launch_select_corr(batch, A, M, K, W, D, dd, off, r, w.W2, ws.C, ws.Cl, ws.uh,
-                                       ldu, tb, st));
       } else {
         HIPCHK(ctx, launch_corr_logits(batch, A, M, r, D, dd, w.W2, wt, ws.C, ws.Cl, ws.uh, ldu,
                                        ws.ell, st));
@@ -1011,7 +1004,6 @@ extern "C" dtree_status dtree_build_round_static(const dtree_weights *w, const d
         if (pe == hipSuccess) pe = corr_logits_prepare(WT_F32, sd.lds_max);
         if (pe == hipSuccess) pe = topb_prepare(sd.lds_max);
         if (pe == hipSuccess) pe = gemm_prepare();
-        if (pe == hipSuccess) pe = select_corr_prepare(sd.lds_max);
         if (pe == hipSuccess) pe = branch_select_prepare(sd.lds_max);
         if (pe != hipSuccess) {
           char m[128];
@@ -1047,9 +1039,6 @@ extern "C" dtree_status dtree_build_round_static(const dtree_weights *w, const d
   ctx.k1_smem = k1_smem;
   ctx.lds_max = sd.lds_max;
   static_layout(*w, *p, batch, P, NT, static_cast<uint8_t *>(sd.scratch), ctx.ws);
-  ctx.sel_corr = w->wtype == DTREE_BF16 && w->r % 8 == 0 && w->r <= 512 &&
-                 reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
-                 select_corr_smem(M, w->r) + 45056 <= sd.lds_max;
   ctx.sel_batch = w->wtype == DTREE_BF16 && w->r % 8 == 0 && w->r <= 512 &&
                   reinterpret_cast<uintptr_t>(w->W2) % 16 == 0 &&
                   branch_select_smem(w->r) + 32768 <= sd.lds_max;

@@ -346,189 +346,6 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
   }
 }
 
-// The same selection with the corrected logits computed in place (bf16 W2,
-// r a multiple of 8, A M <= 2048): the r x M slice of W2 for the depth's
-// candidates is staged in LDS once per request, and all logits
-// ell[a][j] = Cl[j] + W2[C[j]] . u_a are formed on the matrix cores into LDS
-// (an M x r by r x A product over the exact three-term split of u) before
-// the per-branch log-softmax, so the logits never leave the workgroup.
-// (Formed by each branch's wave as fp32 dot products on the vector units,
-// they took a wide-tree depth 18.8 us, mostly those products.)
-__global__ __launch_bounds__(SEL_THREADS) void k_select_corr(int A, int M, int K, int W, int D,
-                                                             int delta, int off, int r,
-                                                             const uint16_t *__restrict__ W2,
-                                                             const int32_t *__restrict__ C,
-                                                             const float *__restrict__ Cl,
-                                                             const float *__restrict__ u, int ldu,
-                                                             TreeBufs t) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ uint64_t ckey[SEL_MAXZ];
-  __shared__ uint32_t clex[SEL_MAXZ];
-  __shared__ uint32_t slex[SEL_MAXW];
-  __shared__ int32_t pnode[SEL_MAXW];
-  __shared__ uint32_t prank[SEL_MAXW];
-  __shared__ float pscore[SEL_MAXW];
-  __shared__ int32_t ctok[128];
-  __shared__ float clv[128];
-  __shared__ uint64_t wkeys[(SEL_THREADS / 64) * 128];   // one row of keys per wave
-  __shared__ int16_t cidx[SEL_MAXZ];                      // children's candidate index
-  const int rs = r + 8;
-  uint16_t *W2s = reinterpret_cast<uint16_t *>(smem);                    // [M][r + 8]
-  float *ell_s = reinterpret_cast<float *>(smem + (((size_t)M * rs * 2 + 15) & ~(size_t)15));  // [A][M]
-  const int q = blockIdx.x, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int nw = blockDim.x >> 6;
-  const int32_t *cq = C + ((size_t)q * D + delta) * M;
-  const size_t nb = (size_t)q * t.NT;
-  const int Z = A * K;
-  const int An = Z < W ? Z : W;
-
-  for (int a = tid; a < A; a += blockDim.x) {
-    const int p = t.surv_node[(size_t)q * t.Wmax + a];
-    pnode[a] = p;
-    prank[a] = (uint32_t)t.surv_rank[(size_t)q * t.Wmax + a];
-    pscore[a] = t.n_score[nb + p];
-  }
-  for (int j = tid; j < M; j += blockDim.x) {
-    ctok[j] = cq[j];
-    clv[j] = Cl[((size_t)q * D + delta) * M + j];
-  }
-  const int r8 = r >> 3;
-  for (int i = tid; i < M * r8; i += blockDim.x) {
-    const int j = i / r8, c8 = i - j * r8;
-    const int tk = cq[j] < 0 ? 0 : cq[j];   // an empty slot never reaches here
-    *reinterpret_cast<uint4 *>(W2s + j * rs + 8 * c8) =
-        *reinterpret_cast<const uint4 *>(W2 + (size_t)tk * r + 8 * c8);
-  }
-  __syncthreads();
-  // Correction logits of every (branch, candidate) pair on the matrix cores,
-  // one 16 x 16 tile (candidates x branches) per wave at a time:
-  // ell_s[a][j] = Cl[j] + W2[C[j]] . u_a over k steps of 32, u split exactly
-  // into three bf16 terms (W2 is bf16, so every product is exact in fp32).
-  {
-    const int lr = lane & 15, g = lane >> 4;
-    const int ntj = (M + 15) >> 4, nta = (A + 15) >> 4;
-    for (int tile = wave; tile < ntj * nta; tile += nw) {
-      const int jt = tile % ntj, at = tile / ntj;
-      const int j = jt * 16 + lr, a = at * 16 + lr;
-      const uint16_t *wr = W2s + (j < M ? j : 0) * rs;
-      const float *ua = u + ((size_t)q * A + (a < A ? a : 0)) * ldu;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      // up to eight k steps at a time: their u loads are all in flight
-      // together
-      for (int k0 = 0; k0 < r; k0 += 256) {
-        // (loads from clamped addresses, always in bounds, then masked: no
-        // branch between them)
-        float x[8][8];
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const int kk = k0 + 32 * st + 8 * g;   // r % 8 == 0: 8 elements all in or all out
-          const bool in = kk < r && a < A;
-          const float *up = ua + min(kk, r - 8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = up[e];
-            x[st][e] = in ? v : 0.f;
-          }
-        }
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const int kk = k0 + 32 * st + 8 * g;
-          uint4 wa = *reinterpret_cast<const uint4 *>(wr + min(kk, r - 8));
-          if (kk >= r) wa = make_uint4(0u, 0u, 0u, 0u);
-          uint4 t3[3];
-          split3_bf16(x[st], t3);
-#pragma unroll
-          for (int tq = 0; tq < 3; ++tq) acc = cl_mfma(wa, t3[tq], acc);
-        }
-      }
-      // lane holds D[candidate 4 g + t][branch lr]
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int jj = jt * 16 + 4 * g + tt;
-        if (jj < M && a < A) ell_s[a * M + jj] = clv[jj] + acc[tt];
-      }
-    }
-  }
-  __syncthreads();
-  const bool h0 = lane < M, h1 = lane + 64 < M;
-  for (int a = wave; a < A; a += nw) {
-    const float l0 = h0 ? ell_s[a * M + lane] : -INFINITY;
-    const float l1 = h1 ? ell_s[a * M + lane + 64] : -INFINITY;
-    const int p = pnode[a];
-    const uint32_t pr = prank[a];
-    const float ps = pscore[a];
-    const float m = wave_max_f32(fmaxf(l0, l1));
-    const float e = (h0 ? expf(l0 - m) : 0.f) + (h1 ? expf(l1 - m) : 0.f);
-    const float lse = m + logf(wave_sum_f32(e));
-    const uint64_t k0 = h0 ? make_key(l0 - lse, (uint32_t)ctok[lane]) : 0ull;
-    const uint64_t k1 = h1 ? make_key(l1 - lse, (uint32_t)ctok[lane + 64]) : 0ull;
-    // Top-K by rank; each selected candidate's lane writes its child
-    int r0, r1;
-    branch_ranks(k0, k1, h0, h1, M, wkeys + wave * 128, lane, r0, r1);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint64_t kk = h ? k1 : k0;
-      const int rk = h ? r1 : r0;
-      if ((h ? h1 : h0) && rk < K) {
-        const uint32_t tok = key_tie(kk);
-        const float lp = key_val(kk);
-        const float sc = __fadd_rn(ps, lp);
-        const uint32_t lex = (pr << 18) | tok;
-        const int c = a * K + rk;
-        const size_t id = nb + off + c;
-        t.n_tok[id] = (int32_t)tok;
-        t.n_par[id] = p;
-        t.n_dep[id] = delta + 1;
-        t.n_score[id] = sc;
-        t.n_lex[id] = lex;
-        ckey[c] = make_key(sc, lex);
-        clex[c] = lex;
-        cidx[c] = (int16_t)(lane + 64 * h);
-      }
-    }
-  }
-  __syncthreads();
-
-  // Top-W by rank: keys are distinct (distinct token paths)
-  for (int c = tid; c < Z; c += blockDim.x) {
-    const uint64_t kc = ckey[c];
-    const int rank = count_greater<uint64_t>(ckey, Z, kc);
-    if (rank < An) {
-      const size_t sl = (size_t)q * t.Wmax + rank;
-      t.nsurv_node[sl] = off + c;
-      slex[rank] = clex[c];
-      t.gidx_tok[(size_t)q * An + rank] = (int32_t)(clex[c] & 0x3FFFFu);
-      t.gidx_par[(size_t)q * An + rank] = q * A + c / K;
-      if (t.gidx_cand) t.gidx_cand[(size_t)q * An + rank] = (q * D + delta) * M + cidx[c];
-      t.surv_hist[((size_t)q * (D + 1) + delta + 1) * t.Wmax + rank] = off + c;
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < An; i += blockDim.x) {
-    const uint32_t li = slex[i];
-    const int rank = An - 1 - count_greater<uint32_t>(slex, An, li);   // lex keys are distinct
-    t.nsurv_rank[(size_t)q * t.Wmax + i] = rank;
-  }
-}
-
-size_t select_corr_smem(int M, int r) {
-  // W2 rows [M][r + 8] bf16, then the logits [A][M] fp32 (A M <= 2048)
-  return (((size_t)M * (r + 8) * 2 + 15) & ~(size_t)15) + (size_t)2048 * 4;
-}
-
-hipError_t select_corr_prepare(size_t lds_bytes) {
-  return set_lds_limit(reinterpret_cast<const void *>(&k_select_corr), lds_bytes);
-}
-
-hipError_t launch_select_corr(int b, int A, int M, int K, int W, int D, int delta, int off, int r,
-                              const void *W2, const int32_t *C, const float *Cl, const float *u,
-                              int ldu, const TreeBufs &t, hipStream_t st) {
-  hipLaunchKernelGGL(k_select_corr, dim3(b), dim3(SEL_THREADS), select_corr_smem(M, r), st, A, M,
-                     K, W, D, delta, off, r, static_cast<const uint16_t *>(W2), C, Cl, u, ldu, t);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------- batched selection
 // The selection of one depth spread over many workgroups (bf16 W2 with
 // 16-byte rows, r a multiple of 8 up to 512, M <= 128):
@@ -539,7 +356,7 @@ hipError_t launch_select_corr(int b, int A, int M, int K, int W, int D, int delt
 //  then the last of a request's workgroups to finish takes the Top-W
 //    survivors among those keys (no second launch: a launch costs several
 //    microseconds here, more than the arrival count and the reload).
-// Same arithmetic, keys and tie-breaks as k_select / k_select_corr
+// Same arithmetic, keys and tie-breaks as k_select
 // ("Resumen Técnico: DominoTree", Componentes Principales 2; DARTree page,
 // Metodología 1).
 constexpr int BS_BR = 16;

@@ -202,13 +202,6 @@ hipError_t launch_branch_select(int b, int A, int M, int K, int W, int D, int de
                                 int r, const void *W2, const int32_t *C, const float *Cl,
                                 const float *u, int ldu, const TreeBufs &t, uint64_t *ckey,
                                 int32_t *ccand, hipStream_t st);
-// selection with the correction logits computed in place (bf16 W2, 16-byte
-// aligned, r % 8 == 0; dynamic LDS select_corr_smem(M, r))
-size_t select_corr_smem(int M, int r);
-hipError_t select_corr_prepare(size_t lds_bytes);
-hipError_t launch_select_corr(int b, int A, int M, int K, int W, int D, int delta, int off, int r,
-                              const void *W2, const int32_t *C, const float *Cl, const float *u,
-                              int ldu, const TreeBufs &t, hipStream_t st);
 hipError_t launch_topb_emit(int b, int NT, int B, float beta, int Bmax,
                             const TreeBufs &t, int32_t *tok, int32_t *parent,
                             int32_t *depth, float *score, uint8_t *mask,
