@@ -515,7 +515,7 @@ static constexpr size_t mm_smem() { return (size_t)STAGES * (BM + BN) * 128; }
 // CU), else 128 x 128 (two workgroups per CU)
 void mm_tile(int R, int N, int *bm, int *bn) {
   const long long big = (long long)((R + 255) / 256) * ((N + 127) / 128);
-  *bm = big >= 200 ? 256 : 128;
+  *bm = big >= 256 ? 256 : 128;
   *bn = 128;
 }
 
