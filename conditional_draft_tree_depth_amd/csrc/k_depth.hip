@@ -422,7 +422,28 @@ __device__ void topw_request(int q, int A, int K, int W, int D, int delta, int o
                              const TreeBufs &t, TopwLds &L) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int Z = A * K, An = Z < W ? Z : W;
-  if (An < Z) {
+  uint64_t tau = 0ull;
+  if (An < Z && An == A) {
+    // full width (m = 1): tau is the weakest of the branches' best children,
+    // found by every wave on its own (no barrier)
+    uint64_t v = ~0ull;
+    for (int a2 = lane; a2 < A; a2 += 64) {
+      const uint64_t k = L.key[a2 * K];
+      v = k < v ? k : v;
+    }
+    v = ~group_max_u64<16>(~v);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+      const auto h = x ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                       : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+      const auto l = x ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                       : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+      const uint64_t k0 = ((uint64_t)h[0] << 32) | l[0], k1 = ((uint64_t)h[1] << 32) | l[1];
+      v = k0 < k1 ? k0 : k1;
+    }
+    tau = v;
+  } else if (An < Z) {
     const int m = (An + A - 1) / A, ns = A * m;
     for (int i = tid; i < ns; i += NT) L.pk[i] = L.key[(i / m) * K + i % m];
     __syncthreads();
@@ -435,8 +456,8 @@ __device__ void topw_request(int q, int A, int K, int W, int D, int delta, int o
       if (i < ns && part == 0 && cnt == An - 1) L.tau = kc;   // keys are distinct: one thread
     }
     __syncthreads();
+    tau = L.tau;
   }
-  const uint64_t tau = L.tau;
   for (int c0 = 0; c0 < Z; c0 += NT) {
     const int c = c0 + tid;
     const bool keep = c < Z && L.key[c] >= tau;
