@@ -509,10 +509,11 @@ hipError_t launch_mm_lm(const GemmArgs &a, int bn, hipStream_t st, hipEvent_t ev
 template <int BM, int BN, int STAGES>
 static constexpr size_t mm_smem() { return (size_t)STAGES * (BM + BN) * 128; }
 
-// the largest per-wave block whose tile count still covers most of the
-// 256 CUs (one workgroup per CU)
-// the larger tile when it still makes 200 or more tiles (one workgroup per
-// CU), else 128 x 128 (two workgroups per CU)
+// 256 x 128 tiles (eight waves of 64 x 64, one workgroup per CU) when they
+// still make 256 or more tiles, else 128 x 128 (eight waves of 32 x 64, two
+// workgroups per CU: four waves per SIMD to cover each other's waits; the
+// stress state product, 416 such tiles, took 53 us with four waves of 64 x 64
+// and 40 us with eight)
 void mm_tile(int R, int N, int *bm, int *bn) {
   const long long big = (long long)((R + 255) / 256) * ((N + 127) / 128);
   *bm = big >= 256 ? 256 : 128;
@@ -527,7 +528,7 @@ bool mm_ok(const GemmArgs &a) {
 }
 
 // configurations: (BM, BN, WM, WN)
-#define MM_CONFIGS(X) X(256, 128, 4, 2, 3) X(128, 128, 2, 2, 2)
+#define MM_CONFIGS(X) X(256, 128, 4, 2, 3) X(128, 128, 4, 2, 2)
 
 hipError_t launch_mm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
                      hipEvent_t ev1) {
