@@ -509,11 +509,12 @@ hipError_t launch_mm_lm(const GemmArgs &a, int bn, hipStream_t st, hipEvent_t ev
 template <int BM, int BN, int STAGES>
 static constexpr size_t mm_smem() { return (size_t)STAGES * (BM + BN) * 128; }
 
-// 256 x 128 tiles (eight waves of 64 x 64, one workgroup per CU) when they
+// 256 x 128 tiles (sixteen waves of 32 x 64, one workgroup per CU) when they
 // still make 256 or more tiles, else 128 x 128 (eight waves of 32 x 64, two
-// workgroups per CU: four waves per SIMD to cover each other's waits; the
-// stress state product, 416 such tiles, took 53 us with four waves of 64 x 64
-// and 40 us with eight)
+// workgroups per CU).  Four waves per SIMD cover each other's waits: the
+// stress state product, 416 tiles of 128 x 128, took 53 us with four waves of
+// 64 x 64 and 40 us with eight of 32 x 64; the stress distinct tokens'
+// projections (256 x 128) 82 us with eight waves of 64 x 64, 75 with sixteen.
 void mm_tile(int R, int N, int *bm, int *bn) {
   const long long big = (long long)((R + 255) / 256) * ((N + 127) / 128);
   *bm = big >= 256 ? 256 : 128;
@@ -528,7 +529,7 @@ bool mm_ok(const GemmArgs &a) {
 }
 
 // configurations: (BM, BN, WM, WN)
-#define MM_CONFIGS(X) X(256, 128, 4, 2, 3) X(128, 128, 4, 2, 2)
+#define MM_CONFIGS(X) X(256, 128, 8, 2, 3) X(128, 128, 4, 2, 2)
 
 hipError_t launch_mm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
                      hipEvent_t ev1) {
