@@ -618,7 +618,7 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
           HIPCHK(ctx, launch_gemm(g, st));
         }
       }
-      // correction logits, log-softmax, Top-K and Top-W: one kernel over 16
+      // correction logits, log-softmax, Top-K and Top-W: one kernel over 8
       // branches per workgroup (bf16 W2), else the logits and the selection
       // as two kernels
       if (ctx->sel_batch) {

@@ -359,7 +359,10 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int A, int M, int K, int
 // Same arithmetic, keys and tie-breaks as k_select
 // ("Resumen Técnico: DominoTree", Componentes Principales 2; DARTree page,
 // Metodología 1).
-constexpr int BS_BR = 16;
+// (8 branches per workgroup: the wide tree's depth loop took 362 us, 392 us
+// with 16, whose single workgroup per request at 16 branches saved nothing on
+// the 8B x 8 shape)
+constexpr int BS_BR = 8;
 constexpr int SEL_FLAGS = 64;   // arrival flags per request (at least SEL_MAXW / BS_BR)
 
 // Ranks of the K best of a wave's candidates, by log-prob descending and
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(64 * BS_BR) void k_branch_topk(
   const bool tile = jt * 16 < M;
   const int jw = min(jt * 16 + lr, M - 1);
   const int tokw = max(C[cb + jw], 0);   // an empty slot never reaches here
-  // u of the workgroup's branches, 8 values per thread (BS_BR r / 8 <= 1024
+  // u of the workgroup's branches, 8 values per thread (BS_BR r / 8 <= 512
   // threads), coalesced
   const int ub = tid / r8, uc = tid - ub * r8;
   const bool uin = ub < BS_BR && a0 + ub < A;
