@@ -118,8 +118,9 @@ __device__ __forceinline__ void lane_best(const uint64_t (&keys)[KPL], uint64_t 
 }
 
 // Each lane holds KPL ordered values of the row (hv, 0 = empty) for columns
-// hl + 32 i.  Fast path (M <= 64): S = every lane's two best values; tau,
-// the M-th largest of S, has at least M keys of the row at or above it, so
+// hl + 32 i.  Fast path (M <= 64): S = every lane's two best values (four
+// when M > 32); tau, the M-th largest of S, has at least M keys of the row at
+// or above it, so
 // the row's M best are among the keys with value >= tau, usually only a few
 // more than M.  Those are written unsorted.  With more than K1_LCAP of them
 // (ties) or M > 64, the row's exact M best are written instead, by M rounds
@@ -147,14 +148,29 @@ __device__ __forceinline__ void wg_topm_epilogue(const float *Ls, int lstride, i
     uint64_t *outr = out + (size_t)r * rstride;
     bool done = false;
     if (M <= 64) {
-      uint32_t sv[2] = {0u, 0u};
+      // S: every lane's NR best values (NR = 4 when M > 32, so that tau, the
+      // M-th largest of 32 NR values, stays high enough for the keys that
+      // reach it to fit a list)
+      auto tau_of = [&](auto nr) -> uint32_t {
+        constexpr int NR = decltype(nr)::value;
+        uint32_t sv[NR];
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) {
-        sv[1] = max(sv[1], min(sv[0], hv[i]));
-        sv[0] = max(sv[0], hv[i]);
-      }
-      bitonic_sort32<2, 2>(sv, hl);
-      const uint32_t tau = bitonic_elem<2>(sv, M - 1);
+        for (int t = 0; t < NR; ++t) sv[t] = 0u;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          uint32_t x = hv[i];
+#pragma unroll
+          for (int t = 0; t < NR; ++t) {
+            const uint32_t hi = max(x, sv[t]);
+            x = min(x, sv[t]);
+            sv[t] = hi;
+          }
+        }
+        bitonic_sort32<NR, 2>(sv, hl);
+        return bitonic_elem<NR>(sv, M - 1);
+      };
+      const uint32_t tau = M <= 32 ? tau_of(std::integral_constant<int, 2>())
+                                   : tau_of(std::integral_constant<int, 4>());
       int cnt = 0;
 #pragma unroll
       for (int i = 0; i < KPL; ++i) cnt += (hv[i] >= tau && hv[i] != 0u) ? 1 : 0;
