@@ -136,11 +136,15 @@ __device__ __forceinline__ void wg_topm_epilogue(const float *Ls, int lstride, i
   for (int rb = wave * 2; rb < nrow; rb += 2 * nw) {
     const int r = rb + (lane >> 5);
     const bool active = r < nrow;
+    // every read in bounds (row r < 16, column clamped), the empty ones
+    // zeroed afterwards: no branch around each read, all in flight at once
     uint32_t hv[KPL];
+    const float *lrow = Ls + (active ? r : 0) * lstride;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
       const int c = hl + 32 * i;
-      hv[i] = (active && c < ncols) ? f32_ord(Ls[r * lstride + c]) : 0u;
+      const float x = lrow[c < ncols ? c : 0];
+      hv[i] = (active && c < ncols) ? f32_ord(x) : 0u;
     }
     auto key_of = [&](int i) -> uint64_t {
       return ((uint64_t)hv[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(col0 + hl + 32 * i));
@@ -355,27 +359,18 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
         for (int j = 0; j < 4; ++j) regs[pp][j] = ptr[pp * 16 + j];
       }
   };
-  // the first loads are in flight while the hidden rows are staged
-  if (ntw > 0) {
-    if constexpr (RING > 0) {
-      ring_rows(0);
-#pragma unroll
-      for (int p0 = 0; p0 < RING; ++p0) ring_issue();
-    } else {
-      reg_start(0);
-    }
-  }
-
-  // bias of this slice's vocabulary columns, staged once
-  float *bs = reinterpret_cast<float *>(smem + lmhead_smem_body(d) + (size_t)K1_WAVES * RING * K1_CHUNK);
-  {
-    const int c0 = t0 * 16, nc = min(min(t1, ntV) * 16, V) - c0;
-    for (int c = threadIdx.x; c < nc; c += K1_WAVES * 64) bs[c] = bias ? bias[c0 + c] : 0.f;
-  }
-  // round start: the first workgroup of each slice starts the tree buffers
-  // of its requests (read only by the kernels after this one)
-  if (bx == 0 && root)
-    for (int q = y; q < b; q += P) init_round_request(q, root, tb, Dp1, threadIdx.x, K1_WAVES * 64);
+  // The hidden rows and the bias are staged before the first W_lm copies
+  // are issued: behind those copies (every CU's, in the same memory queues)
+  // their loads took several microseconds.
+  // bias of this slice's vocabulary columns (at most K1_MAXCOLS = 640 of
+  // them, two per thread)
+  const int bc0 = t0 * 16, bnc = min(min(t1, ntV) * 16, V) - bc0;
+  const int bcA = threadIdx.x, bcB = threadIdx.x + K1_WAVES * 64;
+  static_assert(K1_MAXCOLS <= 2 * K1_WAVES * 64, "two bias values per thread");
+  // (a slice of W1 tiles only has bnc <= 0 and reads nothing)
+  const bool hasb = bias && bnc > 0;
+  const float bvA = hasb ? bias[bc0 + min(bcA, bnc - 1)] : 0.f;
+  const float bvB = hasb ? bias[bc0 + min(bcB, bnc - 1)] : 0.f;
   // the 16 hidden rows of this block, rounded to bf16 (nearest-even) while
   // they are staged in LDS (rows past the last are zeros); 16-byte chunk j
   // of row q is stored at chunk j ^ (q & 7) of the row, so the B-fragment
@@ -408,6 +403,23 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
       }
     }
   }
+  float *bs = reinterpret_cast<float *>(smem + lmhead_smem_body(d) + (size_t)K1_WAVES * RING * K1_CHUNK);
+  if (bcA < bnc) bs[bcA] = bvA;
+  if (bcB < bnc) bs[bcB] = bvB;
+  // the first W_lm loads are in flight while the tree buffers are started
+  if (ntw > 0) {
+    if constexpr (RING > 0) {
+      ring_rows(0);
+#pragma unroll
+      for (int p0 = 0; p0 < RING; ++p0) ring_issue();
+    } else {
+      reg_start(0);
+    }
+  }
+  // round start: the first workgroup of each slice starts the tree buffers
+  // of its requests (read only by the kernels after this one)
+  if (bx == 0 && root)
+    for (int q = y; q < b; q += P) init_round_request(q, root, tb, Dp1, threadIdx.x, K1_WAVES * 64);
   __syncthreads();
 
   float vals[K1_TPW][4];
@@ -462,22 +474,34 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_lmhead_bf16(
 
   float *Ls = reinterpret_cast<float *>(smem);
   constexpr int LSTR = K1_MAXCOLS;
-  if (lr < nrow) {
+  // vocabulary tiles: the bias reads (in bounds: c < K1_MAXCOLS) all issued
+  // before the logit stores, which are predicated, not branched around
+  {
+    float bv[K1_TPW][4];
+#pragma unroll
+    for (int i = 0; i < K1_TPW; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bv[i][t] = bs[(wave + K1_WAVES * i) * 16 + 4 * g + t];
 #pragma unroll
     for (int i = 0; i < K1_TPW; ++i) {
-      const int lt = wave + K1_WAVES * i;
-      if (lt < nt) {
-        const int tt = t0 + lt;
+      const int lt = wave + K1_WAVES * i, tt = t0 + lt;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = lt * 16 + 4 * g + t;
+        if (lr < nrow && lt < nt && tt < ntV && t0 * 16 + c < V) Ls[lr * LSTR + c] = vals[i][t] + bv[i][t];
+      }
+    }
+  }
+  // tiles of W1 rows: uH
+  if (lr < nrow && t1 > ntV) {
+#pragma unroll
+    for (int i = 0; i < K1_TPW; ++i) {
+      const int lt = wave + K1_WAVES * i, tt = t0 + lt;
+      if (lt < nt && tt >= ntV) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          if (tt < ntV) {
-            const int c = lt * 16 + 4 * g + t;
-            const int v = t0 * 16 + c;
-            if (v < V) Ls[lr * LSTR + c] = vals[i][t] + bs[c];
-          } else {
-            const int uc = (tt - ntV) * 16 + 4 * g + t;
-            if (uc < r) uH[(size_t)(row0 + lr) * r + uc] = vals[i][t];
-          }
+          const int uc = (tt - ntV) * 16 + 4 * g + t;
+          if (uc < r) uH[(size_t)(row0 + lr) * r + uc] = vals[i][t];
         }
       }
     }
