@@ -72,6 +72,17 @@ template <int STEP>
 __device__ __forceinline__ uint64_t xchg_u64(uint64_t v) {
   return ((uint64_t)xchg_u32<STEP>((uint32_t)(v >> 32)) << 32) | xchg_u32<STEP>((uint32_t)v);
 }
+// inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within rows
+// of 16 lanes, then the row ends broadcast into the later rows)
+__device__ __forceinline__ int wave_scan_add(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31, rows 2, 3
+  return v;
+}
 __device__ __forceinline__ float wave_max_f32(float v) {
   v = fmaxf(v, xchg_f32<1>(v));
   v = fmaxf(v, xchg_f32<2>(v));

@@ -473,6 +473,11 @@ __global__ __launch_bounds__(WM * WN * 64) void k_mm_lm(GemmArgs a) {
   }
   wait_vm<0>();   // no copy outlives the workgroup
   // lane holds Y[row 4 g + t][output lr] of tile (i, j)
+  uint32_t gm[TM][4];   // the lane's largest ordered output per row
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) gm[i][t] = 0u;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int n = n0 + wn + j * 16 + lr;
@@ -483,7 +488,26 @@ __global__ __launch_bounds__(WM * WN * 64) void k_mm_lm(GemmArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int row = m0 + wm + i * 16 + 4 * g + t;
-        if (row < R) a.Y[(size_t)row * a.ldy + n] = acc[i][j][t] + bv;
+        const float y = acc[i][j][t] + bv;
+        gm[i][t] = max(gm[i][t], f32_ord(y));
+        if (row < R) a.Y[(size_t)row * a.ldy + n] = y;
+      }
+  }
+  // group maxima: the wave's BN / WN columns, over the 16 lanes of a row
+  // (lanes past the last column hold 0, below every ordered value)
+  if (a.gmax && n0 + wn < a.N) {
+    const int gi = (n0 + wn) / (BN / WN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t v = gm[i][t];
+        v = max(v, xchg_u32<1>(v));
+        v = max(v, xchg_u32<2>(v));
+        v = max(v, xchg_u32<4>(v));
+        v = max(v, xchg_u32<8>(v));
+        const int row = m0 + wm + i * 16 + 4 * g + t;
+        if (lr == 0 && row < R) a.gmax[(size_t)row * a.ldg + gi] = v;
       }
   }
 }

@@ -899,9 +899,16 @@ __global__ __launch_bounds__(256) void k1_stage_hidden(const float *__restrict__
 // The keys >= K, exactly M of them, are written unsorted with K as the
 // list's bound, the best key and the count (the layout of the fast path).
 // A slice with fewer than M keys writes all of them with a zero bound.
+// With a row-wide bound rbound[r] (an ordered value that at least M keys of
+// the whole row reach, from k1_row_bound) the list is instead every slice
+// key of value >= that bound, written with it as the list's bound, whenever
+// those keys fit a list for both rows of the wave (usually a few per slice);
+// otherwise the search above runs.  Either list holds every slice key at or
+// above its bound, and at least M keys of the row reach it.
 template <int MAXC>
 __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int ncols, int col0,
-                                               int nrow, int M, uint64_t *out, size_t rstride) {
+                                               int nrow, int M, uint64_t *out, size_t rstride,
+                                               const uint32_t *rbound) {
   constexpr int KPL = MAXC / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6, hl = lane & 31;
@@ -920,14 +927,25 @@ __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int
     const int r = rb + (lane >> 5);
     const bool active = r < nrow;
     uint32_t hv[KPL];   // ordered values, 0 = empty column
+    const float *lrow = Ls + (active ? r : 0) * lstride;   // reads in bounds, no branches
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
       const int c = hl + 32 * i;
-      hv[i] = (active && c < ncols) ? f32_ord(Ls[r * lstride + c]) : 0u;
+      const float x = lrow[c < ncols ? c : 0];
+      hv[i] = (active && c < ncols) ? f32_ord(x) : 0u;
     }
     auto tie_of = [&](int i) { return 0xFFFFFFFFu - (uint32_t)(col0 + hl + 32 * i); };
     uint64_t T = 0;   // the M-th largest key (0: fewer than M keys)
-    if (ncols > M) {
+    bool bounded = false;
+    if (rbound) {
+      const uint32_t tb = active ? rbound[r] : 0xFFFFFFFFu;
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) c += (hv[i] >= tb && hv[i] != 0u) ? 1 : 0;
+      bounded = __all(!active || (tb != 0u && total(c) <= K1_LCAP));
+      if (bounded) T = (uint64_t)tb << 32;
+    }
+    if (!bounded && ncols > M) {
       // (a step whose count is exactly M has found a value bound with
       // exactly M keys at or above it: once every row of the wave has one,
       // the search stops and that bound is the list's)
@@ -1005,7 +1023,8 @@ __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int
 constexpr int LS_ROWS = 8;
 template <bool BISECT>
 __global__ __launch_bounds__(LS_ROWS / 2 * 64) void k1_lists_from_logits(
-    const float *__restrict__ L, int rows, int V, int M, uint64_t *__restrict__ part) {
+    const float *__restrict__ L, int rows, int V, int M, uint64_t *__restrict__ part,
+    const uint32_t *__restrict__ rbound) {
   extern __shared__ __align__(16) uint8_t smem[];
   float *Ls = reinterpret_cast<float *>(smem);
   const int P = gridDim.y, y = blockIdx.y, row0 = blockIdx.x * LS_ROWS;
@@ -1060,9 +1079,54 @@ __global__ __launch_bounds__(LS_ROWS / 2 * 64) void k1_lists_from_logits(
   __syncthreads();
   uint64_t *out = part + ((size_t)row0 * P + y) * K1_LSTRIDE;
   if constexpr (BISECT)
-    wg_topm_bisect<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE);
+    wg_topm_bisect<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE,
+                               rbound ? rbound + row0 : nullptr);
   else
     wg_topm_epilogue<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE);
+}
+
+// Row-wide list bound: the M-th largest of the row's ng column-group maxima
+// (ordered values; ng >= M).  Each maximum is the value of a distinct key
+// of the row, so at least M keys reach the bound, and with many narrow
+// groups it lies close below the row's M-th largest value.  One workgroup
+// per row, radix passes of 8 bits from the top: each pass counts the
+// maxima that match the digits found so far by their next digit and keeps
+// the digit where the count from the top reaches the number still wanted.
+constexpr int RB_THREADS = 256;
+__global__ __launch_bounds__(RB_THREADS) void k1_row_bound(const uint32_t *__restrict__ gmax,
+                                                          int ng, int ldg, int M,
+                                                          uint32_t *__restrict__ bound) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t pick[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint32_t *gm = gmax + (size_t)blockIdx.x * ldg;
+  uint32_t prefix = 0, pmask = 0, need = (uint32_t)M;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < ng; i += RB_THREADS) {
+      const uint32_t k = gm[i];
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l: digits 255 - 4 l .. 252 - 4 l; counts of the higher digits first
+      uint32_t c[4], sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; sum += c[j]; }
+      uint32_t before = (uint32_t)wave_scan_add((int)sum) - sum;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (before < need && before + c[j] >= need) { pick[0] = 255u - 4u * lane - j; pick[1] = before; }
+        before += c[j];
+      }
+    }
+    __syncthreads();
+    prefix |= pick[0] << shift;
+    pmask |= 255u << shift;
+    need -= pick[1];
+  }
+  if (tid == 0) bound[blockIdx.x] = prefix;
 }
 
 // ----------------------------------------------------------------- host side
@@ -1134,25 +1198,34 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
   hipError_t e;
   GemmArgs g{a.rows, a.V, a.d, a.Hb, WT_BF16, a.d, nullptr, 0, a.W, WT_BF16, a.d, a.bias,
              nullptr, 0, 1, 0, 0, logits, a.V};
-  if (a.rows <= 128 && mm_ok(g)) {
-    // one row tile: 320-token tiles make 1.9 rounds of workgroups over the
-    // vocabulary (475 tiles at V = 151936) instead of 2.3 rounds of 256
-    e = launch_mm_lm(g, 320, st, ev0, ev1);
-  } else if (mm_ok(g)) {
-    e = launch_mm_lm(g, 256, st, ev0, ev1);
-  } else {
-    return hipErrorInvalidValue;   // lmhead_tiled_ok admits bf16 rows with d % 64 == 0 only
-  }
+  // one row tile: 320-token tiles make 1.9 rounds of workgroups over the
+  // vocabulary (475 tiles at V = 151936) instead of 2.3 rounds of 256
+  const int bn = a.rows <= 128 ? 320 : 256;
+  const int gw = bn / 4;   // columns per wave of the tile: the maxima's groups
+  const int ng = (a.V + gw - 1) / gw;
+  // the row-wide list bound needs M groups (lmhead_groups sizes gmax for
+  // the narrowest groups)
+  const bool rowb = a.gmax && a.rbound && ng >= a.M;
+  if (rowb) { g.gmax = a.gmax; g.ldg = lmhead_groups(a.V); }
+  if (!mm_ok(g)) return hipErrorInvalidValue;   // lmhead_tiled_ok admits bf16 rows with d % 64 == 0 only
+  e = launch_mm_lm(g, bn, st, ev0, ev1);
   if (e != hipSuccess) return e;
-  // (exact lists for M > 64: a kernel of its own, with fewer registers)
-  if (a.M > 64)
+  if (rowb) {
+    hipLaunchKernelGGL(k1_row_bound, dim3(a.rows), dim3(RB_THREADS), 0, st, a.gmax, ng,
+                       lmhead_groups(a.V), a.M, a.rbound);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // lists by the row bound or by exact bisection (M > 64), else the fast
+  // per-slice lists; (a kernel of its own, with fewer registers)
+  if (rowb || a.M > 64)
     hipExtLaunchKernelGGL(k1_lists_from_logits<true>, dim3((a.rows + LS_ROWS - 1) / LS_ROWS, a.P),
                           dim3(LS_ROWS / 2 * 64), (uint32_t)(LS_ROWS * K1_MAXCOLS * 4), st, nullptr, nullptr,
-                          0u, (const float *)logits, a.rows, a.V, a.M, a.part);
+                          0u, (const float *)logits, a.rows, a.V, a.M, a.part,
+                          rowb ? (const uint32_t *)a.rbound : nullptr);
   else
     hipExtLaunchKernelGGL(k1_lists_from_logits<false>, dim3((a.rows + LS_ROWS - 1) / LS_ROWS, a.P),
                           dim3(LS_ROWS / 2 * 64), (uint32_t)(LS_ROWS * K1_MAXCOLS * 4), st, nullptr, nullptr,
-                          0u, (const float *)logits, a.rows, a.V, a.M, a.part);
+                          0u, (const float *)logits, a.rows, a.V, a.M, a.part, nullptr);
   return hipGetLastError();
 }
 

@@ -26,18 +26,6 @@ constexpr int TB_THREADS = 1024;
 constexpr int TB_MAXDEP = 32;   // depths 0 .. 31: a parent chain has at most 32 nodes
 constexpr int TB_RANK_MAX = 256;   // superarbols up to this size: rank counting
 
-// inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within rows
-// of 16 lanes, then the row ends broadcast into the later rows)
-__device__ __forceinline__ int wave_scan_add(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15, rows 1, 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31, rows 2, 3
-  return v;
-}
-
 // low 4 bits of b as 4 bytes of 0/1 (bit k -> byte k): the product puts a
 // copy of bit k at bit 7m + k of term m, and only m = k lands on bit 8m
 __device__ __forceinline__ uint32_t spread4(uint32_t b) {

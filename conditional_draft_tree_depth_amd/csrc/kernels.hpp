@@ -88,7 +88,13 @@ struct LMHeadArgs {
   TreeBufs t;
   int ring;            // bf16: LDS ring depth from lmhead_ring (0 = register path)
   uint16_t *Hb;        // bf16, tiled product: [rows rounded up to 16, d] rounded hidden rows
+  // tiled product (or null): [rows, lmhead_groups(V)] ordered maxima of column
+  // groups of the logits, and [rows] the row-wide list bound found from them
+  uint32_t *gmax = nullptr, *rbound = nullptr;
 };
+// column groups of the tiled product's per-group logit maxima (the most any
+// of its tile shapes makes)
+inline int lmhead_groups(int V) { return (V + 63) / 64; }
 int lmhead_partitions(int V, int wtype, int extra_tiles);
 // LDS ring depth of the bf16 kernel that fits lds_max (0: register path)
 int lmhead_ring(int d, int wtype, size_t lds_max);
@@ -136,6 +142,11 @@ struct GemmArgs {
   int kw = 0;            // bf16 X only: W's k index is k mod kw (0: kw = Kd); a
                          // state split into bf16 planes [hi | lo]
                          // is multiplied by the same weights once per plane
+  // LM-head product only (or null): gmax[row * ldg + n / GW] = largest
+  // ordered output (f32_ord) of row over the columns n of its group of GW
+  // (the tile's columns per wave: 64 or 80)
+  uint32_t *gmax = nullptr;
+  int ldg = 0;
 };
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
 // GRU gates: gi, gh = input/state projections incl. biases ([R, 3s]); if gh

@@ -155,6 +155,35 @@ def test_tied_base_logits(gpu_lib, wtype, M, mode):
     check_config(x, cfg, f"tied {wtype} M={M} {mode}")
 
 
+@pytest.mark.parametrize("M,V,batch,D,mode", [
+    (128, 40000, 8, 4, None),     # 32 rows: 320-token tiles, maxima of 80-column groups
+    (32, 20011, 8, 4, None),      # odd V: 4-byte logit loads, a ragged last group
+    (64, 30000, 12, 12, None),    # 144 rows: 256-token tiles, maxima of 64-column groups
+    (128, 40000, 8, 4, "equal"),  # every key tied: whole slices reach the bound,
+    (32, 40000, 8, 4, "equal"),   #   so every list falls back to the exact search
+    (32, 40000, 8, 4, "groups"),  # tied groups of 97 tokens spread over the vocabulary
+    (128, 40000, 8, 4, "groups"),
+])
+def test_row_bound_lists(gpu_lib, M, V, batch, D, mode):
+    """Candidate lists from the tiled LM head's logits under the row-wide
+    bound (the M-th largest of the per-group logit maxima): every slice
+    lists its keys at or above it, or, where those overflow a list, its
+    exact M best."""
+    cfg = synth.custom_config(cfg_id=9800 + M + D, d=128, V=V, e=64, s=64, r=32, D=D, M=M, K=4,
+                              W=8, B=60, beta=-0.05, batch=batch, wtype="bf16")
+    x = synth.make_inputs(cfg, 11)
+    if mode is not None:
+        x["weights"]["W_lm"] = np.zeros_like(x["weights"]["W_lm"])
+        if mode == "equal":
+            x["weights"]["bias"] = np.zeros(V, np.float32)
+        else:
+            perm = np.random.default_rng(5).permutation(V)
+            x["weights"]["bias"] = (-0.25 * np.floor(perm / 97.0)).astype(np.float32)
+        check_config(x, cfg, f"row bound M={M} V={V} {mode}")
+    else:
+        check_config(x, cfg, f"row bound M={M} V={V}", max_ties_per_request=2, seed=11)
+
+
 def test_persistent_launch_modes(gpu_lib):
     """The persistent depth loop builds the same round with plain and with
     cooperative launches.  A round whose waits run out (forced from the host
