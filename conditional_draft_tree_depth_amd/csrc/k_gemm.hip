@@ -619,11 +619,14 @@ bool gemm_rdev_ok(const GemmArgs &a) {
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.R <= 0 || a.N <= 0) return hipSuccess;
   // a device row count up to 8192 rows: the contraction-split kernel, whose
-  // workgroups past the count leave at once, keeps every wave busy
-  const bool skinny_first = a.Rdev && a.R <= 8192 && skinny_ok(a);
+  // workgroups past the count leave at once, keeps every wave busy; with a
+  // long contraction (2048 or more) its activation re-reads (once per 16
+  // outputs) cost more, and 128 x 128 tiles take over (few active row tiles:
+  // the device count is often far below the bound)
+  const bool skinny_first = a.Rdev && a.R <= 8192 && skinny_ok(a) && a.Kd < 2048;
   if (!skinny_first && gemm_tiled_ok(a)) {
     int bm = 128, bn = 128;
-    mm_tile(a.R, a.N, &bm, &bn);
+    if (!(a.Rdev && a.R <= 8192)) mm_tile(a.R, a.N, &bm, &bn);
     return launch_mm(a, bm, bn, st, nullptr, nullptr);
   }
   if (a.kw && a.kw != a.Kd) return hipErrorInvalidValue;   // planes need the tiled kernel
