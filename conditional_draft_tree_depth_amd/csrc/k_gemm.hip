@@ -836,6 +836,63 @@ __global__ void k_token_map(int n, const int32_t *__restrict__ tok,
   rowmap[i] = cidx[rep];
 }
 
+// The rest in one workgroup (TT_THREADS threads, each a run of up to TT_PER
+// consecutive rows, so that one block scan of the run counts orders the
+// representatives by row): positions, the distinct tokens, their count, and
+// every row's position through its representative.  Each thread's loads are
+// issued together (unrolled over the run); the positions this workgroup
+// stored are read back with device-coherent loads.
+constexpr int TT_THREADS = 1024, TT_PER = 16;
+__global__ __launch_bounds__(TT_THREADS) void k_token_tables(int n, const int32_t *__restrict__ tok,
+                                                             const unsigned long long *__restrict__ first,
+                                                             uint32_t epoch, int32_t *cidx,
+                                                             int32_t *uniq, int32_t *rowmap,
+                                                             int32_t *count) {
+  __shared__ int wtot[TT_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (n + TT_THREADS - 1) / TT_THREADS;   // <= TT_PER (checked by the host)
+  const int i0 = min(n, tid * per), cnt = min(n, i0 + per) - i0;
+  int tk[TT_PER];
+  uint64_t fv[TT_PER];
+#pragma unroll
+  for (int u = 0; u < TT_PER; ++u) tk[u] = u < cnt ? tok[i0 + u] : 0;
+#pragma unroll
+  for (int u = 0; u < TT_PER; ++u) fv[u] = u < cnt ? first[tk[u]] : 0ull;
+  uint32_t repm = 0;   // bit u: row i0 + u represents its token
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < TT_PER; ++u)
+    if (u < cnt && fv[u] == td_tag(epoch, i0 + u)) { repm |= 1u << u; ++c; }
+  // exclusive prefix of the run counts over the workgroup
+  const int incl = wave_scan_add(c);
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int base = incl - c, total = 0;
+  for (int w = 0; w < TT_THREADS / 64; ++w) {
+    const int t = wtot[w];
+    base += w < wave ? t : 0;
+    total += t;
+  }
+#pragma unroll
+  for (int u = 0; u < TT_PER; ++u)
+    if (repm & (1u << u)) {
+      cidx[i0 + u] = base;
+      uniq[base] = tk[u];
+      ++base;
+    }
+  if (tid == 0) *count = total;
+  __syncthreads();
+  int pos[TT_PER];
+#pragma unroll
+  for (int u = 0; u < TT_PER; ++u)
+    pos[u] = u < cnt ? __hip_atomic_load(cidx + (int)(0xFFFFFFFFu - (uint32_t)fv[u]), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)
+                     : 0;
+#pragma unroll
+  for (int u = 0; u < TT_PER; ++u)
+    if (u < cnt) rowmap[i0 + u] = pos[u];
+}
+
 __global__ void k_zero_u64(unsigned long long *p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0ull;
@@ -854,6 +911,13 @@ hipError_t launch_token_dedupe(int n, const int32_t *tok, void *first, int V, ui
   if (epoch == 1u)
     hipLaunchKernelGGL(k_zero_u64, dim3((V + 255) / 256), dim3(256), 0, st, f, V);
   hipLaunchKernelGGL(k_token_mark, dim3(nb), dim3(TD_B), 0, st, n, tok, f, epoch);
+  // up to TT_PER rows per thread: the one-workgroup tables (one launch
+  // instead of four); more: block scans over many workgroups
+  if (n <= TT_PER * TT_THREADS) {
+    hipLaunchKernelGGL(k_token_tables, dim3(1), dim3(TT_THREADS), 0, st, n, tok, f, epoch, cidx,
+                       uniq, rowmap, count);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_token_scan, dim3(nb), dim3(TD_B), 0, st, n, tok, f, epoch, lpos, btot);
   hipLaunchKernelGGL(k_token_bases, dim3(1), dim3(1024), 0, st, nb, btot, count);
   hipLaunchKernelGGL(k_token_place, dim3(nb), dim3(TD_B), 0, st, n, tok, lpos, btot, cidx, uniq);
