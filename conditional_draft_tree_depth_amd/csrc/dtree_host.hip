@@ -60,6 +60,7 @@ struct Ws {
   float *logits = nullptr;   // [b * D, V] base logits when 32 or more rows (tiled product)
   uint32_t *gmax = nullptr;  //   with it: [b * D, lmhead_groups(V)] column-group maxima
   uint32_t *rbound = nullptr;  //   and [b * D] the rows' list bounds
+  int32_t *ovf = nullptr;      //   and [ceil(b * D / 8), P] overflow flags
   uint16_t *S3[2] = {nullptr, nullptr};   // states as bf16 planes (many branches)
   uint32_t *flags = nullptr;
   HeapBufs hp;               // sequential best-first builder (allocated on first use)
@@ -160,7 +161,7 @@ void free_ws(Ws &ws) {
                   ws.ccand, ws.selflag, ws.sscore[0], ws.sscore[1], ws.gi, ws.wcat, ws.n_tok, ws.n_par, ws.n_dep,
                   ws.n_score, ws.n_lex, ws.surv[0], ws.surv[1], ws.rank[0], ws.rank[1], ws.surv_hist, ws.gidx_tok, ws.gidx_par, ws.sel,
                   ws.status, ws.G, ws.g, ws.pk_part, ws.gitab, ws.pk_terms, ws.w1t, ws.flags,
-                  ws.logits, ws.gmax, ws.rbound, ws.S3[0], ws.S3[1], ws.gi_all, ws.gidx_cand, ws.first_row,
+                  ws.logits, ws.gmax, ws.rbound, ws.ovf, ws.S3[0], ws.S3[1], ws.gi_all, ws.gidx_cand, ws.first_row,
                   ws.cidx_tmp, ws.uniq, ws.rowmap, ws.ucount, ws.lpos, ws.btot,
                   ws.hp.tok, ws.hp.par, ws.hp.dep, ws.hp.score, ws.hp.gref, ws.hp.pv,
                   ws.hp.nnodes, ws.hp.pops, ws.hp.ex, ws.hp.S, ws.hp.UH, ws.hp.gi};
@@ -262,6 +263,7 @@ extern "C" dtree_status dtree_create(const dtree_weights *w, const dtree_caps *c
     A(alloc(&ws.logits, rows * (size_t)w->V));
     A(alloc(&ws.gmax, rows * (size_t)lmhead_groups(w->V)));
     A(alloc(&ws.rbound, rows));
+    A(alloc(&ws.ovf, (rows + 7) / 8 * (size_t)ctx->P));
   }
   A(alloc(&ws.S[0], bw * s));
   A(alloc(&ws.S[1], bw * s));
@@ -440,7 +442,7 @@ static dtree_status enqueue_round(dtree_ctx *ctx, const dtree_params *p, int32_t
                        reinterpret_cast<uintptr_t>(w.W1) % 16 == 0;
   LMHeadArgs la{H, rows, d, w.W_lm, wt, w.V, w.lm_bias, M, ctx->P, ws.part,
                 fuse_uH ? w.W1 : nullptr, d + s, r, ws.uH,
-                root, batch, D + 1, tb, ctx->k1_ring, ws.hb, ws.gmax, ws.rbound};
+                root, batch, D + 1, tb, ctx->k1_ring, ws.hb, ws.gmax, ws.rbound, ws.ovf};
   // round start: a kernel of its own ahead of the tiled product (bf16 rows
   // for it); the streaming kernels round the rows and start the round
   // themselves

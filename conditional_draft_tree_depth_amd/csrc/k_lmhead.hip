@@ -899,16 +899,9 @@ __global__ __launch_bounds__(256) void k1_stage_hidden(const float *__restrict__
 // The keys >= K, exactly M of them, are written unsorted with K as the
 // list's bound, the best key and the count (the layout of the fast path).
 // A slice with fewer than M keys writes all of them with a zero bound.
-// With a row-wide bound rbound[r] (an ordered value that at least M keys of
-// the whole row reach, from k1_row_bound) the list is instead every slice
-// key of value >= that bound, written with it as the list's bound, whenever
-// those keys fit a list for both rows of the wave (usually a few per slice);
-// otherwise the search above runs.  Either list holds every slice key at or
-// above its bound, and at least M keys of the row reach it.
 template <int MAXC>
 __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int ncols, int col0,
-                                               int nrow, int M, uint64_t *out, size_t rstride,
-                                               const uint32_t *rbound) {
+                                               int nrow, int M, uint64_t *out, size_t rstride) {
   constexpr int KPL = MAXC / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6, hl = lane & 31;
@@ -936,16 +929,7 @@ __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int
     }
     auto tie_of = [&](int i) { return 0xFFFFFFFFu - (uint32_t)(col0 + hl + 32 * i); };
     uint64_t T = 0;   // the M-th largest key (0: fewer than M keys)
-    bool bounded = false;
-    if (rbound) {
-      const uint32_t tb = active ? rbound[r] : 0xFFFFFFFFu;
-      int c = 0;
-#pragma unroll
-      for (int i = 0; i < KPL; ++i) c += (hv[i] >= tb && hv[i] != 0u) ? 1 : 0;
-      bounded = __all(!active || (tb != 0u && total(c) <= K1_LCAP));
-      if (bounded) T = (uint64_t)tb << 32;
-    }
-    if (!bounded && ncols > M) {
+    if (ncols > M) {
       // (a step whose count is exactly M has found a value bound with
       // exactly M keys at or above it: once every row of the wave has one,
       // the search stops and that bound is the list's)
@@ -1021,13 +1005,16 @@ __device__ __forceinline__ void wg_topm_bisect(const float *Ls, int lstride, int
 // 8 rows (4 waves) per workgroup: two or more workgroups per CU, so that one
 // workgroup's loads overlap another's selection
 constexpr int LS_ROWS = 8;
+// With ovf given, only the workgroups whose flag k1_lists_bounded raised
+// run (exact lists, BISECT); the others leave at once.
 template <bool BISECT>
 __global__ __launch_bounds__(LS_ROWS / 2 * 64) void k1_lists_from_logits(
     const float *__restrict__ L, int rows, int V, int M, uint64_t *__restrict__ part,
-    const uint32_t *__restrict__ rbound) {
+    const int32_t *__restrict__ ovf) {
   extern __shared__ __align__(16) uint8_t smem[];
   float *Ls = reinterpret_cast<float *>(smem);
   const int P = gridDim.y, y = blockIdx.y, row0 = blockIdx.x * LS_ROWS;
+  if (ovf && ovf[(size_t)blockIdx.x * P + y] == 0) return;
   const int nrow = min(LS_ROWS, rows - row0);
   const int ntV = (V + 15) >> 4;
   const int t0 = (int)((long long)ntV * y / P), t1 = (int)((long long)ntV * (y + 1) / P);
@@ -1079,10 +1066,80 @@ __global__ __launch_bounds__(LS_ROWS / 2 * 64) void k1_lists_from_logits(
   __syncthreads();
   uint64_t *out = part + ((size_t)row0 * P + y) * K1_LSTRIDE;
   if constexpr (BISECT)
-    wg_topm_bisect<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE,
-                               rbound ? rbound + row0 : nullptr);
+    wg_topm_bisect<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE);
   else
     wg_topm_epilogue<K1_MAXCOLS>(Ls, K1_MAXCOLS, ncols, c0, nrow, M, out, (size_t)P * K1_LSTRIDE);
+}
+
+// Lists under the row-wide bound (rbound[row], from k1_row_bound: an ordered
+// value that at least M keys of the row reach): every slice key of value >=
+// the bound, written unsorted with the bound as the list's tau, the slice's
+// best key and the count — usually a few keys per slice.  Such a list holds
+// every slice key at or above its tau, and M keys of the row reach it, which
+// is all the merge relies on.  One row per half-wave, LS_ROWS rows per
+// workgroup (the grid of k1_lists_from_logits); lane l reads columns l + 32 i
+// straight from the logits (128 contiguous bytes per half-wave and step).
+// Where a row's keys would overflow a list (ties) its wave writes nothing and
+// the workgroup's flag ovf[block] is set (else cleared); the exact kernel
+// then rewrites the lists of the flagged workgroups.
+__global__ __launch_bounds__(LS_ROWS / 2 * 64) void k1_lists_bounded(
+    const float *__restrict__ L, int rows, int V, const uint32_t *__restrict__ rbound,
+    uint64_t *__restrict__ part, int32_t *__restrict__ ovf) {
+  constexpr int KPL = K1_MAXCOLS / 32;
+  __shared__ int any_over;
+  const int P = gridDim.y, y = blockIdx.y, row0 = blockIdx.x * LS_ROWS;
+  const int ntV = (V + 15) >> 4;
+  const int t0 = (int)((long long)ntV * y / P), t1 = (int)((long long)ntV * (y + 1) / P);
+  const int c0 = t0 * 16, ncols = max(0, min(t1 * 16, V) - c0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hl = lane & 31;
+  const int rr = 2 * wave + (lane >> 5), r = row0 + rr;
+  const bool active = r < rows;
+  if (threadIdx.x == 0) any_over = 0;
+  const float *lr = L + (size_t)(active ? r : row0) * V + c0;   // in bounds for every lane
+  uint32_t hv[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int c = hl + 32 * i;
+    const float x = lr[c < ncols ? c : 0];
+    hv[i] = (active && c < ncols) ? f32_ord(x) : 0u;
+  }
+  const uint32_t tb = active ? rbound[r] : 0xFFFFFFFFu;
+  int cnt = 0;
+  uint64_t best = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const bool in = hv[i] >= tb && hv[i] != 0u;
+    cnt += in ? 1 : 0;
+    const uint64_t k = ((uint64_t)hv[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(c0 + hl + 32 * i));
+    best = (in && k > best) ? k : best;
+  }
+  // inclusive prefix of the counts over the half-wave, and its total
+  int incl = cnt, tot = cnt, yv;
+  yv = (int)dpp_u32<0xB1>((uint32_t)tot); if (hl & 1) incl += yv; tot += yv;
+  yv = (int)dpp_u32<0x4E>((uint32_t)tot); if (hl & 2) incl += yv; tot += yv;
+  yv = __builtin_amdgcn_ds_swizzle(tot, 0x101F); if (hl & 4) incl += yv; tot += yv;
+  yv = __builtin_amdgcn_ds_swizzle(tot, 0x201F); if (hl & 8) incl += yv; tot += yv;
+  yv = __builtin_amdgcn_ds_swizzle(tot, 0x401F); if (hl & 16) incl += yv; tot += yv;
+  const uint64_t head = group_max_u64<32>(best);
+  const bool over = __any(active && (tb == 0u || tot > K1_LCAP));
+  __syncthreads();   // (any_over cleared)
+  if (over) {
+    if (lane == 0) any_over = 1;
+  } else if (active) {
+    uint64_t *outr = part + ((size_t)r * P + y) * K1_LSTRIDE;
+    int pos = incl - cnt;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (hv[i] >= tb && hv[i] != 0u)
+        outr[pos++] = ((uint64_t)hv[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(c0 + hl + 32 * i));
+    if (hl == 0) {
+      outr[K1_LCAP] = (uint64_t)tb << 32;
+      outr[K1_LCAP + 1] = head;
+      outr[K1_LCAP + 2] = (uint64_t)tot;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) ovf[(size_t)blockIdx.x * P + y] = any_over;
 }
 
 // Row-wide list bound: the M-th largest of the row's ng column-group maxima
@@ -1205,7 +1262,7 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
   const int ng = (a.V + gw - 1) / gw;
   // the row-wide list bound needs M groups (lmhead_groups sizes gmax for
   // the narrowest groups)
-  const bool rowb = a.gmax && a.rbound && ng >= a.M;
+  const bool rowb = a.gmax && a.rbound && a.ovf && ng >= a.M;
   if (rowb) { g.gmax = a.gmax; g.ldg = lmhead_groups(a.V); }
   if (!mm_ok(g)) return hipErrorInvalidValue;   // lmhead_tiled_ok admits bf16 rows with d % 64 == 0 only
   e = launch_mm_lm(g, bn, st, ev0, ev1);
@@ -1215,13 +1272,18 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
                        lmhead_groups(a.V), a.M, a.rbound);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // lists by the row bound or by exact bisection (M > 64), else the fast
-  // per-slice lists; (a kernel of its own, with fewer registers)
+  // lists under the row bound, exact lists (bisection) for the workgroups
+  // whose keys overflowed them; without the bound, exact lists for M > 64,
+  // else the fast per-slice lists (each a kernel of its own: fewer registers)
+  const dim3 lgrid((a.rows + LS_ROWS - 1) / LS_ROWS, a.P);
+  if (rowb)
+    hipLaunchKernelGGL(k1_lists_bounded, lgrid, dim3(LS_ROWS / 2 * 64), 0, st, (const float *)logits,
+                       a.rows, a.V, (const uint32_t *)a.rbound, a.part, a.ovf);
   if (rowb || a.M > 64)
-    hipExtLaunchKernelGGL(k1_lists_from_logits<true>, dim3((a.rows + LS_ROWS - 1) / LS_ROWS, a.P),
+    hipExtLaunchKernelGGL(k1_lists_from_logits<true>, lgrid,
                           dim3(LS_ROWS / 2 * 64), (uint32_t)(LS_ROWS * K1_MAXCOLS * 4), st, nullptr, nullptr,
                           0u, (const float *)logits, a.rows, a.V, a.M, a.part,
-                          rowb ? (const uint32_t *)a.rbound : nullptr);
+                          rowb ? (const int32_t *)a.ovf : nullptr);
   else
     hipExtLaunchKernelGGL(k1_lists_from_logits<false>, dim3((a.rows + LS_ROWS - 1) / LS_ROWS, a.P),
                           dim3(LS_ROWS / 2 * 64), (uint32_t)(LS_ROWS * K1_MAXCOLS * 4), st, nullptr, nullptr,

@@ -91,6 +91,7 @@ struct LMHeadArgs {
   // tiled product (or null): [rows, lmhead_groups(V)] ordered maxima of column
   // groups of the logits, and [rows] the row-wide list bound found from them
   uint32_t *gmax = nullptr, *rbound = nullptr;
+  int32_t *ovf = nullptr;   // [ceil(rows / 8), P] flags: lists that overflowed the bound
 };
 // column groups of the tiled product's per-group logit maxima (the most any
 // of its tile shapes makes)
