@@ -540,14 +540,14 @@ __global__ __launch_bounds__(WM * WN * 64) void k_mm_lm(GemmArgs a) {
 }
 template <int BM, int BN, int SB>
 static constexpr size_t mm_lm_smem() { return (size_t)2 * BM * 128 + (size_t)SB * BN * 128; }
-#define MM_LM_CONFIGS(X) X(128, 256, 2, 4, 4) X(128, 320, 2, 4, 3)
+#define MM_LM_CONFIGS(X) X(128, 256, 2, 4, 4) X(128, 320, 2, 4, 3) X(256, 256, 2, 4, 3)
 
-hipError_t launch_mm_lm(const GemmArgs &a, int bn, hipStream_t st, hipEvent_t ev0,
+hipError_t launch_mm_lm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
                         hipEvent_t ev1) {
-  const int total = ((a.R + 127) / 128) * ((a.N + bn - 1) / bn);
+  const int total = ((a.R + bm - 1) / bm) * ((a.N + bn - 1) / bn);
   const dim3 grid(8 * ((total + 7) / 8));
 #define MM_LM_LAUNCH(BM_, BN_, WM_, WN_, SB_)                                                   \
-  if (bn == BN_) {                                                                              \
+  if (bm == BM_ && bn == BN_) {                                                                 \
     hipExtLaunchKernelGGL((k_mm_lm<BM_, BN_, WM_, WN_, SB_>), grid, dim3(WM_ * WN_ * 64),       \
                           (uint32_t)mm_lm_smem<BM_, BN_, SB_>(), st, ev0, ev1, 0u, a);          \
     return hipGetLastError();                                                                   \

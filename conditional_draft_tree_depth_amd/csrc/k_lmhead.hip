@@ -1258,6 +1258,7 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
   // one row tile: 320-token tiles make 1.9 rounds of workgroups over the
   // vocabulary (475 tiles at V = 151936) instead of 2.3 rounds of 256
   const int bn = a.rows <= 128 ? 320 : 256;
+  const int bm = a.rows >= 256 ? 256 : 128;
   const int gw = bn / 4;   // columns per wave of the tile: the maxima's groups
   const int ng = (a.V + gw - 1) / gw;
   // the row-wide list bound needs M groups (lmhead_groups sizes gmax for
@@ -1265,7 +1266,7 @@ hipError_t launch_lmhead_tiled(const LMHeadArgs &a, float *logits, hipStream_t s
   const bool rowb = a.gmax && a.rbound && a.ovf && ng >= a.M;
   if (rowb) { g.gmax = a.gmax; g.ldg = lmhead_groups(a.V); }
   if (!mm_ok(g)) return hipErrorInvalidValue;   // lmhead_tiled_ok admits bf16 rows with d % 64 == 0 only
-  e = launch_mm_lm(g, bn, st, ev0, ev1);
+  e = launch_mm_lm(g, bm, bn, st, ev0, ev1);
   if (e != hipSuccess) return e;
   if (rowb) {
     hipLaunchKernelGGL(k1_row_bound, dim3(a.rows), dim3(RB_THREADS), 0, st, a.gmax, ng,

@@ -181,9 +181,9 @@ bool mm_ok(const GemmArgs &a);
 void mm_tile(int R, int N, int *bm, int *bn);
 hipError_t launch_mm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
                      hipEvent_t ev1);
-// the LM-head product (no row gather, no planes, bias from n = 0): 128-row
-// tiles of bn in {256, 320} tokens with a ring per operand
-hipError_t launch_mm_lm(const GemmArgs &a, int bn, hipStream_t st, hipEvent_t ev0,
+// the LM-head product (no row gather, no planes, bias from n = 0): tiles of
+// bm x bn in {128 x 256, 128 x 320, 256 x 256} with a ring per operand
+hipError_t launch_mm_lm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
                         hipEvent_t ev1);
 // true when launch_gemm accepts a device row count (a.Rdev) for a
 bool gemm_rdev_ok(const GemmArgs &a);

@@ -159,6 +159,7 @@ def test_tied_base_logits(gpu_lib, wtype, M, mode):
     (128, 40000, 8, 4, None),     # 32 rows: 320-token tiles, maxima of 80-column groups
     (32, 20011, 8, 4, None),      # odd V: 4-byte logit loads, a ragged last group
     (64, 30000, 12, 12, None),    # 144 rows: 256-token tiles, maxima of 64-column groups
+    (32, 20000, 16, 16, None),    # 256 rows: 256 x 256 tiles
     (128, 40000, 8, 4, "equal"),  # every key tied: whole slices reach the bound,
     (32, 40000, 8, 4, "equal"),   #   so every list falls back to the exact search
     (32, 40000, 8, 4, "groups"),  # tied groups of 97 tokens spread over the vocabulary
