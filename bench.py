@@ -62,7 +62,8 @@ def dominant_kernel(cfg):
     Fewer than 32 hidden rows: the streaming kernel with the fused per-slice
     Top-M (the logits never leave the chip): HBM-bound, bytes = W_lm + bias
     + H.  32 or more rows (bf16): the tiled product writing the logits
-    (k_mm_lm, 128 x 320 tiles up to 128 rows, 128 x 256 beyond); its
+    (k_mm_lm, 128 x 320 tiles up to 128 rows, 128 x 256 up to 255, 256 x
+    256 from 256 rows); its
     arithmetic intensity 2 rows d V / (2 V d + 2 rows d + 4 rows V) decides
     the bound against the ridge of the published peaks."""
     es = 2 if cfg.wtype == "bf16" else 4
@@ -74,8 +75,10 @@ def dominant_kernel(cfg):
         ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         if rows <= 128:
             kern, label = "k_mm_lm<128, 320>", "tiled bf16 MFMA LM-head product, 128 x 320 tiles"
-        else:
+        elif rows < 256:
             kern, label = "k_mm_lm<128, 256>", "tiled bf16 MFMA LM-head product, 128 x 256 tiles"
+        else:
+            kern, label = "k_mm_lm<256, 256>", "tiled bf16 MFMA LM-head product, 256 x 256 tiles"
         if flops / nbytes >= ridge:
             return dict(kernel=kern, label=label, bound="mfma", work=flops,
                         peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", scale=1e12)

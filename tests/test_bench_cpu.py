@@ -55,7 +55,7 @@ def test_dominant_kernel_follows_the_path_each_workload_runs():
     assert k["qwen3_8b_x8"]["kernel"] == "k_mm_lm<128, 320>" and k["qwen3_8b_x8"]["bound"] == "hbm"
     # 512 hidden rows: 128 x 256 tiles, past the ridge of the published
     # peaks, MFMA-bound
-    assert k["stress_b0"]["kernel"] == "k_mm_lm<128, 256>"
+    assert k["stress_b0"]["kernel"] == "k_mm_lm<256, 256>"
     assert k["stress_b0"]["bound"] == "mfma" and k["stress_b0"]["unit"] == "TFLOP/s"
     c = synth.CONFIGS["stress_b0"]
     assert k["stress_b0"]["work"] == 2 * c.batch * c.D * c.d * c.V
