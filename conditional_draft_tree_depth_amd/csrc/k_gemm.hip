@@ -580,7 +580,7 @@ bool mm_ok(const GemmArgs &a) {
 }
 
 // configurations: (BM, BN, WM, WN)
-#define MM_CONFIGS(X) X(256, 128, 8, 2, 3) X(128, 128, 4, 2, 2)
+#define MM_CONFIGS(X) X(256, 128, 8, 2, 3) X(128, 128, 4, 2, 2) X(128, 64, 4, 1, 4)
 
 hipError_t launch_mm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
                      hipEvent_t ev1) {
@@ -648,11 +648,12 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   // a device row count up to 8192 rows: the contraction-split kernel, whose
   // workgroups past the count leave at once, keeps every wave busy; with a
   // long contraction (2048 or more) its activation re-reads (once per 16
-  // outputs) cost more, and 128 x 128 tiles take over (few active row tiles:
-  // the device count is often far below the bound)
+  // outputs) cost more, and 128 x 64 tiles take over (few active row tiles:
+  // the device count is often far below the bound, so narrow column tiles
+  // give more active workgroups)
   const bool skinny_first = a.Rdev && a.R <= 8192 && skinny_ok(a) && a.Kd < 2048;
   if (!skinny_first && gemm_tiled_ok(a)) {
-    int bm = 128, bn = 128;
+    int bm = 128, bn = 64;
     if (!(a.Rdev && a.R <= 8192)) mm_tile(a.R, a.N, &bm, &bn);
     return launch_mm(a, bm, bn, st, nullptr, nullptr);
   }

@@ -88,6 +88,9 @@ def test_random_small_shapes(gpu_lib, seed):
     (11, 128, 64, 61, 24, 5, 33, 5, 12, 60, 3),
     # rank 512 (16 k steps), 128 candidates, 64 survivors of 512 children
     (12, 128, 128, 128, 512, 4, 128, 8, 64, 200, 2),
+    # 2560 candidates, e = 2048: the distinct tokens' input projections on
+    # 128 x 64 tiles with the row count read on the device
+    (13, 128, 2048, 192, 32, 4, 64, 4, 8, 60, 10),
 ])
 def test_mfma_product_paths(gpu_lib, seed, d, e, s, r, D, M, K, W, B, batch):
     """bf16 shapes whose products run on the MFMA kernels: the row-gathered
