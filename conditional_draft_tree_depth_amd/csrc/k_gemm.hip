@@ -580,14 +580,19 @@ bool mm_ok(const GemmArgs &a) {
 }
 
 // configurations: (BM, BN, WM, WN)
-#define MM_CONFIGS(X) X(256, 128, 8, 2, 3) X(128, 128, 4, 2, 2) X(128, 64, 4, 1, 4)
+// 128 x 128 tiles: a three-stage ring (96 KiB, one workgroup per CU) when
+// the tiles fit one per CU (wide candidates' projections 54 -> 47 us), else
+// two stages, so that two workgroups share a CU (stress state products: 975
+// against 1,203 us for the depth loop with three)
+#define MM_CONFIGS(X) X(256, 128, 8, 2, 3) X(128, 128, 4, 2, 2) X(128, 128, 4, 2, 3) X(128, 64, 4, 1, 4)
 
 hipError_t launch_mm(const GemmArgs &a, int bm, int bn, hipStream_t st, hipEvent_t ev0,
                      hipEvent_t ev1) {
   const int total = ((a.R + bm - 1) / bm) * ((a.N + bn - 1) / bn);
   const dim3 grid(8 * ((total + 7) / 8));
+  const int stages = (bm == 128 && bn == 128) ? (total <= 256 ? 3 : 2) : 0;
 #define MM_LAUNCH(BM_, BN_, WM_, WN_, S_)                                                       \
-  if (bm == BM_ && bn == BN_) {                                                                 \
+  if (bm == BM_ && bn == BN_ && (stages == 0 || stages == S_)) {                                \
     hipExtLaunchKernelGGL((k_mm<BM_, BN_, WM_, WN_, S_>), grid, dim3(WM_ * WN_ * 64),           \
                           (uint32_t)mm_smem<BM_, BN_, S_>(), st, ev0, ev1, 0u, a);              \
     return hipGetLastError();                                                                   \
